@@ -1,0 +1,331 @@
+"""Pins of the Tensor Cache oracle against things other than itself.
+
+Page: "Tensor Cache: Eviction-conditioned Associative Memory for Transformers"
+(Methodology 1 and 2, Main contributions), with the linear-attention identity
+of the DeltaNet-variants page and the Hebbian memory of the Hebbian-MLP page.
+Every check here is CPU-only.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import tc as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_inputs(seed, B=2, H=2, T=40, dk=5, dv=4, unit_keys=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, dk))
+    if unit_keys:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, H, T, dv))
+    lam = rng.uniform(0.5, 1.0, H)
+    eta = rng.uniform(0.1, 1.0, H)
+    g = rng.standard_normal(H)
+    return q, k, v, lam, eta, g
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def brute_force_m(q, k, v, lam, eta, W):
+    """Pure-Python double sum m_t = sum_{i<=t-W} eta lam^((t-W)-i) <q_t,k_i> v_i."""
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    out = np.zeros((B, H, T, dv))
+    for b in range(B):
+        for h in range(H):
+            for t in range(T):
+                for i in range(0, t - W + 1):
+                    w = eta[h] * lam[h] ** ((t - W) - i)
+                    dot = sum(q[b, h, t, a] * k[b, h, i, a] for a in range(dk))
+                    for c in range(dv):
+                        out[b, h, t, c] += w * dot * v[b, h, i, c]
+    return out
+
+
+# ---------------------------------------------------------------- hand examples
+
+def test_hand_examples():
+    with open(os.path.join(GOLD, "tc_hand_examples.json")) as f:
+        g = json.load(f)
+    inp = g["inputs"]
+    q = np.array(inp["q"], float)[None, None]
+    k = np.array(inp["k"], float)[None, None]
+    v = np.array(inp["v"], float)[None, None]
+    lam = np.array([inp["lam"]])
+    eta = np.array([inp["eta"]])
+    for case in g["cases"]:
+        W = case["W"]
+        m, A = O.tc_scan(q, k, v, lam, eta, W)
+        np.testing.assert_allclose(m[0, 0], case["m"], atol=1e-12)
+        np.testing.assert_allclose(A[0, 0], case["A_final"], atol=1e-12)
+        y, _ = O.tc_fused(q, k, v, lam, eta, np.array([case["g"]]), W, scale=case["scale"])
+        np.testing.assert_allclose(y[0, 0], case["y"], atol=1e-12)
+
+
+# ---------------------------------------------------------------- L2 memory
+
+@pytest.mark.parametrize("W", [1, 3, 7, 40, 45])
+@pytest.mark.parametrize("lam_kind", ["rand", "zero", "one"])
+def test_brute_force_double_sum(W, lam_kind):
+    q, k, v, lam, eta, _ = rand_inputs(1 + W, B=1, H=2, T=24, dk=3, dv=2)
+    if lam_kind == "zero":
+        lam = np.zeros_like(lam)
+    elif lam_kind == "one":
+        lam = np.ones_like(lam)
+    m, _ = O.tc_scan(q, k, v, lam, eta, W)
+    ref = brute_force_m(q, k, v, lam, eta, W)
+    assert np.max(np.abs(m - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_lambda_one_is_cumulative_hebbian_sum():
+    # lam = 1: A_t = eta * sum_{i <= t-W} k_i v_i^T, the classical Hebbian memory
+    # W = sum v k^T of the Hebbian-MLP page (transposed orientation), via np.cumsum.
+    q, k, v, lam, eta, _ = rand_inputs(2, T=50)
+    lam = np.ones_like(lam)
+    W = 6
+    m, A = O.tc_scan(q, k, v, lam, eta, W)
+    outer = k[..., :, None] * v[..., None, :]  # [B,H,T,dk,dv]
+    cums = np.cumsum(outer, axis=2)
+    T = q.shape[2]
+    ref = np.zeros_like(m)
+    for t in range(W, T):
+        ref[:, :, t] = eta[None, :, None] * np.einsum("bhd,bhde->bhe", q[:, :, t], cums[:, :, t - W])
+    np.testing.assert_allclose(m, ref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(A, eta[None, :, None, None] * cums[:, :, T - 1 - W], rtol=1e-12, atol=1e-13)
+
+
+def test_lambda_zero_keeps_only_last_eviction():
+    q, k, v, lam, eta, _ = rand_inputs(3, T=30)
+    W = 4
+    m, _ = O.tc_scan(q, k, v, np.zeros_like(lam), eta, W)
+    ref = np.zeros_like(m)
+    for t in range(W, q.shape[2]):
+        dot = np.einsum("bhd,bhd->bh", q[:, :, t], k[:, :, t - W])
+        ref[:, :, t] = eta[None, :, None] * dot[..., None] * v[:, :, t - W]
+    np.testing.assert_allclose(m, ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("W", [30, 31, 100])
+def test_window_covering_sequence_reads_zero(W):
+    q, k, v, lam, eta, _ = rand_inputs(4, T=30)
+    m, A = O.tc_scan(q, k, v, lam, eta, W)
+    assert np.all(m == 0.0) and np.all(A == 0.0)
+
+
+def test_single_write_is_linear_attention_identity():
+    # One eviction: q (k (x) v) = <q, k> v (read identity of the Tensor Cache page,
+    # core identity of the DeltaNet-variants page).
+    q, k, v, lam, eta, _ = rand_inputs(5, T=9)
+    W = 8
+    m, A = O.tc_scan(q, k, v, lam, eta, W)
+    dot = np.einsum("bhd,bhd->bh", q[:, :, 8], k[:, :, 0])
+    np.testing.assert_allclose(m[:, :, 8], eta[None, :, None] * dot[..., None] * v[:, :, 0], rtol=1e-13)
+    assert np.all(m[:, :, :8] == 0.0)
+
+
+def test_partition_identity_each_token_counted_once():
+    # Main contributions: tokens split cleanly into L1-resident and L2-compressed.
+    # With lam = eta = 1, the L2 read plus the plain linear sum over the L1 window
+    # equals causal linear attention over all tokens (computed as one masked product).
+    q, k, v, lam, eta, _ = rand_inputs(6, T=37)
+    ones = np.ones_like(lam)
+    for W in (1, 5, 16, 37, 50):
+        m, _ = O.tc_scan(q, k, v, ones, ones, W)
+        T = q.shape[2]
+        s = np.einsum("bhtd,bhjd->bhtj", q, k)
+        causal = np.tril(np.ones((T, T)))
+        full = np.einsum("bhtj,bhje->bhte", s * causal, v)
+        rel_win = np.tril(np.ones((T, T))) - np.tril(np.ones((T, T)), -W)
+        local = np.einsum("bhtj,bhje->bhte", s * rel_win, v)
+        np.testing.assert_allclose(m + local, full, rtol=1e-11, atol=1e-12)
+
+
+def test_closed_form_rows_match_recurrence():
+    q, k, v, lam, eta, _ = rand_inputs(7, T=70)
+    W = 9
+    m, _ = O.tc_scan(q, k, v, lam, eta, W)
+    rows = [0, 8, 9, 10, 33, 69]
+    np.testing.assert_allclose(O.tc_scan_rows(q, k, v, lam, eta, W, rows), m[:, :, rows], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("T,W,C", [(200, 13, 64), (64 + 5, 5, 64), (257, 1, 64), (40, 3, 8), (50, 60, 64)])
+def test_chunked_scan_equals_sequential(T, W, C):
+    # Methodology 2: the parallel weighted-sum scan equals the sequential writes.
+    q, k, v, lam, eta, _ = rand_inputs(8, T=T)
+    for lam_v in (lam, np.zeros_like(lam), np.ones_like(lam)):
+        m, A = O.tc_scan(q, k, v, lam_v, eta, W)
+        mc, Ac = O.tc_scan_chunked(q, k, v, lam_v, eta, W, C)
+        assert rel(mc, m) <= 1e-12
+        assert rel(Ac, A) <= 1e-12
+
+
+def test_chunk_mean_shortcut_is_wrong():
+    # Methodology 2: the chunk-mean shortcut adds spurious cross products; it must
+    # differ visibly from the sequential oracle on random data.
+    q, k, v, lam, eta, _ = rand_inputs(9, T=300)
+    m, _ = O.tc_scan(q, k, v, lam, eta, 20)
+    mm, _ = O.chunk_mean_scan(q, k, v, lam, eta, 20, C=64)
+    assert rel(mm, m) > 1e-3
+
+
+def test_chunk_mean_cross_product_count():
+    # With one-hot keys/values e_i, the true chunk write sum_i k_i v_i^T is the identity,
+    # while C * mean(k) (x) mean(v) has C^2 - C nonzero off-diagonal entries.
+    C = 8
+    d = 8
+    k = np.eye(d)[None, None, :C]
+    v = np.eye(d)[None, None, :C]
+    q = np.zeros_like(k)
+    one = np.ones(1)
+    _, A_true = O.tc_scan(q, np.concatenate([k, k[:, :, :1]], 2), np.concatenate([v, v[:, :, :1]], 2),
+                          one, one, 1)
+    _, A_mean = O.chunk_mean_scan(q, k, v, one, one, 0, C=C)
+    off = ~np.eye(d, dtype=bool)
+    assert np.count_nonzero(np.abs(A_true[0, 0][off]) > 1e-15) == 0
+    assert np.count_nonzero(np.abs(A_mean[0, 0][off]) > 1e-15) == C * C - C
+
+
+# ---------------------------------------------------------------- streaming ring
+
+@pytest.mark.parametrize("W", [1, 4, 9])
+def test_decoder_ring_matches_scan(W):
+    q, k, v, lam, eta, _ = rand_inputs(10, T=30)
+    m, A = O.tc_scan(q, k, v, lam, eta, W)
+    B, H, T, dk = q.shape
+    dec = O.TensorCacheDecoder(B, H, dk, v.shape[-1], W, lam, eta)
+    for t in range(T):
+        mt = dec.step(q[:, :, t], k[:, :, t], v[:, :, t])
+        np.testing.assert_allclose(mt, m[:, :, t], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dec.A, A, rtol=1e-12, atol=1e-14)
+    # the ring holds exactly the last W tokens at slots pos mod W
+    for t in range(max(0, T - W), T):
+        np.testing.assert_array_equal(dec.ring_k[:, :, t % W], k[:, :, t])
+
+
+def test_scan_then_decode_equals_longer_scan():
+    # Streaming continuation: prefill with the scan, hand over A_final and the last W
+    # tokens as the ring, continue with single steps.
+    q, k, v, lam, eta, _ = rand_inputs(11, T=45)
+    W, T0 = 7, 30
+    m_full, A_full = O.tc_scan(q, k, v, lam, eta, W)
+    _, A0 = O.tc_scan(q[:, :, :T0], k[:, :, :T0], v[:, :, :T0], lam, eta, W)
+    B, H = q.shape[:2]
+    ring_k = np.zeros((B, H, W, q.shape[-1]))
+    ring_v = np.zeros((B, H, W, v.shape[-1]))
+    for t in range(T0 - W, T0):
+        ring_k[:, :, t % W] = k[:, :, t]
+        ring_v[:, :, t % W] = v[:, :, t]
+    dec = O.TensorCacheDecoder.from_state(ring_k, ring_v, A0, np.full(B, T0), W, lam, eta)
+    for t in range(T0, 45):
+        np.testing.assert_allclose(dec.step(q[:, :, t], k[:, :, t], v[:, :, t]), m_full[:, :, t],
+                                   rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dec.A, A_full, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- L1 and fusion
+
+def test_window_covering_sequence_is_causal_softmax_attention():
+    q, k, v, *_ = rand_inputs(12, T=33)
+    scale = 1 / math.sqrt(q.shape[-1])
+    y = O.window_softmax(q, k, v, 1000, scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True, scale=scale).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_window_is_banded_softmax_attention():
+    # sliding window = softmax attention under a band mask (library routine with an explicit mask)
+    q, k, v, *_ = rand_inputs(13, T=40)
+    W, scale = 6, 0.37
+    T = q.shape[2]
+    i = np.arange(T)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - W)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(band), scale=scale).numpy()
+    np.testing.assert_allclose(O.window_softmax(q, k, v, W, scale), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_window_one_returns_value():
+    q, k, v, *_ = rand_inputs(14, T=20)
+    np.testing.assert_array_equal(O.window_softmax(q, k, v, 1, 0.5), v)
+
+
+def test_gate_limits():
+    q, k, v, lam, eta, _ = rand_inputs(15, T=30)
+    W = 5
+    scale = 0.4
+    y_loc = O.window_softmax(q, k, v, W, scale)
+    m, _ = O.tc_scan(q, k, v, lam, eta, W)
+    y_off, _ = O.tc_fused(q, k, v, lam, eta, np.full(2, -1e4), W, scale)
+    np.testing.assert_array_equal(y_off, y_loc)  # sigmoid(-inf) -> pure sliding window
+    y_half, _ = O.tc_fused(q, k, v, lam, eta, np.zeros(2), W, scale)
+    np.testing.assert_allclose(y_half, y_loc + 0.5 * m, rtol=1e-14, atol=1e-15)
+
+
+def test_fused_rows_match_full():
+    q, k, v, lam, eta, g = rand_inputs(16, T=50)
+    W = 8
+    y, _ = O.tc_fused(q, k, v, lam, eta, g, W)
+    rows = [0, 7, 8, 9, 31, 49]
+    np.testing.assert_allclose(O.tc_fused_rows(q, k, v, lam, eta, g, W, rows), y[:, :, rows],
+                               rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- properties
+
+@settings(max_examples=40, deadline=None)
+@given(T=st.integers(1, 40), W=st.integers(1, 43), d=st.integers(1, 6),
+       lam_kind=st.sampled_from(["u", "0", "1"]), seed=st.integers(0, 10_000))
+def test_property_recurrence_equals_brute_force(T, W, d, lam_kind, seed):
+    q, k, v, lam, eta, _ = rand_inputs(seed, B=1, H=1, T=T, dk=d, dv=max(1, d - 1))
+    lam = {"u": lam, "0": np.zeros(1), "1": np.ones(1)}[lam_kind]
+    m, _ = O.tc_scan(q, k, v, lam, eta, W)
+    ref = brute_force_m(q, k, v, lam, eta, W)
+    assert np.max(np.abs(m - ref)) <= 1e-11 * max(1.0, np.max(np.abs(ref)))
+    mc, _ = O.tc_scan_chunked(q, k, v, lam, eta, W, C=4)
+    assert np.max(np.abs(mc - ref)) <= 1e-11 * max(1.0, np.max(np.abs(ref)))
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _mutant_off_by_one(q, k, v, lam, eta, W):
+    return O.tc_scan(q, k, v, lam, eta, W + 1)
+
+
+def _mutant_read_before_write(q, k, v, lam, eta, W):
+    qq = np.concatenate([q[:, :, 1:], q[:, :, :1]], axis=2)
+    m, A = O.tc_scan(qq, k, v, lam, eta, W)
+    out = np.zeros_like(m)
+    out[:, :, 1:] = m[:, :, :-1]
+    return out, A
+
+
+def _mutant_transposed(q, k, v, lam, eta, W):
+    return O.tc_scan(q, v, k, lam, eta, W)
+
+
+def _mutant_no_decay(q, k, v, lam, eta, W):
+    return O.tc_scan(q, k, v, np.ones_like(lam), eta, W)
+
+
+@pytest.mark.parametrize("mutant", [_mutant_off_by_one, _mutant_read_before_write, _mutant_transposed,
+                                    _mutant_no_decay])
+def test_brute_force_pin_catches_planted_mistakes(mutant):
+    # The brute-force pin must reject plausible slips (copies of the oracle with one
+    # planted mistake each).
+    q, k, v, lam, eta, _ = rand_inputs(17, B=1, H=2, T=20, dk=3, dv=3)
+    ref = brute_force_m(q, k, v, lam, eta, 4)
+    m, _ = mutant(q, k, v, lam, eta, 4)
+    assert np.max(np.abs(m - ref)) > 1e-6
