@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the Tensor Cache hot path on one MI355X.
+
+One step = one fused Tensor Cache layer (sliding-window softmax L1 + L2
+outer-product memory read + gate, which includes the eviction-conditioned
+writes and the chunked scan) over B=1, H=16, T=32768, d=128, W=1024 with
+bf16 inputs and fp32 state.  The other entry points (prefill scan, streaming
+decode, delta-rule scan) are timed on their own workloads and reported under
+"components".
+
+Prints ONE JSON line.  All inputs are synthetic and resident in HBM before
+the timed region; timing uses HIP events on the stream the library launches
+on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "memory-scan tokens/s (B·H·T/s) + % of MFMA or HBM roofline, d=128"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (matrix and vector)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["fused", "scan", "decode", "delta"], default=None,
+                    help="time a single entry point (for profiling runs)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+
+def fused_flops(B, H, T, d, W, C=64):
+    """L1: 4 d flops per (query, key) pair inside the window; L2 per active
+    token: (C+1)(dk+dv) for the intra-chunk part plus 4 dk dv for the state
+    read and write."""
+    pairs = sum(min(W, t + 1) for t in range(min(T, W))) + max(T - W, 0) * W
+    l1 = 4 * d * pairs
+    l2 = max(T - W, 0) * ((C + 1) * 2 * d + 4 * d * d)
+    return B * H * (l1 + l2)
+
+
+def fused_bytes(B, H, T, d):
+    return B * H * T * (3 * d * 2 + d * 4)  # q, k, v bf16 in, y fp32 out
+
+
+def scan_flops(B, H, T, d, W, C=64):
+    return B * H * max(T - W, 0) * ((C + 1) * 2 * d + 4 * d * d)
+
+
+def scan_bytes(B, H, T, d, in_bytes):
+    return B * H * T * (3 * d * in_bytes + d * 4)
+
+
+def decode_bytes_per_head(d, in_bytes=2):
+    # A read + written (fp32), q, k, v in, evicted pair read, new pair written, m out
+    return 2 * d * d * 4 + 3 * d * in_bytes + 2 * d * in_bytes + 2 * d * in_bytes + d * 4
+
+
+def delta_bytes(B, H, T, d, in_bytes=2):
+    return B * H * T * (3 * d * in_bytes + 4 + d * 4)
+
+
+def delta_flops(B, H, T, d):
+    return B * H * T * 6 * d * d  # prediction, write, read per token
+
+
+# ----------------------------------------------------------------------------- timing
+
+def time_calls(fn, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    t_end.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    total = t_start.elapsed_time(t_end)
+    return total / steps, sum(per) / len(per), per
+
+
+def roofline(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 5), "traffic": traffic}
+
+
+def to_dev_bf16(arr, dev):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def to_dev_f32(arr, dev):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def bench_fused(steps, warmup, dev):
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["fused_layer_bf16"]
+    x = I.draw_workload("fused_layer_bf16")
+    q, k, v = (to_dev_bf16(x[n], dev) for n in ("q", "k", "v"))
+    lam, eta, g = (to_dev_f32(x[n], dev) for n in ("lam", "eta", "g"))
+    y = torch.empty((w.B, w.H, w.T, w.d), dtype=torch.float32, device=dev)
+    A = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(ops.fused_workspace(w.B, w.H, w.T, w.d, w.d, w.W, 1), dtype=torch.uint8, device=dev)
+    lib = ops.lib()
+    st = ops._stream()
+    scale = 1.0 / math.sqrt(w.d)
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 1, ops._ptr(lam), ops._ptr(eta), ops._ptr(g),
+            w.B, w.H, w.T, w.d, w.d, w.W, 64, scale, ops._ptr(y), ops._ptr(A), ops._ptr(ws), ws.numel(), st)
+
+    def call(_):
+        s = lib.tc_fused_layer(*args)
+        if s != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, _ = time_calls(call, steps, warmup)
+    tokens = w.B * w.H * w.T
+    flops = fused_flops(w.B, w.H, w.T, w.d, w.W)
+    res = {
+        "workload": w.name, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+        "roofline": roofline("mfma", flops / (ms_call * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
+        "algorithmic_flops": flops, "algorithmic_bytes": fused_bytes(w.B, w.H, w.T, w.d),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "chunk": 64,
+                   "dtype_in": "bf16", "state": "fp32"},
+    }
+    return res, x
+
+
+def bench_scan(steps, warmup, dev):
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["prefill_scan_f32"]
+    x = I.draw_workload(w.name)
+    q, k, v = (to_dev_f32(x[n], dev) for n in ("q", "k", "v"))
+    lam, eta = to_dev_f32(x["lam"], dev), to_dev_f32(x["eta"], dev)
+    m = torch.empty((w.B, w.H, w.T, w.d), dtype=torch.float32, device=dev)
+    A = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev)
+    nb = ops.scan_workspace(w.B, w.H, w.T, w.d, w.d, w.W, 0)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    lib = ops.lib()
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, ops._ptr(lam), ops._ptr(eta), w.B, w.H, w.T, w.d,
+            w.d, w.W, 64, ops._ptr(m), ops._ptr(A), ops._ptr(ws), ws.numel(), ops._stream())
+
+    def call(_):
+        if lib.tc_scan_forward(*args) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, _ = time_calls(call, steps, warmup)
+    flops = scan_flops(w.B, w.H, w.T, w.d, w.W)
+    nbytes = scan_bytes(w.B, w.H, w.T, w.d, 4)
+    tf = flops / (ms_call * 1e-3) / 1e12
+    gbs = nbytes / (ms_call * 1e-3) / 1e9
+    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+            "roofline": roofline("mfma", tf, PEAK_FP32_TFLOPS, "TFLOP/s"),
+            "hbm": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
+
+
+def bench_decode(steps, warmup, dev, n_steps=4096):
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["decode_bf16"]
+    B, H, d, W = w.B, w.H, w.d, w.W
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+
+    n_steps = min(n_steps, w.steps)
+    scale = 1.0 / math.sqrt(d)
+    qs = (torch.randn((n_steps, B, H, d), generator=gen, device=dev) * scale).to(torch.bfloat16)
+    ks = unit(torch.randn((n_steps, B, H, d), generator=gen, device=dev)).to(torch.bfloat16)
+    vs = (torch.randn((n_steps, B, H, d), generator=gen, device=dev) * scale).to(torch.bfloat16)
+    ring_k = unit(torch.randn((B, H, W, d), generator=gen, device=dev)).to(torch.bfloat16)
+    ring_v = (torch.randn((B, H, W, d), generator=gen, device=dev) * scale).to(torch.bfloat16)
+    A = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+    sc = I.decode_scalars(H)
+    lam, eta = to_dev_f32(sc["lam"], dev), to_dev_f32(sc["eta"], dev)
+    pos = (W + torch.arange(n_steps + warmup, device=dev, dtype=torch.int64))[:, None].repeat(1, B).contiguous()
+    m = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    lib = ops.lib()
+    st = ops._stream()
+    P = ops._ptr
+    qp = [P(qs[i]) for i in range(n_steps)]
+    kp = [P(ks[i]) for i in range(n_steps)]
+    vp = [P(vs[i]) for i in range(n_steps)]
+    pp = [P(pos[i]) for i in range(n_steps + warmup)]
+    rk, rv, Ap, lp, ep, mp = P(ring_k), P(ring_v), P(A), P(lam), P(eta), P(m)
+    counter = {"i": 0}
+
+    def call(i):
+        j = counter["i"]
+        counter["i"] += 1
+        s = lib.tc_decode_step(qp[j % n_steps], kp[j % n_steps], vp[j % n_steps], 1, rk, rv, Ap, lp, ep,
+                               pp[j], B, H, d, d, W, mp, st)
+        if s != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    # warmup steps advance the stream position too; the timed steps continue from there
+    ms, ms_call, _ = time_calls(call, n_steps, warmup)
+    per_head = decode_bytes_per_head(d)
+    gbs = B * H * per_head / (ms_call * 1e-3) / 1e9
+    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": B * H / (ms * 1e-3),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
+            "note": "A (128 MiB) fits the 256 MB Infinity Cache; GB/s is algorithmic bytes / time",
+            "config": {"B": B, "H": H, "d": d, "W": W, "steps": n_steps, "dtype_in": "bf16"}}
+
+
+def bench_delta(steps, warmup, dev):
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["delta_scan_bf16"]
+    x = I.draw_workload(w.name)
+    q, k, v = (to_dev_bf16(x[n], dev) for n in ("q", "k", "v"))
+    beta = to_dev_f32(x["beta"], dev)
+    o = torch.empty((w.B, w.H, w.T, w.d), dtype=torch.float32, device=dev)
+    S = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev)
+    nb = ops.delta_workspace(w.B, w.H, w.T, w.d, w.d, 1)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    lib = ops.lib()
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 1, ops._ptr(beta), w.B, w.H, w.T, w.d, w.d, 64, None,
+            ops._ptr(o), ops._ptr(S), ops._ptr(ws), ws.numel(), ops._stream())
+
+    def call(_):
+        if lib.delta_scan_forward(*args) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, _ = time_calls(call, steps, warmup)
+    nbytes = delta_bytes(w.B, w.H, w.T, w.d)
+    gbs = nbytes / (ms_call * 1e-3) / 1e9
+    tf = delta_flops(w.B, w.H, w.T, w.d) / (ms_call * 1e-3) / 1e12
+    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
+            "mfma": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s"),
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "bf16"}}
+
+
+def cpu_baseline_fused(x, T_sample=4096):
+    """The float64 oracle on a bounded prefix of the same input."""
+    import numpy as np
+
+    from oracle import tc as O
+
+    w_W = 1024
+    sl = (slice(None), slice(None), slice(0, T_sample))
+    t0 = time.perf_counter()
+    O.tc_fused(x["q64"][sl], x["k64"][sl], x["v64"][sl], x["lam"].astype(np.float64), x["eta"],
+               x["g"].astype(np.float64), w_W)
+    dt = time.perf_counter() - t0
+    B, H = x["q64"].shape[:2]
+    return {"value": B * H * T_sample / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fused layer oracle (NumPy float64, single thread) on the first {T_sample} tokens "
+                      f"of all {B * H} heads of the same input ({dt:.1f} s; the first {w_W} tokens have "
+                      f"shorter windows)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    only = args.only
+    components = {}
+    if only in (None, "fused"):
+        head, x = bench_fused(args.steps, args.warmup, dev)
+    if only is None and not args.no_components:
+        components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
+        components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
+        components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
+    elif only == "scan":
+        components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
+    elif only == "decode":
+        components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
+    elif only == "delta":
+        components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
+    if only not in (None, "fused"):
+        print(json.dumps({"only": only, "components": components}))
+        return
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1/d) q,k,v with unit keys; per-head lam, eta, g)",
+        "config": head["config"],
+        "roofline": head["roofline"],
+    }
+    if components:
+        line["components"] = components
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_fused(x)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+/*
+ * tc.h — C ABI of libtc.so: the Tensor Cache outer-product memory and the
+ * delta-rule memory on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources: "Tensor Cache: Eviction-conditioned Associative Memory for
+ * Transformers" (Methodology 1: two-level architecture; Methodology 2:
+ * parallel weighted-sum scan) and "DeltaNet-family linear attention variants"
+ * (DeltaNet: writing the prediction error).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to caller-owned, contiguous,
+ *    row-major memory.  The library never allocates, frees or keeps a
+ *    pointer after the call returns; kernels run asynchronously on the
+ *    stream `s`, so the caller keeps every buffer alive until the stream has
+ *    reached the end of the call.
+ *  - q, k, v are [B, H, T, dk | dv] (or [B, H, dk | dv] for one decode step)
+ *    in the input dtype `dt`; per-head lam (decay), eta (write rate) and g
+ *    (gate logit) are float32 [H], shared across the batch; the L2 matrix A
+ *    is float32 [B, H, dk, dv]; the delta-rule state S is float32
+ *    [B, H, dv, dk].  Outputs are always float32.
+ *  - Supported shapes: dk == dv in {16, 32, 64, 128} (fused layer: {64, 128}),
+ *    chunk == 64, W >= 1, B, H, T >= 0.  B, H or T equal to 0 is a valid
+ *    empty call.  Anything else returns TC_ERR_UNSUPPORTED or
+ *    TC_ERR_INVALID_ARG.
+ *  - All argument checks run before any HIP call.  Values that live in
+ *    device memory (lam, eta, g, beta, pos) cannot be checked without a
+ *    synchronisation: lam and beta must lie in [0, 1] and pos must be >= 0;
+ *    the Python binding checks them.  Nothing throws across the ABI.
+ *  - On a non-OK status, tc_last_error() returns a message for the calling
+ *    thread; nothing has been launched unless the status is TC_ERR_HIP.
+ *  - Calls are stream-ordered and keep no state between calls; two calls
+ *    that write the same buffers must not overlap.
+ */
+#ifndef TC_H_
+#define TC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TC_OK = 0,
+  TC_ERR_INVALID_ARG = 1, /* null pointer, negative size, W < 1, ...          */
+  TC_ERR_UNSUPPORTED = 2, /* valid but not implemented: d, chunk, dtype        */
+  TC_ERR_WORKSPACE = 3,   /* ws_bytes smaller than the *_workspace_bytes query */
+  TC_ERR_HIP = 4,         /* a HIP launch failed; message holds the HIP error  */
+  TC_ERR_INTERNAL = 5
+} tc_status;
+
+typedef enum { TC_F32 = 0, TC_BF16 = 1 } tc_dtype; /* input dtype of q, k, v (and the ring) */
+
+/* ---------------------------------------------------------------------------
+ * Prefill scan of the L2 memory (Tensor Cache, Methodology 1 write/read and
+ * Methodology 2 parallel scan).
+ *
+ * Starting from an empty ring and A = 0, at every step t >= W the token t-W
+ * leaves the W-token window and is written, A <- lam[h] A + eta[h] k_{t-W} v_{t-W}^T;
+ * then the query reads m_t = q_t A.  Equivalently
+ *     m_t = sum_{i <= t-W} eta lam^((t-W)-i) <q_t, k_i> v_i,
+ * evaluated in chunks of `chunk` positions, equal to the sequential writes up
+ * to rounding.
+ *   m        out [B, H, T, dv] float32; rows t < W are written as 0.
+ *   A_final  out [B, H, dk, dv] float32 (A after the last write) or NULL.
+ *            The final ring is k, v[max(0, T-W) : T] (slot t mod W), which
+ *            the caller slices itself.
+ *   ws       device workspace of at least tc_scan_workspace_bytes(...) bytes
+ *            (may be NULL when that is 0).
+ * ------------------------------------------------------------------------- */
+size_t tc_scan_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt);
+tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype dt,
+                          const float* lam, const float* eta,
+                          int B, int H, int T, int dk, int dv, int W, int chunk,
+                          float* m, float* A_final, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
+ * One streaming step of the two-level cache (Tensor Cache, Methodology 1).
+ *
+ * For every sequence b and head h, with p = pos[b] (tokens already seen):
+ *   1. if p >= W, the ring slot p mod W is occupied: its pair (k_e, v_e)
+ *      is written into A: A <- lam[h] A + eta[h] k_e v_e^T;
+ *   2. the new (k, v) is stored in slot p mod W;
+ *   3. m = q A (after the write).
+ *   q, k [B, H, dk], v [B, H, dv] in dtype dt; ring_k, ring_v in/out
+ *   [B, H, W, dk | dv] in dtype dt; A in/out float32 [B, H, dk, dv];
+ *   pos [B] int64 >= 0 (the caller advances it after the call);
+ *   m out float32 [B, H, dv].  No workspace.
+ * ------------------------------------------------------------------------- */
+tc_status tc_decode_step(const void* q, const void* k, const void* v, tc_dtype dt,
+                         void* ring_k, void* ring_v, float* A,
+                         const float* lam, const float* eta, const int64_t* pos,
+                         int B, int H, int dk, int dv, int W, float* m, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
+ * Fused Tensor Cache layer (Tensor Cache, Methodology 1: L1 exact softmax
+ * over the ring, L2 read, gated fusion).
+ *
+ *   y_t = sum_{j = max(0,t-W+1)}^{t} softmax_j(softmax_scale <q_t, k_j>) v_j
+ *         + sigmoid(g[h]) m_t,
+ * with m_t the L2 read of tc_scan_forward.  The L1 window holds the W most
+ * recent tokens including token t; a token leaves the window exactly when
+ * it is written into A, so each token is counted once.
+ *   y        out [B, H, T, dv] float32.
+ *   A_final  out [B, H, dk, dv] float32 or NULL.
+ *   ws       at least tc_fused_workspace_bytes(...) bytes.
+ * ------------------------------------------------------------------------- */
+size_t tc_fused_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt);
+tc_status tc_fused_layer(const void* q, const void* k, const void* v, tc_dtype dt,
+                         const float* lam, const float* eta, const float* g,
+                         int B, int H, int T, int dk, int dv, int W, int chunk,
+                         float softmax_scale, float* y, float* A_final,
+                         void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
+ * Delta-rule scan (DeltaNet-family linear attention variants: DeltaNet
+ * writes the prediction error).
+ *
+ *   e_t = beta_t (v_t - S_{t-1} k_t),  S_t = S_{t-1} + e_t k_t^T,  o_t = S_t q_t,
+ * with S [dv, dk] starting from S0 (or zeros), evaluated in chunks of
+ * `chunk` tokens (equal to the per-token rule up to rounding).
+ *   beta     [B, H, T] float32 in [0, 1].
+ *   S0       in [B, H, dv, dk] float32 or NULL for zeros.
+ *   o        out [B, H, T, dv] float32.
+ *   S_final  out [B, H, dv, dk] float32 or NULL.
+ *   ws       at least delta_scan_workspace_bytes(...) bytes.
+ * ------------------------------------------------------------------------- */
+size_t delta_scan_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt);
+tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dtype dt,
+                             const float* beta, int B, int H, int T, int dk, int dv, int chunk,
+                             const float* S0, float* o, float* S_final,
+                             void* ws, size_t ws_bytes, hipStream_t s);
+
+/* Workspace queries return SIZE_MAX when the arguments are invalid or
+ * unsupported (tc_last_error() says why). */
+
+const char* tc_last_error(void); /* thread-local; "" when the last call was OK */
+const char* tc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TC_H_ */

@@ -1,0 +1,202 @@
+// tc_api.cpp — C ABI of libtc.so: argument checks, workspace sizing,
+// dispatch to the gfx950 kernels, thread-local error messages.
+//
+// Every check runs before the first HIP call, so a rejected call launches
+// nothing and needs no device.  Nothing throws across the ABI.
+#include "../../include/tc.h"
+#include "tc_kernels.hpp"
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <exception>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tc_status fail(tc_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+tc_status ok() {
+  g_err[0] = '\0';
+  return TC_OK;
+}
+
+tc_status from_hip(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(TC_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Checks shared by the sequence entry points.  Returns TC_OK when the shapes
+// are valid and supported.
+tc_status check_seq(const char* fn, int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt) {
+  if (B < 0 || H < 0 || T < 0) return fail(TC_ERR_INVALID_ARG, "%s: B, H, T must be >= 0 (got %d, %d, %d)", fn, B, H, T);
+  if (dk <= 0 || dv <= 0) return fail(TC_ERR_INVALID_ARG, "%s: dk, dv must be > 0 (got %d, %d)", fn, dk, dv);
+  if (dt != TC_F32 && dt != TC_BF16) return fail(TC_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  if (chunk != 64) return fail(TC_ERR_UNSUPPORTED, "%s: chunk must be 64 (got %d)", fn, chunk);
+  if (dk != dv || !supported_d(dk))
+    return fail(TC_ERR_UNSUPPORTED, "%s: need dk == dv in {16, 32, 64, 128} (got %d, %d)", fn, dk, dv);
+  // indices are formed in 64-bit, but one (b, h) row block must stay addressable in 32 bits
+  if ((long long)T * dk >= (1LL << 31)) return fail(TC_ERR_UNSUPPORTED, "%s: T * d too large", fn);
+  if ((long long)B * H >= 65536) return fail(TC_ERR_UNSUPPORTED, "%s: B * H must be < 65536", fn);
+  return TC_OK;
+}
+
+template <typename F>
+tc_status guarded(const char* fn, F&& f) {
+  try {
+    return f();
+  } catch (const std::exception& e) {
+    return fail(TC_ERR_INTERNAL, "%s: %s", fn, e.what());
+  } catch (...) {
+    return fail(TC_ERR_INTERNAL, "%s: unknown exception", fn);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tc_last_error(void) { return g_err; }
+
+const char* tc_version(void) { return "libtc 0.1.0 (gfx950)"; }
+
+size_t tc_scan_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt) {
+  if (check_seq("tc_scan_workspace_bytes", B, H, T, dk, dv, chunk, dt) != TC_OK) return SIZE_MAX;
+  if (W < 1) {
+    fail(TC_ERR_INVALID_ARG, "tc_scan_workspace_bytes: W must be >= 1 (got %d)", W);
+    return SIZE_MAX;
+  }
+  ok();
+  return tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
+}
+
+tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype dt,
+                          const float* lam, const float* eta, int B, int H, int T, int dk, int dv,
+                          int W, int chunk, float* m, float* A_final, void* ws, size_t ws_bytes,
+                          hipStream_t s) {
+  return guarded("tc_scan_forward", [&]() -> tc_status {
+    const char* fn = "tc_scan_forward";
+    tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
+    if (st != TC_OK) return st;
+    if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+    if (B == 0 || H == 0) return ok();
+    if (!lam || !eta) return fail(TC_ERR_INVALID_ARG, "%s: lam and eta must not be NULL", fn);
+    if (T > 0 && (!q || !k || !v || !m))
+      return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, m must not be NULL", fn);
+    const size_t need = tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
+    if (ws_bytes < need)
+      return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
+    if (T == 0 && !A_final) return ok();
+    return from_hip(tc::launch_tc_scan(q, k, v, dt == TC_BF16, lam, eta, B, H, T, dk, dv, W, m,
+                                       A_final, ws, s),
+                    fn);
+  });
+}
+
+tc_status tc_decode_step(const void* q, const void* k, const void* v, tc_dtype dt, void* ring_k,
+                         void* ring_v, float* A, const float* lam, const float* eta,
+                         const int64_t* pos, int B, int H, int dk, int dv, int W, float* m,
+                         hipStream_t s) {
+  return guarded("tc_decode_step", [&]() -> tc_status {
+    const char* fn = "tc_decode_step";
+    tc_status st = check_seq(fn, B, H, 1, dk, dv, 64, dt);
+    if (st != TC_OK) return st;
+    if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+    if ((long long)W * dk >= (1LL << 31)) return fail(TC_ERR_UNSUPPORTED, "%s: W * d too large", fn);
+    if (B == 0 || H == 0) return ok();
+    if (!q || !k || !v || !ring_k || !ring_v || !A || !lam || !eta || !pos || !m)
+      return fail(TC_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    return from_hip(tc::launch_tc_decode(q, k, v, dt == TC_BF16, ring_k, ring_v, A, lam, eta, pos,
+                                         B, H, dk, dv, W, m, s),
+                    fn);
+  });
+}
+
+size_t tc_fused_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt) {
+  const char* fn = "tc_fused_workspace_bytes";
+  if (check_seq(fn, B, H, T, dk, dv, chunk, dt) != TC_OK) return SIZE_MAX;
+  if (W < 1) {
+    fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+    return SIZE_MAX;
+  }
+  if (dt != TC_BF16 || (dk != 64 && dk != 128)) {
+    fail(TC_ERR_UNSUPPORTED, "%s: the fused layer takes bf16 inputs with d in {64, 128}", fn);
+    return SIZE_MAX;
+  }
+  ok();
+  return tc::fused_ws_bytes(B, H, T, dk, dv, W);
+}
+
+tc_status tc_fused_layer(const void* q, const void* k, const void* v, tc_dtype dt,
+                         const float* lam, const float* eta, const float* g, int B, int H, int T,
+                         int dk, int dv, int W, int chunk, float softmax_scale, float* y,
+                         float* A_final, void* ws, size_t ws_bytes, hipStream_t s) {
+  return guarded("tc_fused_layer", [&]() -> tc_status {
+    const char* fn = "tc_fused_layer";
+    tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
+    if (st != TC_OK) return st;
+    if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+    if (dt != TC_BF16 || (dk != 64 && dk != 128))
+      return fail(TC_ERR_UNSUPPORTED, "%s: the fused layer takes bf16 inputs with d in {64, 128}", fn);
+    if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
+      return fail(TC_ERR_INVALID_ARG, "%s: softmax_scale must be finite and > 0", fn);
+    if (B == 0 || H == 0) return ok();
+    if (!lam || !eta || !g) return fail(TC_ERR_INVALID_ARG, "%s: lam, eta, g must not be NULL", fn);
+    if (T > 0 && (!q || !k || !v || !y))
+      return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, y must not be NULL", fn);
+    const size_t need = tc::fused_ws_bytes(B, H, T, dk, dv, W);
+    if (ws_bytes < need)
+      return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
+    if (T == 0) {
+      if (!A_final) return ok();
+      return from_hip(tc::launch_tc_scan(q, k, v, true, lam, eta, B, H, 0, dk, dv, W, y, A_final,
+                                         ws, s),
+                      fn);
+    }
+    return from_hip(tc::launch_tc_fused(q, k, v, lam, eta, g, B, H, T, dk, W, softmax_scale, y,
+                                        A_final, ws, s),
+                    fn);
+  });
+}
+
+size_t delta_scan_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt) {
+  if (check_seq("delta_scan_workspace_bytes", B, H, T, dk, dv, chunk, dt) != TC_OK) return SIZE_MAX;
+  ok();
+  return tc::delta_ws_bytes(B, H, T, dk, dv);
+}
+
+tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dtype dt,
+                             const float* beta, int B, int H, int T, int dk, int dv, int chunk,
+                             const float* S0, float* o, float* S_final, void* ws, size_t ws_bytes,
+                             hipStream_t s) {
+  return guarded("delta_scan_forward", [&]() -> tc_status {
+    const char* fn = "delta_scan_forward";
+    tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
+    if (st != TC_OK) return st;
+    if (B == 0 || H == 0) return ok();
+    if (T > 0 && (!q || !k || !v || !beta || !o))
+      return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, beta, o must not be NULL", fn);
+    const size_t need = tc::delta_ws_bytes(B, H, T, dk, dv);
+    if (ws_bytes < need)
+      return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
+    if (T == 0 && !S_final) return ok();
+    return from_hip(tc::launch_delta_scan(q, k, v, dt == TC_BF16, beta, B, H, T, dk, dv, S0, o,
+                                          S_final, ws, s),
+                    fn);
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// tc_common.hpp — device helpers shared by the gfx950 kernels of libtc.so.
+//
+// MFMA operand layouts used throughout (64-lane wavefront, lane = l):
+//   v_mfma_f32_16x16x4_f32   A(m,k): lane m + 16k holds A[m][k]      (k < 4)
+//                            B(k,n): lane n + 16k holds B[k][n]
+//   v_mfma_f32_16x16x32_bf16 A(m,k): lane m + 16*(k/8) slot k%8       (k < 32)
+//                            B(k,n): lane n + 16*(k/8) slot k%8
+//   both                     D(m,n): lane n + 16*(m/4) element m%4
+// Only the M/N placement matters for correctness: any permutation of K is
+// harmless as long as A and B use the same one, which the kernels rely on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tc {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// bfloat16 stored as raw 16-bit patterns (uint16_t) in memory.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round-to-nearest-even float -> bfloat16 bits (inputs here are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct InT;
+template <> struct InT<float> {
+  __device__ __forceinline__ static float ld(const float* p, long i) { return p[i]; }
+};
+template <> struct InT<uint16_t> {
+  __device__ __forceinline__ static float ld(const uint16_t* p, long i) { return bf16_to_f32(p[i]); }
+};
+
+// lam ** e for an integer e >= 0, with 0 ** 0 = 1 and 1 ** e = 1 exactly.
+__device__ __forceinline__ float pow_int(float lam, int e) {
+  if (e == 0) return 1.0f;
+  if (lam == 0.0f) return 0.0f;
+  if (lam == 1.0f) return 1.0f;
+  return exp2f(static_cast<float>(e) * log2f(lam));
+}
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One wave accumulates a 16x16 fp32 tile: C += A[16 x K] * B[K x 16] with
+// both operands in LDS, addressed through element strides so that either
+// operand can be read transposed.  A(m,k) = pa[m*am + k*ak],
+// B(k,n) = pb[k*bk + n*bn].
+template <int K>
+__device__ __forceinline__ floatx4 wave_mma_f32(const float* pa, int am, int ak,
+                                                const float* pb, int bk, int bn, floatx4 c) {
+  const int l = lane_id();
+  const int r = l & 15, kk = l >> 4;
+  const float* a = pa + r * am + kk * ak;
+  const float* b = pb + kk * bk + r * bn;
+#pragma unroll 8
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    c = mfma4(a[k0 * ak], b[k0 * bk], c);
+  }
+  return c;
+}
+
+__device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace tc

@@ -1,0 +1,44 @@
+// tc_kernels.hpp — host-side launchers implemented in the .hip files.
+// Argument checking happens in tc_api.cpp before any of these is called;
+// every launcher returns the hipError_t of its last launch.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tc {
+
+// Segmenting of the prefill scan: the active positions s = t - W in [0, T-W)
+// are split into chunks of 64 and the chunks into segments of `seg_chunks`;
+// one workgroup carries the state through one segment.
+struct ScanPlan {
+  int n_act;       // T - W (>= 0)
+  int n_chunks;    // ceil(n_act / 64)
+  int seg_chunks;  // chunks per segment
+  int n_seg;       // segments per (b, h)
+  int dvt;         // width of the d_v tile one workgroup owns
+};
+ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int W);
+size_t scan_ws_bytes(const ScanPlan& p, int B, int H, int dk, int dv);
+
+hipError_t launch_tc_scan(const void* q, const void* k, const void* v, bool bf16,
+                          const float* lam, const float* eta, int B, int H, int T, int dk, int dv,
+                          int W, float* m, float* A_final, void* ws, hipStream_t s);
+
+hipError_t launch_tc_decode(const void* q, const void* k, const void* v, bool bf16, void* ring_k,
+                            void* ring_v, float* A, const float* lam, const float* eta,
+                            const int64_t* pos, int B, int H, int dk, int dv, int W, float* m,
+                            hipStream_t s);
+
+size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W);
+hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const float* lam,
+                           const float* eta, const float* g, int B, int H, int T, int d, int W,
+                           float scale, float* y, float* A_final, void* ws, hipStream_t s);
+
+size_t delta_ws_bytes(int B, int H, int T, int dk, int dv);
+hipError_t launch_delta_scan(const void* q, const void* k, const void* v, bool bf16,
+                             const float* beta, int B, int H, int T, int dk, int dv,
+                             const float* S0, float* o, float* S_final, void* ws, hipStream_t s);
+
+}  // namespace tc

@@ -31,6 +31,9 @@ __all__ = [
     "round_to_dtype",
     "draw",
     "draw_decode_position",
+    "decode_scalars",
+    "draw_ring",
+    "storage_to_f64",
 ]
 
 
@@ -173,3 +176,24 @@ def decode_scalars(H: int, *, seed: int = 104, lam=("uniform", 0.95, 0.999),
     rng = np.random.Generator(np.random.PCG64([seed, 1 << 40]))
     return {"lam": _draw_scalar(rng, lam, H).astype(np.float32),
             "eta": _draw_scalar(rng, eta, H).astype(np.float32)}
+
+
+def draw_ring(B: int, H: int, W: int, d: int, *, seed: int = 104, dtype: str = "bf16"):
+    """A full W-slot ring of keys and values (one generator per sequence b).
+
+    Slot i holds the token at position i, so with pos = W every slot is
+    occupied and the next step evicts slot 0.  Returns the storage arrays
+    (ring_k, ring_v) [B, H, W, d]; ``storage_to_f64`` gives their values.
+    """
+    ks, vs = [], []
+    for b in range(B):
+        rng = np.random.Generator(np.random.PCG64([seed, 1 << 41, b]))
+        k = _unit_rows(rng.standard_normal((H, W, d)) / np.sqrt(d))
+        v = rng.standard_normal((H, W, d)) / np.sqrt(d)
+        ks.append(round_to_dtype(k, dtype)[0])
+        vs.append(round_to_dtype(v, dtype)[0])
+    return np.stack(ks), np.stack(vs)
+
+
+def storage_to_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits_to_f64(arr) if dtype == "bf16" else np.asarray(arr, np.float64)

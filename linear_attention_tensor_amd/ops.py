@@ -1,0 +1,204 @@
+"""Torch-facing binding of libtc.so with the names of the C entry points.
+
+Argument marshalling only: shape/dtype/contiguity checks, output and
+workspace allocation through torch, ``data_ptr()`` and the current HIP stream
+handed to the C ABI.  Every step of the computation runs in the library's
+kernels; there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import TC_BF16, TC_F32, check, lib
+
+__all__ = ["tc_scan_forward", "tc_decode_step", "tc_fused_layer", "delta_scan_forward",
+           "scan_workspace", "fused_workspace", "delta_workspace"]
+
+CHUNK = 64
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TC_F32
+    if t.dtype == torch.bfloat16:
+        return TC_BF16
+    raise TypeError(f"inputs must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(name: str, t: torch.Tensor, shape, dtype=None, device=None) -> None:
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.is_cuda, f"{name} must be a GPU tensor")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None:
+        _need(t.device == device, f"{name} is on {t.device}, expected {device}")
+
+
+def _check_unit_interval(name: str, t: torch.Tensor) -> None:
+    if t.numel() and (bool((t < 0).any()) or bool((t > 1).any()) or bool(torch.isnan(t).any())):
+        raise ValueError(f"{name} must lie in [0, 1]")
+
+
+def _qkv(q, k, v):
+    _need(q.dim() == 4, "q must be [B, H, T, dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for n, t, s in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv))):
+        _check_tensor(n, t, s, q.dtype, q.device)
+    return B, H, T, dk, dv, dt
+
+
+def scan_workspace(B, H, T, dk, dv, W, dtype_code) -> int:
+    n = lib().tc_scan_workspace_bytes(B, H, T, dk, dv, W, CHUNK, dtype_code)
+    if n == _lib.SIZE_MAX:
+        raise _lib.TCError("tc_scan_workspace_bytes", _lib.TC_ERR_INVALID_ARG, _lib.last_error())
+    return n
+
+
+def fused_workspace(B, H, T, dk, dv, W, dtype_code) -> int:
+    n = lib().tc_fused_workspace_bytes(B, H, T, dk, dv, W, CHUNK, dtype_code)
+    if n == _lib.SIZE_MAX:
+        raise _lib.TCError("tc_fused_workspace_bytes", _lib.TC_ERR_UNSUPPORTED, _lib.last_error())
+    return n
+
+
+def delta_workspace(B, H, T, dk, dv, dtype_code) -> int:
+    n = lib().delta_scan_workspace_bytes(B, H, T, dk, dv, CHUNK, dtype_code)
+    if n == _lib.SIZE_MAX:
+        raise _lib.TCError("delta_scan_workspace_bytes", _lib.TC_ERR_INVALID_ARG, _lib.last_error())
+    return n
+
+
+def _ws(nbytes: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes > 0 else None
+
+
+def tc_scan_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torch.Tensor,
+                    eta: torch.Tensor, W: int, *, return_state: bool = True,
+                    check_values: bool = True, m: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """L2 memory read m [B,H,T,dv] (fp32) and the final state A [B,H,dk,dv]."""
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    _check_tensor("lam", lam, (H,), torch.float32, q.device)
+    _check_tensor("eta", eta, (H,), torch.float32, q.device)
+    if check_values:
+        _check_unit_interval("lam", lam)
+    if m is None:
+        m = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    else:
+        _check_tensor("m", m, (B, H, T, dv), torch.float32, q.device)
+    A = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if return_state else None
+    need = scan_workspace(B, H, T, dk, dv, W, dt)
+    if ws is None:
+        ws = _ws(need, q.device)
+    st = lib().tc_scan_forward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(lam), _ptr(eta), B, H, T, dk, dv,
+                               W, CHUNK, _ptr(m), _ptr(A), _ptr(ws), ws.numel() if ws is not None else 0,
+                               _stream())
+    check("tc_scan_forward", st)
+    return m, A
+
+
+def tc_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_k: torch.Tensor,
+                   ring_v: torch.Tensor, A: torch.Tensor, lam: torch.Tensor, eta: torch.Tensor,
+                   pos: torch.Tensor, W: int, *, m: Optional[torch.Tensor] = None,
+                   check_values: bool = True) -> torch.Tensor:
+    """One streaming step; updates ring_k, ring_v and A in place, returns m [B,H,dv].
+
+    The caller advances ``pos`` (tokens already seen per sequence) afterwards.
+    """
+    _need(q.dim() == 3, "q must be [B, H, dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for n, t, s in (("q", q, (B, H, dk)), ("k", k, (B, H, dk)), ("v", v, (B, H, dv)),
+                    ("ring_k", ring_k, (B, H, W, dk)), ("ring_v", ring_v, (B, H, W, dv))):
+        _check_tensor(n, t, s, q.dtype, q.device)
+    _check_tensor("A", A, (B, H, dk, dv), torch.float32, q.device)
+    _check_tensor("lam", lam, (H,), torch.float32, q.device)
+    _check_tensor("eta", eta, (H,), torch.float32, q.device)
+    _check_tensor("pos", pos, (B,), torch.int64, q.device)
+    if check_values:
+        _check_unit_interval("lam", lam)
+        if pos.numel() and bool((pos < 0).any()):
+            raise ValueError("pos must be >= 0")
+    if m is None:
+        m = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    else:
+        _check_tensor("m", m, (B, H, dv), torch.float32, q.device)
+    st = lib().tc_decode_step(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(ring_k), _ptr(ring_v), _ptr(A),
+                              _ptr(lam), _ptr(eta), _ptr(pos), B, H, dk, dv, W, _ptr(m), _stream())
+    check("tc_decode_step", st)
+    return m
+
+
+def tc_fused_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torch.Tensor,
+                   eta: torch.Tensor, g: torch.Tensor, W: int, *, softmax_scale: Optional[float] = None,
+                   return_state: bool = False, check_values: bool = True,
+                   y: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """y = sliding-window softmax attention + sigmoid(g) * L2 read; optionally A_final."""
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    for n, t in (("lam", lam), ("eta", eta), ("g", g)):
+        _check_tensor(n, t, (H,), torch.float32, q.device)
+    if check_values:
+        _check_unit_interval("lam", lam)
+    scale = 1.0 / math.sqrt(dk) if softmax_scale is None else float(softmax_scale)
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    else:
+        _check_tensor("y", y, (B, H, T, dv), torch.float32, q.device)
+    A = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if return_state else None
+    need = fused_workspace(B, H, T, dk, dv, W, dt)
+    if ws is None:
+        ws = _ws(need, q.device)
+    st = lib().tc_fused_layer(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(lam), _ptr(eta), _ptr(g), B, H, T,
+                              dk, dv, W, CHUNK, scale, _ptr(y), _ptr(A), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _stream())
+    check("tc_fused_layer", st)
+    return (y, A) if return_state else y
+
+
+def delta_scan_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor, *,
+                       S0: Optional[torch.Tensor] = None, return_state: bool = False,
+                       check_values: bool = True, o: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None):
+    """Delta-rule outputs o [B,H,T,dv] (fp32); optionally S_final [B,H,dv,dk]."""
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    _check_tensor("beta", beta, (B, H, T), torch.float32, q.device)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dv, dk), torch.float32, q.device)
+    if check_values:
+        _check_unit_interval("beta", beta)
+    if o is None:
+        o = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    else:
+        _check_tensor("o", o, (B, H, T, dv), torch.float32, q.device)
+    S = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device) if return_state else None
+    need = delta_workspace(B, H, T, dk, dv, dt)
+    if ws is None:
+        ws = _ws(need, q.device)
+    st = lib().delta_scan_forward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(beta), B, H, T, dk, dv, CHUNK,
+                                  _ptr(S0), _ptr(o), _ptr(S), _ptr(ws), ws.numel() if ws is not None else 0,
+                                  _stream())
+    check("delta_scan_forward", st)
+    return (o, S) if return_state else o

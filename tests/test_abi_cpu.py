@@ -1,0 +1,133 @@
+"""The C ABI without a GPU: library loads, every declared symbol is exported,
+and invalid or unsupported arguments are rejected before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_tensor_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tc.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libtc.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("tc_scan_forward", "tc_decode_step", "tc_fused_layer", "delta_scan_forward",
+              "tc_scan_workspace_bytes", "tc_fused_workspace_bytes", "delta_scan_workspace_bytes",
+              "tc_last_error", "tc_version"):
+        assert n in names
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_every_declared_symbol_is_exported():
+    L = ctypes.CDLL(_lib.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_version():
+    assert _lib.lib().tc_version().decode().startswith("libtc")
+
+
+L = None
+
+
+def lib():
+    return _lib.lib()
+
+
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is rejected first
+
+
+def scan(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dt=_lib.TC_F32, lam=FAKE, eta=FAKE, B=1, H=1, T=128, dk=64, dv=64,
+             W=16, chunk=64, m=FAKE, A=NULL, ws=NULL, ws_bytes=0)
+    a.update(kw)
+    return lib().tc_scan_forward(a["q"], a["k"], a["v"], a["dt"], a["lam"], a["eta"], a["B"], a["H"],
+                                 a["T"], a["dk"], a["dv"], a["W"], a["chunk"], a["m"], a["A"], a["ws"],
+                                 a["ws_bytes"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk=32), _lib.TC_ERR_UNSUPPORTED),
+    (dict(dk=48, dv=48), _lib.TC_ERR_UNSUPPORTED),
+    (dict(dk=64, dv=32), _lib.TC_ERR_UNSUPPORTED),
+    (dict(B=-1), _lib.TC_ERR_INVALID_ARG),
+    (dict(T=-5), _lib.TC_ERR_INVALID_ARG),
+    (dict(W=0), _lib.TC_ERR_INVALID_ARG),
+    (dict(dt=7), _lib.TC_ERR_INVALID_ARG),
+    (dict(q=NULL), _lib.TC_ERR_INVALID_ARG),
+    (dict(lam=NULL), _lib.TC_ERR_INVALID_ARG),
+    (dict(m=NULL), _lib.TC_ERR_INVALID_ARG),
+])
+def test_scan_rejects(kw, status):
+    assert scan(**kw) == status
+    assert _lib.last_error() != ""
+
+
+def test_scan_empty_is_ok_without_device():
+    assert scan(B=0) == _lib.TC_OK
+    assert scan(H=0, q=NULL) == _lib.TC_OK
+    assert _lib.last_error() == ""
+
+
+def test_scan_workspace_check():
+    need = lib().tc_scan_workspace_bytes(4, 8, 4096, 64, 64, 512, 64, _lib.TC_F32)
+    assert 0 < need < _lib.SIZE_MAX
+    assert scan(B=4, H=8, T=4096, W=512, ws=FAKE, ws_bytes=need - 1) == _lib.TC_ERR_WORKSPACE
+    assert lib().tc_scan_workspace_bytes(1, 1, 10, 64, 64, 0, 64, _lib.TC_F32) == _lib.SIZE_MAX
+
+
+def test_decode_rejects():
+    f = lib().tc_decode_step
+    args = [FAKE, FAKE, FAKE, _lib.TC_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 128, 16, FAKE, NULL]
+    bad = list(args); bad[14] = 0
+    assert f(*bad) == _lib.TC_ERR_INVALID_ARG
+    bad = list(args); bad[12] = 100; bad[13] = 100
+    assert f(*bad) == _lib.TC_ERR_UNSUPPORTED
+    bad = list(args); bad[9] = NULL
+    assert f(*bad) == _lib.TC_ERR_INVALID_ARG
+    ok = list(args); ok[10] = 0
+    assert f(*ok) == _lib.TC_OK
+
+
+def test_fused_rejects():
+    f = lib().tc_fused_layer
+
+    def call(dt=_lib.TC_BF16, d=128, scale=0.1, ws_bytes=0, W=64, T=256):
+        return f(FAKE, FAKE, FAKE, dt, FAKE, FAKE, FAKE, 1, 2, T, d, d, W, 64, scale, FAKE, NULL, FAKE,
+                 ws_bytes, NULL)
+
+    assert call(dt=_lib.TC_F32) == _lib.TC_ERR_UNSUPPORTED
+    assert call(d=32) == _lib.TC_ERR_UNSUPPORTED
+    assert call(scale=0.0) == _lib.TC_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == _lib.TC_ERR_INVALID_ARG
+    assert call(ws_bytes=0) == _lib.TC_ERR_WORKSPACE
+    assert lib().tc_fused_workspace_bytes(1, 2, 256, 128, 128, 64, 64, _lib.TC_F32) == _lib.SIZE_MAX
+
+
+def test_delta_rejects():
+    f = lib().delta_scan_forward
+
+    def call(**kw):
+        a = dict(dt=_lib.TC_BF16, beta=FAKE, B=1, H=1, T=64, d=64, chunk=64)
+        a.update(kw)
+        return f(FAKE, FAKE, FAKE, a["dt"], a["beta"], a["B"], a["H"], a["T"], a["d"], a["d"], a["chunk"],
+                 NULL, FAKE, NULL, NULL, 0, NULL)
+
+    assert call(chunk=128) == _lib.TC_ERR_UNSUPPORTED
+    assert call(beta=NULL) == _lib.TC_ERR_INVALID_ARG
+    assert call(d=24) == _lib.TC_ERR_UNSUPPORTED
+    assert call(B=0) == _lib.TC_OK
