@@ -30,9 +30,13 @@ __device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-__device__ __forceinline__ __bf16 to_bf16(float f) {
-  const uint16_t b = f32_to_bf16(f);
-  return __builtin_bit_cast(__bf16, b);
+// Eight probabilities (two 4-element score fragments) as one bf16x8 MFMA
+// operand.  The vector is assembled in 32-bit integer lanes and bit-cast as a
+// whole: element-wise insertion into bf16 vectors is avoided.
+__device__ __forceinline__ bf16x8 pack_bf16x8(floatx4 lo, floatx4 hi) {
+  const u32x4 w{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                pack_bf16x2(hi[2], hi[3])};
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 template <int D>
@@ -62,8 +66,7 @@ __global__ __launch_bounds__(256) void swa_kernel(const uint16_t* __restrict__ q
     if (tq < T) {
       qreg[ks] = ld_bf16x8(q + (base + tq) * D + 32 * ks + 8 * g4);
     } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qreg[ks][j] = to_bf16(0.f);
+      qreg[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
   }
 
@@ -79,20 +82,18 @@ __global__ __launch_bounds__(256) void swa_kernel(const uint16_t* __restrict__ q
     // stage K rows kb..kb+63 (row-major) and V (transposed), zero past T
     for (int idx = threadIdx.x; idx < KB * (D / 8); idx += 256) {
       const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-      bf16x8 kx, vx;
+      uint4 kx = make_uint4(0u, 0u, 0u, 0u), vx = make_uint4(0u, 0u, 0u, 0u);
       if (kb + r < T) {
-        kx = ld_bf16x8(k + (base + kb + r) * D + c8);
-        vx = ld_bf16x8(v + (base + kb + r) * D + c8);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          kx[j] = to_bf16(0.f);
-          vx[j] = to_bf16(0.f);
-        }
+        kx = *reinterpret_cast<const uint4*>(k + (base + kb + r) * D + c8);
+        vx = *reinterpret_cast<const uint4*>(v + (base + kb + r) * D + c8);
       }
-      *reinterpret_cast<bf16x8*>(sK + r * SK + c8) = kx;
+      *reinterpret_cast<uint4*>(sK + r * SK + c8) = kx;
+      const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sVt[(c8 + j) * SVT + r] = __builtin_bit_cast(uint16_t, vx[j]);
+      for (int j = 0; j < 4; ++j) {
+        sVt[(c8 + 2 * j) * SVT + r] = static_cast<uint16_t>(vw[j] & 0xFFFFu);
+        sVt[(c8 + 2 * j + 1) * SVT + r] = static_cast<uint16_t>(vw[j] >> 16);
+      }
     }
     __syncthreads();
 
@@ -141,26 +142,13 @@ __global__ __launch_bounds__(256) void swa_kernel(const uint16_t* __restrict__ q
     // O^T += V^T P^T over two 32-key k-steps
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      bf16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = to_bf16(s[2 * u][i]);
-        pb[4 + i] = to_bf16(s[2 * u + 1][i]);
-      }
+      const bf16x8 pb = pack_bf16x8(s[2 * u], s[2 * u + 1]);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const uint16_t* vr = sVt + (16 * dt + qc) * SVT + 32 * u + 4 * g4;
         const uint2 lo = *reinterpret_cast<const uint2*>(vr);
         const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-        bf16x8 a;
-        a[0] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x & 0xFFFF));
-        a[1] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x >> 16));
-        a[2] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y & 0xFFFF));
-        a[3] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y >> 16));
-        a[4] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x & 0xFFFF));
-        a[5] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x >> 16));
-        a[6] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y & 0xFFFF));
-        a[7] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y >> 16));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
         o[dt] = mfma_bf16_16x16x32(a, pb, o[dt]);
       }
     }
