@@ -45,8 +45,8 @@ tc_status check_seq(const char* fn, int B, int H, int T, int dk, int dv, int chu
   if (chunk != 64) return fail(TC_ERR_UNSUPPORTED, "%s: chunk must be 64 (got %d)", fn, chunk);
   if (dk != dv || !supported_d(dk))
     return fail(TC_ERR_UNSUPPORTED, "%s: need dk == dv in {16, 32, 64, 128} (got %d, %d)", fn, dk, dv);
-  // indices are formed in 64-bit, but one (b, h) row block must stay addressable in 32 bits
-  if ((long long)T * dk >= (1LL << 31)) return fail(TC_ERR_UNSUPPORTED, "%s: T * d too large", fn);
+  // one (b, h) block of rows is addressed with 32-bit byte offsets
+  if ((long long)T * dk >= (1LL << 29)) return fail(TC_ERR_UNSUPPORTED, "%s: T * d must be < 2^29", fn);
   if ((long long)B * H >= 65536) return fail(TC_ERR_UNSUPPORTED, "%s: B * H must be < 65536", fn);
   return TC_OK;
 }

@@ -22,7 +22,33 @@ typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Wave index as a scalar: tells the compiler that tests on it are wave-uniform.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// drains every outstanding global load (s_waitcnt vmcnt(0)), which would
+// cancel register prefetching across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Buffer resource over [base, base + nbytes): raw buffer loads past the end
+// (or at a negative offset, which wraps to a huge unsigned one) return zero
+// instead of touching memory, so edge tiles need no branches around loads.
+// 0x00020000 is the gfx9 word-3 value (raw dword data, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(nbytes), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
 
 // bfloat16 stored as raw 16-bit patterns (uint16_t) in memory.
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

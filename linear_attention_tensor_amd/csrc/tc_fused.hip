@@ -94,44 +94,64 @@ struct Lds {
 };
 
 // One 64-key block (K and V rows j..j+63) held in registers between its
-// global load and its LDS store.
+// global load and its LDS store.  K is copied row-major in 16-byte pieces.
+// V is stored transposed: a thread holds rows r, r+1 of 8 consecutive d_v
+// columns and writes 4-byte (key pair) words.  Lane l of a wave takes the row
+// pair l % 16 and the column group l / 16, so one store instruction touches
+// 64 different LDS banks (row stride of V^T: 34 words, 16 column groups of 8
+// rows apart = 16 banks).
 template <int D>
 struct BlockRegs {
-  static constexpr int N = KB * D / 8 / NTHR;  // 16-byte chunks per thread per tensor
-  uint4 k[N], v[N];
+  static constexpr int NK = KB * D / 8 / NTHR;  // 16-byte K pieces per thread
+  static constexpr int NV = 32 * (D / 8);       // threads that own a V piece pair
+  uint4 k[NK], v0, v1;
 };
 
 template <int D>
-__device__ __forceinline__ void load_block(BlockRegs<D>& r, const uint16_t* __restrict__ kg,
-                                           const uint16_t* __restrict__ vg, long base, int j, int T) {
+__device__ __forceinline__ void v_piece(int& r, int& c8) {
+  const int t = threadIdx.x, l = t & 63, w = t >> 6;
+  r = 2 * (l & 15) + 32 * (w & 1);
+  c8 = 8 * (4 * (w >> 1) + (l >> 4));
+  if (c8 >= D) c8 = 0;  // threads without a piece (D < 128) still address valid memory
+}
+
+// rk, rv: buffer resources over this head's K and V rows [0, T)
+template <int D>
+__device__ __forceinline__ BlockRegs<D> load_block(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                                   int j) {
+  BlockRegs<D> r;
 #pragma unroll
-  for (int i = 0; i < BlockRegs<D>::N; ++i) {
+  for (int i = 0; i < BlockRegs<D>::NK; ++i) {
     const int idx = threadIdx.x + i * NTHR;
     const int row = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-    const int jj = j + row;
-    if (jj >= 0 && jj < T) {
-      r.k[i] = *reinterpret_cast<const uint4*>(kg + (base + jj) * D + c8);
-      r.v[i] = *reinterpret_cast<const uint4*>(vg + (base + jj) * D + c8);
-    } else {
-      r.k[i] = make_uint4(0u, 0u, 0u, 0u);
-      r.v[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    r.k[i] = buf_load16(rk, ((j + row) * D + c8) * 2);
   }
+  int row, c8;
+  v_piece<D>(row, c8);
+  r.v0 = buf_load16(rv, ((j + row) * D + c8) * 2);
+  r.v1 = buf_load16(rv, ((j + row + 1) * D + c8) * 2);
+  return r;
 }
 
 template <int D>
 __device__ __forceinline__ void store_block(const BlockRegs<D>& r, uint16_t* sk, uint16_t* svt) {
   using L = Lds<D>;
 #pragma unroll
-  for (int i = 0; i < BlockRegs<D>::N; ++i) {
+  for (int i = 0; i < BlockRegs<D>::NK; ++i) {
     const int idx = threadIdx.x + i * NTHR;
     const int row = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
     *reinterpret_cast<uint4*>(sk + row * L::SK + c8) = r.k[i];
-    const uint32_t vw[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+  }
+  if (threadIdx.x < BlockRegs<D>::NV) {
+    int row, c8;
+    v_piece<D>(row, c8);
+    const uint32_t a[4] = {r.v0.x, r.v0.y, r.v0.z, r.v0.w};
+    const uint32_t b[4] = {r.v1.x, r.v1.y, r.v1.z, r.v1.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      svt[(c8 + 2 * e) * L::SVT + row] = static_cast<uint16_t>(vw[e] & 0xFFFFu);
-      svt[(c8 + 2 * e + 1) * L::SVT + row] = static_cast<uint16_t>(vw[e] >> 16);
+      // column c8+2e: (row, row+1) low halves; column c8+2e+1: high halves
+      *reinterpret_cast<uint32_t*>(svt + (c8 + 2 * e) * L::SVT + row) = (a[e] & 0xFFFFu) | (b[e] << 16);
+      *reinterpret_cast<uint32_t*>(svt + (c8 + 2 * e + 1) * L::SVT + row) = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
     }
   }
 }
@@ -264,13 +284,74 @@ struct FusedGeom {
   }
 };
 
+// Registers of one 64-key block for the state pass: rows r, r+1 of K and V
+// at 8 consecutive columns (the transposed-store piece of v_piece).
+struct PairRegs {
+  uint4 k0, k1, v0, v1;
+};
+
+// rk, rv: buffer resources over this head's K and V rows [0, end)
+template <int D>
+__device__ __forceinline__ PairRegs load_pair(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int j) {
+  int row, c8;
+  v_piece<D>(row, c8);
+  PairRegs p;
+  p.k0 = buf_load16(rk, ((j + row) * D + c8) * 2);
+  p.v0 = buf_load16(rv, ((j + row) * D + c8) * 2);
+  p.k1 = buf_load16(rk, ((j + row + 1) * D + c8) * 2);
+  p.v1 = buf_load16(rv, ((j + row + 1) * D + c8) * 2);
+  return p;
+}
+
+// K^T and (w V)^T into LDS, keys contiguous; w_j = eta lam^(end-1-j).
+template <int D, int SKT>
+__device__ __forceinline__ void store_pair(const PairRegs& p, uint16_t* skt, uint16_t* svt, int j,
+                                           int end, float et, const Decay& dec) {
+  if (threadIdx.x >= 32 * (D / 8)) return;
+  int row, c8;
+  v_piece<D>(row, c8);
+  const int jj = j + row;
+  const float w0 = jj < end ? et * dec(end - 1 - jj) : 0.f;
+  const float w1 = jj + 1 < end ? et * dec(end - 2 - jj) : 0.f;
+  const uint32_t ka[4] = {p.k0.x, p.k0.y, p.k0.z, p.k0.w}, kb[4] = {p.k1.x, p.k1.y, p.k1.z, p.k1.w};
+  const uint32_t va[4] = {p.v0.x, p.v0.y, p.v0.z, p.v0.w}, vb[4] = {p.v1.x, p.v1.y, p.v1.z, p.v1.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    *reinterpret_cast<uint32_t*>(skt + (c8 + 2 * e) * SKT + row) = (ka[e] & 0xFFFFu) | (kb[e] << 16);
+    *reinterpret_cast<uint32_t*>(skt + (c8 + 2 * e + 1) * SKT + row) = (ka[e] >> 16) | (kb[e] & 0xFFFF0000u);
+    *reinterpret_cast<uint32_t*>(svt + (c8 + 2 * e) * SKT + row) = cvt_pk(lo_f(va[e]) * w0, lo_f(vb[e]) * w1);
+    *reinterpret_cast<uint32_t*>(svt + (c8 + 2 * e + 1) * SKT + row) = cvt_pk(hi_f(va[e]) * w0, hi_f(vb[e]) * w1);
+  }
+}
+
+// acc (this wave's S^T tiles) += (w V)^T K over one 64-key block in LDS
+template <int D, int SKT>
+__device__ __forceinline__ void state_block_mma(floatx16* acc, const uint16_t* sKt, const uint16_t* sVt) {
+  using ST = StateTiles<D>;
+  const int w = wave_id(), l = lane_id(), col = l & 31, hh = l >> 5;
+#pragma unroll
+  for (int i = 0; i < ST::TPW; ++i) {
+    if (!ST::owns(w, i)) continue;
+    const int dv0 = ST::dv0(w, i), dk0 = ST::dk0(w, i);
+#pragma unroll
+    for (int ks = 0; ks < KB / 16; ++ks) {
+      const int kb = 16 * ks + 8 * hh;
+      const uint2 a0 = *reinterpret_cast<const uint2*>(sVt + (dv0 + col) * SKT + kb);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(sVt + (dv0 + col) * SKT + kb + 4);
+      const uint2 b0 = *reinterpret_cast<const uint2*>(sKt + (dk0 + col) * SKT + kb);
+      const uint2 b1 = *reinterpret_cast<const uint2*>(sKt + (dk0 + col) * SKT + kb + 4);
+      acc[i] = mfma32(as_bf16x8(a0.x, a0.y, a1.x, a1.y), as_bf16x8(b0.x, b0.y, b1.x, b1.y), acc[i]);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            const float* __restrict__ lam,
                                                            const float* __restrict__ eta, int H,
                                                            FusedGeom G, float* __restrict__ ws) {
-  constexpr int SKT = KB + 4;  // K^T and V^T rows: keys contiguous
+  constexpr int SKT = KB + 4;  // K^T and V^T rows: keys contiguous, 34-word stride
   __shared__ __attribute__((aligned(16))) uint16_t sKt[D * SKT];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[D * SKT];
   using ST = StateTiles<D>;
@@ -285,45 +366,30 @@ __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __res
 #pragma unroll
   for (int i = 0; i < ST::TPW; ++i) acc[i] = zero16();
 
-  for (int j = a; j < b; j += KB) {
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < KB * (D / 8); idx += NTHR) {
-      const int row = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
-      const int jj = j + row;
-      uint4 kx = make_uint4(0u, 0u, 0u, 0u), vx = make_uint4(0u, 0u, 0u, 0u);
-      float wt = 0.f;
-      if (jj < b) {
-        kx = *reinterpret_cast<const uint4*>(k + (base + jj) * D + c8);
-        vx = *reinterpret_cast<const uint4*>(v + (base + jj) * D + c8);
-        wt = et * dec(b - 1 - jj);
-      }
-      const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w};
-      const uint32_t vw[4] = {vx.x, vx.y, vx.z, vx.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sKt[(c8 + 2 * e) * SKT + row] = static_cast<uint16_t>(kw[e] & 0xFFFFu);
-        sKt[(c8 + 2 * e + 1) * SKT + row] = static_cast<uint16_t>(kw[e] >> 16);
-        const uint32_t sv = cvt_pk(lo_f(vw[e]) * wt, hi_f(vw[e]) * wt);
-        sVt[(c8 + 2 * e) * SKT + row] = static_cast<uint16_t>(sv & 0xFFFFu);
-        sVt[(c8 + 2 * e + 1) * SKT + row] = static_cast<uint16_t>(sv >> 16);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < ST::TPW; ++i) {
-      if (!ST::owns(w, i)) continue;
-      const int dv0 = ST::dv0(w, i), dk0 = ST::dk0(w, i);
-#pragma unroll
-      for (int ks = 0; ks < KB / 16; ++ks) {
-        const int kb = 16 * ks + 8 * hh;
-        const uint2 a0 = *reinterpret_cast<const uint2*>(sVt + (dv0 + col) * SKT + kb);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(sVt + (dv0 + col) * SKT + kb + 4);
-        const uint2 b0 = *reinterpret_cast<const uint2*>(sKt + (dk0 + col) * SKT + kb);
-        const uint2 b1 = *reinterpret_cast<const uint2*>(sKt + (dk0 + col) * SKT + kb + 4);
-        acc[i] = mfma32(as_bf16x8(a0.x, a0.y, a1.x, a1.y), as_bf16x8(b0.x, b0.y, b1.x, b1.y), acc[i]);
-      }
-    }
+  // three blocks in flight in registers; one LDS buffer
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base * D, (uint32_t)b * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base * D, (uint32_t)b * D * 2);
+  PairRegs r0 = load_pair<D>(rk, rv, a);
+  PairRegs r1 = load_pair<D>(rk, rv, a + KB);
+  PairRegs r2 = load_pair<D>(rk, rv, a + 2 * KB);
+  // r0, r1, r2 keep fixed roles (a register that is the target of a load in
+  // flight is never copied), so up to three blocks stay in flight.
+  // Loads are issued unconditionally (past the end they read clamped rows as
+  // zero) so the count of loads in flight is the same on every path.
+#define TC_STATE_STEP(R, J)                                    \
+  if ((J) < b) {                                               \
+    lds_barrier();                                             \
+    store_pair<D, SKT>(R, sKt, sVt, (J), b, et, dec);          \
+    lds_barrier();                                             \
+  }                                                            \
+  R = load_pair<D>(rk, rv, (J) + 3 * KB);                      \
+  if ((J) < b) state_block_mma<D, SKT>(acc, sKt, sVt);
+  for (int j = a; j < b; j += 3 * KB) {
+    TC_STATE_STEP(r0, j)
+    TC_STATE_STEP(r1, j + KB)
+    TC_STATE_STEP(r2, j + 2 * KB)
   }
+#undef TC_STATE_STEP
   float* out = ws + ((long)bh * G.n_seg + p) * D * D;
 #pragma unroll
   for (int i = 0; i < ST::TPW; ++i) {
@@ -371,6 +437,9 @@ __global__ __launch_bounds__(NTHR) void fused_main_kernel(
   const float et = eta[h];
   const float sg = 1.f / (1.f + expf(-g[h]));
   const long base = (long)bh * T;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + base * D, (uint32_t)T * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base * D, (uint32_t)T * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base * D, (uint32_t)T * D * 2);
 
   // entering state of the segment, fp32 in LDS
   {
@@ -378,7 +447,7 @@ __global__ __launch_bounds__(NTHR) void fused_main_kernel(
     for (int i = threadIdx.x; i < D * D; i += NTHR)
       lds.s[(i / D) * L::SSF + (i % D)] = in ? in[i] : 0.f;
   }
-  __syncthreads();
+  lds_barrier();
 
   const int nb = (W + MQ + KB - 1) / KB;  // key blocks per tile (>= 5)
   const int tile_begin = seg * G.tiles_per_seg;
@@ -393,9 +462,10 @@ __global__ __launch_bounds__(NTHR) void fused_main_kernel(
 
     bf16x8 qreg[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qreg[ks] = tq < T ? *reinterpret_cast<const bf16x8*>(q + (base + tq) * D + 16 * ks + 8 * hh)
-                        : as_bf16x8(0u, 0u, 0u, 0u);
+    for (int ks = 0; ks < NKS; ++ks) {
+      const uint4 x = buf_load16(rq, (tq * D + 16 * ks + 8 * hh) * 2);
+      qreg[ks] = as_bf16x8(x.x, x.y, x.z, x.w);
+    }
     floatx16 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] = zero16();
@@ -405,15 +475,14 @@ __global__ __launch_bounds__(NTHR) void fused_main_kernel(
     auto block_at = [nb](int idx) {
       return idx < nb - 4 ? idx + 4 : (idx < nb - 2 ? idx - (nb - 4) + 2 : idx - (nb - 2));
     };
-    BlockRegs<D> pre;
-    load_block<D>(pre, k, v, base, j0 + KB * block_at(0), T);
+    BlockRegs<D> pre = load_block<D>(rk, rv, j0 + KB * block_at(0));
     store_block<D>(pre, lds.k[0], lds.vt[0]);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll 1
     for (int idx = 0; idx < nb; ++idx) {
       const int b = block_at(idx);
       const int buf = idx & 1;
-      if (idx + 1 < nb) load_block<D>(pre, k, v, base, j0 + KB * block_at(idx + 1), T);
+      pre = load_block<D>(rk, rv, j0 + KB * block_at(min(idx + 1, nb - 1)));
       const int c_lo = KB * b, c_hi = KB * b + KB - 1;
       const int r_lo = 32 * w, r_hi = 32 * w + 31;
       const int jb = j0 + c_lo;
@@ -424,29 +493,40 @@ __global__ __launch_bounds__(NTHR) void fused_main_kernel(
         block_scores<D>(lds.k[buf], qreg, s);
         const int r = 32 * w + col;
         float bmax = kNegBig;
+        if (full) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            if (!full) {
-              const int c = c_lo + key_of(kt, e, hh);
-              const int j = j0 + c;
-              const bool ok = c > r && c <= r + W && j >= 0 && j < T;
+            for (int e = 0; e < 16; ++e) bmax = fmaxf(bmax, s[kt][e]);
+        } else {
+          // valid key offsets within the block: lo <= key_of(..) <= hi
+          const int lo = max(r + 1 - c_lo, -jb);
+          const int hi = min(r + W - c_lo, T - 1 - jb);
+          const unsigned span = static_cast<unsigned>(hi - lo);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const bool ok = hi >= lo && static_cast<unsigned>(key_of(kt, e, hh) - lo) <= span;
               s[kt][e] = ok ? s[kt][e] : -INFINITY;
+              bmax = fmaxf(bmax, s[kt][e]);
             }
-            bmax = fmaxf(bmax, s[kt][e]);
           }
         }
         bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-        const float mnew = fmaxf(mrun, bmax);
-        if (__ballot(mnew > mrun) != 0) {
+        // Lazy rescaling: the reference maximum moves only when some score of
+        // the wave exceeds it by more than 8 (log2 units), so p <= 2^8 and the
+        // accumulators stay far from overflow; O and lsum share the reference,
+        // so the final O / lsum is unchanged.
+        if (__ballot((bmax - mrun) * scale_log2 > 8.f) != 0) {
+          const float mnew = fmaxf(mrun, bmax);
           const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * scale_log2);
           lsum *= alpha;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+          mrun = mnew;
         }
-        mrun = mnew;
-        const float nms = -mnew * scale_log2;
+        const float nms = -mrun * scale_log2;
         float psum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -461,7 +541,7 @@ __global__ __launch_bounds__(NTHR) void fused_main_kernel(
         block_pv<D>(lds.vt[buf], s, o);
       }
       if (idx + 1 < nb) store_block<D>(pre, lds.k[buf ^ 1], lds.vt[buf ^ 1]);
-      __syncthreads();
+      lds_barrier();
     }
     {
       const float tot = lsum + __shfl_xor(lsum, 32);
@@ -478,12 +558,11 @@ __global__ __launch_bounds__(NTHR) void fused_main_kernel(
       const int jend = min(jc + CHK, T - W);  // one past its last valid eviction
       const bool chunk_live = jc + CHK - 1 >= 0 && jc < T - W;
       if (ch == 1) {
-        BlockRegs<D> r2;
-        load_block<D>(r2, k, v, base, j0 + 2 * KB, T);
+        const BlockRegs<D> r2 = load_block<D>(rk, rv, j0 + 2 * KB);
+        const BlockRegs<D> r3 = load_block<D>(rk, rv, j0 + 3 * KB);
         store_block<D>(r2, lds.k[0], lds.vt[0]);
-        load_block<D>(r2, k, v, base, j0 + 3 * KB, T);
-        store_block<D>(r2, lds.k[1], lds.vt[1]);
-        __syncthreads();
+        store_block<D>(r3, lds.k[1], lds.vt[1]);
+        lds_barrier();
       }
       const uint16_t* sk0 = ch == 0 ? lds.k[(nb - 2) & 1] : lds.k[0];
       const uint16_t* sk1 = ch == 0 ? lds.k[(nb - 1) & 1] : lds.k[1];
@@ -541,19 +620,19 @@ __global__ __launch_bounds__(NTHR) void fused_main_kernel(
       }
       // state step over the chunk's evictions [max(jc, 0), jend)
       const bool writes = jend > max(jc, 0);
-      __syncthreads();  // all reads of unscaled V^T and of the state copy are done
+      lds_barrier();  // all reads of unscaled V^T and of the state copy are done
       if (writes) {
         if (threadIdx.x < CHK) {
           const int j = jc + threadIdx.x;
           lds.w[threadIdx.x] = (j >= 0 && j < jend) ? et * dec(jend - 1 - j) : 0.f;
         }
-        __syncthreads();
+        lds_barrier();
         scale_vt<D>(svt0, svt1, lds.w);
-        __syncthreads();
+        lds_barrier();
         state_update<D>(lds.s, dec(jend - jc), sk0, svt0, sk1, svt1);
       }
       // chunk 0 leaves S_{n+1} for chunk 1's readers, chunk 1 the next tile's state
-      __syncthreads();
+      lds_barrier();
     }
   }
 
