@@ -106,7 +106,12 @@ def test_decode_rejects():
 def test_fused_rejects():
     f = lib().tc_fused_layer
 
-    def call(dt=_lib.TC_BF16, d=128, scale=0.1, ws_bytes=0, W=64, T=256):
+    T = 32768  # long enough that the call needs a workspace
+    need = lib().tc_fused_workspace_bytes(1, 2, T, 128, 128, 64, 64, _lib.TC_BF16)
+    assert 0 < need < _lib.SIZE_MAX
+
+    # every call below is rejected before any launch (a short workspace included)
+    def call(dt=_lib.TC_BF16, d=128, scale=0.1, ws_bytes=0, W=64):
         return f(FAKE, FAKE, FAKE, dt, FAKE, FAKE, FAKE, 1, 2, T, d, d, W, 64, scale, FAKE, NULL, FAKE,
                  ws_bytes, NULL)
 
@@ -114,7 +119,7 @@ def test_fused_rejects():
     assert call(d=32) == _lib.TC_ERR_UNSUPPORTED
     assert call(scale=0.0) == _lib.TC_ERR_INVALID_ARG
     assert call(scale=float("nan")) == _lib.TC_ERR_INVALID_ARG
-    assert call(ws_bytes=0) == _lib.TC_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == _lib.TC_ERR_WORKSPACE
     assert lib().tc_fused_workspace_bytes(1, 2, 256, 128, 128, 64, 64, _lib.TC_F32) == _lib.SIZE_MAX
 
 
