@@ -1,0 +1,604 @@
+// tc_swa.hip — main kernel of the fused Tensor Cache layer (gfx950, bf16
+// inputs): exact softmax attention over the W most recent tokens (L1) plus
+// the gated read of the L2 memory, y = y_local + sigmoid(g) m.
+//
+// Tensor Cache, Methodology 1: the L1 cache is a KV ring of the W most recent
+// tokens with exact softmax attention over it; a token leaves it exactly when
+// it is written into the L2 matrix, A <- lam A + eta k v^T; the read is
+// m_t = q_t A_t, and y_t = y_local,t + sigmoid(g) m_t.  Methodology 2: the L2
+// part is evaluated in chunk form, here one chunk per 256-query tile:
+//   m_r = lam^(r+1) q_r S_n + sum_{c <= r} eta lam^(r-c) <q_r, k_c> v_c,
+// with S_n the state entering the tile (computed by the pre-pass and prefix).
+//
+// One workgroup = 8 waves = 256 queries (one tile); wave w owns 32 queries.
+// Keys are taken in 64-key blocks from j0 = t0 - W (c = j - j0, r = t - t0;
+// key j is in the window of query t iff r < c <= r + W, and has been written
+// into the L2 memory iff c <= r).  Blocks travel global -> LDS by
+// buffer_load ... lds (K row-major, V^T from the transposed copy in the
+// workspace), four blocks resident.  S^T = K Q^T puts one query's scores in
+// every lane (v_mfma_f32_32x32x16_bf16), and P feeds O^T += V^T P^T from
+// registers.  The loop is software-pipelined: the QK^T MFMAs of block i+1
+// are interleaved with the softmax of block i and its PV MFMAs, so the matrix
+// cores and the vector ALUs work at the same time.  Blocks 4.. come first and
+// blocks 0-3 last, so the latter (the tile's evictions) are still resident
+// for the L2 epilogue.  Tiles are mapped so that the workgroups that share an
+// XCD at the same time work on neighbouring tiles of one head and share K/V
+// through its L2 cache.
+#include "tc_common.hpp"
+#include "tc_kernels.hpp"
+#include "tc_mfma.hpp"
+
+#include <math.h>
+
+namespace tc {
+
+namespace {
+
+using namespace mf;
+
+constexpr int NWAVE = 8;
+constexpr int NTHR = 64 * NWAVE;
+constexpr int MQ = 32 * NWAVE;  // queries per tile
+constexpr int NSTAGE = 4;       // blocks resident in LDS
+constexpr int NXCD = 8;         // MI355X: 8 accelerator complex dies, dispatched round-robin
+constexpr float kNegBig = -1.0e30f;
+
+template <int D>
+struct SwaLds {
+  uint16_t k[NSTAGE][KB * D];
+  uint16_t vt[NSTAGE][D * KB];
+  uint16_t st[D * D];  // entering L2 state S^T (rows dv), as D/64 K-layout blocks
+};
+
+template <int D>
+struct Dma {
+  static constexpr int NK = KB * D / 8 / NTHR;  // 16-byte K slots per thread
+  static constexpr int NV = D * 8 / NTHR;       // 16-byte V^T slots per thread
+  static constexpr int N = NK + NV;
+};
+
+// Lane parts of the DMA source offsets (bytes, block start excluded).
+template <int D>
+struct DmaOff {
+  int k[Dma<D>::NK];
+  int v[Dma<D>::NV];
+};
+
+template <int D>
+__device__ __forceinline__ DmaOff<D> dma_offsets(int Tp, int voff) {
+  DmaOff<D> o;
+  const int w = wave_id(), l = lane_id();
+#pragma unroll
+  for (int i = 0; i < Dma<D>::NK; ++i) {
+    int m, c;
+    k_slot_inv<D>((i * NWAVE + w) * 64 + l, m, c);
+    o.k[i] = (perm16(m) * D + 8 * c) * 2;
+  }
+#pragma unroll
+  for (int i = 0; i < Dma<D>::NV; ++i) {
+    int dv, c;
+    v_slot_inv((i * NWAVE + w) * 64 + l, dv, c);
+    o.v[i] = (dv * Tp + voff + 8 * c) * 2;
+  }
+  return o;
+}
+
+// Raw buffer descriptor over [base, base + nbytes) (gfx9 layout: stride 0,
+// word 3 = raw dword data); reads past the end return zero.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 raw_desc(const void* base, uint32_t nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xFFFF), static_cast<int>(nbytes),
+               0x00020000};
+}
+
+// 16 bytes per lane global -> LDS (lane i writes lds_base + 16 i).  Issued
+// as inline asm so that the compiler neither waits for these loads before
+// every later LDS read nor before every barrier: the kernel orders them
+// itself with s_waitcnt vmcnt and a workgroup barrier.  No register is
+// written, and the operands are read when the instruction issues.
+__device__ __forceinline__ void dma16(i32x4 desc, const void* lds_base, int voffset) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(desc)
+               : "memory", "m0");
+}
+
+// DMA of the 64-key block starting at key j (any sign) into one stage.  dk:
+// this head's K rows [0, T); dvt: its V^T copy, rows of Tp columns, key j in
+// column j + voff.  Reads outside the descriptors return zero.  Instruction
+// i of wave w fills the 1 KiB piece i * 8 + w of the stage.
+template <int D>
+__device__ __forceinline__ void dma_block(i32x4 dk, i32x4 dvt, const DmaOff<D>& off, int j,
+                                          uint16_t* sk, uint16_t* svt) {
+  const int w = wave_id();
+#pragma unroll
+  for (int i = 0; i < Dma<D>::NK; ++i) dma16(dk, sk + (i * NWAVE + w) * 512, off.k[i] + j * D * 2);
+#pragma unroll
+  for (int i = 0; i < Dma<D>::NV; ++i) dma16(dvt, svt + (i * NWAVE + w) * 512, off.v[i] + j * 2);
+}
+
+// DMA of the tile's entering state (bf16, [dv][dk] row-major in global) into
+// the K-block layout, rows in natural order (row m of block h holds dv =
+// 64 h + m), so that S^T Q^T comes out in the layout of O^T.
+template <int D>
+__device__ __forceinline__ void dma_state(i32x4 dst_desc, uint16_t* sst) {
+  constexpr int NI = D * D / 8 / NTHR;  // 16-byte slots per thread
+  const int w = wave_id(), l = lane_id();
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int slot = (i * NWAVE + w) * 64 + l;
+    int m, c;
+    k_slot_inv<D>(slot & (8 * D - 1), m, c);
+    const int dv = 64 * (slot / (8 * D)) + m;
+    dma16(dst_desc, sst + (i * NWAVE + w) * 512, (dv * D + 8 * c) * 2);
+  }
+}
+
+// max / sum over the two 32-lane halves (the two halves of a query's keys)
+__device__ __forceinline__ float max_halves(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(s[0]), __int_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(s[0]) + __int_as_float(s[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Operand batches.  Every LDS operand read is issued one batch (four MFMAs,
+// >= 128 cycles) before the MFMA that uses it, and sched_barrier fences keep
+// the compiler from sinking the reads next to their uses (which would expose
+// the LDS latency on every MFMA).
+
+// K operands of k-steps KS, KS+1: rows 0-31 and 32-63 of the block
+template <int KS>
+__device__ __forceinline__ void ld_k2(const char* sk, const uint32_t* ls, bf16x8* x) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t off = ls[(KS + i) & 3] + 8192u * ((KS + i) >> 2);
+    x[2 * i] = lds16(sk, off);
+    x[2 * i + 1] = lds16(sk, off + 4096u);
+  }
+}
+template <int KS>
+__device__ __forceinline__ void mm_k2(const bf16x8* x, const bf16x8* qreg, floatx16& a0, floatx16& a1) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    a0 = mfma32(x[2 * i], qreg[KS + i], a0);
+    a1 = mfma32(x[2 * i + 1], qreg[KS + i], a1);
+  }
+}
+// V^T operands of PV k-step kk (lane slot ls_kk), all D/32 row tiles
+template <int D>
+__device__ __forceinline__ void ld_v(const char* svt, uint32_t ls_kk, bf16x8* x) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) x[dt] = lds16(svt, ls_kk + 4096u * dt);
+}
+template <int D>
+__device__ __forceinline__ void mm_v(const bf16x8* x, bf16x8 pb, floatx16* o) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = mfma32(x[dt], pb, o[dt]);
+}
+
+#define TC_SB() __builtin_amdgcn_sched_barrier(0)
+// reads first, then MFMAs each followed by NV VALU instructions
+#define TC_GROUPS(NR, NM, NV)                                     \
+  do {                                                            \
+    __builtin_amdgcn_sched_group_barrier(0x100, (NR), 0);         \
+    _Pragma("unroll") for (int i_ = 0; i_ < (NM); ++i_) {         \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          \
+      __builtin_amdgcn_sched_group_barrier(0x002, (NV), 0);       \
+    }                                                             \
+  } while (0)
+
+// S^T of a whole block (keys 0-31 -> a0, 32-63 -> a1), batched
+template <int D>
+__device__ __forceinline__ void qk_block(const char* sk, const uint32_t* ls, const bf16x8* qreg,
+                                         floatx16& a0, floatx16& a1) {
+  bf16x8 x0[4], x1[4];
+  a0 = zero16();
+  a1 = zero16();
+  ld_k2<0>(sk, ls, x0);
+  ld_k2<2>(sk, ls, x1);
+  TC_SB();
+  mm_k2<0>(x0, qreg, a0, a1);
+  if constexpr (D == 128) {
+    ld_k2<4>(sk, ls, x0);
+    TC_SB();
+    mm_k2<2>(x1, qreg, a0, a1);
+    ld_k2<6>(sk, ls, x1);
+    TC_SB();
+    mm_k2<4>(x0, qreg, a0, a1);
+    TC_SB();
+    mm_k2<6>(x1, qreg, a0, a1);
+  } else {
+    TC_SB();
+    mm_k2<2>(x1, qreg, a0, a1);
+  }
+}
+
+struct Softmax {
+  float m;  // reference maximum (raw score units), shared by the wave
+  float l;  // sum of this lane's probabilities
+};
+
+// Valid keys of this lane's query in a block: lo <= key <= lo + span (as
+// unsigned), with lo already lowered by 8 hh (key_of without the 8 hh term).
+struct KeyRange {
+  int lo;
+  unsigned span;
+};
+
+// Probabilities of PV k-step KK: p = 2^(s sl2 - m sl2) as bf16, and their
+// sum (of the same bf16 values that multiply V) into psum.
+template <int KK>
+__device__ __forceinline__ bf16x8 probs(const floatx16* sc, float sl2, float nms, float& psum) {
+  constexpr int kt = KK >> 1, e0 = (KK & 1) * 8;
+  const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  uint32_t pw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kt][e0 + 2 * e], sl2, nms));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kt][e0 + 2 * e + 1], sl2, nms));
+    pw[e] = cvt_pk(p0, p1);
+    psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), one2, psum, false);
+  }
+  return as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
+}
+
+// One pipelined step: QK^T of the next block (into sn) interleaved with the
+// softmax of the current block (sc) and its PV product.
+template <int D>
+__device__ __forceinline__ void swa_step(const char* sk_nxt, const char* svt_cur, const uint32_t* ls,
+                                         const bf16x8* qreg, floatx16* sc, floatx16* sn, floatx16* o,
+                                         Softmax& sm, float sl2, bool active, bool masked, KeyRange kr) {
+  constexpr int NDT = D / 32;
+  if (!active) {
+    qk_block<D>(sk_nxt, ls, qreg, sn[0], sn[1]);
+    return;
+  }
+  if (masked) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const unsigned d = static_cast<unsigned>(key_of(kt, e, 0) - kr.lo);
+        sc[kt][e] = d <= kr.span ? sc[kt][e] : -INFINITY;
+      }
+  }
+  floatx16 a0 = zero16(), a1 = zero16();
+  bf16x8 ka[4], kb[4];
+  float m0 = kNegBig, m1 = kNegBig;
+  // region A: QK^T k-steps 0..NKS/2-1 of the next block; block maximum
+  TC_SB();
+  ld_k2<0>(sk_nxt, ls, ka);
+  TC_SB();
+  ld_k2<2>(sk_nxt, ls, kb);
+  mm_k2<0>(ka, qreg, a0, a1);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) m0 = fmaxf(m0, sc[0][e]);
+  if constexpr (D == 64) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m1 = fmaxf(m1, sc[1][e]);
+  }
+  TC_GROUPS(4, 4, D == 128 ? 2 : 4);
+  TC_SB();
+  if constexpr (D == 128) {
+    ld_k2<4>(sk_nxt, ls, ka);
+    mm_k2<2>(kb, qreg, a0, a1);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m1 = fmaxf(m1, sc[1][e]);
+    TC_GROUPS(4, 4, 2);
+    TC_SB();
+  }
+  const float bmax = max_halves(fmaxf(m0, m1));
+  // Lazy rescaling: the reference maximum moves only when a score of the
+  // wave exceeds it by more than 2^8 in probability; O and l share the
+  // reference, so O / l is unchanged and p stays <= 2^8.
+  if (__ballot((bmax - sm.m) * sl2 > 8.f) != 0) {
+    const float mnew = fmaxf(sm.m, bmax);
+    const float alpha = __builtin_amdgcn_exp2f((sm.m - mnew) * sl2);
+    sm.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    sm.m = mnew;
+  }
+  TC_SB();
+  // region B: remaining QK^T k-steps, exponentials, PV
+  const float nms = -sm.m * sl2;
+  float psum = 0.f;
+  bf16x8 va[NDT], vb[NDT];
+  bf16x8 p0, p1, p2, p3;
+  if constexpr (D == 128) {
+    ld_k2<6>(sk_nxt, ls, kb);
+    mm_k2<4>(ka, qreg, a0, a1);
+    p0 = probs<0>(sc, sl2, nms, psum);
+    TC_GROUPS(4, 4, 6);
+    TC_SB();
+    ld_v<D>(svt_cur, ls[0], va);
+    mm_k2<6>(kb, qreg, a0, a1);
+  } else {
+    ld_v<D>(svt_cur, ls[0], va);
+    mm_k2<2>(kb, qreg, a0, a1);
+    p0 = probs<0>(sc, sl2, nms, psum);
+    TC_GROUPS(NDT, 4, 6);
+    TC_SB();
+  }
+  p1 = probs<1>(sc, sl2, nms, psum);
+  if constexpr (D == 128) {
+    TC_GROUPS(NDT, 4, 6);
+    TC_SB();
+  }
+  ld_v<D>(svt_cur, ls[1], vb);
+  mm_v<D>(va, p0, o);
+  p2 = probs<2>(sc, sl2, nms, psum);
+  TC_GROUPS(NDT, NDT, 24 / NDT);
+  TC_SB();
+  ld_v<D>(svt_cur, ls[2], va);
+  mm_v<D>(vb, p1, o);
+  p3 = probs<3>(sc, sl2, nms, psum);
+  TC_GROUPS(NDT, NDT, 24 / NDT);
+  TC_SB();
+  ld_v<D>(svt_cur, ls[3], vb);
+  mm_v<D>(va, p2, o);
+  TC_SB();
+  mm_v<D>(vb, p3, o);
+  sm.l += psum;
+  TC_SB();
+  sn[0] = a0;
+  sn[1] = a1;
+}
+
+// Per-head parameters of the L2 read (nullptr sst: no L2 term).
+struct L2Args {
+  const uint16_t* sst;  // entering states, [B*H][n_tiles][D][D] bf16 (S^T: row dv)
+  const float* lam;
+  const float* eta;
+  const float* g;
+  int H;
+};
+
+// L2 weights of PV k-step KK: p = fe lam^(r-c) <q_r, k_c> for valid keys.
+template <int KK>
+__device__ __forceinline__ bf16x8 l2probs(const floatx16* s, int lo, unsigned span, float xl,
+                                          float log2lam, float fe) {
+  constexpr int kt = KK >> 1, e0 = (KK & 1) * 8;
+  uint32_t pw[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const int k0 = key_of(kt, e0 + e, 0), k1 = key_of(kt, e0 + e + 1, 0);
+    const float w0 = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(-k0), log2lam, xl));
+    const float w1 = __builtin_amdgcn_exp2f(fmaf(static_cast<float>(-k1), log2lam, xl));
+    const float q0 = static_cast<unsigned>(k0 - lo) <= span ? s[kt][e0 + e] * fe * w0 : 0.f;
+    const float q1 = static_cast<unsigned>(k1 - lo) <= span ? s[kt][e0 + e + 1] * fe * w1 : 0.f;
+    pw[e >> 1] = cvt_pk(q0, q1);
+  }
+  return as_bf16x8(pw[0], pw[1], pw[2], pw[3]);
+}
+
+// L2 term of one resident block b (0..3) of the tile's evictions:
+// o += V^T P^T with P[c][r] = fe lam^(r-c) <q_r, k_c> for c <= r, 0 <= j.
+template <int D>
+__device__ __forceinline__ void l2_block(const char* sk, const char* svt, const uint32_t* ls,
+                                         const bf16x8* qreg, floatx16* o, int b, int jb, int r,
+                                         float log2lam, float fe) {
+  constexpr int NDT = D / 32;
+  const int hh = lane_id() >> 5;
+  floatx16 s[2];
+  qk_block<D>(sk, ls, qreg, s[0], s[1]);
+  // valid keys: max(0, -jb) <= key <= r - 64 b  (key = key_of(kt, e, 0) + 8 hh)
+  int lo = max(0, -jb);
+  const int hi = r - KB * b;
+  unsigned span = static_cast<unsigned>(hi - lo);
+  if (hi < lo) {
+    lo = 1 << 20;
+    span = 0;
+  }
+  lo -= 8 * hh;
+  // lam^(r - c) = 2^((n - key0) log2 lam), n = r - 64 b - 8 hh
+  const float xl = static_cast<float>(hi - 8 * hh) * log2lam;
+  bf16x8 va[NDT], vb[NDT];
+  TC_SB();
+  ld_v<D>(svt, ls[0], va);
+  const bf16x8 p0 = l2probs<0>(s, lo, span, xl, log2lam, fe);
+  TC_SB();
+  ld_v<D>(svt, ls[1], vb);
+  mm_v<D>(va, p0, o);
+  const bf16x8 p1 = l2probs<1>(s, lo, span, xl, log2lam, fe);
+  TC_SB();
+  ld_v<D>(svt, ls[2], va);
+  mm_v<D>(vb, p1, o);
+  const bf16x8 p2 = l2probs<2>(s, lo, span, xl, log2lam, fe);
+  TC_SB();
+  ld_v<D>(svt, ls[3], vb);
+  mm_v<D>(va, p2, o);
+  const bf16x8 p3 = l2probs<3>(s, lo, span, xl, log2lam, fe);
+  TC_SB();
+  mm_v<D>(vb, p3, o);
+  TC_SB();
+}
+
+// bf16x8 * f, rounded to bf16
+__device__ __forceinline__ bf16x8 scale_bf16x8(bf16x8 x, float f) {
+  const u32x4 u = __builtin_bit_cast(u32x4, x);
+  return as_bf16x8(cvt_pk(lo_f(u[0]) * f, hi_f(u[0]) * f), cvt_pk(lo_f(u[1]) * f, hi_f(u[1]) * f),
+                   cvt_pk(lo_f(u[2]) * f, hi_f(u[2]) * f), cvt_pk(lo_f(u[3]) * f, hi_f(u[3]) * f));
+}
+
+template <int D>
+__global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ vt, L2Args l2,
+                                                   int T, int W, int Tp, int voff, int n_tiles,
+                                                   int n_items, float sl2, float* __restrict__ y) {
+  constexpr int NKS = D / 16;
+  constexpr int NDT = D / 32;
+  __shared__ __attribute__((aligned(16))) SwaLds<D> lds;
+
+  // XCD-aware mapping: the workgroups dispatched to one XCD take a contiguous
+  // run of (head, tile) items, so concurrent neighbours share K/V in its L2.
+  const int per_xcd = (n_items + NXCD - 1) / NXCD;
+  const int item = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+  if (item >= n_items) return;
+  const int bh = item / n_tiles, tile = item % n_tiles;
+
+  const int w = wave_id(), l = lane_id(), col = l & 31, hh = l >> 5;
+  const long base = (long)bh * T;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + base * D, (uint32_t)T * D * 2);
+  const i32x4 rk = raw_desc(k + base * D, (uint32_t)T * D * 2);
+  const i32x4 rvt = raw_desc(vt + (long)bh * D * Tp, (uint32_t)D * Tp * 2);
+  const DmaOff<D> doff = dma_offsets<D>(Tp, voff);
+
+  const int t0 = tile * MQ;
+  const int j0 = t0 - W;
+  const int tw = t0 + 32 * w;  // first query of this wave
+  const int tq = tw + col;     // this lane's query
+  const int nb = (W + MQ + KB - 1) / KB;  // >= 5
+  const int r_lo = 32 * w, r_hi = r_lo + 31;
+  // the tile writes evictions into the L2 memory iff some key j0 .. j0 + 255 is >= 0
+  const bool has_l2 = l2.sst != nullptr && j0 + MQ > 0;
+  // blocks 4 .. nb-1 first, then 0 .. 3 (left resident for the L2 epilogue)
+  auto block_at = [nb](int idx) { return idx < nb - 4 ? idx + 4 : idx - (nb - 4); };
+
+  bf16x8 qreg[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qreg[ks] = as_bf16x8(buf_load16(rq, (tq * D + 16 * ks + 8 * hh) * 2));
+  floatx16 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = zero16();
+  Softmax sm{kNegBig, 0.f};
+  uint32_t ls[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ls[j] = lane_slot(j);
+
+  // the state is used last but loaded first: the loads below complete in order
+  if (has_l2) dma_state<D>(raw_desc(l2.sst + ((long)bh * n_tiles + tile) * D * D, D * D * 2), lds.st);
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i)
+    dma_block<D>(rk, rvt, doff, j0 + KB * block_at(i), lds.k[i], lds.vt[i]);
+  wait_vmcnt<2 * Dma<D>::N>();
+  lds_barrier();
+  floatx16 s0[2], s1[2];
+  qk_block<D>(reinterpret_cast<const char*>(lds.k[0]), ls, qreg, s0[0], s0[1]);
+
+  // One step per block position; the scores alternate between s0 and s1.
+  auto step = [&](int idx, floatx16* sc, floatx16* sn) __attribute__((always_inline)) {
+    // block idx + 1 must have landed: its scores are formed in this step
+    if (idx + 2 < nb) wait_vmcnt<Dma<D>::N>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // also: every wave is done with step idx - 1, whose stage the next DMA reuses
+    if (idx + NSTAGE - 1 < nb) {
+      const int st = (idx + NSTAGE - 1) & (NSTAGE - 1);
+      dma_block<D>(rk, rvt, doff, j0 + KB * block_at(idx + NSTAGE - 1), lds.k[st], lds.vt[st]);
+    }
+    const int b = block_at(idx);
+    const int c_lo = KB * b, jb = j0 + c_lo;
+    const bool active = idx < nb && tw < T && c_lo + KB - 1 > r_lo && c_lo <= r_hi + W &&
+                        jb + KB - 1 >= 0 && jb < T;
+    const bool full = c_lo > r_hi && c_lo + KB - 1 <= r_lo + W && jb >= 0 && jb + KB - 1 < T &&
+                      tw + 31 < T;
+    // keys c_lo + key valid for query r: r < c <= r + W and 0 <= j < T
+    const int r = r_lo + col;
+    int lo = max(r + 1 - c_lo, -jb);
+    const int hi = min(r + W - c_lo, T - 1 - jb);
+    KeyRange kr;
+    kr.span = static_cast<unsigned>(hi - lo);
+    if (hi < lo) {
+      lo = 1 << 20;  // no key matches
+      kr.span = 0;
+    }
+    kr.lo = lo - 8 * hh;
+    swa_step<D>(reinterpret_cast<const char*>(lds.k[(idx + 1) & (NSTAGE - 1)]),
+                reinterpret_cast<const char*>(lds.vt[idx & (NSTAGE - 1)]), ls, qreg, sc, sn, o, sm,
+                sl2, active, !full, kr);
+  };
+#pragma unroll 1
+  for (int idx = 0; idx < nb; idx += 2) {
+    step(idx, s0, s1);
+    step(idx + 1, s1, s0);  // past the last block: an inactive step
+  }
+
+  const float tot = sum_halves(sm.l);
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] *= inv;
+
+  if (has_l2 && tw < T) {
+    // Every DMA has completed (the last step waited for all of them) and the
+    // barrier of that step made them visible to the whole workgroup.
+    const int h = bh % l2.H;
+    const float lam = l2.lam[h];
+    const float log2lam = lam > 0.f ? log2f(lam) : -1.0e4f;  // 0^0 = 1, 0^n = 0
+    const float gate = 1.f / (1.f + expf(-l2.g[h]));
+    const int r = r_lo + col;
+    // state term: o^T += S_n^T (fs Q)^T, fs = gate lam^(r+1) per query
+    const float fs = gate * __builtin_amdgcn_exp2f(static_cast<float>(r + 1) * log2lam);
+    const char* sst = reinterpret_cast<const char*>(lds.st);
+    bf16x8 sbuf[2][NDT];
+    TC_SB();
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      sbuf[0][dt] = lds16(sst + (dt >> 1) * (KB * D * 2), ls[0] + 4096u * (dt & 1));
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      TC_SB();
+      if (ks + 1 < NKS) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          sbuf[(ks + 1) & 1][dt] = lds16(sst + (dt >> 1) * (KB * D * 2),
+                                         ls[(ks + 1) & 3] + 8192u * ((ks + 1) >> 2) + 4096u * (dt & 1));
+      }
+      const bf16x8 qs = scale_bf16x8(qreg[ks], fs);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma32(sbuf[ks & 1][dt], qs, o[dt]);
+    }
+    TC_SB();
+    // evictions of the tile: blocks 0..3, resident in stages (nb - 4 + b) % 4
+    const float fe = gate * l2.eta[h];
+#pragma unroll 1
+    for (int b = 0; b < 4; ++b) {
+      const int jb = j0 + KB * b;
+      if (KB * b > r_hi || jb + KB - 1 < 0) continue;  // wave-uniform
+      const int st = (nb - 4 + b) & (NSTAGE - 1);
+      l2_block<D>(reinterpret_cast<const char*>(lds.k[st]), reinterpret_cast<const char*>(lds.vt[st]),
+                  ls, qreg, o, b, jb, r, log2lam, fe);
+    }
+  }
+
+  if (tq < T) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int dv = 32 * dt + 8 * g4 + 4 * hh;
+        const float4 out = make_float4(o[dt][4 * g4], o[dt][4 * g4 + 1], o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]);
+        *reinterpret_cast<float4*>(y + (base + tq) * D + dv) = out;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* vt, const uint16_t* sst,
+                      const float* lam, const float* eta, const float* g, int B, int H, int T, int d,
+                      int W, int Tp, int voff, float scale, float* y, hipStream_t s) {
+  const int n_tiles = (T + MQ - 1) / MQ;
+  const int n_items = B * H * n_tiles;
+  const int grid = (n_items + NXCD - 1) / NXCD * NXCD;
+  const float sl2 = scale * 1.4426950408889634f;
+  const L2Args l2{sst, lam, eta, g, H};
+  if (d == 128)
+    hipLaunchKernelGGL(swa_kernel<128>, dim3(grid), dim3(NTHR), 0, s, q, k, vt, l2, T, W, Tp, voff,
+                       n_tiles, n_items, sl2, y);
+  else if (d == 64)
+    hipLaunchKernelGGL(swa_kernel<64>, dim3(grid), dim3(NTHR), 0, s, q, k, vt, l2, T, W, Tp, voff,
+                       n_tiles, n_items, sl2, y);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace tc
