@@ -23,6 +23,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace tc {
 
 namespace {
@@ -32,6 +34,7 @@ using namespace mf;
 constexpr int NWAVE = 8;
 constexpr int NTHR = 64 * NWAVE;
 constexpr int MQ = 32 * NWAVE;  // queries per tile (must match the main kernel)
+constexpr long kPrepassWorkgroups = 256;  // MI355X: 256 CUs
 
 // Tiles and their evictions; V^T copy geometry.
 struct FusedGeom {
@@ -49,6 +52,15 @@ struct FusedGeom {
     if (b > lim) b = lim;
     return (int)(b < 0 ? 0 : b);
   }
+  // copy columns the pre-pass visits for tile p (keys are column - voff): at
+  // least one 64-column block; the last tile runs to Tp, and together the
+  // tiles cover every column of the copy.
+  __host__ __device__ int col_begin(int p) const { return (key_begin(p) + voff) & ~(KB - 1); }
+  __host__ __device__ int col_end(int p) const {
+    const int e = p == n_tiles - 1 ? Tp : ((key_end(p) + voff + KB - 1) & ~(KB - 1));
+    return e > col_begin(p) ? e : col_begin(p) + KB;
+  }
+  int tiles_per_seg;  // tiles one pre-pass workgroup walks through
 };
 
 // Distribution of the fp32 state S^T (D x D, 32x32 tiles) over the waves.
@@ -142,10 +154,21 @@ __device__ __forceinline__ void state_block_mma(floatx16* acc, const uint16_t* s
   }
 }
 
-// Tile p: contribution of its evictions to the state, from zero, and the V^T
-// copy over columns [floor64(key_begin + voff), ceil64(key_end + voff)) (the
-// last tile: up to Tp), so that every column of the copy is written; keys
-// outside [0, T) are written as zero.
+// Next (tile, column block) of a pre-pass walk: every tile has >= 1 block.
+__device__ __forceinline__ void next_block(const FusedGeom& G, int& p, int& j) {
+  j += KB;
+  if (j >= G.col_end(p)) {
+    ++p;
+    j = G.col_begin(p);
+  }
+}
+
+// Workgroup (segment, b, h) walks tiles_per_seg consecutive tiles.  For each
+// tile p: the contribution of its evictions to the state, from zero,
+// delta_p = sum_j eta lam^(b_p - 1 - j) v_j k_j^T over [a_p, b_p), and the
+// V^T copy of its column blocks (keys outside [0, T) written as zero).  The
+// blocks of all the segment's tiles form one stream with three blocks in
+// flight in registers.
 template <int D>
 __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
@@ -157,16 +180,14 @@ __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(16))) uint16_t sKt[D * SKT];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[D * SKT];
   using ST = StateTiles<D>;
-  const int p = blockIdx.x, bh = blockIdx.y;
+  const int bh = blockIdx.y;
+  const int p_begin = blockIdx.x * G.tiles_per_seg;
+  const int p_end = min(p_begin + G.tiles_per_seg, G.n_tiles);
   const int w = wave_id(), l = lane_id(), col = l & 31, hh = l >> 5;
   const Decay dec(lam[bh % H]);
   const float et = eta[bh % H];
   const long base = (long)bh * G.T;
-  const int a = G.key_begin(p), b = G.key_end(p);
-  const bool last = p == G.n_tiles - 1;
   const int voff = G.voff;
-  const int jbeg = (a + voff) & ~(KB - 1);  // copy columns; the keys are column - voff
-  const int jend = last ? G.Tp : ((b + voff + KB - 1) & ~(KB - 1));
   uint16_t* vt_out = ws_vt + (long)bh * D * G.Tp;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base * D, (uint32_t)G.T * D * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base * D, (uint32_t)G.T * D * 2);
@@ -175,57 +196,81 @@ __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __res
 #pragma unroll
   for (int i = 0; i < ST::TPW; ++i) acc[i] = zero16();
 
-  // three blocks in flight in registers; r0, r1, r2 keep fixed roles (a
-  // register that is the target of a load in flight is never copied) and the
-  // loads are issued on every path so their count is the same everywhere.
-  PairRegs r0 = load_pair<D>(rk, rv, jbeg - voff);
-  PairRegs r1 = load_pair<D>(rk, rv, jbeg - voff + KB);
-  PairRegs r2 = load_pair<D>(rk, rv, jbeg - voff + 2 * KB);
-#define TC_STATE_STEP(R, J)                                                     \
-  if ((J) < jend) {                                                             \
-    lds_barrier();                                                              \
-    store_pair<D, SKT>(R, sKt, sVt, vt_out, G.Tp, (J), voff, a, b, et, dec);    \
-    lds_barrier();                                                              \
-  }                                                                             \
-  R = load_pair<D>(rk, rv, (J) - voff + 3 * KB);                                \
-  if ((J) < jend) state_block_mma<D, SKT>(acc, sKt, sVt);
-  for (int j = jbeg; j < jend; j += 3 * KB) {
-    TC_STATE_STEP(r0, j)
-    TC_STATE_STEP(r1, j + KB)
-    TC_STATE_STEP(r2, j + 2 * KB)
+  // compute cursor (pc, jc) and load cursor (pl, jl), three blocks apart.
+  // r0, r1, r2 keep fixed roles (a register that is the target of a load in
+  // flight is never copied) and the loads are issued on every path, so their
+  // count is the same everywhere; loads past the segment read zeros or data
+  // that is not used.
+  int pc = p_begin, jc = G.col_begin(pc);
+  int pl = pc, jl = jc;
+  PairRegs r0 = load_pair<D>(rk, rv, jl - voff);
+  next_block(G, pl, jl);
+  PairRegs r1 = load_pair<D>(rk, rv, jl - voff);
+  next_block(G, pl, jl);
+  PairRegs r2 = load_pair<D>(rk, rv, jl - voff);
+  next_block(G, pl, jl);
+#define TC_STATE_STEP(R)                                                              \
+  if (pc < p_end) {                                                                   \
+    lds_barrier();                                                                    \
+    store_pair<D, SKT>(R, sKt, sVt, vt_out, G.Tp, jc, voff, G.key_begin(pc),          \
+                       G.key_end(pc), et, dec);                                       \
+    lds_barrier();                                                                    \
+  }                                                                                   \
+  R = load_pair<D>(rk, rv, jl - voff);                                                \
+  next_block(G, pl, jl);                                                              \
+  if (pc < p_end) {                                                                   \
+    state_block_mma<D, SKT>(acc, sKt, sVt);                                           \
+    if (jc + KB >= G.col_end(pc)) {                                                   \
+      float* out = ws_state + ((long)bh * G.n_tiles + pc) * D * D;                    \
+      _Pragma("unroll") for (int i = 0; i < ST::TPW; ++i) {                           \
+        if (ST::owns(w, i)) {                                                         \
+          const int dv0 = ST::dv0(w, i), dk0 = ST::dk0(w, i);                         \
+          _Pragma("unroll") for (int e = 0; e < 16; ++e)                              \
+              out[(dv0 + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + dk0 + col] = acc[i][e]; \
+        }                                                                             \
+        acc[i] = zero16();                                                            \
+      }                                                                               \
+    }                                                                                 \
+    next_block(G, pc, jc);                                                            \
+  }
+  while (pc < p_end) {
+    TC_STATE_STEP(r0)
+    TC_STATE_STEP(r1)
+    TC_STATE_STEP(r2)
   }
 #undef TC_STATE_STEP
-  float* out = ws_state + ((long)bh * G.n_tiles + p) * D * D;
-#pragma unroll
-  for (int i = 0; i < ST::TPW; ++i) {
-    if (!ST::owns(w, i)) continue;
-    const int dv0 = ST::dv0(w, i), dk0 = ST::dk0(w, i);
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      out[(dv0 + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + dk0 + col] = acc[i][e];
-  }
 }
 
 // S_0 = 0, S_{p+1} = lam^len(p) S_p + delta_p; element idx = dv * D + dk of
-// S^T.  Entering states go out as bf16 (round to nearest even), the final
-// state as fp32 A[dk][dv].
+// S^T, four consecutive elements per thread.  Entering states go out as bf16
+// (round to nearest even), the final state as fp32 A[dk][dv].
 __global__ void fused_prefix_kernel(const float* __restrict__ lam, int H, int D, FusedGeom G,
                                     const float* __restrict__ delta, uint16_t* __restrict__ sst,
                                     float* __restrict__ A_final) {
-  const int n_el = D * D;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int n_el = D * D, n4 = n_el / 4;
+  const int i4 = blockIdx.x * blockDim.x + threadIdx.x;
   const int bh = blockIdx.y;
-  if (idx >= n_el) return;
+  if (i4 >= n4) return;
   const Decay dec(lam[bh % H]);
-  const float* dp = delta + (long)bh * G.n_tiles * n_el + idx;
-  uint16_t* sp = sst + (long)bh * G.n_tiles * n_el + idx;
-  float run = 0.f;
-#pragma unroll 4
+  const float4* dp = reinterpret_cast<const float4*>(delta + (long)bh * G.n_tiles * n_el) + i4;
+  uint2* sp = reinterpret_cast<uint2*>(sst + (long)bh * G.n_tiles * n_el) + i4;
+  float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 16
   for (int p = 0; p < G.n_tiles; ++p) {
-    sp[(long)p * n_el] = f32_to_bf16(run);
-    run = dec(G.key_end(p) - G.key_begin(p)) * run + dp[(long)p * n_el];
+    sp[(long)p * n4] = make_uint2(pack_bf16x2(run.x, run.y), pack_bf16x2(run.z, run.w));
+    const float d = dec(G.key_end(p) - G.key_begin(p));
+    const float4 x = dp[(long)p * n4];
+    run = make_float4(fmaf(d, run.x, x.x), fmaf(d, run.y, x.y), fmaf(d, run.z, x.z), fmaf(d, run.w, x.w));
   }
-  if (A_final != nullptr) A_final[(long)bh * n_el + (idx % D) * D + idx / D] = run;
+  if (A_final != nullptr) {
+    float* af = A_final + (long)bh * n_el;
+    const float r4[4] = {run.x, run.y, run.z, run.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = 4 * i4 + c;
+      af[(idx % D) * D + idx / D] = r4[c];
+    }
+  }
 }
 
 FusedGeom make_geom(int T, int W) {
@@ -235,6 +280,7 @@ FusedGeom make_geom(int T, int W) {
   G.voff = W & 7;
   G.Tp = (T + G.voff + KB - 1) / KB * KB;
   G.n_tiles = (T + MQ - 1) / MQ;
+  G.tiles_per_seg = 1;
   return G;
 }
 
@@ -249,9 +295,14 @@ hipError_t run_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
   float* delta = static_cast<float*>(ws);
   uint16_t* sst = reinterpret_cast<uint16_t*>(delta + ne);
   uint16_t* vt = sst + ne;
-  hipLaunchKernelGGL(fused_state_kernel<D>, dim3(G.n_tiles, BH), dim3(NTHR), 0, s, k, v, lam, eta, H,
-                     G, delta, vt);
-  hipLaunchKernelGGL(fused_prefix_kernel, dim3((D * D + 255) / 256, BH), dim3(256), 0, s, lam, H, D,
+  // about one pre-pass workgroup per CU, each streaming several tiles
+  FusedGeom Gs = G;
+  const long units = (long)G.n_tiles * BH;
+  Gs.tiles_per_seg = (int)std::max<long>(1, (units + kPrepassWorkgroups - 1) / kPrepassWorkgroups);
+  const int n_seg = (G.n_tiles + Gs.tiles_per_seg - 1) / Gs.tiles_per_seg;
+  hipLaunchKernelGGL(fused_state_kernel<D>, dim3(n_seg, BH), dim3(NTHR), 0, s, k, v, lam, eta, H, Gs,
+                     delta, vt);
+  hipLaunchKernelGGL(fused_prefix_kernel, dim3((D * D / 4 + 63) / 64, BH), dim3(64), 0, s, lam, H, D,
                      G, delta, sst, A_final);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

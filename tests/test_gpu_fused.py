@@ -29,6 +29,8 @@ def run(x, W, g=None, scale=None):
     (1, 2, 64, 64, 64),
     (1, 1, 1, 128, 4),
     (1, 3, 1100, 128, 1024),
+    (1, 32, 2100, 64, 100),  # > 256 tiles: the pre-pass walks two tiles per workgroup
+    (1, 32, 2100, 64, 700),  # ... with tiles that write no evictions, W % 8 != 0
 ])
 def test_fused_small(B, H, T, d, W):
     print(f"[case] fused B={B} H={H} T={T} d={d} W={W}", flush=True)
