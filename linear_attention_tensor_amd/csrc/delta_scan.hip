@@ -188,13 +188,18 @@ hipError_t dispatch_delta(const void* q, const void* k, const void* v, const flo
 
 }  // namespace
 
-size_t delta_ws_bytes(int, int, int, int, int) { return 0; }
+size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, bool bf16) {
+  (void)dv;
+  return delta_bf16_supported(bf16, dk) ? delta_bf16_ws_bytes(B, H, T, dk) : 0;
+}
 
 hipError_t launch_delta_scan(const void* q, const void* k, const void* v, bool bf16,
                              const float* beta, int B, int H, int T, int dk, int dv,
                              const float* S0, float* o, float* S_final, void* ws, hipStream_t s) {
-  (void)ws;
   (void)dv;
+  if (delta_bf16_supported(bf16, dk))
+    return launch_delta_bf16(q, k, v, beta, B, H, T, dk, S0, o, S_final, ws, s);
+  (void)ws;
   if (bf16) return dispatch_delta<uint16_t>(q, k, v, beta, B, H, T, dk, S0, o, S_final, s);
   return dispatch_delta<float>(q, k, v, beta, B, H, T, dk, S0, o, S_final, s);
 }

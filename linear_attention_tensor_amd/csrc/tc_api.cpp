@@ -174,7 +174,7 @@ tc_status tc_fused_layer(const void* q, const void* k, const void* v, tc_dtype d
 size_t delta_scan_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt) {
   if (check_seq("delta_scan_workspace_bytes", B, H, T, dk, dv, chunk, dt) != TC_OK) return SIZE_MAX;
   ok();
-  return tc::delta_ws_bytes(B, H, T, dk, dv);
+  return tc::delta_ws_bytes(B, H, T, dk, dv, dt == TC_BF16);
 }
 
 tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dtype dt,
@@ -188,7 +188,7 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
     if (B == 0 || H == 0) return ok();
     if (T > 0 && (!q || !k || !v || !beta || !o))
       return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, beta, o must not be NULL", fn);
-    const size_t need = tc::delta_ws_bytes(B, H, T, dk, dv);
+    const size_t need = tc::delta_ws_bytes(B, H, T, dk, dv, dt == TC_BF16);
     if (ws_bytes < need)
       return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);

@@ -42,9 +42,16 @@ hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* vt, 
                       const float* lam, const float* eta, const float* g, int B, int H, int T, int d,
                       int W, int Tp, int voff, float scale, float* y, hipStream_t s);
 
-size_t delta_ws_bytes(int B, int H, int T, int dk, int dv);
+size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, bool bf16);
 hipError_t launch_delta_scan(const void* q, const void* k, const void* v, bool bf16,
                              const float* beta, int B, int H, int T, int dk, int dv,
                              const float* S0, float* o, float* S_final, void* ws, hipStream_t s);
+// bf16 inputs with d in {64, 128} (delta_bf16.hip): bf16 MFMA with split
+// operands; launch_delta_scan dispatches to it.
+bool delta_bf16_supported(bool bf16, int d);
+size_t delta_bf16_ws_bytes(int B, int H, int T, int d);
+hipError_t launch_delta_bf16(const void* q, const void* k, const void* v, const float* beta, int B,
+                             int H, int T, int d, const float* S0, float* o, float* S_final, void* ws,
+                             hipStream_t s);
 
 }  // namespace tc
