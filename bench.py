@@ -55,6 +55,15 @@ def fused_flops(B, H, T, d, W, C=64):
     return B * H * (l1 + l2)
 
 
+def fused_main_flops(B, H, T, d, W, C=64):
+    """Algorithmic work of the fused layer's main kernel: the L1 window
+    softmax (4 d per pair) plus the L2 read per active token, (C+1)(dk+dv)
+    intra-chunk and 2 dk dv for q.S; the state writes (2 dk dv per eviction)
+    belong to the pre-pass."""
+    pairs = sum(min(W, t + 1) for t in range(min(T, W))) + max(T - W, 0) * W
+    return B * H * (4 * d * pairs + max(T - W, 0) * ((C + 1) * 2 * d + 2 * d * d))
+
+
 def fused_bytes(B, H, T, d):
     return B * H * T * (3 * d * 2 + d * 4)  # q, k, v bf16 in, y fp32 out
 
@@ -82,7 +91,9 @@ def delta_flops(B, H, T, d):
 
 # ----------------------------------------------------------------------------- timing
 
-def time_calls(fn, steps, warmup):
+def time_calls(fn, steps, warmup, kernel_timer=None):
+    """Whole-call time per step (events bracketing the K steps) and, when a
+    KernelTimer is given, the mean duration of the main kernel of each call."""
     import torch
 
     for _ in range(warmup):
@@ -94,6 +105,8 @@ def time_calls(fn, steps, warmup):
     torch.cuda.synchronize()
     t_start.record()
     for i, (a, b) in enumerate(ev):
+        if kernel_timer is not None:
+            kernel_timer.arm(i)
         a.record()
         fn(i)
         b.record()
@@ -101,7 +114,68 @@ def time_calls(fn, steps, warmup):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
     total = t_start.elapsed_time(t_end)
-    return total / steps, sum(per) / len(per), per
+    kernel_ms = kernel_timer.mean_ms() if kernel_timer is not None else None
+    return total / steps, sum(per) / len(per), kernel_ms
+
+
+class KernelTimer:
+    """HIP events recorded by the library around an entry point's main kernel
+    (tc_profile_next_call), on the stream that kernel is launched on."""
+
+    def __init__(self, n):
+        import ctypes
+
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append((a, b))
+
+    def arm(self, i):
+        from linear_attention_tensor_amd import _lib
+
+        a, b = self.ev[i]
+        _lib.check("tc_profile_next_call", _lib.lib().tc_profile_next_call(a, b))
+
+    def mean_ms(self):
+        import ctypes
+
+        out = []
+        for a, b in self.ev:
+            ms = ctypes.c_float()
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b):
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        for a, b in self.ev:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+        return sum(out) / len(out)
+
+
+def traffic_from_profile(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/traffic_<kernel>_fused_layer_bf16.txt), or None when
+    there is none or its source hash no longer matches the kernel source."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_fused_layer_bf16.txt")
+    src = os.path.join(ROOT, "linear_attention_tensor_amd", "csrc", "tc_swa.hip")
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("source_sha256_16") != digest or "hbm_bytes_per_launch" not in fields:
+        return None
+    return float(fields["hbm_bytes_per_launch"])
 
 
 def roofline(bound, achieved, peak, unit, traffic=None):
@@ -149,13 +223,19 @@ def bench_fused(steps, warmup, dev):
         if s != 0:
             raise RuntimeError(ops._lib.last_error())
 
-    ms, ms_call, _ = time_calls(call, steps, warmup)
+    kt = KernelTimer(steps)
+    ms, ms_call, kernel_ms = time_calls(call, steps, warmup, kt)
     tokens = w.B * w.H * w.T
     flops = fused_flops(w.B, w.H, w.T, w.d, w.W)
+    main_flops = fused_main_flops(w.B, w.H, w.T, w.d, w.W)
     res = {
         "workload": w.name, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
-        "roofline": roofline("mfma", flops / (ms_call * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
-        "algorithmic_flops": flops, "algorithmic_bytes": fused_bytes(w.B, w.H, w.T, w.d),
+        "roofline": roofline("mfma", main_flops / (kernel_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s",
+                             traffic_from_profile("swa_kernel")),
+        "main_kernel": {"name": "swa_kernel<128>", "ms": kernel_ms, "algorithmic_flops": main_flops},
+        "layer": {"ms_per_call": ms_call, "algorithmic_flops": flops,
+                  "tflops": flops / (ms_call * 1e-3) / 1e12,
+                  "algorithmic_bytes": fused_bytes(w.B, w.H, w.T, w.d)},
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "chunk": 64,
                    "dtype_in": "bf16", "state": "fp32"},
     }
@@ -184,7 +264,7 @@ def bench_scan(steps, warmup, dev):
         if lib.tc_scan_forward(*args) != 0:
             raise RuntimeError(ops._lib.last_error())
 
-    ms, ms_call, _ = time_calls(call, steps, warmup)
+    ms, ms_call, kernel_ms = time_calls(call, steps, warmup, KernelTimer(steps))
     flops = scan_flops(w.B, w.H, w.T, w.d, w.W)
     nbytes = scan_bytes(w.B, w.H, w.T, w.d, 4)
     tf = flops / (ms_call * 1e-3) / 1e12
@@ -192,6 +272,7 @@ def bench_scan(steps, warmup, dev):
     return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
             "roofline": roofline("mfma", tf, PEAK_FP32_TFLOPS, "TFLOP/s"),
             "hbm": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
+            "main_kernel": {"name": "scan_output_kernel", "ms": kernel_ms}, "ms_per_call": ms_call,
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
 
 
@@ -239,12 +320,13 @@ def bench_decode(steps, warmup, dev, n_steps=4096):
             raise RuntimeError(ops._lib.last_error())
 
     # warmup steps advance the stream position too; the timed steps continue from there
-    ms, ms_call, _ = time_calls(call, n_steps, warmup)
+    ms, ms_call, kernel_ms = time_calls(call, n_steps, warmup, KernelTimer(n_steps))
     per_head = decode_bytes_per_head(d)
-    gbs = B * H * per_head / (ms_call * 1e-3) / 1e9
+    gbs = B * H * per_head / (kernel_ms * 1e-3) / 1e9
     return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": B * H / (ms * 1e-3),
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
-            "note": "A (128 MiB) fits the 256 MB Infinity Cache; GB/s is algorithmic bytes / time",
+            "note": "A (128 MiB) fits the 256 MB Infinity Cache; GB/s is algorithmic bytes / kernel time",
+            "main_kernel": {"name": "decode_kernel", "ms": kernel_ms}, "ms_per_call": ms_call,
             "config": {"B": B, "H": H, "d": d, "W": W, "steps": n_steps, "dtype_in": "bf16"}}
 
 
@@ -270,33 +352,37 @@ def bench_delta(steps, warmup, dev):
         if lib.delta_scan_forward(*args) != 0:
             raise RuntimeError(ops._lib.last_error())
 
-    ms, ms_call, _ = time_calls(call, steps, warmup)
+    ms, ms_call, kernel_ms = time_calls(call, steps, warmup, KernelTimer(steps))
     nbytes = delta_bytes(w.B, w.H, w.T, w.d)
     gbs = nbytes / (ms_call * 1e-3) / 1e9
     tf = delta_flops(w.B, w.H, w.T, w.d) / (ms_call * 1e-3) / 1e12
     return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
             "mfma": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s"),
+            "main_kernel": {"name": "delta_main_kernel<128>", "ms": kernel_ms}, "ms_per_call": ms_call,
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "bf16"}}
 
 
-def cpu_baseline_fused(x, T_sample=4096):
-    """The float64 oracle on a bounded prefix of the same input."""
+def cpu_baseline_fused(x, T_sample=16384):
+    """The float64 oracle (as it stands) on a bounded prefix of the same
+    input, with its BLAS pinned to one thread."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     from oracle import tc as O
 
     w_W = 1024
     sl = (slice(None), slice(None), slice(0, T_sample))
-    t0 = time.perf_counter()
-    O.tc_fused(x["q64"][sl], x["k64"][sl], x["v64"][sl], x["lam"].astype(np.float64), x["eta"],
-               x["g"].astype(np.float64), w_W)
-    dt = time.perf_counter() - t0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.tc_fused(x["q64"][sl], x["k64"][sl], x["v64"][sl], x["lam"].astype(np.float64), x["eta"],
+                   x["g"].astype(np.float64), w_W)
+        dt = time.perf_counter() - t0
     B, H = x["q64"].shape[:2]
     return {"value": B * H * T_sample / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fused layer oracle (NumPy float64, single thread) on the first {T_sample} tokens "
-                      f"of all {B * H} heads of the same input ({dt:.1f} s; the first {w_W} tokens have "
-                      f"shorter windows)"}
+            "sample": f"fused layer oracle (NumPy float64, BLAS limited to 1 thread) on the first {T_sample} "
+                      f"tokens of all {B * H} heads of the same input ({dt:.1f} s; the first {w_W} tokens "
+                      f"have shorter windows)"}
 
 
 def main():
@@ -341,6 +427,8 @@ def main():
         "data": "synthetic (seeded N(0,1/d) q,k,v with unit keys; per-head lam, eta, g)",
         "config": head["config"],
         "roofline": head["roofline"],
+        "main_kernel": head["main_kernel"],
+        "layer": head["layer"],
     }
     if components:
         line["components"] = components

@@ -137,6 +137,22 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
 /* Workspace queries return SIZE_MAX when the arguments are invalid or
  * unsupported (tc_last_error() says why). */
 
+/* ---------------------------------------------------------------------------
+ * Timing hook for benchmarks (no counterpart on the pages).  Arms the calling
+ * thread so that its next entry-point call that launches work records
+ * `before` on that call's stream just before the entry point's main kernel
+ * and `after` just after it:
+ *   tc_fused_layer      the window-attention + L2-read kernel,
+ *   tc_scan_forward     the output kernel,
+ *   tc_decode_step      its only kernel,
+ *   delta_scan_forward  the kernel that walks the chunks.
+ * `before` and `after` are caller-created HIP events (hipEventCreate); the
+ * caller reads hipEventElapsedTime(before, after) once the stream is done.
+ * The hook is consumed by that call; NULL, NULL disarms it.  Exactly one
+ * NULL is TC_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------- */
+tc_status tc_profile_next_call(hipEvent_t before, hipEvent_t after);
+
 const char* tc_last_error(void); /* thread-local; "" when the last call was OK */
 const char* tc_version(void);
 

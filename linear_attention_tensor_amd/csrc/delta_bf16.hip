@@ -390,8 +390,10 @@ hipError_t run_delta_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* 
                        a_ws, kt_ws);
   const int n_items = BH * (D / DVT);
   const int grid = (n_items + NXCD - 1) / NXCD * NXCD;
+  profile_mark_before(s);
   hipLaunchKernelGGL(delta_main_kernel<D>, dim3(grid), dim3(256), 0, s, q, k, v, a_ws, kt_ws, T,
                      n_chunks, n_items, S0, o, S_final);
+  profile_mark_after(s);
   return hipGetLastError();
 }
 

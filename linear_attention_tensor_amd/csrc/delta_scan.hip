@@ -172,8 +172,10 @@ hipError_t dispatch_delta(const void* q, const void* k, const void* v, const flo
   const int BH = B * H;
 #define TC_DELTA_CASE(DK, DVT)                                                               \
   case DK:                                                                                   \
+    profile_mark_before(s);                                                                  \
     hipLaunchKernelGGL((delta_kernel<DK, DVT, TIn>), dim3(DK / DVT, BH), dim3(256), 0, s, Q, K, \
                        V, beta, T, d, S0, o, S_final);                                        \
+    profile_mark_after(s);                                                                   \
     break;
   switch (d) {
     TC_DELTA_CASE(16, 16)

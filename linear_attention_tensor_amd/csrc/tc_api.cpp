@@ -15,6 +15,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_prof_before = nullptr, g_prof_after = nullptr;
 
 tc_status fail(tc_status st, const char* fmt, ...) {
   va_list ap;
@@ -54,7 +55,9 @@ tc_status check_seq(const char* fn, int B, int H, int T, int dk, int dv, int chu
 template <typename F>
 tc_status guarded(const char* fn, F&& f) {
   try {
-    return f();
+    const tc_status st = f();
+    if (st == TC_OK || st == TC_ERR_HIP) g_prof_before = g_prof_after = nullptr;  // hook consumed
+    return st;
   } catch (const std::exception& e) {
     return fail(TC_ERR_INTERNAL, "%s: %s", fn, e.what());
   } catch (...) {
@@ -64,7 +67,24 @@ tc_status guarded(const char* fn, F&& f) {
 
 }  // namespace
 
+namespace tc {
+void profile_mark_before(hipStream_t s) {
+  if (g_prof_before != nullptr) (void)hipEventRecord(g_prof_before, s);
+}
+void profile_mark_after(hipStream_t s) {
+  if (g_prof_after != nullptr) (void)hipEventRecord(g_prof_after, s);
+}
+}  // namespace tc
+
 extern "C" {
+
+tc_status tc_profile_next_call(hipEvent_t before, hipEvent_t after) {
+  if ((before == nullptr) != (after == nullptr))
+    return fail(TC_ERR_INVALID_ARG, "tc_profile_next_call: pass two events or none");
+  g_prof_before = before;
+  g_prof_after = after;
+  return ok();
+}
 
 const char* tc_last_error(void) { return g_err; }
 

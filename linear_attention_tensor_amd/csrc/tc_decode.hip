@@ -100,6 +100,7 @@ hipError_t launch_tc_decode(const void* q, const void* k, const void* v, bool bf
                             const int64_t* pos, int B, int H, int dk, int dv, int W, float* m,
                             hipStream_t s) {
   const dim3 grid(B * H), block(256);
+  profile_mark_before(s);
   if (bf16) {
     hipLaunchKernelGGL(decode_kernel<uint16_t>, grid, block, 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
@@ -111,6 +112,7 @@ hipError_t launch_tc_decode(const void* q, const void* k, const void* v, bool bf
                        static_cast<float*>(ring_k), static_cast<float*>(ring_v), A, lam, eta, pos,
                        H, dk, dv, W, m);
   }
+  profile_mark_after(s);
   return hipGetLastError();
 }
 

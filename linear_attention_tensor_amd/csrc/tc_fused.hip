@@ -306,7 +306,10 @@ hipError_t run_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
                      G, delta, sst, A_final);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_swa(q, k, vt, sst, lam, eta, g, B, H, G.T, D, G.W, G.Tp, G.voff, scale, y, s);
+  profile_mark_before(s);
+  const hipError_t e2 = launch_swa(q, k, vt, sst, lam, eta, g, B, H, G.T, D, G.W, G.Tp, G.voff, scale, y, s);
+  profile_mark_after(s);
+  return e2;
 }
 
 }  // namespace

@@ -31,6 +31,11 @@ hipError_t launch_tc_decode(const void* q, const void* k, const void* v, bool bf
                             const int64_t* pos, int B, int H, int dk, int dv, int W, float* m,
                             hipStream_t s);
 
+// Benchmark timing hook (armed by tc_profile_next_call, tc_api.cpp): record
+// the armed events around an entry point's main kernel, on its stream.
+void profile_mark_before(hipStream_t s);
+void profile_mark_after(hipStream_t s);
+
 size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W);
 hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const float* lam,
                            const float* eta, const float* g, int B, int H, int T, int d, int W,

@@ -278,8 +278,10 @@ hipError_t run_scan(const TIn* q, const TIn* k, const TIn* v, const float* lam, 
                        p.seg_chunks * CH, p.n_seg, ws);
   }
   dim3 g3(p.n_seg, nvt, BH);
+  profile_mark_before(s);
   hipLaunchKernelGGL((scan_output_kernel<DK, DVT, TIn>), g3, dim3(256), 0, s, q, k, v, lam, eta,
                      H, T, dv, W, p.n_act, p.seg_chunks, p.n_seg, ws, m, A_final);
+  profile_mark_after(s);
   return hipGetLastError();
 }
 

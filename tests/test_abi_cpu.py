@@ -136,3 +136,13 @@ def test_delta_rejects():
     assert call(beta=NULL) == _lib.TC_ERR_INVALID_ARG
     assert call(d=24) == _lib.TC_ERR_UNSUPPORTED
     assert call(B=0) == _lib.TC_OK
+
+
+def test_profile_hook_argument_check():
+    L = _lib.lib()
+    fake = ctypes.c_void_p(0x1000)  # never used: the call with one NULL is rejected first
+    assert L.tc_profile_next_call(fake, None) == _lib.TC_ERR_INVALID_ARG
+    assert "two events" in _lib.last_error()
+    assert L.tc_profile_next_call(None, fake) == _lib.TC_ERR_INVALID_ARG
+    assert L.tc_profile_next_call(None, None) == _lib.TC_OK  # disarmed
+    assert _lib.last_error() == ""
