@@ -136,6 +136,25 @@ __device__ __forceinline__ void dma_state(i32x4 dst_desc, uint16_t* sst) {
   }
 }
 
+// One block's DMA, issued one instruction at a time across a step so that
+// the workgroup's 32 copy instructions do not all queue at the same moment.
+template <int D>
+struct DmaJob {
+  i32x4 dk, dvt;
+  int koff, voff;     // block start in bytes: j * D * 2 (K rows), j * 2 (V^T columns)
+  uint16_t *sk, *svt;
+  bool on;            // a block is left to fetch
+};
+template <int D, int I>
+__device__ __forceinline__ void dma_part(const DmaJob<D>& job, const DmaOff<D>& off) {
+  if (!job.on) return;
+  const int w = wave_id();
+  if constexpr (I < Dma<D>::NK)
+    dma16(job.dk, job.sk + (I * NWAVE + w) * 512, off.k[I] + job.koff);
+  else
+    dma16(job.dvt, job.svt + ((I - Dma<D>::NK) * NWAVE + w) * 512, off.v[I - Dma<D>::NK] + job.voff);
+}
+
 // max / sum over the two 32-lane halves (the two halves of a query's keys)
 __device__ __forceinline__ float max_halves(float x) {
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
@@ -253,9 +272,17 @@ __device__ __forceinline__ bf16x8 probs(const floatx16* sc, float sl2, float nms
 template <int D>
 __device__ __forceinline__ void swa_step(const char* sk_nxt, const char* svt_cur, const uint32_t* ls,
                                          const bf16x8* qreg, floatx16* sc, floatx16* sn, floatx16* o,
-                                         Softmax& sm, float sl2, bool active, bool masked, KeyRange kr) {
+                                         Softmax& sm, float sl2, bool active, bool masked, KeyRange kr,
+                                         const DmaJob<D>& job, const DmaOff<D>& doff) {
   constexpr int NDT = D / 32;
+  constexpr int ND = Dma<D>::N;  // 4 for D = 128, 2 for D = 64
   if (!active) {
+    dma_part<D, 0>(job, doff);
+    dma_part<D, 1>(job, doff);
+    if constexpr (ND > 2) {
+      dma_part<D, 2>(job, doff);
+      dma_part<D, 3>(job, doff);
+    }
     qk_block<D>(sk_nxt, ls, qreg, sn[0], sn[1]);
     return;
   }
@@ -275,6 +302,8 @@ __device__ __forceinline__ void swa_step(const char* sk_nxt, const char* svt_cur
   TC_SB();
   ld_k2<0>(sk_nxt, ls, ka);
   TC_SB();
+  dma_part<D, 0>(job, doff);
+  TC_SB();
   ld_k2<2>(sk_nxt, ls, kb);
   mm_k2<0>(ka, qreg, a0, a1);
 #pragma unroll
@@ -286,6 +315,8 @@ __device__ __forceinline__ void swa_step(const char* sk_nxt, const char* svt_cur
   TC_GROUPS(4, 4, D == 128 ? 2 : 4);
   TC_SB();
   if constexpr (D == 128) {
+    dma_part<D, 1>(job, doff);
+    TC_SB();
     ld_k2<4>(sk_nxt, ls, ka);
     mm_k2<2>(kb, qreg, a0, a1);
 #pragma unroll
@@ -312,6 +343,8 @@ __device__ __forceinline__ void swa_step(const char* sk_nxt, const char* svt_cur
   bf16x8 va[NDT], vb[NDT];
   bf16x8 p0, p1, p2, p3;
   if constexpr (D == 128) {
+    dma_part<D, 2>(job, doff);
+    TC_SB();
     ld_k2<6>(sk_nxt, ls, kb);
     mm_k2<4>(ka, qreg, a0, a1);
     p0 = probs<0>(sc, sl2, nms, psum);
@@ -320,6 +353,8 @@ __device__ __forceinline__ void swa_step(const char* sk_nxt, const char* svt_cur
     ld_v<D>(svt_cur, ls[0], va);
     mm_k2<6>(kb, qreg, a0, a1);
   } else {
+    dma_part<D, 1>(job, doff);
+    TC_SB();
     ld_v<D>(svt_cur, ls[0], va);
     mm_k2<2>(kb, qreg, a0, a1);
     p0 = probs<0>(sc, sl2, nms, psum);
@@ -329,6 +364,10 @@ __device__ __forceinline__ void swa_step(const char* sk_nxt, const char* svt_cur
   p1 = probs<1>(sc, sl2, nms, psum);
   if constexpr (D == 128) {
     TC_GROUPS(NDT, 4, 6);
+    TC_SB();
+  }
+  if constexpr (D == 128) {
+    dma_part<D, 3>(job, doff);
     TC_SB();
   }
   ld_v<D>(svt_cur, ls[1], vb);
@@ -489,9 +528,11 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
     if (idx + 2 < nb) wait_vmcnt<Dma<D>::N>();
     else wait_vmcnt<0>();
     lds_barrier();  // also: every wave is done with step idx - 1, whose stage the next DMA reuses
-    if (idx + NSTAGE - 1 < nb) {
+    DmaJob<D> job;
+    {
       const int st = (idx + NSTAGE - 1) & (NSTAGE - 1);
-      dma_block<D>(rk, rvt, doff, j0 + KB * block_at(idx + NSTAGE - 1), lds.k[st], lds.vt[st]);
+      const int jn = j0 + KB * block_at(idx + NSTAGE - 1);
+      job = DmaJob<D>{rk, rvt, jn * D * 2, jn * 2, lds.k[st], lds.vt[st], idx + NSTAGE - 1 < nb};
     }
     const int b = block_at(idx);
     const int c_lo = KB * b, jb = j0 + c_lo;
@@ -512,7 +553,7 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
     kr.lo = lo - 8 * hh;
     swa_step<D>(reinterpret_cast<const char*>(lds.k[(idx + 1) & (NSTAGE - 1)]),
                 reinterpret_cast<const char*>(lds.vt[idx & (NSTAGE - 1)]), ls, qreg, sc, sn, o, sm,
-                sl2, active, !full, kr);
+                sl2, active, !full, kr, job, doff);
   };
 #pragma unroll 1
   for (int idx = 0; idx < nb; idx += 2) {
