@@ -492,10 +492,14 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
 
   const int t0 = tile * MQ;
   const int j0 = t0 - W;
-  const int tw = t0 + 32 * w;  // first query of this wave
+  // Query slice of this wave.  Waves w and w + 4 share a SIMD and slice s
+  // needs floor(s / 2) + 1 blocks in the L2 epilogue, so the slices 0..3
+  // pair with 7..4 to give every SIMD the same epilogue work.
+  const int slice = w < 4 ? w : 11 - w;
+  const int r_lo = 32 * slice, r_hi = r_lo + 31;
+  const int tw = t0 + r_lo;    // first query of this wave
   const int tq = tw + col;     // this lane's query
   const int nb = (W + MQ + KB - 1) / KB;  // >= 5
-  const int r_lo = 32 * w, r_hi = r_lo + 31;
   // the tile writes evictions into the L2 memory iff some key j0 .. j0 + 255 is >= 0
   const bool has_l2 = l2.sst != nullptr && j0 + MQ > 0;
   // blocks 4 .. nb-1 first, then 0 .. 3 (left resident for the L2 epilogue)
@@ -512,20 +516,29 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int j = 0; j < 4; ++j) ls[j] = lane_slot(j);
 
-  // the state is used last but loaded first: the loads below complete in order
-  if (has_l2) dma_state<D>(raw_desc(l2.sst + ((long)bh * n_tiles + tile) * D * D, D * D * 2), lds.st);
+  // Copies complete in issue order: blocks 0..2, then the state (used only in
+  // the epilogue), so the first waits do not include it.
+  constexpr int NS = D * D / 8 / NTHR;  // state copy instructions per thread
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
     dma_block<D>(rk, rvt, doff, j0 + KB * block_at(i), lds.k[i], lds.vt[i]);
-  wait_vmcnt<2 * Dma<D>::N>();
+  if (has_l2) {
+    dma_state<D>(raw_desc(l2.sst + ((long)bh * n_tiles + tile) * D * D, D * D * 2), lds.st);
+    wait_vmcnt<2 * Dma<D>::N + NS>();
+  } else {
+    wait_vmcnt<2 * Dma<D>::N>();
+  }
   lds_barrier();
   floatx16 s0[2], s1[2];
   qk_block<D>(reinterpret_cast<const char*>(lds.k[0]), ls, qreg, s0[0], s0[1]);
 
   // One step per block position; the scores alternate between s0 and s1.
   auto step = [&](int idx, floatx16* sc, floatx16* sn) __attribute__((always_inline)) {
-    // block idx + 1 must have landed: its scores are formed in this step
-    if (idx + 2 < nb) wait_vmcnt<Dma<D>::N>();
+    // block idx + 1 must have landed: its scores are formed in this step.
+    // Outstanding copies allowed: block idx + 2, and for idx < 2 the state,
+    // which was issued between blocks 2 and 3.
+    if (idx < 2 && has_l2) wait_vmcnt<Dma<D>::N + NS>();
+    else if (idx + 2 < nb) wait_vmcnt<Dma<D>::N>();
     else wait_vmcnt<0>();
     lds_barrier();  // also: every wave is done with step idx - 1, whose stage the next DMA reuses
     DmaJob<D> job;
