@@ -35,7 +35,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed calls first: the GPU needs some tens of ms of load to reach its steady clock")
     ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fused", "scan", "decode", "delta"], default=None,
