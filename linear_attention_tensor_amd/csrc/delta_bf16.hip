@@ -13,7 +13,8 @@
 //   O = Q S0^T + tril_0(Q K^T) U,      S = S0 + U^T K.
 // A depends on K and beta only, so it is computed for every chunk at once:
 //   delta_prep   per (chunk, b, h): A by forward substitution (fp32), stored
-//                as a bf16 pair A = A_hi + A_lo, and K^T of the chunk;
+//                as a bf16 pair A = A_hi + A_lo, K^T of the chunk and
+//                tril_0(Q K^T) (bf16; it depends on q and k only);
 //   delta_main   per (b, h, 16-row slice of S): walks the chunks in order.
 // The rows of S are independent (row j only sees column j of V and U), so
 // the slices need no communication.  The terms that feed the recurrence (K
@@ -46,7 +47,7 @@ __device__ __forceinline__ i32x4 raw_desc(const void* base, uint32_t nbytes) {
 
 // 16 bytes per lane global -> LDS (lane i writes lds_base + 16 i), issued as
 // inline asm so the compiler adds no wait for it before LDS reads and
-// barriers; the kernel orders it with s_waitcnt vmcnt(0) and a barrier.  No
+// barriers; the kernel orders it with s_waitcnt vmcnt(n) and a barrier.  No
 // register is written and the operands are read when the instruction issues.
 __device__ __forceinline__ void dma16(i32x4 desc, const void* lds_base, int voffset) {
   const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
@@ -78,6 +79,9 @@ __device__ __forceinline__ int epos(int r, int col) {
   return pos<NCH>(r, col >> 3) + (col & 7);
 }
 
+// scheduling fence: keeps operand reads ahead of the MFMAs that use them
+#define TC_SB() __builtin_amdgcn_sched_barrier(0)
+
 __device__ __forceinline__ floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -91,18 +95,25 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
 // ---------------------------------------------------------------------------
 // delta_prep: one wave per (chunk, b, h).
 template <int D>
-__global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restrict__ q,
+                                                        const uint16_t* __restrict__ k,
                                                         const float* __restrict__ beta, int T,
                                                         int n_chunks, uint16_t* __restrict__ a_out,
-                                                        uint16_t* __restrict__ kt_out) {
+                                                        uint16_t* __restrict__ kt_out,
+                                                        uint16_t* __restrict__ qm_out) {
   constexpr int NCH = D / 8;
   constexpr int LS = CH + 4;  // fp32 L rows, 16-byte aligned
   __shared__ __attribute__((aligned(16))) uint16_t sK[CH * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[CH * D];
   __shared__ __attribute__((aligned(16))) float sL[CH * LS];
   __shared__ float sB[CH];
   const int n = blockIdx.x, bh = blockIdx.y, l = threadIdx.x;
   const int t0 = n * CH;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (long)bh * T * D, (uint32_t)T * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (long)bh * T * D, (uint32_t)T * D * 2);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    *reinterpret_cast<uint4*>(sQ + pos<NCH>(l, c)) = buf_load16(rq, ((t0 + l) * D + 8 * c) * 2);
   // lane l: key t0 + l (zero past T)
   uint4 kr[NCH];
 #pragma unroll
@@ -142,6 +153,28 @@ __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restri
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * mi + 4 * lg + e, c = 16 * ni + lr;
         sL[r * LS + c] = c < r ? sB[r] * acc[e] : 0.f;
+      }
+    }
+  }
+  // tril_0(Q K^T) of the chunk (queries r, keys c <= r), bf16, row-major
+  uint16_t* qm = qm_out + ((long)bh * n_chunks + n) * CH * CH;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      if (ni > mi) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qm[(16 * mi + 4 * lg + e) * CH + 16 * ni + lr] = 0;
+        continue;
+      }
+      floatx4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        acc = mma(ldc<NCH>(sQ, 16 * mi + lr, 4 * ks + lg), ldc<NCH>(sK, 16 * ni + lr, 4 * ks + lg), acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * mi + 4 * lg + e, c = 16 * ni + lr;
+        qm[r * CH + c] = c <= r ? f32_to_bf16(acc[e]) : static_cast<uint16_t>(0);
       }
     }
   }
@@ -195,7 +228,8 @@ struct DeltaLds {
 template <int D>
 __global__ __launch_bounds__(256) void delta_main_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ a_in, const uint16_t* __restrict__ kt_in, int T, int n_chunks,
+    const uint16_t* __restrict__ a_in, const uint16_t* __restrict__ kt_in,
+    const uint16_t* __restrict__ qm_in, int T, int n_chunks,
     int n_items, const float* __restrict__ S0, float* __restrict__ o, float* __restrict__ S_final) {
   constexpr int NCH = D / 8;  // chunks per q/k/h row
   constexpr int NT = D / 64;  // 16-column state tiles per wave
@@ -214,12 +248,16 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
   const i32x4 dv = raw_desc(v + tb * D, (uint32_t)T * D * 2);
   const i32x4 da = raw_desc(a_in + (long)bh * n_chunks * 2 * CH * CH, (uint32_t)n_chunks * 2 * CH * CH * 2);
   const i32x4 dkt = raw_desc(kt_in + (long)bh * n_chunks * D * CH, (uint32_t)n_chunks * D * CH * 2);
+  const i32x4 dqm = raw_desc(qm_in + (long)bh * n_chunks * CH * CH, (uint32_t)n_chunks * CH * CH * 2);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + tb * D, (uint32_t)T * D * 4);  // rows past T: dropped
 
-  // DMA of chunk n into buffer b: slot s of an array holds the 16-byte
-  // chunk that its swizzle maps there.
-  auto issue = [&](int n, int b) __attribute__((always_inline)) {
+  // DMA of chunk n into buffer b, in three parts issued during different
+  // phases of the previous chunk (so that the workgroup's copy instructions
+  // do not queue all at once).  Slot s of an array holds the 16-byte chunk
+  // that its swizzle maps there.
+  constexpr int NQ = CH * D / 8 / 256;  // 16-byte slots per thread per q/k/k^T array
+  auto issue_qkv = [&](int n, int b) __attribute__((always_inline)) {
     const int t0 = n * CH;
-    constexpr int NQ = CH * D / 8 / 256;  // 16-byte slots per thread per q/k array
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int seg = i * 4 + w, s = seg * 64 + l;
@@ -227,22 +265,41 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
       dma16(dq, lds.q[b] + seg * 512, ((t0 + r) * D + 8 * c) * 2);
       dma16(dk, lds.k[b] + seg * 512, ((t0 + r) * D + 8 * c) * 2);
     }
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {  // K^T: D rows of 8 chunks
-      const int seg = i * 4 + w, s = seg * 64 + l;
-      const int r = s / 8, c = (s % 8) ^ swz<8>(r);
-      dma16(dkt, lds.kt[b] + seg * 512, (((long)n * D + r) * CH + 8 * c) * 2);
+    {  // V slice: 64 rows of two 16-byte chunks; waves w and w + 2 copy the same half
+      const int s = (w & 1) * 64 + l, r = s / 2, c = s % 2;
+      dma16(dv, lds.v[b] + (w & 1) * 512, ((t0 + r) * D + dv0 + 8 * c) * 2);
     }
+  };
+  auto issue_a = [&](int n, int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // A hi, lo: 2 x 64 rows of 8 chunks (16 KiB)
       const int seg = i * 4 + w, s = seg * 64 + l;
       const int h = s / 512, r = (s / 8) % 64, c = (s % 8) ^ swz<8>(r);
       dma16(da, lds.a[b][0] + seg * 512, ((((long)n * 2 + h) * CH + r) * CH + 8 * c) * 2);
     }
-    if (w < 2) {  // V slice: 64 rows of two 16-byte chunks
-      const int s = w * 64 + l, r = s / 2, c = s % 2;
-      dma16(dv, lds.v[b] + w * 512, ((t0 + r) * D + dv0 + 8 * c) * 2);
+  };
+  auto issue_kt = [&](int n, int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {  // K^T: D rows of 8 chunks
+      const int seg = i * 4 + w, s = seg * 64 + l;
+      const int r = s / 8, c = (s % 8) ^ swz<8>(r);
+      dma16(dkt, lds.kt[b] + seg * 512, (((long)n * D + r) * CH + 8 * c) * 2);
     }
+  };
+  auto issue_qm = [&](int n) __attribute__((always_inline)) {  // tril_0(Q K^T): 64 rows of 8 chunks
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int seg = i * 4 + w, s = seg * 64 + l;
+      const int r = s / 8, c = (s % 8) ^ swz<8>(r);
+      dma16(dqm, lds.qk + seg * 512, (((long)n * CH + r) * CH + 8 * c) * 2);
+    }
+  };
+  // copy instructions per wave and part (the waits below count them)
+  constexpr int N_QKV = 2 * NQ + 1, N_A = 4, N_KT = NQ, N_QM = 2;
+  auto issue = [&](int n, int b) __attribute__((always_inline)) {
+    issue_qkv(n, b);
+    issue_a(n, b);
+    issue_kt(n, b);
   };
 
   // state slice: rows dv0 .. dv0+15; wave w owns columns D/4 w .. (NT tiles
@@ -277,64 +334,83 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
 #pragma unroll 1
   for (int n = 0; n < n_chunks; ++n) {
     const int b = n & 1, t0 = n * CH;
-    wait_vmcnt<0>();  // chunk n (and the O stores of chunk n - 2) have landed
-    lds_barrier();    // ... for every wave; chunk n - 1's buffers and h are free / published
-    if (n + 1 < n_chunks) issue(n + 1, b ^ 1);
-    // O of the previous chunk (stored now, so its stores overlap this chunk)
-    if (t_prev >= 0) {
+    // Copies complete in issue order.  Issued for chunk n during chunk n - 1:
+    // q/k/v (phase 1), A (phase 2), k^T (phase 3); at the top of chunk n: the
+    // O stores of chunk n - 1, then tril(Q K^T) of chunk n.
+    wait_vmcnt<N_A + N_KT>();  // q, k, v of chunk n have landed
+    lds_barrier();  // ... for every wave; chunk n - 1's buffers, qk and h are free / published
+    const bool more = n + 1 < n_chunks;  // chunk n + 1 is copied during this one
+    if (t_prev >= 0) {  // O of the previous chunk, stored now so the stores overlap this chunk
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = t_prev + r0 + 4 * lg + e;
-        if (t < T) o[(tb + t) * D + dv0 + lr] = o_prev[e];
-      }
+      for (int e = 0; e < 4; ++e)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o_prev[e]), ro,
+                                              ((t_prev + r0 + 4 * lg + e) * D + dv0 + lr) * 4, 0, 0);
     }
+    issue_qm(n);
 
-    // phase 1: tril_0(Q K^T) rows of this wave's keys; X = V - K S0^T; Q S0^T
+    // phase 1: K S0^T, Q S0^T (this wave's tokens); X = V - K S0^T.  Operand
+    // reads first, then the MFMAs.
+    constexpr int NK = D / 32;
+    bf16x8 ka[NK], hh[NK], hl[NK], qa[NK];
+    TC_SB();
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      // (Q K^T)^T tile: keys c = r0 + 4 lg + e (M), queries 16 ni + lr (N)
-      floatx4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        acc = mma(ldc<NCH>(lds.k[b], r0 + lr, 4 * ks + lg), ldc<NCH>(lds.q[b], 16 * ni + lr, 4 * ks + lg), acc);
-      const int rq = 16 * ni + lr, c0 = r0 + 4 * lg;
-      uint32_t p0, p1;
-      p0 = cvt_pk(c0 <= rq ? acc[0] : 0.f, c0 + 1 <= rq ? acc[1] : 0.f);
-      p1 = cvt_pk(c0 + 2 <= rq ? acc[2] : 0.f, c0 + 3 <= rq ? acc[3] : 0.f);
-      *reinterpret_cast<uint2*>(lds.qk + epos<8>(rq, c0)) = make_uint2(p0, p1);
+    for (int ks = 0; ks < NK; ++ks) {
+      ka[ks] = ldc<NCH>(lds.k[b], r0 + lr, 4 * ks + lg);
+      hh[ks] = ldc<NCH>(lds.h[0], lr, 4 * ks + lg);
+      hl[ks] = ldc<NCH>(lds.h[1], lr, 4 * ks + lg);
+      qa[ks] = ldc<NCH>(lds.q[b], r0 + lr, 4 * ks + lg);
     }
-    floatx4 kh = zero4(), qh = zero4();
+    TC_SB();
+    if (more) issue_qkv(n + 1, b ^ 1);
+    TC_SB();
+    floatx4 kh = zero4(), kl = zero4(), qh = zero4();
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      const bf16x8 hh = ldc<NCH>(lds.h[0], lr, 4 * ks + lg), hl = ldc<NCH>(lds.h[1], lr, 4 * ks + lg);
-      const bf16x8 ka = ldc<NCH>(lds.k[b], r0 + lr, 4 * ks + lg);
-      kh = mma(ka, hh, kh);
-      kh = mma(ka, hl, kh);
-      qh = mma(ldc<NCH>(lds.q[b], r0 + lr, 4 * ks + lg), hh, qh);
+    for (int ks = 0; ks < NK; ++ks) {
+      kh = mma(ka[ks], hh[ks], kh);
+      kl = mma(ka[ks], hl[ks], kl);
+      qh = mma(qa[ks], hh[ks], qh);
     }
     {
       // X^T row dv = lr, tokens r0 + 4 lg + e
       float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = bf16_to_f32(lds.v[b][(r0 + 4 * lg + e) * DVT + lr]) - kh[e];
+      for (int e = 0; e < 4; ++e)
+        x[e] = bf16_to_f32(lds.v[b][(r0 + 4 * lg + e) * DVT + lr]) - (kh[e] + kl[e]);
       uint32_t h0, h1, l0, l1;
       split2(x[0], x[1], h0, l0);
       split2(x[2], x[3], h1, l1);
       *reinterpret_cast<uint2*>(lds.xt[0] + epos<8>(lr, r0 + 4 * lg)) = make_uint2(h0, h1);
       *reinterpret_cast<uint2*>(lds.xt[1] + epos<8>(lr, r0 + 4 * lg)) = make_uint2(l0, l1);
     }
+    // A of chunk n: loads issued after it are k^T, tril(Q K^T) and (if any)
+    // q/k/v of chunk n + 1.  The O stores between them are not counted:
+    // stores may complete ahead of older loads, so the wait is exact only
+    // over loads (which complete in order) and merely longer otherwise.
+    if (more) wait_vmcnt<N_KT + N_QM + N_QKV>();
+    else wait_vmcnt<N_KT + N_QM>();
     lds_barrier();
 
     // phase 2: U = A X for this wave's tokens
-    floatx4 u = zero4();
+    bf16x8 ah[2], al[2], xh[2], xl[2];
+    TC_SB();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 ah = ldc<8>(lds.a[b][0], r0 + lr, 4 * ks + lg), al = ldc<8>(lds.a[b][1], r0 + lr, 4 * ks + lg);
-      const bf16x8 xh = ldc<8>(lds.xt[0], lr, 4 * ks + lg), xl = ldc<8>(lds.xt[1], lr, 4 * ks + lg);
-      u = mma(ah, xh, u);
-      u = mma(ah, xl, u);
-      u = mma(al, xh, u);
+      ah[ks] = ldc<8>(lds.a[b][0], r0 + lr, 4 * ks + lg);
+      al[ks] = ldc<8>(lds.a[b][1], r0 + lr, 4 * ks + lg);
+      xh[ks] = ldc<8>(lds.xt[0], lr, 4 * ks + lg);
+      xl[ks] = ldc<8>(lds.xt[1], lr, 4 * ks + lg);
     }
+    TC_SB();
+    if (more) issue_a(n + 1, b ^ 1);
+    TC_SB();
+    floatx4 u = zero4(), u2 = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u = mma(ah[ks], xh[ks], u);
+      u2 = mma(ah[ks], xl[ks], u2);
+      u = mma(al[ks], xh[ks], u);
+    }
+    u += u2;
     {
       uint32_t h0, h1, l0, l1;
       split2(u[0], u[1], h0, l0);
@@ -342,32 +418,45 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
       *reinterpret_cast<uint2*>(lds.ut[0] + epos<8>(lr, r0 + 4 * lg)) = make_uint2(h0, h1);
       *reinterpret_cast<uint2*>(lds.ut[1] + epos<8>(lr, r0 + 4 * lg)) = make_uint2(l0, l1);
     }
+    // k^T and tril(Q K^T) of chunk n: issued after them are q/k/v and A of
+    // chunk n + 1 (if any)
+    if (more) wait_vmcnt<N_QKV + N_A>();
+    else wait_vmcnt<0>();
     lds_barrier();
 
     // phase 3: O = Q S0^T + tril_0(Q K^T) U;  S += U^T K
+    bf16x8 qkr[2], uh[2], ul[2], kt[NT][2];
+    TC_SB();
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      qh = mma(ldc<8>(lds.qk, r0 + lr, 4 * ks + lg), ldc<8>(lds.ut[0], lr, 4 * ks + lg), qh);
+    for (int ks = 0; ks < 2; ++ks) {
+      qkr[ks] = ldc<8>(lds.qk, r0 + lr, 4 * ks + lg);
+      uh[ks] = ldc<8>(lds.ut[0], lr, 4 * ks + lg);
+      ul[ks] = ldc<8>(lds.ut[1], lr, 4 * ks + lg);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) kt[t][ks] = ldc<8>(lds.kt[b], (D / 4) * w + 16 * t + lr, 4 * ks + lg);
+    }
+    TC_SB();
+    if (more) issue_kt(n + 1, b ^ 1);
+    TC_SB();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qh = mma(qkr[ks], uh[ks], qh);
     o_prev = qh;
     t_prev = t0;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int c = (D / 4) * w + 16 * t + lr;  // d_k column (N)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 kt = ldc<8>(lds.kt[b], c, 4 * ks + lg);
-        hs[t] = mma(ldc<8>(lds.ut[0], lr, 4 * ks + lg), kt, hs[t]);
-        hs[t] = mma(ldc<8>(lds.ut[1], lr, 4 * ks + lg), kt, hs[t]);
+        hs[t] = mma(uh[ks], kt[t][ks], hs[t]);
+        hs[t] = mma(ul[ks], kt[t][ks], hs[t]);
       }
     }
     publish_state();  // read next after the barrier at the top of the loop
   }
   if (t_prev >= 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int t = t_prev + r0 + 4 * lg + e;
-      if (t < T) o[(tb + t) * D + dv0 + lr] = o_prev[e];
-    }
+    for (int e = 0; e < 4; ++e)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o_prev[e]), ro,
+                                            ((t_prev + r0 + 4 * lg + e) * D + dv0 + lr) * 4, 0, 0);
   }
   if (S_final != nullptr) {
 #pragma unroll
@@ -385,14 +474,15 @@ hipError_t run_delta_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* 
   const int n_chunks = (T + CH - 1) / CH;
   uint16_t* a_ws = static_cast<uint16_t*>(ws);
   uint16_t* kt_ws = a_ws + (size_t)BH * n_chunks * 2 * CH * CH;
+  uint16_t* qm_ws = kt_ws + (size_t)BH * n_chunks * D * CH;
   if (n_chunks > 0)
-    hipLaunchKernelGGL(delta_prep_kernel<D>, dim3(n_chunks, BH), dim3(64), 0, s, k, beta, T, n_chunks,
-                       a_ws, kt_ws);
+    hipLaunchKernelGGL(delta_prep_kernel<D>, dim3(n_chunks, BH), dim3(64), 0, s, q, k, beta, T,
+                       n_chunks, a_ws, kt_ws, qm_ws);
   const int n_items = BH * (D / DVT);
   const int grid = (n_items + NXCD - 1) / NXCD * NXCD;
   profile_mark_before(s);
-  hipLaunchKernelGGL(delta_main_kernel<D>, dim3(grid), dim3(256), 0, s, q, k, v, a_ws, kt_ws, T,
-                     n_chunks, n_items, S0, o, S_final);
+  hipLaunchKernelGGL(delta_main_kernel<D>, dim3(grid), dim3(256), 0, s, q, k, v, a_ws, kt_ws, qm_ws,
+                     T, n_chunks, n_items, S0, o, S_final);
   profile_mark_after(s);
   return hipGetLastError();
 }
@@ -403,7 +493,7 @@ bool delta_bf16_supported(bool bf16, int d) { return bf16 && (d == 64 || d == 12
 
 size_t delta_bf16_ws_bytes(int B, int H, int T, int d) {
   const size_t n_chunks = (T + CH - 1) / CH;
-  return (size_t)B * H * n_chunks * (2 * CH * CH + (size_t)d * CH) * sizeof(uint16_t);
+  return (size_t)B * H * n_chunks * (3 * CH * CH + (size_t)d * CH) * sizeof(uint16_t);
 }
 
 hipError_t launch_delta_bf16(const void* q, const void* k, const void* v, const float* beta, int B,
