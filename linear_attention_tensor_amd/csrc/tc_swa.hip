@@ -517,26 +517,25 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
   for (int j = 0; j < 4; ++j) ls[j] = lane_slot(j);
 
   // Copies complete in issue order: blocks 0..2, then the state (used only in
-  // the epilogue), so the first waits do not include it.
+  // the epilogue).  The state is issued after the first scores: the compiler
+  // waits for the q loads with counts that also cover every copy issued
+  // before them, so the first scores wait for blocks 0..2 but not for it.
   constexpr int NS = D * D / 8 / NTHR;  // state copy instructions per thread
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
     dma_block<D>(rk, rvt, doff, j0 + KB * block_at(i), lds.k[i], lds.vt[i]);
-  if (has_l2) {
-    dma_state<D>(raw_desc(l2.sst + ((long)bh * n_tiles + tile) * D * D, D * D * 2), lds.st);
-    wait_vmcnt<2 * Dma<D>::N + NS>();
-  } else {
-    wait_vmcnt<2 * Dma<D>::N>();
-  }
+  wait_vmcnt<2 * Dma<D>::N>();
   lds_barrier();
   floatx16 s0[2], s1[2];
   qk_block<D>(reinterpret_cast<const char*>(lds.k[0]), ls, qreg, s0[0], s0[1]);
+  if (has_l2) dma_state<D>(raw_desc(l2.sst + ((long)bh * n_tiles + tile) * D * D, D * D * 2), lds.st);
 
   // One step per block position; the scores alternate between s0 and s1.
   auto step = [&](int idx, floatx16* sc, floatx16* sn) __attribute__((always_inline)) {
     // block idx + 1 must have landed: its scores are formed in this step.
     // Outstanding copies allowed: block idx + 2, and for idx < 2 the state,
-    // which was issued between blocks 2 and 3.
+    // which was issued between blocks 2 and 3 (at idx = 0 block 1 has landed
+    // already).
     if (idx < 2 && has_l2) wait_vmcnt<Dma<D>::N + NS>();
     else if (idx + 2 < nb) wait_vmcnt<Dma<D>::N>();
     else wait_vmcnt<0>();
