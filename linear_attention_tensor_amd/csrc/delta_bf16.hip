@@ -93,7 +93,10 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// delta_prep: one wave per (chunk, b, h).
+// delta_prep: one wave per (chunk, b, h).  Every output leaves in 16-byte
+// (A, K^T) or 8-byte (tril(Q K^T)) pieces per lane: A and K^T are first
+// transposed through LDS.  One buffer holds in turn the K^T staging, Q, L and
+// the A staging, so that four workgroups fit in a CU's LDS.
 template <int D>
 __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
@@ -103,39 +106,71 @@ __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restri
                                                         uint16_t* __restrict__ qm_out) {
   constexpr int NCH = D / 8;
   constexpr int LS = CH + 4;  // fp32 L rows, 16-byte aligned
+  static_assert(D * CH * 2 <= CH * LS * 4, "K^T and Q fit the L buffer");
   __shared__ __attribute__((aligned(16))) uint16_t sK[CH * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[CH * D];
-  __shared__ __attribute__((aligned(16))) float sL[CH * LS];
+  __shared__ __attribute__((aligned(16))) float sL[CH * LS];  // K^T staging, Q, L, A staging
   __shared__ float sB[CH];
+  uint16_t* const sQ = reinterpret_cast<uint16_t*>(sL);
   const int n = blockIdx.x, bh = blockIdx.y, l = threadIdx.x;
   const int t0 = n * CH;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (long)bh * T * D, (uint32_t)T * D * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (long)bh * T * D, (uint32_t)T * D * 2);
-#pragma unroll
-  for (int c = 0; c < NCH; ++c)
-    *reinterpret_cast<uint4*>(sQ + pos<NCH>(l, c)) = buf_load16(rq, ((t0 + l) * D + 8 * c) * 2);
-  // lane l: key t0 + l (zero past T)
-  uint4 kr[NCH];
+  // lane l: key and query t0 + l (zero past T)
+  uint4 kr[NCH], qr[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) kr[c] = buf_load16(rk, ((t0 + l) * D + 8 * c) * 2);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) qr[c] = buf_load16(rq, ((t0 + l) * D + 8 * c) * 2);
   const float b = t0 + l < T ? beta[(long)bh * T + t0 + l] : 0.f;
   sB[l] = b;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) *reinterpret_cast<uint4*>(sK + pos<NCH>(l, c)) = kr[c];
-  // K^T of the chunk: row dk holds the 64 keys (lane l writes key l)
-  uint16_t* kt = kt_out + ((long)bh * n_chunks + n) * D * CH;
+  // K into sK and, transposed, into the staging area ([dk][key] bf16)
+  uint16_t* skt = reinterpret_cast<uint16_t*>(sL);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
+    *reinterpret_cast<uint4*>(sK + pos<NCH>(l, c)) = kr[c];
     const uint32_t w4[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      kt[(8 * c + 2 * e) * CH + l] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
-      kt[(8 * c + 2 * e + 1) * CH + l] = static_cast<uint16_t>(w4[e] >> 16);
+      skt[(8 * c + 2 * e) * CH + l] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
+      skt[(8 * c + 2 * e + 1) * CH + l] = static_cast<uint16_t>(w4[e] >> 16);
     }
   }
   __syncthreads();
-  // L = diag(beta) tril_{-1}(K K^T): tiles (mi, ni) with ni <= mi
+  // K^T of the chunk: D rows of 64 keys, eight 16-byte pieces per row
+  uint16_t* kt = kt_out + ((long)bh * n_chunks + n) * D * CH;
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) {
+    const int s = i * 64 + l;
+    *reinterpret_cast<uint4*>(kt + s * 8) = *reinterpret_cast<const uint4*>(skt + s * 8);
+  }
+  __syncthreads();  // the staged K^T has been read: Q takes its place
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) *reinterpret_cast<uint4*>(sQ + pos<NCH>(l, c)) = qr[c];
+  __syncthreads();
+  // tril_0(Q K^T) of the chunk, bf16 row-major [query][key], computed as its
+  // transpose (keys as M) so that a lane holds four consecutive keys of one
+  // query: tile (mi, ni) = keys 16 mi.., queries 16 ni..; zero for mi > ni
   const int lr = l & 15, lg = l >> 4;
+  uint16_t* qm = qm_out + ((long)bh * n_chunks + n) * CH * CH;
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int rq = 16 * ni + lr, c0 = 16 * mi + 4 * lg;  // query, first of four keys
+      uint2 out = make_uint2(0u, 0u);
+      if (mi <= ni) {
+        floatx4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+          acc = mma(ldc<NCH>(sK, 16 * mi + lr, 4 * ks + lg), ldc<NCH>(sQ, 16 * ni + lr, 4 * ks + lg), acc);
+        out = make_uint2(cvt_pk(c0 <= rq ? acc[0] : 0.f, c0 + 1 <= rq ? acc[1] : 0.f),
+                         cvt_pk(c0 + 2 <= rq ? acc[2] : 0.f, c0 + 3 <= rq ? acc[3] : 0.f));
+      }
+      *reinterpret_cast<uint2*>(qm + rq * CH + c0) = out;
+    }
+  }
+  __syncthreads();  // Q has been read: L takes its place
+  // L = diag(beta) tril_{-1}(K K^T): tiles (mi, ni) with ni <= mi
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -156,28 +191,6 @@ __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restri
       }
     }
   }
-  // tril_0(Q K^T) of the chunk (queries r, keys c <= r), bf16, row-major
-  uint16_t* qm = qm_out + ((long)bh * n_chunks + n) * CH * CH;
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      if (ni > mi) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qm[(16 * mi + 4 * lg + e) * CH + 16 * ni + lr] = 0;
-        continue;
-      }
-      floatx4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        acc = mma(ldc<NCH>(sQ, 16 * mi + lr, 4 * ks + lg), ldc<NCH>(sK, 16 * ni + lr, 4 * ks + lg), acc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * mi + 4 * lg + e, c = 16 * ni + lr;
-        qm[r * CH + c] = c <= r ? f32_to_bf16(acc[e]) : static_cast<uint16_t>(0);
-      }
-    }
-  }
   __syncthreads();
   // M = (I + L)^-1, one column per lane: M[r] = e_r - sum_{i<r} L[r][i] M[i]
   float m[CH];
@@ -185,25 +198,36 @@ __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restri
   for (int r = 0; r < CH; ++r) m[r] = 0.f;
 #pragma unroll
   for (int r = 0; r < CH; ++r) {
-    float s0 = r == l ? 1.f : 0.f, s1 = 0.f;
+    float s0 = r == l ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll
     for (int i = 0; i < r; i += 4) {  // L[r][i..i+3] is 0 past r - 1
       const float4 lv = *reinterpret_cast<const float4*>(sL + r * LS + i);
       s0 = fmaf(-lv.x, m[i], s0);
       s1 = fmaf(-lv.y, m[i + 1], s1);
-      s0 = fmaf(-lv.z, m[i + 2], s0);
-      s1 = fmaf(-lv.w, m[i + 3], s1);
+      s2 = fmaf(-lv.z, m[i + 2], s2);
+      s3 = fmaf(-lv.w, m[i + 3], s3);
     }
-    m[r] = s0 + s1;
+    m[r] = (s0 + s1) + (s2 + s3);
   }
-  // A = M diag(beta): column l scaled by beta_l; out as bf16 pair [hi | lo]
+  __syncthreads();  // every row of L has been read
+  // A = M diag(beta) (column l scaled by beta_l), transposed through LDS and
+  // written as a bf16 pair A = A_hi + A_lo, [hi | lo] row-major
+#pragma unroll
+  for (int r = 0; r < CH; ++r) sL[r * LS + l] = m[r] * b;
+  __syncthreads();
   uint16_t* ao = a_out + ((long)bh * n_chunks + n) * 2 * CH * CH;
 #pragma unroll
-  for (int r = 0; r < CH; ++r) {
-    const float a = m[r] * b;
-    const uint16_t hi = f32_to_bf16(a);
-    ao[r * CH + l] = hi;
-    ao[CH * CH + r * CH + l] = f32_to_bf16(a - bf16_to_f32(hi));
+  for (int i = 0; i < 8; ++i) {
+    const int s = i * 64 + l, r = s >> 3, c8 = 8 * (s & 7);
+    const float4 x0 = *reinterpret_cast<const float4*>(sL + r * LS + c8);
+    const float4 x1 = *reinterpret_cast<const float4*>(sL + r * LS + c8 + 4);
+    uint32_t h[4], lo[4];
+    split2(x0.x, x0.y, h[0], lo[0]);
+    split2(x0.z, x0.w, h[1], lo[1]);
+    split2(x1.x, x1.y, h[2], lo[2]);
+    split2(x1.z, x1.w, h[3], lo[3]);
+    *reinterpret_cast<uint4*>(ao + r * CH + c8) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(ao + CH * CH + r * CH + c8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
 }
 
