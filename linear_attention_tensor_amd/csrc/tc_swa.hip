@@ -548,10 +548,11 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
     }
     const int b = block_at(idx);
     const int c_lo = KB * b, jb = j0 + c_lo;
-    const bool active = idx < nb && tw < T && c_lo + KB - 1 > r_lo && c_lo <= r_hi + W &&
-                        jb + KB - 1 >= 0 && jb < T;
-    const bool full = c_lo > r_hi && c_lo + KB - 1 <= r_lo + W && jb >= 0 && jb + KB - 1 < T &&
-                      tw + 31 < T;
+    // (bitwise &: the flags are formed without branches)
+    const bool active = (idx < nb) & (tw < T) & (c_lo + KB - 1 > r_lo) & (c_lo <= r_hi + W) &
+                        (jb + KB - 1 >= 0) & (jb < T);
+    const bool full = (c_lo > r_hi) & (c_lo + KB - 1 <= r_lo + W) & (jb >= 0) & (jb + KB - 1 < T) &
+                      (tw + 31 < T);
     // keys c_lo + key valid for query r: r < c <= r + W and 0 <= j < T
     const int r = r_lo + col;
     int lo = max(r + 1 - c_lo, -jb);
