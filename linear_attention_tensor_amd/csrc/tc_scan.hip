@@ -241,6 +241,295 @@ __global__ __launch_bounds__(256) void scan_output_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// d <= 64: one workgroup (4 waves) per (segment, b, h) owns the whole d_v.
+// Every product reads both operands k-contiguous from LDS: the k order is
+// permuted so that MFMA 4J + s takes k = 16J + 4g + s from lane (row, g),
+// and one 16-byte read per operand feeds four MFMAs.  The state S^T
+// (d_v x d_k) lives in the registers of the waves that update it and is
+// published to a double-buffered LDS copy for the reads; the next chunk's
+// inputs are loaded into registers while the current one is computed.
+template <int D>
+struct FastTiles {
+  static constexpr int S = D + 4;    // row stride of [64][D] and [D][D] arrays
+  static constexpr int ST = CH + 4;  // row stride of [D][64] and [64][64] arrays
+  static constexpr int NV4 = CH * D / 4 / 256;  // float4 pieces per thread per input array
+  static constexpr int NTS = (D / 16) * (D / 16);  // 16x16 state tiles
+  static constexpr int TPW = NTS >= 4 ? NTS / 4 : 1;  // state tiles per wave
+};
+
+// acc[t] += A[16 x K] * B_t[K x 16], A rows at a + r sa, B_t given transposed
+// (rows = columns of B_t) at bt + t bstep + r sb.
+template <int K, int NT>
+__device__ __forceinline__ void mma_rows(const float* a, int sa, const float* bt, int bstep, int sb,
+                                         floatx4* acc) {
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const float* ap = a + r * sa + 4 * g;
+  const float* bp = bt + r * sb + 4 * g;
+#pragma unroll
+  for (int J = 0; J < K / 16; ++J) {
+    const float4 x = *reinterpret_cast<const float4*>(ap + 16 * J);
+    float4 y[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = *reinterpret_cast<const float4*>(bp + t * bstep + 16 * J);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.x, y[t].x, acc[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.y, y[t].y, acc[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.z, y[t].z, acc[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.w, y[t].w, acc[t]);
+  }
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
+
+// One chunk's rows [0, 64) of a row-major [., D] input in registers, as
+// float4 pieces i * 256 + thread; rows >= nvalid are zero.
+template <int D, typename TIn>
+__device__ __forceinline__ void load_rows(float4* x, const TIn* src, int nvalid) {
+#pragma unroll
+  for (int i = 0; i < FastTiles<D>::NV4; ++i) {
+    const int e4 = i * 256 + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
+    x[i] = row < nvalid ? ld4(src + (long)row * D + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+// ... into LDS row-major (stride S) ...
+template <int D>
+__device__ __forceinline__ void put_rows(float* dst, const float4* x) {
+#pragma unroll
+  for (int i = 0; i < FastTiles<D>::NV4; ++i) {
+    const int e4 = i * 256 + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
+    *reinterpret_cast<float4*>(dst + row * FastTiles<D>::S + c4) = x[i];
+  }
+}
+// ... or transposed (dst[col][row], stride ST), each row scaled by wr[row].
+template <int D>
+__device__ __forceinline__ void put_cols(float* dst, const float4* x, const float* wr) {
+#pragma unroll
+  for (int i = 0; i < FastTiles<D>::NV4; ++i) {
+    const int e4 = i * 256 + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
+    const float f = wr != nullptr ? wr[row] : 1.f;
+    dst[(c4 + 0) * FastTiles<D>::ST + row] = f * x[i].x;
+    dst[(c4 + 1) * FastTiles<D>::ST + row] = f * x[i].y;
+    dst[(c4 + 2) * FastTiles<D>::ST + row] = f * x[i].z;
+    dst[(c4 + 3) * FastTiles<D>::ST + row] = f * x[i].w;
+  }
+}
+
+// State tiles of this wave: (dv tile a, dk tile b) of S^T.
+template <int D>
+__device__ __forceinline__ bool state_tile(int w, int i, int& a, int& b) {
+  const int t = w * FastTiles<D>::TPW + i;
+  a = t / (D / 16);
+  b = t % (D / 16);
+  return t < FastTiles<D>::NTS;
+}
+
+// acc (this wave's S^T tiles) <- lamL acc + V^T (w K) over one staged chunk
+template <int D>
+__device__ __forceinline__ void fast_state_update(floatx4* acc, const float* sVt, const float* sKt,
+                                                  float lamL) {
+  using F = FastTiles<D>;
+  const int w = wave_id();
+#pragma unroll
+  for (int i = 0; i < F::TPW; ++i) acc[i] *= lamL;
+  if constexpr (F::TPW == 4) {
+    // the wave's four tiles share the dv tile (a = w): one A row block
+    mma_rows<CH, 4>(sVt + 16 * w * F::ST, F::ST, sKt, 16 * F::ST, F::ST, acc);
+  } else {
+    int a, b;
+    if (state_tile<D>(w, 0, a, b))
+      mma_rows<CH, 1>(sVt + 16 * a * F::ST, F::ST, sKt + 16 * b * F::ST, 0, F::ST, acc);
+  }
+}
+
+// S^T tiles from registers to an LDS copy [dv][dk] (stride S)
+template <int D>
+__device__ __forceinline__ void publish_state(float* sSt, const floatx4* acc) {
+  using F = FastTiles<D>;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int i = 0; i < F::TPW; ++i) {
+    int a, b;
+    if (!state_tile<D>(w, i, a, b)) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sSt[(16 * a + 4 * g + e) * F::S + 16 * b + r] = acc[i][e];
+  }
+}
+
+// S^T tiles <-> a global [dk][dv] array (row stride dv)
+template <int D>
+__device__ __forceinline__ void load_state(floatx4* acc, const float* src, int dv) {
+  using F = FastTiles<D>;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int i = 0; i < F::TPW; ++i) {
+    int a, b;
+    const bool own = state_tile<D>(w, i, a, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc[i][e] = own && src != nullptr ? src[(long)(16 * b + r) * dv + 16 * a + 4 * g + e] : 0.f;
+  }
+}
+template <int D>
+__device__ __forceinline__ void store_state(float* dst, const floatx4* acc, int dv) {
+  using F = FastTiles<D>;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int i = 0; i < F::TPW; ++i) {
+    int a, b;
+    if (!state_tile<D>(w, i, a, b)) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[(long)(16 * b + r) * dv + 16 * a + 4 * g + e] = acc[i][e];
+  }
+}
+
+// Per-(segment, b, h) state contribution from zero (all segments but the last).
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void scan_state_fast(const TIn* __restrict__ k,
+                                                       const TIn* __restrict__ v,
+                                                       const float* __restrict__ lam,
+                                                       const float* __restrict__ eta, int H, int T,
+                                                       int n_act, int seg_chunks, int n_seg,
+                                                       float* __restrict__ ws) {
+  using F = FastTiles<D>;
+  __shared__ __attribute__((aligned(16))) float sKt[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sVt[D * F::ST];
+  __shared__ float sW[CH];
+  const int seg = blockIdx.x, bh = blockIdx.z;
+  const float lm = lam[bh % H], et = eta[bh % H];
+  const int c_begin = seg * seg_chunks;
+  const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
+  const TIn* kb = k + (long)bh * T * D;
+  const TIn* vb = v + (long)bh * T * D;
+  floatx4 acc[F::TPW];
+  load_state<D>(acc, nullptr, D);
+  float4 xk[F::NV4], xv[F::NV4];
+  if (c_begin < c_end) {
+    const int L = min(CH, n_act - c_begin * CH);
+    load_rows<D>(xk, kb + (long)c_begin * CH * D, L);
+    load_rows<D>(xv, vb + (long)c_begin * CH * D, L);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const int L = min(CH, n_act - c * CH);
+    lds_barrier();  // every wave is done with the previous chunk
+    if (threadIdx.x < CH) sW[threadIdx.x] = threadIdx.x < L ? et * pow_int(lm, L - 1 - threadIdx.x) : 0.f;
+    lds_barrier();
+    put_cols<D>(sKt, xk, sW);
+    put_cols<D>(sVt, xv, nullptr);
+    lds_barrier();
+    if (c + 1 < c_end) {
+      const int Ln = min(CH, n_act - (c + 1) * CH);
+      load_rows<D>(xk, kb + (long)(c + 1) * CH * D, Ln);
+      load_rows<D>(xv, vb + (long)(c + 1) * CH * D, Ln);
+    }
+    fast_state_update<D>(acc, sVt, sKt, pow_int(lm, L));
+  }
+  store_state<D>(ws + ((long)bh * n_seg + seg) * D * D, acc, D);
+}
+
+// Per-(segment, b, h): carry the entering state through the segment's
+// chunks and write m (rows W + s).
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void scan_output_fast(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ lam, const float* __restrict__ eta, int H, int T, int W, int n_act,
+    int seg_chunks, int n_seg, const float* __restrict__ ws, float* __restrict__ m,
+    float* __restrict__ A_final) {
+  using F = FastTiles<D>;
+  constexpr int NDV = D / 16;
+  __shared__ __attribute__((aligned(16))) float sQ[CH * F::S];
+  __shared__ __attribute__((aligned(16))) float sK[CH * F::S];
+  __shared__ __attribute__((aligned(16))) float sKt[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sVt[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sP[CH * F::ST];
+  __shared__ __attribute__((aligned(16))) float sSt[2][D * F::S];
+  __shared__ float sPow[CH + 1];  // lam^i
+  __shared__ float sW[CH];
+
+  const int seg = blockIdx.x, bh = blockIdx.z;
+  const float lm = lam[bh % H], et = eta[bh % H];
+  const int l = lane_id(), w = wave_id(), r = l & 15, g = l >> 4;
+  const int c_begin = seg * seg_chunks;
+  const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
+  const TIn* qb = q + (long)bh * T * D;
+  const TIn* kb = k + (long)bh * T * D;
+  const TIn* vb = v + (long)bh * T * D;
+  float* mb = m + (long)bh * T * D;
+  if (threadIdx.x <= CH) sPow[threadIdx.x] = pow_int(lm, threadIdx.x);
+
+  floatx4 acc[F::TPW];
+  load_state<D>(acc, n_seg > 1 && seg > 0 ? ws + ((long)bh * n_seg + seg) * D * D : nullptr, D);
+  publish_state<D>(sSt[0], acc);
+  float4 xq[F::NV4], xk[F::NV4], xv[F::NV4];
+  if (c_begin < c_end) {
+    const int s0 = c_begin * CH, L = min(CH, n_act - s0);
+    load_rows<D>(xq, qb + (long)(s0 + W) * D, L);
+    load_rows<D>(xk, kb + (long)s0 * D, L);
+    load_rows<D>(xv, vb + (long)s0 * D, L);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const int s0 = c * CH, L = min(CH, n_act - s0);
+    const int cur = (c - c_begin) & 1;
+    lds_barrier();  // every wave is done with the previous chunk; its state is published
+    if (threadIdx.x < CH) sW[threadIdx.x] = threadIdx.x < L ? et * sPow[L - 1 - threadIdx.x] : 0.f;
+    lds_barrier();
+    put_rows<D>(sQ, xq);
+    put_rows<D>(sK, xk);
+    put_cols<D>(sKt, xk, sW);
+    put_cols<D>(sVt, xv, nullptr);
+    lds_barrier();
+    if (c + 1 < c_end) {
+      const int s1 = s0 + CH, Ln = min(CH, n_act - s1);
+      load_rows<D>(xq, qb + (long)(s1 + W) * D, Ln);
+      load_rows<D>(xk, kb + (long)s1 * D, Ln);
+      load_rows<D>(xv, vb + (long)s1 * D, Ln);
+    }
+    // P = (Q' K^T) masked to c <= r and weighted by eta lam^(r-c): this
+    // wave's rows 16w.., kept in LDS for its own P V below.
+    {
+      floatx4 pa[4] = {zero4(), zero4(), zero4(), zero4()};
+      mma_rows<D, 4>(sQ + 16 * w * F::S, F::S, sK, 16 * F::S, F::S, pa);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 16 * w + 4 * g + e, cc = 16 * ct + r;
+          sP[rr * F::ST + cc] = cc <= rr ? pa[ct][e] * et * sPow[rr - cc] : 0.f;
+        }
+    }
+    // O = diag(lam^(r+1)) Q' S + P V
+    {
+      floatx4 o[NDV];
+#pragma unroll
+      for (int t = 0; t < NDV; ++t) o[t] = zero4();
+      mma_rows<D, NDV>(sQ + 16 * w * F::S, F::S, sSt[cur], 16 * F::S, F::S, o);
+#pragma unroll
+      for (int t = 0; t < NDV; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[t][e] *= sPow[16 * w + 4 * g + e + 1];
+      mma_rows<CH, NDV>(sP + 16 * w * F::ST, F::ST, sVt, 16 * F::ST, F::ST, o);
+#pragma unroll
+      for (int t = 0; t < NDV; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 16 * w + 4 * g + e;
+          if (rr < L) mb[(long)(W + s0 + rr) * D + 16 * t + r] = o[t][e];
+        }
+    }
+    fast_state_update<D>(acc, sVt, sKt, sPow[L]);
+    publish_state<D>(sSt[cur ^ 1], acc);
+  }
+  if (A_final != nullptr && seg == n_seg - 1) store_state<D>(A_final + (long)bh * D * D, acc, D);
+}
+
 // m rows t < min(W, T) are exactly zero; with no active position the final
 // state is zero too.
 __global__ void zero_rows_kernel(float* __restrict__ m, long rows_per_bh, long T, int dv) {
@@ -268,6 +557,20 @@ hipError_t run_scan(const TIn* q, const TIn* k, const TIn* v, const float* lam, 
     return hipGetLastError();
   }
   const int nvt = dv / DVT;
+  if constexpr (DK <= 64 && DVT == DK) {
+    if (p.n_seg > 1) {
+      hipLaunchKernelGGL((scan_state_fast<DK, TIn>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, k, v,
+                         lam, eta, H, T, p.n_act, p.seg_chunks, p.n_seg, ws);
+      const int nel = DK * dv;
+      hipLaunchKernelGGL(scan_prefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H,
+                         nel, p.n_act, p.seg_chunks * CH, p.n_seg, ws);
+    }
+    profile_mark_before(s);
+    hipLaunchKernelGGL((scan_output_fast<DK, TIn>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, q, k, v,
+                       lam, eta, H, T, W, p.n_act, p.seg_chunks, p.n_seg, ws, m, A_final);
+    profile_mark_after(s);
+    return hipGetLastError();
+  }
   if (p.n_seg > 1) {
     dim3 g1(p.n_seg - 1, nvt, BH);
     hipLaunchKernelGGL((scan_state_kernel<DK, DVT, TIn>), g1, dim3(256), 0, s, k, v, lam, eta, H,
