@@ -612,9 +612,12 @@ ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int W) {
   p.n_chunks = (p.n_act + CH - 1) / CH;
   p.dvt = dv > 64 ? 64 : dv;
   const long units = (long)B * H * (dv / p.dvt);
-  // Aim for about 1024 workgroups in the output launch (4 per CU), and never
-  // let a segment be shorter than 2 chunks unless the sequence is.
-  long want_seg = units > 0 ? (1024 + units - 1) / units : 1;
+  // Aim for one round of output workgroups, about one per CU (MI355X: 256
+  // CUs): the kernels hold one workgroup per CU and overlap the loads of a
+  // chunk with the work on the previous one, so longer segments pay off up
+  // to that point.  A segment is never shorter than 2 chunks unless the
+  // sequence is.
+  long want_seg = units > 0 ? (256 + units - 1) / units : 1;
   int seg_chunks = p.n_chunks > 0 ? (int)std::max<long>(2, (p.n_chunks + want_seg - 1) / want_seg) : 1;
   seg_chunks = std::min(seg_chunks, std::max(p.n_chunks, 1));
   p.seg_chunks = seg_chunks;
