@@ -147,6 +147,30 @@ class TensorCacheDecoder:
             self.pos[b] += 1
         return m
 
+    def step_layer(self, q, k, v, g, scale=None):
+        """Full decode step of the layer: q, k [B,H,dk], v [B,H,dv], g [H] -> y [B,H,dv].
+
+        Tensor Cache, Methodology 1: the step above (eviction into A, the new
+        pair into its slot, the read m = q A), then exact softmax attention of
+        q over the pairs the ring holds after the write (the W most recent
+        tokens, the current one included), and the gated sum
+        y = y_local + sigmoid(g) m.  Advances each sequence by one.
+        """
+        q64 = _f64(q)
+        B, H, dk = q64.shape
+        scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+        m = self.step(q, k, v)
+        gate = sigmoid(g)
+        y = np.zeros_like(m)
+        for b in range(B):
+            held = np.flatnonzero(self.occupied[b])
+            for h in range(H):
+                s = (self.ring_k[b, h, held, :] @ q64[b, h]) * scale
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                y[b, h] = p @ self.ring_v[b, h, held, :] + gate[h] * m[b, h]
+        return y
+
 
 def window_softmax(q, k, v, W, scale):
     """L1 output: exact softmax attention over the W most recent tokens.

@@ -283,6 +283,82 @@ def test_fused_rows_match_full():
                                rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------- full decode step
+
+def run_layer_decoder(q, k, v, lam, eta, g, W, scale):
+    B, H, T, dk = q.shape
+    dec = O.TensorCacheDecoder(B, H, dk, v.shape[-1], W, lam, eta)
+    return np.stack([dec.step_layer(q[:, :, t], k[:, :, t], v[:, :, t], g, scale) for t in range(T)],
+                    axis=2)
+
+
+def test_decode_layer_without_evictions_is_causal_softmax_attention():
+    # W >= T: nothing leaves the ring, A stays 0, and the L1 part is causal attention
+    q, k, v, lam, eta, g = rand_inputs(40, T=25)
+    scale = 0.6
+    y = run_layer_decoder(q, k, v, lam, eta, g, 64, scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True, scale=scale).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_layer_l1_is_banded_softmax_attention():
+    # eta = 0: the L2 read is 0, and the ring softmax is attention under the W-band mask
+    q, k, v, lam, _, g = rand_inputs(41, T=40)
+    W, scale = 7, 0.45
+    T = q.shape[2]
+    y = run_layer_decoder(q, k, v, lam, np.zeros(2), g, W, scale)
+    i = np.arange(T)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - W)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(band), scale=scale).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_layer_adds_gated_l2_read():
+    # y(eta) - y(eta = 0) = sigmoid(g) m, m from the brute-force double sum
+    q, k, v, lam, eta, g = rand_inputs(42, T=36)
+    W, scale = 5, 0.3
+    y1 = run_layer_decoder(q, k, v, lam, eta, g, W, scale)
+    y0 = run_layer_decoder(q, k, v, lam, np.zeros(2), g, W, scale)
+    m = brute_force_m(q, k, v, lam, eta, W)
+    gate = 1.0 / (1.0 + np.exp(-g))
+    np.testing.assert_allclose(y1 - y0, gate[None, :, None, None] * m, rtol=1e-11, atol=1e-13)
+
+
+def test_decode_layer_equal_keys_average_the_window():
+    # every key the same: every score the same, so the L1 output is the mean of the
+    # values in the window (the W most recent, the current one included)
+    q, k, v, lam, _, g = rand_inputs(43, T=30)
+    k[...] = k[:, :, :1, :]
+    W = 6
+    y = run_layer_decoder(q, k, v, lam, np.zeros(2), g, W, 1.0)
+    for t in range(q.shape[2]):
+        np.testing.assert_allclose(y[:, :, t], v[:, :, max(0, t - W + 1): t + 1].mean(axis=2),
+                                   rtol=1e-12, atol=1e-14)
+
+
+def test_decode_layer_continues_a_prefill():
+    # prefill with the fused layer's oracle, hand over A and the last W tokens as the
+    # ring, continue with full decode steps: the rows equal the longer prefill
+    q, k, v, lam, eta, g = rand_inputs(44, T=41)
+    W, T0, scale = 6, 27, 0.5
+    y_full, A_full = O.tc_fused(q, k, v, lam, eta, g, W, scale)
+    _, A0 = O.tc_fused(q[:, :, :T0], k[:, :, :T0], v[:, :, :T0], lam, eta, g, W, scale)
+    B, H = q.shape[:2]
+    ring_k = np.zeros((B, H, W, q.shape[-1]))
+    ring_v = np.zeros((B, H, W, v.shape[-1]))
+    for t in range(T0 - W, T0):
+        ring_k[:, :, t % W] = k[:, :, t]
+        ring_v[:, :, t % W] = v[:, :, t]
+    dec = O.TensorCacheDecoder.from_state(ring_k, ring_v, A0, np.full(B, T0), W, lam, eta)
+    for t in range(T0, q.shape[2]):
+        np.testing.assert_allclose(dec.step_layer(q[:, :, t], k[:, :, t], v[:, :, t], g, scale),
+                                   y_full[:, :, t], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dec.A, A_full, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- properties
 
 @settings(max_examples=40, deadline=None)
@@ -329,3 +405,51 @@ def test_brute_force_pin_catches_planted_mistakes(mutant):
     ref = brute_force_m(q, k, v, lam, eta, 4)
     m, _ = mutant(q, k, v, lam, eta, 4)
     assert np.max(np.abs(m - ref)) > 1e-6
+
+
+# Copies of the full decode step with one planted mistake each; the decode-layer pins
+# above (banded attention, gated read) must reject every one.
+def _layer_mutant(kind):
+    def run(q, k, v, lam, eta, g, W, scale):
+        B, H, T, _ = q.shape
+        m = O.tc_scan(q, k, v, lam, eta, W)[0]
+        gate = 1.0 / (1.0 + np.exp(-g))
+        y = np.zeros(v.shape)
+        for t in range(T):
+            lo, hi = {"no_current": (t - W, t), "window_plus_one": (t - W, t + 1)}.get(kind, (t - W + 1, t + 1))
+            lo = max(0, lo)
+            yl = np.zeros((B, H, v.shape[-1]))
+            if hi > lo:
+                s = np.einsum("bhjd,bhd->bhj", k[:, :, lo:hi], q[:, :, t]) * scale
+                p = np.exp(s - s.max(axis=-1, keepdims=True))
+                p /= p.sum(axis=-1, keepdims=True)
+                yl = np.einsum("bhj,bhjd->bhd", p, v[:, :, lo:hi])
+            if kind == "gate_on_local":
+                y[:, :, t] = gate[None, :, None] * yl + m[:, :, t]
+            else:
+                y[:, :, t] = yl + gate[None, :, None] * m[:, :, t]
+        return y
+    return run
+
+
+@pytest.mark.parametrize("kind", ["no_current", "window_plus_one", "gate_on_local"])
+def test_decode_layer_pins_catch_planted_mistakes(kind):
+    q, k, v, lam, eta, g = rand_inputs(45, B=1, T=24, dk=4, dv=3)
+    W, scale = 5, 0.7
+    mut = _layer_mutant(kind)
+    T = q.shape[2]
+    i = np.arange(T)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - W)
+    ref_l1 = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(band), scale=scale).numpy()
+    gate = 1.0 / (1.0 + np.exp(-g))
+    ref_l2 = gate[None, :, None, None] * brute_force_m(q, k, v, lam, eta, W)
+    y1 = mut(q, k, v, lam, eta, g, W, scale)
+    y0 = mut(q, k, v, lam, np.zeros_like(eta), g, W, scale)
+    caught = np.max(np.abs(y0 - ref_l1)) > 1e-6 or np.max(np.abs((y1 - y0) - ref_l2)) > 1e-6
+    assert caught
+    # and the unmutated decoder passes the same two checks
+    y1 = run_layer_decoder(q, k, v, lam, eta, g, W, scale)
+    y0 = run_layer_decoder(q, k, v, lam, np.zeros_like(eta), g, W, scale)
+    assert np.max(np.abs(y0 - ref_l1)) < 1e-12 and np.max(np.abs((y1 - y0) - ref_l2)) < 1e-12
