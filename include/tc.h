@@ -96,6 +96,30 @@ tc_status tc_decode_step(const void* q, const void* k, const void* v, tc_dtype d
                          int B, int H, int dk, int dv, int W, float* m, hipStream_t s);
 
 /* ---------------------------------------------------------------------------
+ * One full decode step of the layer (Tensor Cache, Methodology 1: L1 exact
+ * softmax over the W-slot ring, the L2 write on eviction and read, and the
+ * gated fusion).  Per sequence b and head h, with p = pos[b]:
+ *   1-3. exactly the steps of tc_decode_step (eviction of slot p mod W into
+ *        A, the new pair into that slot, m = q A after the write);
+ *   4.   y_local = sum_j softmax_j(softmax_scale <q, k_j>) v_j over the pairs
+ *        the ring holds after the write: the W most recent tokens, the
+ *        current one included (min(p + 1, W) of them);
+ *   5.   y = y_local + sigmoid(g[h]) m.
+ * Over a sequence from an empty ring and A = 0 this gives the rows of
+ * tc_fused_layer.  dk == dv.
+ *   q, k, v [B, H, d] in dtype dt; ring_k, ring_v in/out [B, H, W, d] in
+ *   dtype dt; A in/out float32 [B, H, d, d]; lam, eta, g [H] float32;
+ *   pos [B] int64 >= 0 (the caller advances it after the call);
+ *   softmax_scale > 0 (the Python binding passes 1/sqrt(d) by default);
+ *   y out [B, H, d] float32.  No workspace.
+ * ------------------------------------------------------------------------- */
+tc_status tc_decode_layer_step(const void* q, const void* k, const void* v, tc_dtype dt,
+                               void* ring_k, void* ring_v, float* A,
+                               const float* lam, const float* eta, const float* g,
+                               const int64_t* pos, int B, int H, int dk, int dv, int W,
+                               float softmax_scale, float* y, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
  * Fused Tensor Cache layer (Tensor Cache, Methodology 1: L1 exact softmax
  * over the ring, L2 read, gated fusion).
  *
@@ -145,6 +169,7 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
  *   tc_fused_layer      the window-attention + L2-read kernel,
  *   tc_scan_forward     the output kernel,
  *   tc_decode_step      its only kernel,
+ *   tc_decode_layer_step its only kernel,
  *   delta_scan_forward  the kernel that walks the chunks.
  * `before` and `after` are caller-created HIP events (hipEventCreate); the
  * caller reads hipEventElapsedTime(before, after) once the stream is done.

@@ -143,6 +143,27 @@ tc_status tc_decode_step(const void* q, const void* k, const void* v, tc_dtype d
   });
 }
 
+tc_status tc_decode_layer_step(const void* q, const void* k, const void* v, tc_dtype dt,
+                               void* ring_k, void* ring_v, float* A, const float* lam,
+                               const float* eta, const float* g, const int64_t* pos, int B, int H,
+                               int dk, int dv, int W, float softmax_scale, float* y, hipStream_t s) {
+  return guarded("tc_decode_layer_step", [&]() -> tc_status {
+    const char* fn = "tc_decode_layer_step";
+    tc_status st = check_seq(fn, B, H, 1, dk, dv, 64, dt);
+    if (st != TC_OK) return st;
+    if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+    if ((long long)W * dk >= (1LL << 31)) return fail(TC_ERR_UNSUPPORTED, "%s: W * d too large", fn);
+    if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
+      return fail(TC_ERR_INVALID_ARG, "%s: softmax_scale must be finite and > 0", fn);
+    if (B == 0 || H == 0) return ok();
+    if (!q || !k || !v || !ring_k || !ring_v || !A || !lam || !eta || !g || !pos || !y)
+      return fail(TC_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    return from_hip(tc::launch_tc_decode_layer(q, k, v, dt == TC_BF16, ring_k, ring_v, A, lam, eta, g,
+                                               pos, B, H, dk, W, softmax_scale, y, s),
+                    fn);
+  });
+}
+
 size_t tc_fused_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt) {
   const char* fn = "tc_fused_workspace_bytes";
   if (check_seq(fn, B, H, T, dk, dv, chunk, dt) != TC_OK) return SIZE_MAX;

@@ -30,6 +30,11 @@ hipError_t launch_tc_decode(const void* q, const void* k, const void* v, bool bf
                             void* ring_v, float* A, const float* lam, const float* eta,
                             const int64_t* pos, int B, int H, int dk, int dv, int W, float* m,
                             hipStream_t s);
+// Full decode step of the layer (L1 ring softmax + L2 step + gate); d = dk = dv.
+hipError_t launch_tc_decode_layer(const void* q, const void* k, const void* v, bool bf16,
+                                  void* ring_k, void* ring_v, float* A, const float* lam,
+                                  const float* eta, const float* g, const int64_t* pos, int B,
+                                  int H, int d, int W, float scale, float* y, hipStream_t s);
 
 // Benchmark timing hook (armed by tc_profile_next_call, tc_api.cpp): record
 // the armed events around an entry point's main kernel, on its stream.

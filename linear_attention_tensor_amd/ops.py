@@ -16,7 +16,8 @@ import torch
 from . import _lib
 from ._lib import TC_BF16, TC_F32, check, lib
 
-__all__ = ["tc_scan_forward", "tc_decode_step", "tc_fused_layer", "delta_scan_forward",
+__all__ = ["tc_scan_forward", "tc_decode_step", "tc_decode_layer_step", "tc_fused_layer",
+           "delta_scan_forward",
            "scan_workspace", "fused_workspace", "delta_workspace"]
 
 CHUNK = 64
@@ -150,6 +151,43 @@ def tc_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_k: to
                               _ptr(lam), _ptr(eta), _ptr(pos), B, H, dk, dv, W, _ptr(m), _stream())
     check("tc_decode_step", st)
     return m
+
+
+def tc_decode_layer_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_k: torch.Tensor,
+                         ring_v: torch.Tensor, A: torch.Tensor, lam: torch.Tensor, eta: torch.Tensor,
+                         g: torch.Tensor, pos: torch.Tensor, W: int, *,
+                         softmax_scale: Optional[float] = None, y: Optional[torch.Tensor] = None,
+                         check_values: bool = True) -> torch.Tensor:
+    """One full decode step of the layer; updates ring_k, ring_v and A in place and
+    returns y [B,H,dv] = ring softmax attention + sigmoid(g) * L2 read.
+
+    The caller advances ``pos`` (tokens already seen per sequence) afterwards.
+    """
+    _need(q.dim() == 3, "q must be [B, H, dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q)
+    for n, t, s in (("q", q, (B, H, dk)), ("k", k, (B, H, dk)), ("v", v, (B, H, dv)),
+                    ("ring_k", ring_k, (B, H, W, dk)), ("ring_v", ring_v, (B, H, W, dv))):
+        _check_tensor(n, t, s, q.dtype, q.device)
+    _check_tensor("A", A, (B, H, dk, dv), torch.float32, q.device)
+    for n, t in (("lam", lam), ("eta", eta), ("g", g)):
+        _check_tensor(n, t, (H,), torch.float32, q.device)
+    _check_tensor("pos", pos, (B,), torch.int64, q.device)
+    if check_values:
+        _check_unit_interval("lam", lam)
+        if pos.numel() and bool((pos < 0).any()):
+            raise ValueError("pos must be >= 0")
+    scale = 1.0 / math.sqrt(dk) if softmax_scale is None else float(softmax_scale)
+    if y is None:
+        y = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    else:
+        _check_tensor("y", y, (B, H, dv), torch.float32, q.device)
+    st = lib().tc_decode_layer_step(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(ring_k), _ptr(ring_v), _ptr(A),
+                                    _ptr(lam), _ptr(eta), _ptr(g), _ptr(pos), B, H, dk, dv, W, scale,
+                                    _ptr(y), _stream())
+    check("tc_decode_layer_step", st)
+    return y
 
 
 def tc_fused_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torch.Tensor,

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("tc_scan_forward", "tc_decode_step", "tc_fused_layer", "delta_scan_forward",
+    for n in ("tc_scan_forward", "tc_decode_step", "tc_decode_layer_step", "tc_fused_layer", "delta_scan_forward",
               "tc_scan_workspace_bytes", "tc_fused_workspace_bytes", "delta_scan_workspace_bytes",
               "tc_last_error", "tc_version"):
         assert n in names
@@ -100,6 +100,26 @@ def test_decode_rejects():
     bad = list(args); bad[9] = NULL
     assert f(*bad) == _lib.TC_ERR_INVALID_ARG
     ok = list(args); ok[10] = 0
+    assert f(*ok) == _lib.TC_OK
+
+
+def test_decode_layer_rejects():
+    f = lib().tc_decode_layer_step
+    args = [FAKE, FAKE, FAKE, _lib.TC_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 128, 16,
+            0.088, FAKE, NULL]
+    bad = list(args); bad[15] = 0  # W
+    assert f(*bad) == _lib.TC_ERR_INVALID_ARG
+    bad = list(args); bad[13] = 100; bad[14] = 100  # d
+    assert f(*bad) == _lib.TC_ERR_UNSUPPORTED
+    bad = list(args); bad[13] = 64  # dk != dv
+    assert f(*bad) == _lib.TC_ERR_UNSUPPORTED
+    bad = list(args); bad[9] = NULL  # g
+    assert f(*bad) == _lib.TC_ERR_INVALID_ARG
+    bad = list(args); bad[16] = 0.0  # softmax scale
+    assert f(*bad) == _lib.TC_ERR_INVALID_ARG
+    bad = list(args); bad[16] = float("nan")
+    assert f(*bad) == _lib.TC_ERR_INVALID_ARG
+    ok = list(args); ok[11] = 0  # B = 0: nothing to do, no device touched
     assert f(*ok) == _lib.TC_OK
 
 
