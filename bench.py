@@ -39,7 +39,7 @@ def parse():
                     help="untimed calls first: the GPU needs some tens of ms of load to reach its steady clock")
     ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fused", "scan", "decode", "delta"], default=None,
+    ap.add_argument("--only", choices=["fused", "scan", "decode", "decode_layer", "delta"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy twice (the reference for "
@@ -83,6 +83,11 @@ def scan_bytes(B, H, T, d, in_bytes):
 def decode_bytes_per_head(d, in_bytes=2):
     # A read + written (fp32), q, k, v in, evicted pair read, new pair written, m out
     return 2 * d * d * 4 + 3 * d * in_bytes + 2 * d * in_bytes + 2 * d * in_bytes + d * 4
+
+
+def decode_layer_bytes_per_head(d, W, in_bytes=2):
+    # the L2 step, plus the other W - 1 ring slots (k and v) read for the window softmax
+    return decode_bytes_per_head(d, in_bytes) + 2 * (W - 1) * d * in_bytes
 
 
 def delta_bytes(B, H, T, d, in_bytes=2):
@@ -334,6 +339,60 @@ def bench_decode(steps, warmup, dev, n_steps=4096):
             "config": {"B": B, "H": H, "d": d, "W": W, "steps": n_steps, "dtype_in": "bf16"}}
 
 
+def bench_decode_layer(steps, warmup, dev, n_steps=256):
+    """Full decode step of the layer (ring softmax + L2 + gate) on the decode workload."""
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["decode_bf16"]
+    B, H, d, W = w.B, w.H, w.d, w.W
+    gen = torch.Generator(device=dev).manual_seed(w.seed + 1)
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+
+    scale = 1.0 / math.sqrt(d)
+    qs = (torch.randn((n_steps, B, H, d), generator=gen, device=dev) * scale).to(torch.bfloat16)
+    ks = unit(torch.randn((n_steps, B, H, d), generator=gen, device=dev)).to(torch.bfloat16)
+    vs = (torch.randn((n_steps, B, H, d), generator=gen, device=dev) * scale).to(torch.bfloat16)
+    ring_k = unit(torch.randn((B, H, W, d), generator=gen, device=dev)).to(torch.bfloat16)
+    ring_v = (torch.randn((B, H, W, d), generator=gen, device=dev) * scale).to(torch.bfloat16)
+    A = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+    sc = I.decode_scalars(H)
+    lam, eta = to_dev_f32(sc["lam"], dev), to_dev_f32(sc["eta"], dev)
+    g = torch.randn((H,), generator=gen, device=dev)
+    pos = (W + torch.arange(n_steps + warmup, device=dev, dtype=torch.int64))[:, None].repeat(1, B).contiguous()
+    y = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    lib = ops.lib()
+    st = ops._stream()
+    P = ops._ptr
+    qp = [P(qs[i]) for i in range(n_steps)]
+    kp = [P(ks[i]) for i in range(n_steps)]
+    vp = [P(vs[i]) for i in range(n_steps)]
+    pp = [P(pos[i]) for i in range(n_steps + warmup)]
+    rk, rv, Ap, lp, ep, gp, yp = P(ring_k), P(ring_v), P(A), P(lam), P(eta), P(g), P(y)
+    counter = {"i": 0}
+
+    def call(i):
+        j = counter["i"]
+        counter["i"] += 1
+        s = lib.tc_decode_layer_step(qp[j % n_steps], kp[j % n_steps], vp[j % n_steps], 1, rk, rv, Ap, lp,
+                                     ep, gp, pp[j], B, H, d, d, W, scale, yp, st)
+        if s != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, kernel_ms = time_calls(call, n_steps, warmup, KernelTimer(n_steps))
+    per_head = decode_layer_bytes_per_head(d, W)
+    gbs = B * H * per_head / (kernel_ms * 1e-3) / 1e9
+    return {"workload": w.name + " (full layer step)", "ms_per_step": ms, "tokens_per_s": B * H / (ms * 1e-3),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
+            "note": "per head-step: the ring (2 (W-1) d bf16) plus the L2 step; GB/s is algorithmic bytes / kernel time",
+            "main_kernel": {"name": "decode_layer_kernel", "ms": kernel_ms}, "ms_per_call": ms_call,
+            "config": {"B": B, "H": H, "d": d, "W": W, "steps": n_steps, "dtype_in": "bf16"}}
+
+
 def bench_delta(steps, warmup, dev):
     import torch
 
@@ -415,11 +474,14 @@ def main():
     if only is None and not args.no_components:
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
+        components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
     elif only == "scan":
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
     elif only == "decode":
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
+    elif only == "decode_layer":
+        components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
     elif only == "delta":
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
     if only not in (None, "fused"):

@@ -108,28 +108,33 @@ struct Piece;
 template <>
 struct Piece<float> {
   static constexpr int E = 4;
-  __device__ __forceinline__ static void load(const float* p, float* x) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  __device__ __forceinline__ static void cvt(u32x4 a, float* x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(a[i]);
   }
 };
 template <>
 struct Piece<uint16_t> {
   static constexpr int E = 8;
-  __device__ __forceinline__ static void load(const uint16_t* p, float* x) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  __device__ __forceinline__ static void cvt(u32x4 a, float* x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      x[2 * i] = __uint_as_float(a[i] << 16);
+      x[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
     }
   }
 };
+// Ring loads are non-temporal: the ring streams through once per step, and
+// marking it so keeps A (reused every step) in the caches.
+template <typename TIn>
+__device__ __forceinline__ u32x4 ld16(const TIn* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // One decode step of the whole layer per (b, h): the L2 step above, then
 // y = softmax over the ring after the write (the current token included)
-// + sigmoid(g) m.  Wave w walks ring slots [lo_w, hi_w); every group of LPR
+// + sigmoid(g) m.  The four waves take turns over batches of consecutive ring
+// slots (so the workgroup reads one K and one V stream); every group of LPR
 // lanes keeps its own running maximum, sum and output piece, merged at the end.
 template <typename TIn, int D>
 __global__ __launch_bounds__(256) void decode_layer_kernel(
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(256) void decode_layer_kernel(
     TIn* __restrict__ ring_k, TIn* __restrict__ ring_v, float* __restrict__ A,
     const float* __restrict__ lam, const float* __restrict__ eta, const float* __restrict__ g,
     const int64_t* __restrict__ pos, int H, int W, float sl2, float* __restrict__ y) {
-  constexpr int E = Piece<TIn>::E, LPR = D / E, RPI = 64 / LPR, U = 4;
+  constexpr int E = Piece<TIn>::E, LPR = D / E, RPI = 64 / LPR, U = 2;
   static_assert(D % E == 0 && LPR <= 64, "row pieces");
   __shared__ float sq[D], ske[D], sve[D], skn[D], svn[D], sm[D];
   __shared__ float4 part[256];
@@ -196,8 +201,8 @@ __global__ __launch_bounds__(256) void decode_layer_kernel(
   // without the slot just overwritten; the current token is added at the end.
   const int w = t >> 6, l = t & 63, c = l % LPR, rs = l / LPR;
   const int n_ring = (int)(p < W ? p : W);
-  const int per_w = (n_ring + 3) / 4;
-  const int lo = min(n_ring, w * per_w), hi = min(n_ring, lo + per_w);
+  const int lo = 0, hi = n_ring;
+  constexpr int BATCH = RPI * U;  // slots per wave and batch; wave w takes batches w, w + 4, ...
   float qs[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) qs[e] = sq[c * E + e] * sl2;
@@ -206,21 +211,40 @@ __global__ __launch_bounds__(256) void decode_layer_kernel(
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   const TIn* kb = ring_k + (long)bh * W * D + c * E;
   const TIn* vb = ring_v + (long)bh * W * D + c * E;
-  for (int r0 = lo; r0 < hi; r0 += RPI * U) {
-    float sc[U], kx[U][E], vx[U][E];
+  // The K and V pieces of a batch (U rows per lane group) are loaded one
+  // batch ahead; rows past the range reload a valid row whose values are
+  // not used.
+  u32x4 kr[U], vr[U];
+  auto load_batch = [&](int r0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = r0 + u * RPI + rs;
-      const bool ok = row < hi && row != slot;
-      const int rr = ok ? row : lo;  // a valid row; its values are not used
-      Piece<TIn>::load(kb + (long)rr * D, kx[u]);
-      Piece<TIn>::load(vb + (long)rr * D, vx[u]);
-      float d = 0.f;
+      const int rr = row < hi ? row : lo;
+      kr[u] = ld16(kb + (long)rr * D);
+      vr[u] = ld16(vb + (long)rr * D);
+    }
+  };
+  if (w * BATCH < hi) load_batch(w * BATCH);
+  for (int r0 = w * BATCH; r0 < hi; r0 += 4 * BATCH) {
+    float sc[U], vx[U][E];
+    {
+      float kx[U][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) d = fmaf(qs[e], kx[u][e], d);
+      for (int u = 0; u < U; ++u) {
+        Piece<TIn>::cvt(kr[u], kx[u]);
+        Piece<TIn>::cvt(vr[u], vx[u]);
+      }
+      if (r0 + 4 * BATCH < hi) load_batch(r0 + 4 * BATCH);
 #pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
-      sc[u] = ok ? d : -INFINITY;
+      for (int u = 0; u < U; ++u) {
+        const int row = r0 + u * RPI + rs;
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) d = fmaf(qs[e], kx[u][e], d);
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+        sc[u] = row < hi && row != slot ? d : -INFINITY;
+      }
     }
     float bm = mx;
 #pragma unroll
