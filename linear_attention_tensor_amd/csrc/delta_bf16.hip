@@ -96,7 +96,7 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
 // delta_prep: one wave per (chunk, b, h).  Every output leaves in 16-byte
 // (A, K^T) or 8-byte (tril(Q K^T)) pieces per lane: A and K^T are first
 // transposed through LDS.  One buffer holds in turn the K^T staging, Q, L and
-// the A staging, so that four workgroups fit in a CU's LDS.
+// M = (I + L)^-1, so that four workgroups fit in a CU's LDS.
 template <int D>
 __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ k,
@@ -108,8 +108,10 @@ __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restri
   constexpr int LS = CH + 4;  // fp32 L rows, 16-byte aligned
   static_assert(D * CH * 2 <= CH * LS * 4, "K^T and Q fit the L buffer");
   __shared__ __attribute__((aligned(16))) uint16_t sK[CH * D];
-  __shared__ __attribute__((aligned(16))) float sL[CH * LS];  // K^T staging, Q, L, A staging
+  __shared__ __attribute__((aligned(16))) float sL[CH * LS];  // K^T staging, Q, L, M
   __shared__ float sB[CH];
+  __shared__ float sD[CH * 17];  // the diagonal blocks of M, [64][16] (+1 pad)
+  __shared__ float sT[16 * 17];  // one 16 x 16 block product
   uint16_t* const sQ = reinterpret_cast<uint16_t*>(sL);
   const int n = blockIdx.x, bh = blockIdx.y, l = threadIdx.x;
   const int t0 = n * CH;
@@ -192,35 +194,86 @@ __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restri
     }
   }
   __syncthreads();
-  // M = (I + L)^-1, one column per lane: M[r] = e_r - sum_{i<r} L[r][i] M[i]
-  float m[CH];
+  // M = (I + L)^-1 by 16 x 16 blocks (L strictly lower triangular):
+  //   M_ii = (I + L_ii)^-1 by forward substitution, one column per lane;
+  //   M_ij = -M_ii sum_{k=j}^{i-1} L_ik M_kj (i > j), block row by block row,
+  // on fp32 MFMA.  Block row i of M overwrites block row i of L once the row
+  // is complete (later rows read only L's own row and M's earlier rows).
+  {
+    const int ib = l >> 4, c = l & 15;  // this lane's diagonal block and column
+    float md[16];
 #pragma unroll
-  for (int r = 0; r < CH; ++r) m[r] = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float s0 = r == c ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-  for (int r = 0; r < CH; ++r) {
-    float s0 = r == l ? 1.f : 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < r; i += 4) {  // L[r][i..i+3] is 0 past r - 1
-      const float4 lv = *reinterpret_cast<const float4*>(sL + r * LS + i);
-      s0 = fmaf(-lv.x, m[i], s0);
-      s1 = fmaf(-lv.y, m[i + 1], s1);
-      s2 = fmaf(-lv.z, m[i + 2], s2);
-      s3 = fmaf(-lv.w, m[i + 3], s3);
+      for (int k = 0; k < r; k += 2) {
+        s0 = fmaf(-sL[(16 * ib + r) * LS + 16 * ib + k], md[k], s0);
+        if (k + 1 < r) s1 = fmaf(-sL[(16 * ib + r) * LS + 16 * ib + k + 1], md[k + 1], s1);
+      }
+      md[r] = s0 + s1;
     }
-    m[r] = (s0 + s1) + (s2 + s3);
-  }
-  __syncthreads();  // every row of L has been read
-  // A = M diag(beta) (column l scaled by beta_l), transposed through LDS and
-  // written as a bf16 pair A = A_hi + A_lo, [hi | lo] row-major
 #pragma unroll
-  for (int r = 0; r < CH; ++r) sL[r * LS + l] = m[r] * b;
+    for (int r = 0; r < 16; ++r) sD[(16 * ib + r) * 17 + c] = md[r];
+  }
   __syncthreads();
+  {
+    const int n16 = l & 15, g = l >> 4;
+    // block (i, i) of M into block row i of the L buffer
+    auto put_diag = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sL[(16 * i + 4 * g + e) * LS + 16 * i + n16] = sD[(16 * i + 4 * g + e) * 17 + n16];
+    };
+    put_diag(0);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      floatx4 res[3];
+#pragma unroll
+      for (int j = 0; j < i; ++j) {
+        floatx4 t = zero4();  // sum_{k=j}^{i-1} L_ik M_kj
+#pragma unroll
+        for (int k = j; k < i; ++k) {
+#pragma unroll
+          for (int kk = 0; kk < 16; kk += 4) {
+            const float av = sL[(16 * i + n16) * LS + 16 * k + kk + g];
+            const float bv = k == j ? sD[(16 * j + kk + g) * 17 + n16]
+                                    : sL[(16 * k + kk + g) * LS + 16 * j + n16];
+            t = mfma4(av, bv, t);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sT[(4 * g + e) * 17 + n16] = t[e];
+        __syncthreads();
+        floatx4 mm = zero4();  // M_ii t
+#pragma unroll
+        for (int kk = 0; kk < 16; kk += 4)
+          mm = mfma4(sD[(16 * i + n16) * 17 + kk + g], sT[(kk + g) * 17 + n16], mm);
+        __syncthreads();  // sT is reused by the next block
+        res[j] = -mm;
+      }
+#pragma unroll
+      for (int j = 0; j < i; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sL[(16 * i + 4 * g + e) * LS + 16 * j + n16] = res[j][e];
+      put_diag(i);
+    }
+  }
+  __syncthreads();
+  // A = M diag(beta), written as a bf16 pair A = A_hi + A_lo, [hi | lo] row-major
   uint16_t* ao = a_out + ((long)bh * n_chunks + n) * 2 * CH * CH;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int s = i * 64 + l, r = s >> 3, c8 = 8 * (s & 7);
-    const float4 x0 = *reinterpret_cast<const float4*>(sL + r * LS + c8);
-    const float4 x1 = *reinterpret_cast<const float4*>(sL + r * LS + c8 + 4);
+    float4 x0 = *reinterpret_cast<const float4*>(sL + r * LS + c8);
+    float4 x1 = *reinterpret_cast<const float4*>(sL + r * LS + c8 + 4);
+    x0.x *= sB[c8];
+    x0.y *= sB[c8 + 1];
+    x0.z *= sB[c8 + 2];
+    x0.w *= sB[c8 + 3];
+    x1.x *= sB[c8 + 4];
+    x1.y *= sB[c8 + 5];
+    x1.z *= sB[c8 + 6];
+    x1.w *= sB[c8 + 7];
     uint32_t h[4], lo[4];
     split2(x0.x, x0.y, h[0], lo[0]);
     split2(x0.z, x0.w, h[1], lo[1]);
