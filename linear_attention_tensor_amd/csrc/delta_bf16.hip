@@ -12,7 +12,7 @@
 //   U = A (V - K S0^T),  A = (I + diag(beta) tril_{-1}(K K^T))^-1 diag(beta),
 //   O = Q S0^T + tril_0(Q K^T) U,      S = S0 + U^T K.
 // A depends on K and beta only, so it is computed for every chunk at once:
-//   delta_prep   per (chunk, b, h): A by forward substitution (fp32), stored
+//   delta_prep   per (chunk, b, h): A by blocked inversion (fp32), stored
 //                as a bf16 pair A = A_hi + A_lo, K^T of the chunk and
 //                tril_0(Q K^T) (bf16; it depends on q and k only);
 //   delta_main   per (b, h, 16-row slice of S): walks the chunks in order.
@@ -93,78 +93,85 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// delta_prep: one wave per (chunk, b, h).  Every output leaves in 16-byte
-// (A, K^T) or 8-byte (tril(Q K^T)) pieces per lane: A and K^T are first
-// transposed through LDS.  One buffer holds in turn the K^T staging, Q, L and
-// M = (I + L)^-1, so that four workgroups fit in a CU's LDS.
+// delta_prep: four waves per (chunk, b, h).  Every output leaves in 16-byte
+// (A, K^T) or 8-byte (tril(Q K^T)) pieces per lane.  One buffer holds in
+// turn the K^T staging, Q, L and M = (I + L)^-1, so that four workgroups
+// fit in a CU's LDS.
 template <int D>
-__global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restrict__ q,
-                                                        const uint16_t* __restrict__ k,
-                                                        const float* __restrict__ beta, int T,
-                                                        int n_chunks, uint16_t* __restrict__ a_out,
-                                                        uint16_t* __restrict__ kt_out,
-                                                        uint16_t* __restrict__ qm_out) {
+__global__ __launch_bounds__(256) void delta_prep_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k,
+                                                         const float* __restrict__ beta, int T,
+                                                         int n_chunks, uint16_t* __restrict__ a_out,
+                                                         uint16_t* __restrict__ kt_out,
+                                                         uint16_t* __restrict__ qm_out) {
   constexpr int NCH = D / 8;
-  constexpr int LS = CH + 4;  // fp32 L rows, 16-byte aligned
+  constexpr int LS = CH + 4;                 // fp32 rows of L and M, 16-byte aligned
+  constexpr int NP = CH * NCH / 256;         // 16-byte pieces per thread of a [64][D] array
   static_assert(D * CH * 2 <= CH * LS * 4, "K^T and Q fit the L buffer");
   __shared__ __attribute__((aligned(16))) uint16_t sK[CH * D];
   __shared__ __attribute__((aligned(16))) float sL[CH * LS];  // K^T staging, Q, L, M
+  __shared__ float sT[4][16 * 17];                            // one block product per wave
   __shared__ float sB[CH];
-  __shared__ float sD[CH * 17];  // the diagonal blocks of M, [64][16] (+1 pad)
-  __shared__ float sT[16 * 17];  // one 16 x 16 block product
   uint16_t* const sQ = reinterpret_cast<uint16_t*>(sL);
-  const int n = blockIdx.x, bh = blockIdx.y, l = threadIdx.x;
+  uint16_t* const skt = reinterpret_cast<uint16_t*>(sL);
+  const int n = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int w = wave_id(), l = lane_id(), lr = l & 15, lg = l >> 4;
   const int t0 = n * CH;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (long)bh * T * D, (uint32_t)T * D * 2);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (long)bh * T * D, (uint32_t)T * D * 2);
-  // lane l: key and query t0 + l (zero past T)
-  uint4 kr[NCH], qr[NCH];
+
+  // rows of K and Q (zero past T); piece i of this thread is row s / NCH,
+  // chunk s % NCH with s = 256 i + t
+  uint4 kr[NP], qr[NP];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) kr[c] = buf_load16(rk, ((t0 + l) * D + 8 * c) * 2);
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) qr[c] = buf_load16(rq, ((t0 + l) * D + 8 * c) * 2);
-  const float b = t0 + l < T ? beta[(long)bh * T + t0 + l] : 0.f;
-  sB[l] = b;
+  for (int i = 0; i < NP; ++i) {
+    const int s = i * 256 + t, row = s / NCH, c = s % NCH;
+    kr[i] = buf_load16(rk, ((t0 + row) * D + 8 * c) * 2);
+    qr[i] = buf_load16(rq, ((t0 + row) * D + 8 * c) * 2);
+  }
+  if (t < CH) sB[t] = t0 + t < T ? beta[(long)bh * T + t0 + t] : 0.f;
   // K into sK and, transposed, into the staging area ([dk][key] bf16)
-  uint16_t* skt = reinterpret_cast<uint16_t*>(sL);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    *reinterpret_cast<uint4*>(sK + pos<NCH>(l, c)) = kr[c];
-    const uint32_t w4[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+  for (int i = 0; i < NP; ++i) {
+    const int s = i * 256 + t, row = s / NCH, c = s % NCH;
+    *reinterpret_cast<uint4*>(sK + pos<NCH>(row, c)) = kr[i];
+    const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      skt[(8 * c + 2 * e) * CH + l] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
-      skt[(8 * c + 2 * e + 1) * CH + l] = static_cast<uint16_t>(w4[e] >> 16);
+      skt[(8 * c + 2 * e) * CH + row] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
+      skt[(8 * c + 2 * e + 1) * CH + row] = static_cast<uint16_t>(w4[e] >> 16);
     }
   }
   __syncthreads();
   // K^T of the chunk: D rows of 64 keys, eight 16-byte pieces per row
   uint16_t* kt = kt_out + ((long)bh * n_chunks + n) * D * CH;
 #pragma unroll
-  for (int i = 0; i < D / 8; ++i) {
-    const int s = i * 64 + l;
+  for (int i = 0; i < D / 32; ++i) {
+    const int s = i * 256 + t;
     *reinterpret_cast<uint4*>(kt + s * 8) = *reinterpret_cast<const uint4*>(skt + s * 8);
   }
   __syncthreads();  // the staged K^T has been read: Q takes its place
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) *reinterpret_cast<uint4*>(sQ + pos<NCH>(l, c)) = qr[c];
+  for (int i = 0; i < NP; ++i) {
+    const int s = i * 256 + t, row = s / NCH, c = s % NCH;
+    *reinterpret_cast<uint4*>(sQ + pos<NCH>(row, c)) = qr[i];
+  }
   __syncthreads();
-  // tril_0(Q K^T) of the chunk, bf16 row-major [query][key], computed as its
-  // transpose (keys as M) so that a lane holds four consecutive keys of one
-  // query: tile (mi, ni) = keys 16 mi.., queries 16 ni..; zero for mi > ni
-  const int lr = l & 15, lg = l >> 4;
-  uint16_t* qm = qm_out + ((long)bh * n_chunks + n) * CH * CH;
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+  // tril_0(Q K^T), bf16 row-major [query][key], formed as its transpose (keys
+  // as M) so that a lane holds four consecutive keys of one query: wave w
+  // takes queries 16w.., tile mi = keys 16mi.. (zero for mi > w)
+  {
+    uint16_t* qm = qm_out + ((long)bh * n_chunks + n) * CH * CH;
+    const int ni = w, rq = 16 * ni + lr;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      const int rq = 16 * ni + lr, c0 = 16 * mi + 4 * lg;  // query, first of four keys
+      const int c0 = 16 * mi + 4 * lg;
       uint2 out = make_uint2(0u, 0u);
       if (mi <= ni) {
         floatx4 acc = zero4();
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks)
-          acc = mma(ldc<NCH>(sK, 16 * mi + lr, 4 * ks + lg), ldc<NCH>(sQ, 16 * ni + lr, 4 * ks + lg), acc);
+          acc = mma(ldc<NCH>(sK, 16 * mi + lr, 4 * ks + lg), ldc<NCH>(sQ, rq, 4 * ks + lg), acc);
         out = make_uint2(cvt_pk(c0 <= rq ? acc[0] : 0.f, c0 + 1 <= rq ? acc[1] : 0.f),
                          cvt_pk(c0 + 2 <= rq ? acc[2] : 0.f, c0 + 3 <= rq ? acc[3] : 0.f));
       }
@@ -172,9 +179,9 @@ __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restri
     }
   }
   __syncthreads();  // Q has been read: L takes its place
-  // L = diag(beta) tril_{-1}(K K^T): tiles (mi, ni) with ni <= mi
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  // L = diag(beta) tril_{-1}(K K^T): wave w takes rows 16w.. (tiles ni <= w)
+  {
+    const int mi = w;
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       if (ni > mi) {
@@ -194,76 +201,64 @@ __global__ __launch_bounds__(64) void delta_prep_kernel(const uint16_t* __restri
     }
   }
   __syncthreads();
-  // M = (I + L)^-1 by 16 x 16 blocks (L strictly lower triangular):
-  //   M_ii = (I + L_ii)^-1 by forward substitution, one column per lane;
-  //   M_ij = -M_ii sum_{k=j}^{i-1} L_ik M_kj (i > j), block row by block row,
-  // on fp32 MFMA.  Block row i of M overwrites block row i of L once the row
-  // is complete (later rows read only L's own row and M's earlier rows).
+  // M = (I + L)^-1 by 16 x 16 blocks (L strictly lower triangular), in place:
+  //   M_ii = (I + L_ii)^-1 by forward substitution (wave i, one column per
+  //   lane; lanes 16.. repeat columns 0..15);
+  //   M_ij = -M_ii sum_{k=j}^{i-1} L_ik M_kj (wave j), block row by block row.
   {
-    const int ib = l >> 4, c = l & 15;  // this lane's diagonal block and column
+    const int c = l & 15;
     float md[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      const float* row = sL + (16 * w + r) * LS + 16 * w;
       float s0 = r == c ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-      for (int k = 0; k < r; k += 2) {
-        s0 = fmaf(-sL[(16 * ib + r) * LS + 16 * ib + k], md[k], s0);
-        if (k + 1 < r) s1 = fmaf(-sL[(16 * ib + r) * LS + 16 * ib + k + 1], md[k + 1], s1);
+      for (int kk = 0; kk < r; kk += 2) {
+        s0 = fmaf(-row[kk], md[kk], s0);
+        if (kk + 1 < r) s1 = fmaf(-row[kk + 1], md[kk + 1], s1);
       }
       md[r] = s0 + s1;
     }
+    if (l < 16) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sD[(16 * ib + r) * 17 + c] = md[r];
-  }
-  __syncthreads();
-  {
-    const int n16 = l & 15, g = l >> 4;
-    // block (i, i) of M into block row i of the L buffer
-    auto put_diag = [&](int i) __attribute__((always_inline)) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sL[(16 * i + 4 * g + e) * LS + 16 * i + n16] = sD[(16 * i + 4 * g + e) * 17 + n16];
-    };
-    put_diag(0);
-#pragma unroll
-    for (int i = 1; i < 4; ++i) {
-      floatx4 res[3];
-#pragma unroll
-      for (int j = 0; j < i; ++j) {
-        floatx4 t = zero4();  // sum_{k=j}^{i-1} L_ik M_kj
-#pragma unroll
-        for (int k = j; k < i; ++k) {
-#pragma unroll
-          for (int kk = 0; kk < 16; kk += 4) {
-            const float av = sL[(16 * i + n16) * LS + 16 * k + kk + g];
-            const float bv = k == j ? sD[(16 * j + kk + g) * 17 + n16]
-                                    : sL[(16 * k + kk + g) * LS + 16 * j + n16];
-            t = mfma4(av, bv, t);
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sT[(4 * g + e) * 17 + n16] = t[e];
-        __syncthreads();
-        floatx4 mm = zero4();  // M_ii t
-#pragma unroll
-        for (int kk = 0; kk < 16; kk += 4)
-          mm = mfma4(sD[(16 * i + n16) * 17 + kk + g], sT[(kk + g) * 17 + n16], mm);
-        __syncthreads();  // sT is reused by the next block
-        res[j] = -mm;
-      }
-#pragma unroll
-      for (int j = 0; j < i; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sL[(16 * i + 4 * g + e) * LS + 16 * j + n16] = res[j][e];
-      put_diag(i);
+      for (int r = 0; r < 16; ++r) sL[(16 * w + r) * LS + 16 * w + c] = md[r];
     }
   }
   __syncthreads();
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    const int j = w;
+    floatx4 res = zero4();
+    if (j < i) {
+      floatx4 tt = zero4();  // sum_{k=j}^{i-1} L_ik M_kj
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb) {
+        const int kk0 = j + kb;
+        if (kk0 >= i) break;
+#pragma unroll
+        for (int kk = 0; kk < 16; kk += 4)
+          tt = mfma4(sL[(16 * i + lr) * LS + 16 * kk0 + kk + lg], sL[(16 * kk0 + kk + lg) * LS + 16 * j + lr], tt);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[w][(4 * lg + e) * 17 + lr] = tt[e];
+      floatx4 mm = zero4();  // M_ii tt (the wave reads back what it wrote)
+#pragma unroll
+      for (int kk = 0; kk < 16; kk += 4)
+        mm = mfma4(sL[(16 * i + lr) * LS + 16 * i + kk + lg], sT[w][(kk + lg) * 17 + lr], mm);
+      res = -mm;
+    }
+    __syncthreads();  // every wave is done reading L's row i
+    if (j < i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sL[(16 * i + 4 * lg + e) * LS + 16 * j + lr] = res[e];
+    }
+    __syncthreads();
+  }
   // A = M diag(beta), written as a bf16 pair A = A_hi + A_lo, [hi | lo] row-major
   uint16_t* ao = a_out + ((long)bh * n_chunks + n) * 2 * CH * CH;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int s = i * 64 + l, r = s >> 3, c8 = 8 * (s & 7);
+  for (int i = 0; i < 2; ++i) {
+    const int s = i * 256 + t, r = s >> 3, c8 = 8 * (s & 7);
     float4 x0 = *reinterpret_cast<const float4*>(sL + r * LS + c8);
     float4 x1 = *reinterpret_cast<const float4*>(sL + r * LS + c8 + 4);
     x0.x *= sB[c8];
@@ -553,7 +548,7 @@ hipError_t run_delta_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* 
   uint16_t* kt_ws = a_ws + (size_t)BH * n_chunks * 2 * CH * CH;
   uint16_t* qm_ws = kt_ws + (size_t)BH * n_chunks * D * CH;
   if (n_chunks > 0)
-    hipLaunchKernelGGL(delta_prep_kernel<D>, dim3(n_chunks, BH), dim3(64), 0, s, q, k, beta, T,
+    hipLaunchKernelGGL(delta_prep_kernel<D>, dim3(n_chunks, BH), dim3(256), 0, s, q, k, beta, T,
                        n_chunks, a_ws, kt_ws, qm_ws);
   const int n_items = BH * (D / DVT);
   const int grid = (n_items + NXCD - 1) / NXCD * NXCD;
