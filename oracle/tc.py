@@ -38,6 +38,7 @@ __all__ = [
     "tc_fused_rows",
     "tc_scan_chunked",
     "chunk_mean_scan",
+    "tc_scan_backward",
 ]
 
 
@@ -306,3 +307,52 @@ def chunk_mean_scan(q, k, v, lam, eta, W, C=64):
         m[:, :, s0 + W : s0 + W + L, :] = np.einsum(
             "bhtd,bhde->bhte", q[:, :, s0 + W : s0 + W + L, :], A)
     return m, A
+
+
+def tc_scan_backward(q, k, v, lam, eta, W, dm):
+    """Gradients of L = sum <dm, m> through the L2 read m of ``tc_scan``.
+
+    Tensor Cache, Methodology 1 (the write A <- lam A + eta k v^T on
+    eviction, the read m_t = q_t A) and Methodology 2 (lam, eta are learned
+    per head).  Reverse-mode through the sequential recurrence: the states
+    A_t of the forward pass are kept, and dA accumulates q_t dm_t^T going
+    backwards; a write at step t (token e = t - W) sends
+    eta dA v_e to k_e, eta dA^T k_e to v_e, <dA, A_{t-1}> to lam and
+    <dA, k_e v_e^T> to eta, and then dA <- lam dA.  A_final takes no
+    upstream gradient.
+
+    Returns (dq [B,H,T,dk], dk [B,H,T,dk], dv [B,H,T,dv], dlam [H], deta [H]);
+    dlam and deta are summed over the batch.
+    """
+    q, k, v, dm = _f64(q), _f64(k), _f64(v), _f64(dm)
+    lam, eta = _f64(lam), _f64(eta)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    lm = lam[None, :, None, None]
+    et = eta[None, :, None, None]
+    A = np.zeros((B, H, dk, dv))
+    states = []  # A_t after step t
+    for t in range(T):
+        if t >= W:
+            e = t - W
+            A = lm * A + et * np.einsum("bhi,bhj->bhij", k[:, :, e], v[:, :, e])
+        states.append(A.copy())
+    gq = np.zeros_like(q)
+    gk = np.zeros_like(k)
+    gv = np.zeros_like(v)
+    glam = np.zeros((B, H))
+    geta = np.zeros((B, H))
+    dA = np.zeros((B, H, dk, dv))
+    for t in range(T - 1, -1, -1):
+        gq[:, :, t] = np.einsum("bhij,bhj->bhi", states[t], dm[:, :, t])
+        dA = dA + np.einsum("bhi,bhj->bhij", q[:, :, t], dm[:, :, t])
+        if t >= W:
+            e = t - W
+            prev = states[t - 1] if t >= 1 else np.zeros_like(dA)
+            glam += np.einsum("bhij,bhij->bh", dA, prev)
+            kv = np.einsum("bhi,bhj->bhij", k[:, :, e], v[:, :, e])
+            geta += np.einsum("bhij,bhij->bh", dA, kv)
+            gk[:, :, e] += et[..., 0] * np.einsum("bhij,bhj->bhi", dA, v[:, :, e])
+            gv[:, :, e] += et[..., 0] * np.einsum("bhij,bhi->bhj", dA, k[:, :, e])
+            dA = lm * dA
+    return gq, gk, gv, glam.sum(axis=0), geta.sum(axis=0)

@@ -453,3 +453,128 @@ def test_decode_layer_pins_catch_planted_mistakes(kind):
     y1 = run_layer_decoder(q, k, v, lam, eta, g, W, scale)
     y0 = run_layer_decoder(q, k, v, lam, np.zeros_like(eta), g, W, scale)
     assert np.max(np.abs(y0 - ref_l1)) < 1e-12 and np.max(np.abs((y1 - y0) - ref_l2)) < 1e-12
+
+
+# ---------------------------------------------------------------- backward of the scan
+
+def _scan_loss(q, k, v, lam, eta, W, dm):
+    return float(np.sum(O.tc_scan(q, k, v, lam, eta, W)[0] * dm))
+
+
+@pytest.mark.parametrize("W,lam_kind", [(3, "u"), (1, "u"), (3, "0"), (3, "1"), (20, "u")])
+def test_scan_backward_matches_central_differences(W, lam_kind):
+    # every partial derivative against a central difference of the forward oracle
+    q, k, v, lam, eta, _ = rand_inputs(50, B=1, H=2, T=12, dk=3, dv=3)
+    lam = {"u": lam, "0": np.zeros(2), "1": np.ones(2)}[lam_kind]
+    dm = np.random.default_rng(51).standard_normal(q.shape[:3] + (3,))
+    gq, gk, gv, glam, geta = O.tc_scan_backward(q, k, v, lam, eta, W, dm)
+    h = 1e-6
+    for name, x, g in (("q", q, gq), ("k", k, gk), ("v", v, gv)):
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[i] += h
+            xm[i] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _scan_loss(args["q"], args["k"], args["v"], lam, eta, W, dm)
+            args[name] = xm
+            lmn = _scan_loss(args["q"], args["k"], args["v"], lam, eta, W, dm)
+            fd[i] = (lp - lmn) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8, err_msg=name)
+    for hh in range(2):
+        for name, g in (("lam", glam), ("eta", geta)):
+            base = {"lam": lam, "eta": eta}[name]
+            if name == "lam" and lam_kind == "0":
+                continue  # lam = 0 sits on the edge of [0, 1]; checked one-sided below
+            xp, xm = base.copy(), base.copy()
+            xp[hh] += h
+            xm[hh] -= h
+            a = {"lam": lam, "eta": eta}
+            a[name] = xp
+            lp = _scan_loss(q, k, v, a["lam"], a["eta"], W, dm)
+            a[name] = xm
+            lmn = _scan_loss(q, k, v, a["lam"], a["eta"], W, dm)
+            np.testing.assert_allclose(g[hh], (lp - lmn) / (2 * h), rtol=1e-6, atol=1e-8, err_msg=name)
+    if lam_kind == "0":  # one-sided difference at lam = 0 (forward differences, second order)
+        for hh in range(2):
+            l1, l2 = lam.copy(), lam.copy()
+            l1[hh], l2[hh] = h, 2 * h
+            f0 = _scan_loss(q, k, v, lam, eta, W, dm)
+            f1 = _scan_loss(q, k, v, l1, eta, W, dm)
+            f2 = _scan_loss(q, k, v, l2, eta, W, dm)
+            np.testing.assert_allclose(glam[hh], (-3 * f0 + 4 * f1 - f2) / (2 * h), rtol=1e-5, atol=1e-7)
+
+
+def test_scan_backward_lambda_one_matches_autograd_of_cumulative_sum():
+    # lam = 1: m_t = eta q_t sum_{i <= t-W} k_i v_i^T, a cumsum; torch autograd of that formula
+    q, k, v, _, eta, _ = rand_inputs(52, B=2, H=2, T=30, dk=4, dv=5)
+    W = 6
+    dm = np.random.default_rng(53).standard_normal(q.shape[:3] + (5,))
+    gq, gk, gv, _, geta = O.tc_scan_backward(q, k, v, np.ones(2), eta, W, dm)
+    tq, tk, tv, te = (torch.tensor(a, requires_grad=True) for a in (q, k, v, eta))
+    kv = torch.einsum("bhti,bhtj->bhtij", tk, tv)
+    S = torch.cumsum(kv, dim=2)  # S[:, :, i] = sum_{j <= i} k_j v_j^T
+    T = q.shape[2]
+    Spad = torch.cat([torch.zeros_like(S[:, :, :W]), S[:, :, : T - W]], dim=2)  # state read at t
+    m = te[None, :, None, None] * torch.einsum("bhti,bhtij->bhtj", tq, Spad)
+    (m * torch.tensor(dm)).sum().backward()
+    np.testing.assert_allclose(gq, tq.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gk, tk.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gv, tv.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(geta, te.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_scan_backward_scaling_identities():
+    # scaling q (or k) by c scales m by c: sum <q, dq> = sum <k, dk> = <dm, m>;
+    # m is linear in eta: eta * deta = <dm, m>
+    q, k, v, lam, eta, _ = rand_inputs(54, B=2, H=2, T=40, dk=4, dv=4)
+    W = 5
+    dm = np.random.default_rng(55).standard_normal(q.shape)
+    m, _ = O.tc_scan(q, k, v, lam, eta, W)
+    gq, gk, gv, _, geta = O.tc_scan_backward(q, k, v, lam, eta, W, dm)
+    per_head = np.einsum("bhtd,bhtd->h", dm, m)
+    np.testing.assert_allclose(np.einsum("bhtd,bhtd->h", q, gq), per_head, rtol=1e-12)
+    np.testing.assert_allclose(np.einsum("bhtd,bhtd->h", k, gk), per_head, rtol=1e-12)
+    np.testing.assert_allclose(np.einsum("bhtd,bhtd->h", v, gv), per_head, rtol=1e-12)
+    np.testing.assert_allclose(eta * geta, per_head, rtol=1e-12)
+
+
+def _backward_mutant(kind):
+    def run(q, k, v, lam, eta, W, dm):
+        gq, gk, gv, glam, geta = O.tc_scan_backward(q, k, v, lam, eta, W, dm)
+        if kind == "dk_one_token_late":
+            gk = np.roll(gk, 1, axis=2)
+        elif kind == "dlam_missing_a_term":
+            glam = glam * 0.9
+        elif kind == "dv_not_scaled_by_eta":
+            gv = gv / eta[None, :, None, None]
+        return gq, gk, gv, glam, geta
+    return run
+
+
+@pytest.mark.parametrize("kind", ["dk_one_token_late", "dlam_missing_a_term", "dv_not_scaled_by_eta"])
+def test_scan_backward_pins_catch_planted_mistakes(kind):
+    q, k, v, lam, eta, _ = rand_inputs(56, B=1, H=2, T=10, dk=2, dv=2)
+    W = 2
+    dm = np.random.default_rng(57).standard_normal(q.shape)
+    gq, gk, gv, glam, geta = _backward_mutant(kind)(q, k, v, lam, eta, W, dm)
+    h = 1e-6
+    worst = 0.0
+    for name, x, g in (("k", k, gk), ("v", v, gv)):
+        for i in [(0, 0, 0, 0), (0, 1, 3, 1), (0, 0, 5, 0)]:
+            xp, xm = x.copy(), x.copy()
+            xp[i] += h
+            xm[i] -= h
+            a = {"k": k, "v": v}
+            a[name] = xp
+            lp = _scan_loss(q, a["k"], a["v"], lam, eta, W, dm)
+            a[name] = xm
+            lmn = _scan_loss(q, a["k"], a["v"], lam, eta, W, dm)
+            worst = max(worst, abs(g[i] - (lp - lmn) / (2 * h)))
+    lp = _scan_loss(q, k, v, lam + np.array([h, 0]), eta, W, dm)
+    lmn = _scan_loss(q, k, v, lam - np.array([h, 0]), eta, W, dm)
+    worst = max(worst, abs(glam[0] - (lp - lmn) / (2 * h)))
+    assert worst > 1e-4
