@@ -78,6 +78,26 @@ tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype 
                           float* m, float* A_final, void* ws, size_t ws_bytes, hipStream_t s);
 
 /* ---------------------------------------------------------------------------
+ * Backward of the L2 read (Tensor Cache, Methodology 1 and 2: lam and eta
+ * are learned per head): gradients of L = sum_t <dm_t, m_t>, m as returned
+ * by tc_scan_forward for the same arguments.  A_final takes no gradient.
+ *   dm       [B, H, T, dv] float32 (rows t < W are ignored: m is 0 there).
+ *   dq, dk   out [B, H, T, dk] float32; dv out [B, H, T, dv] float32
+ *            (dq rows t < W and dk, dv rows t >= T - W are 0).
+ *   dlam, deta out [H] float32, summed over the batch.
+ *   ws       at least tc_scan_backward_workspace_bytes(...) bytes.
+ * Supported: dt = TC_F32, dk == dv in {16, 32, 64}, chunk = 64; anything
+ * else is TC_ERR_UNSUPPORTED.  dlam at lam = 0 is the one-sided derivative.
+ * ------------------------------------------------------------------------- */
+size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk,
+                                        tc_dtype dt);
+tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt,
+                           const float* lam, const float* eta,
+                           int B, int H, int T, int dk, int dv, int W, int chunk,
+                           const float* dm, float* dq, float* dk_out, float* dv_out,
+                           float* dlam, float* deta, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
  * One streaming step of the two-level cache (Tensor Cache, Methodology 1).
  *
  * For every sequence b and head h, with p = pos[b] (tokens already seen):
@@ -168,6 +188,7 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
  * and `after` just after it:
  *   tc_fused_layer      the window-attention + L2-read kernel,
  *   tc_scan_forward     the output kernel,
+ *   tc_scan_backward    the output kernel of the dq scan,
  *   tc_decode_step      its only kernel,
  *   tc_decode_layer_step its only kernel,
  *   delta_scan_forward  the kernel that walks the chunks.

@@ -124,6 +124,48 @@ tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype 
   });
 }
 
+static tc_status check_scan_bwd(const char* fn, int B, int H, int T, int dk, int dv, int W, int chunk,
+                                tc_dtype dt) {
+  tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
+  if (st != TC_OK) return st;
+  if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+  if (dt != TC_F32 || dk > 64)
+    return fail(TC_ERR_UNSUPPORTED, "%s: the backward takes float32 inputs with d in {16, 32, 64}", fn);
+  return TC_OK;
+}
+
+size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk,
+                                        tc_dtype dt) {
+  if (check_scan_bwd("tc_scan_backward_workspace_bytes", B, H, T, dk, dv, W, chunk, dt) != TC_OK)
+    return SIZE_MAX;
+  ok();
+  return tc::scan_bwd_ws_bytes(B, H, T, dk, W);
+}
+
+tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt, const float* lam,
+                           const float* eta, int B, int H, int T, int dk, int dv, int W, int chunk,
+                           const float* dm, float* dq, float* dk_out, float* dv_out, float* dlam,
+                           float* deta, void* ws, size_t ws_bytes, hipStream_t s) {
+  return guarded("tc_scan_backward", [&]() -> tc_status {
+    const char* fn = "tc_scan_backward";
+    tc_status st = check_scan_bwd(fn, B, H, T, dk, dv, W, chunk, dt);
+    if (st != TC_OK) return st;
+    if (B == 0 || H == 0) return ok();
+    if (!lam || !eta || !dlam || !deta)
+      return fail(TC_ERR_INVALID_ARG, "%s: lam, eta, dlam, deta must not be NULL", fn);
+    if (T > 0 && (!q || !k || !v || !dm || !dq || !dk_out || !dv_out))
+      return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, dm, dq, dk, dv must not be NULL", fn);
+    const size_t need = tc::scan_bwd_ws_bytes(B, H, T, dk, W);
+    if (ws_bytes < need)
+      return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    if (!ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
+    return from_hip(tc::launch_tc_scan_backward(static_cast<const float*>(q), static_cast<const float*>(k),
+                                                static_cast<const float*>(v), lam, eta, B, H, T, dk, W, dm,
+                                                dq, dk_out, dv_out, dlam, deta, ws, s),
+                    fn);
+  });
+}
+
 tc_status tc_decode_step(const void* q, const void* k, const void* v, tc_dtype dt, void* ring_k,
                          void* ring_v, float* A, const float* lam, const float* eta,
                          const int64_t* pos, int B, int H, int dk, int dv, int W, float* m,

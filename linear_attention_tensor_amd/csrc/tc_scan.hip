@@ -290,14 +290,25 @@ __device__ __forceinline__ float4 ld4(const uint16_t* p) {
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
 }
 
-// One chunk's rows [0, 64) of a row-major [., D] input in registers, as
-// float4 pieces i * 256 + thread; rows >= nvalid are zero.
+// Rows of one (b, h) of a [., D] array seen through a view: row s sits at
+// base + bh * bh_stride + s * rs.  A negative rs walks the array backwards
+// (the time-reversed scans of the backward pass).
+template <typename TP>
+struct RowView {
+  TP* base;
+  long bh_stride;
+  long rs;
+  __device__ __forceinline__ TP* row(int bh, long s) const { return base + bh * bh_stride + s * rs; }
+};
+
+// One chunk's rows [0, 64) (row r at src + r rs) in registers, as float4
+// pieces i * 256 + thread; rows >= nvalid are zero.
 template <int D, typename TIn>
-__device__ __forceinline__ void load_rows(float4* x, const TIn* src, int nvalid) {
+__device__ __forceinline__ void load_rows(float4* x, const TIn* src, long rs, int nvalid) {
 #pragma unroll
   for (int i = 0; i < FastTiles<D>::NV4; ++i) {
     const int e4 = i * 256 + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
-    x[i] = row < nvalid ? ld4(src + (long)row * D + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    x[i] = row < nvalid ? ld4(src + (long)row * rs + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 // ... into LDS row-major (stride S) ...
@@ -393,10 +404,9 @@ __device__ __forceinline__ void store_state(float* dst, const floatx4* acc, int 
 
 // Per-(segment, b, h) state contribution from zero (all segments but the last).
 template <int D, typename TIn>
-__global__ __launch_bounds__(256) void scan_state_fast(const TIn* __restrict__ k,
-                                                       const TIn* __restrict__ v,
+__global__ __launch_bounds__(256) void scan_state_fast(RowView<const TIn> kv_k, RowView<const TIn> kv_v,
                                                        const float* __restrict__ lam,
-                                                       const float* __restrict__ eta, int H, int T,
+                                                       const float* __restrict__ eta, int H,
                                                        int n_act, int seg_chunks, int n_seg,
                                                        float* __restrict__ ws) {
   using F = FastTiles<D>;
@@ -407,15 +417,13 @@ __global__ __launch_bounds__(256) void scan_state_fast(const TIn* __restrict__ k
   const float lm = lam[bh % H], et = eta[bh % H];
   const int c_begin = seg * seg_chunks;
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
-  const TIn* kb = k + (long)bh * T * D;
-  const TIn* vb = v + (long)bh * T * D;
   floatx4 acc[F::TPW];
   load_state<D>(acc, nullptr, D);
   float4 xk[F::NV4], xv[F::NV4];
   if (c_begin < c_end) {
     const int L = min(CH, n_act - c_begin * CH);
-    load_rows<D>(xk, kb + (long)c_begin * CH * D, L);
-    load_rows<D>(xv, vb + (long)c_begin * CH * D, L);
+    load_rows<D>(xk, kv_k.row(bh, (long)c_begin * CH), kv_k.rs, L);
+    load_rows<D>(xv, kv_v.row(bh, (long)c_begin * CH), kv_v.rs, L);
   }
   for (int c = c_begin; c < c_end; ++c) {
     const int L = min(CH, n_act - c * CH);
@@ -427,8 +435,8 @@ __global__ __launch_bounds__(256) void scan_state_fast(const TIn* __restrict__ k
     lds_barrier();
     if (c + 1 < c_end) {
       const int Ln = min(CH, n_act - (c + 1) * CH);
-      load_rows<D>(xk, kb + (long)(c + 1) * CH * D, Ln);
-      load_rows<D>(xv, vb + (long)(c + 1) * CH * D, Ln);
+      load_rows<D>(xk, kv_k.row(bh, (long)(c + 1) * CH), kv_k.rs, Ln);
+      load_rows<D>(xv, kv_v.row(bh, (long)(c + 1) * CH), kv_v.rs, Ln);
     }
     fast_state_update<D>(acc, sVt, sKt, pow_int(lm, L));
   }
@@ -439,10 +447,9 @@ __global__ __launch_bounds__(256) void scan_state_fast(const TIn* __restrict__ k
 // chunks and write m (rows W + s).
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void scan_output_fast(
-    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ lam, const float* __restrict__ eta, int H, int T, int W, int n_act,
-    int seg_chunks, int n_seg, const float* __restrict__ ws, float* __restrict__ m,
-    float* __restrict__ A_final) {
+    RowView<const TIn> vq, RowView<const TIn> vk, RowView<const TIn> vv, const float* __restrict__ lam,
+    const float* __restrict__ eta, int H, int n_act, int seg_chunks, int n_seg,
+    const float* __restrict__ ws, RowView<float> vm, float* __restrict__ A_final) {
   using F = FastTiles<D>;
   constexpr int NDV = D / 16;
   __shared__ __attribute__((aligned(16))) float sQ[CH * F::S];
@@ -459,10 +466,6 @@ __global__ __launch_bounds__(256) void scan_output_fast(
   const int l = lane_id(), w = wave_id(), r = l & 15, g = l >> 4;
   const int c_begin = seg * seg_chunks;
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
-  const TIn* qb = q + (long)bh * T * D;
-  const TIn* kb = k + (long)bh * T * D;
-  const TIn* vb = v + (long)bh * T * D;
-  float* mb = m + (long)bh * T * D;
   if (threadIdx.x <= CH) sPow[threadIdx.x] = pow_int(lm, threadIdx.x);
 
   floatx4 acc[F::TPW];
@@ -471,9 +474,9 @@ __global__ __launch_bounds__(256) void scan_output_fast(
   float4 xq[F::NV4], xk[F::NV4], xv[F::NV4];
   if (c_begin < c_end) {
     const int s0 = c_begin * CH, L = min(CH, n_act - s0);
-    load_rows<D>(xq, qb + (long)(s0 + W) * D, L);
-    load_rows<D>(xk, kb + (long)s0 * D, L);
-    load_rows<D>(xv, vb + (long)s0 * D, L);
+    load_rows<D>(xq, vq.row(bh, s0), vq.rs, L);
+    load_rows<D>(xk, vk.row(bh, s0), vk.rs, L);
+    load_rows<D>(xv, vv.row(bh, s0), vv.rs, L);
   }
   for (int c = c_begin; c < c_end; ++c) {
     const int s0 = c * CH, L = min(CH, n_act - s0);
@@ -488,9 +491,9 @@ __global__ __launch_bounds__(256) void scan_output_fast(
     lds_barrier();
     if (c + 1 < c_end) {
       const int s1 = s0 + CH, Ln = min(CH, n_act - s1);
-      load_rows<D>(xq, qb + (long)(s1 + W) * D, Ln);
-      load_rows<D>(xk, kb + (long)s1 * D, Ln);
-      load_rows<D>(xv, vb + (long)s1 * D, Ln);
+      load_rows<D>(xq, vq.row(bh, s1), vq.rs, Ln);
+      load_rows<D>(xk, vk.row(bh, s1), vk.rs, Ln);
+      load_rows<D>(xv, vv.row(bh, s1), vv.rs, Ln);
     }
     // P = (Q' K^T) masked to c <= r and weighted by eta lam^(r-c): this
     // wave's rows 16w.., kept in LDS for its own P V below.
@@ -521,7 +524,7 @@ __global__ __launch_bounds__(256) void scan_output_fast(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = 16 * w + 4 * g + e;
-          if (rr < L) mb[(long)(W + s0 + rr) * D + 16 * t + r] = o[t][e];
+          if (rr < L) vm.row(bh, s0 + rr)[16 * t + r] = o[t][e];
         }
     }
     fast_state_update<D>(acc, sVt, sKt, sPow[L]);
@@ -537,6 +540,366 @@ __global__ void zero_rows_kernel(float* __restrict__ m, long rows_per_bh, long T
   const long n = rows_per_bh * dv;
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x)
     m[bh * T * dv + i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the read (fp32 inputs, d <= 64).  With s = t - W, q'_s = q_{s+W}
+// and G_s = dm_{s+W}, L = sum_s <G_s, m'_s> and
+//   dq'_s = eta sum_{j<=s} lam^(s-j) <G_s, v_j> k_j     : the forward read with
+//           (q, k, v) -> (G, v, k);
+//   dk_j  = eta sum_{s>=j} lam^(s-j) <G_s, v_j> q'_s    : the forward read of the
+//           time-reversed sequence with (q, k, v) -> (v, G, q') and no shift;
+//   dv_j  = eta sum_{s>=j} lam^(s-j) <q'_s, k_j> G_s    : ... with (k, q', G).
+// The three scans run with eta = 1 (the read is linear in eta), and
+// deta = sum_s <q'_s, dq1'_s>.
+//
+// dlam comes from its own pass.  With A_s = sum_{j<=s} lam^(s-j) k_j v_j^T
+// (eta = 1), dL/dlam = eta sum_s q'_s^T A'_s G_s, where the derivative state
+// A'_s = sum_{j<=s} (s-j) lam^(s-j-1) k_j v_j^T is carried next to the state.
+// For a chunk with entering states S, S' (S' = dS/dlam) its share is
+//   <S, sum_r (r+1) lam^r q'_r G_r^T> + <S', sum_r lam^(r+1) q'_r G_r^T>
+//   + sum_{c<r} (r-c) lam^(r-c-1) <q'_r, k_c> <v_c, G_r>,
+// and S' <- lam^L S' + L lam^(L-1) S + sum_c (L-1-c) lam^(L-2-c) k_c v_c^T.
+// Every weight is non-negative, so no large terms cancel (the shortcut
+// through sum_s s <q'_s, dq'_s> - sum_j j <k_j, dk_j> loses about log10(T)
+// digits to cancellation).  At lam = 0 the weights n lam^(n-1) reduce to the
+// one-sided derivative (only n = 1 survives).
+constexpr int kBwdBlocks = 8;  // finalize workgroups per (b, h)
+
+// n lam^(n-1), the derivative of lam^n (0 for n = 0)
+__device__ __forceinline__ float dpow_int(float lam, int n) {
+  return n > 0 ? static_cast<float>(n) * pow_int(lam, n - 1) : 0.f;
+}
+
+// workspace of the backward: ones (eta = 1 for the scans) | fp64 partial
+// sums of deta [BH][kBwdBlocks] and dlam [BH][n_seg] | the scans' state
+// workspace (also S of the dlam pass) | S' of the dlam pass
+size_t scan_bwd_head_bytes(int H) { return ((size_t)H * sizeof(float) + 255) / 256 * 256; }
+size_t scan_bwd_part_bytes(int B, int H, int n_seg) {
+  return ((size_t)B * H * (kBwdBlocks + n_seg) * sizeof(double) + 255) / 256 * 256;
+}
+
+__global__ void fill_kernel(float* __restrict__ p, int n, float x) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = x;
+}
+
+// Per (block, b, h): fp64 partial sums of <q'_s, dq1'_s> over rows of the
+// active range, and dq, dk, dv scaled by eta in place.
+template <int D>
+__global__ __launch_bounds__(256) void scan_bwd_finalize(const float* __restrict__ q,
+                                                         const float* __restrict__ eta, int H, int T,
+                                                         int W, int n_act, float* __restrict__ dq,
+                                                         float* __restrict__ dk, float* __restrict__ dv,
+                                                         double* __restrict__ part) {
+  __shared__ double red[256];
+  const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const float et = eta[bh % H];
+  const int per = (n_act + kBwdBlocks - 1) / kBwdBlocks;
+  const int r0 = min(n_act, blk * per), r1 = min(n_act, r0 + per);
+  const long base = (long)bh * T * D;
+  double s = 0.0;
+  for (long i = (long)r0 * D + t; i < (long)r1 * D; i += 256) {
+    const float dqv = dq[base + (long)W * D + i];
+    s += (double)q[base + (long)W * D + i] * dqv;
+    dq[base + (long)W * D + i] = et * dqv;
+    dk[base + i] *= et;
+    dv[base + i] *= et;
+  }
+  red[t] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) red[t] += red[t + off];
+    __syncthreads();
+  }
+  if (t == 0) part[(long)bh * kBwdBlocks + blk] = red[0];
+}
+
+// Per (segment, b, h) but the last: the segment's own state U and its lam
+// derivative U' from zero (eta = 1).
+template <int D>
+__global__ __launch_bounds__(256) void scan_dstate_fast(RowView<const float> vk, RowView<const float> vv,
+                                                        const float* __restrict__ lam, int H, int n_act,
+                                                        int seg_chunks, int n_seg, float* __restrict__ ws,
+                                                        float* __restrict__ dws) {
+  using F = FastTiles<D>;
+  __shared__ __attribute__((aligned(16))) float sKt[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sKd[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sVt[D * F::ST];
+  __shared__ float sW[CH], sWd[CH];
+  const int seg = blockIdx.x, bh = blockIdx.z;
+  const float lm = lam[bh % H];
+  const int c_begin = seg * seg_chunks;
+  const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
+  floatx4 acc[F::TPW], dacc[F::TPW];
+  load_state<D>(acc, nullptr, D);
+  load_state<D>(dacc, nullptr, D);
+  float4 xk[F::NV4], xv[F::NV4];
+  if (c_begin < c_end) {
+    const int L = min(CH, n_act - c_begin * CH);
+    load_rows<D>(xk, vk.row(bh, (long)c_begin * CH), vk.rs, L);
+    load_rows<D>(xv, vv.row(bh, (long)c_begin * CH), vv.rs, L);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const int L = min(CH, n_act - c * CH);
+    lds_barrier();
+    if (threadIdx.x < CH) {
+      const int n = L - 1 - (int)threadIdx.x;
+      sW[threadIdx.x] = n >= 0 ? pow_int(lm, n) : 0.f;
+      sWd[threadIdx.x] = n >= 0 ? dpow_int(lm, n) : 0.f;
+    }
+    lds_barrier();
+    put_cols<D>(sKt, xk, sW);
+    put_cols<D>(sKd, xk, sWd);
+    put_cols<D>(sVt, xv, nullptr);
+    lds_barrier();
+    if (c + 1 < c_end) {
+      const int Ln = min(CH, n_act - (c + 1) * CH);
+      load_rows<D>(xk, vk.row(bh, (long)(c + 1) * CH), vk.rs, Ln);
+      load_rows<D>(xv, vv.row(bh, (long)(c + 1) * CH), vv.rs, Ln);
+    }
+    const float lL = pow_int(lm, L), dL = dpow_int(lm, L);
+#pragma unroll
+    for (int i = 0; i < F::TPW; ++i) dacc[i] = lL * dacc[i] + dL * acc[i];
+    fast_state_update<D>(dacc, sVt, sKd, 1.f);
+    fast_state_update<D>(acc, sVt, sKt, lL);
+  }
+  store_state<D>(ws + ((long)bh * n_seg + seg) * D * D, acc, D);
+  store_state<D>(dws + ((long)bh * n_seg + seg) * D * D, dacc, D);
+}
+
+// Entering (S, S') of every segment from the segments' own (U, U').
+__global__ void scan_dprefix_kernel(const float* __restrict__ lam, int H, int n_per_bh, int seg_len,
+                                    int n_seg, float* __restrict__ ws, float* __restrict__ dws) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int bh = blockIdx.y;
+  if (idx >= n_per_bh) return;
+  const float lm = lam[bh % H];
+  const float lf = pow_int(lm, seg_len), dlf = dpow_int(lm, seg_len);
+  float* p = ws + (long)bh * n_seg * n_per_bh + idx;
+  float* dp = dws + (long)bh * n_seg * n_per_bh + idx;
+  float run = 0.f, drun = 0.f;
+  for (int s = 0; s < n_seg - 1; ++s) {  // every segment but the last is full length
+    const float u = p[(long)s * n_per_bh], du = dp[(long)s * n_per_bh];
+    p[(long)s * n_per_bh] = run;
+    dp[(long)s * n_per_bh] = drun;
+    drun = lf * drun + dlf * run + du;
+    run = lf * run + u;
+  }
+  p[(long)(n_seg - 1) * n_per_bh] = run;
+  dp[(long)(n_seg - 1) * n_per_bh] = drun;
+}
+
+// Per (segment, b, h): this segment's share of dL/dlam (eta = 1) in fp64.
+// Phase 1 stages q', k, G, v row-major for the two 64 x 64 Gram matrices of
+// the in-chunk term; phase 2 reuses the same LDS for the transposed,
+// weighted copies that feed the state products.
+template <int D>
+__global__ __launch_bounds__(256) void scan_dlam_fast(RowView<const float> vq, RowView<const float> vk,
+                                                      RowView<const float> vv, RowView<const float> vg,
+                                                      const float* __restrict__ lam, int H, int n_act,
+                                                      int seg_chunks, int n_seg,
+                                                      const float* __restrict__ ws,
+                                                      const float* __restrict__ dws,
+                                                      double* __restrict__ part) {
+  using F = FastTiles<D>;
+  constexpr int ROWS = CH * F::S;  // one [64][D] array
+  constexpr int COLS = D * F::ST;  // one [D][64] array
+  constexpr int NLDS = 4 * ROWS > 6 * COLS ? 4 * ROWS : 6 * COLS;
+  __shared__ __attribute__((aligned(16))) float lds[NLDS];
+  __shared__ float sPow[CH + 1];
+  __shared__ float sW[CH], sWd[CH], sW1[CH], sW2[CH];
+  __shared__ double red[256];
+  float* const sQ = lds;
+  float* const sK = lds + ROWS;
+  float* const sG = lds + 2 * ROWS;
+  float* const sV = lds + 3 * ROWS;
+  float* const sKt = lds;
+  float* const sKd = lds + COLS;
+  float* const sVt = lds + 2 * COLS;
+  float* const sQ1 = lds + 3 * COLS;
+  float* const sQ2 = lds + 4 * COLS;
+  float* const sGt = lds + 5 * COLS;
+
+  const int seg = blockIdx.x, bh = blockIdx.z;
+  const float lm = lam[bh % H];
+  const int l = lane_id(), w = wave_id(), r = l & 15, g = l >> 4;
+  const int c_begin = seg * seg_chunks;
+  const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
+  if (threadIdx.x <= CH) sPow[threadIdx.x] = pow_int(lm, threadIdx.x);
+
+  floatx4 acc[F::TPW], dacc[F::TPW];
+  const bool entering = n_seg > 1 && seg > 0;
+  load_state<D>(acc, entering ? ws + ((long)bh * n_seg + seg) * D * D : nullptr, D);
+  load_state<D>(dacc, entering ? dws + ((long)bh * n_seg + seg) * D * D : nullptr, D);
+  float4 xq[F::NV4], xk[F::NV4], xv[F::NV4], xg[F::NV4];
+  if (c_begin < c_end) {
+    const int s0 = c_begin * CH, L = min(CH, n_act - s0);
+    load_rows<D>(xq, vq.row(bh, s0), vq.rs, L);
+    load_rows<D>(xk, vk.row(bh, s0), vk.rs, L);
+    load_rows<D>(xv, vv.row(bh, s0), vv.rs, L);
+    load_rows<D>(xg, vg.row(bh, s0), vg.rs, L);
+  }
+  double tot = 0.0;
+  for (int c = c_begin; c < c_end; ++c) {
+    const int s0 = c * CH, L = min(CH, n_act - s0);
+    lds_barrier();  // every wave is done with the previous chunk's phase 2
+    if (threadIdx.x < CH) {
+      const int t = threadIdx.x, n = L - 1 - t;
+      sW[t] = n >= 0 ? sPow[n] : 0.f;
+      sWd[t] = n >= 0 ? dpow_int(lm, n) : 0.f;
+      sW1[t] = static_cast<float>(t + 1) * sPow[t];
+      sW2[t] = sPow[t + 1];
+    }
+    put_rows<D>(sQ, xq);
+    put_rows<D>(sK, xk);
+    put_rows<D>(sG, xg);
+    put_rows<D>(sV, xv);
+    lds_barrier();
+    // in-chunk term from <q'_r, k_c> and <G_r, v_c>, this wave's rows 16w..
+    float intra = 0.f;
+    {
+      floatx4 pa[4] = {zero4(), zero4(), zero4(), zero4()};
+      floatx4 pb[4] = {zero4(), zero4(), zero4(), zero4()};
+      mma_rows<D, 4>(sQ + 16 * w * F::S, F::S, sK, 16 * F::S, F::S, pa);
+      mma_rows<D, 4>(sG + 16 * w * F::S, F::S, sV, 16 * F::S, F::S, pb);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = (16 * w + 4 * g + e) - (16 * ct + r);
+          if (n > 0) intra += static_cast<float>(n) * sPow[n - 1] * pa[ct][e] * pb[ct][e];
+        }
+    }
+    lds_barrier();  // phase-1 arrays are read
+    put_cols<D>(sKt, xk, sW);
+    put_cols<D>(sKd, xk, sWd);
+    put_cols<D>(sVt, xv, nullptr);
+    put_cols<D>(sQ1, xq, sW1);
+    put_cols<D>(sQ2, xq, sW2);
+    put_cols<D>(sGt, xg, nullptr);
+    lds_barrier();
+    if (c + 1 < c_end) {
+      const int s1 = s0 + CH, Ln = min(CH, n_act - s1);
+      load_rows<D>(xq, vq.row(bh, s1), vq.rs, Ln);
+      load_rows<D>(xk, vk.row(bh, s1), vk.rs, Ln);
+      load_rows<D>(xv, vv.row(bh, s1), vv.rs, Ln);
+      load_rows<D>(xg, vg.row(bh, s1), vg.rs, Ln);
+    }
+    // entering-state term: <S, E1> + <S', E2> with E^T = G^T diag(w) Q' in
+    // the tile layout of the state
+    float inter = 0.f;
+    {
+      floatx4 e1[F::TPW], e2[F::TPW];
+#pragma unroll
+      for (int i = 0; i < F::TPW; ++i) e1[i] = e2[i] = zero4();
+      fast_state_update<D>(e1, sGt, sQ1, 1.f);
+      fast_state_update<D>(e2, sGt, sQ2, 1.f);
+#pragma unroll
+      for (int i = 0; i < F::TPW; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) inter += acc[i][e] * e1[i][e] + dacc[i][e] * e2[i][e];
+    }
+    tot += (double)intra + (double)inter;
+    const float lL = sPow[L], dL = dpow_int(lm, L);
+#pragma unroll
+    for (int i = 0; i < F::TPW; ++i) dacc[i] = lL * dacc[i] + dL * acc[i];
+    fast_state_update<D>(dacc, sVt, sKd, 1.f);
+    fast_state_update<D>(acc, sVt, sKt, lL);
+  }
+  red[threadIdx.x] = tot;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[(long)bh * n_seg + seg] = red[0];
+}
+
+// Per head: deta and dlam from the partial sums of every sequence.
+__global__ void scan_bwd_reduce(const double* __restrict__ part_eta, const double* __restrict__ part_lam,
+                                const float* __restrict__ eta, int B, int H, int n_seg,
+                                float* __restrict__ dlam, float* __restrict__ deta) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  double a = 0.0, b = 0.0;
+  for (int bb = 0; bb < B; ++bb) {
+    const long bh = (long)bb * H + h;
+    for (int i = 0; i < kBwdBlocks; ++i) a += part_eta[bh * kBwdBlocks + i];
+    for (int i = 0; i < n_seg; ++i) b += part_lam[bh * n_seg + i];
+  }
+  deta[h] = (float)a;
+  dlam[h] = (float)((double)eta[h] * b);
+}
+
+template <int D>
+hipError_t run_scan_backward(const float* q, const float* k, const float* v, const float* lam,
+                             const float* eta, int B, int H, int T, int W, const float* dm,
+                             float* dq, float* dk, float* dv, float* dlam, float* deta, char* ws,
+                             hipStream_t s) {
+  const int BH = B * H;
+  const ScanPlan p = plan_scan(B, H, T, D, D, W);
+  const int n_act = p.n_act;
+  const size_t off_part = scan_bwd_head_bytes(H);
+  const size_t off_sws = off_part + scan_bwd_part_bytes(B, H, p.n_seg);
+  float* ones = reinterpret_cast<float*>(ws);
+  double* part_eta = reinterpret_cast<double*>(ws + off_part);
+  double* part_lam = part_eta + (long)BH * kBwdBlocks;
+  float* sws = reinterpret_cast<float*>(ws + off_sws);
+  float* dws = reinterpret_cast<float*>(ws + off_sws + scan_ws_bytes(p, B, H, D, D));
+  hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, ones, H, 1.f);
+  const long zq = std::min<long>(W, T);
+  if (zq > 0)
+    hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)std::min<long>((zq * D + 255) / 256, 1024), BH),
+                       dim3(256), 0, s, dq, zq, (long)T, D);
+  if (T - n_act > 0) {
+    const long zr = T - n_act;
+    const dim3 g((unsigned)std::min<long>((zr * D + 255) / 256, 1024), BH);
+    hipLaunchKernelGGL(zero_rows_kernel, g, dim3(256), 0, s, dk + (long)n_act * D, zr, (long)T, D);
+    hipLaunchKernelGGL(zero_rows_kernel, g, dim3(256), 0, s, dv + (long)n_act * D, zr, (long)T, D);
+  }
+  if (n_act <= 0) {
+    hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dlam, H, 0.f);
+    hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, deta, H, 0.f);
+    return hipGetLastError();
+  }
+  const long bs = (long)T * D;
+  const int nel = D * D;
+  auto scan = [&](RowView<const float> vq, RowView<const float> vk, RowView<const float> vv,
+                  RowView<float> vm, bool timed) {
+    if (p.n_seg > 1) {
+      hipLaunchKernelGGL((scan_state_fast<D, float>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, vk, vv,
+                         lam, ones, H, n_act, p.seg_chunks, p.n_seg, sws);
+      hipLaunchKernelGGL(scan_prefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H, nel,
+                         n_act, p.seg_chunks * CH, p.n_seg, sws);
+    }
+    if (timed) profile_mark_before(s);
+    hipLaunchKernelGGL((scan_output_fast<D, float>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, vq, vk, vv,
+                       lam, ones, H, n_act, p.seg_chunks, p.n_seg, sws, vm, nullptr);
+    if (timed) profile_mark_after(s);
+  };
+  const long last = (long)(n_act - 1) * D, tl = (long)(T - 1) * D;
+  // dq' = read of (G, v, k)
+  scan({dm + (long)W * D, bs, D}, {v, bs, D}, {k, bs, D}, {dq + (long)W * D, bs, D}, true);
+  // dk, dv: reads of the time-reversed sequence (row s' of a view is s = n_act - 1 - s')
+  scan({v + last, bs, -D}, {dm + tl, bs, -D}, {q + tl, bs, -D}, {dk + last, bs, -D}, false);
+  scan({k + last, bs, -D}, {q + tl, bs, -D}, {dm + tl, bs, -D}, {dv + last, bs, -D}, false);
+  // dlam: its own pass over (q', k, v, G) with the derivative state
+  const RowView<const float> fq{q + (long)W * D, bs, D}, fk{k, bs, D}, fv{v, bs, D},
+      fg{dm + (long)W * D, bs, D};
+  if (p.n_seg > 1) {
+    hipLaunchKernelGGL((scan_dstate_fast<D>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, fk, fv, lam, H,
+                       n_act, p.seg_chunks, p.n_seg, sws, dws);
+    hipLaunchKernelGGL(scan_dprefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H, nel,
+                       p.seg_chunks * CH, p.n_seg, sws, dws);
+  }
+  hipLaunchKernelGGL((scan_dlam_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, fq, fk, fv, fg, lam, H,
+                     n_act, p.seg_chunks, p.n_seg, sws, dws, part_lam);
+  hipLaunchKernelGGL((scan_bwd_finalize<D>), dim3(kBwdBlocks, BH), dim3(256), 0, s, q, eta, H, T, W, n_act,
+                     dq, dk, dv, part_eta);
+  hipLaunchKernelGGL(scan_bwd_reduce, dim3((H + 63) / 64), dim3(64), 0, s, part_eta, part_lam, eta, B, H,
+                     p.n_seg, dlam, deta);
+  return hipGetLastError();
 }
 
 template <int DK, int DVT, typename TIn>
@@ -558,16 +921,19 @@ hipError_t run_scan(const TIn* q, const TIn* k, const TIn* v, const float* lam, 
   }
   const int nvt = dv / DVT;
   if constexpr (DK <= 64 && DVT == DK) {
+    const long bs = (long)T * DK;
+    const RowView<const TIn> vq{q + (long)W * DK, bs, DK}, vk{k, bs, DK}, vv{v, bs, DK};
+    const RowView<float> vm{m + (long)W * DK, bs, DK};
     if (p.n_seg > 1) {
-      hipLaunchKernelGGL((scan_state_fast<DK, TIn>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, k, v,
-                         lam, eta, H, T, p.n_act, p.seg_chunks, p.n_seg, ws);
+      hipLaunchKernelGGL((scan_state_fast<DK, TIn>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, vk, vv,
+                         lam, eta, H, p.n_act, p.seg_chunks, p.n_seg, ws);
       const int nel = DK * dv;
       hipLaunchKernelGGL(scan_prefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H,
                          nel, p.n_act, p.seg_chunks * CH, p.n_seg, ws);
     }
     profile_mark_before(s);
-    hipLaunchKernelGGL((scan_output_fast<DK, TIn>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, q, k, v,
-                       lam, eta, H, T, W, p.n_act, p.seg_chunks, p.n_seg, ws, m, A_final);
+    hipLaunchKernelGGL((scan_output_fast<DK, TIn>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, vq, vk, vv,
+                       lam, eta, H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, A_final);
     profile_mark_after(s);
     return hipGetLastError();
   }
@@ -640,6 +1006,28 @@ hipError_t launch_tc_scan(const void* q, const void* k, const void* v, bool bf16
   if (bf16)
     return dispatch_scan<uint16_t>(q, k, v, lam, eta, B, H, T, dk, W, m, A_final, w, p, s);
   return dispatch_scan<float>(q, k, v, lam, eta, B, H, T, dk, W, m, A_final, w, p, s);
+}
+
+}  // namespace tc
+
+namespace tc {
+
+size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W) {
+  const ScanPlan p = plan_scan(B, H, T, d, d, W);
+  return scan_bwd_head_bytes(H) + scan_bwd_part_bytes(B, H, p.n_seg) + 2 * scan_ws_bytes(p, B, H, d, d);
+}
+
+hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
+                                   const float* eta, int B, int H, int T, int d, int W,
+                                   const float* dm, float* dq, float* dk, float* dv, float* dlam,
+                                   float* deta, void* ws, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  switch (d) {
+    case 16: return run_scan_backward<16>(q, k, v, lam, eta, B, H, T, W, dm, dq, dk, dv, dlam, deta, w, s);
+    case 32: return run_scan_backward<32>(q, k, v, lam, eta, B, H, T, W, dm, dq, dk, dv, dlam, deta, w, s);
+    case 64: return run_scan_backward<64>(q, k, v, lam, eta, B, H, T, W, dm, dq, dk, dv, dlam, deta, w, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace tc

@@ -26,6 +26,7 @@ import numpy as np
 __all__ = [
     "Workload",
     "WORKLOADS",
+    "draw_cotangent",
     "bf16_round_bits",
     "bf16_bits_to_f64",
     "round_to_dtype",
@@ -141,6 +142,13 @@ def draw(B: int, H: int, T: int, d: int, *, seed: int, dtype: str = "f32",
         out[name] = s
         out[name + "64"] = f
     return out
+
+
+def draw_cotangent(B: int, H: int, T: int, dv: int, *, seed: int) -> np.ndarray:
+    """Upstream gradient dm [B, H, T, dv] of the L2 read: float32 N(0, 1/dv),
+    drawn from PCG64([seed, 1 << 42]) so it is independent of ``draw``."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1 << 42]))
+    return (rng.standard_normal((B, H, T, dv)) / np.sqrt(dv)).astype(np.float32)
 
 
 def draw_workload(name: str, *, T: Optional[int] = None, B: Optional[int] = None,

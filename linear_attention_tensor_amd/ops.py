@@ -16,8 +16,8 @@ import torch
 from . import _lib
 from ._lib import TC_BF16, TC_F32, check, lib
 
-__all__ = ["tc_scan_forward", "tc_decode_step", "tc_decode_layer_step", "tc_fused_layer",
-           "delta_scan_forward",
+__all__ = ["tc_scan_forward", "tc_scan_backward", "tc_decode_step", "tc_decode_layer_step",
+           "tc_fused_layer", "delta_scan_forward", "scan_backward_workspace",
            "scan_workspace", "fused_workspace", "delta_workspace"]
 
 CHUNK = 64
@@ -118,6 +118,38 @@ def tc_scan_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torc
                                _stream())
     check("tc_scan_forward", st)
     return m, A
+
+
+def scan_backward_workspace(B, H, T, dk, dv, W, dtype_code) -> int:
+    n = lib().tc_scan_backward_workspace_bytes(B, H, T, dk, dv, W, CHUNK, dtype_code)
+    if n == _lib.SIZE_MAX:
+        raise _lib.TCError("tc_scan_backward_workspace_bytes", _lib.TC_ERR_UNSUPPORTED, _lib.last_error())
+    return n
+
+
+def tc_scan_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torch.Tensor,
+                     eta: torch.Tensor, W: int, dm: torch.Tensor, *, check_values: bool = True,
+                     ws: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv, dlam, deta) of sum <dm, m> through the L2 read m."""
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    _check_tensor("lam", lam, (H,), torch.float32, q.device)
+    _check_tensor("eta", eta, (H,), torch.float32, q.device)
+    _check_tensor("dm", dm, (B, H, T, dv), torch.float32, q.device)
+    if check_values:
+        _check_unit_interval("lam", lam)
+    gq = torch.empty((B, H, T, dk), dtype=torch.float32, device=q.device)
+    gk = torch.empty((B, H, T, dk), dtype=torch.float32, device=q.device)
+    gv = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    glam = torch.empty((H,), dtype=torch.float32, device=q.device)
+    geta = torch.empty((H,), dtype=torch.float32, device=q.device)
+    need = scan_backward_workspace(B, H, T, dk, dv, W, dt)
+    if ws is None:
+        ws = _ws(need, q.device)
+    st = lib().tc_scan_backward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(lam), _ptr(eta), B, H, T, dk, dv, W,
+                                CHUNK, _ptr(dm), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(glam), _ptr(geta),
+                                _ptr(ws), ws.numel() if ws is not None else 0, _stream())
+    check("tc_scan_backward", st)
+    return gq, gk, gv, glam, geta
 
 
 def tc_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_k: torch.Tensor,

@@ -166,3 +166,27 @@ def test_profile_hook_argument_check():
     assert L.tc_profile_next_call(None, fake) == _lib.TC_ERR_INVALID_ARG
     assert L.tc_profile_next_call(None, None) == _lib.TC_OK  # disarmed
     assert _lib.last_error() == ""
+
+
+def test_scan_backward_rejects():
+    f = lib().tc_scan_backward
+    need = lib().tc_scan_backward_workspace_bytes(4, 8, 4096, 64, 64, 512, 64, _lib.TC_F32)
+    assert 0 < need < _lib.SIZE_MAX
+
+    def call(**kw):
+        a = dict(dt=_lib.TC_F32, B=4, H=8, T=4096, d=64, W=512, chunk=64, dm=FAKE, dlam=FAKE, ws=FAKE,
+                 ws_bytes=need)
+        a.update(kw)
+        return f(FAKE, FAKE, FAKE, a["dt"], FAKE, FAKE, a["B"], a["H"], a["T"], a["d"], a["d"], a["W"],
+                 a["chunk"], a["dm"], FAKE, FAKE, FAKE, a["dlam"], FAKE, a["ws"], a["ws_bytes"], NULL)
+
+    assert call(dt=_lib.TC_BF16) == _lib.TC_ERR_UNSUPPORTED
+    assert call(d=128) == _lib.TC_ERR_UNSUPPORTED
+    assert call(W=0) == _lib.TC_ERR_INVALID_ARG
+    assert call(chunk=128) == _lib.TC_ERR_UNSUPPORTED
+    assert call(dm=NULL) == _lib.TC_ERR_INVALID_ARG
+    assert call(dlam=NULL) == _lib.TC_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == _lib.TC_ERR_WORKSPACE
+    assert call(ws=NULL) == _lib.TC_ERR_INVALID_ARG
+    assert call(B=0) == _lib.TC_OK
+    assert lib().tc_scan_backward_workspace_bytes(1, 1, 10, 128, 128, 4, 64, _lib.TC_F32) == _lib.SIZE_MAX
