@@ -39,7 +39,7 @@ def parse():
                     help="untimed calls first: the GPU needs some tens of ms of load to reach its steady clock")
     ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fused", "scan", "decode", "decode_layer", "delta"], default=None,
+    ap.add_argument("--only", choices=["fused", "scan", "scan_backward", "decode", "decode_layer", "delta"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy twice (the reference for "
@@ -78,6 +78,18 @@ def scan_flops(B, H, T, d, W, C=64):
 
 def scan_bytes(B, H, T, d, in_bytes):
     return B * H * T * (3 * d * in_bytes + d * 4)
+
+
+def scan_backward_flops(B, H, T, d, W, C=64):
+    # three reads of the forward's shape (dq, dk, dv) plus the dlam pass: per
+    # active row two in-chunk Gram rows (2 x 2Cd) and four d x d products
+    # (two entering-state terms, two state updates)
+    return 3 * scan_flops(B, H, T, d, W, C) + B * H * max(T - W, 0) * (4 * C * d + 8 * d * d)
+
+
+def scan_backward_bytes(B, H, T, d):
+    # read q, k, v, dm and write dq, dk, dv once, fp32
+    return B * H * T * d * 4 * 7
 
 
 def decode_bytes_per_head(d, in_bytes=2):
@@ -285,6 +297,43 @@ def bench_scan(steps, warmup, dev):
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
 
 
+def bench_scan_backward(steps, warmup, dev):
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["prefill_scan_f32"]
+    x = I.draw_workload(w.name)
+    q, k, v = (to_dev_f32(x[n], dev) for n in ("q", "k", "v"))
+    lam, eta = to_dev_f32(x["lam"], dev), to_dev_f32(x["eta"], dev)
+    dm = to_dev_f32(I.draw_cotangent(w.B, w.H, w.T, w.d, seed=w.seed), dev)
+    shape = (w.B, w.H, w.T, w.d)
+    gq, gk, gv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
+    glam, geta = (torch.empty((w.H,), dtype=torch.float32, device=dev) for _ in range(2))
+    nb = ops.scan_backward_workspace(w.B, w.H, w.T, w.d, w.d, w.W, 0)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    lib = ops.lib()
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, ops._ptr(lam), ops._ptr(eta), w.B, w.H, w.T, w.d,
+            w.d, w.W, 64, ops._ptr(dm), ops._ptr(gq), ops._ptr(gk), ops._ptr(gv), ops._ptr(glam),
+            ops._ptr(geta), ops._ptr(ws), ws.numel(), ops._stream())
+
+    def call(_):
+        if lib.tc_scan_backward(*args) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, kernel_ms = time_calls(call, steps, warmup, KernelTimer(steps))
+    flops = scan_backward_flops(w.B, w.H, w.T, w.d, w.W)
+    nbytes = scan_backward_bytes(w.B, w.H, w.T, w.d)
+    return {"workload": w.name + " backward", "ms_per_step": ms,
+            "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+            "roofline": roofline("mfma", flops / (ms_call * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
+            "hbm": roofline("hbm", nbytes / (ms_call * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"),
+            "main_kernel": {"name": "scan_output_fast<64> (the dq read)", "ms": kernel_ms},
+            "ms_per_call": ms_call,
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
+
+
 def bench_decode(steps, warmup, dev, n_steps=4096):
     import torch
 
@@ -473,11 +522,14 @@ def main():
         head, x = bench_fused(args.steps, args.warmup, dev)
     if only is None and not args.no_components:
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
+        components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
         components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
     elif only == "scan":
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
+    elif only == "scan_backward":
+        components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
     elif only == "decode":
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
     elif only == "decode_layer":
