@@ -329,7 +329,7 @@ def bench_scan_backward(steps, warmup, dev):
             "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
             "roofline": roofline("mfma", flops / (ms_call * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
             "hbm": roofline("hbm", nbytes / (ms_call * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"),
-            "main_kernel": {"name": "scan_output_fast<64> (the dq read)", "ms": kernel_ms},
+            "main_kernel": {"name": "scan_bwd_fwd_fast<64>", "ms": kernel_ms},
             "ms_per_call": ms_call,
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
 

@@ -85,7 +85,8 @@ tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype 
  *   dq, dk   out [B, H, T, dk] float32; dv out [B, H, T, dv] float32
  *            (dq rows t < W and dk, dv rows t >= T - W are 0).
  *   dlam, deta out [H] float32, summed over the batch.
- *   ws       at least tc_scan_backward_workspace_bytes(...) bytes.
+ *   ws       at least tc_scan_backward_workspace_bytes(...) bytes (may be NULL
+ *            when that is 0).
  * Supported: dt = TC_F32, dk == dv in {16, 32, 64}, chunk = 64; anything
  * else is TC_ERR_UNSUPPORTED.  dlam at lam = 0 is the one-sided derivative.
  * ------------------------------------------------------------------------- */
@@ -188,7 +189,7 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
  * and `after` just after it:
  *   tc_fused_layer      the window-attention + L2-read kernel,
  *   tc_scan_forward     the output kernel,
- *   tc_scan_backward    the output kernel of the dq scan,
+ *   tc_scan_backward    its forward-direction kernel (dq, deta, dlam),
  *   tc_decode_step      its only kernel,
  *   tc_decode_layer_step its only kernel,
  *   delta_scan_forward  the kernel that walks the chunks.

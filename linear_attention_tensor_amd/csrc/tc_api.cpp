@@ -158,7 +158,7 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
     const size_t need = tc::scan_bwd_ws_bytes(B, H, T, dk, W);
     if (ws_bytes < need)
       return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
-    if (!ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
+    if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
     return from_hip(tc::launch_tc_scan_backward(static_cast<const float*>(q), static_cast<const float*>(k),
                                                 static_cast<const float*>(v), lam, eta, B, H, T, dk, W, dm,
                                                 dq, dk_out, dv_out, dlam, deta, ws, s),

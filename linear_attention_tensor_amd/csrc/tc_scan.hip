@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256) void scan_state_fast(RowView<const TIn> kv_k, 
   __shared__ __attribute__((aligned(16))) float sVt[D * F::ST];
   __shared__ float sW[CH];
   const int seg = blockIdx.x, bh = blockIdx.z;
-  const float lm = lam[bh % H], et = eta[bh % H];
+  const float lm = lam[bh % H], et = eta != nullptr ? eta[bh % H] : 1.f;  // NULL: eta = 1
   const int c_begin = seg * seg_chunks;
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
   floatx4 acc[F::TPW];
@@ -544,39 +544,41 @@ __global__ void zero_rows_kernel(float* __restrict__ m, long rows_per_bh, long T
 
 // ---------------------------------------------------------------------------
 // Backward of the read (fp32 inputs, d <= 64).  With s = t - W, q'_s = q_{s+W}
-// and G_s = dm_{s+W}, L = sum_s <G_s, m'_s> and
-//   dq'_s = eta sum_{j<=s} lam^(s-j) <G_s, v_j> k_j     : the forward read with
-//           (q, k, v) -> (G, v, k);
-//   dk_j  = eta sum_{s>=j} lam^(s-j) <G_s, v_j> q'_s    : the forward read of the
-//           time-reversed sequence with (q, k, v) -> (v, G, q') and no shift;
-//   dv_j  = eta sum_{s>=j} lam^(s-j) <q'_s, k_j> G_s    : ... with (k, q', G).
-// The three scans run with eta = 1 (the read is linear in eta), and
-// deta = sum_s <q'_s, dq1'_s>.
-//
-// dlam comes from its own pass.  With A_s = sum_{j<=s} lam^(s-j) k_j v_j^T
-// (eta = 1), dL/dlam = eta sum_s q'_s^T A'_s G_s, where the derivative state
-// A'_s = sum_{j<=s} (s-j) lam^(s-j-1) k_j v_j^T is carried next to the state.
-// For a chunk with entering states S, S' (S' = dS/dlam) its share is
-//   <S, sum_r (r+1) lam^r q'_r G_r^T> + <S', sum_r lam^(r+1) q'_r G_r^T>
-//   + sum_{c<r} (r-c) lam^(r-c-1) <q'_r, k_c> <v_c, G_r>,
-// and S' <- lam^L S' + L lam^(L-1) S + sum_c (L-1-c) lam^(L-2-c) k_c v_c^T.
-// Every weight is non-negative, so no large terms cancel (the shortcut
-// through sum_s s <q'_s, dq'_s> - sum_j j <k_j, dk_j> loses about log10(T)
-// digits to cancellation).  At lam = 0 the weights n lam^(n-1) reduce to the
-// one-sided derivative (only n = 1 survives).
-constexpr int kBwdBlocks = 8;  // finalize workgroups per (b, h)
+// and G_s = dm_{s+W}, L = sum_s <G_s, m'_s> and, with the state
+// A_s = sum_{j<=s} lam^(s-j) k_j v_j^T and the adjoint state
+// R_j = sum_{s>=j} lam^(s-j) G_s q'_s^T (eta = 1):
+//   dq'_s = eta A_s G_s,   dk_j = eta R_j^T v_j,   dv_j = eta R_j k_j,
+//   deta  = sum_s q'_s^T A_s G_s                     (the read is linear in eta),
+//   dlam  = eta sum_s q'_s^T A'_s G_s,  A'_s = sum_{j<=s} (s-j) lam^(s-j-1) k_j v_j^T.
+// Two passes:
+//   forward (scan_bwd_fwd_fast): walks the chunks carrying A and A' (the lam
+//     derivative) and writes dq and the fp64 shares of deta and dlam.  For a
+//     chunk with entering S, S':
+//       dq'_r = lam^(r+1) S G_r + sum_{c<=r} lam^(r-c) <G_r, v_c> k_c,
+//       dlam share = <S, sum_r (r+1) lam^r q'_r G_r^T> + <S', sum_r lam^(r+1) q'_r G_r^T>
+//                  + sum_{c<r} (r-c) lam^(r-c-1) <q'_r, k_c> <G_r, v_c>,
+//       deta share = <S, sum_r lam^(r+1) q'_r G_r^T> + sum_{c<=r} lam^(r-c) <q'_r, k_c> <G_r, v_c>,
+//       S' <- lam^L S' + L lam^(L-1) S + sum_c (L-1-c) lam^(L-2-c) k_c v_c^T.
+//     Every weight is non-negative, so no large terms cancel (the shortcut
+//     sum_s s <q'_s, dq'_s> - sum_j j <k_j, dk_j> loses digits to
+//     cancellation that grow with T).  At lam = 0 the weights n lam^(n-1)
+//     keep only n = 1: the one-sided derivative.
+//   reverse (scan_bwd_rev_fast): walks the time-reversed sequence (row views
+//     with a negative row stride) carrying R, and writes dk and dv from the
+//     one state.
+// Segment-entering states come from the usual state + prefix kernels
+// (scan_dstate_fast / scan_dprefix_kernel for the pair (A, A')).
+constexpr int kZeroBlocks = 64;  // workgroups per (b, h) of the zeroing kernel
 
 // n lam^(n-1), the derivative of lam^n (0 for n = 0)
 __device__ __forceinline__ float dpow_int(float lam, int n) {
   return n > 0 ? static_cast<float>(n) * pow_int(lam, n - 1) : 0.f;
 }
 
-// workspace of the backward: ones (eta = 1 for the scans) | fp64 partial
-// sums of deta [BH][kBwdBlocks] and dlam [BH][n_seg] | the scans' state
-// workspace (also S of the dlam pass) | S' of the dlam pass
-size_t scan_bwd_head_bytes(int H) { return ((size_t)H * sizeof(float) + 255) / 256 * 256; }
+// workspace of the backward: fp64 shares of deta and dlam [2][BH][n_seg] |
+// segment-entering states (A, then R) | segment-entering A'
 size_t scan_bwd_part_bytes(int B, int H, int n_seg) {
-  return ((size_t)B * H * (kBwdBlocks + n_seg) * sizeof(double) + 255) / 256 * 256;
+  return ((size_t)2 * B * H * n_seg * sizeof(double) + 255) / 256 * 256;
 }
 
 __global__ void fill_kernel(float* __restrict__ p, int n, float x) {
@@ -584,35 +586,35 @@ __global__ void fill_kernel(float* __restrict__ p, int n, float x) {
   if (i < n) p[i] = x;
 }
 
-// Per (block, b, h): fp64 partial sums of <q'_s, dq1'_s> over rows of the
-// active range, and dq, dk, dv scaled by eta in place.
+// dq rows t < W and dk, dv rows t >= T - W are 0 (nothing reads or writes them).
+__global__ void scan_bwd_zero_kernel(float* __restrict__ dq, float* __restrict__ dk,
+                                     float* __restrict__ dv, long T, int D, long zq, long n_act) {
+  const long bh = blockIdx.y, n1 = zq * D, n2 = (T - n_act) * D;
+  const long base = bh * T * D;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n1 + 2 * n2;
+       i += (long)gridDim.x * blockDim.x) {
+    if (i < n1)
+      dq[base + i] = 0.f;
+    else if (i < n1 + n2)
+      dk[base + n_act * D + (i - n1)] = 0.f;
+    else
+      dv[base + n_act * D + (i - n1 - n2)] = 0.f;
+  }
+}
+
+// S tiles of this wave (S^T layout in registers) to an LDS copy of S itself,
+// [dk][dv] with stride S.
 template <int D>
-__global__ __launch_bounds__(256) void scan_bwd_finalize(const float* __restrict__ q,
-                                                         const float* __restrict__ eta, int H, int T,
-                                                         int W, int n_act, float* __restrict__ dq,
-                                                         float* __restrict__ dk, float* __restrict__ dv,
-                                                         double* __restrict__ part) {
-  __shared__ double red[256];
-  const int blk = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  const float et = eta[bh % H];
-  const int per = (n_act + kBwdBlocks - 1) / kBwdBlocks;
-  const int r0 = min(n_act, blk * per), r1 = min(n_act, r0 + per);
-  const long base = (long)bh * T * D;
-  double s = 0.0;
-  for (long i = (long)r0 * D + t; i < (long)r1 * D; i += 256) {
-    const float dqv = dq[base + (long)W * D + i];
-    s += (double)q[base + (long)W * D + i] * dqv;
-    dq[base + (long)W * D + i] = et * dqv;
-    dk[base + i] *= et;
-    dv[base + i] *= et;
+__device__ __forceinline__ void publish_state_t(float* sS, const floatx4* acc) {
+  using F = FastTiles<D>;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int i = 0; i < F::TPW; ++i) {
+    int a, b;
+    if (!state_tile<D>(w, i, a, b)) continue;
+    *reinterpret_cast<float4*>(sS + (16 * b + r) * F::S + 16 * a + 4 * g) =
+        make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
   }
-  red[t] = s;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (t < off) red[t] += red[t + off];
-    __syncthreads();
-  }
-  if (t == 0) part[(long)bh * kBwdBlocks + blk] = red[0];
 }
 
 // Per (segment, b, h) but the last: the segment's own state U and its lam
@@ -624,8 +626,8 @@ __global__ __launch_bounds__(256) void scan_dstate_fast(RowView<const float> vk,
                                                         float* __restrict__ dws) {
   using F = FastTiles<D>;
   __shared__ __attribute__((aligned(16))) float sKt[D * F::ST];
-  __shared__ __attribute__((aligned(16))) float sKd[D * F::ST];
-  __shared__ __attribute__((aligned(16))) float sVt[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sVw[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sVd[D * F::ST];
   __shared__ float sW[CH], sWd[CH];
   const int seg = blockIdx.x, bh = blockIdx.z;
   const float lm = lam[bh % H];
@@ -649,9 +651,9 @@ __global__ __launch_bounds__(256) void scan_dstate_fast(RowView<const float> vk,
       sWd[threadIdx.x] = n >= 0 ? dpow_int(lm, n) : 0.f;
     }
     lds_barrier();
-    put_cols<D>(sKt, xk, sW);
-    put_cols<D>(sKd, xk, sWd);
-    put_cols<D>(sVt, xv, nullptr);
+    put_cols<D>(sKt, xk, nullptr);
+    put_cols<D>(sVw, xv, sW);
+    put_cols<D>(sVd, xv, sWd);
     lds_barrier();
     if (c + 1 < c_end) {
       const int Ln = min(CH, n_act - (c + 1) * CH);
@@ -661,8 +663,8 @@ __global__ __launch_bounds__(256) void scan_dstate_fast(RowView<const float> vk,
     const float lL = pow_int(lm, L), dL = dpow_int(lm, L);
 #pragma unroll
     for (int i = 0; i < F::TPW; ++i) dacc[i] = lL * dacc[i] + dL * acc[i];
-    fast_state_update<D>(dacc, sVt, sKd, 1.f);
-    fast_state_update<D>(acc, sVt, sKt, lL);
+    fast_state_update<D>(dacc, sVd, sKt, 1.f);
+    fast_state_update<D>(acc, sVw, sKt, lL);
   }
   store_state<D>(ws + ((long)bh * n_seg + seg) * D * D, acc, D);
   store_state<D>(dws + ((long)bh * n_seg + seg) * D * D, dacc, D);
@@ -690,39 +692,40 @@ __global__ void scan_dprefix_kernel(const float* __restrict__ lam, int H, int n_
   dp[(long)(n_seg - 1) * n_per_bh] = drun;
 }
 
-// Per (segment, b, h): this segment's share of dL/dlam (eta = 1) in fp64.
-// Phase 1 stages q', k, G, v row-major for the two 64 x 64 Gram matrices of
-// the in-chunk term; phase 2 reuses the same LDS for the transposed,
-// weighted copies that feed the state products.
+// Forward-direction pass, per (segment, b, h).  Phase 1 stages q', k, G, v
+// row-major for the two 64 x 64 Gram matrices and the entering-state read;
+// phase 2 reuses the same LDS for the transposed copies that feed the
+// in-chunk part of dq, the entering-state terms and the state updates.
 template <int D>
-__global__ __launch_bounds__(256) void scan_dlam_fast(RowView<const float> vq, RowView<const float> vk,
-                                                      RowView<const float> vv, RowView<const float> vg,
-                                                      const float* __restrict__ lam, int H, int n_act,
-                                                      int seg_chunks, int n_seg,
-                                                      const float* __restrict__ ws,
-                                                      const float* __restrict__ dws,
-                                                      double* __restrict__ part) {
+__global__ __launch_bounds__(256) void scan_bwd_fwd_fast(
+    RowView<const float> vq, RowView<const float> vk, RowView<const float> vv, RowView<const float> vg,
+    const float* __restrict__ lam, const float* __restrict__ eta, int H, int n_act, int seg_chunks,
+    int n_seg, const float* __restrict__ ws, const float* __restrict__ dws, RowView<float> vdq,
+    double* __restrict__ part_eta, double* __restrict__ part_lam) {
   using F = FastTiles<D>;
+  constexpr int NT = D / 16;
   constexpr int ROWS = CH * F::S;  // one [64][D] array
   constexpr int COLS = D * F::ST;  // one [D][64] array
   constexpr int NLDS = 4 * ROWS > 6 * COLS ? 4 * ROWS : 6 * COLS;
   __shared__ __attribute__((aligned(16))) float lds[NLDS];
+  __shared__ __attribute__((aligned(16))) float sS[D * F::S];   // entering S, [dk][dv]
+  __shared__ __attribute__((aligned(16))) float sP[CH * F::ST]; // lam^(r-c) <G_r, v_c>, c <= r
   __shared__ float sPow[CH + 1];
   __shared__ float sW[CH], sWd[CH], sW1[CH], sW2[CH];
-  __shared__ double red[256];
+  __shared__ double red[2][256];
   float* const sQ = lds;
   float* const sK = lds + ROWS;
   float* const sG = lds + 2 * ROWS;
   float* const sV = lds + 3 * ROWS;
   float* const sKt = lds;
-  float* const sKd = lds + COLS;
-  float* const sVt = lds + 2 * COLS;
+  float* const sVw = lds + COLS;
+  float* const sVd = lds + 2 * COLS;
   float* const sQ1 = lds + 3 * COLS;
   float* const sQ2 = lds + 4 * COLS;
   float* const sGt = lds + 5 * COLS;
 
   const int seg = blockIdx.x, bh = blockIdx.z;
-  const float lm = lam[bh % H];
+  const float lm = lam[bh % H], et = eta[bh % H];
   const int l = lane_id(), w = wave_id(), r = l & 15, g = l >> 4;
   const int c_begin = seg * seg_chunks;
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
@@ -740,10 +743,10 @@ __global__ __launch_bounds__(256) void scan_dlam_fast(RowView<const float> vq, R
     load_rows<D>(xv, vv.row(bh, s0), vv.rs, L);
     load_rows<D>(xg, vg.row(bh, s0), vg.rs, L);
   }
-  double tot = 0.0;
+  double tot_eta = 0.0, tot_lam = 0.0;
   for (int c = c_begin; c < c_end; ++c) {
     const int s0 = c * CH, L = min(CH, n_act - s0);
-    lds_barrier();  // every wave is done with the previous chunk's phase 2
+    lds_barrier();  // every wave is done with the previous chunk
     if (threadIdx.x < CH) {
       const int t = threadIdx.x, n = L - 1 - t;
       sW[t] = n >= 0 ? sPow[n] : 0.f;
@@ -755,9 +758,10 @@ __global__ __launch_bounds__(256) void scan_dlam_fast(RowView<const float> vq, R
     put_rows<D>(sK, xk);
     put_rows<D>(sG, xg);
     put_rows<D>(sV, xv);
+    publish_state_t<D>(sS, acc);
     lds_barrier();
-    // in-chunk term from <q'_r, k_c> and <G_r, v_c>, this wave's rows 16w..
-    float intra = 0.f;
+    // in-chunk pairs from <q'_r, k_c> and <G_r, v_c>, this wave's rows 16w..
+    float in_eta = 0.f, in_lam = 0.f;
     {
       floatx4 pa[4] = {zero4(), zero4(), zero4(), zero4()};
       floatx4 pb[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -767,14 +771,26 @@ __global__ __launch_bounds__(256) void scan_dlam_fast(RowView<const float> vq, R
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int n = (16 * w + 4 * g + e) - (16 * ct + r);
-          if (n > 0) intra += static_cast<float>(n) * sPow[n - 1] * pa[ct][e] * pb[ct][e];
+          const int rr = 16 * w + 4 * g + e, cc = 16 * ct + r, n = rr - cc;
+          const float wpb = n >= 0 ? sPow[n] * pb[ct][e] : 0.f;
+          sP[rr * F::ST + cc] = wpb;
+          in_eta += wpb * pa[ct][e];
+          if (n > 0) in_lam += static_cast<float>(n) * sPow[n - 1] * pa[ct][e] * pb[ct][e];
         }
     }
+    // dq' rows: lam^(r+1) S G_r now, the in-chunk part after phase 2
+    floatx4 o[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[t] = zero4();
+    mma_rows<D, NT>(sG + 16 * w * F::S, F::S, sS, 16 * F::S, F::S, o);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[t][e] *= sPow[16 * w + 4 * g + e + 1];
     lds_barrier();  // phase-1 arrays are read
-    put_cols<D>(sKt, xk, sW);
-    put_cols<D>(sKd, xk, sWd);
-    put_cols<D>(sVt, xv, nullptr);
+    put_cols<D>(sKt, xk, nullptr);
+    put_cols<D>(sVw, xv, sW);
+    put_cols<D>(sVd, xv, sWd);
     put_cols<D>(sQ1, xq, sW1);
     put_cols<D>(sQ2, xq, sW2);
     put_cols<D>(sGt, xg, nullptr);
@@ -786,9 +802,16 @@ __global__ __launch_bounds__(256) void scan_dlam_fast(RowView<const float> vq, R
       load_rows<D>(xv, vv.row(bh, s1), vv.rs, Ln);
       load_rows<D>(xg, vg.row(bh, s1), vg.rs, Ln);
     }
-    // entering-state term: <S, E1> + <S', E2> with E^T = G^T diag(w) Q' in
-    // the tile layout of the state
-    float inter = 0.f;
+    mma_rows<CH, NT>(sP + 16 * w * F::ST, F::ST, sKt, 16 * F::ST, F::ST, o);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * w + 4 * g + e;
+        if (rr < L) vdq.row(bh, s0 + rr)[16 * t + r] = et * o[t][e];
+      }
+    // entering-state terms with E^T = G^T diag(w) Q' in the state's tile layout
+    float st_eta = 0.f, st_lam = 0.f;
     {
       floatx4 e1[F::TPW], e2[F::TPW];
 #pragma unroll
@@ -798,25 +821,154 @@ __global__ __launch_bounds__(256) void scan_dlam_fast(RowView<const float> vq, R
 #pragma unroll
       for (int i = 0; i < F::TPW; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) inter += acc[i][e] * e1[i][e] + dacc[i][e] * e2[i][e];
+        for (int e = 0; e < 4; ++e) {
+          st_eta += acc[i][e] * e2[i][e];
+          st_lam += acc[i][e] * e1[i][e] + dacc[i][e] * e2[i][e];
+        }
     }
-    tot += (double)intra + (double)inter;
+    tot_eta += (double)in_eta + (double)st_eta;
+    tot_lam += (double)in_lam + (double)st_lam;
     const float lL = sPow[L], dL = dpow_int(lm, L);
 #pragma unroll
     for (int i = 0; i < F::TPW; ++i) dacc[i] = lL * dacc[i] + dL * acc[i];
-    fast_state_update<D>(dacc, sVt, sKd, 1.f);
-    fast_state_update<D>(acc, sVt, sKt, lL);
+    fast_state_update<D>(dacc, sVd, sKt, 1.f);
+    fast_state_update<D>(acc, sVw, sKt, lL);
   }
-  red[threadIdx.x] = tot;
+  red[0][threadIdx.x] = tot_eta;
+  red[1][threadIdx.x] = tot_lam;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
-    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    if ((int)threadIdx.x < off) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + off];
+      red[1][threadIdx.x] += red[1][threadIdx.x + off];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) part[(long)bh * n_seg + seg] = red[0];
+  if (threadIdx.x == 0) {
+    part_eta[(long)bh * n_seg + seg] = red[0][0];
+    part_lam[(long)bh * n_seg + seg] = red[1][0];
+  }
 }
 
-// Per head: deta and dlam from the partial sums of every sequence.
+// Reverse-direction pass, per (segment, b, h), on views that are already
+// time-reversed (row r of each view is position n_act - 1 - r; q' and G are
+// shifted by W).  R^T tiles live in the registers; per chunk
+//   dk_r = lam^(r+1) R^T v_r + sum_{c<=r} lam^(r-c) <v_r, G_c> q'_c,
+//   dv_r = lam^(r+1) R k_r   + sum_{c<=r} lam^(r-c) <k_r, q'_c> G_c,
+//   R <- lam^L R + sum_c lam^(L-1-c) G_c q'_c^T.
+template <int D>
+__global__ __launch_bounds__(256) void scan_bwd_rev_fast(
+    RowView<const float> vv, RowView<const float> vk, RowView<const float> vq, RowView<const float> vg,
+    const float* __restrict__ lam, const float* __restrict__ eta, int H, int n_act, int seg_chunks,
+    int n_seg, const float* __restrict__ ws, RowView<float> vdk, RowView<float> vdv) {
+  using F = FastTiles<D>;
+  constexpr int NT = D / 16;
+  constexpr int ROWS = CH * F::S;
+  constexpr int COLS = D * F::ST;
+  constexpr int NLDS = 4 * ROWS > 3 * COLS ? 4 * ROWS : 3 * COLS;
+  __shared__ __attribute__((aligned(16))) float lds[NLDS];
+  __shared__ __attribute__((aligned(16))) float sRt[D * F::S];   // R^T, [dk][dv]
+  __shared__ __attribute__((aligned(16))) float sR[D * F::S];    // R, [dv][dk]
+  __shared__ __attribute__((aligned(16))) float sPk[CH * F::ST]; // lam^(r-c) <v_r, G_c>
+  __shared__ __attribute__((aligned(16))) float sPv[CH * F::ST]; // lam^(r-c) <k_r, q'_c>
+  __shared__ float sPow[CH + 1];
+  __shared__ float sW[CH];
+  float* const sV = lds;
+  float* const sK = lds + ROWS;
+  float* const sQ = lds + 2 * ROWS;
+  float* const sG = lds + 3 * ROWS;
+  float* const sQt = lds;
+  float* const sGt = lds + COLS;
+  float* const sQw = lds + 2 * COLS;
+
+  const int seg = blockIdx.x, bh = blockIdx.z;
+  const float lm = lam[bh % H], et = eta[bh % H];
+  const int l = lane_id(), w = wave_id(), r = l & 15, g = l >> 4;
+  const int c_begin = seg * seg_chunks;
+  const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
+  if (threadIdx.x <= CH) sPow[threadIdx.x] = pow_int(lm, threadIdx.x);
+
+  floatx4 acc[F::TPW];  // R^T tiles: (dk tile a, dv tile b)
+  load_state<D>(acc, n_seg > 1 && seg > 0 ? ws + ((long)bh * n_seg + seg) * D * D : nullptr, D);
+  float4 xv[F::NV4], xk[F::NV4], xq[F::NV4], xg[F::NV4];
+  if (c_begin < c_end) {
+    const int s0 = c_begin * CH, L = min(CH, n_act - s0);
+    load_rows<D>(xv, vv.row(bh, s0), vv.rs, L);
+    load_rows<D>(xk, vk.row(bh, s0), vk.rs, L);
+    load_rows<D>(xq, vq.row(bh, s0), vq.rs, L);
+    load_rows<D>(xg, vg.row(bh, s0), vg.rs, L);
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const int s0 = c * CH, L = min(CH, n_act - s0);
+    lds_barrier();  // every wave is done with the previous chunk
+    if (threadIdx.x < CH) {
+      const int n = L - 1 - (int)threadIdx.x;
+      sW[threadIdx.x] = n >= 0 ? sPow[n] : 0.f;
+    }
+    put_rows<D>(sV, xv);
+    put_rows<D>(sK, xk);
+    put_rows<D>(sQ, xq);
+    put_rows<D>(sG, xg);
+    publish_state<D>(sRt, acc);
+    publish_state_t<D>(sR, acc);
+    lds_barrier();
+    {
+      floatx4 pk[4] = {zero4(), zero4(), zero4(), zero4()};
+      floatx4 pv[4] = {zero4(), zero4(), zero4(), zero4()};
+      mma_rows<D, 4>(sV + 16 * w * F::S, F::S, sG, 16 * F::S, F::S, pk);
+      mma_rows<D, 4>(sK + 16 * w * F::S, F::S, sQ, 16 * F::S, F::S, pv);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 16 * w + 4 * g + e, cc = 16 * ct + r, n = rr - cc;
+          const float f = n >= 0 ? sPow[n] : 0.f;
+          sPk[rr * F::ST + cc] = f * pk[ct][e];
+          sPv[rr * F::ST + cc] = f * pv[ct][e];
+        }
+    }
+    floatx4 ok[NT], ov[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ok[t] = ov[t] = zero4();
+    mma_rows<D, NT>(sV + 16 * w * F::S, F::S, sRt, 16 * F::S, F::S, ok);
+    mma_rows<D, NT>(sK + 16 * w * F::S, F::S, sR, 16 * F::S, F::S, ov);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = sPow[16 * w + 4 * g + e + 1];
+        ok[t][e] *= f;
+        ov[t][e] *= f;
+      }
+    lds_barrier();  // phase-1 arrays are read
+    put_cols<D>(sQt, xq, nullptr);
+    put_cols<D>(sGt, xg, nullptr);
+    put_cols<D>(sQw, xq, sW);
+    lds_barrier();
+    if (c + 1 < c_end) {
+      const int s1 = s0 + CH, Ln = min(CH, n_act - s1);
+      load_rows<D>(xv, vv.row(bh, s1), vv.rs, Ln);
+      load_rows<D>(xk, vk.row(bh, s1), vk.rs, Ln);
+      load_rows<D>(xq, vq.row(bh, s1), vq.rs, Ln);
+      load_rows<D>(xg, vg.row(bh, s1), vg.rs, Ln);
+    }
+    mma_rows<CH, NT>(sPk + 16 * w * F::ST, F::ST, sQt, 16 * F::ST, F::ST, ok);
+    mma_rows<CH, NT>(sPv + 16 * w * F::ST, F::ST, sGt, 16 * F::ST, F::ST, ov);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * w + 4 * g + e;
+        if (rr < L) {
+          vdk.row(bh, s0 + rr)[16 * t + r] = et * ok[t][e];
+          vdv.row(bh, s0 + rr)[16 * t + r] = et * ov[t][e];
+        }
+      }
+    fast_state_update<D>(acc, sQw, sGt, sPow[L]);
+  }
+}
+
+// Per head: deta and dlam from the shares of every sequence and segment.
 __global__ void scan_bwd_reduce(const double* __restrict__ part_eta, const double* __restrict__ part_lam,
                                 const float* __restrict__ eta, int B, int H, int n_seg,
                                 float* __restrict__ dlam, float* __restrict__ deta) {
@@ -825,8 +977,10 @@ __global__ void scan_bwd_reduce(const double* __restrict__ part_eta, const doubl
   double a = 0.0, b = 0.0;
   for (int bb = 0; bb < B; ++bb) {
     const long bh = (long)bb * H + h;
-    for (int i = 0; i < kBwdBlocks; ++i) a += part_eta[bh * kBwdBlocks + i];
-    for (int i = 0; i < n_seg; ++i) b += part_lam[bh * n_seg + i];
+    for (int i = 0; i < n_seg; ++i) {
+      a += part_eta[bh * n_seg + i];
+      b += part_lam[bh * n_seg + i];
+    }
   }
   deta[h] = (float)a;
   dlam[h] = (float)((double)eta[h] * b);
@@ -840,51 +994,21 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   const int BH = B * H;
   const ScanPlan p = plan_scan(B, H, T, D, D, W);
   const int n_act = p.n_act;
-  const size_t off_part = scan_bwd_head_bytes(H);
-  const size_t off_sws = off_part + scan_bwd_part_bytes(B, H, p.n_seg);
-  float* ones = reinterpret_cast<float*>(ws);
-  double* part_eta = reinterpret_cast<double*>(ws + off_part);
-  double* part_lam = part_eta + (long)BH * kBwdBlocks;
-  float* sws = reinterpret_cast<float*>(ws + off_sws);
-  float* dws = reinterpret_cast<float*>(ws + off_sws + scan_ws_bytes(p, B, H, D, D));
-  hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, ones, H, 1.f);
   const long zq = std::min<long>(W, T);
-  if (zq > 0)
-    hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)std::min<long>((zq * D + 255) / 256, 1024), BH),
-                       dim3(256), 0, s, dq, zq, (long)T, D);
-  if (T - n_act > 0) {
-    const long zr = T - n_act;
-    const dim3 g((unsigned)std::min<long>((zr * D + 255) / 256, 1024), BH);
-    hipLaunchKernelGGL(zero_rows_kernel, g, dim3(256), 0, s, dk + (long)n_act * D, zr, (long)T, D);
-    hipLaunchKernelGGL(zero_rows_kernel, g, dim3(256), 0, s, dv + (long)n_act * D, zr, (long)T, D);
-  }
+  hipLaunchKernelGGL(scan_bwd_zero_kernel, dim3(kZeroBlocks, BH), dim3(256), 0, s, dq, dk, dv, (long)T, D,
+                     zq, (long)std::max(n_act, 0));
   if (n_act <= 0) {
     hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dlam, H, 0.f);
     hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, deta, H, 0.f);
     return hipGetLastError();
   }
+  double* part_eta = reinterpret_cast<double*>(ws);
+  double* part_lam = part_eta + (long)BH * p.n_seg;
+  float* sws = reinterpret_cast<float*>(ws + scan_bwd_part_bytes(B, H, p.n_seg));
+  float* dws = reinterpret_cast<float*>(ws + scan_bwd_part_bytes(B, H, p.n_seg) + scan_ws_bytes(p, B, H, D, D));
   const long bs = (long)T * D;
   const int nel = D * D;
-  auto scan = [&](RowView<const float> vq, RowView<const float> vk, RowView<const float> vv,
-                  RowView<float> vm, bool timed) {
-    if (p.n_seg > 1) {
-      hipLaunchKernelGGL((scan_state_fast<D, float>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, vk, vv,
-                         lam, ones, H, n_act, p.seg_chunks, p.n_seg, sws);
-      hipLaunchKernelGGL(scan_prefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H, nel,
-                         n_act, p.seg_chunks * CH, p.n_seg, sws);
-    }
-    if (timed) profile_mark_before(s);
-    hipLaunchKernelGGL((scan_output_fast<D, float>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, vq, vk, vv,
-                       lam, ones, H, n_act, p.seg_chunks, p.n_seg, sws, vm, nullptr);
-    if (timed) profile_mark_after(s);
-  };
-  const long last = (long)(n_act - 1) * D, tl = (long)(T - 1) * D;
-  // dq' = read of (G, v, k)
-  scan({dm + (long)W * D, bs, D}, {v, bs, D}, {k, bs, D}, {dq + (long)W * D, bs, D}, true);
-  // dk, dv: reads of the time-reversed sequence (row s' of a view is s = n_act - 1 - s')
-  scan({v + last, bs, -D}, {dm + tl, bs, -D}, {q + tl, bs, -D}, {dk + last, bs, -D}, false);
-  scan({k + last, bs, -D}, {q + tl, bs, -D}, {dm + tl, bs, -D}, {dv + last, bs, -D}, false);
-  // dlam: its own pass over (q', k, v, G) with the derivative state
+  // forward direction: dq, deta, dlam
   const RowView<const float> fq{q + (long)W * D, bs, D}, fk{k, bs, D}, fv{v, bs, D},
       fg{dm + (long)W * D, bs, D};
   if (p.n_seg > 1) {
@@ -893,10 +1017,24 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
     hipLaunchKernelGGL(scan_dprefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H, nel,
                        p.seg_chunks * CH, p.n_seg, sws, dws);
   }
-  hipLaunchKernelGGL((scan_dlam_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, fq, fk, fv, fg, lam, H,
-                     n_act, p.seg_chunks, p.n_seg, sws, dws, part_lam);
-  hipLaunchKernelGGL((scan_bwd_finalize<D>), dim3(kBwdBlocks, BH), dim3(256), 0, s, q, eta, H, T, W, n_act,
-                     dq, dk, dv, part_eta);
+  profile_mark_before(s);
+  hipLaunchKernelGGL((scan_bwd_fwd_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, fq, fk, fv, fg, lam,
+                     eta, H, n_act, p.seg_chunks, p.n_seg, sws, dws, RowView<float>{dq + (long)W * D, bs, D},
+                     part_eta, part_lam);
+  profile_mark_after(s);
+  // reverse direction: dk, dv (row r of each view is position n_act - 1 - r)
+  const long last = (long)(n_act - 1) * D, tl = (long)(T - 1) * D;
+  const RowView<const float> rv{v + last, bs, -D}, rk{k + last, bs, -D}, rq{q + tl, bs, -D},
+      rg{dm + tl, bs, -D};
+  if (p.n_seg > 1) {
+    hipLaunchKernelGGL((scan_state_fast<D, float>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, rg, rq, lam,
+                       nullptr, H, n_act, p.seg_chunks, p.n_seg, sws);
+    hipLaunchKernelGGL(scan_prefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H, nel, n_act,
+                       p.seg_chunks * CH, p.n_seg, sws);
+  }
+  hipLaunchKernelGGL((scan_bwd_rev_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, rv, rk, rq, rg, lam, eta,
+                     H, n_act, p.seg_chunks, p.n_seg, sws, RowView<float>{dk + last, bs, -D},
+                     RowView<float>{dv + last, bs, -D});
   hipLaunchKernelGGL(scan_bwd_reduce, dim3((H + 63) / 64), dim3(64), 0, s, part_eta, part_lam, eta, B, H,
                      p.n_seg, dlam, deta);
   return hipGetLastError();
@@ -1014,7 +1152,7 @@ namespace tc {
 
 size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W) {
   const ScanPlan p = plan_scan(B, H, T, d, d, W);
-  return scan_bwd_head_bytes(H) + scan_bwd_part_bytes(B, H, p.n_seg) + 2 * scan_ws_bytes(p, B, H, d, d);
+  return scan_bwd_part_bytes(B, H, p.n_seg) + 2 * scan_ws_bytes(p, B, H, d, d);
 }
 
 hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
