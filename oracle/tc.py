@@ -39,6 +39,7 @@ __all__ = [
     "tc_scan_chunked",
     "chunk_mean_scan",
     "tc_scan_backward",
+    "tc_gated_read_backward",
 ]
 
 
@@ -356,3 +357,22 @@ def tc_scan_backward(q, k, v, lam, eta, W, dm):
             gv[:, :, e] += et[..., 0] * np.einsum("bhij,bhi->bhj", dA, k[:, :, e])
             dA = lm * dA
     return gq, gk, gv, glam.sum(axis=0), geta.sum(axis=0)
+
+
+def tc_gated_read_backward(q, k, v, lam, eta, g, W, dy):
+    """Gradients of L = sum <dy, sigmoid(g) m> through the L2 branch of the
+    fused layer y = y_local + sigmoid(g) m (Tensor Cache, Methodology 1,
+    fusion; g is learned per head).  y_local does not depend on lam, eta, g;
+    its own gradients are not part of this function.
+
+    Chain rule: the read's cotangent is dm = sigmoid(g) dy; the gate's is
+    dg = sigmoid(g) (1 - sigmoid(g)) sum_{b,t} <dy_t, m_t>.
+
+    Returns (dq, dk, dv, dlam, deta, dg); per-head terms summed over the batch.
+    """
+    dy = _f64(dy)
+    s = sigmoid(g)
+    gq, gk, gv, glam, geta = tc_scan_backward(q, k, v, lam, eta, W, s[None, :, None, None] * dy)
+    m, _ = tc_scan(q, k, v, lam, eta, W)
+    gg = s * (1.0 - s) * np.einsum("bhtd,bhtd->h", dy, m)
+    return gq, gk, gv, glam, geta, gg

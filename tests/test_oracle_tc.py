@@ -578,3 +578,62 @@ def test_scan_backward_pins_catch_planted_mistakes(kind):
     lmn = _scan_loss(q, k, v, lam - np.array([h, 0]), eta, W, dm)
     worst = max(worst, abs(glam[0] - (lp - lmn) / (2 * h)))
     assert worst > 1e-4
+
+
+def _gated_loss(q, k, v, lam, eta, g, W, dy):
+    m = O.tc_scan(q, k, v, lam, eta, W)[0]
+    return float(np.sum(O.sigmoid(g)[None, :, None, None] * m * dy))
+
+
+def test_gated_read_backward_matches_central_differences():
+    q, k, v, lam, eta, g = rand_inputs(60, B=2, H=2, T=11, dk=3, dv=2)
+    g = np.array([0.7, -1.9])
+    W = 3
+    dy = np.random.default_rng(61).standard_normal(q.shape[:3] + (2,))
+    gq, gk, gv, glam, geta, gg = O.tc_gated_read_backward(q, k, v, lam, eta, g, W, dy)
+    h = 1e-6
+    for name, x, gr in (("q", q, gq), ("k", k, gk), ("v", v, gv)):
+        for i in [(0, 0, 5, 0), (1, 1, 9, 1), (0, 1, 2, 1), (1, 0, 0, 0)]:
+            xp, xm = x.copy(), x.copy()
+            xp[i] += h
+            xm[i] -= h
+            a = {"q": q, "k": k, "v": v}
+            a[name] = xp
+            lp = _gated_loss(a["q"], a["k"], a["v"], lam, eta, g, W, dy)
+            a[name] = xm
+            lmn = _gated_loss(a["q"], a["k"], a["v"], lam, eta, g, W, dy)
+            np.testing.assert_allclose(gr[i], (lp - lmn) / (2 * h), rtol=1e-6, atol=1e-9, err_msg=name)
+    for hh in range(2):
+        for name, gr in (("lam", glam), ("eta", geta), ("g", gg)):
+            a = {"lam": lam.copy(), "eta": eta.copy(), "g": g.copy()}
+            a[name][hh] += h
+            lp = _gated_loss(q, k, v, a["lam"], a["eta"], a["g"], W, dy)
+            a[name][hh] -= 2 * h
+            lmn = _gated_loss(q, k, v, a["lam"], a["eta"], a["g"], W, dy)
+            np.testing.assert_allclose(gr[hh], (lp - lmn) / (2 * h), rtol=1e-6, atol=1e-9, err_msg=name)
+
+
+def test_gated_read_backward_gate_limits():
+    # a wide-open gate passes the read's gradients through with dg -> 0; a
+    # closed gate stops every gradient
+    q, k, v, lam, eta, _ = rand_inputs(62, B=1, H=2, T=9, dk=2, dv=2)
+    dy = np.random.default_rng(63).standard_normal(q.shape)
+    ref = O.tc_scan_backward(q, k, v, lam, eta, 2, dy)
+    out = O.tc_gated_read_backward(q, k, v, lam, eta, np.array([40.0, 40.0]), 2, dy)
+    for a, b in zip(out[:5], ref):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+    assert np.all(np.abs(out[5]) < 1e-15)
+    out = O.tc_gated_read_backward(q, k, v, lam, eta, np.array([-800.0, -800.0]), 2, dy)
+    assert all(np.all(a == 0) for a in out)
+
+
+def test_gated_read_backward_pin_catches_sigmoid_for_its_derivative():
+    q, k, v, lam, eta, _ = rand_inputs(64, B=1, H=1, T=8, dk=2, dv=2)
+    g = np.array([0.3])
+    dy = np.random.default_rng(65).standard_normal(q.shape)
+    m = O.tc_scan(q, k, v, lam, eta, 2)[0]
+    wrong = O.sigmoid(g) * np.einsum("bhtd,bhtd->h", dy, m)
+    h = 1e-6
+    fd = (_gated_loss(q, k, v, lam, eta, g + h, 2, dy) - _gated_loss(q, k, v, lam, eta, g - h, 2, dy)) / (2 * h)
+    assert abs(wrong[0] - fd) > 1e-3
+
