@@ -314,9 +314,9 @@ def bench_scan_backward(steps, warmup, dev):
     nb = ops.scan_backward_workspace(w.B, w.H, w.T, w.d, w.d, w.W, 0)
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     lib = ops.lib()
-    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, ops._ptr(lam), ops._ptr(eta), w.B, w.H, w.T, w.d,
-            w.d, w.W, 64, ops._ptr(dm), ops._ptr(gq), ops._ptr(gk), ops._ptr(gv), ops._ptr(glam),
-            ops._ptr(geta), ops._ptr(ws), ws.numel(), ops._stream())
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, ops._ptr(lam), ops._ptr(eta), None, w.B, w.H, w.T,
+            w.d, w.d, w.W, 64, ops._ptr(dm), ops._ptr(gq), ops._ptr(gk), ops._ptr(gv), ops._ptr(glam),
+            ops._ptr(geta), None, ops._ptr(ws), ws.numel(), ops._stream())
 
     def call(_):
         if lib.tc_scan_backward(*args) != 0:

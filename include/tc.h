@@ -79,12 +79,19 @@ tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype 
 
 /* ---------------------------------------------------------------------------
  * Backward of the L2 read (Tensor Cache, Methodology 1 and 2: lam and eta
- * are learned per head): gradients of L = sum_t <dm_t, m_t>, m as returned
- * by tc_scan_forward for the same arguments.  A_final takes no gradient.
+ * are learned per head), optionally through the gate of the fused layer
+ * (Methodology 1, fusion: y = y_local + sigmoid(g) m with g learned per head).
+ *   g == NULL: dm is the cotangent of m as returned by tc_scan_forward for the
+ *     same arguments; the gradients are those of L = sum_t <dm_t, m_t>.
+ *   g != NULL ([H] float32 gate logits): dm is the cotangent dy of the gated
+ *     branch sigmoid(g) m; the gradients are those of L = sum_t <dy_t,
+ *     sigmoid(g) m_t>, and dg [H] receives dL/dg.  y_local's own gradients
+ *     are not computed here.  g and dg are given together or not at all.
+ * A_final takes no gradient.
  *   dm       [B, H, T, dv] float32 (rows t < W are ignored: m is 0 there).
  *   dq, dk   out [B, H, T, dk] float32; dv out [B, H, T, dv] float32
  *            (dq rows t < W and dk, dv rows t >= T - W are 0).
- *   dlam, deta out [H] float32, summed over the batch.
+ *   dlam, deta (and dg) out [H] float32, summed over the batch.
  *   ws       at least tc_scan_backward_workspace_bytes(...) bytes (may be NULL
  *            when that is 0).
  * Supported: dt = TC_F32, dk == dv in {16, 32, 64}, chunk = 64; anything
@@ -93,10 +100,11 @@ tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype 
 size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk,
                                         tc_dtype dt);
 tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt,
-                           const float* lam, const float* eta,
+                           const float* lam, const float* eta, const float* g,
                            int B, int H, int T, int dk, int dv, int W, int chunk,
                            const float* dm, float* dq, float* dk_out, float* dv_out,
-                           float* dlam, float* deta, void* ws, size_t ws_bytes, hipStream_t s);
+                           float* dlam, float* deta, float* dg, void* ws, size_t ws_bytes,
+                           hipStream_t s);
 
 /* ---------------------------------------------------------------------------
  * One streaming step of the two-level cache (Tensor Cache, Methodology 1).

@@ -33,8 +33,8 @@ SIGNATURES = {
     "tc_scan_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "tc_scan_forward": (_i, [_p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _z, _p]),
     "tc_scan_backward_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
-    "tc_scan_backward": (_i, [_p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p,
-                              _p, _z, _p]),
+    "tc_scan_backward": (_i, [_p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p,
+                              _p, _p, _p, _z, _p]),
     "tc_decode_step": (_i, [_p, _p, _p, _i, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p]),
     "tc_decode_layer_step": (_i, [_p, _p, _p, _i, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p,
                                   _p]),

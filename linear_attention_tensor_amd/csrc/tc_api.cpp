@@ -143,13 +143,15 @@ size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int
 }
 
 tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt, const float* lam,
-                           const float* eta, int B, int H, int T, int dk, int dv, int W, int chunk,
-                           const float* dm, float* dq, float* dk_out, float* dv_out, float* dlam,
-                           float* deta, void* ws, size_t ws_bytes, hipStream_t s) {
+                           const float* eta, const float* g, int B, int H, int T, int dk, int dv, int W,
+                           int chunk, const float* dm, float* dq, float* dk_out, float* dv_out, float* dlam,
+                           float* deta, float* dg, void* ws, size_t ws_bytes, hipStream_t s) {
   return guarded("tc_scan_backward", [&]() -> tc_status {
     const char* fn = "tc_scan_backward";
     tc_status st = check_scan_bwd(fn, B, H, T, dk, dv, W, chunk, dt);
     if (st != TC_OK) return st;
+    if ((g == nullptr) != (dg == nullptr))
+      return fail(TC_ERR_INVALID_ARG, "%s: g and dg are given together or not at all", fn);
     if (B == 0 || H == 0) return ok();
     if (!lam || !eta || !dlam || !deta)
       return fail(TC_ERR_INVALID_ARG, "%s: lam, eta, dlam, deta must not be NULL", fn);
@@ -160,8 +162,8 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
       return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
     return from_hip(tc::launch_tc_scan_backward(static_cast<const float*>(q), static_cast<const float*>(k),
-                                                static_cast<const float*>(v), lam, eta, B, H, T, dk, W, dm,
-                                                dq, dk_out, dv_out, dlam, deta, ws, s),
+                                                static_cast<const float*>(v), lam, eta, g, B, H, T, dk, W,
+                                                dm, dq, dk_out, dv_out, dlam, deta, dg, ws, s),
                     fn);
   });
 }

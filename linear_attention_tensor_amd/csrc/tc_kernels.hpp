@@ -24,9 +24,9 @@ size_t scan_ws_bytes(const ScanPlan& p, int B, int H, int dk, int dv);
 // Backward of the read (fp32 inputs, d = dk = dv in {16, 32, 64}).
 size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W);
 hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
-                                   const float* eta, int B, int H, int T, int d, int W,
+                                   const float* eta, const float* g, int B, int H, int T, int d, int W,
                                    const float* dm, float* dq, float* dk, float* dv, float* dlam,
-                                   float* deta, void* ws, hipStream_t s);
+                                   float* deta, float* dg, void* ws, hipStream_t s);
 
 hipError_t launch_tc_scan(const void* q, const void* k, const void* v, bool bf16,
                           const float* lam, const float* eta, int B, int H, int T, int dk, int dv,

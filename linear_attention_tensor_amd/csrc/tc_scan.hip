@@ -575,6 +575,11 @@ __device__ __forceinline__ float dpow_int(float lam, int n) {
   return n > 0 ? static_cast<float>(n) * pow_int(lam, n - 1) : 0.f;
 }
 
+// sigmoid(gate[h]) of the gated branch y = y_local + sigmoid(g) m, or 1 without a gate
+__device__ __forceinline__ float gate_factor(const float* gate, int h) {
+  return gate != nullptr ? 1.f / (1.f + expf(-gate[h])) : 1.f;
+}
+
 // workspace of the backward: fp64 shares of deta and dlam [2][BH][n_seg] |
 // segment-entering states (A, then R) | segment-entering A'
 size_t scan_bwd_part_bytes(int B, int H, int n_seg) {
@@ -700,8 +705,8 @@ template <int D>
 __global__ __launch_bounds__(256) void scan_bwd_fwd_fast(
     RowView<const float> vq, RowView<const float> vk, RowView<const float> vv, RowView<const float> vg,
     const float* __restrict__ lam, const float* __restrict__ eta, int H, int n_act, int seg_chunks,
-    int n_seg, const float* __restrict__ ws, const float* __restrict__ dws, RowView<float> vdq,
-    double* __restrict__ part_eta, double* __restrict__ part_lam) {
+    int n_seg, const float* __restrict__ ws, const float* __restrict__ dws, const float* __restrict__ gate,
+    RowView<float> vdq, double* __restrict__ part_eta, double* __restrict__ part_lam) {
   using F = FastTiles<D>;
   constexpr int NT = D / 16;
   constexpr int ROWS = CH * F::S;  // one [64][D] array
@@ -725,7 +730,7 @@ __global__ __launch_bounds__(256) void scan_bwd_fwd_fast(
   float* const sGt = lds + 5 * COLS;
 
   const int seg = blockIdx.x, bh = blockIdx.z;
-  const float lm = lam[bh % H], et = eta[bh % H];
+  const float lm = lam[bh % H], et = eta[bh % H] * gate_factor(gate, bh % H);
   const int l = lane_id(), w = wave_id(), r = l & 15, g = l >> 4;
   const int c_begin = seg * seg_chunks;
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
@@ -860,7 +865,8 @@ template <int D>
 __global__ __launch_bounds__(256) void scan_bwd_rev_fast(
     RowView<const float> vv, RowView<const float> vk, RowView<const float> vq, RowView<const float> vg,
     const float* __restrict__ lam, const float* __restrict__ eta, int H, int n_act, int seg_chunks,
-    int n_seg, const float* __restrict__ ws, RowView<float> vdk, RowView<float> vdv) {
+    int n_seg, const float* __restrict__ ws, const float* __restrict__ gate, RowView<float> vdk,
+    RowView<float> vdv) {
   using F = FastTiles<D>;
   constexpr int NT = D / 16;
   constexpr int ROWS = CH * F::S;
@@ -882,7 +888,7 @@ __global__ __launch_bounds__(256) void scan_bwd_rev_fast(
   float* const sQw = lds + 2 * COLS;
 
   const int seg = blockIdx.x, bh = blockIdx.z;
-  const float lm = lam[bh % H], et = eta[bh % H];
+  const float lm = lam[bh % H], et = eta[bh % H] * gate_factor(gate, bh % H);
   const int l = lane_id(), w = wave_id(), r = l & 15, g = l >> 4;
   const int c_begin = seg * seg_chunks;
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
@@ -968,10 +974,14 @@ __global__ __launch_bounds__(256) void scan_bwd_rev_fast(
   }
 }
 
-// Per head: deta and dlam from the shares of every sequence and segment.
+// Per head: deta, dlam (and dg) from the shares of every sequence and
+// segment.  With X = sum q'^T A G and Y = sum q'^T A' G (eta = 1, G the
+// cotangent passed in) and s = sigmoid(g) (1 without a gate):
+// deta = s X, dlam = s eta Y, dg = s (1 - s) eta X.
 __global__ void scan_bwd_reduce(const double* __restrict__ part_eta, const double* __restrict__ part_lam,
-                                const float* __restrict__ eta, int B, int H, int n_seg,
-                                float* __restrict__ dlam, float* __restrict__ deta) {
+                                const float* __restrict__ eta, const float* __restrict__ gate, int B, int H,
+                                int n_seg, float* __restrict__ dlam, float* __restrict__ deta,
+                                float* __restrict__ dgate) {
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= H) return;
   double a = 0.0, b = 0.0;
@@ -982,15 +992,17 @@ __global__ void scan_bwd_reduce(const double* __restrict__ part_eta, const doubl
       b += part_lam[bh * n_seg + i];
     }
   }
-  deta[h] = (float)a;
-  dlam[h] = (float)((double)eta[h] * b);
+  const double s = gate != nullptr ? 1.0 / (1.0 + exp(-(double)gate[h])) : 1.0;
+  deta[h] = (float)(s * a);
+  dlam[h] = (float)(s * (double)eta[h] * b);
+  if (dgate != nullptr) dgate[h] = (float)(s * (1.0 - s) * (double)eta[h] * a);
 }
 
 template <int D>
 hipError_t run_scan_backward(const float* q, const float* k, const float* v, const float* lam,
-                             const float* eta, int B, int H, int T, int W, const float* dm,
-                             float* dq, float* dk, float* dv, float* dlam, float* deta, char* ws,
-                             hipStream_t s) {
+                             const float* eta, const float* gate, int B, int H, int T, int W, const float* dm,
+                             float* dq, float* dk, float* dv, float* dlam, float* deta, float* dgate,
+                             char* ws, hipStream_t s) {
   const int BH = B * H;
   const ScanPlan p = plan_scan(B, H, T, D, D, W);
   const int n_act = p.n_act;
@@ -1000,6 +1012,8 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   if (n_act <= 0) {
     hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dlam, H, 0.f);
     hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, deta, H, 0.f);
+    if (dgate != nullptr)
+      hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dgate, H, 0.f);
     return hipGetLastError();
   }
   double* part_eta = reinterpret_cast<double*>(ws);
@@ -1019,8 +1033,8 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   }
   profile_mark_before(s);
   hipLaunchKernelGGL((scan_bwd_fwd_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, fq, fk, fv, fg, lam,
-                     eta, H, n_act, p.seg_chunks, p.n_seg, sws, dws, RowView<float>{dq + (long)W * D, bs, D},
-                     part_eta, part_lam);
+                     eta, H, n_act, p.seg_chunks, p.n_seg, sws, dws, gate,
+                     RowView<float>{dq + (long)W * D, bs, D}, part_eta, part_lam);
   profile_mark_after(s);
   // reverse direction: dk, dv (row r of each view is position n_act - 1 - r)
   const long last = (long)(n_act - 1) * D, tl = (long)(T - 1) * D;
@@ -1033,10 +1047,10 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
                        p.seg_chunks * CH, p.n_seg, sws);
   }
   hipLaunchKernelGGL((scan_bwd_rev_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, rv, rk, rq, rg, lam, eta,
-                     H, n_act, p.seg_chunks, p.n_seg, sws, RowView<float>{dk + last, bs, -D},
+                     H, n_act, p.seg_chunks, p.n_seg, sws, gate, RowView<float>{dk + last, bs, -D},
                      RowView<float>{dv + last, bs, -D});
-  hipLaunchKernelGGL(scan_bwd_reduce, dim3((H + 63) / 64), dim3(64), 0, s, part_eta, part_lam, eta, B, H,
-                     p.n_seg, dlam, deta);
+  hipLaunchKernelGGL(scan_bwd_reduce, dim3((H + 63) / 64), dim3(64), 0, s, part_eta, part_lam, eta, gate, B,
+                     H, p.n_seg, dlam, deta, dgate);
   return hipGetLastError();
 }
 
@@ -1156,14 +1170,14 @@ size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W) {
 }
 
 hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
-                                   const float* eta, int B, int H, int T, int d, int W,
+                                   const float* eta, const float* g, int B, int H, int T, int d, int W,
                                    const float* dm, float* dq, float* dk, float* dv, float* dlam,
-                                   float* deta, void* ws, hipStream_t s) {
+                                   float* deta, float* dg, void* ws, hipStream_t s) {
   char* w = static_cast<char*>(ws);
   switch (d) {
-    case 16: return run_scan_backward<16>(q, k, v, lam, eta, B, H, T, W, dm, dq, dk, dv, dlam, deta, w, s);
-    case 32: return run_scan_backward<32>(q, k, v, lam, eta, B, H, T, W, dm, dq, dk, dv, dlam, deta, w, s);
-    case 64: return run_scan_backward<64>(q, k, v, lam, eta, B, H, T, W, dm, dq, dk, dv, dlam, deta, w, s);
+    case 16: return run_scan_backward<16>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s);
+    case 32: return run_scan_backward<32>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s);
+    case 64: return run_scan_backward<64>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s);
     default: return hipErrorInvalidValue;
   }
 }

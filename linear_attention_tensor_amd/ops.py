@@ -128,13 +128,19 @@ def scan_backward_workspace(B, H, T, dk, dv, W, dtype_code) -> int:
 
 
 def tc_scan_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torch.Tensor,
-                     eta: torch.Tensor, W: int, dm: torch.Tensor, *, check_values: bool = True,
-                     ws: Optional[torch.Tensor] = None):
-    """Gradients (dq, dk, dv, dlam, deta) of sum <dm, m> through the L2 read m."""
+                     eta: torch.Tensor, W: int, dm: torch.Tensor, *, g: Optional[torch.Tensor] = None,
+                     check_values: bool = True, ws: Optional[torch.Tensor] = None):
+    """Gradients of sum <dm, m> through the L2 read m: (dq, dk, dv, dlam, deta).
+
+    With a per-head gate ``g`` [H], ``dm`` is the cotangent of sigmoid(g) m
+    (the gated branch of the fused layer) and dg [H] is returned last.
+    """
     B, H, T, dk, dv, dt = _qkv(q, k, v)
     _check_tensor("lam", lam, (H,), torch.float32, q.device)
     _check_tensor("eta", eta, (H,), torch.float32, q.device)
     _check_tensor("dm", dm, (B, H, T, dv), torch.float32, q.device)
+    if g is not None:
+        _check_tensor("g", g, (H,), torch.float32, q.device)
     if check_values:
         _check_unit_interval("lam", lam)
     gq = torch.empty((B, H, T, dk), dtype=torch.float32, device=q.device)
@@ -142,13 +148,16 @@ def tc_scan_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: tor
     gv = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
     glam = torch.empty((H,), dtype=torch.float32, device=q.device)
     geta = torch.empty((H,), dtype=torch.float32, device=q.device)
+    gg = torch.empty((H,), dtype=torch.float32, device=q.device) if g is not None else None
     need = scan_backward_workspace(B, H, T, dk, dv, W, dt)
     if ws is None:
         ws = _ws(need, q.device)
-    st = lib().tc_scan_backward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(lam), _ptr(eta), B, H, T, dk, dv, W,
-                                CHUNK, _ptr(dm), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(glam), _ptr(geta),
-                                _ptr(ws), ws.numel() if ws is not None else 0, _stream())
+    st = lib().tc_scan_backward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(lam), _ptr(eta), _ptr(g), B, H, T, dk,
+                                dv, W, CHUNK, _ptr(dm), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(glam), _ptr(geta),
+                                _ptr(gg), _ptr(ws), ws.numel() if ws is not None else 0, _stream())
     check("tc_scan_backward", st)
+    if g is not None:
+        return gq, gk, gv, glam, geta, gg
     return gq, gk, gv, glam, geta
 
 

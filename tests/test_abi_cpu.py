@@ -175,10 +175,10 @@ def test_scan_backward_rejects():
 
     def call(**kw):
         a = dict(dt=_lib.TC_F32, B=4, H=8, T=4096, d=64, W=512, chunk=64, dm=FAKE, dlam=FAKE, ws=FAKE,
-                 ws_bytes=need)
+                 ws_bytes=need, g=NULL, dg=NULL)
         a.update(kw)
-        return f(FAKE, FAKE, FAKE, a["dt"], FAKE, FAKE, a["B"], a["H"], a["T"], a["d"], a["d"], a["W"],
-                 a["chunk"], a["dm"], FAKE, FAKE, FAKE, a["dlam"], FAKE, a["ws"], a["ws_bytes"], NULL)
+        return f(FAKE, FAKE, FAKE, a["dt"], FAKE, FAKE, a["g"], a["B"], a["H"], a["T"], a["d"], a["d"], a["W"],
+                 a["chunk"], a["dm"], FAKE, FAKE, FAKE, a["dlam"], FAKE, a["dg"], a["ws"], a["ws_bytes"], NULL)
 
     assert call(dt=_lib.TC_BF16) == _lib.TC_ERR_UNSUPPORTED
     assert call(d=128) == _lib.TC_ERR_UNSUPPORTED
@@ -188,5 +188,7 @@ def test_scan_backward_rejects():
     assert call(dlam=NULL) == _lib.TC_ERR_INVALID_ARG
     assert call(ws_bytes=need - 1) == _lib.TC_ERR_WORKSPACE
     assert call(ws=NULL) == _lib.TC_ERR_INVALID_ARG
+    assert call(g=FAKE) == _lib.TC_ERR_INVALID_ARG  # a gate without dg
+    assert call(dg=FAKE) == _lib.TC_ERR_INVALID_ARG
     assert call(B=0) == _lib.TC_OK
     assert lib().tc_scan_backward_workspace_bytes(1, 1, 10, 128, 128, 4, 64, _lib.TC_F32) == _lib.SIZE_MAX

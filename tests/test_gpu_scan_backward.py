@@ -92,3 +92,18 @@ def test_scan_backward_prefill_full_size_sampled_heads():
                                  w.W, dm[:, sl].astype(np.float64))
         for name, a, b in zip(("dq", "dk", "dv", "dlam", "deta"), got, ref):
             assert report(f"head {h} {name}", a[:, sl] if a.ndim == 4 else a[sl], b) <= TOL, name
+
+
+@pytest.mark.parametrize("B,H,T,d,W", [(2, 3, 300, 32, 17), (1, 2, 1000, 64, 100), (1, 1, 20, 16, 45)])
+def test_scan_backward_through_the_gate(B, H, T, d, W):
+    print(f"[case] gated scan backward B={B} H={H} T={T} d={d} W={W}", flush=True)
+    x = I.draw(B, H, T, d, seed=4500 + T, dtype="f32")
+    dy = I.draw_cotangent(B, H, T, d, seed=4500 + T)
+    g = np.linspace(-2.0, 1.5, H).astype(np.float32)
+    out = ops.tc_scan_backward(to_dev(x["q"], "f32"), to_dev(x["k"], "f32"), to_dev(x["v"], "f32"),
+                               f32_dev(x["lam"]), f32_dev(x["eta"]), W, f32_dev(dy), g=f32_dev(g))
+    torch.cuda.synchronize()
+    ref = O.tc_gated_read_backward(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64),
+                                   x["eta"].astype(np.float64), g.astype(np.float64), W, dy.astype(np.float64))
+    for name, a, b in zip(("dq", "dk", "dv", "dlam", "deta", "dg"), out, ref):
+        assert report(f"gated {name}", a.cpu().numpy(), b) <= TOL, name
