@@ -14,7 +14,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["delta_scan", "additive_scan", "delta_scan_chunked", "reconstruction_loss"]
+__all__ = ["delta_scan", "additive_scan", "delta_scan_chunked", "reconstruction_loss", "delta_scan_backward"]
 
 
 def _f64(x):
@@ -95,3 +95,48 @@ def delta_scan_chunked(q, k, v, beta, C=64, S0=None):
         o[:, :, t0 : t0 + L, :] = np.einsum("bhrd,bhed->bhre", Q, S) + QK @ U
         S = S + np.einsum("bhre,bhrd->bhed", U, K)
     return o, S
+
+
+def delta_scan_backward(q, k, v, beta, do, S0=None, dS_final=None):
+    """Gradients of L = sum_t <do_t, o_t> + <dS_final, S_T> through ``delta_scan``.
+
+    DeltaNet section of the page (beta is the learned write strength of every
+    token).  Reverse mode through the per-token rule, with the states S_t of
+    the forward pass kept: going backwards, dS (the adjoint of S_t) gathers
+    do_t q_t^T and gives dq_t = S_t^T do_t; the write S_t = S_{t-1} + e_t k_t^T
+    with e_t = beta_t (v_t - S_{t-1} k_t) sends de_t = dS k_t to
+    dv_t = beta_t de_t and dbeta_t = <de_t, v_t - S_{t-1} k_t>, gives
+    dk_t = dS^T e_t - beta_t S_{t-1}^T de_t, and leaves
+    dS <- dS - beta_t de_t k_t^T for S_{t-1}.
+
+    Returns (dq [B,H,T,dk], dk [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T],
+    dS0 [B,H,dv,dk]).
+    """
+    q, k, v, beta, do = _f64(q), _f64(k), _f64(v), _f64(beta), _f64(do)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dv, dk)) if S0 is None else _f64(S0).copy()
+    states = [S.copy()]  # states[t] = S_{t-1}, the state before step t
+    for t in range(T):
+        e = beta[:, :, t, None] * (v[:, :, t] - np.einsum("bhij,bhj->bhi", S, k[:, :, t]))
+        S = S + e[..., :, None] * k[:, :, t, None, :]
+        states.append(S.copy())
+    gq = np.zeros_like(q)
+    gk = np.zeros_like(k)
+    gv = np.zeros_like(v)
+    gb = np.zeros_like(beta)
+    dS = np.zeros((B, H, dv, dk)) if dS_final is None else _f64(dS_final).copy()
+    for t in range(T - 1, -1, -1):
+        S_t, S_prev = states[t + 1], states[t]
+        dS = dS + do[:, :, t, :, None] * q[:, :, t, None, :]
+        gq[:, :, t] = np.einsum("bhij,bhi->bhj", S_t, do[:, :, t])
+        resid = v[:, :, t] - np.einsum("bhij,bhj->bhi", S_prev, k[:, :, t])
+        e = beta[:, :, t, None] * resid
+        de = np.einsum("bhij,bhj->bhi", dS, k[:, :, t])
+        gv[:, :, t] = beta[:, :, t, None] * de
+        gb[:, :, t] = np.einsum("bhi,bhi->bh", de, resid)
+        gk[:, :, t] = (np.einsum("bhij,bhi->bhj", dS, e)
+                       - beta[:, :, t, None] * np.einsum("bhij,bhi->bhj", S_prev, de))
+        dS = dS - beta[:, :, t, None, None] * de[..., :, None] * k[:, :, t, None, :]
+    return gq, gk, gv, gb, dS
+

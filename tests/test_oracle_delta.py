@@ -180,3 +180,138 @@ def test_hand_example_catches_planted_mistakes(mutant):
     q, k, v = (np.array(i[n], float)[None, None] for n in ("q", "k", "v"))
     o, _ = mutant(q, k, v, np.array(i["beta"], float)[None, None])
     assert np.max(np.abs(o[0, 0] - np.array(g["o"]))) > 1e-6
+
+
+# ---------------------------------------------------------------- backward
+
+def _delta_loss(q, k, v, beta, do, S0=None, dSf=None):
+    o, S = D.delta_scan(q, k, v, beta, S0)
+    out = float(np.sum(o * do))
+    if dSf is not None:
+        out += float(np.sum(S * dSf))
+    return out
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_delta_backward_matches_central_differences(with_state):
+    q, k, v, beta = rand_inputs(70, B=1, H=2, T=9, dk=3, dv=4)
+    rng = np.random.default_rng(71)
+    do = rng.standard_normal(v.shape)
+    S0 = rng.standard_normal((1, 2, 4, 3)) if with_state else None
+    dSf = rng.standard_normal((1, 2, 4, 3)) if with_state else None
+    gq, gk, gv, gb, gS0 = D.delta_scan_backward(q, k, v, beta, do, S0, dSf)
+    h = 1e-6
+    args = {"q": q, "k": k, "v": v, "beta": beta}
+    grads = {"q": gq, "k": gk, "v": gv, "beta": gb}
+    for name, x in args.items():
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            a = dict(args)
+            a[name] = x.copy()
+            a[name][i] += h
+            lp = _delta_loss(a["q"], a["k"], a["v"], a["beta"], do, S0, dSf)
+            a[name][i] -= 2 * h
+            lm = _delta_loss(a["q"], a["k"], a["v"], a["beta"], do, S0, dSf)
+            fd[i] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grads[name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+    if with_state:
+        fd = np.zeros_like(S0)
+        it = np.nditer(S0, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            sp, sm = S0.copy(), S0.copy()
+            sp[i] += h
+            sm[i] -= h
+            fd[i] = (_delta_loss(q, k, v, beta, do, sp, dSf) - _delta_loss(q, k, v, beta, do, sm, dSf)) / (2 * h)
+        np.testing.assert_allclose(gS0, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_delta_backward_matches_autograd_of_the_per_token_rule():
+    torch = pytest.importorskip("torch")
+    q, k, v, beta = rand_inputs(72, B=2, H=1, T=20, dk=4, dv=3)
+    do = np.random.default_rng(73).standard_normal(v.shape)
+    gq, gk, gv, gb, _ = D.delta_scan_backward(q, k, v, beta, do)
+    tq, tk, tv, tb = (torch.tensor(a, requires_grad=True) for a in (q, k, v, beta))
+    # the rule written as S_t = S_{t-1} (I - beta k k^T) + beta v k^T
+    S = torch.zeros(2, 1, 3, 4, dtype=torch.float64)
+    outs = []
+    eye = torch.eye(4, dtype=torch.float64)
+    for t in range(20):
+        kt, bt = tk[:, :, t], tb[:, :, t, None, None]
+        S = S @ (eye - bt * kt[..., :, None] * kt[..., None, :]) + bt * tv[:, :, t, :, None] * kt[..., None, :]
+        outs.append(S @ tq[:, :, t, :, None])
+    o = torch.cat(outs, dim=-1).transpose(-1, -2)
+    (o * torch.tensor(do)).sum().backward()
+    for a, b in ((gq, tq), (gk, tk), (gv, tv), (gb, tb)):
+        np.testing.assert_allclose(a, b.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_delta_backward_beta_zero_special_case():
+    # beta = 0: nothing is written, o_t = S0 q_t; dq = S0^T do, dk = dv = 0,
+    # dbeta_t = <(sum_{s>=t} do_s q_s^T) k_t, v_t - S0 k_t>
+    q, k, v, _ = rand_inputs(74, B=1, H=1, T=7, dk=3, dv=2)
+    rng = np.random.default_rng(75)
+    do = rng.standard_normal(v.shape)
+    S0 = rng.standard_normal((1, 1, 2, 3))
+    gq, gk, gv, gb, gS0 = D.delta_scan_backward(q, k, v, np.zeros((1, 1, 7)), do, S0)
+    np.testing.assert_allclose(gq[0, 0], do[0, 0] @ S0[0, 0], rtol=1e-13)
+    assert np.all(gk == 0) and np.all(gv == 0)
+    for t in range(7):
+        G = sum(np.outer(do[0, 0, s], q[0, 0, s]) for s in range(t, 7))
+        want = (G @ k[0, 0, t]) @ (v[0, 0, t] - S0[0, 0] @ k[0, 0, t])
+        assert abs(gb[0, 0, t] - want) < 1e-12
+    np.testing.assert_allclose(gS0[0, 0], sum(np.outer(do[0, 0, s], q[0, 0, s]) for s in range(7)), rtol=1e-13)
+
+
+def _delta_backward_mutant(q, k, v, beta, do, kind):
+    # the reverse sweep of the oracle with one planted mistake
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dv, dk))
+    states = [S.copy()]
+    for t in range(T):
+        e = beta[:, :, t, None] * (v[:, :, t] - np.einsum("bhij,bhj->bhi", S, k[:, :, t]))
+        S = S + e[..., :, None] * k[:, :, t, None, :]
+        states.append(S.copy())
+    gq, gk, gb = np.zeros_like(q), np.zeros_like(k), np.zeros_like(beta)
+    dS = np.zeros((B, H, dv, dk))
+    for t in range(T - 1, -1, -1):
+        S_t, S_prev = states[t + 1], states[t]
+        dS = dS + do[:, :, t, :, None] * q[:, :, t, None, :]
+        gq[:, :, t] = np.einsum("bhij,bhi->bhj", S_t, do[:, :, t])
+        resid = v[:, :, t] - np.einsum("bhij,bhj->bhi", S_prev, k[:, :, t])
+        e = beta[:, :, t, None] * resid
+        de = np.einsum("bhij,bhj->bhi", dS, k[:, :, t])
+        gb[:, :, t] = np.einsum("bhi,bhi->bh", de, resid) * (-1.0 if kind == "dbeta_sign" else 1.0)
+        gk[:, :, t] = np.einsum("bhij,bhi->bhj", dS, e)
+        if kind != "dk_missing_read_term":
+            gk[:, :, t] -= beta[:, :, t, None] * np.einsum("bhij,bhi->bhj", S_prev, de)
+        if kind != "dS_no_erase":
+            dS = dS - beta[:, :, t, None, None] * de[..., :, None] * k[:, :, t, None, :]
+    return gq, gk, gb
+
+
+@pytest.mark.parametrize("kind", ["dk_missing_read_term", "dbeta_sign", "dS_no_erase", "none"])
+def test_delta_backward_pins_catch_planted_mistakes(kind):
+    q, k, v, beta = rand_inputs(76, B=1, H=1, T=6, dk=2, dv=2)
+    do = np.random.default_rng(77).standard_normal(v.shape)
+    gq, gk, gb = _delta_backward_mutant(q, k, v, beta, do, kind)
+    h = 1e-6
+    worst = 0.0
+    for name, x, g in (("k", k, gk), ("beta", beta, gb)):
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a = {"k": k, "beta": beta}
+            a[name] = xp
+            lp = _delta_loss(q, a["k"], v, a["beta"], do)
+            a[name] = xm
+            lm = _delta_loss(q, a["k"], v, a["beta"], do)
+            worst = max(worst, abs(g[idx] - (lp - lm) / (2 * h)))
+    if kind == "none":
+        assert worst < 1e-7  # the unmutated sweep passes the same check
+    else:
+        assert worst > 1e-4
