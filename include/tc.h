@@ -187,6 +187,30 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
                              const float* S0, float* o, float* S_final,
                              void* ws, size_t ws_bytes, hipStream_t s);
 
+/* ---------------------------------------------------------------------------
+ * Backward of the delta-rule scan (DeltaNet-family linear attention
+ * variants, DeltaNet: beta_t is the learned write strength of each token).
+ * Gradients of L = sum_t <do_t, o_t> + <dS_final, S_final> for the outputs
+ * of delta_scan_forward with the same q, k, v, beta, S0.
+ *   do       [B, H, T, dv] float32.
+ *   dS_final [B, H, dv, dk] float32 or NULL (no gradient on S_final).
+ *   dq, dk   out [B, H, T, dk] float32; dv out [B, H, T, dv] float32.
+ *   dbeta    out [B, H, T] float32.
+ *   dS0      out [B, H, dv, dk] float32 (the gradient on S0, zeros taken as
+ *            S0 when it is NULL) or NULL.
+ *   ws       at least delta_scan_backward_workspace_bytes(...) bytes; it holds
+ *            every chunk's (I + diag(beta) tril(K K^T))^-1, entering state and
+ *            exit adjoint (B*H*ceil(T/64)*(64*64 + 2*d*d) floats).
+ * Supported: dt = TC_F32, dk == dv in {16, 32, 64}, chunk = 64; anything
+ * else is TC_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------- */
+size_t delta_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt);
+tc_status delta_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt,
+                              const float* beta, int B, int H, int T, int dk, int dv, int chunk,
+                              const float* S0, const float* d_o, const float* dS_final,
+                              float* dq, float* dk_out, float* dv_out, float* dbeta, float* dS0,
+                              void* ws, size_t ws_bytes, hipStream_t s);
+
 /* Workspace queries return SIZE_MAX when the arguments are invalid or
  * unsupported (tc_last_error() says why). */
 
@@ -198,6 +222,7 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
  *   tc_fused_layer      the window-attention + L2-read kernel,
  *   tc_scan_forward     the output kernel,
  *   tc_scan_backward    its forward-direction kernel (dq, deta, dlam),
+ *   delta_scan_backward its chunk-parallel gradient kernel,
  *   tc_decode_step      its only kernel,
  *   tc_decode_layer_step its only kernel,
  *   delta_scan_forward  the kernel that walks the chunks.

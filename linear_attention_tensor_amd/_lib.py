@@ -42,6 +42,9 @@ SIGNATURES = {
     "tc_fused_layer": (_i, [_p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _z, _p]),
     "delta_scan_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i]),
     "delta_scan_forward": (_i, [_p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _z, _p]),
+    "delta_scan_backward_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i]),
+    "delta_scan_backward": (_i, [_p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                 _z, _p]),
     "tc_profile_next_call": (_i, [_p, _p]),
     "tc_last_error": (ctypes.c_char_p, []),
     "tc_version": (ctypes.c_char_p, []),

@@ -284,4 +284,43 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
   });
 }
 
+static tc_status check_delta_bwd(const char* fn, int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt) {
+  tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
+  if (st != TC_OK) return st;
+  if (dt != TC_F32 || dk > 64)
+    return fail(TC_ERR_UNSUPPORTED, "%s: the backward takes float32 inputs with d in {16, 32, 64}", fn);
+  return TC_OK;
+}
+
+size_t delta_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt) {
+  if (check_delta_bwd("delta_scan_backward_workspace_bytes", B, H, T, dk, dv, chunk, dt) != TC_OK)
+    return SIZE_MAX;
+  ok();
+  return tc::delta_bwd_ws_bytes(B, H, T, dk);
+}
+
+tc_status delta_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt, const float* beta,
+                              int B, int H, int T, int dk, int dv, int chunk, const float* S0,
+                              const float* d_o, const float* dS_final, float* dq, float* dk_out,
+                              float* dv_out, float* dbeta, float* dS0, void* ws, size_t ws_bytes,
+                              hipStream_t s) {
+  return guarded("delta_scan_backward", [&]() -> tc_status {
+    const char* fn = "delta_scan_backward";
+    tc_status st = check_delta_bwd(fn, B, H, T, dk, dv, chunk, dt);
+    if (st != TC_OK) return st;
+    if (B == 0 || H == 0) return ok();
+    if (T > 0 && (!q || !k || !v || !beta || !d_o || !dq || !dk_out || !dv_out || !dbeta))
+      return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, beta, do, dq, dk, dv, dbeta must not be NULL", fn);
+    const size_t need = tc::delta_bwd_ws_bytes(B, H, T, dk);
+    if (ws_bytes < need)
+      return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
+    if (T == 0 && !dS0) return ok();
+    return from_hip(tc::launch_delta_backward(static_cast<const float*>(q), static_cast<const float*>(k),
+                                              static_cast<const float*>(v), beta, B, H, T, dk, S0, d_o,
+                                              dS_final, dq, dk_out, dv_out, dbeta, dS0, ws, s),
+                    fn);
+  });
+}
+
 }  // extern "C"

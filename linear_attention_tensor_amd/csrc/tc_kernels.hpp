@@ -65,6 +65,11 @@ hipError_t launch_delta_scan(const void* q, const void* k, const void* v, bool b
 // bf16 inputs with d in {64, 128} (delta_bf16.hip): bf16 MFMA with split
 // operands; launch_delta_scan dispatches to it.
 bool delta_bf16_supported(bool bf16, int d);
+// Backward of the delta-rule scan (delta_bwd.hip): fp32 inputs, d in {16, 32, 64}.
+size_t delta_bwd_ws_bytes(int B, int H, int T, int d);
+hipError_t launch_delta_backward(const float* q, const float* k, const float* v, const float* beta, int B, int H,
+                                 int T, int d, const float* S0, const float* dO, const float* dSf, float* dq,
+                                 float* dk, float* dv, float* dbeta, float* dS0, void* ws, hipStream_t s);
 size_t delta_bf16_ws_bytes(int B, int H, int T, int d);
 hipError_t launch_delta_bf16(const void* q, const void* k, const void* v, const float* beta, int B,
                              int H, int T, int d, const float* S0, float* o, float* S_final, void* ws,

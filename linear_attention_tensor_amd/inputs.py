@@ -67,6 +67,9 @@ WORKLOADS = {
                             ("uniform", 0.95, 0.999), ("uniform", 0.1, 1.0), steps=4096),
     "delta_scan_bf16": Workload("delta_scan_bf16", 2, 16, 16384, 128, 0, "bf16", 105,
                                 ("fixed", 1.0), ("fixed", 1.0)),
+    # the delta scan's backward: same B, H, T; float32 inputs with d = 64
+    "delta_backward_f32": Workload("delta_backward_f32", 2, 16, 16384, 64, 0, "f32", 106,
+                                   ("fixed", 1.0), ("fixed", 1.0)),
 }
 
 

@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import TC_BF16, TC_F32, check, lib
 
 __all__ = ["tc_scan_forward", "tc_scan_backward", "tc_decode_step", "tc_decode_layer_step",
-           "tc_fused_layer", "delta_scan_forward", "scan_backward_workspace",
+           "tc_fused_layer", "delta_scan_forward", "delta_scan_backward", "scan_backward_workspace",
            "scan_workspace", "fused_workspace", "delta_workspace"]
 
 CHUNK = 64
@@ -281,3 +281,35 @@ def delta_scan_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: 
                                   _stream())
     check("delta_scan_forward", st)
     return (o, S) if return_state else o
+
+
+def delta_scan_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor,
+                        do: torch.Tensor, *, S0: Optional[torch.Tensor] = None,
+                        dS_final: Optional[torch.Tensor] = None, return_dS0: bool = False,
+                        check_values: bool = True, ws: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv, dbeta[, dS0]) of sum <do, o> (+ <dS_final, S_final>)
+    through delta_scan_forward; float32 inputs, d in {16, 32, 64}."""
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    _check_tensor("beta", beta, (B, H, T), torch.float32, q.device)
+    _check_tensor("do", do, (B, H, T, dv), torch.float32, q.device)
+    for name, t in (("S0", S0), ("dS_final", dS_final)):
+        if t is not None:
+            _check_tensor(name, t, (B, H, dv, dk), torch.float32, q.device)
+    if check_values:
+        _check_unit_interval("beta", beta)
+    gq = torch.empty((B, H, T, dk), dtype=torch.float32, device=q.device)
+    gk = torch.empty((B, H, T, dk), dtype=torch.float32, device=q.device)
+    gv = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    gb = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    gS0 = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device) if return_dS0 else None
+    n = lib().delta_scan_backward_workspace_bytes(B, H, T, dk, dv, CHUNK, dt)
+    if n == _lib.SIZE_MAX:
+        raise _lib.TCError("delta_scan_backward_workspace_bytes", _lib.TC_ERR_UNSUPPORTED, _lib.last_error())
+    if ws is None:
+        ws = _ws(n, q.device)
+    st = lib().delta_scan_backward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(beta), B, H, T, dk, dv, CHUNK, _ptr(S0),
+                                   _ptr(do), _ptr(dS_final), _ptr(gq), _ptr(gk), _ptr(gv), _ptr(gb), _ptr(gS0),
+                                   _ptr(ws), ws.numel() if ws is not None else 0, _stream())
+    check("delta_scan_backward", st)
+    return (gq, gk, gv, gb, gS0) if return_dS0 else (gq, gk, gv, gb)
+

@@ -1,0 +1,98 @@
+"""Parity of delta_scan_backward (C ABI, HIP kernels) against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_tensor_amd import inputs as I
+from linear_attention_tensor_amd import ops
+from oracle import delta as D
+from tests._helpers import f32_dev, report, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+NAMES = ("dq", "dk", "dv", "dbeta", "dS0")
+
+
+def run(x, do, S0=None, dSf=None):
+    g = ops.delta_scan_backward(to_dev(x["q"], "f32"), to_dev(x["k"], "f32"), to_dev(x["v"], "f32"),
+                                f32_dev(x["beta"]), f32_dev(do), S0=None if S0 is None else f32_dev(S0),
+                                dS_final=None if dSf is None else f32_dev(dSf), return_dS0=True)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in g]
+
+
+def ref(x, do, S0=None, dSf=None):
+    f = (lambda a: None if a is None else np.asarray(a, np.float64))
+    return D.delta_scan_backward(x["q64"], x["k64"], x["v64"], x["beta"].astype(np.float64),
+                                 do.astype(np.float64), f(S0), f(dSf))
+
+
+@pytest.mark.parametrize("B,H,T,d,states", [
+    (1, 1, 64, 16, False),     # one full chunk
+    (1, 2, 200, 64, False),    # ragged tail
+    (2, 1, 130, 32, True),     # initial state and final-state cotangent
+    (1, 1, 1, 16, True),       # one token
+    (1, 2, 37, 64, True),      # shorter than a chunk
+    (2, 2, 513, 64, False),    # many chunks
+    (1, 3, 300, 16, True),
+])
+def test_delta_backward_small(B, H, T, d, states):
+    print(f"[case] delta backward B={B} H={H} T={T} d={d} states={states}", flush=True)
+    x = I.draw(B, H, T, d, seed=6000 + T + d, dtype="f32")
+    do = I.draw_cotangent(B, H, T, d, seed=6000 + T + d)
+    rng = np.random.default_rng(T + d)
+    S0 = (rng.standard_normal((B, H, d, d)) * 0.2).astype(np.float32) if states else None
+    dSf = (rng.standard_normal((B, H, d, d)) * 0.2).astype(np.float32) if states else None
+    got = run(x, do, S0, dSf)
+    want = ref(x, do, S0, dSf)
+    for name, a, b in zip(NAMES, got, want):
+        assert report(name, a, b) <= TOL, name
+
+
+@pytest.mark.parametrize("beta_val", [0.0, 1.0])
+def test_delta_backward_beta_edges(beta_val):
+    print(f"[case] delta backward beta={beta_val}", flush=True)
+    x = I.draw(1, 2, 150, 32, seed=81, dtype="f32")
+    x["beta"] = np.full_like(x["beta"], beta_val)
+    do = I.draw_cotangent(1, 2, 150, 32, seed=81)
+    S0 = (np.random.default_rng(82).standard_normal((1, 2, 32, 32)) * 0.2).astype(np.float32)
+    got = run(x, do, S0)
+    want = ref(x, do, S0)
+    for name, a, b in zip(NAMES, got, want):
+        assert report(f"beta={beta_val} {name}", a, b) <= TOL, name
+
+
+def test_delta_backward_empty_sequence():
+    x = I.draw(1, 2, 1, 16, seed=5, dtype="f32")
+    q = to_dev(x["q"], "f32")[:, :, :0].contiguous()
+    dSf = torch.randn(1, 2, 16, 16, device="cuda")
+    g = ops.delta_scan_backward(q, q.clone(), q.clone(), torch.zeros(1, 2, 0, device="cuda"), q.clone(),
+                                dS_final=dSf, return_dS0=True)
+    torch.cuda.synchronize()
+    assert g[0].shape == (1, 2, 0, 16)
+    assert torch.equal(g[4], dSf)
+
+
+def test_delta_backward_repeat_is_deterministic():
+    x = I.draw(1, 2, 700, 64, seed=9, dtype="f32")
+    do = I.draw_cotangent(1, 2, 700, 64, seed=9)
+    a = run(x, do)
+    b = run(x, do)
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+
+
+def test_delta_backward_full_size_sampled_heads():
+    # B=2 H=16 T=16384 d=64: the oracle on two whole heads (every b, t)
+    w = I.WORKLOADS["delta_backward_f32"]
+    print("[case] delta backward full size", flush=True)
+    x = I.draw_workload("delta_backward_f32")
+    do = I.draw_cotangent(w.B, w.H, w.T, w.d, seed=w.seed)
+    got = run(x, do)
+    for b, h in ((0, 0), (1, 11)):
+        xs = {n: x[n][b:b + 1, h:h + 1] for n in ("q64", "k64", "v64", "beta")}
+        want = D.delta_scan_backward(xs["q64"], xs["k64"], xs["v64"], xs["beta"].astype(np.float64),
+                                     do[b:b + 1, h:h + 1].astype(np.float64))
+        for name, a, r in zip(NAMES, got, want):
+            assert report(f"b={b} h={h} {name}", a[b:b + 1, h:h + 1], r) <= TOL, name
