@@ -39,7 +39,8 @@ def parse():
                     help="untimed calls first: the GPU needs some tens of ms of load to reach its steady clock")
     ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fused", "scan", "scan_backward", "decode", "decode_layer", "delta"], default=None,
+    ap.add_argument("--only", choices=["fused", "scan", "scan_backward", "decode", "decode_layer", "delta",
+                                           "delta_backward"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy twice (the reference for "
@@ -108,6 +109,17 @@ def delta_bytes(B, H, T, d, in_bytes=2):
 
 def delta_flops(B, H, T, d):
     return B * H * T * 6 * d * d  # prediction, write, read per token
+
+
+def delta_backward_bytes(B, H, T, d):
+    # read q, k, v, do, beta and write dq, dk, dv, dbeta once, fp32
+    return B * H * T * (7 * d * 4 + 8)
+
+
+def delta_backward_flops(B, H, T, d):
+    # the reverse of the per-token rule: per token the forward's prediction,
+    # write and read (6 d^2) and their adjoints (12 d^2)
+    return B * H * T * 18 * d * d
 
 
 # ----------------------------------------------------------------------------- timing
@@ -475,6 +487,42 @@ def bench_delta(steps, warmup, dev):
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "bf16"}}
 
 
+def bench_delta_backward(steps, warmup, dev):
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["delta_backward_f32"]
+    x = I.draw_workload(w.name)
+    q, k, v = (to_dev_f32(x[n], dev) for n in ("q", "k", "v"))
+    beta = to_dev_f32(x["beta"], dev)
+    do = to_dev_f32(I.draw_cotangent(w.B, w.H, w.T, w.d, seed=w.seed), dev)
+    shape = (w.B, w.H, w.T, w.d)
+    gq, gk, gv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
+    gb = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+    lib = ops.lib()
+    nb = lib.delta_scan_backward_workspace_bytes(w.B, w.H, w.T, w.d, w.d, 64, 0)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, ops._ptr(beta), w.B, w.H, w.T, w.d, w.d, 64, None,
+            ops._ptr(do), None, ops._ptr(gq), ops._ptr(gk), ops._ptr(gv), ops._ptr(gb), None, ops._ptr(ws),
+            ws.numel(), ops._stream())
+
+    def call(_):
+        if lib.delta_scan_backward(*args) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, kernel_ms = time_calls(call, steps, warmup, KernelTimer(steps))
+    gbs = delta_backward_bytes(w.B, w.H, w.T, w.d) / (ms_call * 1e-3) / 1e9
+    tf = delta_backward_flops(w.B, w.H, w.T, w.d) / (ms_call * 1e-3) / 1e12
+    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
+            "mfma": roofline("mfma", tf, PEAK_FP32_TFLOPS, "TFLOP/s"),
+            "main_kernel": {"name": "delta_bwd_grads<64>", "ms": kernel_ms}, "ms_per_call": ms_call,
+            "workspace_bytes": nb,
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "f32"}}
+
+
 def cpu_baseline_fused(x, T_sample=16384):
     """The float64 oracle (as it stands) on a bounded prefix of the same
     input, with its BLAS pinned to one thread."""
@@ -526,6 +574,7 @@ def main():
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
         components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
+        components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
     elif only == "scan":
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
     elif only == "scan_backward":
@@ -536,6 +585,8 @@ def main():
         components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
     elif only == "delta":
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
+    elif only == "delta_backward":
+        components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
     if only not in (None, "fused"):
         print(json.dumps({"only": only, "components": components}))
         return

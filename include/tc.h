@@ -199,8 +199,9 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
  *   dS0      out [B, H, dv, dk] float32 (the gradient on S0, zeros taken as
  *            S0 when it is NULL) or NULL.
  *   ws       at least delta_scan_backward_workspace_bytes(...) bytes; it holds
- *            every chunk's (I + diag(beta) tril(K K^T))^-1, entering state and
- *            exit adjoint (B*H*ceil(T/64)*(64*64 + 2*d*d) floats).
+ *            four state-independent products of every chunk, its entering
+ *            state and its exit adjoint (B*H*ceil(T/64)*(2*64*64 + 2*64*d
+ *            + 2*d*d) floats).
  * Supported: dt = TC_F32, dk == dv in {16, 32, 64}, chunk = 64; anything
  * else is TC_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------- */

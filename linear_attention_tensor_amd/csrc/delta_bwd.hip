@@ -18,12 +18,14 @@
 //   dQ  = dO S0 + P1 K,
 //   dK  = -dX S0 + U dS1 + P1^T Q + (dLk + dLk^T) K,
 //   dbeta_r = <dY_r, X_r> - sum_{c<r} P2[r][c] <k_r, k_c>.
-// Four launches:
-//   1. delta_bwd_prep   (chunks in parallel): W of every chunk;
+// Three launches:
+//   1. delta_bwd_prep   (chunks in parallel): W of every chunk and the
+//      state-independent products the walks use (below);
 //   2. delta_bwd_fwd    (per b, h and 16-row slice of S, chunks in order):
 //      the entering state S0 of every chunk;
 //   3. delta_bwd_rev    (per b, h and 16-row slice of dS, chunks in reverse):
-//      the exit adjoint dS1 of every chunk, and dS0 of the sequence;
+//      the exit adjoint dS1 of every chunk, and dS0 of the sequence
+//      (2 and 3 are one launch, delta_bwd_walks);
 //   4. delta_bwd_grads  (chunks in parallel): dq, dk, dv, dbeta.
 // The rows of S (and of dS) are independent in 2 and 3: row j of S only sees
 // column j of V and U, row j of dS only column j of dO and dU.
@@ -71,6 +73,29 @@ __device__ __forceinline__ void stage(float* dst, int dst_ld, const float* src, 
   }
 }
 
+// The same rows held in registers (float4 pieces i * 256 + thread), so that
+// the next chunk's loads are in flight while the current one is computed.
+template <int NC>
+struct Rows {
+  static constexpr int N = (CH * NC / 4 + 255) / 256;
+  float4 x[N];
+  __device__ __forceinline__ void load(const float* src, long ld, int col0, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = i * 256 + threadIdx.x, r = idx / (NC / 4), c = (idx % (NC / 4)) * 4;
+      x[i] = r < nvalid ? *reinterpret_cast<const float4*>(src + (long)r * ld + col0 + c)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void put(float* dst, int dst_ld) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = i * 256 + threadIdx.x, r = idx / (NC / 4), c = (idx % (NC / 4)) * 4;
+      *reinterpret_cast<float4*>(dst + r * dst_ld + c) = x[i];
+    }
+  }
+};
+
 // one [R][D] block (row stride D in global) <-> LDS (stride S)
 template <int R, int D>
 __device__ __forceinline__ void load_block(float* dst, const float* src) {
@@ -87,92 +112,136 @@ __device__ __forceinline__ void store_block(float* dst, const float* src) {
   }
 }
 
-// 1. W = (I + diag(beta) tril_-1(K K^T))^-1 of one chunk: one wave; lane c
-//    solves column c by forward substitution.  Rows past the sequence end
-//    have beta = 0, so their rows and columns of W are those of I.
+// Per chunk, the prep kernel leaves [Tm | E2 | G2 | E1] (floats):
+//   Tm = W diag(beta) [64][64],  E2 = W^T tril_0(Q K^T)^T [64][64],
+//   G2 = Tm K [64][D],           E1 = W^T K [64][D],
+// so that the state walks need two products per chunk:
+//   U  = Tm V - G2 S0^T                       (forward walk, then S1 = S0 + U^T K),
+//   dY = E1 dS1^T + E2 dO,  dX = diag(beta) dY  (reverse walk, then dS0).
 template <int D>
-__global__ __launch_bounds__(64) void delta_bwd_prep(const float* __restrict__ k, const float* __restrict__ beta,
-                                                     int T, int n_chunks, float* __restrict__ Wout) {
-  constexpr int S = DB<D>::S;
+struct Pre {
+  static constexpr long TM = 0, E2 = CH * CH, G2 = 2 * CH * CH, E1 = 2 * CH * CH + CH * D;
+  static constexpr long SIZE = 2 * CH * CH + 2 * CH * D;
+};
+
+// 1. Per chunk (in parallel): W = (I + diag(beta) tril_-1(K K^T))^-1 by forward
+//    substitution (wave 0, lane c solves column c), then Tm, E2, G2, E1.  Rows
+//    past the sequence end have beta = 0, so their rows and columns of W are
+//    those of I and their rows of Tm, G2 are zero.
+template <int D>
+__global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ q, const float* __restrict__ k,
+                                                      const float* __restrict__ beta, int T, int n_chunks,
+                                                      float* __restrict__ pre) {
+  constexpr int S = DB<D>::S, NT = D / 16;
+  using P = Pre<D>;
+  __shared__ __attribute__((aligned(16))) float sQ[CH * S];
   __shared__ __attribute__((aligned(16))) float sK[CH * S];
-  __shared__ __attribute__((aligned(16))) float sM[CH * SW];
+  __shared__ __attribute__((aligned(16))) float sM[CH * SW];  // beta_r <k_r, k_c> (c < r), then W
+  __shared__ __attribute__((aligned(16))) float sA[CH * SW];  // tril_0(Q K^T)
   __shared__ float sB[CH];
-  const int c = blockIdx.x, bh = blockIdx.y, l = threadIdx.x;
+  const int c = blockIdx.x, bh = blockIdx.y;
   const int t0 = c * CH, L = min(CH, T - t0);
+  const int w = wave_id(), l = lane_id(), col = l & 15, rq = (l >> 4) * 4;
+  stage<D>(sQ, S, q + ((long)bh * T + t0) * D, D, 0, L);
   stage<D>(sK, S, k + ((long)bh * T + t0) * D, D, 0, L);
-  sB[l] = l < L ? beta[(long)bh * T + t0 + l] : 0.f;
+  if (threadIdx.x < CH) sB[threadIdx.x] = (int)threadIdx.x < L ? beta[(long)bh * T + t0 + threadIdx.x] : 0.f;
   __syncthreads();
-  const int col = l & 15, rq = (l >> 4) * 4;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int ct = 0; ct < 4; ++ct) {
+    floatx4 kk = wave_mma_f32<D>(sK + 16 * w * S, S, 1, sK + 16 * ct * S, 1, S, zero4());
+    floatx4 qk = wave_mma_f32<D>(sQ + 16 * w * S, S, 1, sK + 16 * ct * S, 1, S, zero4());
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      floatx4 kk = wave_mma_f32<D>(sK + 16 * rt * S, S, 1, sK + 16 * ct * S, 1, S, zero4());
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + rq + i, cc = 16 * ct + col;
-        sM[r * SW + cc] = cc < r ? sB[r] * kk[i] : 0.f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + rq + i, cc = 16 * ct + col;
+      sM[r * SW + cc] = cc < r ? sB[r] * kk[i] : 0.f;
+      sA[r * SW + cc] = cc <= r ? qk[i] : 0.f;
     }
-  __syncthreads();
-  float w[CH];
-#pragma unroll
-  for (int r = 0; r < CH; ++r) {
-    float acc = r == l ? 1.f : 0.f;
-#pragma unroll
-    for (int i = 0; i < r; ++i) acc -= sM[r * SW + i] * w[i];
-    w[r] = acc;
   }
-  float* dst = Wout + ((long)bh * n_chunks + c) * CH * CH + l;
+  __syncthreads();
+  if (w == 0) {
+    float x[CH];
 #pragma unroll
-  for (int r = 0; r < CH; ++r) dst[r * CH] = w[r];
+    for (int r = 0; r < CH; ++r) {
+      float acc = r == l ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) acc -= sM[r * SW + i] * x[i];
+      x[r] = acc;
+    }
+    // one wave: its LDS operations run in issue order; this only stops the
+    // compiler from moving the stores of W above the reads of sM
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < CH; ++r) sM[r * SW + l] = x[r];
+  }
+  __syncthreads();
+  float* out = pre + ((long)bh * n_chunks + c) * P::SIZE;
+  for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) {
+    const int r = i / CH, cc = i % CH;
+    out[P::TM + i] = sM[r * SW + cc] * sB[cc];
+  }
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {  // E2 = W^T A^T
+    floatx4 e = wave_mma_f32<CH>(sM + 16 * w, 1, SW, sA + 16 * ct * SW, 1, SW, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[P::E2 + (16 * w + rq + i) * CH + 16 * ct + col] = e[i];
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {  // G2 = W diag(beta) K, E1 = W^T K
+    floatx4 g = wave_mma_f32_scaled<CH>(sM + 16 * w * SW, SW, 1, sB, sK + 16 * t, S, 1, zero4());
+    floatx4 e = wave_mma_f32<CH>(sM + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
+      out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = e[i];
+    }
+  }
 }
 
 // 2. Entering state of every chunk, per (16-row slice of S, b, h).
 template <int D>
-__global__ __launch_bounds__(256) void delta_bwd_fwd(const float* __restrict__ k, const float* __restrict__ v,
-                                                     const float* __restrict__ beta, int T, int n_chunks,
-                                                     const float* __restrict__ S0, const float* __restrict__ Wm,
-                                                     float* __restrict__ Sc) {
+__device__ __forceinline__ void delta_bwd_fwd(const float* __restrict__ k, const float* __restrict__ v,
+                                                     int T, int n_chunks, const float* __restrict__ S0,
+                                                     const float* __restrict__ pre, float* __restrict__ Sc) {
   constexpr int S = DB<D>::S, SV = DB<D>::SV;
+  using P = Pre<D>;
   __shared__ __attribute__((aligned(16))) float sS[SL * S];
   __shared__ __attribute__((aligned(16))) float sK[CH * S];
-  __shared__ __attribute__((aligned(16))) float sX[CH * SV];
+  __shared__ __attribute__((aligned(16))) float sG[CH * S];   // G2
+  __shared__ __attribute__((aligned(16))) float sV[CH * SV];
   __shared__ __attribute__((aligned(16))) float sU[CH * SV];
-  __shared__ __attribute__((aligned(16))) float sW[CH * SW];
-  __shared__ float sB[CH];
+  __shared__ __attribute__((aligned(16))) float sT[CH * SW];  // Tm
   const int j0 = blockIdx.x * SL, bh = blockIdx.y;
   const int w = wave_id(), l = lane_id(), col = l & 15, rq = (l >> 4) * 4;
   for (int i = threadIdx.x; i < SL * D; i += blockDim.x) {
     const int r = i / D, cc = i % D;
     sS[r * S + cc] = S0 != nullptr ? S0[((long)bh * D + j0 + r) * D + cc] : 0.f;
   }
-  for (int c = 0; c < n_chunks; ++c) {
+  Rows<D> pk, pg;
+  Rows<SL> pv;
+  Rows<CH> pt;
+  auto fetch = [&](int c) {
     const int t0 = c * CH, L = min(CH, T - t0);
+    const float* pc = pre + ((long)bh * n_chunks + c) * P::SIZE;
+    pk.load(k + ((long)bh * T + t0) * D, D, 0, L);
+    pv.load(v + ((long)bh * T + t0) * D, D, j0, L);
+    pt.load(pc + P::TM, CH, 0, CH);
+    pg.load(pc + P::G2, D, 0, CH);
+  };
+  fetch(0);
+  for (int c = 0; c < n_chunks; ++c) {
     __syncthreads();  // the previous chunk's update of sS is complete
     store_block<SL, D>(Sc + (((long)bh * n_chunks + c) * D + j0) * D, sS);
-    stage<D>(sK, S, k + ((long)bh * T + t0) * D, D, 0, L);
-    stage<SL>(sX, SV, v + ((long)bh * T + t0) * D, D, j0, L);
-    for (int i = threadIdx.x; i < CH * CH / 4; i += blockDim.x) {
-      const int r = i / (CH / 4), cc = (i % (CH / 4)) * 4;
-      *reinterpret_cast<float4*>(sW + r * SW + cc) =
-          *reinterpret_cast<const float4*>(Wm + ((long)bh * n_chunks + c) * CH * CH + r * CH + cc);
-    }
-    if (threadIdx.x < CH) sB[threadIdx.x] = (int)threadIdx.x < L ? beta[(long)bh * T + t0 + threadIdx.x] : 0.f;
+    pk.put(sK, S);
+    pg.put(sG, S);
+    pv.put(sV, SV);
+    pt.put(sT, SW);
     __syncthreads();
-    {  // X = V - K S^T, rows 16w..
-      floatx4 ks = wave_mma_f32<D>(sK + 16 * w * S, S, 1, sS, 1, S, zero4());
+    if (c + 1 < n_chunks) fetch(c + 1);
+    {  // U = Tm V - G2 S^T, rows 16w..
+      floatx4 u = wave_mma_f32<CH>(sT + 16 * w * SW, SW, 1, sV, SV, 1, zero4());
+      floatx4 g = wave_mma_f32<D>(sG + 16 * w * S, S, 1, sS, 1, S, zero4());
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* x = sX + (16 * w + rq + i) * SV + col;
-        *x -= ks[i];
-      }
-    }
-    __syncthreads();
-    {  // U = W diag(beta) X
-      floatx4 u = wave_mma_f32_scaled<CH>(sW + 16 * w * SW, SW, 1, sB, sX, SV, 1, zero4());
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sU[(16 * w + rq + i) * SV + col] = u[i];
+      for (int i = 0; i < 4; ++i) sU[(16 * w + rq + i) * SV + col] = u[i] - g[i];
     }
     __syncthreads();
     if (w < D / 16) {  // S += U^T K, tile (rows j0.., columns 16w..)
@@ -190,20 +259,20 @@ __global__ __launch_bounds__(256) void delta_bwd_fwd(const float* __restrict__ k
 // 3. Exit adjoint dS1 of every chunk, per (16-row slice of dS, b, h), chunks
 //    in reverse; dS0 of the sequence at the end.
 template <int D>
-__global__ __launch_bounds__(256) void delta_bwd_rev(const float* __restrict__ q, const float* __restrict__ k,
+__device__ __forceinline__ void delta_bwd_rev(const float* __restrict__ q, const float* __restrict__ k,
                                                      const float* __restrict__ dO, const float* __restrict__ beta,
                                                      int T, int n_chunks, const float* __restrict__ dSf,
-                                                     const float* __restrict__ Wm, float* __restrict__ dSc,
+                                                     const float* __restrict__ pre, float* __restrict__ dSc,
                                                      float* __restrict__ dS0) {
   constexpr int S = DB<D>::S, SV = DB<D>::SV;
-  __shared__ __attribute__((aligned(16))) float sD[SL * S];   // dS slice
+  using P = Pre<D>;
+  __shared__ __attribute__((aligned(16))) float sD[SL * S];    // dS slice
   __shared__ __attribute__((aligned(16))) float sQ[CH * S];
   __shared__ __attribute__((aligned(16))) float sK[CH * S];
-  __shared__ __attribute__((aligned(16))) float sO[CH * SV];  // dO slice
-  __shared__ __attribute__((aligned(16))) float sA[CH * SW];  // tril_0(Q K^T)
-  __shared__ __attribute__((aligned(16))) float sW[CH * SW];
-  __shared__ __attribute__((aligned(16))) float sU[CH * SV];  // dU
-  __shared__ __attribute__((aligned(16))) float sX[CH * SV];  // dX
+  __shared__ __attribute__((aligned(16))) float sE1[CH * S];
+  __shared__ __attribute__((aligned(16))) float sO[CH * SV];   // dO slice
+  __shared__ __attribute__((aligned(16))) float sX[CH * SV];   // dX
+  __shared__ __attribute__((aligned(16))) float sE2[CH * SW];
   __shared__ float sB[CH];
   const int j0 = blockIdx.x * SL, bh = blockIdx.y;
   const int w = wave_id(), l = lane_id(), col = l & 15, rq = (l >> 4) * 4;
@@ -211,43 +280,39 @@ __global__ __launch_bounds__(256) void delta_bwd_rev(const float* __restrict__ q
     const int r = i / D, cc = i % D;
     sD[r * S + cc] = dSf != nullptr ? dSf[((long)bh * D + j0 + r) * D + cc] : 0.f;
   }
-  for (int c = n_chunks - 1; c >= 0; --c) {
+  Rows<D> pq, pk, pe1;
+  Rows<SL> po;
+  Rows<CH> pe2;
+  float pb = 0.f;
+  auto fetch = [&](int c) {
     const int t0 = c * CH, L = min(CH, T - t0);
+    const float* pc = pre + ((long)bh * n_chunks + c) * P::SIZE;
+    pq.load(q + ((long)bh * T + t0) * D, D, 0, L);
+    pk.load(k + ((long)bh * T + t0) * D, D, 0, L);
+    po.load(dO + ((long)bh * T + t0) * D, D, j0, L);
+    pe1.load(pc + P::E1, D, 0, CH);
+    pe2.load(pc + P::E2, CH, 0, CH);
+    if (threadIdx.x < CH) pb = (int)threadIdx.x < L ? beta[(long)bh * T + t0 + threadIdx.x] : 0.f;
+  };
+  fetch(n_chunks - 1);
+  for (int c = n_chunks - 1; c >= 0; --c) {
     __syncthreads();  // the previous chunk's update of sD is complete
     store_block<SL, D>(dSc + (((long)bh * n_chunks + c) * D + j0) * D, sD);
-    stage<D>(sQ, S, q + ((long)bh * T + t0) * D, D, 0, L);
-    stage<D>(sK, S, k + ((long)bh * T + t0) * D, D, 0, L);
-    stage<SL>(sO, SV, dO + ((long)bh * T + t0) * D, D, j0, L);
-    for (int i = threadIdx.x; i < CH * CH / 4; i += blockDim.x) {
-      const int r = i / (CH / 4), cc = (i % (CH / 4)) * 4;
-      *reinterpret_cast<float4*>(sW + r * SW + cc) =
-          *reinterpret_cast<const float4*>(Wm + ((long)bh * n_chunks + c) * CH * CH + r * CH + cc);
-    }
-    if (threadIdx.x < CH) sB[threadIdx.x] = (int)threadIdx.x < L ? beta[(long)bh * T + t0 + threadIdx.x] : 0.f;
+    pq.put(sQ, S);
+    pk.put(sK, S);
+    pe1.put(sE1, S);
+    po.put(sO, SV);
+    pe2.put(sE2, SW);
+    if (threadIdx.x < CH) sB[threadIdx.x] = pb;
     __syncthreads();
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {  // tril_0(Q K^T), rows 16w..
-      floatx4 qk = wave_mma_f32<D>(sQ + 16 * w * S, S, 1, sK + 16 * ct * S, 1, S, zero4());
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + rq + i, cc = 16 * ct + col;
-        sA[r * SW + cc] = cc <= r ? qk[i] : 0.f;
-      }
-    }
-    __syncthreads();
-    {  // dU = K dS^T + A^T dO, rows 16w..
-      floatx4 u = wave_mma_f32<D>(sK + 16 * w * S, S, 1, sD, 1, S, zero4());
-      u = wave_mma_f32<CH>(sA + 16 * w, 1, SW, sO, SV, 1, u);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sU[(16 * w + rq + i) * SV + col] = u[i];
-    }
-    __syncthreads();
-    {  // dX = diag(beta) W^T dU
-      floatx4 x = wave_mma_f32<CH>(sW + 16 * w, 1, SW, sU, SV, 1, zero4());
+    if (c > 0) fetch(c - 1);
+    {  // dX = diag(beta) (E1 dS^T + E2 dO), rows 16w..
+      floatx4 y = wave_mma_f32<D>(sE1 + 16 * w * S, S, 1, sD, 1, S, zero4());
+      y = wave_mma_f32<CH>(sE2 + 16 * w * SW, SW, 1, sO, SV, 1, y);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + rq + i;
-        sX[r * SV + col] = sB[r] * x[i];
+        sX[r * SV + col] = sB[r] * y[i];
       }
     }
     __syncthreads();
@@ -271,106 +336,107 @@ __global__ __launch_bounds__(256) void delta_bwd_rev(const float* __restrict__ q
   }
 }
 
-// 4. Gradients of one chunk from its S0, dS1 and W.  Wave w owns rows
-//    16w..16w+15 of every [64][.] result.
+// 2 and 3 in one launch: they are independent, and each alone fills only
+// D/16 x B x H workgroups.
+template <int D>
+__global__ __launch_bounds__(256) void delta_bwd_walks(const float* __restrict__ q, const float* __restrict__ k,
+                                                       const float* __restrict__ v, const float* __restrict__ dO,
+                                                       const float* __restrict__ beta, int T, int n_chunks,
+                                                       const float* __restrict__ S0, const float* __restrict__ dSf,
+                                                       const float* __restrict__ pre, float* __restrict__ Sc,
+                                                       float* __restrict__ dSc, float* __restrict__ dS0) {
+  if (blockIdx.z == 0)
+    delta_bwd_fwd<D>(k, v, T, n_chunks, S0, pre, Sc);
+  else
+    delta_bwd_rev<D>(q, k, dO, beta, T, n_chunks, dSf, pre, dSc, dS0);
+}
+
+// 4. Gradients of one chunk from its S0, dS1 and prep block.  Wave w owns
+//    rows 16w..16w+15 of every [64][.] result.
 template <int D>
 __global__ __launch_bounds__(256) void delta_bwd_grads(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ dO, const float* __restrict__ beta, int T, int n_chunks,
-    const float* __restrict__ Wm, const float* __restrict__ Sc, const float* __restrict__ dSc,
+    const float* __restrict__ pre, const float* __restrict__ Sc, const float* __restrict__ dSc,
     float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta) {
   constexpr int S = DB<D>::S;
   constexpr int NT = D / 16;
+  using P = Pre<D>;
   __shared__ __attribute__((aligned(16))) float bS[D * S];    // S0, then dS1, then S0
   __shared__ __attribute__((aligned(16))) float bQ[CH * S];
   __shared__ __attribute__((aligned(16))) float bK[CH * S];
   __shared__ __attribute__((aligned(16))) float bX[CH * S];   // V, then X
   __shared__ __attribute__((aligned(16))) float bU[CH * S];
   __shared__ __attribute__((aligned(16))) float bO[CH * S];   // dO
-  __shared__ __attribute__((aligned(16))) float bY[CH * SW];  // dU, then P1
-  __shared__ __attribute__((aligned(16))) float bW[CH * SW];  // W, then dLk
-  __shared__ __attribute__((aligned(16))) float bP[CH * SW];  // tril_0(Q K^T), then dY
+  __shared__ __attribute__((aligned(16))) float bT[CH * SW];  // Tm, then dLk
+  __shared__ __attribute__((aligned(16))) float bE[CH * SW];  // E2, then dY
+  __shared__ __attribute__((aligned(16))) float bF[CH * SW];  // E1, then P1
   __shared__ float sB[CH], sDb[CH];
   const int c = blockIdx.x, bh = blockIdx.y;
   const int t0 = c * CH, L = min(CH, T - t0);
   const int w = wave_id(), l = lane_id(), col = l & 15, rq = (l >> 4) * 4;
   const long cs = ((long)bh * n_chunks + c) * D * D;  // this chunk's state block
   const long row0 = (long)bh * T + t0;
+  const float* pc = pre + ((long)bh * n_chunks + c) * P::SIZE;
 
   load_block<D, D>(bS, Sc + cs);
   stage<D>(bQ, S, q + row0 * D, D, 0, L);
   stage<D>(bK, S, k + row0 * D, D, 0, L);
   stage<D>(bX, S, v + row0 * D, D, 0, L);
   stage<D>(bO, S, dO + row0 * D, D, 0, L);
-  for (int i = threadIdx.x; i < CH * CH / 4; i += blockDim.x) {
-    const int r = i / (CH / 4), cc = (i % (CH / 4)) * 4;
-    *reinterpret_cast<float4*>(bW + r * SW + cc) =
-        *reinterpret_cast<const float4*>(Wm + ((long)bh * n_chunks + c) * CH * CH + r * CH + cc);
-  }
+  stage<CH>(bT, SW, pc + P::TM, CH, 0, CH);
+  stage<CH>(bE, SW, pc + P::E2, CH, 0, CH);
+  stage<D>(bF, SW, pc + P::E1, D, 0, CH);
   if (threadIdx.x < CH) sB[threadIdx.x] = (int)threadIdx.x < L ? beta[row0 + threadIdx.x] : 0.f;
   __syncthreads();
 
-  // X = V - K S0^T; A = tril_0(Q K^T); dQ = dO S0 (first part)
-  floatx4 aq[NT], ak[NT];
+  // X = V - K S0^T; dQ = dO S0 (first part)
+  floatx4 aq[NT], ak[NT], y[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     floatx4 ks = wave_mma_f32<D>(bK + 16 * w * S, S, 1, bS + 16 * t * S, 1, S, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) bX[(16 * w + rq + i) * S + 16 * t + col] -= ks[i];
     aq[t] = wave_mma_f32<D>(bO + 16 * w * S, S, 1, bS + 16 * t, S, 1, zero4());
-    ak[t] = zero4();
-  }
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    floatx4 qk = wave_mma_f32<D>(bQ + 16 * w * S, S, 1, bK + 16 * ct * S, 1, S, zero4());
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + rq + i, cc = 16 * ct + col;
-      bP[r * SW + cc] = cc <= r ? qk[i] : 0.f;
-    }
   }
   __syncthreads();
-  // U = W diag(beta) X; bring dS1 in
+  // U = Tm X; bring dS1 in
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    floatx4 u = wave_mma_f32_scaled<CH>(bW + 16 * w * SW, SW, 1, sB, bX + 16 * t, S, 1, zero4());
+    floatx4 u = wave_mma_f32<CH>(bT + 16 * w * SW, SW, 1, bX + 16 * t, S, 1, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) bU[(16 * w + rq + i) * S + 16 * t + col] = u[i];
   }
   load_block<D, D>(bS, dSc + cs);
   __syncthreads();
-  // dU = K dS1^T + A^T dO; dK = U dS1 (first part)
+  // dY = E1 dS1^T + E2 dO (registers); dK = U dS1 (first part)
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    floatx4 u = wave_mma_f32<D>(bK + 16 * w * S, S, 1, bS + 16 * t * S, 1, S, zero4());
-    u = wave_mma_f32<CH>(bP + 16 * w, 1, SW, bO + 16 * t, S, 1, u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bY[(16 * w + rq + i) * SW + 16 * t + col] = u[i];
-    ak[t] = wave_mma_f32<D>(bU + 16 * w * S, S, 1, bS + 16 * t, S, 1, ak[t]);
+    y[t] = wave_mma_f32<D>(bF + 16 * w * SW, SW, 1, bS + 16 * t * S, 1, S, zero4());
+    y[t] = wave_mma_f32<CH>(bE + 16 * w * SW, SW, 1, bO + 16 * t, S, 1, y[t]);
+    ak[t] = wave_mma_f32<D>(bU + 16 * w * S, S, 1, bS + 16 * t, S, 1, zero4());
   }
   __syncthreads();
-  // dY = W^T dU into bP; S0 back in
+  // dY into bE; S0 back in
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    floatx4 y = wave_mma_f32<CH>(bW + 16 * w, 1, SW, bY + 16 * t, SW, 1, zero4());
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bP[(16 * w + rq + i) * SW + 16 * t + col] = y[i];
-  }
+    for (int i = 0; i < 4; ++i) bE[(16 * w + rq + i) * SW + 16 * t + col] = y[t][i];
   load_block<D, D>(bS, Sc + cs);
   __syncthreads();
   // dV = diag(beta) dY; dbeta first part <dY_r, X_r>; P1 = tril_0(dO U^T) into
-  // bY; P2 = tril_-1(dY U^T) gives dLk into bW and the second part of dbeta
+  // bF; P2 = tril_-1(dY U^T) gives dLk into bT and the second part of dbeta
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + rq + i;
-      if (r < L) dv[(row0 + r) * D + 16 * t + col] = sB[r] * bP[r * SW + 16 * t + col];
+      if (r < L) dv[(row0 + r) * D + 16 * t + col] = sB[r] * y[t][i];
     }
   {
     const int r = 16 * w + (l >> 2), part = l & 3;
     float s = 0.f;
-    for (int j = part; j < D; j += 4) s += bP[r * SW + j] * bX[r * S + j];
+    for (int j = part; j < D; j += 4) s += bE[r * SW + j] * bX[r * S + j];
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
     if (part == 0) sDb[r] = s;
@@ -379,14 +445,14 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
     floatx4 p1 = wave_mma_f32<D>(bO + 16 * w * S, S, 1, bU + 16 * ct * S, 1, S, zero4());
-    floatx4 p2 = wave_mma_f32<D>(bP + 16 * w * SW, SW, 1, bU + 16 * ct * S, 1, S, zero4());
+    floatx4 p2 = wave_mma_f32<D>(bE + 16 * w * SW, SW, 1, bU + 16 * ct * S, 1, S, zero4());
     floatx4 kk = wave_mma_f32<D>(bK + 16 * w * S, S, 1, bK + 16 * ct * S, 1, S, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + rq + i, cc = 16 * ct + col;
-      bY[r * SW + cc] = cc <= r ? p1[i] : 0.f;
+      bF[r * SW + cc] = cc <= r ? p1[i] : 0.f;
       const float p = cc < r ? p2[i] : 0.f;
-      bW[r * SW + cc] = -sB[r] * p;
+      bT[r * SW + cc] = -sB[r] * p;
       db2[i] += p * kk[i];
     }
   }
@@ -406,13 +472,13 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
   // dQ = dO S0 + P1 K;  dK = U dS1 - diag(beta) dY S0 + P1^T Q + dLk K + dLk^T K
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    aq[t] = wave_mma_f32<CH>(bY + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, aq[t]);
-    floatx4 ys = wave_mma_f32<D>(bP + 16 * w * SW, SW, 1, bS + 16 * t, S, 1, zero4());
+    aq[t] = wave_mma_f32<CH>(bF + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, aq[t]);
+    floatx4 ys = wave_mma_f32<D>(bE + 16 * w * SW, SW, 1, bS + 16 * t, S, 1, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) ak[t][i] -= sB[16 * w + rq + i] * ys[i];
-    ak[t] = wave_mma_f32<CH>(bY + 16 * w, 1, SW, bQ + 16 * t, S, 1, ak[t]);
-    ak[t] = wave_mma_f32<CH>(bW + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, ak[t]);
-    ak[t] = wave_mma_f32<CH>(bW + 16 * w, 1, SW, bK + 16 * t, S, 1, ak[t]);
+    ak[t] = wave_mma_f32<CH>(bF + 16 * w, 1, SW, bQ + 16 * t, S, 1, ak[t]);
+    ak[t] = wave_mma_f32<CH>(bT + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, ak[t]);
+    ak[t] = wave_mma_f32<CH>(bT + 16 * w, 1, SW, bK + 16 * t, S, 1, ak[t]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + rq + i;
@@ -429,15 +495,14 @@ hipError_t run_delta_backward(const float* q, const float* k, const float* v, co
                               int T, const float* S0, const float* dO, const float* dSf, float* dq, float* dk,
                               float* dv, float* dbeta, float* dS0, char* ws, hipStream_t s) {
   const int BH = B * H, nC = (T + CH - 1) / CH;
-  float* Wm = reinterpret_cast<float*>(ws);
-  float* Sc = Wm + (long)BH * nC * CH * CH;
+  float* pre = reinterpret_cast<float*>(ws);
+  float* Sc = pre + (long)BH * nC * Pre<D>::SIZE;
   float* dSc = Sc + (long)BH * nC * D * D;
-  hipLaunchKernelGGL((delta_bwd_prep<D>), dim3(nC, BH), dim3(64), 0, s, k, beta, T, nC, Wm);
-  hipLaunchKernelGGL((delta_bwd_fwd<D>), dim3(D / SL, BH), dim3(256), 0, s, k, v, beta, T, nC, S0, Wm, Sc);
-  hipLaunchKernelGGL((delta_bwd_rev<D>), dim3(D / SL, BH), dim3(256), 0, s, q, k, dO, beta, T, nC, dSf, Wm, dSc,
-                     dS0);
+  hipLaunchKernelGGL((delta_bwd_prep<D>), dim3(nC, BH), dim3(256), 0, s, q, k, beta, T, nC, pre);
+  hipLaunchKernelGGL((delta_bwd_walks<D>), dim3(D / SL, BH, 2), dim3(256), 0, s, q, k, v, dO, beta, T, nC, S0, dSf,
+                     pre, Sc, dSc, dS0);
   profile_mark_before(s);
-  hipLaunchKernelGGL((delta_bwd_grads<D>), dim3(nC, BH), dim3(256), 0, s, q, k, v, dO, beta, T, nC, Wm, Sc, dSc,
+  hipLaunchKernelGGL((delta_bwd_grads<D>), dim3(nC, BH), dim3(256), 0, s, q, k, v, dO, beta, T, nC, pre, Sc, dSc,
                      dq, dk, dv, dbeta);
   profile_mark_after(s);
   return hipGetLastError();
@@ -453,7 +518,7 @@ __global__ void delta_bwd_empty(const float* __restrict__ dSf, float* __restrict
 
 size_t delta_bwd_ws_bytes(int B, int H, int T, int d) {
   const long nC = (T + CH - 1) / CH;
-  return (size_t)B * H * nC * ((size_t)CH * CH + 2 * (size_t)d * d) * sizeof(float);
+  return (size_t)B * H * nC * (2 * (size_t)CH * CH + 2 * (size_t)CH * d + 2 * (size_t)d * d) * sizeof(float);
 }
 
 hipError_t launch_delta_backward(const float* q, const float* k, const float* v, const float* beta, int B, int H,
