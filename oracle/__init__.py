@@ -16,9 +16,11 @@ Sources (cited by page title and section):
   core identity, the additive-write problem, DeltaNet's prediction-error
   write, locality in key space and the reconstruction-loss derivation.
 * "Hebbian memory MLP stores facts in Transformers without training"
-  (mo.ai.kr), "a simple MLP construction": the classical memory W = sum v k^T.
+  (mo.ai.kr), "a simple MLP construction": the classical memory W = sum v k^T,
+  the gated feature map phi(x) = (A x) * (G x), the output matrix
+  B = (1/F) sum v phi(k)^T and the storage definition (``hebbian``).
 
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 brute-force sums, special cases and invariants; none is "parity unpinned".
 """
-from . import tc, delta  # noqa: F401
+from . import tc, delta, hebbian  # noqa: F401
