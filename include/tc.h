@@ -212,6 +212,41 @@ tc_status delta_scan_backward(const void* q, const void* k, const void* v, tc_dt
                               float* dq, float* dk_out, float* dv_out, float* dbeta, float* dS0,
                               void* ws, size_t ws_bytes, hipStream_t s);
 
+/* ---------------------------------------------------------------------------
+ * Outer-product fact memories and their recall, float32, d in {32, 64, 128}.
+ *
+ * Hebbian gated-MLP fact store ("Hebbian-memory MLP stores facts in a
+ * Transformer without training", simple MLP construction): with A, G
+ * [m, d] (row-major; the page draws them from a Gaussian) the features are
+ * phi(x) = (A x) * (G x) and the output matrix is B = (1/F) sum_i
+ * v_f(i) phi(k_i)^T.
+ *   hebbian_write: K [F, d], V [n_values, d], f [F] int32 (value row of each
+ *     key; an index outside [0, n_values) contributes nothing) -> Bt [m, d],
+ *     the transpose of B.  m must be a multiple of 64.  ws: at least
+ *     hebbian_workspace_bytes(F, m, d) bytes (partial sums of B^T).
+ *   hebbian_read: Q [n, d] -> out [n, d] = B phi(q) for every row q.
+ * L2 read against a given matrix ("Tensor Cache", Methodology 1, m = q A):
+ *   tc_memory_read: for every group g (a (b, h)), out[g] [n, d] =
+ *     Q[g] [n, d] A[g] [d, d] (A as tc_scan_forward returns A_final).
+ * Recall (the page's storage definition: the largest inner product with a
+ * value embedding):
+ *   recall_argmax: for every group g and query row R[g][i] [d], arg[g][i] =
+ *     the index j of the largest <R[g][i], V[g][j]> over the group's nc
+ *     candidates V[g] [nc, d] (the smallest j on a tie); best[g][i] = that
+ *     inner product (best may be NULL).  groups <= 65535.
+ * All pointers are device pointers owned by the caller.
+ * ------------------------------------------------------------------------- */
+size_t hebbian_workspace_bytes(int F, int m, int d);
+tc_status hebbian_write(const float* K, const float* V, const int32_t* f, int F, int n_values,
+                        const float* A, const float* G, int m, int d, float* Bt,
+                        void* ws, size_t ws_bytes, hipStream_t s);
+tc_status hebbian_read(const float* Q, int n, const float* A, const float* G, const float* Bt,
+                       int m, int d, float* out, hipStream_t s);
+tc_status tc_memory_read(const float* Q, const float* A, int groups, int n, int d, float* out,
+                         hipStream_t s);
+tc_status recall_argmax(const float* R, const float* V, int groups, int nq, int nc, int d,
+                        int32_t* arg, float* best, hipStream_t s);
+
 /* Workspace queries return SIZE_MAX when the arguments are invalid or
  * unsupported (tc_last_error() says why). */
 
@@ -224,6 +259,7 @@ tc_status delta_scan_backward(const void* q, const void* k, const void* v, tc_dt
  *   tc_scan_forward     the output kernel,
  *   tc_scan_backward    its forward-direction kernel (dq, deta, dlam),
  *   delta_scan_backward its chunk-parallel gradient kernel,
+ *   hebbian_write       its write kernel (not the segment sum),
  *   tc_decode_step      its only kernel,
  *   tc_decode_layer_step its only kernel,
  *   delta_scan_forward  the kernel that walks the chunks.

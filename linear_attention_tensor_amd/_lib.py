@@ -45,6 +45,11 @@ SIGNATURES = {
     "delta_scan_backward_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i]),
     "delta_scan_backward": (_i, [_p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                  _z, _p]),
+    "hebbian_workspace_bytes": (_z, [_i, _i, _i]),
+    "hebbian_write": (_i, [_p, _p, _p, _i, _i, _p, _p, _i, _i, _p, _p, _z, _p]),
+    "hebbian_read": (_i, [_p, _i, _p, _p, _p, _i, _i, _p, _p]),
+    "tc_memory_read": (_i, [_p, _p, _i, _i, _i, _p, _p]),
+    "recall_argmax": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p]),
     "tc_profile_next_call": (_i, [_p, _p]),
     "tc_last_error": (ctypes.c_char_p, []),
     "tc_version": (ctypes.c_char_p, []),

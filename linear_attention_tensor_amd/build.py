@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtc.so")
 
 SOURCES = ["tc_api.cpp", "tc_scan.hip", "tc_decode.hip", "tc_fused.hip", "tc_swa.hip", "delta_scan.hip", "delta_bf16.hip",
-           "delta_bwd.hip"]
+           "delta_bwd.hip", "tc_memory.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

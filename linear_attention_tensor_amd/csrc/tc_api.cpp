@@ -323,4 +323,84 @@ tc_status delta_scan_backward(const void* q, const void* k, const void* v, tc_dt
   });
 }
 
+static tc_status check_mem_d(const char* fn, int d) {
+  if (d != 32 && d != 64 && d != 128) return fail(TC_ERR_UNSUPPORTED, "%s: d must be 32, 64 or 128 (got %d)", fn, d);
+  return TC_OK;
+}
+
+static tc_status check_hebbian(const char* fn, int F, int n_values, int m, int d) {
+  if (F < 1 || n_values < 1 || m < 1)
+    return fail(TC_ERR_INVALID_ARG, "%s: F, n_values and m must be >= 1 (got %d, %d, %d)", fn, F, n_values, m);
+  if (m % 64 != 0) return fail(TC_ERR_UNSUPPORTED, "%s: m must be a multiple of 64 (got %d)", fn, m);
+  if ((long long)F * d >= (1LL << 31) || (long long)m * d >= (1LL << 31))
+    return fail(TC_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  return check_mem_d(fn, d);
+}
+
+size_t hebbian_workspace_bytes(int F, int m, int d) {
+  if (check_hebbian("hebbian_workspace_bytes", F, 1, m, d) != TC_OK) return SIZE_MAX;
+  ok();
+  return tc::hebbian_ws_bytes(F, m, d);
+}
+
+tc_status hebbian_write(const float* K, const float* V, const int32_t* f, int F, int n_values, const float* A,
+                        const float* G, int m, int d, float* Bt, void* ws, size_t ws_bytes, hipStream_t s) {
+  return guarded("hebbian_write", [&]() -> tc_status {
+    const char* fn = "hebbian_write";
+    tc_status st = check_hebbian(fn, F, n_values, m, d);
+    if (st != TC_OK) return st;
+    if (!K || !V || !f || !A || !G || !Bt || !ws)
+      return fail(TC_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    const size_t need = tc::hebbian_ws_bytes(F, m, d);
+    if (ws_bytes < need)
+      return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    return from_hip(tc::launch_hebbian_write(K, V, f, F, n_values, A, G, m, d, Bt, ws, s), fn);
+  });
+}
+
+tc_status hebbian_read(const float* Q, int n, const float* A, const float* G, const float* Bt, int m, int d,
+                       float* out, hipStream_t s) {
+  return guarded("hebbian_read", [&]() -> tc_status {
+    const char* fn = "hebbian_read";
+    tc_status st = check_hebbian(fn, 1, 1, m, d);
+    if (st != TC_OK) return st;
+    if (n < 0) return fail(TC_ERR_INVALID_ARG, "%s: n must be >= 0 (got %d)", fn, n);
+    if ((long long)n * d >= (1LL << 31)) return fail(TC_ERR_UNSUPPORTED, "%s: n * d too large", fn);
+    if (n == 0) return ok();
+    if (!Q || !A || !G || !Bt || !out) return fail(TC_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    return from_hip(tc::launch_hebbian_read(Q, n, A, G, Bt, m, d, out, s), fn);
+  });
+}
+
+tc_status tc_memory_read(const float* Q, const float* A, int groups, int n, int d, float* out, hipStream_t s) {
+  return guarded("tc_memory_read", [&]() -> tc_status {
+    const char* fn = "tc_memory_read";
+    tc_status st = check_mem_d(fn, d);
+    if (st != TC_OK) return st;
+    if (groups < 0 || n < 0) return fail(TC_ERR_INVALID_ARG, "%s: groups and n must be >= 0", fn);
+    if (groups > 65535) return fail(TC_ERR_UNSUPPORTED, "%s: at most 65535 groups", fn);
+    if ((long long)groups * n * d >= (1LL << 31)) return fail(TC_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+    if (groups == 0 || n == 0) return ok();
+    if (!Q || !A || !out) return fail(TC_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    return from_hip(tc::launch_memory_read(Q, A, groups, n, d, out, s), fn);
+  });
+}
+
+tc_status recall_argmax(const float* R, const float* V, int groups, int nq, int nc, int d, int32_t* arg,
+                        float* best, hipStream_t s) {
+  return guarded("recall_argmax", [&]() -> tc_status {
+    const char* fn = "recall_argmax";
+    tc_status st = check_mem_d(fn, d);
+    if (st != TC_OK) return st;
+    if (groups < 0 || nq < 0 || nc < 1)
+      return fail(TC_ERR_INVALID_ARG, "%s: groups, nq must be >= 0 and nc >= 1", fn);
+    if (groups > 65535) return fail(TC_ERR_UNSUPPORTED, "%s: at most 65535 groups", fn);
+    if ((long long)groups * nq * d >= (1LL << 31) || (long long)groups * nc * d >= (1LL << 31))
+      return fail(TC_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+    if (groups == 0 || nq == 0) return ok();
+    if (!R || !V || !arg) return fail(TC_ERR_INVALID_ARG, "%s: R, V, arg must not be NULL", fn);
+    return from_hip(tc::launch_recall_argmax(R, V, groups, nq, nc, d, arg, best, s), fn);
+  });
+}
+
 }  // extern "C"

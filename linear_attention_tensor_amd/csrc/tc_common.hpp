@@ -110,4 +110,33 @@ __device__ __forceinline__ floatx4 wave_mma_f32(const float* pa, int am, int ak,
 
 __device__ __forceinline__ floatx4 zero4() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 
+// fp32 MFMA over LDS rows that are contiguous in k:
+// acc[t] += A[16 x K] * B_t[K x 16], A rows at a + r sa, B_t given transposed
+// (rows = columns of B_t) at bt + t bstep + r sb.
+template <int K, int NT>
+__device__ __forceinline__ void mma_rows(const float* a, int sa, const float* bt, int bstep, int sb,
+                                         floatx4* acc) {
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const float* ap = a + r * sa + 4 * g;
+  const float* bp = bt + r * sb + 4 * g;
+#pragma unroll
+  for (int J = 0; J < K / 16; ++J) {
+    const float4 x = *reinterpret_cast<const float4*>(ap + 16 * J);
+    float4 y[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y[t] = *reinterpret_cast<const float4*>(bp + t * bstep + 16 * J);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.x, y[t].x, acc[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.y, y[t].y, acc[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.z, y[t].z, acc[t]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.w, y[t].w, acc[t]);
+  }
+}
+// (MFMA 4J + s takes k = 16J + 4g + s from lane (row, g), so one 16-byte
+// read per operand feeds four MFMAs; the permutation of k is shared by A and
+// B and changes nothing.)
+
 }  // namespace tc

@@ -65,6 +65,15 @@ hipError_t launch_delta_scan(const void* q, const void* k, const void* v, bool b
 // bf16 inputs with d in {64, 128} (delta_bf16.hip): bf16 MFMA with split
 // operands; launch_delta_scan dispatches to it.
 bool delta_bf16_supported(bool bf16, int d);
+// Outer-product fact memories and recall (tc_memory.hip): fp32, d in {32, 64, 128}.
+size_t hebbian_ws_bytes(int F, int m, int d);
+hipError_t launch_hebbian_write(const float* K, const float* V, const int* f, int F, int n_values, const float* A,
+                                const float* G, int m, int d, float* Bt, void* ws, hipStream_t s);
+hipError_t launch_hebbian_read(const float* Q, int n, const float* A, const float* G, const float* Bt, int m, int d,
+                               float* out, hipStream_t s);
+hipError_t launch_memory_read(const float* Q, const float* A, int groups, int n, int d, float* out, hipStream_t s);
+hipError_t launch_recall_argmax(const float* R, const float* V, int groups, int nq, int nc, int d, int* arg,
+                                float* best, hipStream_t s);
 // Backward of the delta-rule scan (delta_bwd.hip): fp32 inputs, d in {16, 32, 64}.
 size_t delta_bwd_ws_bytes(int B, int H, int T, int d);
 hipError_t launch_delta_backward(const float* q, const float* k, const float* v, const float* beta, int B, int H,

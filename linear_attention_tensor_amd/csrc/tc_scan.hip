@@ -258,31 +258,6 @@ struct FastTiles {
   static constexpr int TPW = NTS >= 4 ? NTS / 4 : 1;  // state tiles per wave
 };
 
-// acc[t] += A[16 x K] * B_t[K x 16], A rows at a + r sa, B_t given transposed
-// (rows = columns of B_t) at bt + t bstep + r sb.
-template <int K, int NT>
-__device__ __forceinline__ void mma_rows(const float* a, int sa, const float* bt, int bstep, int sb,
-                                         floatx4* acc) {
-  const int l = lane_id(), r = l & 15, g = l >> 4;
-  const float* ap = a + r * sa + 4 * g;
-  const float* bp = bt + r * sb + 4 * g;
-#pragma unroll
-  for (int J = 0; J < K / 16; ++J) {
-    const float4 x = *reinterpret_cast<const float4*>(ap + 16 * J);
-    float4 y[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) y[t] = *reinterpret_cast<const float4*>(bp + t * bstep + 16 * J);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.x, y[t].x, acc[t]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.y, y[t].y, acc[t]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.z, y[t].z, acc[t]);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = mfma4(x.w, y[t].w, acc[t]);
-  }
-}
-
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ float4 ld4(const uint16_t* p) {
   const uint2 u = *reinterpret_cast<const uint2*>(p);

@@ -27,6 +27,9 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "draw_cotangent",
+    "draw_facts",
+    "FactWorkload",
+    "FACT_WORKLOADS",
     "bf16_round_bits",
     "bf16_bits_to_f64",
     "round_to_dtype",
@@ -152,6 +155,36 @@ def draw_cotangent(B: int, H: int, T: int, dv: int, *, seed: int) -> np.ndarray:
     drawn from PCG64([seed, 1 << 42]) so it is independent of ``draw``."""
     rng = np.random.Generator(np.random.PCG64([seed, 1 << 42]))
     return (rng.standard_normal((B, H, T, dv)) / np.sqrt(dv)).astype(np.float32)
+
+
+@dataclasses.dataclass(frozen=True)
+class FactWorkload:
+    """A fact-store workload: F facts, m gated features, dimension d."""
+    name: str
+    F: int
+    m: int
+    d: int
+    seed: int
+
+
+FACT_WORKLOADS = {
+    "hebbian_f32": FactWorkload("hebbian_f32", 16384, 4096, 128, 107),
+}
+
+
+def draw_facts(F: int, d: int, m: int, *, seed: int, n_values: Optional[int] = None) -> dict:
+    """A fact set and a gated feature map, float32: keys and values uniform on
+    the unit sphere, f a random map of keys to values (a permutation when
+    n_values == F), A and G with N(0, 1) entries [m, d]."""
+    nv = F if n_values is None else n_values
+    rng = np.random.Generator(np.random.PCG64([seed, 1 << 43]))
+    K = _unit_rows(rng.standard_normal((F, d)))
+    V = _unit_rows(rng.standard_normal((nv, d)))
+    f = rng.permutation(F) if nv == F else rng.integers(0, nv, size=F)
+    A = rng.standard_normal((m, d))
+    G = rng.standard_normal((m, d))
+    return {"K": K.astype(np.float32), "V": V.astype(np.float32), "f": f.astype(np.int32),
+            "A": A.astype(np.float32), "G": G.astype(np.float32)}
 
 
 def draw_workload(name: str, *, T: Optional[int] = None, B: Optional[int] = None,

@@ -17,7 +17,8 @@ from . import _lib
 from ._lib import TC_BF16, TC_F32, check, lib
 
 __all__ = ["tc_scan_forward", "tc_scan_backward", "tc_decode_step", "tc_decode_layer_step",
-           "tc_fused_layer", "delta_scan_forward", "delta_scan_backward", "scan_backward_workspace",
+           "tc_fused_layer", "delta_scan_forward", "delta_scan_backward", "hebbian_write", "hebbian_read",
+           "tc_memory_read", "recall_argmax", "scan_backward_workspace",
            "scan_workspace", "fused_workspace", "delta_workspace"]
 
 CHUNK = 64
@@ -312,4 +313,67 @@ def delta_scan_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta:
                                    _ptr(ws), ws.numel() if ws is not None else 0, _stream())
     check("delta_scan_backward", st)
     return (gq, gk, gv, gb, gS0) if return_dS0 else (gq, gk, gv, gb)
+
+
+def _f32_2d(name, t, shape0, d, device):
+    _check_tensor(name, t, (shape0, d), torch.float32, device)
+
+
+def hebbian_write(K: torch.Tensor, V: torch.Tensor, f: torch.Tensor, A: torch.Tensor, G: torch.Tensor, *,
+                  ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """B^T [m, d] of the Hebbian gated-MLP store (B = (1/F) sum_i V[f[i]] phi(K[i])^T)."""
+    F, d = K.shape
+    m = A.shape[0]
+    _f32_2d("K", K, F, d, K.device)
+    _f32_2d("V", V, V.shape[0], d, K.device)
+    _f32_2d("A", A, m, d, K.device)
+    _f32_2d("G", G, m, d, K.device)
+    _check_tensor("f", f, (F,), torch.int32, K.device)
+    n = lib().hebbian_workspace_bytes(F, m, d)
+    if n == _lib.SIZE_MAX:
+        raise _lib.TCError("hebbian_workspace_bytes", _lib.TC_ERR_UNSUPPORTED, _lib.last_error())
+    if ws is None:
+        ws = _ws(n, K.device)
+    Bt = torch.empty((m, d), dtype=torch.float32, device=K.device)
+    st = lib().hebbian_write(_ptr(K), _ptr(V), _ptr(f), F, V.shape[0], _ptr(A), _ptr(G), m, d, _ptr(Bt), _ptr(ws),
+                             ws.numel(), _stream())
+    check("hebbian_write", st)
+    return Bt
+
+
+def hebbian_read(Q: torch.Tensor, A: torch.Tensor, G: torch.Tensor, Bt: torch.Tensor) -> torch.Tensor:
+    """B phi(q) for every row q of Q [n, d]."""
+    n, d = Q.shape
+    m = A.shape[0]
+    _f32_2d("Q", Q, n, d, Q.device)
+    _f32_2d("A", A, m, d, Q.device)
+    _f32_2d("G", G, m, d, Q.device)
+    _f32_2d("Bt", Bt, m, d, Q.device)
+    out = torch.empty((n, d), dtype=torch.float32, device=Q.device)
+    check("hebbian_read", lib().hebbian_read(_ptr(Q), n, _ptr(A), _ptr(G), _ptr(Bt), m, d, _ptr(out), _stream()))
+    return out
+
+
+def tc_memory_read(Q: torch.Tensor, A: torch.Tensor) -> torch.Tensor:
+    """Q[g] A[g] for every group g: Q [groups, n, d], A [groups, d, d]."""
+    groups, n, d = Q.shape
+    _check_tensor("Q", Q, (groups, n, d), torch.float32, Q.device)
+    _check_tensor("A", A, (groups, d, d), torch.float32, Q.device)
+    out = torch.empty((groups, n, d), dtype=torch.float32, device=Q.device)
+    check("tc_memory_read", lib().tc_memory_read(_ptr(Q), _ptr(A), groups, n, d, _ptr(out), _stream()))
+    return out
+
+
+def recall_argmax(R: torch.Tensor, V: torch.Tensor):
+    """(arg, best): the candidate of V[g] [nc, d] with the largest inner product
+    with each row of R[g] [nq, d] (smallest index on a tie), and that product."""
+    groups, nq, d = R.shape
+    nc = V.shape[1]
+    _check_tensor("R", R, (groups, nq, d), torch.float32, R.device)
+    _check_tensor("V", V, (groups, nc, d), torch.float32, R.device)
+    arg = torch.empty((groups, nq), dtype=torch.int32, device=R.device)
+    best = torch.empty((groups, nq), dtype=torch.float32, device=R.device)
+    check("recall_argmax", lib().recall_argmax(_ptr(R), _ptr(V), groups, nq, nc, d, _ptr(arg), _ptr(best),
+                                               _stream()))
+    return arg, best
 

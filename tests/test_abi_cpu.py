@@ -192,3 +192,23 @@ def test_scan_backward_rejects():
     assert call(dg=FAKE) == _lib.TC_ERR_INVALID_ARG
     assert call(B=0) == _lib.TC_OK
     assert lib().tc_scan_backward_workspace_bytes(1, 1, 10, 128, 128, 4, 64, _lib.TC_F32) == _lib.SIZE_MAX
+
+
+def test_memory_entry_points_reject():
+    L = lib()
+    assert L.hebbian_workspace_bytes(100, 100, 64) == _lib.SIZE_MAX  # m not a multiple of 64
+    assert L.hebbian_workspace_bytes(100, 128, 48) == _lib.SIZE_MAX
+    assert 0 < L.hebbian_workspace_bytes(100, 128, 64) < _lib.SIZE_MAX
+    need = L.hebbian_workspace_bytes(100, 128, 64)
+    w = L.hebbian_write
+    assert w(FAKE, FAKE, FAKE, 100, 100, FAKE, FAKE, 128, 64, FAKE, FAKE, need - 1, NULL) == _lib.TC_ERR_WORKSPACE
+    assert w(FAKE, FAKE, NULL, 100, 100, FAKE, FAKE, 128, 64, FAKE, FAKE, need, NULL) == _lib.TC_ERR_INVALID_ARG
+    assert w(FAKE, FAKE, FAKE, 0, 100, FAKE, FAKE, 128, 64, FAKE, FAKE, need, NULL) == _lib.TC_ERR_INVALID_ARG
+    assert L.hebbian_read(FAKE, 0, FAKE, FAKE, FAKE, 128, 64, FAKE, NULL) == _lib.TC_OK
+    assert L.hebbian_read(FAKE, 10, FAKE, FAKE, FAKE, 96, 64, FAKE, NULL) == _lib.TC_ERR_UNSUPPORTED
+    assert L.tc_memory_read(FAKE, FAKE, 2, 10, 16, FAKE, NULL) == _lib.TC_ERR_UNSUPPORTED
+    assert L.tc_memory_read(FAKE, FAKE, 0, 10, 64, FAKE, NULL) == _lib.TC_OK
+    assert L.tc_memory_read(NULL, FAKE, 2, 10, 64, FAKE, NULL) == _lib.TC_ERR_INVALID_ARG
+    assert L.recall_argmax(FAKE, FAKE, 1, 10, 0, 64, FAKE, NULL, NULL) == _lib.TC_ERR_INVALID_ARG
+    assert L.recall_argmax(FAKE, FAKE, 70000, 10, 5, 64, FAKE, NULL, NULL) == _lib.TC_ERR_UNSUPPORTED
+    assert L.recall_argmax(FAKE, FAKE, 1, 0, 5, 64, FAKE, NULL, NULL) == _lib.TC_OK
