@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fused", "scan", "scan_backward", "decode", "decode_layer", "delta",
-                                           "delta_backward"], default=None,
+                                           "delta_backward", "hebbian"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy twice (the reference for "
@@ -523,6 +523,52 @@ def bench_delta_backward(steps, warmup, dev):
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "f32"}}
 
 
+def bench_hebbian(steps, warmup, dev):
+    import numpy as np
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.FACT_WORKLOADS["hebbian_f32"]
+    F, m, d = w.F, w.m, w.d
+    x = I.draw_facts(F, d, m, seed=w.seed)
+    K, V, A, G = (torch.from_numpy(x[n]).to(dev) for n in ("K", "V", "A", "G"))
+    f = torch.from_numpy(x["f"]).to(dev)
+    lib = ops.lib()
+    nb = lib.hebbian_workspace_bytes(F, m, d)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    Bt = torch.empty((m, d), dtype=torch.float32, device=dev)
+    out = torch.empty((F, d), dtype=torch.float32, device=dev)
+    arg = torch.empty((F,), dtype=torch.int32, device=dev)
+    st = ops._stream()
+    p = ops._ptr
+
+    def write(_):
+        if lib.hebbian_write(p(K), p(V), p(f), F, F, p(A), p(G), m, d, p(Bt), p(ws), ws.numel(), st) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    def read_recall(_):
+        if lib.hebbian_read(p(K), F, p(A), p(G), p(Bt), m, d, p(out), st) != 0:
+            raise RuntimeError(ops._lib.last_error())
+        if lib.recall_argmax(p(out), p(V), 1, F, F, d, p(arg), None, st) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    _, ms_w, kernel_ms = time_calls(write, steps, warmup, KernelTimer(steps))
+    _, ms_r, _ = time_calls(read_recall, steps, warmup)
+    torch.cuda.synchronize()
+    stored = float((arg.cpu().numpy() == x["f"]).mean())
+    w_flops = 6.0 * F * m * d       # two feature products, their product, the accumulation
+    r_flops = 6.0 * F * m * d + 2.0 * F * F * d  # the same for the reads, then the recall scores
+    return {"workload": w.name, "ms_per_step": ms_w + ms_r, "facts_per_s": F / ((ms_w + ms_r) * 1e-3),
+            "roofline": roofline("mfma", w_flops / (kernel_ms * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
+            "main_kernel": {"name": "hebbian_write_kernel<128>", "ms": kernel_ms},
+            "write_ms": ms_w, "read_recall_ms": ms_r,
+            "read_recall_tflops": r_flops / (ms_r * 1e-3) / 1e12,
+            "stored_fraction": stored,
+            "config": {"F": F, "m": m, "d": d, "dtype_in": "f32"}}
+
+
 def cpu_baseline_fused(x, T_sample=16384):
     """The float64 oracle (as it stands) on a bounded prefix of the same
     input, with its BLAS pinned to one thread."""
@@ -575,6 +621,7 @@ def main():
         components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
         components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
+        components["hebbian_f32"] = bench_hebbian(args.steps, args.warmup, dev)
     elif only == "scan":
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
     elif only == "scan_backward":
@@ -587,6 +634,8 @@ def main():
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
     elif only == "delta_backward":
         components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
+    elif only == "hebbian":
+        components["hebbian_f32"] = bench_hebbian(args.steps, args.warmup, dev)
     if only not in (None, "fused"):
         print(json.dumps({"only": only, "components": components}))
         return
