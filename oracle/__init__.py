@@ -11,7 +11,8 @@ Sources (cited by page title and section):
 * "Tensor Cache: Eviction-conditioned Associative Memory for Transformers"
   (gist.science summary), Methodology 1 (two-level architecture: L1 ring of
   the W most recent tokens, L2 outer-product matrix A, write, read, fusion)
-  and Methodology 2 (parallel weighted-sum scan vs the chunk-mean shortcut).
+  and Methodology 2 (parallel weighted-sum scan vs the chunk-mean shortcut);
+  the capacity diagnostic of its results (``capacity``).
 * "DeltaNet-family linear attention variants" (molayo1419.me), sections on the
   core identity, the additive-write problem, DeltaNet's prediction-error
   write, locality in key space and the reconstruction-loss derivation.
@@ -23,4 +24,4 @@ Sources (cited by page title and section):
 Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
 brute-force sums, special cases and invariants; none is "parity unpinned".
 """
-from . import tc, delta, hebbian  # noqa: F401
+from . import tc, delta, hebbian, capacity  # noqa: F401
