@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fused", "scan", "scan_backward", "decode", "decode_layer", "delta",
-                                           "delta_backward", "hebbian"], default=None,
+                                           "delta_backward", "hebbian", "capacity"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy twice (the reference for "
@@ -569,6 +569,33 @@ def bench_hebbian(steps, warmup, dev):
             "config": {"F": F, "m": m, "d": d, "dtype_in": "f32"}}
 
 
+def bench_capacity(dev, groups=64, d=64, W=256, ns=(32, 64, 128, 256, 512, 1024, 2048), lams=(1.0, 0.999)):
+    """Recall of old pairs from the eviction-conditioned and the ingest-all
+    memory as pairs pile up (every step in libtc; one untimed pass first)."""
+    import numpy as np
+    import torch
+
+    from linear_attention_tensor_amd import diagnostics as Dg
+    from linear_attention_tensor_amd import inputs as I
+
+    curves = []
+    t0 = time.perf_counter()
+    for lam in lams:
+        for n in ns:
+            x = I.draw_pairs(groups, n + W, d, seed=1000 + n)
+            k, v = to_dev_f32(x["k"], dev), to_dev_f32(x["v"], dev)
+            lam_t, eta_t = to_dev_f32(np.full(1, lam), dev), to_dev_f32(np.ones(1), dev)
+            Dg.capacity_point(k, v, lam_t, eta_t, W, n)
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            tc_rate, ia_rate = Dg.capacity_point(k, v, lam_t, eta_t, W, n)
+            torch.cuda.synchronize()
+            curves.append({"lam": lam, "n_old": n, "recall_eviction_conditioned": tc_rate,
+                           "recall_ingest_all": ia_rate, "ms": (time.perf_counter() - a) * 1e3})
+    return {"workload": "capacity_diagnostic", "config": {"groups": groups, "d": d, "W": W, "dtype_in": "f32"},
+            "curve": curves, "wall_s": time.perf_counter() - t0}
+
+
 def cpu_baseline_fused(x, T_sample=16384):
     """The float64 oracle (as it stands) on a bounded prefix of the same
     input, with its BLAS pinned to one thread."""
@@ -622,6 +649,7 @@ def main():
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
         components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
         components["hebbian_f32"] = bench_hebbian(args.steps, args.warmup, dev)
+        components["capacity_diagnostic"] = bench_capacity(dev)
     elif only == "scan":
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
     elif only == "scan_backward":
@@ -636,6 +664,8 @@ def main():
         components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
     elif only == "hebbian":
         components["hebbian_f32"] = bench_hebbian(args.steps, args.warmup, dev)
+    elif only == "capacity":
+        components["capacity_diagnostic"] = bench_capacity(dev)
     if only not in (None, "fused"):
         print(json.dumps({"only": only, "components": components}))
         return

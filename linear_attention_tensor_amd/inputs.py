@@ -28,6 +28,7 @@ __all__ = [
     "WORKLOADS",
     "draw_cotangent",
     "draw_facts",
+    "draw_pairs",
     "FactWorkload",
     "FACT_WORKLOADS",
     "bf16_round_bits",
@@ -185,6 +186,15 @@ def draw_facts(F: int, d: int, m: int, *, seed: int, n_values: Optional[int] = N
     G = rng.standard_normal((m, d))
     return {"K": K.astype(np.float32), "V": V.astype(np.float32), "f": f.astype(np.int32),
             "A": A.astype(np.float32), "G": G.astype(np.float32)}
+
+
+def draw_pairs(groups: int, T: int, d: int, *, seed: int) -> dict:
+    """Key-value pairs uniform on the unit sphere, float32 [groups, 1, T, d]
+    (one head per group), for the capacity diagnostic."""
+    rng = np.random.Generator(np.random.PCG64([seed, 1 << 44]))
+    k = _unit_rows(rng.standard_normal((groups, 1, T, d)))
+    v = _unit_rows(rng.standard_normal((groups, 1, T, d)))
+    return {"k": k.astype(np.float32), "v": v.astype(np.float32)}
 
 
 def draw_workload(name: str, *, T: Optional[int] = None, B: Optional[int] = None,
