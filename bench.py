@@ -39,7 +39,7 @@ def parse():
                     help="untimed calls first: the GPU needs some tens of ms of load to reach its steady clock")
     ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fused", "scan", "scan_backward", "decode", "decode_layer", "delta",
+    ap.add_argument("--only", choices=["fused", "scan", "scan_bf16", "scan_backward", "decode", "decode_layer", "delta",
                                            "delta_backward", "hebbian", "capacity"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -307,6 +307,40 @@ def bench_scan(steps, warmup, dev):
             "hbm": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
             "main_kernel": {"name": "scan_output_fast<64>", "ms": kernel_ms}, "ms_per_call": ms_call,
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
+
+
+def bench_scan_bf16(steps, warmup, dev):
+    """tc_scan_forward (the L2 read alone) with bf16 inputs at the fused-layer size."""
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["fused_layer_bf16"]
+    x = I.draw_workload(w.name)
+    q, k, v = (to_dev_bf16(x[n], dev) for n in ("q", "k", "v"))
+    lam, eta = to_dev_f32(x["lam"], dev), to_dev_f32(x["eta"], dev)
+    m = torch.empty((w.B, w.H, w.T, w.d), dtype=torch.float32, device=dev)
+    A = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device=dev)
+    nb = ops.scan_workspace(w.B, w.H, w.T, w.d, w.d, w.W, 1)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    lib = ops.lib()
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 1, ops._ptr(lam), ops._ptr(eta), w.B, w.H, w.T, w.d,
+            w.d, w.W, 64, ops._ptr(m), ops._ptr(A), ops._ptr(ws), ws.numel(), ops._stream())
+
+    def call(_):
+        if lib.tc_scan_forward(*args) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, kernel_ms = time_calls(call, steps, warmup, KernelTimer(steps))
+    nbytes = scan_bytes(w.B, w.H, w.T, w.d, 2)
+    return {"workload": w.name + " (L2 read only)", "ms_per_step": ms,
+            "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+            "roofline": roofline("hbm", nbytes / (ms_call * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"),
+            "mfma": roofline("mfma", scan_flops(w.B, w.H, w.T, w.d, w.W, 256) / (ms_call * 1e-3) / 1e12,
+                             PEAK_BF16_TFLOPS, "TFLOP/s"),
+            "main_kernel": {"name": "scan_read_kernel<128>", "ms": kernel_ms}, "ms_per_call": ms_call,
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "bf16"}}
 
 
 def bench_scan_backward(steps, warmup, dev):
@@ -644,6 +678,7 @@ def main():
     if only is None and not args.no_components:
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
         components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
+        components["scan_bf16_fused_size"] = bench_scan_bf16(args.steps, args.warmup, dev)
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
         components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
@@ -652,6 +687,8 @@ def main():
         components["capacity_diagnostic"] = bench_capacity(dev)
     elif only == "scan":
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
+    elif only == "scan_bf16":
+        components["scan_bf16_fused_size"] = bench_scan_bf16(args.steps, args.warmup, dev)
     elif only == "scan_backward":
         components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
     elif only == "decode":

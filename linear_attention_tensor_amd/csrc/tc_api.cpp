@@ -97,6 +97,7 @@ size_t tc_scan_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int c
     return SIZE_MAX;
   }
   ok();
+  if (tc::scan_bf16_fast(dt == TC_BF16, dk, dv, T)) return tc::fused_ws_bytes(B, H, T, dk, dv, W);
   return tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
 }
 
@@ -113,11 +114,15 @@ tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype 
     if (!lam || !eta) return fail(TC_ERR_INVALID_ARG, "%s: lam and eta must not be NULL", fn);
     if (T > 0 && (!q || !k || !v || !m))
       return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, m must not be NULL", fn);
-    const size_t need = tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
+    const bool fast16 = tc::scan_bf16_fast(dt == TC_BF16, dk, dv, T);
+    const size_t need = fast16 ? tc::fused_ws_bytes(B, H, T, dk, dv, W)
+                               : tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
     if (ws_bytes < need)
       return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
     if (T == 0 && !A_final) return ok();
+    if (fast16)
+      return from_hip(tc::launch_tc_scan_bf16(q, k, v, lam, eta, B, H, T, dk, W, m, A_final, ws, s), fn);
     return from_hip(tc::launch_tc_scan(q, k, v, dt == TC_BF16, lam, eta, B, H, T, dk, dv, W, m,
                                        A_final, ws, s),
                     fn);

@@ -273,6 +273,175 @@ __global__ void fused_prefix_kernel(const float* __restrict__ lam, int H, int D,
   }
 }
 
+// ---------------------------------------------------------------------------
+// The L2 read alone (tc_scan_forward with bf16 inputs, d in {64, 128}), on the
+// same pre-pass and prefix: per 256-query tile p with entering state S_n
+// (bf16 S^T) and evictions k_c, v_c = keys t0 - W + c,
+//   m_r = lam^(r+1) q_r S_n + sum_{c <= r} eta lam^(r-c) <q_r, k_c> v_c.
+// One workgroup (8 waves) per (tile, b, h); K (256 rows), V^T (256 columns,
+// from the pre-pass copy) and S^T are staged whole in LDS (160 KiB at
+// d = 128).  v_mfma_f32_16x16x32_bf16 (A: lane m + 16 (k / 8), B: lane
+// n + 16 (k / 8), eight consecutive k per lane; D: lane n + 16 (m / 4),
+// element m % 4):
+//   O^T  = S^T Q^T                         (then column r scaled by lam^(r+1)),
+//   P^T  = K Q^T over 32-key steps, masked to c <= r and weighted eta lam^(r-c),
+//   O^T += V^T P^T.
+// The two 16-key M tiles of a 32-key step take keys 8 (m / 4) + m % 4 (+ 4),
+// so that lane (n, g) ends up with keys 8g .. 8g+7 of the step: P^T feeds the
+// next MFMA from registers.  A wave owns 32 queries and visits only the steps
+// with c <= its last query; the row groups are paired on the SIMDs
+// (waves w and w + 4 take groups w and 7 - w) to balance that triangle.
+template <int NCH>
+__device__ __forceinline__ int rswz(int r) {  // 16-byte chunk swizzle of a row
+  return NCH >= 16 ? ((r & 3) | (((r >> 3) & 3) << 2)) : (((r >> 1) & 1) | (((r >> 3) & 3) << 1));
+}
+template <int NCH>
+__device__ __forceinline__ int rpos(int r, int c) {  // element offset of chunk c of row r
+  return (r * NCH + (c ^ rswz<NCH>(r))) * 8;
+}
+
+template <int D>
+__global__ __launch_bounds__(NTHR) void scan_read_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ vt,
+                                                         const uint16_t* __restrict__ sst,
+                                                         const float* __restrict__ lam,
+                                                         const float* __restrict__ eta, int H,
+                                                         FusedGeom G, float* __restrict__ m) {
+  constexpr int NCK = D / 8;   // chunks per K / S^T row
+  constexpr int NCV = MQ / 8;  // chunks per V^T row
+  constexpr int NKS = D / 32;  // k-steps over d
+  __shared__ __attribute__((aligned(16))) uint16_t sK[MQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[D * MQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sS[D * D];
+  const int p = blockIdx.x, bh = blockIdx.y;
+  const int T = G.T, t0 = MQ * p, j0 = t0 - G.W;
+  // every load of the tile is issued before the first LDS store
+  constexpr int NLK = MQ * NCK / NTHR, NLV = D * NCV / NTHR, NLS = D * NCK / NTHR;
+  uint4 xk[NLK], xv[NLV], xs[NLS];
+#pragma unroll
+  for (int u = 0; u < NLK; ++u) {  // K rows c: key j0 + c
+    const int i = u * NTHR + threadIdx.x, c = i / NCK, ch = i % NCK, j = j0 + c;
+    xk[u] = make_uint4(0u, 0u, 0u, 0u);
+    if (j >= 0 && j < T) xk[u] = *reinterpret_cast<const uint4*>(k + ((long)bh * T + j) * D + 8 * ch);
+  }
+#pragma unroll
+  for (int u = 0; u < NLV; ++u) {  // V^T rows: key j0 + c at column j0 + c + voff
+    const int i = u * NTHR + threadIdx.x, dv = i / NCV, ch = i % NCV, col = j0 + G.voff + 8 * ch;
+    xv[u] = make_uint4(0u, 0u, 0u, 0u);
+    if (col >= 0 && col + 8 <= G.Tp) xv[u] = *reinterpret_cast<const uint4*>(vt + ((long)bh * D + dv) * G.Tp + col);
+  }
+  const uint16_t* sp = sst + ((long)bh * G.n_tiles + p) * D * D;
+#pragma unroll
+  for (int u = 0; u < NLS; ++u) {
+    const int i = u * NTHR + threadIdx.x;
+    xs[u] = *reinterpret_cast<const uint4*>(sp + (i / NCK) * D + 8 * (i % NCK));
+  }
+
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+  const int grp = w < 4 ? w : 11 - w;  // 32-query row group of this wave
+  const int r0 = 32 * grp;
+  // Q^T operand: lane (n, g) holds q[query][32 ks + 8 g .. + 7]
+  bf16x8 qb[2][NKS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int t = t0 + r0 + 16 * nt + n;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (t < T) x = *reinterpret_cast<const uint4*>(q + ((long)bh * T + t) * D + 32 * ks + 8 * g);
+      qb[nt][ks] = as_bf16x8(x);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NLK; ++u) {
+    const int i = u * NTHR + threadIdx.x;
+    *reinterpret_cast<uint4*>(sK + rpos<NCK>(i / NCK, i % NCK)) = xk[u];
+  }
+#pragma unroll
+  for (int u = 0; u < NLV; ++u) {
+    const int i = u * NTHR + threadIdx.x;
+    *reinterpret_cast<uint4*>(sV + rpos<NCV>(i / NCV, i % NCV)) = xv[u];
+  }
+#pragma unroll
+  for (int u = 0; u < NLS; ++u) {
+    const int i = u * NTHR + threadIdx.x;
+    *reinterpret_cast<uint4*>(sS + rpos<NCK>(i / NCK, i % NCK)) = xs[u];
+  }
+  __syncthreads();
+
+  const Decay dec(lam[bh % H]);
+  const float et = eta[bh % H];
+  floatx4 o[D / 16][2];
+  // state term, then column r scaled by lam^(r+1)
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) {
+    o[mt][0] = zero4();
+    o[mt][1] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sS + rpos<NCK>(16 * mt + n, 4 * ks + g)));
+      o[mt][0] = mfma_bf16_16x16x32(a, qb[0][ks], o[mt][0]);
+      o[mt][1] = mfma_bf16_16x16x32(a, qb[1][ks], o[mt][1]);
+    }
+  }
+  {
+    const float f0 = dec(r0 + n + 1), f1 = dec(r0 + 16 + n + 1);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      o[mt][0] *= f0;
+      o[mt][1] *= f1;
+    }
+  }
+  // evictions of the tile, 32 keys per step, up to this wave's last query
+  for (int st = 0; st <= grp; ++st) {
+    floatx4 sc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};  // [key half][query tile]
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int row = 32 * st + 8 * (n >> 2) + (n & 3) + 4 * hf;
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sK + rpos<NCK>(row, 4 * ks + g)));
+        sc[hf][0] = mfma_bf16_16x16x32(a, qb[0][ks], sc[hf][0]);
+        sc[hf][1] = mfma_bf16_16x16x32(a, qb[1][ks], sc[hf][1]);
+      }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int dr = r0 + 16 * nt + n - (32 * st + 8 * g);  // r - c of element (hf, e) is dr - 4 hf - e
+      uint32_t pk[4];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const floatx4 x = sc[hf][nt];
+        const float w0 = dr - 4 * hf >= 0 ? et * dec(dr - 4 * hf) * x[0] : 0.f;
+        const float w1 = dr - 4 * hf - 1 >= 0 ? et * dec(dr - 4 * hf - 1) * x[1] : 0.f;
+        const float w2 = dr - 4 * hf - 2 >= 0 ? et * dec(dr - 4 * hf - 2) * x[2] : 0.f;
+        const float w3 = dr - 4 * hf - 3 >= 0 ? et * dec(dr - 4 * hf - 3) * x[3] : 0.f;
+        pk[2 * hf] = cvt_pk(w0, w1);
+        pk[2 * hf + 1] = cvt_pk(w2, w3);
+      }
+      pb[nt] = as_bf16x8(pk[0], pk[1], pk[2], pk[3]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sV + rpos<NCV>(16 * mt + n, 4 * st + g)));
+      o[mt][0] = mfma_bf16_16x16x32(a, pb[0], o[mt][0]);
+      o[mt][1] = mfma_bf16_16x16x32(a, pb[1], o[mt][1]);
+    }
+  }
+  // O^T element (dv = 16 mt + 4 g + e, query r0 + 16 nt + n)
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int t = t0 + r0 + 16 * nt + n;
+    if (t >= T) continue;
+    float* out = m + ((long)bh * T + t) * D + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+      *reinterpret_cast<float4*>(out + 16 * mt) = make_float4(o[mt][nt][0], o[mt][nt][1], o[mt][nt][2], o[mt][nt][3]);
+  }
+}
+
 FusedGeom make_geom(int T, int W) {
   FusedGeom G{};
   G.T = T;
@@ -314,11 +483,47 @@ hipError_t run_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
 
 }  // namespace
 
+template <int D>
+hipError_t run_scan_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lam,
+                         const float* eta, int B, int H, const FusedGeom& G, float* m, float* A_final, void* ws,
+                         hipStream_t s) {
+  const int BH = B * H;
+  const size_t ne = state_elems(G, B, H, D);
+  float* delta = static_cast<float*>(ws);
+  uint16_t* sst = reinterpret_cast<uint16_t*>(delta + ne);
+  uint16_t* vt = sst + ne;
+  FusedGeom Gs = G;
+  const long units = (long)G.n_tiles * BH;
+  Gs.tiles_per_seg = (int)std::max<long>(1, (units + kPrepassWorkgroups - 1) / kPrepassWorkgroups);
+  const int n_seg = (G.n_tiles + Gs.tiles_per_seg - 1) / Gs.tiles_per_seg;
+  hipLaunchKernelGGL(fused_state_kernel<D>, dim3(n_seg, BH), dim3(NTHR), 0, s, k, v, lam, eta, H, Gs,
+                     delta, vt);
+  hipLaunchKernelGGL(fused_prefix_kernel, dim3((D * D / 4 + 63) / 64, BH), dim3(64), 0, s, lam, H, D,
+                     G, delta, sst, A_final);
+  profile_mark_before(s);
+  hipLaunchKernelGGL(scan_read_kernel<D>, dim3(G.n_tiles, BH), dim3(NTHR), 0, s, q, k, vt, sst, lam, eta, H, G, m);
+  profile_mark_after(s);
+  return hipGetLastError();
+}
+
 size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W) {
   (void)dv;
   const FusedGeom G = make_geom(T, W);
   return state_elems(G, B, H, dk) * (sizeof(float) + sizeof(uint16_t)) +
          (size_t)B * H * dk * G.Tp * sizeof(uint16_t);
+}
+
+bool scan_bf16_fast(bool bf16, int dk, int dv, int T) { return bf16 && dk == dv && (dk == 64 || dk == 128) && T > 0; }
+
+hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, const float* lam, const float* eta,
+                               int B, int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s) {
+  const FusedGeom G = make_geom(T, W);
+  const uint16_t* Q = static_cast<const uint16_t*>(q);
+  const uint16_t* K = static_cast<const uint16_t*>(k);
+  const uint16_t* V = static_cast<const uint16_t*>(v);
+  if (d == 128) return run_scan_bf16<128>(Q, K, V, lam, eta, B, H, G, m, A_final, ws, s);
+  if (d == 64) return run_scan_bf16<64>(Q, K, V, lam, eta, B, H, G, m, A_final, ws, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const float* lam,

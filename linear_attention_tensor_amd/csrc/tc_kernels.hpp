@@ -48,6 +48,12 @@ void profile_mark_before(hipStream_t s);
 void profile_mark_after(hipStream_t s);
 
 size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W);
+// tc_scan_forward with bf16 inputs and d in {64, 128} runs on the fused
+// layer's pre-pass and prefix plus an L2-read kernel (tc_fused.hip); its
+// workspace is fused_ws_bytes.
+bool scan_bf16_fast(bool bf16, int dk, int dv, int T);
+hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, const float* lam, const float* eta,
+                               int B, int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s);
 hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const float* lam,
                            const float* eta, const float* g, int B, int H, int T, int d, int W,
                            float scale, float* y, float* A_final, void* ws, hipStream_t s);

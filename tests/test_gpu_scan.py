@@ -84,3 +84,23 @@ def test_scan_fused_size_bf16_sampled_rows():
     rows = [0, w.W - 1, w.W, w.W + 1, w.W + 63, w.W + 64, 5000, 16384, 20001, w.T - 65, w.T - 1]
     ref = O.tc_scan_rows(x["q64"], x["k64"], x["v64"], lam_of(x), x["eta"], w.W, rows)
     assert report("m rows", m[:, :, rows], ref) <= 2e-2
+
+
+@pytest.mark.parametrize("B,H,T,d,W", [
+    (1, 2, 300, 128, 1),       # W = 1
+    (2, 1, 100, 64, 150),      # T < W: nothing evicted
+    (1, 1, 257, 128, 256),     # one eviction
+    (1, 3, 1000, 64, 300),     # several tiles, W not a multiple of 8
+    (2, 2, 2049, 128, 1024),   # many tiles, ragged last tile
+    (1, 1, 513, 64, 7),
+])
+def test_scan_bf16_tiled_path(B, H, T, d, W):
+    # bf16 inputs with d in {64, 128} run on the fused layer's pre-pass and
+    # prefix plus the L2-read kernel (256-query chunks)
+    print(f"[case] scan bf16 tiled B={B} H={H} T={T} d={d} W={W}", flush=True)
+    x = I.draw(B, H, T, d, seed=5000 + T + W, dtype="bf16", lam=("uniform", 0.95, 0.999))
+    m, A = run(x, W)
+    m_ref, A_ref = O.tc_scan(x["q64"], x["k64"], x["v64"], lam_of(x), x["eta"], W)
+    assert report("m", m, m_ref) <= 2e-2
+    assert report("A", A, A_ref) <= 2e-2
+    assert np.all(m[:, :, : min(W, T)] == 0.0)
