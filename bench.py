@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fused", "scan", "scan_bf16", "scan_backward", "decode", "decode_layer", "delta",
-                                           "delta_backward", "hebbian", "capacity"], default=None,
+                                           "delta_f32", "delta_backward", "hebbian", "capacity"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy twice (the reference for "
@@ -521,6 +521,36 @@ def bench_delta(steps, warmup, dev):
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "bf16"}}
 
 
+def bench_delta_f32(steps, warmup, dev):
+    """delta_scan_forward with float32 inputs at the backward's workload."""
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["delta_backward_f32"]
+    x = I.draw_workload(w.name)
+    q, k, v = (to_dev_f32(x[n], dev) for n in ("q", "k", "v"))
+    beta = to_dev_f32(x["beta"], dev)
+    o = torch.empty((w.B, w.H, w.T, w.d), dtype=torch.float32, device=dev)
+    nb = ops.delta_workspace(w.B, w.H, w.T, w.d, w.d, 0)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    lib = ops.lib()
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, ops._ptr(beta), w.B, w.H, w.T, w.d, w.d, 64, None,
+            ops._ptr(o), None, ops._ptr(ws), ws.numel(), ops._stream())
+
+    def call(_):
+        if lib.delta_scan_forward(*args) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, kernel_ms = time_calls(call, steps, warmup, KernelTimer(steps))
+    gbs = delta_bytes(w.B, w.H, w.T, w.d, 4) / (ms_call * 1e-3) / 1e9
+    return {"workload": "delta_scan_f32", "ms_per_step": ms, "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
+            "main_kernel": {"name": "delta_fwd_walk<64>", "ms": kernel_ms}, "ms_per_call": ms_call,
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "f32"}}
+
+
 def bench_delta_backward(steps, warmup, dev):
     import torch
 
@@ -682,6 +712,7 @@ def main():
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
         components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
+        components["delta_scan_f32"] = bench_delta_f32(args.steps, args.warmup, dev)
         components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
         components["hebbian_f32"] = bench_hebbian(args.steps, args.warmup, dev)
         components["capacity_diagnostic"] = bench_capacity(dev)
@@ -697,6 +728,8 @@ def main():
         components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
     elif only == "delta":
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
+    elif only == "delta_f32":
+        components["delta_scan_f32"] = bench_delta_f32(args.steps, args.warmup, dev)
     elif only == "delta_backward":
         components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
     elif only == "hebbian":

@@ -128,7 +128,7 @@ struct Pre {
 //    substitution (wave 0, lane c solves column c), then Tm, E2, G2, E1.  Rows
 //    past the sequence end have beta = 0, so their rows and columns of W are
 //    those of I and their rows of Tm, G2 are zero.
-template <int D>
+template <int D, bool FWD>
 __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ q, const float* __restrict__ k,
                                                       const float* __restrict__ beta, int T, int n_chunks,
                                                       float* __restrict__ pre) {
@@ -179,20 +179,25 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
     const int r = i / CH, cc = i % CH;
     out[P::TM + i] = sM[r * SW + cc] * sB[cc];
   }
+  if constexpr (FWD) {  // the forward keeps tril_0(Q K^T) itself in the E2 slot
+    for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) out[P::E2 + i] = sA[(i / CH) * SW + i % CH];
+  } else {
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {  // E2 = W^T A^T
-    floatx4 e = wave_mma_f32<CH>(sM + 16 * w, 1, SW, sA + 16 * ct * SW, 1, SW, zero4());
+    for (int ct = 0; ct < 4; ++ct) {  // E2 = W^T A^T
+      floatx4 e = wave_mma_f32<CH>(sM + 16 * w, 1, SW, sA + 16 * ct * SW, 1, SW, zero4());
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[P::E2 + (16 * w + rq + i) * CH + 16 * ct + col] = e[i];
+      for (int i = 0; i < 4; ++i) out[P::E2 + (16 * w + rq + i) * CH + 16 * ct + col] = e[i];
+    }
   }
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {  // G2 = W diag(beta) K, E1 = W^T K
+  for (int t = 0; t < NT; ++t) {  // G2 = W diag(beta) K (and E1 = W^T K for the backward)
     floatx4 g = wave_mma_f32_scaled<CH>(sM + 16 * w * SW, SW, 1, sB, sK + 16 * t, S, 1, zero4());
-    floatx4 e = wave_mma_f32<CH>(sM + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
-      out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = e[i];
+    for (int i = 0; i < 4; ++i) out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
+    if constexpr (!FWD) {
+      floatx4 e = wave_mma_f32<CH>(sM + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = e[i];
     }
   }
 }
@@ -498,12 +503,111 @@ hipError_t run_delta_backward(const float* q, const float* k, const float* v, co
   float* pre = reinterpret_cast<float*>(ws);
   float* Sc = pre + (long)BH * nC * Pre<D>::SIZE;
   float* dSc = Sc + (long)BH * nC * D * D;
-  hipLaunchKernelGGL((delta_bwd_prep<D>), dim3(nC, BH), dim3(256), 0, s, q, k, beta, T, nC, pre);
+  hipLaunchKernelGGL((delta_bwd_prep<D, false>), dim3(nC, BH), dim3(256), 0, s, q, k, beta, T, nC, pre);
   hipLaunchKernelGGL((delta_bwd_walks<D>), dim3(D / SL, BH, 2), dim3(256), 0, s, q, k, v, dO, beta, T, nC, S0, dSf,
                      pre, Sc, dSc, dS0);
   profile_mark_before(s);
   hipLaunchKernelGGL((delta_bwd_grads<D>), dim3(nC, BH), dim3(256), 0, s, q, k, v, dO, beta, T, nC, pre, Sc, dSc,
                      dq, dk, dv, dbeta);
+  profile_mark_after(s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The forward itself (fp32, d <= 64) on the same prep: per chunk, with A =
+// tril_0(Q K^T) kept by the prep in place of E2,
+//   U = Tm V - G2 S0^T,   O = Q S0^T + A U,   S1 = S0 + U^T K,
+// per (16-row slice of S, b, h), chunks in order, the next chunk prefetched
+// into registers.  O's columns j0.. come from the slice (row j of S only
+// sees column j of V, U and O).
+template <int D>
+__global__ __launch_bounds__(256) void delta_fwd_walk(const float* __restrict__ q, const float* __restrict__ k,
+                                                      const float* __restrict__ v, int T, int n_chunks,
+                                                      const float* __restrict__ S0, const float* __restrict__ pre,
+                                                      float* __restrict__ o, float* __restrict__ S_final) {
+  constexpr int S = DB<D>::S, SV = DB<D>::SV;
+  using P = Pre<D>;
+  __shared__ __attribute__((aligned(16))) float sS[SL * S];
+  __shared__ __attribute__((aligned(16))) float sQ[CH * S];
+  __shared__ __attribute__((aligned(16))) float sK[CH * S];
+  __shared__ __attribute__((aligned(16))) float sG[CH * S];   // G2
+  __shared__ __attribute__((aligned(16))) float sV[CH * SV];
+  __shared__ __attribute__((aligned(16))) float sU[CH * SV];
+  __shared__ __attribute__((aligned(16))) float sT[CH * SW];  // Tm
+  __shared__ __attribute__((aligned(16))) float sA[CH * SW];  // tril_0(Q K^T)
+  const int j0 = blockIdx.x * SL, bh = blockIdx.y;
+  const int w = wave_id(), l = lane_id(), col = l & 15, rq = (l >> 4) * 4;
+  for (int i = threadIdx.x; i < SL * D; i += blockDim.x) {
+    const int r = i / D, cc = i % D;
+    sS[r * S + cc] = S0 != nullptr ? S0[((long)bh * D + j0 + r) * D + cc] : 0.f;
+  }
+  Rows<D> pq, pk, pg;
+  Rows<SL> pv;
+  Rows<CH> pt, pa;
+  auto fetch = [&](int c) {
+    const int t0 = c * CH, L = min(CH, T - t0);
+    const float* pc = pre + ((long)bh * n_chunks + c) * P::SIZE;
+    pq.load(q + ((long)bh * T + t0) * D, D, 0, L);
+    pk.load(k + ((long)bh * T + t0) * D, D, 0, L);
+    pv.load(v + ((long)bh * T + t0) * D, D, j0, L);
+    pt.load(pc + P::TM, CH, 0, CH);
+    pa.load(pc + P::E2, CH, 0, CH);
+    pg.load(pc + P::G2, D, 0, CH);
+  };
+  fetch(0);
+  for (int c = 0; c < n_chunks; ++c) {
+    const int t0 = c * CH, L = min(CH, T - t0);
+    __syncthreads();  // the previous chunk's update of sS is complete
+    pq.put(sQ, S);
+    pk.put(sK, S);
+    pg.put(sG, S);
+    pv.put(sV, SV);
+    pt.put(sT, SW);
+    pa.put(sA, SW);
+    __syncthreads();
+    if (c + 1 < n_chunks) fetch(c + 1);
+    floatx4 out;
+    {  // U = Tm V - G2 S^T and O = Q S^T, rows 16w..
+      floatx4 u = wave_mma_f32<CH>(sT + 16 * w * SW, SW, 1, sV, SV, 1, zero4());
+      floatx4 g = wave_mma_f32<D>(sG + 16 * w * S, S, 1, sS, 1, S, zero4());
+      out = wave_mma_f32<D>(sQ + 16 * w * S, S, 1, sS, 1, S, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sU[(16 * w + rq + i) * SV + col] = u[i] - g[i];
+    }
+    __syncthreads();
+    out = wave_mma_f32<CH>(sA + 16 * w * SW, SW, 1, sU, SV, 1, out);  // O += A U
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + rq + i;
+      if (r < L) o[((long)bh * T + t0 + r) * D + j0 + col] = out[i];
+    }
+    if (w < D / 16) {  // S += U^T K, tile (rows j0.., columns 16w..)
+      float* base = sS + rq * S + 16 * w + col;
+      floatx4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = base[i * S];
+      acc = wave_mma_f32<CH>(sU, 1, SV, sK + 16 * w, S, 1, acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) base[i * S] = acc[i];
+    }
+  }
+  if (S_final != nullptr) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < SL * D; i += blockDim.x) {
+      const int r = i / D, cc = i % D;
+      S_final[((long)bh * D + j0 + r) * D + cc] = sS[r * S + cc];
+    }
+  }
+}
+
+template <int D>
+hipError_t run_delta_forward(const float* q, const float* k, const float* v, const float* beta, int B, int H, int T,
+                             const float* S0, float* o, float* S_final, char* ws, hipStream_t s) {
+  const int BH = B * H, nC = (T + CH - 1) / CH;
+  float* pre = reinterpret_cast<float*>(ws);
+  hipLaunchKernelGGL((delta_bwd_prep<D, true>), dim3(nC, BH), dim3(256), 0, s, q, k, beta, T, nC, pre);
+  profile_mark_before(s);
+  hipLaunchKernelGGL((delta_fwd_walk<D>), dim3(D / SL, BH), dim3(256), 0, s, q, k, v, T, nC, S0, pre, o, S_final);
   profile_mark_after(s);
   return hipGetLastError();
 }
@@ -515,6 +619,24 @@ __global__ void delta_bwd_empty(const float* __restrict__ dSf, float* __restrict
 }
 
 }  // namespace
+
+bool delta_f32_fast(bool bf16, int d) { return !bf16 && (d == 16 || d == 32 || d == 64); }
+
+size_t delta_f32_ws_bytes(int B, int H, int T, int d) {
+  const long nC = (T + CH - 1) / CH;
+  return (size_t)B * H * nC * (2 * (size_t)CH * CH + 2 * (size_t)CH * d) * sizeof(float);
+}
+
+hipError_t launch_delta_f32(const float* q, const float* k, const float* v, const float* beta, int B, int H, int T,
+                            int d, const float* S0, float* o, float* S_final, void* ws, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  switch (d) {
+    case 16: return run_delta_forward<16>(q, k, v, beta, B, H, T, S0, o, S_final, w, s);
+    case 32: return run_delta_forward<32>(q, k, v, beta, B, H, T, S0, o, S_final, w, s);
+    case 64: return run_delta_forward<64>(q, k, v, beta, B, H, T, S0, o, S_final, w, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 size_t delta_bwd_ws_bytes(int B, int H, int T, int d) {
   const long nC = (T + CH - 1) / CH;

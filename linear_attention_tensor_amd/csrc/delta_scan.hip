@@ -192,7 +192,9 @@ hipError_t dispatch_delta(const void* q, const void* k, const void* v, const flo
 
 size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, bool bf16) {
   (void)dv;
-  return delta_bf16_supported(bf16, dk) ? delta_bf16_ws_bytes(B, H, T, dk) : 0;
+  if (delta_bf16_supported(bf16, dk)) return delta_bf16_ws_bytes(B, H, T, dk);
+  if (delta_f32_fast(bf16, dk) && T > 0) return delta_f32_ws_bytes(B, H, T, dk);
+  return 0;
 }
 
 hipError_t launch_delta_scan(const void* q, const void* k, const void* v, bool bf16,
@@ -201,7 +203,9 @@ hipError_t launch_delta_scan(const void* q, const void* k, const void* v, bool b
   (void)dv;
   if (delta_bf16_supported(bf16, dk))
     return launch_delta_bf16(q, k, v, beta, B, H, T, dk, S0, o, S_final, ws, s);
-  (void)ws;
+  if (delta_f32_fast(bf16, dk) && T > 0)
+    return launch_delta_f32(static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                            beta, B, H, T, dk, S0, o, S_final, ws, s);
   if (bf16) return dispatch_delta<uint16_t>(q, k, v, beta, B, H, T, dk, S0, o, S_final, s);
   return dispatch_delta<float>(q, k, v, beta, B, H, T, dk, S0, o, S_final, s);
 }
