@@ -96,6 +96,28 @@ struct Rows {
   }
 };
 
+// One [D][D] state block (row stride D in global) in registers, for LDS
+// (stride D + 4); 256 threads.
+template <int D>
+struct Blk {
+  static constexpr int N = (D * D / 4 + 255) / 256;
+  float4 x[N];
+  __device__ __forceinline__ void load(const float* src) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = i * 256 + threadIdx.x;
+      x[i] = idx < D * D / 4 ? *reinterpret_cast<const float4*>(src + 4 * idx) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void put(float* dst) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int idx = i * 256 + threadIdx.x, r = idx / (D / 4), c = 4 * (idx % (D / 4));
+      if (idx < D * D / 4) *reinterpret_cast<float4*>(dst + r * DB<D>::S + c) = x[i];
+    }
+  }
+};
+
 // one [R][D] block (row stride D in global) <-> LDS (stride S)
 template <int R, int D>
 __device__ __forceinline__ void load_block(float* dst, const float* src) {
@@ -124,10 +146,10 @@ struct Pre {
   static constexpr long SIZE = 2 * CH * CH + 2 * CH * D;
 };
 
-// 1. Per chunk (in parallel): W = (I + diag(beta) tril_-1(K K^T))^-1 by forward
-//    substitution (wave 0, lane c solves column c), then Tm, E2, G2, E1.  Rows
-//    past the sequence end have beta = 0, so their rows and columns of W are
-//    those of I and their rows of Tm, G2 are zero.
+// 1. Per chunk (in parallel): W = (I + diag(beta) tril_-1(K K^T))^-1 (blocked:
+//    diagonal 16-blocks by substitution, the rest by 16x16 products), then
+//    Tm, E2, G2, E1.  Rows past the sequence end have beta = 0, so their rows
+//    and columns of W are those of I and their rows of Tm, G2 are zero.
 template <int D, bool FWD>
 __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ q, const float* __restrict__ k,
                                                       const float* __restrict__ beta, int T, int n_chunks,
@@ -136,15 +158,24 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
   using P = Pre<D>;
   __shared__ __attribute__((aligned(16))) float sQ[CH * S];
   __shared__ __attribute__((aligned(16))) float sK[CH * S];
-  __shared__ __attribute__((aligned(16))) float sM[CH * SW];  // beta_r <k_r, k_c> (c < r), then W
+  __shared__ __attribute__((aligned(16))) float sM[CH * SW];  // beta_r <k_r, k_c> (c < r)
   __shared__ __attribute__((aligned(16))) float sA[CH * SW];  // tril_0(Q K^T)
+  __shared__ __attribute__((aligned(16))) float sWx[D == 64 ? 1 : CH * SW];
+  __shared__ __attribute__((aligned(16))) float sTmp[3 * 16 * 17];
   __shared__ float sB[CH];
+  float* const sWm = D == 64 ? sQ : sWx;  // W; at d = 64 it takes the place of Q, read before it is written
   const int c = blockIdx.x, bh = blockIdx.y;
   const int t0 = c * CH, L = min(CH, T - t0);
   const int w = wave_id(), l = lane_id(), col = l & 15, rq = (l >> 4) * 4;
-  stage<D>(sQ, S, q + ((long)bh * T + t0) * D, D, 0, L);
-  stage<D>(sK, S, k + ((long)bh * T + t0) * D, D, 0, L);
-  if (threadIdx.x < CH) sB[threadIdx.x] = (int)threadIdx.x < L ? beta[(long)bh * T + t0 + threadIdx.x] : 0.f;
+  {
+    Rows<D> xq, xk;
+    xq.load(q + ((long)bh * T + t0) * D, D, 0, L);
+    xk.load(k + ((long)bh * T + t0) * D, D, 0, L);
+    const float bb = (int)threadIdx.x < L ? beta[(long)bh * T + t0 + threadIdx.x] : 0.f;
+    xq.put(sQ, S);
+    xk.put(sK, S);
+    if (threadIdx.x < CH) sB[threadIdx.x] = bb;
+  }
   __syncthreads();
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
@@ -158,44 +189,70 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
     }
   }
   __syncthreads();
+  // W = M^-1 in 16-row blocks: the four diagonal blocks by substitution
+  // (wave 0, one lane per column of every block), then the off-diagonal
+  // blocks one block diagonal at a time, W_ab = -W_aa sum_{c=b}^{a-1} M_ac W_cb
+  // (a wave per block, 16x16 MFMA products through a small LDS tile).
+  for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) {
+    const int r = i / CH, cc = i % CH;
+    if (cc / 16 > r / 16) sWm[r * SW + cc] = 0.f;
+  }
   if (w == 0) {
-    float x[CH];
+    const int blk = l >> 4, cc = l & 15, o = 16 * blk;
+    float x[16];
 #pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      float acc = r == l ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float acc = r == cc ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc -= sM[r * SW + i] * x[i];
+      for (int i = 0; i < r; ++i) acc -= sM[(o + r) * SW + o + i] * x[i];
       x[r] = acc;
     }
-    // one wave: its LDS operations run in issue order; this only stops the
-    // compiler from moving the stores of W above the reads of sM
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int r = 0; r < CH; ++r) sM[r * SW + l] = x[r];
+    for (int r = 0; r < 16; ++r) sWm[(o + r) * SW + o + cc] = x[r];
   }
   __syncthreads();
+#pragma unroll
+  for (int dist = 1; dist < 4; ++dist) {
+    if (w < 4 - dist) {
+      const int bb = w, aa = w + dist;
+      floatx4 t = zero4();
+      for (int cb = bb; cb < aa; ++cb)
+        t = wave_mma_f32<16>(sM + 16 * aa * SW + 16 * cb, SW, 1, sWm + 16 * cb * SW + 16 * bb, SW, 1, t);
+      float* tw = sTmp + w * 16 * 17;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tw[(rq + i) * 17 + col] = t[i];
+      // the tile is read back by this wave only
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      const floatx4 wab = wave_mma_f32<16>(sWm + 16 * aa * SW + 16 * aa, SW, 1, tw, 17, 1, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sWm[(16 * aa + rq + i) * SW + 16 * bb + col] = -wab[i];
+    }
+    __syncthreads();
+  }
   float* out = pre + ((long)bh * n_chunks + c) * P::SIZE;
   for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) {
     const int r = i / CH, cc = i % CH;
-    out[P::TM + i] = sM[r * SW + cc] * sB[cc];
+    out[P::TM + i] = sWm[r * SW + cc] * sB[cc];
   }
   if constexpr (FWD) {  // the forward keeps tril_0(Q K^T) itself in the E2 slot
     for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) out[P::E2 + i] = sA[(i / CH) * SW + i % CH];
   } else {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {  // E2 = W^T A^T
-      floatx4 e = wave_mma_f32<CH>(sM + 16 * w, 1, SW, sA + 16 * ct * SW, 1, SW, zero4());
+      floatx4 e = wave_mma_f32<CH>(sWm + 16 * w, 1, SW, sA + 16 * ct * SW, 1, SW, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[P::E2 + (16 * w + rq + i) * CH + 16 * ct + col] = e[i];
     }
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {  // G2 = W diag(beta) K (and E1 = W^T K for the backward)
-    floatx4 g = wave_mma_f32_scaled<CH>(sM + 16 * w * SW, SW, 1, sB, sK + 16 * t, S, 1, zero4());
+    floatx4 g = wave_mma_f32_scaled<CH>(sWm + 16 * w * SW, SW, 1, sB, sK + 16 * t, S, 1, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
     if constexpr (!FWD) {
-      floatx4 e = wave_mma_f32<CH>(sM + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
+      floatx4 e = wave_mma_f32<CH>(sWm + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = e[i];
     }
@@ -384,15 +441,32 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
   const long row0 = (long)bh * T + t0;
   const float* pc = pre + ((long)bh * n_chunks + c) * P::SIZE;
 
-  load_block<D, D>(bS, Sc + cs);
-  stage<D>(bQ, S, q + row0 * D, D, 0, L);
-  stage<D>(bK, S, k + row0 * D, D, 0, L);
-  stage<D>(bX, S, v + row0 * D, D, 0, L);
-  stage<D>(bO, S, dO + row0 * D, D, 0, L);
-  stage<CH>(bT, SW, pc + P::TM, CH, 0, CH);
-  stage<CH>(bE, SW, pc + P::E2, CH, 0, CH);
-  stage<D>(bF, SW, pc + P::E1, D, 0, CH);
-  if (threadIdx.x < CH) sB[threadIdx.x] = (int)threadIdx.x < L ? beta[row0 + threadIdx.x] : 0.f;
+  // every load of the chunk is issued before the first LDS store; S0 and
+  // dS1 stay in registers for the later phases that reload them
+  Blk<D> s0, s1;
+  s0.load(Sc + cs);
+  s1.load(dSc + cs);
+  {
+    Rows<D> xq, xk, xv, xo, xf;
+    Rows<CH> xt, xe;
+    xq.load(q + row0 * D, D, 0, L);
+    xk.load(k + row0 * D, D, 0, L);
+    xv.load(v + row0 * D, D, 0, L);
+    xo.load(dO + row0 * D, D, 0, L);
+    xt.load(pc + P::TM, CH, 0, CH);
+    xe.load(pc + P::E2, CH, 0, CH);
+    xf.load(pc + P::E1, D, 0, CH);
+    const float bb = (int)threadIdx.x < L ? beta[row0 + threadIdx.x] : 0.f;
+    s0.put(bS);
+    xq.put(bQ, S);
+    xk.put(bK, S);
+    xv.put(bX, S);
+    xo.put(bO, S);
+    xt.put(bT, SW);
+    xe.put(bE, SW);
+    xf.put(bF, SW);
+    if (threadIdx.x < CH) sB[threadIdx.x] = bb;
+  }
   __syncthreads();
 
   // X = V - K S0^T; dQ = dO S0 (first part)
@@ -412,7 +486,7 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
 #pragma unroll
     for (int i = 0; i < 4; ++i) bU[(16 * w + rq + i) * S + 16 * t + col] = u[i];
   }
-  load_block<D, D>(bS, dSc + cs);
+  s1.put(bS);
   __syncthreads();
   // dY = E1 dS1^T + E2 dO (registers); dK = U dS1 (first part)
 #pragma unroll
@@ -427,7 +501,7 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) bE[(16 * w + rq + i) * SW + 16 * t + col] = y[t][i];
-  load_block<D, D>(bS, Sc + cs);
+  s0.put(bS);
   __syncthreads();
   // dV = diag(beta) dY; dbeta first part <dY_r, X_r>; P1 = tril_0(dO U^T) into
   // bF; P2 = tril_-1(dY U^T) gives dLk into bT and the second part of dbeta
