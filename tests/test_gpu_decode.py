@@ -63,11 +63,15 @@ def test_decode_sequences_at_different_positions():
 
 
 def test_scan_prefill_then_decode_continues_the_scan():
-    # prefill T0 tokens with the scan, hand over A_final and the last W tokens, decode the rest
+    # prefill T0 tokens with the scan, hand over A_final and the last W tokens,
+    # decode the rest: every decoded read and the final A against the oracle's
+    # scan of the whole sequence (the bf16 bar), and against the GPU scan of the
+    # whole sequence (bf16 scans round P and the state to bf16 for the MFMAs)
     B, H, d, W, T0, T = 1, 2, 128, 16, 100, 130
     x = I.draw(B, H, T, d, seed=55, dtype="bf16")
     q, k, v = (to_dev(x[n], "bf16") for n in ("q", "k", "v"))
     lam, eta = f32_dev(x["lam"]), f32_dev(x["eta"])
+    m_ref, A_ref = O.tc_scan(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64), x["eta"], W)
     m_full, A_full = ops.tc_scan_forward(q, k, v, lam, eta, W)
     _, A = ops.tc_scan_forward(q[:, :, :T0].contiguous(), k[:, :, :T0].contiguous(),
                                v[:, :, :T0].contiguous(), lam, eta, W)
@@ -80,8 +84,10 @@ def test_scan_prefill_then_decode_continues_the_scan():
         pos = torch.full((B,), t, dtype=torch.int64, device="cuda")
         m = ops.tc_decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
                                ring_k, ring_v, A, lam, eta, pos, W)
-        assert report(f"t={t}", m.cpu().numpy(), m_full[:, :, t].cpu().numpy()) <= 1e-4
-    assert report("A", A.cpu().numpy(), A_full.cpu().numpy()) <= 1e-4
+        assert report(f"t={t}", m.cpu().numpy(), m_ref[:, :, t]) <= 2e-2
+        assert report(f"t={t} vs GPU scan", m.cpu().numpy(), m_full[:, :, t].cpu().numpy()) <= 1e-2
+    assert report("A", A.cpu().numpy(), A_ref) <= 2e-2
+    assert report("A vs GPU scan", A.cpu().numpy(), A_full.cpu().numpy()) <= 1e-2
 
 
 def test_decode_workload_full_size_sampled_sequences():
