@@ -10,13 +10,15 @@
 // Launches (all on the caller's stream):
 //   fused_state   per (tile, b, h): the tile's own contribution to the
 //                 state, from zero, delta_p = sum_c eta lam^(L-1-c) v_c k_c^T
-//                 (S^T layout, fp32, bf16 MFMA with fp32 accumulation); it also
+//                 (S^T layout, bf16 MFMA with fp32 accumulation, stored as
+//                 bf16); it also
 //                 writes V^T (per head [d][Tp] bf16) into the workspace, so
 //                 that the main kernel can copy V^T blocks straight to LDS;
-//   fused_prefix  S_0 = 0, S_{p+1} = lam^L_p S_p + delta_p: the state entering
-//                 every tile (bf16) and the final state A (fp32);
+//   fused_prefix  S_0 = 0, S_{p+1} = lam^L_p S_p + delta_p, carried in fp32:
+//                 the state entering every tile (bf16) and the final state A
+//                 (fp32);
 //   swa           per (tile, b, h): window softmax plus the L2 read.
-// Workspace: delta (fp32) | entering states (bf16) | V^T copy (bf16).
+// Workspace: delta (bf16) | entering states (bf16) | V^T copy (bf16).
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
 #include "tc_mfma.hpp"
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __res
                                                            const uint16_t* __restrict__ v,
                                                            const float* __restrict__ lam,
                                                            const float* __restrict__ eta, int H,
-                                                           FusedGeom G, float* __restrict__ ws_state,
+                                                           FusedGeom G, uint16_t* __restrict__ ws_state,
                                                            uint16_t* __restrict__ ws_vt) {
   constexpr int SKT = KB + 4;  // K^T and V^T rows: keys contiguous, 34-word stride
   __shared__ __attribute__((aligned(16))) uint16_t sKt[D * SKT];
@@ -221,12 +223,13 @@ __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __res
   if (pc < p_end) {                                                                   \
     state_block_mma<D, SKT>(acc, sKt, sVt);                                           \
     if (jc + KB >= G.col_end(pc)) {                                                   \
-      float* out = ws_state + ((long)bh * G.n_tiles + pc) * D * D;                    \
+      uint16_t* out = ws_state + ((long)bh * G.n_tiles + pc) * D * D;                 \
       _Pragma("unroll") for (int i = 0; i < ST::TPW; ++i) {                           \
         if (ST::owns(w, i)) {                                                         \
           const int dv0 = ST::dv0(w, i), dk0 = ST::dk0(w, i);                         \
           _Pragma("unroll") for (int e = 0; e < 16; ++e)                              \
-              out[(dv0 + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + dk0 + col] = acc[i][e]; \
+              out[(dv0 + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + dk0 + col] =          \
+                  f32_to_bf16(acc[i][e]);                                             \
         }                                                                             \
         acc[i] = zero16();                                                            \
       }                                                                               \
@@ -241,26 +244,28 @@ __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __res
 #undef TC_STATE_STEP
 }
 
-// S_0 = 0, S_{p+1} = lam^len(p) S_p + delta_p; element idx = dv * D + dk of
-// S^T, four consecutive elements per thread.  Entering states go out as bf16
-// (round to nearest even), the final state as fp32 A[dk][dv].
+// S_0 = 0, S_{p+1} = lam^len(p) S_p + delta_p, carried in fp32 (delta_p is
+// stored as bf16); element idx = dv * D + dk of S^T, four consecutive
+// elements per thread.  Entering states go out as bf16 (round to nearest
+// even), the final state as fp32 A[dk][dv].
 __global__ void fused_prefix_kernel(const float* __restrict__ lam, int H, int D, FusedGeom G,
-                                    const float* __restrict__ delta, uint16_t* __restrict__ sst,
+                                    const uint16_t* __restrict__ delta, uint16_t* __restrict__ sst,
                                     float* __restrict__ A_final) {
   const int n_el = D * D, n4 = n_el / 4;
   const int i4 = blockIdx.x * blockDim.x + threadIdx.x;
   const int bh = blockIdx.y;
   if (i4 >= n4) return;
   const Decay dec(lam[bh % H]);
-  const float4* dp = reinterpret_cast<const float4*>(delta + (long)bh * G.n_tiles * n_el) + i4;
+  const uint2* dp = reinterpret_cast<const uint2*>(delta + (long)bh * G.n_tiles * n_el) + i4;
   uint2* sp = reinterpret_cast<uint2*>(sst + (long)bh * G.n_tiles * n_el) + i4;
   float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 16
   for (int p = 0; p < G.n_tiles; ++p) {
     sp[(long)p * n4] = make_uint2(pack_bf16x2(run.x, run.y), pack_bf16x2(run.z, run.w));
     const float d = dec(G.key_end(p) - G.key_begin(p));
-    const float4 x = dp[(long)p * n4];
-    run = make_float4(fmaf(d, run.x, x.x), fmaf(d, run.y, x.y), fmaf(d, run.z, x.z), fmaf(d, run.w, x.w));
+    const uint2 x = dp[(long)p * n4];
+    run = make_float4(fmaf(d, run.x, lo_f(x.x)), fmaf(d, run.y, hi_f(x.x)), fmaf(d, run.z, lo_f(x.y)),
+                      fmaf(d, run.w, hi_f(x.y)));
   }
   if (A_final != nullptr) {
     float* af = A_final + (long)bh * n_el;
@@ -461,8 +466,8 @@ hipError_t run_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
                      float* y, float* A_final, void* ws, hipStream_t s) {
   const int BH = B * H;
   const size_t ne = state_elems(G, B, H, D);
-  float* delta = static_cast<float*>(ws);
-  uint16_t* sst = reinterpret_cast<uint16_t*>(delta + ne);
+  uint16_t* delta = static_cast<uint16_t*>(ws);
+  uint16_t* sst = delta + ne;
   uint16_t* vt = sst + ne;
   // about one pre-pass workgroup per CU, each streaming several tiles
   FusedGeom Gs = G;
@@ -489,8 +494,8 @@ hipError_t run_scan_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          hipStream_t s) {
   const int BH = B * H;
   const size_t ne = state_elems(G, B, H, D);
-  float* delta = static_cast<float*>(ws);
-  uint16_t* sst = reinterpret_cast<uint16_t*>(delta + ne);
+  uint16_t* delta = static_cast<uint16_t*>(ws);
+  uint16_t* sst = delta + ne;
   uint16_t* vt = sst + ne;
   FusedGeom Gs = G;
   const long units = (long)G.n_tiles * BH;
@@ -509,7 +514,7 @@ hipError_t run_scan_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v
 size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W) {
   (void)dv;
   const FusedGeom G = make_geom(T, W);
-  return state_elems(G, B, H, dk) * (sizeof(float) + sizeof(uint16_t)) +
+  return state_elems(G, B, H, dk) * 2 * sizeof(uint16_t) +
          (size_t)B * H * dk * G.Tp * sizeof(uint16_t);
 }
 
