@@ -37,6 +37,7 @@ constexpr int NWAVE = 8;
 constexpr int NTHR = 64 * NWAVE;
 constexpr int MQ = 32 * NWAVE;  // queries per tile (must match the main kernel)
 constexpr long kPrepassWorkgroups = 256;  // MI355X: 256 CUs
+constexpr int kComputeUnits = 256;
 
 // Tiles and their evictions; V^T copy geometry.
 struct FusedGeom {
@@ -283,9 +284,9 @@ __global__ void fused_prefix_kernel(const float* __restrict__ lam, int H, int D,
 // same pre-pass and prefix: per 256-query tile p with entering state S_n
 // (bf16 S^T) and evictions k_c, v_c = keys t0 - W + c,
 //   m_r = lam^(r+1) q_r S_n + sum_{c <= r} eta lam^(r-c) <q_r, k_c> v_c.
-// One workgroup (8 waves) per (tile, b, h); K (256 rows), V^T (256 columns,
-// from the pre-pass copy) and S^T are staged whole in LDS (160 KiB at
-// d = 128).  v_mfma_f32_16x16x32_bf16 (A: lane m + 16 (k / 8), B: lane
+// A workgroup (8 waves) handles one (tile, b, h) at a time; K (256 rows), V^T
+// (256 columns, from the pre-pass copy) and S^T are staged whole in LDS
+// (160 KiB at d = 128).  v_mfma_f32_16x16x32_bf16 (A: lane m + 16 (k / 8), B: lane
 // n + 16 (k / 8), eight consecutive k per lane; D: lane n + 16 (m / 4),
 // element m % 4):
 //   O^T  = S^T Q^T                         (then column r scaled by lam^(r+1)),
@@ -305,6 +306,77 @@ __device__ __forceinline__ int rpos(int r, int c) {  // element offset of chunk 
   return (r * NCH + (c ^ rswz<NCH>(r))) * 8;
 }
 
+// Global operands of one (tile, b, h) unit that go through LDS, in 16-byte
+// pieces (every thread the same count): the K rows, loaded one unit ahead,
+// and (ReadLateRegs) the V^T columns and S^T, loaded at the top of the unit.
+template <int D>
+struct ReadUnitRegs {
+  static constexpr int NCK = D / 8, NCV = MQ / 8, NKS = D / 32;
+  static constexpr int NLK = MQ * NCK / NTHR, NLV = D * NCV / NTHR, NLS = D * NCK / NTHR;
+  uint4 xk[NLK];
+};
+
+template <int D>
+struct ReadLateRegs {
+  uint4 xv[ReadUnitRegs<D>::NLV], xs[ReadUnitRegs<D>::NLS];
+};
+
+template <int D>
+__device__ __forceinline__ void load_read_late(ReadLateRegs<D>& L, const uint16_t* __restrict__ vt,
+                                               const uint16_t* __restrict__ sst, const FusedGeom& G, int p,
+                                               int bh) {
+  using RU = ReadUnitRegs<D>;
+  const int j0 = MQ * p - G.W;
+#pragma unroll
+  for (int u = 0; u < RU::NLV; ++u) {  // V^T rows: key j0 + c at column j0 + c + voff
+    const int i = u * NTHR + threadIdx.x, dv = i / RU::NCV, ch = i % RU::NCV, col = j0 + G.voff + 8 * ch;
+    L.xv[u] = make_uint4(0u, 0u, 0u, 0u);
+    if (col >= 0 && col + 8 <= G.Tp) L.xv[u] = *reinterpret_cast<const uint4*>(vt + ((long)bh * D + dv) * G.Tp + col);
+  }
+  const uint16_t* sp = sst + ((long)bh * G.n_tiles + p) * D * D;
+#pragma unroll
+  for (int u = 0; u < RU::NLS; ++u) {
+    const int i = u * NTHR + threadIdx.x;
+    L.xs[u] = *reinterpret_cast<const uint4*>(sp + (i / RU::NCK) * D + 8 * (i % RU::NCK));
+  }
+}
+
+// Q^T operand: lane (n, g) holds q[query][32 ks + 8 g .. + 7]
+template <int D>
+__device__ __forceinline__ void load_read_q(bf16x8 (&qb)[2][D / 32], const uint16_t* __restrict__ q,
+                                            int T, int t0, int bh, int r0) {
+  const int l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int t = t0 + r0 + 16 * nt + n;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (t < T) x = *reinterpret_cast<const uint4*>(q + ((long)bh * T + t) * D + 32 * ks + 8 * g);
+      qb[nt][ks] = as_bf16x8(x);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_read_unit(ReadUnitRegs<D>& R, const uint16_t* __restrict__ k,
+                                               const FusedGeom& G, int p, int bh) {
+  using RU = ReadUnitRegs<D>;
+  const int T = G.T, t0 = MQ * p, j0 = t0 - G.W;
+#pragma unroll
+  for (int u = 0; u < RU::NLK; ++u) {  // K rows c: key j0 + c
+    const int i = u * NTHR + threadIdx.x, c = i / RU::NCK, ch = i % RU::NCK, j = j0 + c;
+    R.xk[u] = make_uint4(0u, 0u, 0u, 0u);
+    if (j >= 0 && j < T) R.xk[u] = *reinterpret_cast<const uint4*>(k + ((long)bh * T + j) * D + 8 * ch);
+  }
+}
+
+// Persistent: workgroup i takes the units i, i + gridDim.x, ... (unit =
+// tile + n_tiles * bh).  The next unit's K rows are loaded before the
+// current unit's MFMAs and wait in registers until the LDS is free; V^T, S^T
+// and Q are loaded at the top of their unit.  (Loading more of the next unit
+// ahead, or loading V^T and S^T ahead of the current unit's stores, made the
+// compiler spill: slower.)
 template <int D>
 __global__ __launch_bounds__(NTHR) void scan_read_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
@@ -312,138 +384,116 @@ __global__ __launch_bounds__(NTHR) void scan_read_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ sst,
                                                          const float* __restrict__ lam,
                                                          const float* __restrict__ eta, int H,
-                                                         FusedGeom G, float* __restrict__ m) {
-  constexpr int NCK = D / 8;   // chunks per K / S^T row
-  constexpr int NCV = MQ / 8;  // chunks per V^T row
-  constexpr int NKS = D / 32;  // k-steps over d
+                                                         FusedGeom G, int n_units, float* __restrict__ m) {
+  using RU = ReadUnitRegs<D>;
+  constexpr int NCK = RU::NCK, NCV = RU::NCV, NKS = RU::NKS;
   __shared__ __attribute__((aligned(16))) uint16_t sK[MQ * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[D * MQ];
   __shared__ __attribute__((aligned(16))) uint16_t sS[D * D];
-  const int p = blockIdx.x, bh = blockIdx.y;
-  const int T = G.T, t0 = MQ * p, j0 = t0 - G.W;
-  // every load of the tile is issued before the first LDS store
-  constexpr int NLK = MQ * NCK / NTHR, NLV = D * NCV / NTHR, NLS = D * NCK / NTHR;
-  uint4 xk[NLK], xv[NLV], xs[NLS];
-#pragma unroll
-  for (int u = 0; u < NLK; ++u) {  // K rows c: key j0 + c
-    const int i = u * NTHR + threadIdx.x, c = i / NCK, ch = i % NCK, j = j0 + c;
-    xk[u] = make_uint4(0u, 0u, 0u, 0u);
-    if (j >= 0 && j < T) xk[u] = *reinterpret_cast<const uint4*>(k + ((long)bh * T + j) * D + 8 * ch);
-  }
-#pragma unroll
-  for (int u = 0; u < NLV; ++u) {  // V^T rows: key j0 + c at column j0 + c + voff
-    const int i = u * NTHR + threadIdx.x, dv = i / NCV, ch = i % NCV, col = j0 + G.voff + 8 * ch;
-    xv[u] = make_uint4(0u, 0u, 0u, 0u);
-    if (col >= 0 && col + 8 <= G.Tp) xv[u] = *reinterpret_cast<const uint4*>(vt + ((long)bh * D + dv) * G.Tp + col);
-  }
-  const uint16_t* sp = sst + ((long)bh * G.n_tiles + p) * D * D;
-#pragma unroll
-  for (int u = 0; u < NLS; ++u) {
-    const int i = u * NTHR + threadIdx.x;
-    xs[u] = *reinterpret_cast<const uint4*>(sp + (i / NCK) * D + 8 * (i % NCK));
-  }
-
+  const int T = G.T;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
   const int grp = w < 4 ? w : 11 - w;  // 32-query row group of this wave
   const int r0 = 32 * grp;
-  // Q^T operand: lane (n, g) holds q[query][32 ks + 8 g .. + 7]
-  bf16x8 qb[2][NKS];
+  int unit = blockIdx.x;
+  if (unit >= n_units) return;  // uniform over the workgroup
+  ReadUnitRegs<D> R;
+  load_read_unit<D>(R, k, G, unit % G.n_tiles, unit / G.n_tiles);
+  for (; unit < n_units; unit += gridDim.x) {
+    const int p = unit % G.n_tiles, bh = unit / G.n_tiles, t0 = MQ * p;
+    ReadLateRegs<D> L;
+    load_read_late<D>(L, vt, sst, G, p, bh);
+    bf16x8 qb[2][NKS];
+    load_read_q<D>(qb, q, T, t0, bh, r0);
+    __syncthreads();  // the previous unit's LDS reads are done
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int t = t0 + r0 + 16 * nt + n;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 x = make_uint4(0u, 0u, 0u, 0u);
-      if (t < T) x = *reinterpret_cast<const uint4*>(q + ((long)bh * T + t) * D + 32 * ks + 8 * g);
-      qb[nt][ks] = as_bf16x8(x);
+    for (int u = 0; u < RU::NLK; ++u) {
+      const int i = u * NTHR + threadIdx.x;
+      *reinterpret_cast<uint4*>(sK + rpos<NCK>(i / NCK, i % NCK)) = R.xk[u];
     }
-  }
 #pragma unroll
-  for (int u = 0; u < NLK; ++u) {
-    const int i = u * NTHR + threadIdx.x;
-    *reinterpret_cast<uint4*>(sK + rpos<NCK>(i / NCK, i % NCK)) = xk[u];
-  }
+    for (int u = 0; u < RU::NLV; ++u) {
+      const int i = u * NTHR + threadIdx.x;
+      *reinterpret_cast<uint4*>(sV + rpos<NCV>(i / NCV, i % NCV)) = L.xv[u];
+    }
 #pragma unroll
-  for (int u = 0; u < NLV; ++u) {
-    const int i = u * NTHR + threadIdx.x;
-    *reinterpret_cast<uint4*>(sV + rpos<NCV>(i / NCV, i % NCV)) = xv[u];
-  }
-#pragma unroll
-  for (int u = 0; u < NLS; ++u) {
-    const int i = u * NTHR + threadIdx.x;
-    *reinterpret_cast<uint4*>(sS + rpos<NCK>(i / NCK, i % NCK)) = xs[u];
-  }
-  __syncthreads();
+    for (int u = 0; u < RU::NLS; ++u) {
+      const int i = u * NTHR + threadIdx.x;
+      *reinterpret_cast<uint4*>(sS + rpos<NCK>(i / NCK, i % NCK)) = L.xs[u];
+    }
+    __syncthreads();
+    const int next = unit + gridDim.x;
+    if (next < n_units) load_read_unit<D>(R, k, G, next % G.n_tiles, next / G.n_tiles);
 
-  const Decay dec(lam[bh % H]);
-  const float et = eta[bh % H];
-  floatx4 o[D / 16][2];
-  // state term, then column r scaled by lam^(r+1)
-#pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt) {
-    o[mt][0] = zero4();
-    o[mt][1] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sS + rpos<NCK>(16 * mt + n, 4 * ks + g)));
-      o[mt][0] = mfma_bf16_16x16x32(a, qb[0][ks], o[mt][0]);
-      o[mt][1] = mfma_bf16_16x16x32(a, qb[1][ks], o[mt][1]);
-    }
-  }
-  {
-    const float f0 = dec(r0 + n + 1), f1 = dec(r0 + 16 + n + 1);
+    const Decay dec(lam[bh % H]);
+    const float et = eta[bh % H];
+    floatx4 o[D / 16][2];
+    // state term, then column r scaled by lam^(r+1)
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt) {
-      o[mt][0] *= f0;
-      o[mt][1] *= f1;
-    }
-  }
-  // evictions of the tile, 32 keys per step, up to this wave's last query
-  for (int st = 0; st <= grp; ++st) {
-    floatx4 sc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};  // [key half][query tile]
+      o[mt][0] = zero4();
+      o[mt][1] = zero4();
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int row = 32 * st + 8 * (n >> 2) + (n & 3) + 4 * hf;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sK + rpos<NCK>(row, 4 * ks + g)));
-        sc[hf][0] = mfma_bf16_16x16x32(a, qb[0][ks], sc[hf][0]);
-        sc[hf][1] = mfma_bf16_16x16x32(a, qb[1][ks], sc[hf][1]);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sS + rpos<NCK>(16 * mt + n, 4 * ks + g)));
+        o[mt][0] = mfma_bf16_16x16x32(a, qb[0][ks], o[mt][0]);
+        o[mt][1] = mfma_bf16_16x16x32(a, qb[1][ks], o[mt][1]);
       }
     }
-    bf16x8 pb[2];
+    {
+      const float f0 = dec(r0 + n + 1), f1 = dec(r0 + 16 + n + 1);
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        o[mt][0] *= f0;
+        o[mt][1] *= f1;
+      }
+    }
+    // evictions of the tile, 32 keys per step, up to this wave's last query
+    for (int st = 0; st <= grp; ++st) {
+      floatx4 sc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};  // [key half][query tile]
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int row = 32 * st + 8 * (n >> 2) + (n & 3) + 4 * hf;
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sK + rpos<NCK>(row, 4 * ks + g)));
+          sc[hf][0] = mfma_bf16_16x16x32(a, qb[0][ks], sc[hf][0]);
+          sc[hf][1] = mfma_bf16_16x16x32(a, qb[1][ks], sc[hf][1]);
+        }
+      }
+      bf16x8 pb[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int dr = r0 + 16 * nt + n - (32 * st + 8 * g);  // r - c of element (hf, e) is dr - 4 hf - e
+        uint32_t pk[4];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const floatx4 x = sc[hf][nt];
+          const float w0 = dr - 4 * hf >= 0 ? et * dec(dr - 4 * hf) * x[0] : 0.f;
+          const float w1 = dr - 4 * hf - 1 >= 0 ? et * dec(dr - 4 * hf - 1) * x[1] : 0.f;
+          const float w2 = dr - 4 * hf - 2 >= 0 ? et * dec(dr - 4 * hf - 2) * x[2] : 0.f;
+          const float w3 = dr - 4 * hf - 3 >= 0 ? et * dec(dr - 4 * hf - 3) * x[3] : 0.f;
+          pk[2 * hf] = cvt_pk(w0, w1);
+          pk[2 * hf + 1] = cvt_pk(w2, w3);
+        }
+        pb[nt] = as_bf16x8(pk[0], pk[1], pk[2], pk[3]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sV + rpos<NCV>(16 * mt + n, 4 * st + g)));
+        o[mt][0] = mfma_bf16_16x16x32(a, pb[0], o[mt][0]);
+        o[mt][1] = mfma_bf16_16x16x32(a, pb[1], o[mt][1]);
+      }
+    }
+    // O^T element (dv = 16 mt + 4 g + e, query r0 + 16 nt + n)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int dr = r0 + 16 * nt + n - (32 * st + 8 * g);  // r - c of element (hf, e) is dr - 4 hf - e
-      uint32_t pk[4];
+      const int t = t0 + r0 + 16 * nt + n;
+      if (t >= T) continue;
+      float* out = m + ((long)bh * T + t) * D + 4 * g;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const floatx4 x = sc[hf][nt];
-        const float w0 = dr - 4 * hf >= 0 ? et * dec(dr - 4 * hf) * x[0] : 0.f;
-        const float w1 = dr - 4 * hf - 1 >= 0 ? et * dec(dr - 4 * hf - 1) * x[1] : 0.f;
-        const float w2 = dr - 4 * hf - 2 >= 0 ? et * dec(dr - 4 * hf - 2) * x[2] : 0.f;
-        const float w3 = dr - 4 * hf - 3 >= 0 ? et * dec(dr - 4 * hf - 3) * x[3] : 0.f;
-        pk[2 * hf] = cvt_pk(w0, w1);
-        pk[2 * hf + 1] = cvt_pk(w2, w3);
-      }
-      pb[nt] = as_bf16x8(pk[0], pk[1], pk[2], pk[3]);
+      for (int mt = 0; mt < D / 16; ++mt)
+        *reinterpret_cast<float4*>(out + 16 * mt) = make_float4(o[mt][nt][0], o[mt][nt][1], o[mt][nt][2], o[mt][nt][3]);
     }
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(sV + rpos<NCV>(16 * mt + n, 4 * st + g)));
-      o[mt][0] = mfma_bf16_16x16x32(a, pb[0], o[mt][0]);
-      o[mt][1] = mfma_bf16_16x16x32(a, pb[1], o[mt][1]);
-    }
-  }
-  // O^T element (dv = 16 mt + 4 g + e, query r0 + 16 nt + n)
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int t = t0 + r0 + 16 * nt + n;
-    if (t >= T) continue;
-    float* out = m + ((long)bh * T + t) * D + 4 * g;
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt)
-      *reinterpret_cast<float4*>(out + 16 * mt) = make_float4(o[mt][nt][0], o[mt][nt][1], o[mt][nt][2], o[mt][nt][3]);
   }
 }
 
@@ -506,7 +556,10 @@ hipError_t run_scan_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v
   hipLaunchKernelGGL(fused_prefix_kernel, dim3((D * D / 4 + 63) / 64, BH), dim3(64), 0, s, lam, H, D,
                      G, delta, sst, A_final);
   profile_mark_before(s);
-  hipLaunchKernelGGL(scan_read_kernel<D>, dim3(G.n_tiles, BH), dim3(NTHR), 0, s, q, k, vt, sst, lam, eta, H, G, m);
+  // persistent: as many workgroups as fit at once (LDS: one per CU at d = 128, two at d = 64)
+  const int n_units = G.n_tiles * BH;
+  const int grid = std::min<int>(n_units, kComputeUnits * (D == 128 ? 1 : 2));
+  hipLaunchKernelGGL(scan_read_kernel<D>, dim3(grid), dim3(NTHR), 0, s, q, k, vt, sst, lam, eta, H, G, n_units, m);
   profile_mark_after(s);
   return hipGetLastError();
 }

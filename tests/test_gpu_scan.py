@@ -93,6 +93,11 @@ def test_scan_fused_size_bf16_sampled_rows():
     (1, 3, 1000, 64, 300),     # several tiles, W not a multiple of 8
     (2, 2, 2049, 128, 1024),   # many tiles, ragged last tile
     (1, 1, 513, 64, 7),
+    # more (tile, b, h) units than the read kernel's persistent grid (256
+    # workgroups at d = 128, 512 at d = 64): some workgroups take a second
+    # unit, with its K rows loaded during the first
+    (1, 3, 256 * 90 + 77, 128, 1000),
+    (2, 2, 256 * 130 + 5, 64, 64),
 ])
 def test_scan_bf16_tiled_path(B, H, T, d, W):
     # bf16 inputs with d in {64, 128} run on the fused layer's pre-pass and
