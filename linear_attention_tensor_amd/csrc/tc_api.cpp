@@ -97,7 +97,7 @@ size_t tc_scan_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int c
     return SIZE_MAX;
   }
   ok();
-  if (tc::scan_bf16_fast(dt == TC_BF16, dk, dv, T)) return tc::fused_ws_bytes(B, H, T, dk, dv, W);
+  if (tc::scan_bf16_fast(dt == TC_BF16, dk, dv, T)) return tc::scan_bf16_ws_bytes(B, H, T, dk, W);
   return tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
 }
 
@@ -115,7 +115,7 @@ tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype 
     if (T > 0 && (!q || !k || !v || !m))
       return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, m must not be NULL", fn);
     const bool fast16 = tc::scan_bf16_fast(dt == TC_BF16, dk, dv, T);
-    const size_t need = fast16 ? tc::fused_ws_bytes(B, H, T, dk, dv, W)
+    const size_t need = fast16 ? tc::scan_bf16_ws_bytes(B, H, T, dk, W)
                                : tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
     if (ws_bytes < need)
       return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);

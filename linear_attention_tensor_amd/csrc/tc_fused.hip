@@ -11,14 +11,15 @@
 //   fused_state   per (tile, b, h): the tile's own contribution to the
 //                 state, from zero, delta_p = sum_c eta lam^(L-1-c) v_c k_c^T
 //                 (S^T layout, bf16 MFMA with fp32 accumulation, stored as
-//                 bf16); it also
-//                 writes V^T (per head [d][Tp] bf16) into the workspace, so
-//                 that the main kernel can copy V^T blocks straight to LDS;
+//                 bf16); for the layer it also writes V^T (per head [d][Tp]
+//                 bf16) into the workspace, so that the main kernel can copy
+//                 V^T blocks straight to LDS;
 //   fused_prefix  S_0 = 0, S_{p+1} = lam^L_p S_p + delta_p, carried in fp32:
 //                 the state entering every tile (bf16) and the final state A
 //                 (fp32);
 //   swa           per (tile, b, h): window softmax plus the L2 read.
-// Workspace: delta (bf16) | entering states (bf16) | V^T copy (bf16).
+// Workspace: delta (bf16) | entering states (bf16) | V^T copy (bf16, the
+// layer only).
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
 #include "tc_mfma.hpp"
@@ -56,14 +57,15 @@ struct FusedGeom {
     return (int)(b < 0 ? 0 : b);
   }
   // copy columns the pre-pass visits for tile p (keys are column - voff): at
-  // least one 64-column block; the last tile runs to Tp, and together the
-  // tiles cover every column of the copy.
+  // least one 64-column block; with the copy, the last tile runs to Tp, and
+  // together the tiles cover every column of the copy.
   __host__ __device__ int col_begin(int p) const { return (key_begin(p) + voff) & ~(KB - 1); }
   __host__ __device__ int col_end(int p) const {
-    const int e = p == n_tiles - 1 ? Tp : ((key_end(p) + voff + KB - 1) & ~(KB - 1));
+    const int e = (vt_copy && p == n_tiles - 1) ? Tp : ((key_end(p) + voff + KB - 1) & ~(KB - 1));
     return e > col_begin(p) ? e : col_begin(p) + KB;
   }
   int tiles_per_seg;  // tiles one pre-pass workgroup walks through
+  int vt_copy;        // 1: the pre-pass writes the V^T copy
 };
 
 // Distribution of the fp32 state S^T (D x D, 32x32 tiles) over the waves.
@@ -129,7 +131,7 @@ __device__ __forceinline__ void store_pair(const PairRegs& p, uint16_t* skt, uin
     *reinterpret_cast<uint32_t*>(skt + (c8 + 2 * e + 1) * SKT + row) = (ka[e] >> 16) | (kb[e] & 0xFFFF0000u);
     *reinterpret_cast<uint32_t*>(svt + (c8 + 2 * e) * SKT + row) = cvt_pk(lo_f(va[e]) * w0, lo_f(vb[e]) * w1);
     *reinterpret_cast<uint32_t*>(svt + (c8 + 2 * e + 1) * SKT + row) = cvt_pk(hi_f(va[e]) * w0, hi_f(vb[e]) * w1);
-    if (cc < Tp) {  // cc is even and Tp a multiple of 64: the pair is in range
+    if (vt_out != nullptr && cc < Tp) {  // cc is even and Tp a multiple of 64: the pair is in range
       *reinterpret_cast<uint32_t*>(vt_out + (long)(c8 + 2 * e) * Tp + cc) = vlo;
       *reinterpret_cast<uint32_t*>(vt_out + (long)(c8 + 2 * e + 1) * Tp + cc) = vhi;
     }
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __res
   const float et = eta[bh % H];
   const long base = (long)bh * G.T;
   const int voff = G.voff;
-  uint16_t* vt_out = ws_vt + (long)bh * D * G.Tp;
+  uint16_t* vt_out = G.vt_copy ? ws_vt + (long)bh * D * G.Tp : nullptr;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base * D, (uint32_t)G.T * D * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base * D, (uint32_t)G.T * D * 2);
 
@@ -285,8 +287,9 @@ __global__ void fused_prefix_kernel(const float* __restrict__ lam, int H, int D,
 // (bf16 S^T) and evictions k_c, v_c = keys t0 - W + c,
 //   m_r = lam^(r+1) q_r S_n + sum_{c <= r} eta lam^(r-c) <q_r, k_c> v_c.
 // A workgroup (8 waves) handles one (tile, b, h) at a time; K (256 rows), V^T
-// (256 columns, from the pre-pass copy) and S^T are staged whole in LDS
-// (160 KiB at d = 128).  v_mfma_f32_16x16x32_bf16 (A: lane m + 16 (k / 8), B: lane
+// (256 columns, transposed from the V rows on their way to LDS) and S^T are
+// staged whole in LDS (160 KiB at d = 128); the pre-pass writes no V^T copy
+// here.  v_mfma_f32_16x16x32_bf16 (A: lane m + 16 (k / 8), B: lane
 // n + 16 (k / 8), eight consecutive k per lane; D: lane n + 16 (m / 4),
 // element m % 4):
 //   O^T  = S^T Q^T                         (then column r scaled by lam^(r+1)),
@@ -308,30 +311,42 @@ __device__ __forceinline__ int rpos(int r, int c) {  // element offset of chunk 
 
 // Global operands of one (tile, b, h) unit that go through LDS, in 16-byte
 // pieces (every thread the same count): the K rows, loaded one unit ahead,
-// and (ReadLateRegs) the V^T columns and S^T, loaded at the top of the unit.
+// and (ReadLateRegs) the V rows and S^T, loaded at the top of the unit.
 template <int D>
 struct ReadUnitRegs {
   static constexpr int NCK = D / 8, NCV = MQ / 8, NKS = D / 32;
-  static constexpr int NLK = MQ * NCK / NTHR, NLV = D * NCV / NTHR, NLS = D * NCK / NTHR;
+  static constexpr int NLK = MQ * NCK / NTHR, NLS = D * NCK / NTHR;
+  static constexpr int NIV = D / 32;  // V items per thread: two keys x 8 columns
   uint4 xk[NLK];
 };
 
+// V item u of a thread: keys 2 kp and 2 kp + 1 (kp = 16 w + l % 16, relative
+// to the tile's first eviction) at columns 8 ch .. 8 ch + 7 (ch = 4 u + l / 16).
+// Stored transposed (S^T-like [d_v][key] layout, key pairs as 4-byte words),
+// the 64 lanes of a store hit 64 different banks: the word's bank is
+// 4 ((kp / 4) ^ rswz(d_v)) % 16 + kp % 4, and rswz(d_v) carries ch % 4 in its
+// upper two bits.
 template <int D>
 struct ReadLateRegs {
-  uint4 xv[ReadUnitRegs<D>::NLV], xs[ReadUnitRegs<D>::NLS];
+  uint4 xv[2 * ReadUnitRegs<D>::NIV], xs[ReadUnitRegs<D>::NLS];
 };
 
 template <int D>
-__device__ __forceinline__ void load_read_late(ReadLateRegs<D>& L, const uint16_t* __restrict__ vt,
+__device__ __forceinline__ void load_read_late(ReadLateRegs<D>& L, const uint16_t* __restrict__ v,
                                                const uint16_t* __restrict__ sst, const FusedGeom& G, int p,
                                                int bh) {
   using RU = ReadUnitRegs<D>;
-  const int j0 = MQ * p - G.W;
+  const int T = G.T, j0 = MQ * p - G.W;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, kp = 16 * w + (l & 15);
 #pragma unroll
-  for (int u = 0; u < RU::NLV; ++u) {  // V^T rows: key j0 + c at column j0 + c + voff
-    const int i = u * NTHR + threadIdx.x, dv = i / RU::NCV, ch = i % RU::NCV, col = j0 + G.voff + 8 * ch;
-    L.xv[u] = make_uint4(0u, 0u, 0u, 0u);
-    if (col >= 0 && col + 8 <= G.Tp) L.xv[u] = *reinterpret_cast<const uint4*>(vt + ((long)bh * D + dv) * G.Tp + col);
+  for (int u = 0; u < RU::NIV; ++u) {
+    const int ch = 4 * u + (l >> 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // keys outside [0, T) read as zero
+      const int j = j0 + 2 * kp + h;
+      L.xv[2 * u + h] = make_uint4(0u, 0u, 0u, 0u);
+      if (j >= 0 && j < T) L.xv[2 * u + h] = *reinterpret_cast<const uint4*>(v + ((long)bh * T + j) * D + 8 * ch);
+    }
   }
   const uint16_t* sp = sst + ((long)bh * G.n_tiles + p) * D * D;
 #pragma unroll
@@ -380,7 +395,7 @@ __device__ __forceinline__ void load_read_unit(ReadUnitRegs<D>& R, const uint16_
 template <int D>
 __global__ __launch_bounds__(NTHR) void scan_read_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ vt,
+                                                         const uint16_t* __restrict__ v,
                                                          const uint16_t* __restrict__ sst,
                                                          const float* __restrict__ lam,
                                                          const float* __restrict__ eta, int H,
@@ -401,7 +416,7 @@ __global__ __launch_bounds__(NTHR) void scan_read_kernel(const uint16_t* __restr
   for (; unit < n_units; unit += gridDim.x) {
     const int p = unit % G.n_tiles, bh = unit / G.n_tiles, t0 = MQ * p;
     ReadLateRegs<D> L;
-    load_read_late<D>(L, vt, sst, G, p, bh);
+    load_read_late<D>(L, v, sst, G, p, bh);
     bf16x8 qb[2][NKS];
     load_read_q<D>(qb, q, T, t0, bh, r0);
     __syncthreads();  // the previous unit's LDS reads are done
@@ -410,10 +425,21 @@ __global__ __launch_bounds__(NTHR) void scan_read_kernel(const uint16_t* __restr
       const int i = u * NTHR + threadIdx.x;
       *reinterpret_cast<uint4*>(sK + rpos<NCK>(i / NCK, i % NCK)) = R.xk[u];
     }
+    {
+      const int kp = 16 * w + (l & 15);
 #pragma unroll
-    for (int u = 0; u < RU::NLV; ++u) {
-      const int i = u * NTHR + threadIdx.x;
-      *reinterpret_cast<uint4*>(sV + rpos<NCV>(i / NCV, i % NCV)) = L.xv[u];
+      for (int u = 0; u < RU::NIV; ++u) {
+        const int ch = 4 * u + (l >> 4);
+        const uint4 xa = L.xv[2 * u], xb = L.xv[2 * u + 1];
+        const uint32_t a[4] = {xa.x, xa.y, xa.z, xa.w}, b[4] = {xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dv = 8 * ch + 2 * e;
+          *reinterpret_cast<uint32_t*>(sV + rpos<NCV>(dv, kp >> 2) + 2 * (kp & 3)) = (a[e] & 0xFFFFu) | (b[e] << 16);
+          *reinterpret_cast<uint32_t*>(sV + rpos<NCV>(dv + 1, kp >> 2) + 2 * (kp & 3)) =
+              (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < RU::NLS; ++u) {
@@ -505,6 +531,7 @@ FusedGeom make_geom(int T, int W) {
   G.Tp = (T + G.voff + KB - 1) / KB * KB;
   G.n_tiles = (T + MQ - 1) / MQ;
   G.tiles_per_seg = 1;
+  G.vt_copy = 1;
   return G;
 }
 
@@ -546,22 +573,27 @@ hipError_t run_scan_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v
   const size_t ne = state_elems(G, B, H, D);
   uint16_t* delta = static_cast<uint16_t*>(ws);
   uint16_t* sst = delta + ne;
-  uint16_t* vt = sst + ne;
+  // the read kernel transposes V itself: no V^T copy
   FusedGeom Gs = G;
+  Gs.vt_copy = 0;
   const long units = (long)G.n_tiles * BH;
   Gs.tiles_per_seg = (int)std::max<long>(1, (units + kPrepassWorkgroups - 1) / kPrepassWorkgroups);
   const int n_seg = (G.n_tiles + Gs.tiles_per_seg - 1) / Gs.tiles_per_seg;
   hipLaunchKernelGGL(fused_state_kernel<D>, dim3(n_seg, BH), dim3(NTHR), 0, s, k, v, lam, eta, H, Gs,
-                     delta, vt);
+                     delta, static_cast<uint16_t*>(nullptr));
   hipLaunchKernelGGL(fused_prefix_kernel, dim3((D * D / 4 + 63) / 64, BH), dim3(64), 0, s, lam, H, D,
                      G, delta, sst, A_final);
   profile_mark_before(s);
   // persistent: as many workgroups as fit at once (LDS: one per CU at d = 128, two at d = 64)
   const int n_units = G.n_tiles * BH;
   const int grid = std::min<int>(n_units, kComputeUnits * (D == 128 ? 1 : 2));
-  hipLaunchKernelGGL(scan_read_kernel<D>, dim3(grid), dim3(NTHR), 0, s, q, k, vt, sst, lam, eta, H, G, n_units, m);
+  hipLaunchKernelGGL(scan_read_kernel<D>, dim3(grid), dim3(NTHR), 0, s, q, k, v, sst, lam, eta, H, G, n_units, m);
   profile_mark_after(s);
   return hipGetLastError();
+}
+
+size_t scan_bf16_ws_bytes(int B, int H, int T, int d, int W) {
+  return state_elems(make_geom(T, W), B, H, d) * 2 * sizeof(uint16_t);
 }
 
 size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W) {

@@ -49,8 +49,9 @@ void profile_mark_after(hipStream_t s);
 
 size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W);
 // tc_scan_forward with bf16 inputs and d in {64, 128} runs on the fused
-// layer's pre-pass and prefix plus an L2-read kernel (tc_fused.hip); its
-// workspace is fused_ws_bytes.
+// layer's pre-pass (without the V^T copy) and prefix plus an L2-read kernel
+// (tc_fused.hip); its workspace is scan_bf16_ws_bytes.
+size_t scan_bf16_ws_bytes(int B, int H, int T, int d, int W);
 bool scan_bf16_fast(bool bf16, int dk, int dv, int T);
 hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, const float* lam, const float* eta,
                                int B, int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s);
