@@ -151,6 +151,33 @@ def time_calls(fn, steps, warmup, kernel_timer=None):
     return total / steps, sum(per) / len(per), kernel_ms
 
 
+def graph_ms_per_step(launch, n, reps=3):
+    """Mean time per step of n consecutive steps captured in one HIP graph
+    (torch.cuda.CUDAGraph) and replayed reps times, after one untimed replay:
+    the launch gaps between steps shrink to the graph's.  launch(i, stream)
+    issues step i on the given stream."""
+    import torch
+
+    from linear_attention_tensor_amd import ops
+
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        st = ops._stream()  # the capturing stream
+        for i in range(n):
+            launch(i, st)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * n)
+
+
 class KernelTimer:
     """HIP events recorded by the library around an entry point's main kernel
     (tc_profile_next_call), on the stream that kernel is launched on."""
@@ -425,11 +452,26 @@ def bench_decode(steps, warmup, dev, n_steps=4096):
 
     # warmup steps advance the stream position too; the timed steps continue from there
     ms, ms_call, kernel_ms = time_calls(call, n_steps, warmup, KernelTimer(n_steps))
+    # the same steps as one HIP graph (positions continue after the eager ones;
+    # every replay repeats them, each step still evicting and writing one slot)
+    posg = (W + n_steps + warmup + torch.arange(n_steps, device=dev, dtype=torch.int64))[:, None].repeat(1, B)
+    posg = posg.contiguous()
+    pg = [P(posg[i]) for i in range(n_steps)]
+
+    def launch(i, stream):
+        s = lib.tc_decode_step(qp[i], kp[i], vp[i], 1, rk, rv, Ap, lp, ep, pg[i], B, H, d, d, W, mp, stream)
+        if s != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms_graph = graph_ms_per_step(launch, n_steps)
     per_head = decode_bytes_per_head(d)
     gbs = B * H * per_head / (kernel_ms * 1e-3) / 1e9
-    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": B * H / (ms * 1e-3),
+    return {"workload": w.name, "ms_per_step": ms_graph, "tokens_per_s": B * H / (ms_graph * 1e-3),
+            "ms_per_step_eager": ms, "tokens_per_s_eager": B * H / (ms * 1e-3),
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
-            "note": "A (128 MiB) fits the 256 MB Infinity Cache; GB/s is algorithmic bytes / kernel time",
+            "note": "ms_per_step: the 4096 steps replayed as one HIP graph; eager: one launch per step with "
+                    "per-step events. A (128 MiB) fits the 256 MB Infinity Cache; GB/s is algorithmic "
+                    "bytes / kernel time",
             "main_kernel": {"name": "decode_kernel", "ms": kernel_ms}, "ms_per_call": ms_call,
             "config": {"B": B, "H": H, "d": d, "W": W, "steps": n_steps, "dtype_in": "bf16"}}
 
@@ -479,11 +521,26 @@ def bench_decode_layer(steps, warmup, dev, n_steps=256):
             raise RuntimeError(ops._lib.last_error())
 
     ms, ms_call, kernel_ms = time_calls(call, n_steps, warmup, KernelTimer(n_steps))
+    posg = (W + n_steps + warmup + torch.arange(n_steps, device=dev, dtype=torch.int64))[:, None].repeat(1, B)
+    posg = posg.contiguous()
+    pg = [P(posg[i]) for i in range(n_steps)]
+
+    def launch(i, stream):
+        s = lib.tc_decode_layer_step(qp[i], kp[i], vp[i], 1, rk, rv, Ap, lp, ep, gp, pg[i], B, H, d, d, W,
+                                     scale, yp, stream)
+        if s != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms_graph = graph_ms_per_step(launch, n_steps)
     per_head = decode_layer_bytes_per_head(d, W)
     gbs = B * H * per_head / (kernel_ms * 1e-3) / 1e9
-    return {"workload": w.name + " (full layer step)", "ms_per_step": ms, "tokens_per_s": B * H / (ms * 1e-3),
+    return {"workload": w.name + " (full layer step)", "ms_per_step": ms_graph,
+            "tokens_per_s": B * H / (ms_graph * 1e-3),
+            "ms_per_step_eager": ms, "tokens_per_s_eager": B * H / (ms * 1e-3),
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
-            "note": "per head-step: the ring (2 (W-1) d bf16) plus the L2 step; GB/s is algorithmic bytes / kernel time",
+            "note": "ms_per_step: the steps replayed as one HIP graph; eager: one launch per step with per-step "
+                    "events. Per head-step: the ring (2 (W-1) d bf16) plus the L2 step; GB/s is algorithmic "
+                    "bytes / kernel time",
             "main_kernel": {"name": "decode_layer_kernel", "ms": kernel_ms}, "ms_per_call": ms_call,
             "config": {"B": B, "H": H, "d": d, "W": W, "steps": n_steps, "dtype_in": "bf16"}}
 
