@@ -159,6 +159,37 @@ __device__ __forceinline__ void state_block_mma(floatx16* acc, const uint16_t* s
   }
 }
 
+// A tile's delta (this wave's S^T tiles) into the workspace as bf16.  At
+// d = 128 a wave's two 32x32 tiles cover the same rows and adjacent column
+// blocks (dk0, dk0 + 32): the two halves of the wave trade values (lane
+// c <-> c + 32), so that each store writes 64 consecutive columns (128 bytes)
+// of one row instead of 32.
+template <int D>
+__device__ __forceinline__ void store_delta(uint16_t* __restrict__ out, const floatx16* acc) {
+  using ST = StateTiles<D>;
+  const int w = wave_id(), l = lane_id(), col = l & 31, hh = l >> 5;
+  if constexpr (ST::TPW == 2) {
+    const int dv0 = ST::dv0(w, 0), dk0 = ST::dk0(w, 0);  // tile 1: same rows, columns dk0 + 32 ..
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float a0 = acc[0][e], a1 = acc[1][e];
+      const float s0 = __shfl_xor(a0, 32), s1 = __shfl_xor(a1, 32);
+      const int ra = dv0 + 8 * (e >> 2) + (e & 3);  // row of element e in the lower half
+      uint16_t* p = out + ra * D + dk0 + 32 * hh + col;
+      p[0] = f32_to_bf16(hh ? s1 : a0);      // row ra
+      p[4 * D] = f32_to_bf16(hh ? a1 : s0);  // row ra + 4
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < ST::TPW; ++i) {
+      if (!ST::owns(w, i)) continue;
+      const int dv0 = ST::dv0(w, i), dk0 = ST::dk0(w, i);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) out[(dv0 + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + dk0 + col] = f32_to_bf16(acc[i][e]);
+    }
+  }
+}
+
 // Next (tile, column block) of a pre-pass walk: every tile has >= 1 block.
 __device__ __forceinline__ void next_block(const FusedGeom& G, int& p, int& j) {
   j += KB;
@@ -226,16 +257,8 @@ __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __res
   if (pc < p_end) {                                                                   \
     state_block_mma<D, SKT>(acc, sKt, sVt);                                           \
     if (jc + KB >= G.col_end(pc)) {                                                   \
-      uint16_t* out = ws_state + ((long)bh * G.n_tiles + pc) * D * D;                 \
-      _Pragma("unroll") for (int i = 0; i < ST::TPW; ++i) {                           \
-        if (ST::owns(w, i)) {                                                         \
-          const int dv0 = ST::dv0(w, i), dk0 = ST::dk0(w, i);                         \
-          _Pragma("unroll") for (int e = 0; e < 16; ++e)                              \
-              out[(dv0 + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + dk0 + col] =          \
-                  f32_to_bf16(acc[i][e]);                                             \
-        }                                                                             \
-        acc[i] = zero16();                                                            \
-      }                                                                               \
+      store_delta<D>(ws_state + ((long)bh * G.n_tiles + pc) * D * D, acc);            \
+      _Pragma("unroll") for (int i = 0; i < ST::TPW; ++i) acc[i] = zero16();          \
     }                                                                                 \
     next_block(G, pc, jc);                                                            \
   }
