@@ -364,6 +364,19 @@ __device__ __forceinline__ void load_state(floatx4* acc, const float* src, int d
       acc[i][e] = own && src != nullptr ? src[(long)(16 * b + r) * dv + 16 * a + 4 * g + e] : 0.f;
   }
 }
+// acc = f acc + src over this wave's S^T tiles (src as in load_state)
+template <int D>
+__device__ __forceinline__ void fma_state(floatx4* acc, float f, const float* __restrict__ src, int dv) {
+  using F = FastTiles<D>;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int i = 0; i < F::TPW; ++i) {
+    int a, b;
+    if (!state_tile<D>(w, i, a, b)) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(f, acc[i][e], src[(long)(16 * b + r) * dv + 16 * a + 4 * g + e]);
+  }
+}
 template <int D>
 __device__ __forceinline__ void store_state(float* dst, const floatx4* acc, int dv) {
   using F = FastTiles<D>;
@@ -418,13 +431,17 @@ __global__ __launch_bounds__(256) void scan_state_fast(RowView<const TIn> kv_k, 
   store_state<D>(ws + ((long)bh * n_seg + seg) * D * D, acc, D);
 }
 
-// Per-(segment, b, h): carry the entering state through the segment's
-// chunks and write m (rows W + s).
+// Per-(segment, b, h): the entering state from the earlier segments'
+// contributions (ws, from scan_state_fast; every segment but the last is
+// seg_chunks chunks long), S_in(s) = sum_{s' < s} lam^(L (s-1-s')) U_s'
+// evaluated as a Horner recurrence; then carry it through the segment's
+// chunks and write m (rows W + s).  The segments also clear rows t < zrows
+// (= min(W, T)) of m between them.
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void scan_output_fast(
     RowView<const TIn> vq, RowView<const TIn> vk, RowView<const TIn> vv, const float* __restrict__ lam,
     const float* __restrict__ eta, int H, int n_act, int seg_chunks, int n_seg,
-    const float* __restrict__ ws, RowView<float> vm, float* __restrict__ A_final) {
+    const float* __restrict__ ws, RowView<float> vm, int zrows, float* __restrict__ A_final) {
   using F = FastTiles<D>;
   constexpr int NDV = D / 16;
   __shared__ __attribute__((aligned(16))) float sQ[CH * F::S];
@@ -443,15 +460,25 @@ __global__ __launch_bounds__(256) void scan_output_fast(
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
   if (threadIdx.x <= CH) sPow[threadIdx.x] = pow_int(lm, threadIdx.x);
 
-  floatx4 acc[F::TPW];
-  load_state<D>(acc, n_seg > 1 && seg > 0 ? ws + ((long)bh * n_seg + seg) * D * D : nullptr, D);
-  publish_state<D>(sSt[0], acc);
   float4 xq[F::NV4], xk[F::NV4], xv[F::NV4];
   if (c_begin < c_end) {
     const int s0 = c_begin * CH, L = min(CH, n_act - s0);
     load_rows<D>(xq, vq.row(bh, s0), vq.rs, L);
     load_rows<D>(xk, vk.row(bh, s0), vk.rs, L);
     load_rows<D>(xv, vv.row(bh, s0), vv.rs, L);
+  }
+  floatx4 acc[F::TPW];
+  load_state<D>(acc, nullptr, D);
+  if (seg > 0) {
+    const float lam_seg = pow_int(lm, seg_chunks * CH);
+    for (int sp = 0; sp < seg; ++sp) fma_state<D>(acc, lam_seg, ws + ((long)bh * n_seg + sp) * D * D, D);
+  }
+  publish_state<D>(sSt[0], acc);
+  {  // this segment's share of the rows t < zrows (row s of vm is t = W + s)
+    const int per = (zrows + n_seg - 1) / n_seg, z0 = seg * per, z1 = min(zrows, z0 + per);
+    for (int i = threadIdx.x; i < (z1 - z0) * (D / 4); i += blockDim.x)
+      *reinterpret_cast<float4*>(vm.row(bh, z0 + i / (D / 4) - zrows) + 4 * (i % (D / 4))) =
+          make_float4(0.f, 0.f, 0.f, 0.f);
   }
   for (int c = c_begin; c < c_end; ++c) {
     const int s0 = c * CH, L = min(CH, n_act - s0);
@@ -1035,7 +1062,8 @@ hipError_t run_scan(const TIn* q, const TIn* k, const TIn* v, const float* lam, 
                     const ScanPlan& p, hipStream_t s) {
   const int BH = B * H;
   const long zrows = std::min<long>(W, T);
-  if (zrows > 0) {
+  constexpr bool fast = DK <= 64 && DVT == DK;  // the output kernel clears these rows itself
+  if (zrows > 0 && (!fast || p.n_act <= 0)) {
     dim3 g((unsigned)std::min<long>((zrows * dv + 255) / 256, 1024), BH);
     hipLaunchKernelGGL(zero_rows_kernel, g, dim3(256), 0, s, m, zrows, (long)T, dv);
   }
@@ -1051,16 +1079,12 @@ hipError_t run_scan(const TIn* q, const TIn* k, const TIn* v, const float* lam, 
     const long bs = (long)T * DK;
     const RowView<const TIn> vq{q + (long)W * DK, bs, DK}, vk{k, bs, DK}, vv{v, bs, DK};
     const RowView<float> vm{m + (long)W * DK, bs, DK};
-    if (p.n_seg > 1) {
+    if (p.n_seg > 1)
       hipLaunchKernelGGL((scan_state_fast<DK, TIn>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, vk, vv,
                          lam, eta, H, p.n_act, p.seg_chunks, p.n_seg, ws);
-      const int nel = DK * dv;
-      hipLaunchKernelGGL(scan_prefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H,
-                         nel, p.n_act, p.seg_chunks * CH, p.n_seg, ws);
-    }
     profile_mark_before(s);
     hipLaunchKernelGGL((scan_output_fast<DK, TIn>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, vq, vk, vv,
-                       lam, eta, H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, A_final);
+                       lam, eta, H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, (int)zrows, A_final);
     profile_mark_after(s);
     return hipGetLastError();
   }
