@@ -219,7 +219,6 @@ __global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __res
   const int bh = blockIdx.y;
   const int p_begin = blockIdx.x * G.tiles_per_seg;
   const int p_end = min(p_begin + G.tiles_per_seg, G.n_tiles);
-  const int w = wave_id(), l = lane_id(), col = l & 31, hh = l >> 5;
   const Decay dec(lam[bh % H]);
   const float et = eta[bh % H];
   const long base = (long)bh * G.T;

@@ -9,13 +9,17 @@
 // of 64 positions: for chunk n with entering state S_n (all writes j < 64n),
 //   o_r     = lam^(r+1) q'_r S_n + eta sum_{c<=r} lam^(r-c) <q'_r, k_c> v_c
 //   S_{n+1} = lam^L S_n + eta sum_c lam^(L-1-c) k_c v_c^T        (L = chunk length)
-// Three launches:
+// Launches:
 //   1. scan_state:  per segment of `seg_chunks` chunks, the segment's own
 //      contribution to the state (from zero), fully parallel;
-//   2. scan_prefix: entering state of every segment, sequential over the
-//      segments but parallel over the d_k x d_v elements;
-//   3. scan_output: per segment, carry the state through its chunks and
-//      write m.  Rows t < W are zero.
+//   2. scan_output: per segment, the entering state from the earlier
+//      segments' contributions (a Horner recurrence over them), then carry
+//      it through the segment's chunks and write m; the segments also clear
+//      the rows t < W, which are zero.
+// For d = 128 with fp32 inputs (scan_state_kernel / scan_output_kernel) the
+// entering states come from a separate scan_prefix launch, sequential over
+// the segments but parallel over the d_k x d_v elements, and the rows t < W
+// from zero_rows_kernel.
 // Arithmetic: fp32 MFMA (v_mfma_f32_16x16x4_f32) on LDS tiles; bf16 inputs
 // are widened to fp32 when staged, and the state is fp32 throughout.
 #include "tc_common.hpp"
@@ -377,6 +381,36 @@ __device__ __forceinline__ void fma_state(floatx4* acc, float f, const float* __
     for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(f, acc[i][e], src[(long)(16 * b + r) * dv + 16 * a + 4 * g + e]);
   }
 }
+// Entering state and its lam derivative from the earlier segments' (U, U')
+// pairs: run <- lf run + U, drun <- lf drun + dlf run + U' (dlf = d lf / d lam).
+template <int D>
+__device__ __forceinline__ void fma_state_d(floatx4* acc, floatx4* dacc, float lf, float dlf,
+                                            const float* __restrict__ src, const float* __restrict__ dsrc, int dv) {
+  using F = FastTiles<D>;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+  for (int i = 0; i < F::TPW; ++i) {
+    int a, b;
+    if (!state_tile<D>(w, i, a, b)) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const long o = (long)(16 * b + r) * dv + 16 * a + 4 * g + e;
+      dacc[i][e] = fmaf(lf, dacc[i][e], fmaf(dlf, acc[i][e], dsrc[o]));
+      acc[i][e] = fmaf(lf, acc[i][e], src[o]);
+    }
+  }
+}
+
+// Rows [-nrows, 0) of a row view set to zero, shared among the n_seg
+// segments (workgroups) of one (b, h).
+template <int D>
+__device__ __forceinline__ void clear_rows_before(RowView<float> v, int bh, int nrows, int seg, int n_seg) {
+  const int per = (nrows + n_seg - 1) / n_seg, z0 = seg * per, z1 = min(nrows, z0 + per);
+  for (int i = threadIdx.x; i < (z1 - z0) * (D / 4); i += blockDim.x)
+    *reinterpret_cast<float4*>(v.row(bh, z0 + i / (D / 4) - nrows) + 4 * (i % (D / 4))) =
+        make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 template <int D>
 __device__ __forceinline__ void store_state(float* dst, const floatx4* acc, int dv) {
   using F = FastTiles<D>;
@@ -474,12 +508,7 @@ __global__ __launch_bounds__(256) void scan_output_fast(
     for (int sp = 0; sp < seg; ++sp) fma_state<D>(acc, lam_seg, ws + ((long)bh * n_seg + sp) * D * D, D);
   }
   publish_state<D>(sSt[0], acc);
-  {  // this segment's share of the rows t < zrows (row s of vm is t = W + s)
-    const int per = (zrows + n_seg - 1) / n_seg, z0 = seg * per, z1 = min(zrows, z0 + per);
-    for (int i = threadIdx.x; i < (z1 - z0) * (D / 4); i += blockDim.x)
-      *reinterpret_cast<float4*>(vm.row(bh, z0 + i / (D / 4) - zrows) + 4 * (i % (D / 4))) =
-          make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  clear_rows_before<D>(vm, bh, zrows, seg, n_seg);  // row s of vm is t = W + s
   for (int c = c_begin; c < c_end; ++c) {
     const int s0 = c * CH, L = min(CH, n_act - s0);
     const int cur = (c - c_begin) & 1;
@@ -568,8 +597,10 @@ __global__ void zero_rows_kernel(float* __restrict__ m, long rows_per_bh, long T
 //   reverse (scan_bwd_rev_fast): walks the time-reversed sequence (row views
 //     with a negative row stride) carrying R, and writes dk and dv from the
 //     one state.
-// Segment-entering states come from the usual state + prefix kernels
-// (scan_dstate_fast / scan_dprefix_kernel for the pair (A, A')).
+// Each direction kernel forms its segment's entering state (A and A'
+// forward, R reverse) from the earlier segments' contributions
+// (scan_dstate_fast, scan_state_fast) and clears the gradient rows that no
+// position writes (dq for t < W, dk and dv for t >= T - W).
 constexpr int kZeroBlocks = 64;  // workgroups per (b, h) of the zeroing kernel
 
 // n lam^(n-1), the derivative of lam^n (0 for n = 0)
@@ -677,28 +708,6 @@ __global__ __launch_bounds__(256) void scan_dstate_fast(RowView<const float> vk,
   store_state<D>(dws + ((long)bh * n_seg + seg) * D * D, dacc, D);
 }
 
-// Entering (S, S') of every segment from the segments' own (U, U').
-__global__ void scan_dprefix_kernel(const float* __restrict__ lam, int H, int n_per_bh, int seg_len,
-                                    int n_seg, float* __restrict__ ws, float* __restrict__ dws) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int bh = blockIdx.y;
-  if (idx >= n_per_bh) return;
-  const float lm = lam[bh % H];
-  const float lf = pow_int(lm, seg_len), dlf = dpow_int(lm, seg_len);
-  float* p = ws + (long)bh * n_seg * n_per_bh + idx;
-  float* dp = dws + (long)bh * n_seg * n_per_bh + idx;
-  float run = 0.f, drun = 0.f;
-  for (int s = 0; s < n_seg - 1; ++s) {  // every segment but the last is full length
-    const float u = p[(long)s * n_per_bh], du = dp[(long)s * n_per_bh];
-    p[(long)s * n_per_bh] = run;
-    dp[(long)s * n_per_bh] = drun;
-    drun = lf * drun + dlf * run + du;
-    run = lf * run + u;
-  }
-  p[(long)(n_seg - 1) * n_per_bh] = run;
-  dp[(long)(n_seg - 1) * n_per_bh] = drun;
-}
-
 // Forward-direction pass, per (segment, b, h).  Phase 1 stages q', k, G, v
 // row-major for the two 64 x 64 Gram matrices and the entering-state read;
 // phase 2 reuses the same LDS for the transposed copies that feed the
@@ -708,7 +717,7 @@ __global__ __launch_bounds__(256) void scan_bwd_fwd_fast(
     RowView<const float> vq, RowView<const float> vk, RowView<const float> vv, RowView<const float> vg,
     const float* __restrict__ lam, const float* __restrict__ eta, int H, int n_act, int seg_chunks,
     int n_seg, const float* __restrict__ ws, const float* __restrict__ dws, const float* __restrict__ gate,
-    RowView<float> vdq, double* __restrict__ part_eta, double* __restrict__ part_lam) {
+    RowView<float> vdq, int zq, double* __restrict__ part_eta, double* __restrict__ part_lam) {
   using F = FastTiles<D>;
   constexpr int NT = D / 16;
   constexpr int ROWS = CH * F::S;  // one [64][D] array
@@ -738,10 +747,18 @@ __global__ __launch_bounds__(256) void scan_bwd_fwd_fast(
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
   if (threadIdx.x <= CH) sPow[threadIdx.x] = pow_int(lm, threadIdx.x);
 
+  // entering A and A' from the earlier segments' (U, U'), every one of them
+  // seg_chunks chunks long; the segments also clear dq rows t < zq
   floatx4 acc[F::TPW], dacc[F::TPW];
-  const bool entering = n_seg > 1 && seg > 0;
-  load_state<D>(acc, entering ? ws + ((long)bh * n_seg + seg) * D * D : nullptr, D);
-  load_state<D>(dacc, entering ? dws + ((long)bh * n_seg + seg) * D * D : nullptr, D);
+  load_state<D>(acc, nullptr, D);
+  load_state<D>(dacc, nullptr, D);
+  if (seg > 0) {
+    const float lf = pow_int(lm, seg_chunks * CH), dlf = dpow_int(lm, seg_chunks * CH);
+    for (int sp = 0; sp < seg; ++sp)
+      fma_state_d<D>(acc, dacc, lf, dlf, ws + ((long)bh * n_seg + sp) * D * D,
+                     dws + ((long)bh * n_seg + sp) * D * D, D);
+  }
+  clear_rows_before<D>(vdq, bh, zq, seg, n_seg);  // row s of vdq is t = W + s
   float4 xq[F::NV4], xk[F::NV4], xv[F::NV4], xg[F::NV4];
   if (c_begin < c_end) {
     const int s0 = c_begin * CH, L = min(CH, n_act - s0);
@@ -868,7 +885,7 @@ __global__ __launch_bounds__(256) void scan_bwd_rev_fast(
     RowView<const float> vv, RowView<const float> vk, RowView<const float> vq, RowView<const float> vg,
     const float* __restrict__ lam, const float* __restrict__ eta, int H, int n_act, int seg_chunks,
     int n_seg, const float* __restrict__ ws, const float* __restrict__ gate, RowView<float> vdk,
-    RowView<float> vdv) {
+    RowView<float> vdv, int ztail) {
   using F = FastTiles<D>;
   constexpr int NT = D / 16;
   constexpr int ROWS = CH * F::S;
@@ -896,8 +913,17 @@ __global__ __launch_bounds__(256) void scan_bwd_rev_fast(
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
   if (threadIdx.x <= CH) sPow[threadIdx.x] = pow_int(lm, threadIdx.x);
 
-  floatx4 acc[F::TPW];  // R^T tiles: (dk tile a, dv tile b)
-  load_state<D>(acc, n_seg > 1 && seg > 0 ? ws + ((long)bh * n_seg + seg) * D * D : nullptr, D);
+  // R^T tiles (dk tile a, dv tile b) entering the segment, from the earlier
+  // (reversed) segments' contributions; the segments also clear the dk, dv
+  // rows of the positions t >= n_act (rows -ztail .. -1 of the reversed views)
+  floatx4 acc[F::TPW];
+  load_state<D>(acc, nullptr, D);
+  if (seg > 0) {
+    const float lf = pow_int(lm, seg_chunks * CH);
+    for (int sp = 0; sp < seg; ++sp) fma_state<D>(acc, lf, ws + ((long)bh * n_seg + sp) * D * D, D);
+  }
+  clear_rows_before<D>(vdk, bh, ztail, seg, n_seg);
+  clear_rows_before<D>(vdv, bh, ztail, seg, n_seg);
   float4 xv[F::NV4], xk[F::NV4], xq[F::NV4], xg[F::NV4];
   if (c_begin < c_end) {
     const int s0 = c_begin * CH, L = min(CH, n_act - s0);
@@ -1009,9 +1035,9 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   const ScanPlan p = plan_scan(B, H, T, D, D, W);
   const int n_act = p.n_act;
   const long zq = std::min<long>(W, T);
-  hipLaunchKernelGGL(scan_bwd_zero_kernel, dim3(kZeroBlocks, BH), dim3(256), 0, s, dq, dk, dv, (long)T, D,
-                     zq, (long)std::max(n_act, 0));
-  if (n_act <= 0) {
+  if (n_act <= 0) {  // (otherwise the two direction kernels clear these rows)
+    hipLaunchKernelGGL(scan_bwd_zero_kernel, dim3(kZeroBlocks, BH), dim3(256), 0, s, dq, dk, dv, (long)T, D,
+                       zq, 0L);
     hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dlam, H, 0.f);
     hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, deta, H, 0.f);
     if (dgate != nullptr)
@@ -1027,30 +1053,24 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   // forward direction: dq, deta, dlam
   const RowView<const float> fq{q + (long)W * D, bs, D}, fk{k, bs, D}, fv{v, bs, D},
       fg{dm + (long)W * D, bs, D};
-  if (p.n_seg > 1) {
+  if (p.n_seg > 1)
     hipLaunchKernelGGL((scan_dstate_fast<D>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, fk, fv, lam, H,
                        n_act, p.seg_chunks, p.n_seg, sws, dws);
-    hipLaunchKernelGGL(scan_dprefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H, nel,
-                       p.seg_chunks * CH, p.n_seg, sws, dws);
-  }
   profile_mark_before(s);
   hipLaunchKernelGGL((scan_bwd_fwd_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, fq, fk, fv, fg, lam,
                      eta, H, n_act, p.seg_chunks, p.n_seg, sws, dws, gate,
-                     RowView<float>{dq + (long)W * D, bs, D}, part_eta, part_lam);
+                     RowView<float>{dq + (long)W * D, bs, D}, (int)zq, part_eta, part_lam);
   profile_mark_after(s);
   // reverse direction: dk, dv (row r of each view is position n_act - 1 - r)
   const long last = (long)(n_act - 1) * D, tl = (long)(T - 1) * D;
   const RowView<const float> rv{v + last, bs, -D}, rk{k + last, bs, -D}, rq{q + tl, bs, -D},
       rg{dm + tl, bs, -D};
-  if (p.n_seg > 1) {
+  if (p.n_seg > 1)
     hipLaunchKernelGGL((scan_state_fast<D, float>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, rg, rq, lam,
                        nullptr, H, n_act, p.seg_chunks, p.n_seg, sws);
-    hipLaunchKernelGGL(scan_prefix_kernel, dim3((nel + 255) / 256, BH), dim3(256), 0, s, lam, H, nel, n_act,
-                       p.seg_chunks * CH, p.n_seg, sws);
-  }
   hipLaunchKernelGGL((scan_bwd_rev_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, rv, rk, rq, rg, lam, eta,
                      H, n_act, p.seg_chunks, p.n_seg, sws, gate, RowView<float>{dk + last, bs, -D},
-                     RowView<float>{dv + last, bs, -D});
+                     RowView<float>{dv + last, bs, -D}, T - n_act);
   hipLaunchKernelGGL(scan_bwd_reduce, dim3((H + 63) / 64), dim3(64), 0, s, part_eta, part_lam, eta, gate, B,
                      H, p.n_seg, dlam, deta, dgate);
   return hipGetLastError();
