@@ -288,31 +288,30 @@ __global__ __launch_bounds__(256) void recall_argmax_kernel(const float* __restr
     if (j0 + CH < nc) xv.load(vg + (long)(j0 + CH) * D, D, min(CH, nc - j0 - CH));
     floatx4 s[4] = {zero4(), zero4(), zero4(), zero4()};
     mma_rows<D, 4>(sR + 16 * w * M::S, M::S, sV, 16 * M::S, M::S, s);
+    // this lane's running best over its own columns 16 ct + r: they come in
+    // increasing order, so a strict > keeps the smallest index of a tie
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      // this lane's 4 columns 16 ct + r, then the 16 lanes of the row
-      float v = -__builtin_inff();
-      int j = 0;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int jj = j0 + 16 * ct + r;
-        if (jj < nc && s[ct][e] > v) {
-          v = s[ct][e];
-          j = jj;
+        if (jj < nc && s[ct][e] > bv[e]) {
+          bv[e] = s[ct][e];
+          bi[e] = jj;
         }
       }
+    }
+  }
+  // the 16 lanes of a row: largest value, smallest index among equal ones
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const float ov = __shfl_xor(v, off);
-        const int oj = __shfl_xor(j, off);
-        if (ov > v || (ov == v && oj < j)) {
-          v = ov;
-          j = oj;
-        }
-      }
-      if (v > bv[e]) {  // later chunks hold larger indices: a tie keeps the earlier one
-        bv[e] = v;
-        bi[e] = j;
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const float ov = __shfl_xor(bv[e], off);
+      const int oj = __shfl_xor(bi[e], off);
+      if (ov > bv[e] || (ov == bv[e] && oj < bi[e])) {
+        bv[e] = ov;
+        bi[e] = oj;
       }
     }
   }

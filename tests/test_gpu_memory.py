@@ -109,6 +109,22 @@ def test_recall_argmax_ties_take_the_smallest_index():
     assert arg.cpu().numpy().tolist() == [[0, 0, 0]]
 
 
+@pytest.mark.parametrize("tied", [(37, 150, 199), (37, 101, 165), (200, 64, 63), (130, 2)])
+def test_recall_argmax_planted_ties(tied):
+    # equal maxima in different lanes, in the same lane of different 64-value
+    # chunks, and across chunk edges: the smallest index wins
+    V = np.full((1, 260, 32), 0.0, np.float32)
+    V[0, :, 0] = 0.5
+    for j in tied:
+        V[0, j, 0] = 1.0
+    R = np.zeros((1, 5, 32), np.float32)
+    R[0, :, 0] = 1.0
+    arg, best = ops.recall_argmax(dev(R), dev(V))
+    torch.cuda.synchronize()
+    assert arg.cpu().numpy().tolist() == [[min(tied)] * 5]
+    assert np.all(best.cpu().numpy() == 1.0)
+
+
 def test_hebbian_workload_full_size_sampled():
     # F = 16384 facts, m = 4096 features, d = 128: B in full, reads and recall
     # of 512 sampled facts
