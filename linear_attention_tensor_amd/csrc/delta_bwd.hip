@@ -593,27 +593,30 @@ hipError_t run_delta_backward(const float* q, const float* k, const float* v, co
 //   U = Tm V - G2 S0^T,   O = Q S0^T + A U,   S1 = S0 + U^T K,
 // per (16-row slice of S, b, h), chunks in order, the next chunk prefetched
 // into registers.  O's columns j0.. come from the slice (row j of S only
-// sees column j of V, U and O).
+// sees column j of V, U and O).  The products are formed transposed, so that
+// every MFMA operand is an LDS row contiguous in k (mma_rows: one 16-byte
+// read feeds four MFMAs): wave w takes the chunk's tokens 16w..16w+15 in
+//   U^T = V^T Tm^T - S G2^T,   O^T = S Q^T + U^T A^T,
+// and the state tile (slice rows, d_k columns 16w..) in S += U^T K.
 template <int D>
 __global__ __launch_bounds__(256) void delta_fwd_walk(const float* __restrict__ q, const float* __restrict__ k,
                                                       const float* __restrict__ v, int T, int n_chunks,
                                                       const float* __restrict__ S0, const float* __restrict__ pre,
                                                       float* __restrict__ o, float* __restrict__ S_final) {
-  constexpr int S = DB<D>::S, SV = DB<D>::SV;
+  constexpr int S = DB<D>::S;
   using P = Pre<D>;
-  __shared__ __attribute__((aligned(16))) float sS[SL * S];
-  __shared__ __attribute__((aligned(16))) float sQ[CH * S];
-  __shared__ __attribute__((aligned(16))) float sK[CH * S];
-  __shared__ __attribute__((aligned(16))) float sG[CH * S];   // G2
-  __shared__ __attribute__((aligned(16))) float sV[CH * SV];
-  __shared__ __attribute__((aligned(16))) float sU[CH * SV];
-  __shared__ __attribute__((aligned(16))) float sT[CH * SW];  // Tm
-  __shared__ __attribute__((aligned(16))) float sA[CH * SW];  // tril_0(Q K^T)
+  __shared__ __attribute__((aligned(16))) float sS[SL * S];        // the slice [16][D]
+  __shared__ __attribute__((aligned(16))) float sGQ[2][CH * S];    // G2, Q rows [64][D]
+  __shared__ __attribute__((aligned(16))) float sKt[D * SW];       // K^T [D][64]
+  __shared__ __attribute__((aligned(16))) float sVt[SL * SW];      // V^T of the slice [16][64]
+  __shared__ __attribute__((aligned(16))) float sUt[SL * SW];      // U^T [16][64]
+  __shared__ __attribute__((aligned(16))) float sT[CH * SW];       // Tm
+  __shared__ __attribute__((aligned(16))) float sA[CH * SW];       // tril_0(Q K^T)
   const int j0 = blockIdx.x * SL, bh = blockIdx.y;
-  const int w = wave_id(), l = lane_id(), col = l & 15, rq = (l >> 4) * 4;
+  const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
   for (int i = threadIdx.x; i < SL * D; i += blockDim.x) {
-    const int r = i / D, cc = i % D;
-    sS[r * S + cc] = S0 != nullptr ? S0[((long)bh * D + j0 + r) * D + cc] : 0.f;
+    const int rr = i / D, cc = i % D;
+    sS[rr * S + cc] = S0 != nullptr ? S0[((long)bh * D + j0 + rr) * D + cc] : 0.f;
   }
   Rows<D> pq, pk, pg;
   Rows<SL> pv;
@@ -628,39 +631,48 @@ __global__ __launch_bounds__(256) void delta_fwd_walk(const float* __restrict__ 
     pa.load(pc + P::E2, CH, 0, CH);
     pg.load(pc + P::G2, D, 0, CH);
   };
+  // a [64][NC] row block into LDS transposed ([NC][64], row stride SW)
+  auto put_t = [](float* dst, const float4* x, int n4, int nc) __attribute__((always_inline)) {
+    for (int i = 0; i < n4; ++i) {
+      const int idx = i * 256 + (int)threadIdx.x, row = idx / (nc / 4), c = (idx % (nc / 4)) * 4;
+      if (row < CH) {
+        dst[(c + 0) * SW + row] = x[i].x;
+        dst[(c + 1) * SW + row] = x[i].y;
+        dst[(c + 2) * SW + row] = x[i].z;
+        dst[(c + 3) * SW + row] = x[i].w;
+      }
+    }
+  };
   fetch(0);
   for (int c = 0; c < n_chunks; ++c) {
     const int t0 = c * CH, L = min(CH, T - t0);
-    __syncthreads();  // the previous chunk's update of sS is complete
-    pq.put(sQ, S);
-    pk.put(sK, S);
-    pg.put(sG, S);
-    pv.put(sV, SV);
+    __syncthreads();  // the previous chunk's update of sS and reads of U^T are complete
+    pg.put(sGQ[0], S);
+    pq.put(sGQ[1], S);
+    put_t(sKt, pk.x, Rows<D>::N, D);
+    put_t(sVt, pv.x, Rows<SL>::N, SL);
     pt.put(sT, SW);
     pa.put(sA, SW);
     __syncthreads();
     if (c + 1 < n_chunks) fetch(c + 1);
-    floatx4 out;
-    {  // U = Tm V - G2 S^T and O = Q S^T, rows 16w..
-      floatx4 u = wave_mma_f32<CH>(sT + 16 * w * SW, SW, 1, sV, SV, 1, zero4());
-      floatx4 g = wave_mma_f32<D>(sG + 16 * w * S, S, 1, sS, 1, S, zero4());
-      out = wave_mma_f32<D>(sQ + 16 * w * S, S, 1, sS, 1, S, zero4());
+    floatx4 gq[2] = {zero4(), zero4()}, ut = zero4();
+    mma_rows<D, 2>(sS, S, sGQ[0] + 16 * w * S, CH * S, S, gq);  // S G2^T, S Q^T (tokens 16w..)
+    mma_rows<CH, 1>(sVt, SW, sT + 16 * w * SW, 0, SW, &ut);     // V^T Tm^T
+    // element i of lane (r, g): slice row 4g + i, token 16w + r
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sU[(16 * w + rq + i) * SV + col] = u[i] - g[i];
-    }
+    for (int i = 0; i < 4; ++i) sUt[(4 * g + i) * SW + 16 * w + r] = ut[i] - gq[0][i];
     __syncthreads();
-    out = wave_mma_f32<CH>(sA + 16 * w * SW, SW, 1, sU, SV, 1, out);  // O += A U
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + rq + i;
-      if (r < L) o[((long)bh * T + t0 + r) * D + j0 + col] = out[i];
-    }
-    if (w < D / 16) {  // S += U^T K, tile (rows j0.., columns 16w..)
-      float* base = sS + rq * S + 16 * w + col;
+    floatx4 ot = gq[1];
+    mma_rows<CH, 1>(sUt, SW, sA + 16 * w * SW, 0, SW, &ot);  // O^T += U^T A^T
+    if (16 * w + r < L)
+      *reinterpret_cast<float4*>(o + ((long)bh * T + t0 + 16 * w + r) * D + j0 + 4 * g) =
+          make_float4(ot[0], ot[1], ot[2], ot[3]);
+    if (w < D / 16) {  // S += U^T K, tile (slice rows, columns 16w..)
+      float* base = sS + 4 * g * S + 16 * w + r;
       floatx4 acc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = base[i * S];
-      acc = wave_mma_f32<CH>(sU, 1, SV, sK + 16 * w, S, 1, acc);
+      mma_rows<CH, 1>(sUt, SW, sKt + 16 * w * SW, 0, SW, &acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) base[i * S] = acc[i];
     }
@@ -668,8 +680,8 @@ __global__ __launch_bounds__(256) void delta_fwd_walk(const float* __restrict__ 
   if (S_final != nullptr) {
     __syncthreads();
     for (int i = threadIdx.x; i < SL * D; i += blockDim.x) {
-      const int r = i / D, cc = i % D;
-      S_final[((long)bh * D + j0 + r) * D + cc] = sS[r * S + cc];
+      const int rr = i / D, cc = i % D;
+      S_final[((long)bh * D + j0 + rr) * D + cc] = sS[rr * S + cc];
     }
   }
 }
