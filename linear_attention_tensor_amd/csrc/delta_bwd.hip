@@ -62,6 +62,38 @@ __device__ __forceinline__ floatx4 wave_mma_f32_scaled(const float* pa, int am, 
 
 // rows [0, 64) x [0, NC) of a row-major source (row stride ld, first column
 // col0) into LDS (stride dst_ld); rows >= nvalid become zero.
+// C += A B over K (a multiple of 16), A[m][k] at pa + m am + k ak, B[k][n] at
+// pb + k bk + n bn: MFMA 4J + s takes k = 16J + 4g + s from lane (row, g), so
+// an operand that is contiguous in k (ak or bk = 1; every such operand here
+// starts 16-byte aligned with a row stride that is a multiple of 4) comes in
+// one 16-byte read per four MFMAs; the permutation of k is shared by A and B.
+template <int K>
+__device__ __forceinline__ floatx4 wmma_k4(const float* pa, int am, int ak, const float* pb, int bk, int bn,
+                                           floatx4 c) {
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const float* a = pa + r * am + 4 * g * ak;
+  const float* b = pb + r * bn + 4 * g * bk;
+#pragma unroll
+  for (int J = 0; J < K / 16; ++J) {
+    float4 x, y;
+    if (ak == 1) {
+      x = *reinterpret_cast<const float4*>(a + 16 * J);
+    } else {
+      x = make_float4(a[(16 * J) * ak], a[(16 * J + 1) * ak], a[(16 * J + 2) * ak], a[(16 * J + 3) * ak]);
+    }
+    if (bk == 1) {
+      y = *reinterpret_cast<const float4*>(b + 16 * J);
+    } else {
+      y = make_float4(b[(16 * J) * bk], b[(16 * J + 1) * bk], b[(16 * J + 2) * bk], b[(16 * J + 3) * bk]);
+    }
+    c = mfma4(x.x, y.x, c);
+    c = mfma4(x.y, y.y, c);
+    c = mfma4(x.z, y.z, c);
+    c = mfma4(x.w, y.w, c);
+  }
+  return c;
+}
+
 template <int NC>
 __device__ __forceinline__ void stage(float* dst, int dst_ld, const float* src, long ld, int col0, int nvalid) {
   constexpr int V4 = NC / 4;
@@ -179,8 +211,8 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
   __syncthreads();
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    floatx4 kk = wave_mma_f32<D>(sK + 16 * w * S, S, 1, sK + 16 * ct * S, 1, S, zero4());
-    floatx4 qk = wave_mma_f32<D>(sQ + 16 * w * S, S, 1, sK + 16 * ct * S, 1, S, zero4());
+    floatx4 kk = wmma_k4<D>(sK + 16 * w * S, S, 1, sK + 16 * ct * S, 1, S, zero4());
+    floatx4 qk = wmma_k4<D>(sQ + 16 * w * S, S, 1, sK + 16 * ct * S, 1, S, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + rq + i, cc = 16 * ct + col;
@@ -217,7 +249,7 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
       const int bb = w, aa = w + dist;
       floatx4 t = zero4();
       for (int cb = bb; cb < aa; ++cb)
-        t = wave_mma_f32<16>(sM + 16 * aa * SW + 16 * cb, SW, 1, sWm + 16 * cb * SW + 16 * bb, SW, 1, t);
+        t = wmma_k4<16>(sM + 16 * aa * SW + 16 * cb, SW, 1, sWm + 16 * cb * SW + 16 * bb, SW, 1, t);
       float* tw = sTmp + w * 16 * 17;
 #pragma unroll
       for (int i = 0; i < 4; ++i) tw[(rq + i) * 17 + col] = t[i];
@@ -225,7 +257,7 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-      const floatx4 wab = wave_mma_f32<16>(sWm + 16 * aa * SW + 16 * aa, SW, 1, tw, 17, 1, zero4());
+      const floatx4 wab = wmma_k4<16>(sWm + 16 * aa * SW + 16 * aa, SW, 1, tw, 17, 1, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) sWm[(16 * aa + rq + i) * SW + 16 * bb + col] = -wab[i];
     }
@@ -241,7 +273,7 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
   } else {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {  // E2 = W^T A^T
-      floatx4 e = wave_mma_f32<CH>(sWm + 16 * w, 1, SW, sA + 16 * ct * SW, 1, SW, zero4());
+      floatx4 e = wmma_k4<CH>(sWm + 16 * w, 1, SW, sA + 16 * ct * SW, 1, SW, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[P::E2 + (16 * w + rq + i) * CH + 16 * ct + col] = e[i];
     }
@@ -252,7 +284,7 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i) out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
     if constexpr (!FWD) {
-      floatx4 e = wave_mma_f32<CH>(sWm + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
+      floatx4 e = wmma_k4<CH>(sWm + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = e[i];
     }
@@ -300,8 +332,8 @@ __device__ __forceinline__ void delta_bwd_fwd(const float* __restrict__ k, const
     __syncthreads();
     if (c + 1 < n_chunks) fetch(c + 1);
     {  // U = Tm V - G2 S^T, rows 16w..
-      floatx4 u = wave_mma_f32<CH>(sT + 16 * w * SW, SW, 1, sV, SV, 1, zero4());
-      floatx4 g = wave_mma_f32<D>(sG + 16 * w * S, S, 1, sS, 1, S, zero4());
+      floatx4 u = wmma_k4<CH>(sT + 16 * w * SW, SW, 1, sV, SV, 1, zero4());
+      floatx4 g = wmma_k4<D>(sG + 16 * w * S, S, 1, sS, 1, S, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) sU[(16 * w + rq + i) * SV + col] = u[i] - g[i];
     }
@@ -311,7 +343,7 @@ __device__ __forceinline__ void delta_bwd_fwd(const float* __restrict__ k, const
       floatx4 acc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = base[i * S];
-      acc = wave_mma_f32<CH>(sU, 1, SV, sK + 16 * w, S, 1, acc);
+      acc = wmma_k4<CH>(sU, 1, SV, sK + 16 * w, S, 1, acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) base[i * S] = acc[i];
     }
@@ -369,8 +401,8 @@ __device__ __forceinline__ void delta_bwd_rev(const float* __restrict__ q, const
     __syncthreads();
     if (c > 0) fetch(c - 1);
     {  // dX = diag(beta) (E1 dS^T + E2 dO), rows 16w..
-      floatx4 y = wave_mma_f32<D>(sE1 + 16 * w * S, S, 1, sD, 1, S, zero4());
-      y = wave_mma_f32<CH>(sE2 + 16 * w * SW, SW, 1, sO, SV, 1, y);
+      floatx4 y = wmma_k4<D>(sE1 + 16 * w * S, S, 1, sD, 1, S, zero4());
+      y = wmma_k4<CH>(sE2 + 16 * w * SW, SW, 1, sO, SV, 1, y);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + rq + i;
@@ -383,8 +415,8 @@ __device__ __forceinline__ void delta_bwd_rev(const float* __restrict__ q, const
       floatx4 acc, neg = zero4();
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = base[i * S];
-      acc = wave_mma_f32<CH>(sO, 1, SV, sQ + 16 * w, S, 1, acc);
-      neg = wave_mma_f32<CH>(sX, 1, SV, sK + 16 * w, S, 1, neg);
+      acc = wmma_k4<CH>(sO, 1, SV, sQ + 16 * w, S, 1, acc);
+      neg = wmma_k4<CH>(sX, 1, SV, sK + 16 * w, S, 1, neg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) base[i * S] = acc[i] - neg[i];
     }
@@ -473,16 +505,16 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
   floatx4 aq[NT], ak[NT], y[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    floatx4 ks = wave_mma_f32<D>(bK + 16 * w * S, S, 1, bS + 16 * t * S, 1, S, zero4());
+    floatx4 ks = wmma_k4<D>(bK + 16 * w * S, S, 1, bS + 16 * t * S, 1, S, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) bX[(16 * w + rq + i) * S + 16 * t + col] -= ks[i];
-    aq[t] = wave_mma_f32<D>(bO + 16 * w * S, S, 1, bS + 16 * t, S, 1, zero4());
+    aq[t] = wmma_k4<D>(bO + 16 * w * S, S, 1, bS + 16 * t, S, 1, zero4());
   }
   __syncthreads();
   // U = Tm X; bring dS1 in
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    floatx4 u = wave_mma_f32<CH>(bT + 16 * w * SW, SW, 1, bX + 16 * t, S, 1, zero4());
+    floatx4 u = wmma_k4<CH>(bT + 16 * w * SW, SW, 1, bX + 16 * t, S, 1, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) bU[(16 * w + rq + i) * S + 16 * t + col] = u[i];
   }
@@ -491,9 +523,9 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
   // dY = E1 dS1^T + E2 dO (registers); dK = U dS1 (first part)
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    y[t] = wave_mma_f32<D>(bF + 16 * w * SW, SW, 1, bS + 16 * t * S, 1, S, zero4());
-    y[t] = wave_mma_f32<CH>(bE + 16 * w * SW, SW, 1, bO + 16 * t, S, 1, y[t]);
-    ak[t] = wave_mma_f32<D>(bU + 16 * w * S, S, 1, bS + 16 * t, S, 1, zero4());
+    y[t] = wmma_k4<D>(bF + 16 * w * SW, SW, 1, bS + 16 * t * S, 1, S, zero4());
+    y[t] = wmma_k4<CH>(bE + 16 * w * SW, SW, 1, bO + 16 * t, S, 1, y[t]);
+    ak[t] = wmma_k4<D>(bU + 16 * w * S, S, 1, bS + 16 * t, S, 1, zero4());
   }
   __syncthreads();
   // dY into bE; S0 back in
@@ -523,9 +555,9 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
   float db2[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) {
-    floatx4 p1 = wave_mma_f32<D>(bO + 16 * w * S, S, 1, bU + 16 * ct * S, 1, S, zero4());
-    floatx4 p2 = wave_mma_f32<D>(bE + 16 * w * SW, SW, 1, bU + 16 * ct * S, 1, S, zero4());
-    floatx4 kk = wave_mma_f32<D>(bK + 16 * w * S, S, 1, bK + 16 * ct * S, 1, S, zero4());
+    floatx4 p1 = wmma_k4<D>(bO + 16 * w * S, S, 1, bU + 16 * ct * S, 1, S, zero4());
+    floatx4 p2 = wmma_k4<D>(bE + 16 * w * SW, SW, 1, bU + 16 * ct * S, 1, S, zero4());
+    floatx4 kk = wmma_k4<D>(bK + 16 * w * S, S, 1, bK + 16 * ct * S, 1, S, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + rq + i, cc = 16 * ct + col;
@@ -551,13 +583,13 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
   // dQ = dO S0 + P1 K;  dK = U dS1 - diag(beta) dY S0 + P1^T Q + dLk K + dLk^T K
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    aq[t] = wave_mma_f32<CH>(bF + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, aq[t]);
-    floatx4 ys = wave_mma_f32<D>(bE + 16 * w * SW, SW, 1, bS + 16 * t, S, 1, zero4());
+    aq[t] = wmma_k4<CH>(bF + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, aq[t]);
+    floatx4 ys = wmma_k4<D>(bE + 16 * w * SW, SW, 1, bS + 16 * t, S, 1, zero4());
 #pragma unroll
     for (int i = 0; i < 4; ++i) ak[t][i] -= sB[16 * w + rq + i] * ys[i];
-    ak[t] = wave_mma_f32<CH>(bF + 16 * w, 1, SW, bQ + 16 * t, S, 1, ak[t]);
-    ak[t] = wave_mma_f32<CH>(bT + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, ak[t]);
-    ak[t] = wave_mma_f32<CH>(bT + 16 * w, 1, SW, bK + 16 * t, S, 1, ak[t]);
+    ak[t] = wmma_k4<CH>(bF + 16 * w, 1, SW, bQ + 16 * t, S, 1, ak[t]);
+    ak[t] = wmma_k4<CH>(bT + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, ak[t]);
+    ak[t] = wmma_k4<CH>(bT + 16 * w, 1, SW, bK + 16 * t, S, 1, ak[t]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + rq + i;
