@@ -1049,7 +1049,6 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   float* sws = reinterpret_cast<float*>(ws + scan_bwd_part_bytes(B, H, p.n_seg));
   float* dws = reinterpret_cast<float*>(ws + scan_bwd_part_bytes(B, H, p.n_seg) + scan_ws_bytes(p, B, H, D, D));
   const long bs = (long)T * D;
-  const int nel = D * D;
   // forward direction: dq, deta, dlam
   const RowView<const float> fq{q + (long)W * D, bs, D}, fk{k, bs, D}, fv{v, bs, D},
       fg{dm + (long)W * D, bs, D};
