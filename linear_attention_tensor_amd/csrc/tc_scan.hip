@@ -614,7 +614,7 @@ __device__ __forceinline__ float gate_factor(const float* gate, int h) {
 }
 
 // workspace of the backward: fp64 shares of deta and dlam [2][BH][n_seg] |
-// segment-entering states (A, then R) | segment-entering A'
+// per-segment state contributions (A, then R) | per-segment contributions to A'
 size_t scan_bwd_part_bytes(int B, int H, int n_seg) {
   return ((size_t)2 * B * H * n_seg * sizeof(double) + 255) / 256 * 256;
 }
