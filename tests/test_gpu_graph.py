@@ -1,6 +1,7 @@
 """The entry points under HIP graph capture (torch.cuda.CUDAGraph): a serving
 loop captures one decode step (and the caller's position advance) once and
-replays it per token; a prefill captures one fused-layer call.  Every replay
+replays it per token; a prefill captures one fused-layer, scan or delta-rule
+call (with the workspace the wrapper allocates inside the capture).  Every replay
 is checked against the same call made eagerly: the kernels use no atomics,
 so the results must agree bit for bit.  Eager work (input copies, other
 calls, synchronisations) runs between the replays."""
@@ -109,3 +110,58 @@ def test_fused_layer_graph_replays():
         j = (i + 1) % 3
         qj, kj, vj, lj, ej = inputs(xs[j])
         assert torch.equal(ops.tc_fused_layer(qj, kj, vj, lj, ej, g, W), refs[j][0])
+
+
+def _graph_vs_eager(call, make_inputs, n_inputs, what):
+    """Capture call(*static) once, replay it on several inputs copied into the
+    static tensors (eager calls between the replays) and compare every output
+    with the eager call on the same input, bit for bit."""
+    ins = [make_inputs(i) for i in range(n_inputs)]
+    refs = [tuple(t.clone() for t in call(*x)) for x in ins]
+    torch.cuda.synchronize()
+    static = tuple(t.clone() for t in ins[0])
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        outs = call(*static)
+    torch.cuda.synchronize()
+    for rnd, i in enumerate([1, 0, n_inputs - 1, 1]):
+        for dst, src in zip(static, ins[i]):
+            dst.copy_(src)
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (got, want) in enumerate(zip(outs, refs[i])):
+            assert torch.equal(got, want), f"{what}: replay {rnd} (input {i}), output {j}"
+        other = ins[(i + 1) % n_inputs]  # eager work between the replays
+        assert all(torch.equal(a, b) for a, b in zip(call(*other), refs[(i + 1) % n_inputs]))
+
+
+@pytest.mark.parametrize("dtype,d,T,W", [("f32", 64, 900, 100), ("bf16", 128, 1500, 256), ("bf16", 32, 300, 40)])
+def test_scan_forward_graph_replays(dtype, d, T, W):
+    print(f"[case] scan graph dtype={dtype} d={d} T={T} W={W}", flush=True)
+
+    def make(i):
+        x = I.draw(1, 3, T, d, seed=950 + i, dtype=dtype, lam=("uniform", 0.95, 0.999))
+        return (to_dev(x["q"], dtype), to_dev(x["k"], dtype), to_dev(x["v"], dtype), f32_dev(x["lam"]),
+                f32_dev(x["eta"]))
+
+    def call(q, k, v, lam, eta):
+        return ops.tc_scan_forward(q, k, v, lam, eta, W, check_values=False)
+
+    _graph_vs_eager(call, make, 3, "tc_scan_forward")
+
+
+@pytest.mark.parametrize("dtype,d,T", [("f32", 64, 700), ("bf16", 128, 600)])
+def test_delta_forward_graph_replays(dtype, d, T):
+    print(f"[case] delta graph dtype={dtype} d={d} T={T}", flush=True)
+
+    def make(i):
+        x = I.draw(1, 2, T, d, seed=970 + i, dtype=dtype)
+        rng = np.random.default_rng(980 + i)
+        beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((1, 2, T))))
+        return (to_dev(x["q"], dtype), to_dev(x["k"], dtype), to_dev(x["v"], dtype), f32_dev(beta))
+
+    def call(q, k, v, beta):
+        return ops.delta_scan_forward(q, k, v, beta, return_state=True, check_values=False)
+
+    _graph_vs_eager(call, make, 3, "delta_scan_forward")
