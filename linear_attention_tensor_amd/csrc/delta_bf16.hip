@@ -23,6 +23,7 @@
 // bf16 term, since their rounding does not accumulate.
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
+#include "tc_dma.hpp"
 #include "tc_mfma.hpp"
 
 #include <math.h>
@@ -32,30 +33,13 @@ namespace tc {
 namespace {
 
 using namespace mf;
+using dma::dma16;
+using dma::i32x4;
+using dma::raw_desc;
 
 constexpr int CH = 64;   // tokens per chunk
 constexpr int DVT = 16;  // rows of S per workgroup
 constexpr int NXCD = 8;  // MI355X: 8 accelerator complex dies, dispatched round-robin
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ i32x4 raw_desc(const void* base, uint32_t nbytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xFFFF), static_cast<int>(nbytes),
-               0x00020000};
-}
-
-// 16 bytes per lane global -> LDS (lane i writes lds_base + 16 i), issued as
-// inline asm so the compiler adds no wait for it before LDS reads and
-// barriers; the kernel orders it with s_waitcnt vmcnt(n) and a barrier.  No
-// register is written and the operands are read when the instruction issues.
-__device__ __forceinline__ void dma16(i32x4 desc, const void* lds_base, int voffset) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voffset), "s"(desc)
-               : "memory", "m0");
-}
 
 // Swizzled bf16 LDS rows of NCH 16-byte chunks: chunk c of row r sits at
 // position c ^ swz(r), so 16 lanes reading one chunk of 16 consecutive rows
@@ -398,6 +382,19 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
     }
   };
   publish_state();
+  if (T % CH != 0) {
+    // A ragged last chunk copies rows past T, which the descriptors turn
+    // into zeros; the buffers are cleared first as well, so those rows can
+    // never hold what an earlier kernel left in LDS (U's rows past T are
+    // 0 * X, which a NaN pattern there would poison).
+    auto clear = [&](uint16_t* p, int bytes) __attribute__((always_inline)) {
+      for (int i = threadIdx.x; i < bytes / 16; i += 256) reinterpret_cast<uint4*>(p)[i] = make_uint4(0, 0, 0, 0);
+    };
+    clear(&lds.q[0][0], (int)sizeof(lds.q));
+    clear(&lds.k[0][0], (int)sizeof(lds.k));
+    clear(&lds.v[0][0], (int)sizeof(lds.v));
+    lds_barrier();
+  }
   if (n_chunks > 0) issue(0, 0);
 
   floatx4 o_prev = zero4();

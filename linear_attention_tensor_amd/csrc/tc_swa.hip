@@ -26,6 +26,7 @@
 // through its L2 cache.
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
+#include "tc_dma.hpp"
 #include "tc_mfma.hpp"
 
 #include <math.h>
@@ -35,6 +36,9 @@ namespace tc {
 namespace {
 
 using namespace mf;
+using dma::dma16;
+using dma::i32x4;
+using dma::raw_desc;
 
 constexpr int NWAVE = 8;
 constexpr int NTHR = 64 * NWAVE;
@@ -81,28 +85,6 @@ __device__ __forceinline__ DmaOff<D> dma_offsets(int Tp, int voff) {
     o.v[i] = (dv * Tp + voff + 8 * c) * 2;
   }
   return o;
-}
-
-// Raw buffer descriptor over [base, base + nbytes) (gfx9 layout: stride 0,
-// word 3 = raw dword data); reads past the end return zero.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 raw_desc(const void* base, uint32_t nbytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{static_cast<int>(a), static_cast<int>((a >> 32) & 0xFFFF), static_cast<int>(nbytes),
-               0x00020000};
-}
-
-// 16 bytes per lane global -> LDS (lane i writes lds_base + 16 i).  Issued
-// as inline asm so that the compiler neither waits for these loads before
-// every later LDS read nor before every barrier: the kernel orders them
-// itself with s_waitcnt vmcnt and a workgroup barrier.  No register is
-// written, and the operands are read when the instruction issues.
-__device__ __forceinline__ void dma16(i32x4 desc, const void* lds_base, int voffset) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds), "v"(voffset), "s"(desc)
-               : "memory", "m0");
 }
 
 // DMA of the 64-key block starting at key j (any sign) into one stage.  dk:
