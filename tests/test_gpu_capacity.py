@@ -7,7 +7,7 @@ import torch
 from linear_attention_tensor_amd import diagnostics as Dg
 from linear_attention_tensor_amd import inputs as I
 from oracle import capacity as C
-from tests._helpers import f32_dev, report
+from tests._helpers import f32_dev, check, report
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def test_capacity_diagnostic_matches_oracle(n_old, W, lam, ingest_all):
     lam64 = np.full(1, np.float32(lam), np.float64)
     A_ref = C.ingest_all_memory(k64, v64, lam64, np.ones(1)) if ingest_all else C.tc_memory(k64, v64, lam64,
                                                                                              np.ones(1), W)
-    assert report("A", A.cpu().numpy(), A_ref) <= 1e-5
+    check("A", A.cpu().numpy(), A_ref, 1e-5)
     want = C.recall_hits(A_ref, k64, v64, n_old)
     tie = near_tie(A_ref, k64, v64, n_old)
     assert np.array_equal(hits[~tie], want[~tie])

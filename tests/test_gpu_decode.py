@@ -6,7 +6,7 @@ import torch
 from linear_attention_tensor_amd import inputs as I
 from linear_attention_tensor_amd import ops
 from oracle import tc as O
-from tests._helpers import f32_dev, report, to_dev
+from tests._helpers import f32_dev, check, report, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -31,8 +31,8 @@ def test_decode_from_empty_matches_scan(dtype, B, H, d, W, T):
         ms.append(ops.tc_decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
                                      ring_k, ring_v, A, lam, eta, pos, W).clone())
     m = torch.stack(ms, dim=2).cpu().numpy()
-    assert report("m", m, m_ref) <= TOL[dtype]
-    assert report("A", A.cpu().numpy(), A_ref) <= TOL[dtype]
+    check("m", m, m_ref, TOL[dtype])
+    check("A", A.cpu().numpy(), A_ref, TOL[dtype])
     # the ring holds the last W tokens in slots t mod W, bit for bit
     rk = ring_k.cpu()
     kk = k.cpu()
@@ -58,8 +58,8 @@ def test_decode_sequences_at_different_positions():
         m = ops.tc_decode_step(to_dev(x["q"], "f32"), to_dev(x["k"], "f32"), to_dev(x["v"], "f32"),
                                g_rk, g_rv, g_A, lam, eta, pos, W)
         m_ref = dec.step(x["q64"], x["k64"], x["v64"])
-        assert report(f"step {step}", m.cpu().numpy(), m_ref) <= 1e-5
-    assert report("A", g_A.cpu().numpy(), dec.A) <= 1e-5
+        check(f"step {step}", m.cpu().numpy(), m_ref, 1e-5)
+    check("A", g_A.cpu().numpy(), dec.A, 1e-5)
 
 
 def test_scan_prefill_then_decode_continues_the_scan():
@@ -84,10 +84,10 @@ def test_scan_prefill_then_decode_continues_the_scan():
         pos = torch.full((B,), t, dtype=torch.int64, device="cuda")
         m = ops.tc_decode_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
                                ring_k, ring_v, A, lam, eta, pos, W)
-        assert report(f"t={t}", m.cpu().numpy(), m_ref[:, :, t]) <= 2e-2
-        assert report(f"t={t} vs GPU scan", m.cpu().numpy(), m_full[:, :, t].cpu().numpy()) <= 1e-2
-    assert report("A", A.cpu().numpy(), A_ref) <= 2e-2
-    assert report("A vs GPU scan", A.cpu().numpy(), A_full.cpu().numpy()) <= 1e-2
+        check(f"t={t}", m.cpu().numpy(), m_ref[:, :, t], 2e-2)
+        check(f"t={t} vs GPU scan", m.cpu().numpy(), m_full[:, :, t].cpu().numpy(), 1e-2)
+    check("A", A.cpu().numpy(), A_ref, 2e-2)
+    check("A vs GPU scan", A.cpu().numpy(), A_full.cpu().numpy(), 1e-2)
 
 
 def test_decode_workload_full_size_sampled_sequences():
@@ -110,5 +110,5 @@ def test_decode_workload_full_size_sampled_sequences():
         m = ops.tc_decode_step(to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"),
                                g_rk, g_rv, g_A, lam, eta, pos, W)
         m_ref = dec.step(x["q64"][bs], x["k64"][bs], x["v64"][bs])
-        assert report(f"step {step}", m.cpu().numpy()[bs], m_ref) <= 2e-2
-    assert report("A", g_A.cpu().numpy()[bs], dec.A) <= 2e-2
+        check(f"step {step}", m.cpu().numpy()[bs], m_ref, 2e-2)
+    check("A", g_A.cpu().numpy()[bs], dec.A, 2e-2)

@@ -12,7 +12,7 @@ import torch
 from linear_attention_tensor_amd import inputs as I
 from linear_attention_tensor_amd import ops
 from oracle import tc as O
-from tests._helpers import f32_dev, report, to_dev
+from tests._helpers import f32_dev, check, report, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -41,8 +41,8 @@ def test_decode_layer_from_empty_matches_fused_layer(dtype, B, H, d, W, T):
                                            v[:, :, t].contiguous(), ring_k, ring_v, A, lam, eta, g, pos,
                                            W).clone())
     y = torch.stack(ys, dim=2).cpu().numpy()
-    assert report("y", y, y_ref) <= TOL[dtype]
-    assert report("A", A.cpu().numpy(), A_ref) <= TOL[dtype]
+    check("y", y, y_ref, TOL[dtype])
+    check("A", A.cpu().numpy(), A_ref, TOL[dtype])
     rk = ring_k.cpu()
     kk = k.cpu()
     for t in range(max(0, T - W), T):
@@ -71,8 +71,8 @@ def test_decode_layer_sequences_at_different_positions(dtype):
         y = ops.tc_decode_layer_step(to_dev(x["q"], dtype), to_dev(x["k"], dtype), to_dev(x["v"], dtype),
                                      g_rk, g_rv, g_A, lam, eta, gg, pos, W, softmax_scale=0.3)
         y_ref = dec.step_layer(x["q64"], x["k64"], x["v64"], g, 0.3)
-        assert report(f"step {step}", y.cpu().numpy(), y_ref) <= TOL[dtype]
-    assert report("A", g_A.cpu().numpy(), dec.A) <= TOL[dtype]
+        check(f"step {step}", y.cpu().numpy(), y_ref, TOL[dtype])
+    check("A", g_A.cpu().numpy(), dec.A, TOL[dtype])
 
 
 def test_decode_layer_workload_full_size_sampled_sequences():
@@ -96,5 +96,5 @@ def test_decode_layer_workload_full_size_sampled_sequences():
         y = ops.tc_decode_layer_step(to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16"),
                                      g_rk, g_rv, g_A, lam, eta, gg, pos, W)
         y_ref = dec.step_layer(x["q64"][bs], x["k64"][bs], x["v64"][bs], g)
-        assert report(f"step {step}", y.cpu().numpy()[bs], y_ref) <= 2e-2
-    assert report("A", g_A.cpu().numpy()[bs], dec.A) <= 2e-2
+        check(f"step {step}", y.cpu().numpy()[bs], y_ref, 2e-2)
+    check("A", g_A.cpu().numpy()[bs], dec.A, 2e-2)

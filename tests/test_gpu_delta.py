@@ -6,7 +6,7 @@ import torch
 from linear_attention_tensor_amd import inputs as I
 from linear_attention_tensor_amd import ops
 from oracle import delta as D
-from tests._helpers import f32_dev, report, to_dev
+from tests._helpers import f32_dev, check, report, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +28,14 @@ def run(x, S0=None):
     (1, 1, 64, 16, False),
     (1, 2, 1, 32, True),
     (1, 1, 257, 128, False),
+    # one ragged chunk (T < 64) and a full chunk plus a ragged one, at the
+    # widths of the bf16 LDS-DMA kernel
+    (1, 2, 1, 64, False),
+    (1, 2, 40, 64, True),
+    (2, 1, 100, 64, False),
+    (1, 2, 1, 128, True),
+    (1, 2, 40, 128, False),
+    (2, 1, 100, 128, True),
 ])
 def test_delta_small(dtype, B, H, T, d, with_s0):
     print(f"[case] delta dtype={dtype} B={B} H={H} T={T} d={d} S0={with_s0}", flush=True)
@@ -36,8 +44,8 @@ def test_delta_small(dtype, B, H, T, d, with_s0):
     o, S = run(x, S0)
     o_ref, S_ref = D.delta_scan(x["q64"], x["k64"], x["v64"], x["beta"].astype(np.float64),
                                 None if S0 is None else S0.astype(np.float64))
-    assert report("o", o, o_ref) <= TOL[dtype]
-    assert report("S", S, S_ref) <= TOL[dtype]
+    check("o", o, o_ref, TOL[dtype])
+    check("S", S, S_ref, TOL[dtype])
 
 
 def test_delta_beta_one_rereads_value():
@@ -46,7 +54,7 @@ def test_delta_beta_one_rereads_value():
     x["q"] = x["k"].copy()
     x["beta"] = np.ones_like(x["beta"])
     o, _ = run(x)
-    assert report("o vs v", o, x["v64"]) <= 1e-5
+    check("o vs v", o, x["v64"], 1e-5)
 
 
 def test_delta_workload_full_size_sampled_heads():
@@ -57,5 +65,5 @@ def test_delta_workload_full_size_sampled_heads():
     hs = [0, 7, 15]
     sl = (slice(None), hs)
     o_ref, S_ref = D.delta_scan(x["q64"][sl], x["k64"][sl], x["v64"][sl], x["beta"][sl].astype(np.float64))
-    assert report("o", o[sl], o_ref) <= 2e-2
-    assert report("S", S[sl], S_ref) <= 2e-2
+    check("o", o[sl], o_ref, 2e-2)
+    check("S", S[sl], S_ref, 2e-2)

@@ -6,7 +6,7 @@ import torch
 from linear_attention_tensor_amd import inputs as I
 from linear_attention_tensor_amd import ops
 from oracle import delta as D
-from tests._helpers import f32_dev, report, to_dev
+from tests._helpers import f32_dev, check, report, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -47,7 +47,7 @@ def test_delta_backward_small(B, H, T, d, states):
     got = run(x, do, S0, dSf)
     want = ref(x, do, S0, dSf)
     for name, a, b in zip(NAMES, got, want):
-        assert report(name, a, b) <= TOL, name
+        check(name, a, b, TOL)
 
 
 @pytest.mark.parametrize("beta_val", [0.0, 1.0])
@@ -60,7 +60,7 @@ def test_delta_backward_beta_edges(beta_val):
     got = run(x, do, S0)
     want = ref(x, do, S0)
     for name, a, b in zip(NAMES, got, want):
-        assert report(f"beta={beta_val} {name}", a, b) <= TOL, name
+        check(f"beta={beta_val} {name}", a, b, TOL)
 
 
 def test_delta_backward_empty_sequence():
@@ -95,4 +95,4 @@ def test_delta_backward_full_size_sampled_heads():
         want = D.delta_scan_backward(xs["q64"], xs["k64"], xs["v64"], xs["beta"].astype(np.float64),
                                      do[b:b + 1, h:h + 1].astype(np.float64))
         for name, a, r in zip(NAMES, got, want):
-            assert report(f"b={b} h={h} {name}", a[b:b + 1, h:h + 1], r) <= TOL, name
+            check(f"b={b} h={h} {name}", a[b:b + 1, h:h + 1], r, TOL)

@@ -8,7 +8,7 @@ import torch
 from linear_attention_tensor_amd import inputs as I
 from linear_attention_tensor_amd import ops
 from oracle import tc as O
-from tests._helpers import f32_dev, report, to_dev
+from tests._helpers import f32_dev, check, report, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +38,8 @@ def test_fused_small(B, H, T, d, W):
     y, A = run(x, W)
     y_ref, A_ref = O.tc_fused(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64), x["eta"],
                               x["g"].astype(np.float64), W)
-    assert report("y", y, y_ref) <= 2e-2
-    assert report("A", A, A_ref) <= 2e-2
+    check("y", y, y_ref, 2e-2)
+    check("A", A, A_ref, 2e-2)
 
 
 def test_fused_gate_closed_is_sliding_window():
@@ -47,7 +47,7 @@ def test_fused_gate_closed_is_sliding_window():
     W = 96
     y, _ = run(x, W, g=np.full(2, -1e4, np.float32), scale=0.2)
     ref = O.window_softmax(x["q64"], x["k64"], x["v64"], W, 0.2)
-    assert report("y", y, ref) <= 2e-2
+    check("y", y, ref, 2e-2)
 
 
 def test_fused_layer_full_size_sampled_rows():
@@ -58,4 +58,4 @@ def test_fused_layer_full_size_sampled_rows():
     rows = [0, 1, 63, 64, w.W - 1, w.W, w.W + 1, w.W + 127, 4097, 16383, 16384, 30000, w.T - 64, w.T - 1]
     ref = O.tc_fused_rows(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64), x["eta"],
                           x["g"].astype(np.float64), w.W, rows)
-    assert report("y rows", y[:, :, rows], ref) <= 2e-2
+    check("y rows", y[:, :, rows], ref, 2e-2)

@@ -7,7 +7,7 @@ import torch
 from linear_attention_tensor_amd import inputs as I
 from linear_attention_tensor_amd import ops
 from oracle import hebbian as Hb
-from tests._helpers import f32_dev, report
+from tests._helpers import f32_dev, check, report
 
 pytestmark = pytest.mark.gpu
 
@@ -52,9 +52,9 @@ def test_hebbian_write_read_recall(F, m, d, nv):
     arg, best = ops.recall_argmax(out[None].contiguous(), V[None].contiguous())
     torch.cuda.synchronize()
     B_ref = Hb.hebbian_write(x["K"], x["V"], x["f"], x["A"], x["G"])
-    assert report("B", Bt.cpu().numpy(), B_ref.T) <= TOL
+    check("B", Bt.cpu().numpy(), B_ref.T, TOL)
     out_ref = Hb.hebbian_read(x["K"], B_ref, x["A"], x["G"])
-    assert report("read", out.cpu().numpy(), out_ref) <= TOL
+    check("read", out.cpu().numpy(), out_ref, TOL)
     check_argmax(arg.cpu().numpy()[0], out_ref, f64(x["V"]), "recall")
     # the stored fraction from the GPU picks agrees with the oracle's within the near-ties
     frac_gpu = float(np.mean(arg.cpu().numpy()[0] == x["f"]))
@@ -72,7 +72,7 @@ def test_hebbian_index_outside_the_values_adds_nothing():
     keep = (f >= 0) & (f < 200)
     Phi = Hb.features(x["K"], x["A"], x["G"])
     ref = f64(x["V"])[f[keep]].T @ Phi[keep] / 200
-    assert report("B", Bt.cpu().numpy(), ref.T) <= TOL
+    check("B", Bt.cpu().numpy(), ref.T, TOL)
 
 
 @pytest.mark.parametrize("groups,n,d", [(3, 100, 64), (1, 64, 32), (5, 7, 128), (2, 130, 128)])
@@ -83,7 +83,7 @@ def test_memory_read(groups, n, d):
     out = ops.tc_memory_read(dev(Q), dev(A))
     torch.cuda.synchronize()
     ref = np.einsum("gni,giv->gnv", f64(Q), f64(A))
-    assert report("q A", out.cpu().numpy(), ref) <= TOL
+    check("q A", out.cpu().numpy(), ref, TOL)
 
 
 @pytest.mark.parametrize("groups,nq,nc,d", [(4, 70, 1000, 64), (1, 5, 3, 32), (2, 200, 129, 128)])
@@ -96,7 +96,7 @@ def test_recall_argmax_groups(groups, nq, nc, d):
     for gr in range(groups):
         check_argmax(arg.cpu().numpy()[gr], f64(R[gr]), f64(V[gr]), f"group {gr}")
         ref_best = np.max(f64(R[gr]) @ f64(V[gr]).T, axis=1)
-        assert report("best", best.cpu().numpy()[gr], ref_best) <= TOL
+        check("best", best.cpu().numpy()[gr], ref_best, TOL)
 
 
 def test_recall_argmax_ties_take_the_smallest_index():
@@ -139,7 +139,7 @@ def test_hebbian_workload_full_size_sampled():
     arg, _ = ops.recall_argmax(out[None].contiguous(), V[None].contiguous())
     torch.cuda.synchronize()
     B_ref = Hb.hebbian_write(x["K"], x["V"], x["f"], x["A"], x["G"])
-    assert report("B", Bt.cpu().numpy(), B_ref.T) <= TOL
+    check("B", Bt.cpu().numpy(), B_ref.T, TOL)
     out_ref = Hb.hebbian_read(x["K"][rows], B_ref, x["A"], x["G"])
-    assert report("read", out.cpu().numpy(), out_ref) <= TOL
+    check("read", out.cpu().numpy(), out_ref, TOL)
     check_argmax(arg.cpu().numpy()[0], out_ref, f64(x["V"]), "recall")

@@ -6,7 +6,7 @@ import torch
 from linear_attention_tensor_amd import inputs as I
 from linear_attention_tensor_amd import ops
 from oracle import tc as O
-from tests._helpers import f32_dev, report, to_dev
+from tests._helpers import f32_dev, check, report, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -41,8 +41,8 @@ def test_scan_small(dtype, B, H, T, d, W):
     x = I.draw(B, H, T, d, seed=1000 + T + d, dtype=dtype)
     m, A = run(x, W)
     m_ref, A_ref = O.tc_scan(x["q64"], x["k64"], x["v64"], lam_of(x), x["eta"], W)
-    assert report("m", m, m_ref) <= TOL[dtype]
-    assert report("A", A, A_ref) <= TOL[dtype]
+    check("m", m, m_ref, TOL[dtype])
+    check("A", A, A_ref, TOL[dtype])
     assert np.all(m[:, :, : min(W, T)] == 0.0)
 
 
@@ -51,8 +51,8 @@ def test_scan_lambda_edges(lam_val):
     x = I.draw(1, 2, 333, 64, seed=77, dtype="f32", lam=("fixed", lam_val))
     m, A = run(x, 20)
     m_ref, A_ref = O.tc_scan(x["q64"], x["k64"], x["v64"], lam_of(x), x["eta"], 20)
-    assert report(f"m lam={lam_val}", m, m_ref) <= 1e-5
-    assert report(f"A lam={lam_val}", A, A_ref) <= 1e-5
+    check(f"m lam={lam_val}", m, m_ref, 1e-5)
+    check(f"A lam={lam_val}", A, A_ref, 1e-5)
 
 
 def test_scan_empty_sequence():
@@ -71,8 +71,8 @@ def test_scan_workloads_full_size(name):
     x = I.draw_workload(name)
     m, A = run(x, w.W)
     m_ref, A_ref = O.tc_scan(x["q64"], x["k64"], x["v64"], lam_of(x), x["eta"], w.W)
-    assert report(f"{name} m", m, m_ref) <= TOL[w.dtype]
-    assert report(f"{name} A", A, A_ref) <= TOL[w.dtype]
+    check(f"{name} m", m, m_ref, TOL[w.dtype])
+    check(f"{name} A", A, A_ref, TOL[w.dtype])
 
 
 def test_scan_fused_size_bf16_sampled_rows():
@@ -83,7 +83,7 @@ def test_scan_fused_size_bf16_sampled_rows():
     m, A = run(x, w.W)
     rows = [0, w.W - 1, w.W, w.W + 1, w.W + 63, w.W + 64, 5000, 16384, 20001, w.T - 65, w.T - 1]
     ref = O.tc_scan_rows(x["q64"], x["k64"], x["v64"], lam_of(x), x["eta"], w.W, rows)
-    assert report("m rows", m[:, :, rows], ref) <= 2e-2
+    check("m rows", m[:, :, rows], ref, 2e-2)
 
 
 @pytest.mark.parametrize("B,H,T,d,W", [
@@ -106,6 +106,6 @@ def test_scan_bf16_tiled_path(B, H, T, d, W):
     x = I.draw(B, H, T, d, seed=5000 + T + W, dtype="bf16", lam=("uniform", 0.95, 0.999))
     m, A = run(x, W)
     m_ref, A_ref = O.tc_scan(x["q64"], x["k64"], x["v64"], lam_of(x), x["eta"], W)
-    assert report("m", m, m_ref) <= 2e-2
-    assert report("A", A, A_ref) <= 2e-2
+    check("m", m, m_ref, 2e-2)
+    check("A", A, A_ref, 2e-2)
     assert np.all(m[:, :, : min(W, T)] == 0.0)

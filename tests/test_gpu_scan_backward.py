@@ -6,7 +6,7 @@ import torch
 from linear_attention_tensor_amd import inputs as I
 from linear_attention_tensor_amd import ops
 from oracle import tc as O
-from tests._helpers import f32_dev, report, to_dev
+from tests._helpers import f32_dev, check, report, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -20,12 +20,12 @@ def run(x, W, dm):
     return [t.cpu().numpy() for t in g]
 
 
-def check(x, W, dm, label):
+def check_case(x, W, dm, label):
     got = run(x, W, dm)
     ref = O.tc_scan_backward(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64),
                              x["eta"].astype(np.float64), W, dm.astype(np.float64))
     for name, a, b in zip(("dq", "dk", "dv", "dlam", "deta"), got, ref):
-        assert report(f"{label} {name}", a, b) <= TOL, name
+        check(f"{label} {name}", a, b, TOL)
     T = x["q"].shape[2]
     gq, gk, gv = got[:3]
     assert np.all(gq[:, :, : min(W, T)] == 0.0)
@@ -48,7 +48,7 @@ def test_scan_backward_small(B, H, T, d, W):
     print(f"[case] scan backward B={B} H={H} T={T} d={d} W={W}", flush=True)
     x = I.draw(B, H, T, d, seed=4000 + T + d, dtype="f32")
     dm = I.draw_cotangent(B, H, T, d, seed=4000 + T + d)
-    check(x, W, dm, "small")
+    check_case(x, W, dm, "small")
 
 
 @pytest.mark.parametrize("lam_val", [0.0, 1.0, 0.5])
@@ -56,7 +56,7 @@ def test_scan_backward_lambda_edges(lam_val):
     print(f"[case] scan backward lam={lam_val}", flush=True)
     x = I.draw(2, 2, 333, 64, seed=78, dtype="f32", lam=("fixed", lam_val))
     dm = I.draw_cotangent(2, 2, 333, 64, seed=78)
-    check(x, 20, dm, f"lam={lam_val}")
+    check_case(x, 20, dm, f"lam={lam_val}")
 
 
 def test_scan_backward_empty_sequence():
@@ -91,7 +91,7 @@ def test_scan_backward_prefill_full_size_sampled_heads():
                                  x["lam"][sl].astype(np.float64), x["eta"][sl].astype(np.float64),
                                  w.W, dm[:, sl].astype(np.float64))
         for name, a, b in zip(("dq", "dk", "dv", "dlam", "deta"), got, ref):
-            assert report(f"head {h} {name}", a[:, sl] if a.ndim == 4 else a[sl], b) <= TOL, name
+            check(f"head {h} {name}", a[:, sl] if a.ndim == 4 else a[sl], b, TOL)
 
 
 @pytest.mark.parametrize("B,H,T,d,W", [(2, 3, 300, 32, 17), (1, 2, 1000, 64, 100), (1, 1, 20, 16, 45)])
@@ -106,4 +106,4 @@ def test_scan_backward_through_the_gate(B, H, T, d, W):
     ref = O.tc_gated_read_backward(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64),
                                    x["eta"].astype(np.float64), g.astype(np.float64), W, dy.astype(np.float64))
     for name, a, b in zip(("dq", "dk", "dv", "dlam", "deta", "dg"), out, ref):
-        assert report(f"gated {name}", a.cpu().numpy(), b) <= TOL, name
+        check(f"gated {name}", a.cpu().numpy(), b, TOL)
