@@ -57,7 +57,13 @@ def _check_tensor(name: str, t: torch.Tensor, shape, dtype=None, device=None) ->
 
 
 def _check_unit_interval(name: str, t: torch.Tensor) -> None:
-    if t.numel() and (bool((t < 0).any()) or bool((t > 1).any()) or bool(torch.isnan(t).any())):
+    # Reading the verdict back synchronises with the device, which a stream
+    # under graph capture forbids: there the check is skipped (as with
+    # check_values=False, which latency-bound callers pass anyway).
+    if not t.numel() or torch.cuda.is_current_stream_capturing():
+        return
+    bad = (t < 0) | (t > 1) | torch.isnan(t)
+    if bool(bad.any()):
         raise ValueError(f"{name} must lie in [0, 1]")
 
 
@@ -183,7 +189,7 @@ def tc_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring_k: to
     _check_tensor("pos", pos, (B,), torch.int64, q.device)
     if check_values:
         _check_unit_interval("lam", lam)
-        if pos.numel() and bool((pos < 0).any()):
+        if pos.numel() and not torch.cuda.is_current_stream_capturing() and bool((pos < 0).any()):
             raise ValueError("pos must be >= 0")
     if m is None:
         m = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
@@ -218,7 +224,7 @@ def tc_decode_layer_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, ring
     _check_tensor("pos", pos, (B,), torch.int64, q.device)
     if check_values:
         _check_unit_interval("lam", lam)
-        if pos.numel() and bool((pos < 0).any()):
+        if pos.numel() and not torch.cuda.is_current_stream_capturing() and bool((pos < 0).any()):
             raise ValueError("pos must be >= 0")
     scale = 1.0 / math.sqrt(dk) if softmax_scale is None else float(softmax_scale)
     if y is None:
