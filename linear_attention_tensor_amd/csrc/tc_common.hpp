@@ -30,8 +30,16 @@ __device__ __forceinline__ int wave_id() {
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // drains every outstanding global load (s_waitcnt vmcnt(0)), which would
 // cancel register prefetching across the barrier.
+//
+// The wave's own LDS reads and writes are drained explicitly (s_waitcnt
+// lgkmcnt(0)) before s_barrier: a fence restricted to LDS lets the compiler
+// assume that the LDS of a CU serves every wave's requests in one order and
+// leave the wait out, but requests from different waves can be served out of
+// order, so a write issued just before the barrier could still be pending
+// when another wave reads the same address after it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
