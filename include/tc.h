@@ -78,6 +78,29 @@ tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype 
                           float* m, float* A_final, void* ws, size_t ws_bytes, hipStream_t s);
 
 /* ---------------------------------------------------------------------------
+ * tc_scan_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * tc_scan_forward, minus ws / ws_bytes.
+ *
+ * The scratch it needs (tc_scan_workspace_bytes(...) bytes for the same
+ * arguments) comes from a 32 MiB array that the library holds on every GPU
+ * it runs on, from the first call there until the process ends.  A call
+ * that needs more returns TC_ERR_WORKSPACE (and launches nothing); use
+ * tc_scan_forward with a workspace for those shapes.  It never calls
+ * hipMalloc or hipFree.
+ *
+ * Every call on one GPU shares that GPU's array, and each call overwrites
+ * the part it uses: calls that can overlap on one GPU (different streams,
+ * different host threads without ordering) race and must not be issued.
+ * The stream must belong to the current device.
+ * ------------------------------------------------------------------------- */
+tc_status tc_scan_forward_noalloc(const void* q, const void* k, const void* v, tc_dtype dt,
+                                  const float* lam, const float* eta,
+                                  int B, int H, int T, int dk, int dv, int W, int chunk,
+                                  float* m, float* A_final, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
  * Backward of the L2 read (Tensor Cache, Methodology 1 and 2: lam and eta
  * are learned per head), optionally through the gate of the fused layer
  * (Methodology 1, fusion: y = y_local + sigmoid(g) m with g learned per head).

@@ -32,6 +32,7 @@ _z = ctypes.c_size_t
 SIGNATURES = {
     "tc_scan_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "tc_scan_forward": (_i, [_p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _z, _p]),
+    "tc_scan_forward_noalloc": (_i, [_p, _p, _p, _i, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p]),
     "tc_scan_backward_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "tc_scan_backward": (_i, [_p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p,
                               _p, _p, _p, _z, _p]),

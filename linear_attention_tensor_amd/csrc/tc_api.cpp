@@ -3,6 +3,8 @@
 //
 // Every check runs before the first HIP call, so a rejected call launches
 // nothing and needs no device.  Nothing throws across the ABI.
+#include <hip/hip_runtime.h>
+
 #include "../../include/tc.h"
 #include "tc_kernels.hpp"
 
@@ -11,6 +13,7 @@
 #include <stdio.h>
 
 #include <exception>
+#include <mutex>
 
 namespace {
 
@@ -76,6 +79,42 @@ void profile_mark_after(hipStream_t s) {
 }
 }  // namespace tc
 
+// ---------------------------------------------------------------------------
+// Scratch memory of tc_scan_forward_noalloc: a file-scope device array that
+// each GPU the library runs on holds from module load to process end.  In
+// host code `scratch` names a host-side stand-in, not device memory: the
+// device address comes from hipGetSymbolAddress, once per device with that
+// device current, and only that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+tc_status current_scratch(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TC_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TC_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(TC_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TC_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 tc_status tc_profile_next_call(hipEvent_t before, hipEvent_t after) {
@@ -121,6 +160,42 @@ tc_status tc_scan_forward(const void* q, const void* k, const void* v, tc_dtype 
       return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
     if (T == 0 && !A_final) return ok();
+    if (fast16)
+      return from_hip(tc::launch_tc_scan_bf16(q, k, v, lam, eta, B, H, T, dk, W, m, A_final, ws, s), fn);
+    return from_hip(tc::launch_tc_scan(q, k, v, dt == TC_BF16, lam, eta, B, H, T, dk, dv, W, m,
+                                       A_final, ws, s),
+                    fn);
+  });
+}
+
+tc_status tc_scan_forward_noalloc(const void* q, const void* k, const void* v, tc_dtype dt,
+                                  const float* lam, const float* eta, int B, int H, int T, int dk,
+                                  int dv, int W, int chunk, float* m, float* A_final, hipStream_t s) {
+  return guarded("tc_scan_forward_noalloc", [&]() -> tc_status {
+    const char* fn = "tc_scan_forward_noalloc";
+    tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
+    if (st != TC_OK) return st;
+    if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+    if (B == 0 || H == 0) return ok();
+    if (!lam || !eta) return fail(TC_ERR_INVALID_ARG, "%s: lam and eta must not be NULL", fn);
+    if (T > 0 && (!q || !k || !v || !m))
+      return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, m must not be NULL", fn);
+    const bool fast16 = tc::scan_bf16_fast(dt == TC_BF16, dk, dv, T);
+    const size_t need = fast16 ? tc::scan_bf16_ws_bytes(B, H, T, dk, W)
+                               : tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
+    if (need > kScratchBytes)
+      return fail(TC_ERR_WORKSPACE,
+                  "%s: this call needs %zu bytes of scratch, more than the %zu the library holds per "
+                  "device; call tc_scan_forward with a workspace instead",
+                  fn, need, kScratchBytes);
+    if (T == 0 && !A_final) return ok();
+    void* ws = nullptr;
+    if (need > 0) {
+      st = current_scratch(fn, &ws);
+      if (st != TC_OK) return st;
+    }
+    // Every kernel below writes the scratch it reads (segment or tile states)
+    // earlier in the same call, so the previous call's contents never matter.
     if (fast16)
       return from_hip(tc::launch_tc_scan_bf16(q, k, v, lam, eta, B, H, T, dk, W, m, A_final, ws, s), fn);
     return from_hip(tc::launch_tc_scan(q, k, v, dt == TC_BF16, lam, eta, B, H, T, dk, dv, W, m,

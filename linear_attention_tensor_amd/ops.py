@@ -16,7 +16,7 @@ import torch
 from . import _lib
 from ._lib import TC_BF16, TC_F32, check, lib
 
-__all__ = ["tc_scan_forward", "tc_scan_backward", "tc_decode_step", "tc_decode_layer_step",
+__all__ = ["tc_scan_forward", "tc_scan_forward_noalloc", "tc_scan_backward", "tc_decode_step", "tc_decode_layer_step",
            "tc_fused_layer", "delta_scan_forward", "delta_scan_backward", "hebbian_write", "hebbian_read",
            "tc_memory_read", "recall_argmax", "scan_backward_workspace",
            "scan_workspace", "fused_workspace", "delta_workspace"]
@@ -125,6 +125,26 @@ def tc_scan_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torc
                                _stream())
     check("tc_scan_forward", st)
     return m, A
+
+
+def tc_scan_forward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torch.Tensor,
+                            eta: torch.Tensor, W: int, *, m: torch.Tensor,
+                            A_final: Optional[torch.Tensor] = None,
+                            check_values: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """tc_scan_forward into caller-given outputs with the library's own scratch:
+    nothing is allocated (m [B,H,T,dv] and A_final [B,H,dk,dv] or None)."""
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    _check_tensor("lam", lam, (H,), torch.float32, q.device)
+    _check_tensor("eta", eta, (H,), torch.float32, q.device)
+    _check_tensor("m", m, (B, H, T, dv), torch.float32, q.device)
+    if A_final is not None:
+        _check_tensor("A_final", A_final, (B, H, dk, dv), torch.float32, q.device)
+    if check_values:
+        _check_unit_interval("lam", lam)
+    st = lib().tc_scan_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(lam), _ptr(eta), B, H, T, dk,
+                                       dv, W, CHUNK, _ptr(m), _ptr(A_final), _stream())
+    check("tc_scan_forward_noalloc", st)
+    return m, A_final
 
 
 def scan_backward_workspace(B, H, T, dk, dv, W, dtype_code) -> int:

@@ -90,6 +90,24 @@ def test_scan_workspace_check():
     assert lib().tc_scan_workspace_bytes(1, 1, 10, 64, 64, 0, 64, _lib.TC_F32) == _lib.SIZE_MAX
 
 
+def test_scan_noalloc_rejects_before_any_device_call():
+    f = lib().tc_scan_forward_noalloc
+
+    def call(**kw):
+        a = dict(dt=_lib.TC_BF16, B=1, H=8, T=32768, d=128, W=1024, chunk=64, q=FAKE, m=FAKE)
+        a.update(kw)
+        return f(a["q"], FAKE, FAKE, a["dt"], FAKE, FAKE, a["B"], a["H"], a["T"], a["d"], a["d"], a["W"],
+                 a["chunk"], a["m"], NULL, NULL)
+
+    # more scratch than the library holds (64 MiB of bf16 tile states > 32 MiB)
+    assert call() == _lib.TC_ERR_WORKSPACE
+    assert "scratch" in _lib.last_error()
+    assert call(chunk=32) == _lib.TC_ERR_UNSUPPORTED
+    assert call(W=0) == _lib.TC_ERR_INVALID_ARG
+    assert call(q=NULL, B=1, H=1, T=16, d=16, W=4) == _lib.TC_ERR_INVALID_ARG
+    assert call(B=0) == _lib.TC_OK
+
+
 def test_decode_rejects():
     f = lib().tc_decode_step
     args = [FAKE, FAKE, FAKE, _lib.TC_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 128, 16, FAKE, NULL]
