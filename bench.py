@@ -38,8 +38,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed calls first: the GPU needs some tens of ms of load to reach its steady clock")
     ap.add_argument("--no-components", action="store_true", help="time only the fused layer")
+    ap.add_argument("--decode-steps", type=int, default=None,
+                    help="decode steps to time (default: the workload's 4096; 1024 for the 4x side run); "
+                         "short runs are for profiler counter passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fused", "scan", "scan_bf16", "scan_backward", "decode", "decode_layer", "delta",
+    ap.add_argument("--only", choices=["fused", "scan", "scan_bf16", "scan_backward", "decode", "decode_x4", "decode_layer", "delta",
                                            "delta_f32", "delta_backward", "hebbian", "capacity"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -217,6 +220,27 @@ class KernelTimer:
         return sum(out) / len(out)
 
 
+def counters_from_profile(name, source):
+    """Fields of a committed rocprofv3 counter summary profiles/<name>.txt
+    ("key: value" lines), or None when there is none or its recorded source
+    hash no longer matches csrc/<source>."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", name + ".txt")
+    src = os.path.join(ROOT, "linear_attention_tensor_amd", "csrc", source)
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("source_sha256_16") != digest:
+        return None
+    return fields
+
+
 def traffic_from_profile(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (profiles/traffic_<kernel>_fused_layer_bf16.txt), or None when
@@ -290,8 +314,11 @@ def bench_fused(steps, warmup, dev):
     main_flops = fused_main_flops(w.B, w.H, w.T, w.d, w.W)
     res = {
         "workload": w.name, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
-        "roofline": roofline("mfma", main_flops / (kernel_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s",
-                             traffic_from_profile("swa_kernel")),
+        "roofline": dict(roofline("mfma", main_flops / (kernel_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                  traffic_from_profile("swa_kernel")),
+                         scope="swa_kernel<128> alone: its algorithmic flops / its own event-timed duration"),
+        "layer_roofline": dict(roofline("mfma", flops / (ms_call * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
+                               scope="whole layer: all algorithmic flops / whole-call time"),
         "main_kernel": {"name": "swa_kernel<128>", "ms": kernel_ms, "algorithmic_flops": main_flops},
         "layer": {"ms_per_call": ms_call, "algorithmic_flops": flops,
                   "tflops": flops / (ms_call * 1e-3) / 1e12,
@@ -407,14 +434,18 @@ def bench_scan_backward(steps, warmup, dev):
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
 
 
-def bench_decode(steps, warmup, dev, n_steps=4096):
+def bench_decode(steps, warmup, dev, n_steps=4096, B=None):
+    """The decode workload's L2 step (4096 steps, 64 x 32 heads).  With B
+    given (the side run: 256 sequences, 512 MiB of A) the state no longer
+    fits the 256 MB Infinity Cache, so every step streams A from HBM."""
     import torch
 
     from linear_attention_tensor_amd import inputs as I
     from linear_attention_tensor_amd import ops
 
     w = I.WORKLOADS["decode_bf16"]
-    B, H, d, W = w.B, w.H, w.d, w.W
+    B = w.B if B is None else B
+    H, d, W = w.H, w.d, w.W
     gen = torch.Generator(device=dev).manual_seed(w.seed)
 
     def unit(x):
@@ -466,14 +497,25 @@ def bench_decode(steps, warmup, dev, n_steps=4096):
     ms_graph = graph_ms_per_step(launch, n_steps)
     per_head = decode_bytes_per_head(d)
     gbs = B * H * per_head / (kernel_ms * 1e-3) / 1e9
-    return {"workload": w.name, "ms_per_step": ms_graph, "tokens_per_s": B * H / (ms_graph * 1e-3),
-            "ms_per_step_eager": ms, "tokens_per_s_eager": B * H / (ms * 1e-3),
-            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
-            "note": "ms_per_step: the 4096 steps replayed as one HIP graph; eager: one launch per step with "
-                    "per-step events. A (128 MiB) fits the 256 MB Infinity Cache; GB/s is algorithmic "
-                    "bytes / kernel time",
-            "main_kernel": {"name": "decode_kernel", "ms": kernel_ms}, "ms_per_call": ms_call,
-            "config": {"B": B, "H": H, "d": d, "W": W, "steps": n_steps, "dtype_in": "bf16"}}
+    a_mib = B * H * d * d * 4 / 2 ** 20
+    name = w.name if B == w.B else f"{w.name} x{B // w.B} sequences"
+    tag = "decode_bf16" if B == w.B else f"decode_bf16_x{B // w.B}"
+    res = {"workload": name, "ms_per_step": ms_graph, "tokens_per_s": B * H / (ms_graph * 1e-3),
+           "ms_per_step_eager": ms, "tokens_per_s_eager": B * H / (ms * 1e-3),
+           "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
+           "note": f"ms_per_step: the {n_steps} steps replayed as one HIP graph; eager: one launch per step with "
+                   f"per-step events. A is {a_mib:.0f} MiB ({'inside' if a_mib < 256 else 'beyond'} the "
+                   f"256 MB Infinity Cache); GB/s is algorithmic bytes / kernel time",
+           "main_kernel": {"name": "decode_kernel", "ms": kernel_ms}, "ms_per_call": ms_call,
+           "algorithmic_bytes_per_step": B * H * per_head,
+           "config": {"B": B, "H": H, "d": d, "W": W, "steps": n_steps, "dtype_in": "bf16"}}
+    c = counters_from_profile(f"traffic_decode_kernel_{tag}", "tc_decode.hip")
+    if c is not None and "hbm_bytes_per_launch" in c:
+        hb = float(c["hbm_bytes_per_launch"])
+        res["hbm_counters"] = {"bytes_per_step": hb, "vs_algorithmic": hb / (B * H * per_head),
+                               "gbs": hb / (kernel_ms * 1e-3) / 1e9,
+                               "frac": hb / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    return res
 
 
 def bench_decode_layer(steps, warmup, dev, n_steps=256):
@@ -734,6 +776,7 @@ def cpu_baseline_fused(x, T_sample=16384):
         dt = time.perf_counter() - t0
     B, H = x["q64"].shape[:2]
     return {"value": B * H * T_sample / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host_cores": len(os.sched_getaffinity(0)), "blas_threads": 1,
             "sample": f"fused layer oracle (NumPy float64, BLAS limited to 1 thread) on the first {T_sample} "
                       f"tokens of all {B * H} heads of the same input ({dt:.1f} s; the first {w_W} tokens "
                       f"have shorter windows)"}
@@ -766,7 +809,9 @@ def main():
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
         components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
         components["scan_bf16_fused_size"] = bench_scan_bf16(args.steps, args.warmup, dev)
-        components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
+        components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 4096)
+        components["decode_bf16_x4"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 1024,
+                                                    B=256)
         components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
         components["delta_scan_f32"] = bench_delta_f32(args.steps, args.warmup, dev)
@@ -780,7 +825,10 @@ def main():
     elif only == "scan_backward":
         components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
     elif only == "decode":
-        components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev)
+        components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 4096)
+    elif only == "decode_x4":
+        components["decode_bf16_x4"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 1024,
+                                                    B=256)
     elif only == "decode_layer":
         components["decode_layer_bf16"] = bench_decode_layer(args.steps, args.warmup, dev)
     elif only == "delta":
@@ -811,11 +859,16 @@ def main():
         "data": "synthetic (seeded N(0,1/d) q,k,v with unit keys; per-head lam, eta, g)",
         "config": head["config"],
         "roofline": head["roofline"],
+        "layer_roofline": head["layer_roofline"],
         "main_kernel": head["main_kernel"],
         "layer": head["layer"],
     }
     if components:
         line["components"] = components
+        if "scan_bf16_fused_size" in components:
+            line["memory_scan_roofline"] = dict(
+                components["scan_bf16_fused_size"]["mfma"],
+                scope="the L2 memory scan alone (tc_scan_forward, bf16, same sizes): its flops / call time")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_fused(x)
     print(json.dumps(line))
