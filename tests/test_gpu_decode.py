@@ -6,7 +6,7 @@ import torch
 from linear_attention_tensor_amd import inputs as I
 from linear_attention_tensor_amd import ops
 from oracle import tc as O
-from tests._helpers import f32_dev, check, report, to_dev
+from tests._helpers import f32_dev, check, report, same_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -112,3 +112,93 @@ def test_decode_workload_full_size_sampled_sequences():
         m_ref = dec.step(x["q64"][bs], x["k64"][bs], x["v64"][bs])
         check(f"step {step}", m.cpu().numpy()[bs], m_ref, 2e-2)
     check("A", g_A.cpu().numpy()[bs], dec.A, 2e-2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_streaming_path_beyond_the_cache(dtype):
+    # 80 sequences x 32 heads at d = 128: 160 MiB of A, more than the library
+    # keeps cached, so A's stores are non-temporal.  Sampled sequences against
+    # the oracle, and bit for bit against the same sequences run alone (40 MiB
+    # of A: the cached path, same arithmetic).
+    B, H, d, W = 80, 32, 128, 8
+    print(f"[case] decode streaming path {dtype}", flush=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    rk, rv = I.draw_ring(B, H, W, d, dtype=dtype)
+    A0 = (np.random.default_rng(21).standard_normal((B, H, d, d)) * 0.05).astype(np.float32)
+    sc = I.decode_scalars(H)
+    lam, eta = f32_dev(sc["lam"]), f32_dev(sc["eta"])
+    bs = [0, 41, 79]
+    big = [to_dev(rk, dtype), to_dev(rv, dtype), f32_dev(A0)]
+    small = [to_dev(rk[bs], dtype), to_dev(rv[bs], dtype), f32_dev(A0[bs])]
+    assert big[0].dtype == tdt
+    dec = O.TensorCacheDecoder.from_state(I.storage_to_f64(rk[bs], dtype), I.storage_to_f64(rv[bs], dtype),
+                                          A0[bs].astype(np.float64), np.full(len(bs), W), W, sc["lam"], sc["eta"])
+    for step in range(3):
+        x = I.draw_decode_position(B, H, d, W + step, dtype=dtype)
+        qkv = [to_dev(x[n], dtype) for n in ("q", "k", "v")]
+        m_big = ops.tc_decode_step(*qkv, *big, lam, eta, torch.full((B,), W + step, dtype=torch.int64, device="cuda"), W)
+        m_small = ops.tc_decode_step(*(t[bs].contiguous() for t in qkv), *small, lam, eta,
+                                     torch.full((len(bs),), W + step, dtype=torch.int64, device="cuda"), W)
+        same_bits(f"step {step} m: streaming vs cached path", m_big[bs], m_small)
+        m_ref = dec.step(x["q64"][bs], x["k64"][bs], x["v64"][bs])
+        check(f"step {step}", m_big.cpu().numpy()[bs], m_ref, TOL[dtype])
+    same_bits("A: streaming vs cached path", big[2][bs], small[2])
+    check("A", big[2].cpu().numpy()[bs], dec.A, TOL[dtype])
+
+
+def test_decode_workload_full_length_streamed_parity():
+    # The whole decode workload: 64 sequences x 32 heads, d = 128, W = 2048,
+    # bf16, a full ring at pos = W and A = 0, then all 4096 steps (every one
+    # evicts).  Two sequences (64 heads) are followed by the oracle through
+    # every step; the error is accumulated per 256-step chunk (squared error
+    # and squared reference), each chunk held to the bf16 bar, and the final
+    # A of those sequences too.  The inputs come from a seeded device
+    # generator (the N(0, 1/d) / unit-key recipe), rounded to bf16 once; the
+    # oracle consumes the same rounded values.
+    w = I.WORKLOADS["decode_bf16"]
+    B, H, d, W, S = w.B, w.H, w.d, w.W, w.steps
+    print("[case] decode full length", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(4104)
+
+    def unit(t):
+        return t / t.norm(dim=-1, keepdim=True)
+
+    scale = d ** -0.5
+    qs = (torch.randn((S, B, H, d), generator=gen, device="cuda") * scale).to(torch.bfloat16)
+    ks = unit(torch.randn((S, B, H, d), generator=gen, device="cuda")).to(torch.bfloat16)
+    vs = (torch.randn((S, B, H, d), generator=gen, device="cuda") * scale).to(torch.bfloat16)
+    rk, rv = I.draw_ring(B, H, W, d)
+    g_rk, g_rv = to_dev(rk, "bf16"), to_dev(rv, "bf16")
+    g_A = torch.zeros((B, H, d, d), dtype=torch.float32, device="cuda")
+    sc = I.decode_scalars(H)
+    lam, eta = f32_dev(sc["lam"]), f32_dev(sc["eta"])
+    bs = [5, 58]
+    ms = torch.empty((S, len(bs), H, d), dtype=torch.float32, device="cuda")
+    pos_all = (W + torch.arange(S, device="cuda", dtype=torch.int64))[:, None].repeat(1, B).contiguous()
+    for s in range(S):
+        m = ops.tc_decode_step(qs[s], ks[s], vs[s], g_rk, g_rv, g_A, lam, eta, pos_all[s], W, check_values=False)
+        ms[s] = m[bs]
+    torch.cuda.synchronize()
+    print("[case] decode full length: GPU done, oracle running", flush=True)
+
+    def host(t):
+        return t[:, bs].float().cpu().numpy().astype(np.float64)
+
+    q64, k64, v64 = host(qs), host(ks), host(vs)
+    m_gpu = ms.cpu().numpy()
+    dec = O.TensorCacheDecoder.from_state(I.storage_to_f64(rk[bs], "bf16"), I.storage_to_f64(rv[bs], "bf16"),
+                                          np.zeros((len(bs), H, d, d)), np.full(len(bs), W), W,
+                                          sc["lam"], sc["eta"])
+    chunk = 256
+    worst = 0.0
+    for c0 in range(0, S, chunk):
+        num = den = 0.0
+        for s in range(c0, min(S, c0 + chunk)):
+            ref = dec.step(q64[s], k64[s], v64[s])
+            num += float(np.sum((m_gpu[s] - ref) ** 2))
+            den += float(np.sum(ref ** 2))
+        rel = (num / den) ** 0.5
+        worst = max(worst, rel)
+        assert rel <= 2e-2, f"steps {c0}..{c0 + chunk - 1}: rel-L2 {rel:.3e}"
+    print(f"[parity] decode full length: worst 256-step chunk rel_l2={worst:.3e}", flush=True)
+    check("A after 4096 steps", g_A.cpu().numpy()[bs], dec.A, 2e-2)
