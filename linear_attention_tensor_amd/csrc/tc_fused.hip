@@ -567,20 +567,21 @@ hipError_t run_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
   const size_t ne = state_elems(G, B, H, D);
   uint16_t* delta = static_cast<uint16_t*>(ws);
   uint16_t* sst = delta + ne;
-  uint16_t* vt = sst + ne;
-  // about one pre-pass workgroup per CU, each streaming several tiles
+  // about one pre-pass workgroup per CU, each streaming several tiles; the
+  // main kernel reads V rows itself (LDS transpose reads): no V^T copy
   FusedGeom Gs = G;
+  Gs.vt_copy = 0;
   const long units = (long)G.n_tiles * BH;
   Gs.tiles_per_seg = (int)std::max<long>(1, (units + kPrepassWorkgroups - 1) / kPrepassWorkgroups);
   const int n_seg = (G.n_tiles + Gs.tiles_per_seg - 1) / Gs.tiles_per_seg;
   hipLaunchKernelGGL(fused_state_kernel<D>, dim3(n_seg, BH), dim3(NTHR), 0, s, k, v, lam, eta, H, Gs,
-                     delta, vt);
+                     delta, static_cast<uint16_t*>(nullptr));
   hipLaunchKernelGGL(fused_prefix_kernel, dim3((D * D / 4 + 63) / 64, BH), dim3(64), 0, s, lam, H, D,
                      G, delta, sst, A_final);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   profile_mark_before(s);
-  const hipError_t e2 = launch_swa(q, k, vt, sst, lam, eta, g, B, H, G.T, D, G.W, G.Tp, G.voff, scale, y, s);
+  const hipError_t e2 = launch_swa(q, k, v, sst, lam, eta, g, B, H, G.T, D, G.W, scale, y, s);
   profile_mark_after(s);
   return e2;
 }
@@ -620,9 +621,7 @@ size_t scan_bf16_ws_bytes(int B, int H, int T, int d, int W) {
 
 size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W) {
   (void)dv;
-  const FusedGeom G = make_geom(T, W);
-  return state_elems(G, B, H, dk) * 2 * sizeof(uint16_t) +
-         (size_t)B * H * dk * G.Tp * sizeof(uint16_t);
+  return state_elems(make_geom(T, W), B, H, dk) * 2 * sizeof(uint16_t);
 }
 
 bool scan_bf16_fast(bool bf16, int dk, int dv, int T) { return bf16 && dk == dv && (dk == 64 || dk == 128) && T > 0; }

@@ -58,12 +58,12 @@ hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, cons
 hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const float* lam,
                            const float* eta, const float* g, int B, int H, int T, int d, int W,
                            float scale, float* y, float* A_final, void* ws, hipStream_t s);
-// Main kernel of the fused layer (tc_swa.hip): vt is the V^T copy ([B*H][d][Tp],
-// key j in column j + voff), sst the entering state of every 256-query tile
+// Main kernel of the fused layer (tc_swa.hip): q, k, v rows [B*H][T][d] bf16,
+// sst the entering state of every 256-query tile
 // ([B*H][ceil(T/256)][d][d] bf16, S^T) or nullptr for no L2 term.
-hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* vt, const uint16_t* sst,
+hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* sst,
                       const float* lam, const float* eta, const float* g, int B, int H, int T, int d,
-                      int W, int Tp, int voff, float scale, float* y, hipStream_t s);
+                      int W, float scale, float* y, hipStream_t s);
 
 size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, bool bf16);
 hipError_t launch_delta_scan(const void* q, const void* k, const void* v, bool bf16,

@@ -14,10 +14,11 @@
 // Keys are taken in 64-key blocks from j0 = t0 - W (c = j - j0, r = t - t0;
 // key j is in the window of query t iff r < c <= r + W, and has been written
 // into the L2 memory iff c <= r).  Blocks travel global -> LDS by
-// buffer_load ... lds (K row-major, V^T from the transposed copy in the
-// workspace), four blocks resident.  S^T = K Q^T puts one query's scores in
-// every lane (v_mfma_f32_32x32x16_bf16), and P feeds O^T += V^T P^T from
-// registers.  The loop is software-pipelined: the QK^T MFMAs of block i+1
+// buffer_load ... lds (K and V rows as they are in memory, 16-byte pieces
+// permuted within each row), four blocks resident.  S^T = K Q^T puts one
+// query's scores in every lane (v_mfma_f32_32x32x16_bf16), and P feeds
+// O^T += V^T P^T from registers; the V^T operand comes from the V rows by
+// LDS transpose reads (ds_read_b64_tr_b16), so V needs no transposed copy.  The loop is software-pipelined: the QK^T MFMAs of block i+1
 // are interleaved with the softmax of block i and its PV MFMAs, so the matrix
 // cores and the vector ALUs work at the same time.  Blocks 4.. come first and
 // blocks 0-3 last, so the latter (the tile's evictions) are still resident
@@ -50,14 +51,26 @@ constexpr float kNegBig = -1.0e30f;
 template <int D>
 struct SwaLds {
   uint16_t k[NSTAGE][KB * D];
-  uint16_t vt[NSTAGE][D * KB];
+  uint16_t v[NSTAGE][KB * D];  // V rows (key-major), 16-byte pieces permuted per row (v_swz)
   uint16_t st[D * D];  // entering L2 state S^T (rows dv), as D/64 K-layout blocks
 };
+
+// V block layout: row c (key c of the block) holds that key's D features; its
+// 16-byte piece p (features 8p .. 8p+7) sits at position p ^ v_swz(c).  A
+// transpose read of PV k-step j gives the 16 lanes of a quarter wave 4 keys
+// (rows) of 16 features: over the wave 8 rows x 4 pieces, and the XOR puts
+// every 4-bank group under exactly two of the 32 pieces (two LDS cycles, no
+// further conflict).
+template <int D>
+__device__ __forceinline__ int v_swz(int c) {
+  static_assert(D == 64 || D == 128, "V rows of 8 or 16 pieces");
+  return D == 128 ? 4 * (c & 3) : 4 * ((c >> 1) & 1);
+}
 
 template <int D>
 struct Dma {
   static constexpr int NK = KB * D / 8 / NTHR;  // 16-byte K slots per thread
-  static constexpr int NV = D * 8 / NTHR;       // 16-byte V^T slots per thread
+  static constexpr int NV = KB * D / 8 / NTHR;  // 16-byte V slots per thread
   static constexpr int N = NK + NV;
 };
 
@@ -69,7 +82,7 @@ struct DmaOff {
 };
 
 template <int D>
-__device__ __forceinline__ DmaOff<D> dma_offsets(int Tp, int voff) {
+__device__ __forceinline__ DmaOff<D> dma_offsets() {
   DmaOff<D> o;
   const int w = wave_id(), l = lane_id();
 #pragma unroll
@@ -80,25 +93,24 @@ __device__ __forceinline__ DmaOff<D> dma_offsets(int Tp, int voff) {
   }
 #pragma unroll
   for (int i = 0; i < Dma<D>::NV; ++i) {
-    int dv, c;
-    v_slot_inv((i * NWAVE + w) * 64 + l, dv, c);
-    o.v[i] = (dv * Tp + voff + 8 * c) * 2;
+    // slot s of the stage holds row s / (D / 8), position s % (D / 8)
+    const int sl = (i * NWAVE + w) * 64 + l, row = sl / (D / 8), pos = sl % (D / 8);
+    o.v[i] = (row * D + 8 * (pos ^ v_swz<D>(row))) * 2;
   }
   return o;
 }
 
-// DMA of the 64-key block starting at key j (any sign) into one stage.  dk:
-// this head's K rows [0, T); dvt: its V^T copy, rows of Tp columns, key j in
-// column j + voff.  Reads outside the descriptors return zero.  Instruction
-// i of wave w fills the 1 KiB piece i * 8 + w of the stage.
+// DMA of the 64-key block starting at key j (any sign) into one stage.  dk,
+// dv: this head's K and V rows [0, T).  Reads outside the descriptors return
+// zero.  Instruction i of wave w fills the 1 KiB piece i * 8 + w of the stage.
 template <int D>
-__device__ __forceinline__ void dma_block(i32x4 dk, i32x4 dvt, const DmaOff<D>& off, int j,
-                                          uint16_t* sk, uint16_t* svt) {
+__device__ __forceinline__ void dma_block(i32x4 dk, i32x4 dv, const DmaOff<D>& off, int j,
+                                          uint16_t* sk, uint16_t* sv) {
   const int w = wave_id();
 #pragma unroll
   for (int i = 0; i < Dma<D>::NK; ++i) dma16(dk, sk + (i * NWAVE + w) * 512, off.k[i] + j * D * 2);
 #pragma unroll
-  for (int i = 0; i < Dma<D>::NV; ++i) dma16(dvt, svt + (i * NWAVE + w) * 512, off.v[i] + j * 2);
+  for (int i = 0; i < Dma<D>::NV; ++i) dma16(dv, sv + (i * NWAVE + w) * 512, off.v[i] + j * D * 2);
 }
 
 // DMA of the tile's entering state (bf16, [dv][dk] row-major in global) into
@@ -122,9 +134,9 @@ __device__ __forceinline__ void dma_state(i32x4 dst_desc, uint16_t* sst) {
 // the workgroup's 32 copy instructions do not all queue at the same moment.
 template <int D>
 struct DmaJob {
-  i32x4 dk, dvt;
-  int koff, voff;     // block start in bytes: j * D * 2 (K rows), j * 2 (V^T columns)
-  uint16_t *sk, *svt;
+  i32x4 dk, dv;
+  int off;            // block start in bytes: j * D * 2 (K and V rows)
+  uint16_t *sk, *sv;
   bool on;            // a block is left to fetch
 };
 template <int D, int I>
@@ -132,9 +144,9 @@ __device__ __forceinline__ void dma_part(const DmaJob<D>& job, const DmaOff<D>& 
   if (!job.on) return;
   const int w = wave_id();
   if constexpr (I < Dma<D>::NK)
-    dma16(job.dk, job.sk + (I * NWAVE + w) * 512, off.k[I] + job.koff);
+    dma16(job.dk, job.sk + (I * NWAVE + w) * 512, off.k[I] + job.off);
   else
-    dma16(job.dvt, job.svt + ((I - Dma<D>::NK) * NWAVE + w) * 512, off.v[I - Dma<D>::NK] + job.voff);
+    dma16(job.dv, job.sv + ((I - Dma<D>::NK) * NWAVE + w) * 512, off.v[I - Dma<D>::NK] + job.off);
 }
 
 // max / sum over the two 32-lane halves (the two halves of a query's keys)
@@ -171,11 +183,38 @@ __device__ __forceinline__ void mm_k2(const bf16x8* x, const bf16x8* qreg, float
     a1 = mfma32(x[2 * i + 1], qreg[KS + i], a1);
   }
 }
-// V^T operands of PV k-step kk (lane slot ls_kk), all D/32 row tiles
-template <int D>
-__device__ __forceinline__ void ld_v(const char* svt, uint32_t ls_kk, bf16x8* x) {
+// V^T operands of PV k-step KK, all D/32 row tiles: lane (col, hh) needs
+// keys 16 KK + 8 hh .. +7 of feature 32 dt + col.  Each comes from two
+// transpose reads of 4 key rows; vls[dt] is the lane's byte offset for tile dt
+// (v_lane_offsets), the key rows add immediates.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr(const char* base, uint32_t off) {
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + off));
+  return __builtin_bit_cast(uint2, x);
+}
+template <int D, int KK>
+__device__ __forceinline__ void ld_v(const char* sv, const uint32_t* vls, bf16x8* x) {
+  constexpr uint32_t RB = 2 * D;  // bytes per V row
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) x[dt] = lds16(svt, ls_kk + 4096u * dt);
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const uint2 a = lds_tr(sv, vls[dt] + (16 * KK) * RB);
+    const uint2 b = lds_tr(sv, vls[dt] + (16 * KK + 4) * RB);
+    x[dt] = as_bf16x8(a.x, a.y, b.x, b.y);
+  }
+}
+// Lane offsets of the transpose reads (ld_v): the 16 lanes i of a quarter
+// wave (feature half (col / 16) % 2, key half hh) read row 8 hh + i / 4 at
+// features 32 dt + 16 ((col / 16) % 2) + 4 (i % 4), placed by v_swz.
+template <int D>
+__device__ __forceinline__ void v_lane_offsets(uint32_t* vls) {
+  const int l = lane_id(), col = l & 31, hh = l >> 5, i = col & 15;
+  const int row = 8 * hh + (i >> 2);
+  const int piece_lo = ((col & 16) >> 3) + ((col & 3) >> 1);  // piece within the 32 features of a tile
+  const int half = col & 1;                                    // 8-byte half of that piece
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+    vls[dt] = (uint32_t)(row * 2 * D + 16 * ((4 * dt + piece_lo) ^ v_swz<D>(row)) + 8 * half);
 }
 template <int D>
 __device__ __forceinline__ void mm_v(const bf16x8* x, bf16x8 pb, floatx16* o) {
@@ -252,11 +291,12 @@ __device__ __forceinline__ bf16x8 probs(const floatx16* sc, float sl2, float nms
 // One pipelined step: QK^T of the next block (into sn) interleaved with the
 // softmax of the current block (sc) and its PV product.
 template <int D>
-__device__ __forceinline__ void swa_step(const char* sk_nxt, const char* svt_cur, const uint32_t* ls,
-                                         const bf16x8* qreg, floatx16* sc, floatx16* sn, floatx16* o,
+__device__ __forceinline__ void swa_step(const char* sk_nxt, const char* sv_cur, const uint32_t* ls,
+                                         const uint32_t* vls, const bf16x8* qreg, floatx16* sc, floatx16* sn, floatx16* o,
                                          Softmax& sm, float sl2, bool active, bool masked, KeyRange kr,
                                          const DmaJob<D>& job, const DmaOff<D>& doff) {
   constexpr int NDT = D / 32;
+  constexpr int NVR = 2 * NDT;  // LDS reads of one V operand batch (two transpose reads per tile)
   constexpr int ND = Dma<D>::N;  // 4 for D = 128, 2 for D = 64
   if (!active) {
     dma_part<D, 0>(job, doff);
@@ -332,37 +372,37 @@ __device__ __forceinline__ void swa_step(const char* sk_nxt, const char* svt_cur
     p0 = probs<0>(sc, sl2, nms, psum);
     TC_GROUPS(4, 4, 6);
     TC_SB();
-    ld_v<D>(svt_cur, ls[0], va);
+    ld_v<D, 0>(sv_cur, vls, va);
     mm_k2<6>(kb, qreg, a0, a1);
   } else {
     dma_part<D, 1>(job, doff);
     TC_SB();
-    ld_v<D>(svt_cur, ls[0], va);
+    ld_v<D, 0>(sv_cur, vls, va);
     mm_k2<2>(kb, qreg, a0, a1);
     p0 = probs<0>(sc, sl2, nms, psum);
-    TC_GROUPS(NDT, 4, 6);
+    TC_GROUPS(NVR, 4, 6);
     TC_SB();
   }
   p1 = probs<1>(sc, sl2, nms, psum);
   if constexpr (D == 128) {
-    TC_GROUPS(NDT, 4, 6);
+    TC_GROUPS(NVR, 4, 6);
     TC_SB();
   }
   if constexpr (D == 128) {
     dma_part<D, 3>(job, doff);
     TC_SB();
   }
-  ld_v<D>(svt_cur, ls[1], vb);
+  ld_v<D, 1>(sv_cur, vls, vb);
   mm_v<D>(va, p0, o);
   p2 = probs<2>(sc, sl2, nms, psum);
-  TC_GROUPS(NDT, NDT, 24 / NDT);
+  TC_GROUPS(NVR, NDT, 24 / NDT);
   TC_SB();
-  ld_v<D>(svt_cur, ls[2], va);
+  ld_v<D, 2>(sv_cur, vls, va);
   mm_v<D>(vb, p1, o);
   p3 = probs<3>(sc, sl2, nms, psum);
-  TC_GROUPS(NDT, NDT, 24 / NDT);
+  TC_GROUPS(NVR, NDT, 24 / NDT);
   TC_SB();
-  ld_v<D>(svt_cur, ls[3], vb);
+  ld_v<D, 3>(sv_cur, vls, vb);
   mm_v<D>(va, p2, o);
   TC_SB();
   mm_v<D>(vb, p3, o);
@@ -402,8 +442,8 @@ __device__ __forceinline__ bf16x8 l2probs(const floatx16* s, int lo, unsigned sp
 // L2 term of one resident block b (0..3) of the tile's evictions:
 // o += V^T P^T with P[c][r] = fe lam^(r-c) <q_r, k_c> for c <= r, 0 <= j.
 template <int D>
-__device__ __forceinline__ void l2_block(const char* sk, const char* svt, const uint32_t* ls,
-                                         const bf16x8* qreg, floatx16* o, int b, int jb, int r,
+__device__ __forceinline__ void l2_block(const char* sk, const char* sv, const uint32_t* ls,
+                                         const uint32_t* vls, const bf16x8* qreg, floatx16* o, int b, int jb, int r,
                                          float log2lam, float fe) {
   constexpr int NDT = D / 32;
   const int hh = lane_id() >> 5;
@@ -422,18 +462,18 @@ __device__ __forceinline__ void l2_block(const char* sk, const char* svt, const 
   const float xl = static_cast<float>(hi - 8 * hh) * log2lam;
   bf16x8 va[NDT], vb[NDT];
   TC_SB();
-  ld_v<D>(svt, ls[0], va);
+  ld_v<D, 0>(sv, vls, va);
   const bf16x8 p0 = l2probs<0>(s, lo, span, xl, log2lam, fe);
   TC_SB();
-  ld_v<D>(svt, ls[1], vb);
+  ld_v<D, 1>(sv, vls, vb);
   mm_v<D>(va, p0, o);
   const bf16x8 p1 = l2probs<1>(s, lo, span, xl, log2lam, fe);
   TC_SB();
-  ld_v<D>(svt, ls[2], va);
+  ld_v<D, 2>(sv, vls, va);
   mm_v<D>(vb, p1, o);
   const bf16x8 p2 = l2probs<2>(s, lo, span, xl, log2lam, fe);
   TC_SB();
-  ld_v<D>(svt, ls[3], vb);
+  ld_v<D, 3>(sv, vls, vb);
   mm_v<D>(va, p2, o);
   const bf16x8 p3 = l2probs<3>(s, lo, span, xl, log2lam, fe);
   TC_SB();
@@ -451,9 +491,9 @@ __device__ __forceinline__ bf16x8 scale_bf16x8(bf16x8 x, float f) {
 template <int D>
 __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ k,
-                                                   const uint16_t* __restrict__ vt, L2Args l2,
-                                                   int T, int W, int Tp, int voff, int n_tiles,
-                                                   int n_items, float sl2, float* __restrict__ y) {
+                                                   const uint16_t* __restrict__ v, L2Args l2,
+                                                   int T, int W, int n_tiles, int n_items, float sl2,
+                                                   float* __restrict__ y) {
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
   __shared__ __attribute__((aligned(16))) SwaLds<D> lds;
@@ -469,8 +509,8 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
   const long base = (long)bh * T;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + base * D, (uint32_t)T * D * 2);
   const i32x4 rk = raw_desc(k + base * D, (uint32_t)T * D * 2);
-  const i32x4 rvt = raw_desc(vt + (long)bh * D * Tp, (uint32_t)D * Tp * 2);
-  const DmaOff<D> doff = dma_offsets<D>(Tp, voff);
+  const i32x4 rv = raw_desc(v + base * D, (uint32_t)T * D * 2);
+  const DmaOff<D> doff = dma_offsets<D>();
 
   const int t0 = tile * MQ;
   const int j0 = t0 - W;
@@ -497,6 +537,8 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
   uint32_t ls[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) ls[j] = lane_slot(j);
+  uint32_t vls[NDT];
+  v_lane_offsets<D>(vls);
 
   // Copies complete in issue order: blocks 0..2, then the state (used only in
   // the epilogue).  The state is issued after the first scores: the compiler
@@ -505,7 +547,7 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
   constexpr int NS = D * D / 8 / NTHR;  // state copy instructions per thread
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i)
-    dma_block<D>(rk, rvt, doff, j0 + KB * block_at(i), lds.k[i], lds.vt[i]);
+    dma_block<D>(rk, rv, doff, j0 + KB * block_at(i), lds.k[i], lds.v[i]);
   wait_vmcnt<2 * Dma<D>::N>();
   lds_barrier();
   floatx16 s0[2], s1[2];
@@ -526,7 +568,7 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
     {
       const int st = (idx + NSTAGE - 1) & (NSTAGE - 1);
       const int jn = j0 + KB * block_at(idx + NSTAGE - 1);
-      job = DmaJob<D>{rk, rvt, jn * D * 2, jn * 2, lds.k[st], lds.vt[st], idx + NSTAGE - 1 < nb};
+      job = DmaJob<D>{rk, rv, jn * D * 2, lds.k[st], lds.v[st], idx + NSTAGE - 1 < nb};
     }
     const int b = block_at(idx);
     const int c_lo = KB * b, jb = j0 + c_lo;
@@ -547,7 +589,7 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
     }
     kr.lo = lo - 8 * hh;
     swa_step<D>(reinterpret_cast<const char*>(lds.k[(idx + 1) & (NSTAGE - 1)]),
-                reinterpret_cast<const char*>(lds.vt[idx & (NSTAGE - 1)]), ls, qreg, sc, sn, o, sm,
+                reinterpret_cast<const char*>(lds.v[idx & (NSTAGE - 1)]), ls, vls, qreg, sc, sn, o, sm,
                 sl2, active, !full, kr, job, doff);
   };
 #pragma unroll 1
@@ -598,8 +640,8 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
       const int jb = j0 + KB * b;
       if (KB * b > r_hi || jb + KB - 1 < 0) continue;  // wave-uniform
       const int st = (nb - 4 + b) & (NSTAGE - 1);
-      l2_block<D>(reinterpret_cast<const char*>(lds.k[st]), reinterpret_cast<const char*>(lds.vt[st]),
-                  ls, qreg, o, b, jb, r, log2lam, fe);
+      l2_block<D>(reinterpret_cast<const char*>(lds.k[st]), reinterpret_cast<const char*>(lds.v[st]),
+                  ls, vls, qreg, o, b, jb, r, log2lam, fe);
     }
   }
 
@@ -618,20 +660,20 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* vt, const uint16_t* sst,
+hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* sst,
                       const float* lam, const float* eta, const float* g, int B, int H, int T, int d,
-                      int W, int Tp, int voff, float scale, float* y, hipStream_t s) {
+                      int W, float scale, float* y, hipStream_t s) {
   const int n_tiles = (T + MQ - 1) / MQ;
   const int n_items = B * H * n_tiles;
   const int grid = (n_items + NXCD - 1) / NXCD * NXCD;
   const float sl2 = scale * 1.4426950408889634f;
   const L2Args l2{sst, lam, eta, g, H};
   if (d == 128)
-    hipLaunchKernelGGL(swa_kernel<128>, dim3(grid), dim3(NTHR), 0, s, q, k, vt, l2, T, W, Tp, voff,
-                       n_tiles, n_items, sl2, y);
+    hipLaunchKernelGGL(swa_kernel<128>, dim3(grid), dim3(NTHR), 0, s, q, k, v, l2, T, W, n_tiles, n_items,
+                       sl2, y);
   else if (d == 64)
-    hipLaunchKernelGGL(swa_kernel<64>, dim3(grid), dim3(NTHR), 0, s, q, k, vt, l2, T, W, Tp, voff,
-                       n_tiles, n_items, sl2, y);
+    hipLaunchKernelGGL(swa_kernel<64>, dim3(grid), dim3(NTHR), 0, s, q, k, v, l2, T, W, n_tiles, n_items,
+                       sl2, y);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
