@@ -19,8 +19,8 @@
  *    (gate logit) are float32 [H], shared across the batch; the L2 matrix A
  *    is float32 [B, H, dk, dv]; the delta-rule state S is float32
  *    [B, H, dv, dk].  Outputs are always float32.
- *  - Supported shapes: dk == dv in {16, 32, 64, 128} (fused layer: {64, 128}),
- *    chunk == 64, W >= 1, B, H, T >= 0.  B, H or T equal to 0 is a valid
+ *  - Supported shapes: dk == dv in {16, 32, 64, 128}, chunk == 64, W >= 1,
+ *    B, H, T >= 0 (the backward passes and the fact memories state their own).  B, H or T equal to 0 is a valid
  *    empty call.  Anything else returns TC_ERR_UNSUPPORTED or
  *    TC_ERR_INVALID_ARG.
  *  - All argument checks run before any HIP call.  Values that live in
@@ -183,6 +183,10 @@ tc_status tc_decode_layer_step(const void* q, const void* k, const void* v, tc_d
  *   y        out [B, H, T, dv] float32.
  *   A_final  out [B, H, dk, dv] float32 or NULL.
  *   ws       at least tc_fused_workspace_bytes(...) bytes.
+ * bf16 inputs with d in {64, 128} run on bf16 MFMA kernels (the L2 state is
+ * carried in fp32; each 256-token tile's contribution passes through bf16);
+ * fp32 inputs (any supported d) and bf16 with d in {16, 32} run the prefill
+ * scan of tc_scan_forward and an fp32-arithmetic window softmax.
  * ------------------------------------------------------------------------- */
 size_t tc_fused_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt);
 tc_status tc_fused_layer(const void* q, const void* k, const void* v, tc_dtype dt,
@@ -190,6 +194,19 @@ tc_status tc_fused_layer(const void* q, const void* k, const void* v, tc_dtype d
                          int B, int H, int T, int dk, int dv, int W, int chunk,
                          float softmax_scale, float* y, float* A_final,
                          void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
+ * The L1 cache alone: exact softmax attention over the W most recent tokens
+ * (Tensor Cache, Methodology 1, L1 cache), without the L2 memory and gate:
+ *   y_t = sum_{j = max(0,t-W+1)}^{t} softmax_j(softmax_scale <q_t, k_j>) v_j.
+ * This is the pure sliding window the layer's cost is compared against.
+ *   y        out [B, H, T, dv] float32.  No workspace.
+ * bf16 inputs with d in {64, 128} run on the bf16 MFMA kernel of the fused
+ * layer; other inputs on an fp32-arithmetic kernel.
+ * ------------------------------------------------------------------------- */
+tc_status tc_window_attention(const void* q, const void* k, const void* v, tc_dtype dt,
+                              int B, int H, int T, int dk, int dv, int W, float softmax_scale,
+                              float* y, hipStream_t s);
 
 /* ---------------------------------------------------------------------------
  * Delta-rule scan (DeltaNet-family linear attention variants: DeltaNet
@@ -279,6 +296,7 @@ tc_status recall_argmax(const float* R, const float* V, int groups, int nq, int 
  * `before` on that call's stream just before the entry point's main kernel
  * and `after` just after it:
  *   tc_fused_layer      the window-attention + L2-read kernel,
+ *   tc_window_attention its only kernel,
  *   tc_scan_forward     the output kernel,
  *   tc_scan_backward    its forward-direction kernel (dq, deta, dlam),
  *   delta_scan_backward its chunk-parallel gradient kernel,

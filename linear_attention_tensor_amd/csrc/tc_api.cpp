@@ -79,6 +79,11 @@ void profile_mark_after(hipStream_t s) {
 }
 }  // namespace tc
 
+// The fused layer and the window attention run on the bf16 MFMA kernels for
+// bf16 inputs with d in {64, 128}, and on the fp32-arithmetic window kernel
+// (plus, for the layer, the prefill scan) otherwise.
+static bool fused_mfma_path(tc_dtype dt, int d) { return dt == TC_BF16 && (d == 64 || d == 128); }
+
 // ---------------------------------------------------------------------------
 // Scratch memory of tc_scan_forward_noalloc: a file-scope device array that
 // each GPU the library runs on holds from module load to process end.  In
@@ -295,12 +300,9 @@ size_t tc_fused_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int 
     fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
     return SIZE_MAX;
   }
-  if (dt != TC_BF16 || (dk != 64 && dk != 128)) {
-    fail(TC_ERR_UNSUPPORTED, "%s: the fused layer takes bf16 inputs with d in {64, 128}", fn);
-    return SIZE_MAX;
-  }
   ok();
-  return tc::fused_ws_bytes(B, H, T, dk, dv, W);
+  if (fused_mfma_path(dt, dk)) return tc::fused_ws_bytes(B, H, T, dk, dv, W);
+  return tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
 }
 
 tc_status tc_fused_layer(const void* q, const void* k, const void* v, tc_dtype dt,
@@ -312,15 +314,15 @@ tc_status tc_fused_layer(const void* q, const void* k, const void* v, tc_dtype d
     tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
     if (st != TC_OK) return st;
     if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
-    if (dt != TC_BF16 || (dk != 64 && dk != 128))
-      return fail(TC_ERR_UNSUPPORTED, "%s: the fused layer takes bf16 inputs with d in {64, 128}", fn);
     if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
       return fail(TC_ERR_INVALID_ARG, "%s: softmax_scale must be finite and > 0", fn);
     if (B == 0 || H == 0) return ok();
     if (!lam || !eta || !g) return fail(TC_ERR_INVALID_ARG, "%s: lam, eta, g must not be NULL", fn);
     if (T > 0 && (!q || !k || !v || !y))
       return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, y must not be NULL", fn);
-    const size_t need = tc::fused_ws_bytes(B, H, T, dk, dv, W);
+    const bool mfma = fused_mfma_path(dt, dk);
+    const size_t need = mfma ? tc::fused_ws_bytes(B, H, T, dk, dv, W)
+                             : tc::scan_ws_bytes(tc::plan_scan(B, H, T, dk, dv, W), B, H, dk, dv);
     if (ws_bytes < need)
       return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
@@ -330,9 +332,43 @@ tc_status tc_fused_layer(const void* q, const void* k, const void* v, tc_dtype d
                                          ws, s),
                       fn);
     }
-    return from_hip(tc::launch_tc_fused(q, k, v, lam, eta, g, B, H, T, dk, W, softmax_scale, y,
-                                        A_final, ws, s),
-                    fn);
+    if (mfma)
+      return from_hip(tc::launch_tc_fused(q, k, v, lam, eta, g, B, H, T, dk, W, softmax_scale, y,
+                                          A_final, ws, s),
+                      fn);
+    // the L2 read into y (rows t < W are 0), then y = window softmax + sigmoid(g) y
+    hipError_t e = tc::launch_tc_scan(q, k, v, dt == TC_BF16, lam, eta, B, H, T, dk, dv, W, y, A_final, ws, s);
+    if (e != hipSuccess) return from_hip(e, fn);
+    tc::profile_mark_before(s);
+    e = tc::launch_window(q, k, v, dt == TC_BF16, B, H, T, dk, W, softmax_scale, g, y, s);
+    tc::profile_mark_after(s);
+    return from_hip(e, fn);
+  });
+}
+
+tc_status tc_window_attention(const void* q, const void* k, const void* v, tc_dtype dt, int B, int H, int T,
+                              int dk, int dv, int W, float softmax_scale, float* y, hipStream_t s) {
+  return guarded("tc_window_attention", [&]() -> tc_status {
+    const char* fn = "tc_window_attention";
+    tc_status st = check_seq(fn, B, H, T, dk, dv, 64, dt);
+    if (st != TC_OK) return st;
+    if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+    if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
+      return fail(TC_ERR_INVALID_ARG, "%s: softmax_scale must be finite and > 0", fn);
+    if (B == 0 || H == 0 || T == 0) return ok();
+    if (!q || !k || !v || !y) return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, y must not be NULL", fn);
+    if (fused_mfma_path(dt, dk)) {
+      tc::profile_mark_before(s);
+      const hipError_t e = tc::launch_swa(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                          static_cast<const uint16_t*>(v), nullptr, nullptr, nullptr, nullptr, B,
+                                          H, T, dk, W, softmax_scale, y, s);
+      tc::profile_mark_after(s);
+      return from_hip(e, fn);
+    }
+    tc::profile_mark_before(s);
+    const hipError_t e = tc::launch_window(q, k, v, dt == TC_BF16, B, H, T, dk, W, softmax_scale, nullptr, y, s);
+    tc::profile_mark_after(s);
+    return from_hip(e, fn);
   });
 }
 

@@ -61,6 +61,11 @@ hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const fl
 // Main kernel of the fused layer (tc_swa.hip): q, k, v rows [B*H][T][d] bf16,
 // sst the entering state of every 256-query tile
 // ([B*H][ceil(T/256)][d][d] bf16, S^T) or nullptr for no L2 term.
+// Exact window softmax in fp32 arithmetic (tc_window.hip): fp32 inputs or
+// bf16 with d in {16, 32}.  With g, y already holds the L2 read m and becomes
+// y_local + sigmoid(g[h]) m; without, y = y_local.
+hipError_t launch_window(const void* q, const void* k, const void* v, bool bf16, int B, int H, int T, int d, int W,
+                         float scale, const float* g, float* y, hipStream_t s);
 hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* sst,
                       const float* lam, const float* eta, const float* g, int B, int H, int T, int d,
                       int W, float scale, float* y, hipStream_t s);

@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import TC_BF16, TC_F32, check, lib
 
 __all__ = ["tc_scan_forward", "tc_scan_forward_noalloc", "tc_scan_backward", "tc_decode_step", "tc_decode_layer_step",
-           "tc_fused_layer", "delta_scan_forward", "delta_scan_backward", "hebbian_write", "hebbian_read",
+           "tc_fused_layer", "tc_window_attention", "delta_scan_forward", "delta_scan_backward", "hebbian_write", "hebbian_read",
            "tc_memory_read", "recall_argmax", "scan_backward_workspace",
            "scan_workspace", "fused_workspace", "delta_workspace"]
 
@@ -282,6 +282,21 @@ def tc_fused_layer(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torch
                               ws.numel() if ws is not None else 0, _stream())
     check("tc_fused_layer", st)
     return (y, A) if return_state else y
+
+
+def tc_window_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: int, *,
+                        softmax_scale: Optional[float] = None,
+                        y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The L1 cache alone: exact softmax attention over the W most recent tokens, y [B,H,T,dv] fp32."""
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    scale = 1.0 / math.sqrt(dk) if softmax_scale is None else float(softmax_scale)
+    if y is None:
+        y = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    else:
+        _check_tensor("y", y, (B, H, T, dv), torch.float32, q.device)
+    st = lib().tc_window_attention(_ptr(q), _ptr(k), _ptr(v), dt, B, H, T, dk, dv, W, scale, _ptr(y), _stream())
+    check("tc_window_attention", st)
+    return y
 
 
 def delta_scan_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor, *,

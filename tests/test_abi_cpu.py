@@ -108,6 +108,32 @@ def test_scan_noalloc_rejects_before_any_device_call():
     assert call(B=0) == _lib.TC_OK
 
 
+def test_window_attention_rejects():
+    f = lib().tc_window_attention
+
+    def call(**kw):
+        a = dict(dt=_lib.TC_F32, B=1, H=2, T=100, dk=64, dv=64, W=16, scale=0.125, q=FAKE, y=FAKE)
+        a.update(kw)
+        return f(a["q"], FAKE, FAKE, a["dt"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["W"], a["scale"], a["y"],
+                 NULL)
+
+    assert call(W=0) == _lib.TC_ERR_INVALID_ARG
+    assert call(dk=48, dv=48) == _lib.TC_ERR_UNSUPPORTED
+    assert call(dk=64, dv=32) == _lib.TC_ERR_UNSUPPORTED
+    assert call(scale=0.0) == _lib.TC_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == _lib.TC_ERR_INVALID_ARG
+    assert call(q=NULL) == _lib.TC_ERR_INVALID_ARG
+    assert call(y=NULL) == _lib.TC_ERR_INVALID_ARG
+    assert call(T=0, q=NULL, y=NULL) == _lib.TC_OK
+
+
+def test_fused_workspace_query_covers_every_dtype_and_width():
+    q = lib().tc_fused_workspace_bytes
+    for dt in (_lib.TC_F32, _lib.TC_BF16):
+        for d in (16, 32, 64, 128):
+            assert q(2, 3, 1000, d, d, 100, 64, dt) < _lib.SIZE_MAX
+
+
 def test_decode_rejects():
     f = lib().tc_decode_step
     args = [FAKE, FAKE, FAKE, _lib.TC_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 128, 16, FAKE, NULL]
@@ -153,12 +179,14 @@ def test_fused_rejects():
         return f(FAKE, FAKE, FAKE, dt, FAKE, FAKE, FAKE, 1, 2, T, d, d, W, 64, scale, FAKE, NULL, FAKE,
                  ws_bytes, NULL)
 
-    assert call(dt=_lib.TC_F32) == _lib.TC_ERR_UNSUPPORTED
-    assert call(d=32) == _lib.TC_ERR_UNSUPPORTED
+    # fp32 inputs and d = 32 are supported (the prefill scan's path), and need a workspace here
+    assert call(dt=_lib.TC_F32) == _lib.TC_ERR_WORKSPACE
+    assert call(d=32) == _lib.TC_ERR_WORKSPACE
+    assert call(d=48) == _lib.TC_ERR_UNSUPPORTED
     assert call(scale=0.0) == _lib.TC_ERR_INVALID_ARG
     assert call(scale=float("nan")) == _lib.TC_ERR_INVALID_ARG
     assert call(ws_bytes=need - 1) == _lib.TC_ERR_WORKSPACE
-    assert lib().tc_fused_workspace_bytes(1, 2, 256, 128, 128, 64, 64, _lib.TC_F32) == _lib.SIZE_MAX
+    assert lib().tc_fused_workspace_bytes(1, 2, 256, 48, 48, 64, 64, _lib.TC_F32) == _lib.SIZE_MAX
 
 
 def test_delta_rejects():

@@ -59,3 +59,41 @@ def test_fused_layer_full_size_sampled_rows():
     ref = O.tc_fused_rows(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64), x["eta"],
                           x["g"].astype(np.float64), w.W, rows)
     check("y rows", y[:, :, rows], ref, 2e-2)
+
+
+@pytest.mark.parametrize("dtype,B,H,T,d,W", [
+    ("f32", 1, 1, 256, 16, 32),     # the tiny single-head workload's shape
+    ("f32", 2, 3, 300, 32, 17),
+    ("f32", 1, 2, 1000, 64, 100),
+    ("f32", 1, 1, 300, 128, 64),
+    ("f32", 1, 2, 40, 16, 100),     # T < W: the L2 memory stays empty
+    ("bf16", 1, 2, 300, 16, 40),
+    ("bf16", 2, 1, 257, 32, 64),
+])
+def test_fused_fp32_and_small_d(dtype, B, H, T, d, W):
+    # fp32 inputs and d in {16, 32}: the prefill scan's read, then the window
+    # softmax with the gate in fp32 arithmetic
+    print(f"[case] fused {dtype} B={B} H={H} T={T} d={d} W={W}", flush=True)
+    x = I.draw(B, H, T, d, seed=2500 + T + d, dtype=dtype)
+    y, A = ops.tc_fused_layer(*(to_dev(x[n], dtype) for n in ("q", "k", "v")), f32_dev(x["lam"]),
+                              f32_dev(x["eta"]), f32_dev(x["g"]), W, return_state=True)
+    torch.cuda.synchronize()
+    y_ref, A_ref = O.tc_fused(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64), x["eta"],
+                              x["g"].astype(np.float64), W)
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    check("y", y.cpu().numpy(), y_ref, tol)
+    check("A", A.cpu().numpy(), A_ref, tol)
+
+
+def test_fused_fp32_prefill_workload_sampled_rows():
+    # the batched fp32 prefill workload's inputs (B=4, H=8, T=4096, d=64, W=512) through the whole layer
+    w = I.WORKLOADS["prefill_scan_f32"]
+    print("[case] fused fp32 at the prefill workload", flush=True)
+    x = I.draw_workload(w.name)
+    g = np.random.default_rng(3).standard_normal(w.H).astype(np.float32)
+    y = ops.tc_fused_layer(*(to_dev(x[n], "f32") for n in ("q", "k", "v")), f32_dev(x["lam"]),
+                           f32_dev(x["eta"]), f32_dev(g), w.W).cpu().numpy()
+    rows = [0, 511, 512, 513, 1000, 2047, 4095]
+    ref = O.tc_fused_rows(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64), x["eta"],
+                          g.astype(np.float64), w.W, rows)
+    check("y rows", y[:, :, rows], ref, 1e-5)

@@ -105,3 +105,17 @@ def test_decode_repeat(layer, dtype):
         again = run()
         for name, a, b in zip(("out", "A", "ring_k", "ring_v"), first, again):
             same_bits(name, a, b)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 16)])
+def test_window_and_fp32_layer_repeat(dtype, d):
+    B, H, T, W = 1, 4, 2000, 300
+    print(f"[case] window / layer repeat {dtype} d={d}", flush=True)
+    x = I.draw(B, H, T, d, seed=64 + d, dtype=dtype)
+    q, k, v = dev_inputs(x)
+    lam, eta, g = f32_dev(x["lam"]), f32_dev(x["eta"]), f32_dev(x["g"])
+    first = (ops.tc_window_attention(q, k, v, W), ops.tc_fused_layer(q, k, v, lam, eta, g, W))
+    for _ in range(REPEATS - 1):
+        again = (ops.tc_window_attention(q, k, v, W), ops.tc_fused_layer(q, k, v, lam, eta, g, W))
+        same_bits("window y", first[0], again[0])
+        same_bits("layer y", first[1], again[1])
