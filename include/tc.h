@@ -117,8 +117,11 @@ tc_status tc_scan_forward_noalloc(const void* q, const void* k, const void* v, t
  *   dlam, deta (and dg) out [H] float32, summed over the batch.
  *   ws       at least tc_scan_backward_workspace_bytes(...) bytes (may be NULL
  *            when that is 0).
- * Supported: dt = TC_F32, dk == dv in {16, 32, 64}, chunk = 64; anything
- * else is TC_ERR_UNSUPPORTED.  dlam at lam = 0 is the one-sided derivative.
+ * Supported: dk == dv in {16, 32, 64}, chunk = 64; anything else is
+ * TC_ERR_UNSUPPORTED.  bf16 inputs are widened to fp32 copies inside the
+ * workspace first (exact), so the gradients are those of the bf16 values at
+ * fp32 accuracy; the workspace query includes the copies.  dlam at lam = 0
+ * is the one-sided derivative.
  * ------------------------------------------------------------------------- */
 size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk,
                                         tc_dtype dt);
@@ -241,9 +244,10 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
  *   ws       at least delta_scan_backward_workspace_bytes(...) bytes; it holds
  *            four state-independent products of every chunk, its entering
  *            state and its exit adjoint (B*H*ceil(T/64)*(2*64*64 + 2*64*d
- *            + 2*d*d) floats).
- * Supported: dt = TC_F32, dk == dv in {16, 32, 64}, chunk = 64; anything
- * else is TC_ERR_UNSUPPORTED.
+ *            + 2*d*d) floats), and with bf16 inputs fp32 copies of q, k, v.
+ * Supported: dk == dv in {16, 32, 64}, chunk = 64; anything else is
+ * TC_ERR_UNSUPPORTED.  bf16 inputs are widened to fp32 copies inside the
+ * workspace first (exact); the workspace query includes the copies.
  * ------------------------------------------------------------------------- */
 size_t delta_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt);
 tc_status delta_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt,

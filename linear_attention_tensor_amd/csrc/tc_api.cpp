@@ -79,6 +79,11 @@ void profile_mark_after(hipStream_t s) {
 }
 }  // namespace tc
 
+// The backward passes run on fp32 kernels; with bf16 inputs, q, k and v are
+// widened to fp32 copies placed after the fp32 workspace (256-byte aligned).
+static size_t round_up_256(size_t n) { return (n + 255) & ~(size_t)255; }
+static size_t widened_bytes(int B, int H, int T, int d) { return round_up_256((size_t)B * H * T * d * sizeof(float)); }
+
 // The fused layer and the window attention run on the bf16 MFMA kernels for
 // bf16 inputs with d in {64, 128}, and on the fp32-arithmetic window kernel
 // (plus, for the layer, the prefill scan) otherwise.
@@ -214,9 +219,13 @@ static tc_status check_scan_bwd(const char* fn, int B, int H, int T, int dk, int
   tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
   if (st != TC_OK) return st;
   if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
-  if (dt != TC_F32 || dk > 64)
-    return fail(TC_ERR_UNSUPPORTED, "%s: the backward takes float32 inputs with d in {16, 32, 64}", fn);
+  if (dk > 64) return fail(TC_ERR_UNSUPPORTED, "%s: the backward takes d in {16, 32, 64}", fn);
   return TC_OK;
+}
+
+static size_t scan_bwd_need(int B, int H, int T, int d, int W, tc_dtype dt) {
+  const size_t base = tc::scan_bwd_ws_bytes(B, H, T, d, W);
+  return dt == TC_BF16 ? round_up_256(base) + 3 * widened_bytes(B, H, T, d) : base;
 }
 
 size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk,
@@ -224,7 +233,7 @@ size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int
   if (check_scan_bwd("tc_scan_backward_workspace_bytes", B, H, T, dk, dv, W, chunk, dt) != TC_OK)
     return SIZE_MAX;
   ok();
-  return tc::scan_bwd_ws_bytes(B, H, T, dk, W);
+  return scan_bwd_need(B, H, T, dk, W, dt);
 }
 
 tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt, const float* lam,
@@ -242,13 +251,27 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
       return fail(TC_ERR_INVALID_ARG, "%s: lam, eta, dlam, deta must not be NULL", fn);
     if (T > 0 && (!q || !k || !v || !dm || !dq || !dk_out || !dv_out))
       return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, dm, dq, dk, dv must not be NULL", fn);
-    const size_t need = tc::scan_bwd_ws_bytes(B, H, T, dk, W);
+    const size_t need = scan_bwd_need(B, H, T, dk, W, dt);
     if (ws_bytes < need)
       return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
-    return from_hip(tc::launch_tc_scan_backward(static_cast<const float*>(q), static_cast<const float*>(k),
-                                                static_cast<const float*>(v), lam, eta, g, B, H, T, dk, W,
-                                                dm, dq, dk_out, dv_out, dlam, deta, dg, ws, s),
+    const float *q32 = static_cast<const float*>(q), *k32 = static_cast<const float*>(k),
+                *v32 = static_cast<const float*>(v);
+    if (dt == TC_BF16 && T > 0) {
+      char* wide = static_cast<char*>(ws) + round_up_256(tc::scan_bwd_ws_bytes(B, H, T, dk, W));
+      float* tmp[3];
+      const void* src[3] = {q, k, v};
+      for (int i = 0; i < 3; ++i) {
+        tmp[i] = reinterpret_cast<float*>(wide + i * widened_bytes(B, H, T, dk));
+        const hipError_t e = tc::launch_widen_bf16(src[i], tmp[i], (long)B * H * T * dk, s);
+        if (e != hipSuccess) return from_hip(e, fn);
+      }
+      q32 = tmp[0];
+      k32 = tmp[1];
+      v32 = tmp[2];
+    }
+    return from_hip(tc::launch_tc_scan_backward(q32, k32, v32, lam, eta, g, B, H, T, dk, W, dm, dq, dk_out,
+                                                dv_out, dlam, deta, dg, ws, s),
                     fn);
   });
 }
@@ -403,16 +426,20 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
 static tc_status check_delta_bwd(const char* fn, int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt) {
   tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
   if (st != TC_OK) return st;
-  if (dt != TC_F32 || dk > 64)
-    return fail(TC_ERR_UNSUPPORTED, "%s: the backward takes float32 inputs with d in {16, 32, 64}", fn);
+  if (dk > 64) return fail(TC_ERR_UNSUPPORTED, "%s: the backward takes d in {16, 32, 64}", fn);
   return TC_OK;
+}
+
+static size_t delta_bwd_need(int B, int H, int T, int d, tc_dtype dt) {
+  const size_t base = tc::delta_bwd_ws_bytes(B, H, T, d);
+  return dt == TC_BF16 ? round_up_256(base) + 3 * widened_bytes(B, H, T, d) : base;
 }
 
 size_t delta_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt) {
   if (check_delta_bwd("delta_scan_backward_workspace_bytes", B, H, T, dk, dv, chunk, dt) != TC_OK)
     return SIZE_MAX;
   ok();
-  return tc::delta_bwd_ws_bytes(B, H, T, dk);
+  return delta_bwd_need(B, H, T, dk, dt);
 }
 
 tc_status delta_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt, const float* beta,
@@ -427,14 +454,28 @@ tc_status delta_scan_backward(const void* q, const void* k, const void* v, tc_dt
     if (B == 0 || H == 0) return ok();
     if (T > 0 && (!q || !k || !v || !beta || !d_o || !dq || !dk_out || !dv_out || !dbeta))
       return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, beta, do, dq, dk, dv, dbeta must not be NULL", fn);
-    const size_t need = tc::delta_bwd_ws_bytes(B, H, T, dk);
+    const size_t need = delta_bwd_need(B, H, T, dk, dt);
     if (ws_bytes < need)
       return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
     if (T == 0 && !dS0) return ok();
-    return from_hip(tc::launch_delta_backward(static_cast<const float*>(q), static_cast<const float*>(k),
-                                              static_cast<const float*>(v), beta, B, H, T, dk, S0, d_o,
-                                              dS_final, dq, dk_out, dv_out, dbeta, dS0, ws, s),
+    const float *q32 = static_cast<const float*>(q), *k32 = static_cast<const float*>(k),
+                *v32 = static_cast<const float*>(v);
+    if (dt == TC_BF16 && T > 0) {
+      char* wide = static_cast<char*>(ws) + round_up_256(tc::delta_bwd_ws_bytes(B, H, T, dk));
+      float* tmp[3];
+      const void* src[3] = {q, k, v};
+      for (int i = 0; i < 3; ++i) {
+        tmp[i] = reinterpret_cast<float*>(wide + i * widened_bytes(B, H, T, dk));
+        const hipError_t e = tc::launch_widen_bf16(src[i], tmp[i], (long)B * H * T * dk, s);
+        if (e != hipSuccess) return from_hip(e, fn);
+      }
+      q32 = tmp[0];
+      k32 = tmp[1];
+      v32 = tmp[2];
+    }
+    return from_hip(tc::launch_delta_backward(q32, k32, v32, beta, B, H, T, dk, S0, d_o, dS_final, dq, dk_out,
+                                              dv_out, dbeta, dS0, ws, s),
                     fn);
   });
 }

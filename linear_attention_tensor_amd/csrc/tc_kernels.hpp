@@ -28,6 +28,9 @@ hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* 
                                    const float* dm, float* dq, float* dk, float* dv, float* dlam,
                                    float* deta, float* dg, void* ws, hipStream_t s);
 
+// bf16 -> fp32 of n elements (tc_convert.hip); any alignment, any n.
+hipError_t launch_widen_bf16(const void* in, float* out, long n, hipStream_t s);
+
 hipError_t launch_tc_scan(const void* q, const void* k, const void* v, bool bf16,
                           const float* lam, const float* eta, int B, int H, int T, int dk, int dv,
                           int W, float* m, float* A_final, void* ws, hipStream_t s);

@@ -226,7 +226,10 @@ def test_scan_backward_rejects():
         return f(FAKE, FAKE, FAKE, a["dt"], FAKE, FAKE, a["g"], a["B"], a["H"], a["T"], a["d"], a["d"], a["W"],
                  a["chunk"], a["dm"], FAKE, FAKE, FAKE, a["dlam"], FAKE, a["dg"], a["ws"], a["ws_bytes"], NULL)
 
-    assert call(dt=_lib.TC_BF16) == _lib.TC_ERR_UNSUPPORTED
+    # bf16 inputs are widened to fp32 copies in the workspace, which is larger by those
+    need16 = lib().tc_scan_backward_workspace_bytes(4, 8, 4096, 64, 64, 512, 64, _lib.TC_BF16)
+    assert need16 >= need + 3 * 4 * 8 * 4096 * 64 * 4
+    assert call(dt=_lib.TC_BF16) == _lib.TC_ERR_WORKSPACE
     assert call(d=128) == _lib.TC_ERR_UNSUPPORTED
     assert call(W=0) == _lib.TC_ERR_INVALID_ARG
     assert call(chunk=128) == _lib.TC_ERR_UNSUPPORTED

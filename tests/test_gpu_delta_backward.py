@@ -11,6 +11,7 @@ from tests._helpers import f32_dev, check, report, to_dev
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
+TOL_BF16 = 2e-2  # the bar for bf16 inputs
 NAMES = ("dq", "dk", "dv", "dbeta", "dS0")
 
 
@@ -96,3 +97,25 @@ def test_delta_backward_full_size_sampled_heads():
                                      do[b:b + 1, h:h + 1].astype(np.float64))
         for name, a, r in zip(NAMES, got, want):
             check(f"b={b} h={h} {name}", a[b:b + 1, h:h + 1], r, TOL)
+
+
+@pytest.mark.parametrize("B,H,T,d,states", [
+    (1, 2, 200, 64, False),
+    (2, 1, 130, 32, True),
+    (1, 1, 37, 16, True),
+])
+def test_delta_backward_bf16_inputs(B, H, T, d, states):
+    # bf16 q, k, v are widened to fp32 in the workspace: the gradients are those
+    # of the bf16 values, held to the bar for bf16 inputs
+    print(f"[case] delta backward bf16 B={B} H={H} T={T} d={d} states={states}", flush=True)
+    x = I.draw(B, H, T, d, seed=6100 + T + d, dtype="bf16")
+    do = I.draw_cotangent(B, H, T, d, seed=6100 + T + d)
+    rng = np.random.default_rng(T + d + 1)
+    S0 = (rng.standard_normal((B, H, d, d)) * 0.2).astype(np.float32) if states else None
+    dSf = (rng.standard_normal((B, H, d, d)) * 0.2).astype(np.float32) if states else None
+    g = ops.delta_scan_backward(*(to_dev(x[n], "bf16") for n in ("q", "k", "v")), f32_dev(x["beta"]), f32_dev(do),
+                                S0=None if S0 is None else f32_dev(S0),
+                                dS_final=None if dSf is None else f32_dev(dSf), return_dS0=True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(NAMES, [t.cpu().numpy() for t in g], ref(x, do, S0, dSf)):
+        check(name, a, b, TOL_BF16)

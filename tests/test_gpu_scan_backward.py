@@ -11,6 +11,7 @@ from tests._helpers import f32_dev, check, report, to_dev
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
+TOL_BF16 = 2e-2  # the bar for bf16 inputs
 
 
 def run(x, W, dm):
@@ -107,3 +108,21 @@ def test_scan_backward_through_the_gate(B, H, T, d, W):
                                    x["eta"].astype(np.float64), g.astype(np.float64), W, dy.astype(np.float64))
     for name, a, b in zip(("dq", "dk", "dv", "dlam", "deta", "dg"), out, ref):
         check(f"gated {name}", a.cpu().numpy(), b, TOL)
+
+
+@pytest.mark.parametrize("B,H,T,d,W", [(2, 3, 300, 32, 17), (1, 2, 1000, 64, 100), (1, 1, 256, 16, 32)])
+def test_scan_backward_bf16_inputs(B, H, T, d, W):
+    # bf16 q, k, v are widened to fp32 in the workspace: the gradients are those
+    # of the bf16 values.  Held to the bar for bf16 inputs (2e-2); dq, dk, dv
+    # and deta come out near 1e-6, dlam (a per-head sum with much cancellation
+    # when lam is near 1) has reached 2e-5 on this data.
+    print(f"[case] scan backward bf16 B={B} H={H} T={T} d={d} W={W}", flush=True)
+    x = I.draw(B, H, T, d, seed=4300 + T + d, dtype="bf16")
+    dm = I.draw_cotangent(B, H, T, d, seed=4300 + T + d)
+    got = ops.tc_scan_backward(*(to_dev(x[n], "bf16") for n in ("q", "k", "v")), f32_dev(x["lam"]),
+                               f32_dev(x["eta"]), W, f32_dev(dm))
+    torch.cuda.synchronize()
+    ref = O.tc_scan_backward(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64),
+                             x["eta"].astype(np.float64), W, dm.astype(np.float64))
+    for name, a, b in zip(("dq", "dk", "dv", "dlam", "deta"), got, ref):
+        check(f"bf16 {name}", a.cpu().numpy(), b, TOL_BF16)
