@@ -36,6 +36,8 @@ __all__ = [
     "sigmoid",
     "tc_fused",
     "tc_fused_rows",
+    "window_softmax_backward",
+    "tc_fused_backward",
     "tc_scan_chunked",
     "chunk_mean_scan",
     "tc_scan_backward",
@@ -376,3 +378,48 @@ def tc_gated_read_backward(q, k, v, lam, eta, g, W, dy):
     m, _ = tc_scan(q, k, v, lam, eta, W)
     gg = s * (1.0 - s) * np.einsum("bhtd,bhtd->h", dy, m)
     return gq, gk, gv, glam, geta, gg
+
+
+def window_softmax_backward(q, k, v, W, scale, dy):
+    """Gradients of L = sum_t <dy_t, y_local,t> for the window softmax of
+    window_softmax (Tensor Cache, Methodology 1, L1 cache; the pages give no
+    backward, this is reverse mode through that definition).
+
+    Per query t with window J = max(0, t-W+1) .. t, scores s_j = scale
+    <q_t, k_j>, weights p = softmax(s) and y = sum_j p_j v_j:
+      dv_j += p_j dy_t;
+      dp_j = <dy_t, v_j>;  ds_j = p_j (dp_j - sum_i p_i dp_i);
+      dq_t = scale sum_j ds_j k_j;  dk_j += scale ds_j q_t.
+    Returns (dq, dk, dv).
+    """
+    q, k, v, dy = _f64(q), _f64(k), _f64(v), _f64(dy)
+    B, H, T, _ = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for t in range(T):
+        lo = max(0, t - W + 1)
+        kw, vw = k[:, :, lo : t + 1, :], v[:, :, lo : t + 1, :]
+        s = np.einsum("bhjd,bhd->bhj", kw, q[:, :, t, :]) * scale
+        s = s - s.max(axis=-1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=-1, keepdims=True)
+        dv[:, :, lo : t + 1, :] += p[..., None] * dy[:, :, t, None, :]
+        dp = np.einsum("bhjd,bhd->bhj", vw, dy[:, :, t, :])
+        ds = p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+        dq[:, :, t, :] = scale * np.einsum("bhj,bhjd->bhd", ds, kw)
+        dk[:, :, lo : t + 1, :] += scale * ds[..., None] * q[:, :, t, None, :]
+    return dq, dk, dv
+
+
+def tc_fused_backward(q, k, v, lam, eta, g, W, dy, scale=None):
+    """Gradients of L = sum_t <dy_t, y_t> for the fused layer y = y_local +
+    sigmoid(g) m of tc_fused (Tensor Cache, Methodology 1, fusion): the two
+    branches depend on q, k, v separately, so their gradients add; lam, eta
+    and g enter only the L2 branch.
+
+    Returns (dq, dk, dv, dlam, deta, dg); per-head terms summed over the batch.
+    """
+    dk_ = np.shape(q)[-1]
+    scale = 1.0 / math.sqrt(dk_) if scale is None else float(scale)
+    wq, wk, wv = window_softmax_backward(q, k, v, W, scale, dy)
+    gq, gk, gv, glam, geta, gg = tc_gated_read_backward(q, k, v, lam, eta, g, W, dy)
+    return wq + gq, wk + gk, wv + gv, glam, geta, gg
