@@ -212,6 +212,46 @@ tc_status tc_window_attention(const void* q, const void* k, const void* v, tc_dt
                               float* y, hipStream_t s);
 
 /* ---------------------------------------------------------------------------
+ * Backward of the window softmax (Tensor Cache, Methodology 1, L1 cache; the
+ * pages give no backward): gradients of L = sum_t <dy_t, y_t> for the y of
+ * tc_window_attention with the same arguments,
+ *   dv_j = sum_t p_tj dy_t,  ds_tj = p_tj (<dy_t, v_j> - <dy_t, y_t>),
+ *   dq_t = scale sum_j ds_tj k_j,  dk_j = scale sum_t ds_tj q_t,
+ * with p_tj the softmax weights over the window.  fp32 arithmetic for fp32
+ * or bf16 inputs, any supported d.
+ *   dy           [B, H, T, dv] float32.
+ *   dq, dk, dv   out [B, H, T, d] float32.
+ *   ws           at least tc_window_attention_backward_workspace_bytes(...)
+ *                bytes (per query: the log-sum-exp of its scores and <dy, y>).
+ * ------------------------------------------------------------------------- */
+size_t tc_window_attention_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, tc_dtype dt);
+tc_status tc_window_attention_backward(const void* q, const void* k, const void* v, tc_dtype dt,
+                                       int B, int H, int T, int dk, int dv, int W, float softmax_scale,
+                                       const float* dy, float* dq, float* dk_out, float* dv_out,
+                                       void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
+ * Backward of the whole fused layer (Tensor Cache, Methodology 1, fusion:
+ * y = y_local + sigmoid(g) m, with lam, eta, g learned per head): gradients
+ * of L = sum_t <dy_t, y_t> for tc_fused_layer with the same arguments.  The
+ * two branches see q, k, v separately, so their gradients add: the gated
+ * L2-read backward of tc_scan_backward (which also gives dlam, deta, dg) and
+ * the window softmax's of tc_window_attention_backward.
+ *   dy               [B, H, T, dv] float32.
+ *   dq, dk, dv       out [B, H, T, d] float32.
+ *   dlam, deta, dg   out [H] float32, summed over the batch.
+ *   ws               at least tc_fused_layer_backward_workspace_bytes(...).
+ * Supported: dk == dv in {16, 32, 64}, fp32 or bf16 inputs, chunk = 64.
+ * The timing hook times the L2-read backward's forward-direction kernel.
+ * ------------------------------------------------------------------------- */
+size_t tc_fused_layer_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt);
+tc_status tc_fused_layer_backward(const void* q, const void* k, const void* v, tc_dtype dt,
+                                  const float* lam, const float* eta, const float* g,
+                                  int B, int H, int T, int dk, int dv, int W, int chunk, float softmax_scale,
+                                  const float* dy, float* dq, float* dk_out, float* dv_out,
+                                  float* dlam, float* deta, float* dg, void* ws, size_t ws_bytes, hipStream_t s);
+
+/* ---------------------------------------------------------------------------
  * Delta-rule scan (DeltaNet-family linear attention variants: DeltaNet
  * writes the prediction error).
  *
@@ -301,6 +341,7 @@ tc_status recall_argmax(const float* R, const float* V, int groups, int nq, int 
  * and `after` just after it:
  *   tc_fused_layer      the window-attention + L2-read kernel,
  *   tc_window_attention its only kernel,
+ *   tc_window_attention_backward  its dk/dv kernel,
  *   tc_scan_forward     the output kernel,
  *   tc_scan_backward    its forward-direction kernel (dq, deta, dlam),
  *   delta_scan_backward its chunk-parallel gradient kernel,

@@ -42,6 +42,11 @@ SIGNATURES = {
     "tc_fused_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "tc_fused_layer": (_i, [_p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _z, _p]),
     "tc_window_attention": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p]),
+    "tc_window_attention_backward_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i]),
+    "tc_window_attention_backward": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _z, _p]),
+    "tc_fused_layer_backward_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "tc_fused_layer_backward": (_i, [_p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p,
+                                     _p, _p, _p, _z, _p]),
     "delta_scan_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i]),
     "delta_scan_forward": (_i, [_p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _z, _p]),
     "delta_scan_backward_workspace_bytes": (_z, [_i, _i, _i, _i, _i, _i, _i]),

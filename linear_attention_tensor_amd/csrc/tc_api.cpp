@@ -276,6 +276,48 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
   });
 }
 
+static size_t fused_bwd_need(int B, int H, int T, int d, int W, tc_dtype dt) {
+  return round_up_256(scan_bwd_need(B, H, T, d, W, dt)) + tc::window_bwd_ws_bytes(B, H, T);
+}
+
+size_t tc_fused_layer_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt) {
+  if (check_scan_bwd("tc_fused_layer_backward_workspace_bytes", B, H, T, dk, dv, W, chunk, dt) != TC_OK)
+    return SIZE_MAX;
+  ok();
+  return fused_bwd_need(B, H, T, dk, W, dt);
+}
+
+tc_status tc_fused_layer_backward(const void* q, const void* k, const void* v, tc_dtype dt, const float* lam,
+                                  const float* eta, const float* g, int B, int H, int T, int dk, int dv, int W,
+                                  int chunk, float softmax_scale, const float* dy, float* dq, float* dk_out,
+                                  float* dv_out, float* dlam, float* deta, float* dg, void* ws, size_t ws_bytes,
+                                  hipStream_t s) {
+  return guarded("tc_fused_layer_backward", [&]() -> tc_status {
+    const char* fn = "tc_fused_layer_backward";
+    tc_status st = check_scan_bwd(fn, B, H, T, dk, dv, W, chunk, dt);
+    if (st != TC_OK) return st;
+    if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
+      return fail(TC_ERR_INVALID_ARG, "%s: softmax_scale must be finite and > 0", fn);
+    if (B == 0 || H == 0) return ok();
+    if (!lam || !eta || !g || !dlam || !deta || !dg)
+      return fail(TC_ERR_INVALID_ARG, "%s: lam, eta, g, dlam, deta, dg must not be NULL", fn);
+    if (T > 0 && (!q || !k || !v || !dy || !dq || !dk_out || !dv_out))
+      return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, dy, dq, dk, dv must not be NULL", fn);
+    const size_t need = fused_bwd_need(B, H, T, dk, W, dt);
+    if (ws_bytes < need) return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    if (!ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
+    // the L2 branch (gated read) writes dq, dk, dv, dlam, deta, dg; the window
+    // softmax's gradients are then added to dq, dk, dv
+    st = tc_scan_backward(q, k, v, dt, lam, eta, g, B, H, T, dk, dv, W, chunk, dy, dq, dk_out, dv_out, dlam, deta,
+                          dg, ws, round_up_256(scan_bwd_need(B, H, T, dk, W, dt)), s);
+    if (st != TC_OK) return st;
+    void* wws = static_cast<char*>(ws) + round_up_256(scan_bwd_need(B, H, T, dk, W, dt));
+    return from_hip(tc::launch_window_backward(q, k, v, dt == TC_BF16, dy, B, H, T, dk, W, softmax_scale, wws, true,
+                                               dq, dk_out, dv_out, s),
+                    fn);
+  });
+}
+
 tc_status tc_decode_step(const void* q, const void* k, const void* v, tc_dtype dt, void* ring_k,
                          void* ring_v, float* A, const float* lam, const float* eta,
                          const int64_t* pos, int B, int H, int dk, int dv, int W, float* m,
@@ -392,6 +434,39 @@ tc_status tc_window_attention(const void* q, const void* k, const void* v, tc_dt
     const hipError_t e = tc::launch_window(q, k, v, dt == TC_BF16, B, H, T, dk, W, softmax_scale, nullptr, y, s);
     tc::profile_mark_after(s);
     return from_hip(e, fn);
+  });
+}
+
+size_t tc_window_attention_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, tc_dtype dt) {
+  const char* fn = "tc_window_attention_backward_workspace_bytes";
+  if (check_seq(fn, B, H, T, dk, dv, 64, dt) != TC_OK) return SIZE_MAX;
+  if (W < 1) {
+    fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+    return SIZE_MAX;
+  }
+  ok();
+  return tc::window_bwd_ws_bytes(B, H, T);
+}
+
+tc_status tc_window_attention_backward(const void* q, const void* k, const void* v, tc_dtype dt, int B, int H, int T,
+                                       int dk, int dv, int W, float softmax_scale, const float* dy, float* dq,
+                                       float* dk_out, float* dv_out, void* ws, size_t ws_bytes, hipStream_t s) {
+  return guarded("tc_window_attention_backward", [&]() -> tc_status {
+    const char* fn = "tc_window_attention_backward";
+    tc_status st = check_seq(fn, B, H, T, dk, dv, 64, dt);
+    if (st != TC_OK) return st;
+    if (W < 1) return fail(TC_ERR_INVALID_ARG, "%s: W must be >= 1 (got %d)", fn, W);
+    if (!(softmax_scale > 0.f) || softmax_scale > 1e30f)
+      return fail(TC_ERR_INVALID_ARG, "%s: softmax_scale must be finite and > 0", fn);
+    if (B == 0 || H == 0 || T == 0) return ok();
+    if (!q || !k || !v || !dy || !dq || !dk_out || !dv_out)
+      return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, dy, dq, dk, dv must not be NULL", fn);
+    const size_t need = tc::window_bwd_ws_bytes(B, H, T);
+    if (ws_bytes < need) return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    if (!ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
+    return from_hip(tc::launch_window_backward(q, k, v, dt == TC_BF16, dy, B, H, T, dk, W, softmax_scale, ws, false,
+                                               dq, dk_out, dv_out, s),
+                    fn);
   });
 }
 

@@ -69,6 +69,13 @@ hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const fl
 // y_local + sigmoid(g[h]) m; without, y = y_local.
 hipError_t launch_window(const void* q, const void* k, const void* v, bool bf16, int B, int H, int T, int d, int W,
                          float scale, const float* g, float* y, hipStream_t s);
+// Backward of the exact window softmax (tc_window_bwd.hip), fp32 arithmetic:
+// dq, dk, dv of sum <dy, y_local>; with accumulate they are added to what the
+// buffers hold.  ws: window_bwd_ws_bytes (per-query log-sum-exp and <dy, y>).
+size_t window_bwd_ws_bytes(int B, int H, int T);
+hipError_t launch_window_backward(const void* q, const void* k, const void* v, bool bf16, const float* dy, int B,
+                                  int H, int T, int d, int W, float scale, void* ws, bool accumulate, float* dq,
+                                  float* dk, float* dv, hipStream_t s);
 hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* sst,
                       const float* lam, const float* eta, const float* g, int B, int H, int T, int d,
                       int W, float scale, float* y, hipStream_t s);

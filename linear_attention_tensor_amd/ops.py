@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import TC_BF16, TC_F32, check, lib
 
 __all__ = ["tc_scan_forward", "tc_scan_forward_noalloc", "tc_scan_backward", "tc_decode_step", "tc_decode_layer_step",
-           "tc_fused_layer", "tc_window_attention", "delta_scan_forward", "delta_scan_backward", "hebbian_write", "hebbian_read",
+           "tc_fused_layer", "tc_window_attention", "tc_window_attention_backward", "tc_fused_layer_backward", "delta_scan_forward", "delta_scan_backward", "hebbian_write", "hebbian_read",
            "tc_memory_read", "recall_argmax", "scan_backward_workspace",
            "scan_workspace", "fused_workspace", "delta_workspace"]
 
@@ -297,6 +297,49 @@ def tc_window_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: in
     st = lib().tc_window_attention(_ptr(q), _ptr(k), _ptr(v), dt, B, H, T, dk, dv, W, scale, _ptr(y), _stream())
     check("tc_window_attention", st)
     return y
+
+
+def tc_window_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, W: int, dy: torch.Tensor, *,
+                                 softmax_scale: Optional[float] = None):
+    """Gradients (dq, dk, dv) of sum <dy, y> for y = tc_window_attention(q, k, v, W)."""
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    _check_tensor("dy", dy, (B, H, T, dv), torch.float32, q.device)
+    scale = 1.0 / math.sqrt(dk) if softmax_scale is None else float(softmax_scale)
+    n = lib().tc_window_attention_backward_workspace_bytes(B, H, T, dk, dv, W, dt)
+    if n == _lib.SIZE_MAX:
+        raise _lib.TCError("tc_window_attention_backward_workspace_bytes", _lib.TC_ERR_INVALID_ARG, _lib.last_error())
+    ws = _ws(n, q.device)
+    grads = [torch.empty((B, H, T, x), dtype=torch.float32, device=q.device) for x in (dk, dk, dv)]
+    st = lib().tc_window_attention_backward(_ptr(q), _ptr(k), _ptr(v), dt, B, H, T, dk, dv, W, scale, _ptr(dy),
+                                            *(_ptr(t) for t in grads), _ptr(ws), ws.numel() if ws is not None else 0,
+                                            _stream())
+    check("tc_window_attention_backward", st)
+    return tuple(grads)
+
+
+def tc_fused_layer_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: torch.Tensor, eta: torch.Tensor,
+                            g: torch.Tensor, W: int, dy: torch.Tensor, *, softmax_scale: Optional[float] = None,
+                            check_values: bool = True):
+    """Gradients (dq, dk, dv, dlam, deta, dg) of sum <dy, y> for y = tc_fused_layer(...)."""
+    B, H, T, dk, dv, dt = _qkv(q, k, v)
+    for n_, t in (("lam", lam), ("eta", eta), ("g", g)):
+        _check_tensor(n_, t, (H,), torch.float32, q.device)
+    _check_tensor("dy", dy, (B, H, T, dv), torch.float32, q.device)
+    if check_values:
+        _check_unit_interval("lam", lam)
+    scale = 1.0 / math.sqrt(dk) if softmax_scale is None else float(softmax_scale)
+    n = lib().tc_fused_layer_backward_workspace_bytes(B, H, T, dk, dv, W, CHUNK, dt)
+    if n == _lib.SIZE_MAX:
+        raise _lib.TCError("tc_fused_layer_backward_workspace_bytes", _lib.TC_ERR_UNSUPPORTED, _lib.last_error())
+    ws = _ws(n, q.device)
+    grads = [torch.empty((B, H, T, x), dtype=torch.float32, device=q.device) for x in (dk, dk, dv)]
+    hg = [torch.empty((H,), dtype=torch.float32, device=q.device) for _ in range(3)]
+    st = lib().tc_fused_layer_backward(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(lam), _ptr(eta), _ptr(g), B, H, T, dk,
+                                       dv, W, CHUNK, scale, _ptr(dy), *(_ptr(t) for t in grads),
+                                       *(_ptr(t) for t in hg), _ptr(ws), ws.numel() if ws is not None else 0,
+                                       _stream())
+    check("tc_fused_layer_backward", st)
+    return tuple(grads) + tuple(hg)
 
 
 def delta_scan_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta: torch.Tensor, *,

@@ -134,6 +134,35 @@ def test_fused_workspace_query_covers_every_dtype_and_width():
             assert q(2, 3, 1000, d, d, 100, 64, dt) < _lib.SIZE_MAX
 
 
+def test_backward_entry_points_reject():
+    L = lib()
+    wq = L.tc_window_attention_backward_workspace_bytes
+    assert 0 < wq(1, 2, 100, 64, 64, 16, _lib.TC_F32) < _lib.SIZE_MAX
+    assert wq(1, 2, 100, 48, 48, 16, _lib.TC_F32) == _lib.SIZE_MAX
+    need = wq(1, 2, 100, 64, 64, 16, _lib.TC_F32)
+    f = L.tc_window_attention_backward
+    base = [FAKE, FAKE, FAKE, _lib.TC_F32, 1, 2, 100, 64, 64, 16, 0.125, FAKE, FAKE, FAKE, FAKE, FAKE, need, NULL]
+    bad = list(base); bad[9] = 0
+    assert f(*bad) == _lib.TC_ERR_INVALID_ARG
+    bad = list(base); bad[16] = need - 1
+    assert f(*bad) == _lib.TC_ERR_WORKSPACE
+    bad = list(base); bad[11] = NULL
+    assert f(*bad) == _lib.TC_ERR_INVALID_ARG
+    fq = L.tc_fused_layer_backward_workspace_bytes
+    assert fq(1, 2, 100, 128, 128, 16, 64, _lib.TC_BF16) == _lib.SIZE_MAX  # d = 128: not supported
+    assert 0 < fq(1, 2, 100, 64, 64, 16, 64, _lib.TC_BF16) < _lib.SIZE_MAX
+    g = L.tc_fused_layer_backward
+    n2 = fq(1, 2, 100, 64, 64, 16, 64, _lib.TC_F32)
+    args = [FAKE, FAKE, FAKE, _lib.TC_F32, FAKE, FAKE, FAKE, 1, 2, 100, 64, 64, 16, 64, 0.125, FAKE, FAKE, FAKE, FAKE,
+            FAKE, FAKE, FAKE, FAKE, n2, NULL]
+    bad = list(args); bad[6] = NULL  # g
+    assert g(*bad) == _lib.TC_ERR_INVALID_ARG
+    bad = list(args); bad[23] = n2 - 1
+    assert g(*bad) == _lib.TC_ERR_WORKSPACE
+    bad = list(args); bad[14] = -1.0
+    assert g(*bad) == _lib.TC_ERR_INVALID_ARG
+
+
 def test_decode_rejects():
     f = lib().tc_decode_step
     args = [FAKE, FAKE, FAKE, _lib.TC_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 128, 128, 16, FAKE, NULL]
