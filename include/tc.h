@@ -117,11 +117,14 @@ tc_status tc_scan_forward_noalloc(const void* q, const void* k, const void* v, t
  *   dlam, deta (and dg) out [H] float32, summed over the batch.
  *   ws       at least tc_scan_backward_workspace_bytes(...) bytes (may be NULL
  *            when that is 0).
- * Supported: dk == dv in {16, 32, 64}, chunk = 64; anything else is
- * TC_ERR_UNSUPPORTED.  bf16 inputs are widened to fp32 copies inside the
- * workspace first (exact), so the gradients are those of the bf16 values at
- * fp32 accuracy; the workspace query includes the copies.  dlam at lam = 0
- * is the one-sided derivative.
+ * Supported: dk == dv in {16, 32, 64, 128}, chunk = 64; anything else is
+ * TC_ERR_UNSUPPORTED.  d = 128 runs as four d = 64 problems, one per pair of
+ * column halves (q and k columns of one half, v and dm columns of one half:
+ * the read is a sum of those four), whose gradients are added; the workspace
+ * then also holds the gathered halves (11 * B*H*T*64 floats).  bf16 inputs
+ * are widened to fp32 copies inside the workspace first (exact), so the
+ * gradients are those of the bf16 values at fp32 accuracy; the workspace
+ * query includes the copies.  dlam at lam = 0 is the one-sided derivative.
  * ------------------------------------------------------------------------- */
 size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk,
                                         tc_dtype dt);
@@ -241,7 +244,8 @@ tc_status tc_window_attention_backward(const void* q, const void* k, const void*
  *   dq, dk, dv       out [B, H, T, d] float32.
  *   dlam, deta, dg   out [H] float32, summed over the batch.
  *   ws               at least tc_fused_layer_backward_workspace_bytes(...).
- * Supported: dk == dv in {16, 32, 64}, fp32 or bf16 inputs, chunk = 64.
+ * Supported: dk == dv in {16, 32, 64, 128} (d = 128 as tc_scan_backward
+ * does it), fp32 or bf16 inputs, chunk = 64.
  * The timing hook times the L2-read backward's forward-direction kernel.
  * ------------------------------------------------------------------------- */
 size_t tc_fused_layer_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt);
@@ -343,7 +347,8 @@ tc_status recall_argmax(const float* R, const float* V, int groups, int nq, int 
  *   tc_window_attention its only kernel,
  *   tc_window_attention_backward  its dk/dv kernel,
  *   tc_scan_forward     the output kernel,
- *   tc_scan_backward    its forward-direction kernel (dq, deta, dlam),
+ *   tc_scan_backward    its forward-direction kernel (dq, deta, dlam; at d = 128
+ *                       that of the last of the four d = 64 pieces),
  *   delta_scan_backward its chunk-parallel gradient kernel,
  *   hebbian_write       its write kernel (not the segment sum),
  *   tc_decode_step      its only kernel,

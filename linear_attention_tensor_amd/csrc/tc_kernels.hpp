@@ -30,6 +30,12 @@ hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* 
 
 // bf16 -> fp32 of n elements (tc_convert.hip); any alignment, any n.
 hipError_t launch_widen_bf16(const void* in, float* out, long n, hipStream_t s);
+// Column pieces of row-major fp32 arrays (tc_convert.hip): gather
+// dst[r][c] = src[r * ds + c0 + c]; scatter dst[r * dd + c0 + c] (+)= src[r][c];
+// c < w, r < rows.
+hipError_t launch_gather_cols(const float* src, int ds, int c0, int w, float* dst, long rows, hipStream_t s);
+hipError_t launch_scatter_cols(const float* src, int w, float* dst, int dd, int c0, long rows, bool add,
+                               hipStream_t s);
 
 hipError_t launch_tc_scan(const void* q, const void* k, const void* v, bool bf16,
                           const float* lam, const float* eta, int B, int H, int T, int dk, int dv,

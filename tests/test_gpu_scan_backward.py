@@ -44,6 +44,9 @@ def check_case(x, W, dm, label):
     (1, 2, 40, 16, 39),         # one eviction
     (1, 1, 30, 16, 30),         # T == W: nothing is evicted
     (1, 1, 20, 32, 45),         # T < W
+    (1, 2, 700, 128, 60),       # d = 128: four d = 64 pieces, gradients added
+    (2, 1, 150, 128, 149),      # d = 128, one eviction
+    (1, 1, 90, 128, 100),       # d = 128, T < W
 ])
 def test_scan_backward_small(B, H, T, d, W):
     print(f"[case] scan backward B={B} H={H} T={T} d={d} W={W}", flush=True)
@@ -60,19 +63,21 @@ def test_scan_backward_lambda_edges(lam_val):
     check_case(x, 20, dm, f"lam={lam_val}")
 
 
-def test_scan_backward_empty_sequence():
-    x = I.draw(1, 2, 1, 64, seed=5, dtype="f32")
+@pytest.mark.parametrize("d", [64, 128])
+def test_scan_backward_empty_sequence(d):
+    x = I.draw(1, 2, 1, d, seed=5, dtype="f32")
     q = to_dev(x["q"], "f32")[:, :, :0].contiguous()
     g = ops.tc_scan_backward(q, q.clone(), q.clone(), f32_dev(x["lam"]), f32_dev(x["eta"]), 8,
                              q.clone())
     torch.cuda.synchronize()
-    assert g[0].shape == (1, 2, 0, 64)
+    assert g[0].shape == (1, 2, 0, d)
     assert torch.all(g[3] == 0) and torch.all(g[4] == 0)
 
 
-def test_scan_backward_repeat_is_deterministic():
-    x = I.draw(1, 2, 700, 64, seed=9, dtype="f32")
-    dm = I.draw_cotangent(1, 2, 700, 64, seed=9)
+@pytest.mark.parametrize("d", [64, 128])
+def test_scan_backward_repeat_is_deterministic(d):
+    x = I.draw(1, 2, 700, d, seed=9, dtype="f32")
+    dm = I.draw_cotangent(1, 2, 700, d, seed=9)
     a = run(x, 64, dm)
     b = run(x, 64, dm)
     for u, w in zip(a, b):
@@ -95,7 +100,8 @@ def test_scan_backward_prefill_full_size_sampled_heads():
             check(f"head {h} {name}", a[:, sl] if a.ndim == 4 else a[sl], b, TOL)
 
 
-@pytest.mark.parametrize("B,H,T,d,W", [(2, 3, 300, 32, 17), (1, 2, 1000, 64, 100), (1, 1, 20, 16, 45)])
+@pytest.mark.parametrize("B,H,T,d,W", [(2, 3, 300, 32, 17), (1, 2, 1000, 64, 100), (1, 1, 20, 16, 45),
+                                       (1, 3, 400, 128, 50)])
 def test_scan_backward_through_the_gate(B, H, T, d, W):
     print(f"[case] gated scan backward B={B} H={H} T={T} d={d} W={W}", flush=True)
     x = I.draw(B, H, T, d, seed=4500 + T, dtype="f32")
@@ -110,7 +116,8 @@ def test_scan_backward_through_the_gate(B, H, T, d, W):
         check(f"gated {name}", a.cpu().numpy(), b, TOL)
 
 
-@pytest.mark.parametrize("B,H,T,d,W", [(2, 3, 300, 32, 17), (1, 2, 1000, 64, 100), (1, 1, 256, 16, 32)])
+@pytest.mark.parametrize("B,H,T,d,W", [(2, 3, 300, 32, 17), (1, 2, 1000, 64, 100), (1, 1, 256, 16, 32),
+                                       (1, 2, 400, 128, 70)])
 def test_scan_backward_bf16_inputs(B, H, T, d, W):
     # bf16 q, k, v are widened to fp32 in the workspace: the gradients are those
     # of the bf16 values.  Held to the bar for bf16 inputs (2e-2); dq, dk, dv

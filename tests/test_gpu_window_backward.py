@@ -41,6 +41,8 @@ def test_window_backward(dtype, B, H, T, d, W):
     ("f32", 1, 2, 700, 64, 100),
     ("f32", 1, 1, 40, 16, 100),     # T < W: only the window branch
     ("bf16", 1, 2, 400, 64, 64),
+    ("f32", 1, 2, 500, 128, 80),    # d = 128: the L2 branch in four d = 64 pieces
+    ("bf16", 1, 1, 300, 128, 64),
 ])
 def test_fused_layer_backward(dtype, B, H, T, d, W):
     print(f"[case] fused backward {dtype} B={B} H={H} T={T} d={d} W={W}", flush=True)
