@@ -22,9 +22,10 @@
 // are interleaved with the softmax of block i and its PV MFMAs, so the matrix
 // cores and the vector ALUs work at the same time.  Blocks 4.. come first and
 // blocks 0-3 last, so the latter (the tile's evictions) are still resident
-// for the L2 epilogue.  Tiles are mapped so that the workgroups that share an
-// XCD at the same time work on neighbouring tiles of one head and share K/V
-// through its L2 cache.
+// for the L2 epilogue.  The grid is persistent (as many workgroups as fit at
+// once, each walking several tiles), and tiles are mapped so that the
+// workgroups that share an XCD at the same time work on neighbouring tiles of
+// one head and share K/V through its L2 cache.
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
 #include "tc_dma.hpp"
@@ -46,6 +47,7 @@ constexpr int NTHR = 64 * NWAVE;
 constexpr int MQ = 32 * NWAVE;  // queries per tile
 constexpr int NSTAGE = 4;       // blocks resident in LDS
 constexpr int NXCD = 8;         // MI355X: 8 accelerator complex dies, dispatched round-robin
+constexpr int kComputeUnits = 256;
 constexpr float kNegBig = -1.0e30f;
 
 template <int D>
@@ -498,164 +500,173 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
   constexpr int NDT = D / 32;
   __shared__ __attribute__((aligned(16))) SwaLds<D> lds;
 
-  // XCD-aware mapping: the workgroups dispatched to one XCD take a contiguous
-  // run of (head, tile) items, so concurrent neighbours share K/V in its L2.
+  // Persistent, XCD-aware: the workgroups dispatched to one XCD share a
+  // contiguous run of (head, tile) items and walk it with the stride of their
+  // number, so the tiles in flight on an XCD are neighbours of one head that
+  // share K/V through its L2.  A workgroup's next tile starts while the
+  // previous tile's output stores drain.
   const int per_xcd = (n_items + NXCD - 1) / NXCD;
-  const int item = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
-  if (item >= n_items) return;
-  const int bh = item / n_tiles, tile = item % n_tiles;
-
+  const int xcd = blockIdx.x % NXCD, n_slots = gridDim.x / NXCD;
   const int w = wave_id(), l = lane_id(), col = l & 31, hh = l >> 5;
-  const long base = (long)bh * T;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + base * D, (uint32_t)T * D * 2);
-  const i32x4 rk = raw_desc(k + base * D, (uint32_t)T * D * 2);
-  const i32x4 rv = raw_desc(v + base * D, (uint32_t)T * D * 2);
   const DmaOff<D> doff = dma_offsets<D>();
-
-  const int t0 = tile * MQ;
-  const int j0 = t0 - W;
-  // Query slice of this wave.  Waves w and w + 4 share a SIMD and slice s
-  // needs floor(s / 2) + 1 blocks in the L2 epilogue, so the slices 0..3
-  // pair with 7..4 to give every SIMD the same epilogue work.
-  const int slice = w < 4 ? w : 11 - w;
-  const int r_lo = 32 * slice, r_hi = r_lo + 31;
-  const int tw = t0 + r_lo;    // first query of this wave
-  const int tq = tw + col;     // this lane's query
-  const int nb = (W + MQ + KB - 1) / KB;  // >= 5
-  // the tile writes evictions into the L2 memory iff some key j0 .. j0 + 255 is >= 0
-  const bool has_l2 = l2.sst != nullptr && j0 + MQ > 0;
-  // blocks 4 .. nb-1 first, then 0 .. 3 (left resident for the L2 epilogue)
-  auto block_at = [nb](int idx) { return idx < nb - 4 ? idx + 4 : idx - (nb - 4); };
-
-  bf16x8 qreg[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qreg[ks] = as_bf16x8(buf_load16(rq, (tq * D + 16 * ks + 8 * hh) * 2));
-  floatx16 o[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = zero16();
-  Softmax sm{kNegBig, 0.f};
   uint32_t ls[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) ls[j] = lane_slot(j);
   uint32_t vls[NDT];
   v_lane_offsets<D>(vls);
 
-  // Copies complete in issue order: blocks 0..2, then the state (used only in
-  // the epilogue).  The state is issued after the first scores: the compiler
-  // waits for the q loads with counts that also cover every copy issued
-  // before them, so the first scores wait for blocks 0..2 but not for it.
-  constexpr int NS = D * D / 8 / NTHR;  // state copy instructions per thread
-#pragma unroll
-  for (int i = 0; i < NSTAGE - 1; ++i)
-    dma_block<D>(rk, rv, doff, j0 + KB * block_at(i), lds.k[i], lds.v[i]);
-  wait_vmcnt<2 * Dma<D>::N>();
-  lds_barrier();
-  floatx16 s0[2], s1[2];
-  qk_block<D>(reinterpret_cast<const char*>(lds.k[0]), ls, qreg, s0[0], s0[1]);
-  if (has_l2) dma_state<D>(raw_desc(l2.sst + ((long)bh * n_tiles + tile) * D * D, D * D * 2), lds.st);
-
-  // One step per block position; the scores alternate between s0 and s1.
-  auto step = [&](int idx, floatx16* sc, floatx16* sn) __attribute__((always_inline)) {
-    // block idx + 1 must have landed: its scores are formed in this step.
-    // Outstanding copies allowed: block idx + 2, and for idx < 2 the state,
-    // which was issued between blocks 2 and 3 (at idx = 0 block 1 has landed
-    // already).
-    if (idx < 2 && has_l2) wait_vmcnt<Dma<D>::N + NS>();
-    else if (idx + 2 < nb) wait_vmcnt<Dma<D>::N>();
-    else wait_vmcnt<0>();
-    lds_barrier();  // also: every wave is done with step idx - 1, whose stage the next DMA reuses
-    DmaJob<D> job;
-    {
-      const int st = (idx + NSTAGE - 1) & (NSTAGE - 1);
-      const int jn = j0 + KB * block_at(idx + NSTAGE - 1);
-      job = DmaJob<D>{rk, rv, jn * D * 2, lds.k[st], lds.v[st], idx + NSTAGE - 1 < nb};
-    }
-    const int b = block_at(idx);
-    const int c_lo = KB * b, jb = j0 + c_lo;
-    // (bitwise &: the flags are formed without branches)
-    const bool active = (idx < nb) & (tw < T) & (c_lo + KB - 1 > r_lo) & (c_lo <= r_hi + W) &
-                        (jb + KB - 1 >= 0) & (jb < T);
-    const bool full = (c_lo > r_hi) & (c_lo + KB - 1 <= r_lo + W) & (jb >= 0) & (jb + KB - 1 < T) &
-                      (tw + 31 < T);
-    // keys c_lo + key valid for query r: r < c <= r + W and 0 <= j < T
-    const int r = r_lo + col;
-    int lo = max(r + 1 - c_lo, -jb);
-    const int hi = min(r + W - c_lo, T - 1 - jb);
-    KeyRange kr;
-    kr.span = static_cast<unsigned>(hi - lo);
-    if (hi < lo) {
-      lo = 1 << 20;  // no key matches
-      kr.span = 0;
-    }
-    kr.lo = lo - 8 * hh;
-    swa_step<D>(reinterpret_cast<const char*>(lds.k[(idx + 1) & (NSTAGE - 1)]),
-                reinterpret_cast<const char*>(lds.v[idx & (NSTAGE - 1)]), ls, vls, qreg, sc, sn, o, sm,
-                sl2, active, !full, kr, job, doff);
-  };
 #pragma unroll 1
-  for (int idx = 0; idx < nb; idx += 2) {
-    step(idx, s0, s1);
-    step(idx + 1, s1, s0);  // past the last block: an inactive step
-  }
+  for (int local = blockIdx.x / NXCD; local < per_xcd; local += n_slots) {
+    const int item = xcd * per_xcd + local;
+    if (item >= n_items) break;
+    const int bh = item / n_tiles, tile = item % n_tiles;
+    // every wave is done with the LDS stages and the state of the previous tile
+    lds_barrier();
+    const long base = (long)bh * T;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + base * D, (uint32_t)T * D * 2);
+    const i32x4 rk = raw_desc(k + base * D, (uint32_t)T * D * 2);
+    const i32x4 rv = raw_desc(v + base * D, (uint32_t)T * D * 2);
 
-  const float tot = sum_halves(sm.l);
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] *= inv;
+    const int t0 = tile * MQ;
+    const int j0 = t0 - W;
+    // Query slice of this wave.  Waves w and w + 4 share a SIMD and slice s
+    // needs floor(s / 2) + 1 blocks in the L2 epilogue, so the slices 0..3
+    // pair with 7..4 to give every SIMD the same epilogue work.
+    const int slice = w < 4 ? w : 11 - w;
+    const int r_lo = 32 * slice, r_hi = r_lo + 31;
+    const int tw = t0 + r_lo;    // first query of this wave
+    const int tq = tw + col;     // this lane's query
+    const int nb = (W + MQ + KB - 1) / KB;  // >= 5
+    // the tile writes evictions into the L2 memory iff some key j0 .. j0 + 255 is >= 0
+    const bool has_l2 = l2.sst != nullptr && j0 + MQ > 0;
+    // blocks 4 .. nb-1 first, then 0 .. 3 (left resident for the L2 epilogue)
+    auto block_at = [nb](int idx) { return idx < nb - 4 ? idx + 4 : idx - (nb - 4); };
 
-  if (has_l2 && tw < T) {
-    // Every DMA has completed (the last step waited for all of them) and the
-    // barrier of that step made them visible to the whole workgroup.
-    const int h = bh % l2.H;
-    const float lam = l2.lam[h];
-    const float log2lam = lam > 0.f ? log2f(lam) : -1.0e4f;  // 0^0 = 1, 0^n = 0
-    const float gate = 1.f / (1.f + expf(-l2.g[h]));
-    const int r = r_lo + col;
-    // state term: o^T += S_n^T (fs Q)^T, fs = gate lam^(r+1) per query
-    const float fs = gate * __builtin_amdgcn_exp2f(static_cast<float>(r + 1) * log2lam);
-    const char* sst = reinterpret_cast<const char*>(lds.st);
-    bf16x8 sbuf[2][NDT];
-    TC_SB();
+    bf16x8 qreg[NKS];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      sbuf[0][dt] = lds16(sst + (dt >> 1) * (KB * D * 2), ls[0] + 4096u * (dt & 1));
+    for (int ks = 0; ks < NKS; ++ks) qreg[ks] = as_bf16x8(buf_load16(rq, (tq * D + 16 * ks + 8 * hh) * 2));
+    floatx16 o[NDT];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = zero16();
+    Softmax sm{kNegBig, 0.f};
+
+    // Copies complete in issue order: blocks 0..2, then the state (used only in
+    // the epilogue).  The state is issued after the first scores: the compiler
+    // waits for the q loads with counts that also cover every copy issued
+    // before them, so the first scores wait for blocks 0..2 but not for it.
+    constexpr int NS = D * D / 8 / NTHR;  // state copy instructions per thread
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i)
+      dma_block<D>(rk, rv, doff, j0 + KB * block_at(i), lds.k[i], lds.v[i]);
+    wait_vmcnt<2 * Dma<D>::N>();
+    lds_barrier();
+    floatx16 s0[2], s1[2];
+    qk_block<D>(reinterpret_cast<const char*>(lds.k[0]), ls, qreg, s0[0], s0[1]);
+    if (has_l2) dma_state<D>(raw_desc(l2.sst + ((long)bh * n_tiles + tile) * D * D, D * D * 2), lds.st);
+
+    // One step per block position; the scores alternate between s0 and s1.
+    auto step = [&](int idx, floatx16* sc, floatx16* sn) __attribute__((always_inline)) {
+      // block idx + 1 must have landed: its scores are formed in this step.
+      // Outstanding copies allowed: block idx + 2, and for idx < 2 the state,
+      // which was issued between blocks 2 and 3 (at idx = 0 block 1 has landed
+      // already).
+      if (idx < 2 && has_l2) wait_vmcnt<Dma<D>::N + NS>();
+      else if (idx + 2 < nb) wait_vmcnt<Dma<D>::N>();
+      else wait_vmcnt<0>();
+      lds_barrier();  // also: every wave is done with step idx - 1, whose stage the next DMA reuses
+      DmaJob<D> job;
+      {
+        const int st = (idx + NSTAGE - 1) & (NSTAGE - 1);
+        const int jn = j0 + KB * block_at(idx + NSTAGE - 1);
+        job = DmaJob<D>{rk, rv, jn * D * 2, lds.k[st], lds.v[st], idx + NSTAGE - 1 < nb};
+      }
+      const int b = block_at(idx);
+      const int c_lo = KB * b, jb = j0 + c_lo;
+      // (bitwise &: the flags are formed without branches)
+      const bool active = (idx < nb) & (tw < T) & (c_lo + KB - 1 > r_lo) & (c_lo <= r_hi + W) &
+                          (jb + KB - 1 >= 0) & (jb < T);
+      const bool full = (c_lo > r_hi) & (c_lo + KB - 1 <= r_lo + W) & (jb >= 0) & (jb + KB - 1 < T) &
+                        (tw + 31 < T);
+      // keys c_lo + key valid for query r: r < c <= r + W and 0 <= j < T
+      const int r = r_lo + col;
+      int lo = max(r + 1 - c_lo, -jb);
+      const int hi = min(r + W - c_lo, T - 1 - jb);
+      KeyRange kr;
+      kr.span = static_cast<unsigned>(hi - lo);
+      if (hi < lo) {
+        lo = 1 << 20;  // no key matches
+        kr.span = 0;
+      }
+      kr.lo = lo - 8 * hh;
+      swa_step<D>(reinterpret_cast<const char*>(lds.k[(idx + 1) & (NSTAGE - 1)]),
+                  reinterpret_cast<const char*>(lds.v[idx & (NSTAGE - 1)]), ls, vls, qreg, sc, sn, o, sm,
+                  sl2, active, !full, kr, job, doff);
+    };
+#pragma unroll 1
+    for (int idx = 0; idx < nb; idx += 2) {
+      step(idx, s0, s1);
+      step(idx + 1, s1, s0);  // past the last block: an inactive step
+    }
+
+    const float tot = sum_halves(sm.l);
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] *= inv;
+
+    if (has_l2 && tw < T) {
+      // Every DMA has completed (the last step waited for all of them) and the
+      // barrier of that step made them visible to the whole workgroup.
+      const int h = bh % l2.H;
+      const float lam = l2.lam[h];
+      const float log2lam = lam > 0.f ? log2f(lam) : -1.0e4f;  // 0^0 = 1, 0^n = 0
+      const float gate = 1.f / (1.f + expf(-l2.g[h]));
+      const int r = r_lo + col;
+      // state term: o^T += S_n^T (fs Q)^T, fs = gate lam^(r+1) per query
+      const float fs = gate * __builtin_amdgcn_exp2f(static_cast<float>(r + 1) * log2lam);
+      const char* sst = reinterpret_cast<const char*>(lds.st);
+      bf16x8 sbuf[2][NDT];
       TC_SB();
-      if (ks + 1 < NKS) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          sbuf[(ks + 1) & 1][dt] = lds16(sst + (dt >> 1) * (KB * D * 2),
-                                         ls[(ks + 1) & 3] + 8192u * ((ks + 1) >> 2) + 4096u * (dt & 1));
+      for (int dt = 0; dt < NDT; ++dt)
+        sbuf[0][dt] = lds16(sst + (dt >> 1) * (KB * D * 2), ls[0] + 4096u * (dt & 1));
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        TC_SB();
+        if (ks + 1 < NKS) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            sbuf[(ks + 1) & 1][dt] = lds16(sst + (dt >> 1) * (KB * D * 2),
+                                           ls[(ks + 1) & 3] + 8192u * ((ks + 1) >> 2) + 4096u * (dt & 1));
+        }
+        const bf16x8 qs = scale_bf16x8(qreg[ks], fs);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma32(sbuf[ks & 1][dt], qs, o[dt]);
       }
-      const bf16x8 qs = scale_bf16x8(qreg[ks], fs);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma32(sbuf[ks & 1][dt], qs, o[dt]);
-    }
-    TC_SB();
-    // evictions of the tile: blocks 0..3, resident in stages (nb - 4 + b) % 4
-    const float fe = gate * l2.eta[h];
+      TC_SB();
+      // evictions of the tile: blocks 0..3, resident in stages (nb - 4 + b) % 4
+      const float fe = gate * l2.eta[h];
 #pragma unroll 1
-    for (int b = 0; b < 4; ++b) {
-      const int jb = j0 + KB * b;
-      if (KB * b > r_hi || jb + KB - 1 < 0) continue;  // wave-uniform
-      const int st = (nb - 4 + b) & (NSTAGE - 1);
-      l2_block<D>(reinterpret_cast<const char*>(lds.k[st]), reinterpret_cast<const char*>(lds.v[st]),
-                  ls, vls, qreg, o, b, jb, r, log2lam, fe);
-    }
-  }
-
-  if (tq < T) {
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dv = 32 * dt + 8 * g4 + 4 * hh;
-        const float4 out = make_float4(o[dt][4 * g4], o[dt][4 * g4 + 1], o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]);
-        *reinterpret_cast<float4*>(y + (base + tq) * D + dv) = out;
+      for (int b = 0; b < 4; ++b) {
+        const int jb = j0 + KB * b;
+        if (KB * b > r_hi || jb + KB - 1 < 0) continue;  // wave-uniform
+        const int st = (nb - 4 + b) & (NSTAGE - 1);
+        l2_block<D>(reinterpret_cast<const char*>(lds.k[st]), reinterpret_cast<const char*>(lds.v[st]),
+                    ls, vls, qreg, o, b, jb, r, log2lam, fe);
       }
     }
-  }
+
+    if (tq < T) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dv = 32 * dt + 8 * g4 + 4 * hh;
+          const float4 out = make_float4(o[dt][4 * g4], o[dt][4 * g4 + 1], o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]);
+          *reinterpret_cast<float4*>(y + (base + tq) * D + dv) = out;
+        }
+      }
+    }
+  }  // tiles
 }
 
 }  // namespace
@@ -665,7 +676,9 @@ hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
                       int W, float scale, float* y, hipStream_t s) {
   const int n_tiles = (T + MQ - 1) / MQ;
   const int n_items = B * H * n_tiles;
-  const int grid = (n_items + NXCD - 1) / NXCD * NXCD;
+  // as many workgroups as fit at once (LDS: one per CU at d = 128, two at d = 64), a multiple of NXCD
+  const int per_xcd = (n_items + NXCD - 1) / NXCD;
+  const int grid = NXCD * std::min(per_xcd, kComputeUnits / NXCD * (d == 128 ? 1 : 2));
   const float sl2 = scale * 1.4426950408889634f;
   const L2Args l2{sst, lam, eta, g, H};
   if (d == 128)
