@@ -20,9 +20,10 @@
 // O^T += V^T P^T from registers; the V^T operand comes from the V rows by
 // LDS transpose reads (ds_read_b64_tr_b16), so V needs no transposed copy.  The loop is software-pipelined: the QK^T MFMAs of block i+1
 // are interleaved with the softmax of block i and its PV MFMAs, so the matrix
-// cores and the vector ALUs work at the same time.  Blocks 4.. come first and
-// blocks 0-3 last, so the latter (the tile's evictions) are still resident
-// for the L2 epilogue.  The grid is persistent (as many workgroups as fit at
+// cores and the vector ALUs work at the same time.  Blocks 4.. come first (in an
+// order rotated per tile, so that neighbouring tiles read the same keys at the
+// same time) and blocks 0-3 last, so the latter (the tile's evictions) are
+// still resident for the L2 epilogue.  The grid is persistent (as many workgroups as fit at
 // once, each walking several tiles), and tiles are mapped so that the
 // workgroups that share an XCD at the same time work on neighbouring tiles of
 // one head and share K/V through its L2 cache.
@@ -539,8 +540,12 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
     const int nb = (W + MQ + KB - 1) / KB;  // >= 5
     // the tile writes evictions into the L2 memory iff some key j0 .. j0 + 255 is >= 0
     const bool has_l2 = l2.sst != nullptr && j0 + MQ > 0;
-    // blocks 4 .. nb-1 first, then 0 .. 3 (left resident for the L2 epilogue)
-    auto block_at = [nb](int idx) { return idx < nb - 4 ? idx + 4 : idx - (nb - 4); };
+    // Blocks 4 .. nb-1 first, then 0 .. 3 (left resident for the L2 epilogue).
+    // The first part is rotated by 4 blocks per tile: block b of tile p + 1 is
+    // block b + 4 of tile p, so neighbouring tiles (which run at the same time
+    // on one XCD) read the same keys at the same step, out of its L2.
+    const int nw = nb - 4, rot = (MQ / KB * tile) % nw;
+    auto block_at = [nw, rot](int idx) { return idx < nw ? 4 + (idx + nw - rot) % nw : idx - nw; };
 
     bf16x8 qreg[NKS];
 #pragma unroll
