@@ -8,21 +8,20 @@
 // [256 p - W, 256 (p+1) - W) clipped to [0, T - W).
 //
 // Launches (all on the caller's stream):
-//   fused_state   per (tile, b, h): the tile's own contribution to the
+//   state_tile    per (tile, b, h): the tile's own contribution to the
 //                 state, from zero, delta_p = sum_c eta lam^(L-1-c) v_c k_c^T
 //                 (S^T layout, bf16 MFMA with fp32 accumulation, stored as
-//                 bf16); for the layer it also writes V^T (per head [d][Tp]
-//                 bf16) into the workspace, so that the main kernel can copy
-//                 V^T blocks straight to LDS;
+//                 bf16);
 //   fused_prefix  S_0 = 0, S_{p+1} = lam^L_p S_p + delta_p, carried in fp32:
 //                 the state entering every tile (bf16) and the final state A
 //                 (fp32);
 //   swa           per (tile, b, h): window softmax plus the L2 read.
-// Workspace: delta (bf16) | entering states (bf16) | V^T copy (bf16, the
-// layer only).
+// Workspace: delta (bf16) | entering states (bf16).
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
 #include "tc_mfma.hpp"
+#include "tc_dma.hpp"
+#include "tc_tr.hpp"
 
 #include <math.h>
 
@@ -33,19 +32,19 @@ namespace tc {
 namespace {
 
 using namespace mf;
+using dma::dma16;
+using dma::i32x4;
+using dma::raw_desc;
 
 constexpr int NWAVE = 8;
 constexpr int NTHR = 64 * NWAVE;
 constexpr int MQ = 32 * NWAVE;  // queries per tile (must match the main kernel)
-constexpr long kPrepassWorkgroups = 256;  // MI355X: 256 CUs
 constexpr int kComputeUnits = 256;
 
-// Tiles and their evictions; V^T copy geometry.
+// Tiles and their evictions: tile p (queries 256 p ..) writes the keys
+// [256 p - W, 256 (p + 1) - W) clipped to [0, T - W) into the L2 memory.
 struct FusedGeom {
   int T, W, n_tiles;
-  // V^T copy: key j sits in column j + voff of rows of length Tp; voff = W mod 8
-  // puts every main-kernel block (first key t0 - W) on a 16-byte boundary.
-  int voff, Tp;
   __host__ __device__ int key_begin(int p) const {
     const long a = (long)MQ * p - W;
     return (int)(a < 0 ? 0 : a);
@@ -56,217 +55,141 @@ struct FusedGeom {
     if (b > lim) b = lim;
     return (int)(b < 0 ? 0 : b);
   }
-  // copy columns the pre-pass visits for tile p (keys are column - voff): at
-  // least one 64-column block; with the copy, the last tile runs to Tp, and
-  // together the tiles cover every column of the copy.
-  __host__ __device__ int col_begin(int p) const { return (key_begin(p) + voff) & ~(KB - 1); }
-  __host__ __device__ int col_end(int p) const {
-    const int e = (vt_copy && p == n_tiles - 1) ? Tp : ((key_end(p) + voff + KB - 1) & ~(KB - 1));
-    return e > col_begin(p) ? e : col_begin(p) + KB;
+};
+
+// ---------------------------------------------------------------------------
+// Pre-pass.  Workgroup (tile p, b, h), four waves: the tile's own contribution
+// to the state, from zero,
+//   delta_p^T = sum_{j in [a_p, e_p)} eta lam^(e_p - 1 - j) v_j k_j^T   (D x D, [dv][dk]),
+// over its at most 256 evictions in 64-key blocks.  K and V rows travel
+// global -> LDS by buffer_load ... lds in the row layout of tc_tr.hpp, and
+// both MFMA operands are transpose reads of those rows:
+// A = (w V)^T, the weights w_j = eta lam^(e_p - 1 - j) applied in registers
+// and rounded to bf16 (keys past e_p weigh 0), and B = K.  Wave w owns the
+// 32x32 output tiles w TPW .. w TPW + TPW - 1 (row-major over the D/32 x D/32
+// tiles: one row of tiles at d = 128).  delta leaves through LDS as bf16
+// rows, 16 bytes per lane.
+constexpr int PW = 4;  // waves per pre-pass workgroup
+constexpr int PTHR = 64 * PW;
+// LDS stages per workgroup.  One (32 KiB at d = 128) lets five workgroups
+// share a CU, whose copies and waits overlap; same-box timings at B=1 H=16
+// T=32768 d=128 W=1024: 62 us with one stage, 65 us with two (two
+// workgroups per CU), 107 us with four (a tile's blocks all in flight, one
+// workgroup per CU).
+constexpr int PSTG = 1;
+
+template <int D>
+struct PrepLds {
+  uint16_t k[PSTG][KB * D];
+  uint16_t v[PSTG][KB * D];
+};
+
+// wait until at most n blocks (2 NS copies each) are still in flight
+template <int NS>
+__device__ __forceinline__ void wait_blocks(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<2 * NS>(); break;
+    case 2: wait_vmcnt<4 * NS>(); break;
+    default: wait_vmcnt<6 * NS>(); break;
   }
-  int tiles_per_seg;  // tiles one pre-pass workgroup walks through
-  int vt_copy;        // 1: the pre-pass writes the V^T copy
-};
-
-// Distribution of the fp32 state S^T (D x D, 32x32 tiles) over the waves.
-template <int D>
-struct StateTiles {
-  static constexpr int NST = (D / 32) * (D / 32);
-  static constexpr int TPW = NST >= NWAVE ? NST / NWAVE : 1;
-  __device__ static bool owns(int w, int i) { return w * TPW + i < NST; }
-  __device__ static int dv0(int w, int i) { return 32 * ((w * TPW + i) / (D / 32)); }
-  __device__ static int dk0(int w, int i) { return 32 * ((w * TPW + i) % (D / 32)); }
-};
-
-// Pre-pass piece: rows r, r+1 of K and V at 8 consecutive columns.  Lane l of
-// wave w takes the row pair l % 16 (+16 for odd waves) and the column group
-// 4 (w / 2) + l / 16, so each 4-byte LDS store of the transposed pieces hits
-// 64 different banks.
-struct PairRegs {
-  uint4 k0, k1, v0, v1;
-};
-
-template <int D>
-__device__ __forceinline__ void pair_piece(int& r, int& c8) {
-  const int t = threadIdx.x, l = t & 63, w = t >> 6;
-  r = 2 * (l & 15) + 32 * (w & 1);
-  c8 = 8 * (4 * (w >> 1) + (l >> 4));
-  if (c8 >= D) c8 = 0;  // threads without a piece (D < 128) still address valid memory
 }
 
-// rows j + row, j + row + 1 (j may be negative: those rows read as zero)
-template <int D>
-__device__ __forceinline__ PairRegs load_pair(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int j) {
-  int row, c8;
-  pair_piece<D>(row, c8);
-  PairRegs p;
-  p.k0 = buf_load16(rk, ((j + row) * D + c8) * 2);
-  p.v0 = buf_load16(rv, ((j + row) * D + c8) * 2);
-  p.k1 = buf_load16(rk, ((j + row + 1) * D + c8) * 2);
-  p.v1 = buf_load16(rv, ((j + row + 1) * D + c8) * 2);
-  return p;
-}
-
-// K^T and (w V)^T of one block into LDS (keys contiguous, 34-word rows), and
-// the raw V^T into the global copy.  The block holds keys col - voff for the
-// copy's columns col = jc .. jc+63 (jc a multiple of 64, so the 4-byte key
-// pair stores are aligned); w_j = eta lam^(wend-1-j) on [wbeg, wend).
-template <int D, int SKT>
-__device__ __forceinline__ void store_pair(const PairRegs& p, uint16_t* skt, uint16_t* svt,
-                                           uint16_t* __restrict__ vt_out, int Tp, int jc, int voff,
-                                           int wbeg, int wend, float et, const Decay& dec) {
-  if (threadIdx.x >= 32 * (D / 8)) return;
-  int row, c8;
-  pair_piece<D>(row, c8);
-  const int cc = jc + row;      // copy column of the first key of the pair
-  const int jj = cc - voff;     // that key
-  const float w0 = (jj >= wbeg && jj < wend) ? et * dec(wend - 1 - jj) : 0.f;
-  const float w1 = (jj + 1 >= wbeg && jj + 1 < wend) ? et * dec(wend - 2 - jj) : 0.f;
-  const uint32_t ka[4] = {p.k0.x, p.k0.y, p.k0.z, p.k0.w}, kb[4] = {p.k1.x, p.k1.y, p.k1.z, p.k1.w};
-  const uint32_t va[4] = {p.v0.x, p.v0.y, p.v0.z, p.v0.w}, vb[4] = {p.v1.x, p.v1.y, p.v1.z, p.v1.w};
+// One 16-key step of a block: acc[i] += (w V)^T K over keys jb + 16 KK ..
+template <int D, int KK, int TPW>
+__device__ __forceinline__ void prep_step(const char* sk, const char* sv, uint32_t vl, const uint32_t* kl,
+                                          int jb, int e, float et, const Decay& dec, floatx16* acc) {
+  const int hh = lane_id() >> 5;
+  u32x4 u = __builtin_bit_cast(u32x4, tr::ld1<D, KK>(sv, vl));  // keys j .. j + 7 of one feature
+  const int j = jb + 16 * KK + 8 * hh;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t vlo = (va[e] & 0xFFFFu) | (vb[e] << 16), vhi = (va[e] >> 16) | (vb[e] & 0xFFFF0000u);
-    *reinterpret_cast<uint32_t*>(skt + (c8 + 2 * e) * SKT + row) = (ka[e] & 0xFFFFu) | (kb[e] << 16);
-    *reinterpret_cast<uint32_t*>(skt + (c8 + 2 * e + 1) * SKT + row) = (ka[e] >> 16) | (kb[e] & 0xFFFF0000u);
-    *reinterpret_cast<uint32_t*>(svt + (c8 + 2 * e) * SKT + row) = cvt_pk(lo_f(va[e]) * w0, lo_f(vb[e]) * w1);
-    *reinterpret_cast<uint32_t*>(svt + (c8 + 2 * e + 1) * SKT + row) = cvt_pk(hi_f(va[e]) * w0, hi_f(vb[e]) * w1);
-    if (vt_out != nullptr && cc < Tp) {  // cc is even and Tp a multiple of 64: the pair is in range
-      *reinterpret_cast<uint32_t*>(vt_out + (long)(c8 + 2 * e) * Tp + cc) = vlo;
-      *reinterpret_cast<uint32_t*>(vt_out + (long)(c8 + 2 * e + 1) * Tp + cc) = vhi;
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int j0 = j + 2 * q, j1 = j0 + 1;
+    const float w0 = j0 < e ? et * dec(e - 1 - j0) : 0.f;
+    const float w1 = j1 < e ? et * dec(e - 1 - j1) : 0.f;
+    u[q] = cvt_pk(lo_f(u[q]) * w0, hi_f(u[q]) * w1);
   }
+  const bf16x8 xa = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = mfma32(xa, tr::ld1<D, KK>(sk, kl[i]), acc[i]);
 }
 
-// acc (this wave's S^T tiles) += (w V)^T K over one 64-key block in LDS
-template <int D, int SKT>
-__device__ __forceinline__ void state_block_mma(floatx16* acc, const uint16_t* sKt, const uint16_t* sVt) {
-  using ST = StateTiles<D>;
+template <int D>
+__global__ __launch_bounds__(PTHR) void state_tile_kernel(const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          const float* __restrict__ lam,
+                                                          const float* __restrict__ eta, int H, FusedGeom G,
+                                                          uint16_t* __restrict__ ws_state) {
+  constexpr int NT = D / 32;             // 32-wide tiles per dimension
+  constexpr int TPW = NT * NT / PW;      // output tiles per wave: 4 (d = 128), 1 (d = 64)
+  constexpr int NS = KB * D / 8 / PTHR;  // 16-byte copies per thread and block, K and V each
+  static_assert(sizeof(PrepLds<D>) >= sizeof(uint16_t) * D * D, "delta staging fits in the stages");
+  __shared__ __attribute__((aligned(16))) PrepLds<D> lds;
+  const int p = blockIdx.x, bh = blockIdx.y;
   const int w = wave_id(), l = lane_id(), col = l & 31, hh = l >> 5;
+  const int a = G.key_begin(p), e = G.key_end(p);
+  const int t0 = w * TPW, dvt = t0 / NT;  // this wave's tiles share one row of tiles
+  floatx16 acc[TPW];
 #pragma unroll
-  for (int i = 0; i < ST::TPW; ++i) {
-    if (!ST::owns(w, i)) continue;
-    const int dv0 = ST::dv0(w, i), dk0 = ST::dk0(w, i);
+  for (int i = 0; i < TPW; ++i) acc[i] = zero16();
+
+  if (e > a) {
+    const long base = (long)bh * G.T;
+    const i32x4 rk = raw_desc(k + base * D, (uint32_t)G.T * D * 2);
+    const i32x4 rv = raw_desc(v + base * D, (uint32_t)G.T * D * 2);
+    int src[NS];
 #pragma unroll
-    for (int ks = 0; ks < KB / 16; ++ks) {
-      const int kb = 16 * ks + 8 * hh;
-      const uint2 a0 = *reinterpret_cast<const uint2*>(sVt + (dv0 + col) * SKT + kb);
-      const uint2 a1 = *reinterpret_cast<const uint2*>(sVt + (dv0 + col) * SKT + kb + 4);
-      const uint2 b0 = *reinterpret_cast<const uint2*>(sKt + (dk0 + col) * SKT + kb);
-      const uint2 b1 = *reinterpret_cast<const uint2*>(sKt + (dk0 + col) * SKT + kb + 4);
-      acc[i] = mfma32(as_bf16x8(a0.x, a0.y, a1.x, a1.y), as_bf16x8(b0.x, b0.y, b1.x, b1.y), acc[i]);
+    for (int i = 0; i < NS; ++i) src[i] = tr::slot_src<D>((i * PW + w) * 64 + l);
+    // block b (keys a + 64 b ..; rows past T read as zero) into stage b % PSTG
+    auto copy = [&](int b) __attribute__((always_inline)) {
+      const int off = (a + KB * b) * D * 2;
+#pragma unroll
+      for (int i = 0; i < NS; ++i) dma16(rk, lds.k[b % PSTG] + (i * PW + w) * 512, src[i] + off);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) dma16(rv, lds.v[b % PSTG] + (i * PW + w) * 512, src[i] + off);
+    };
+    const uint32_t vl = tr::lane_offset<D>(dvt);
+    uint32_t kl[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) kl[i] = tr::lane_offset<D>((t0 + i) % NT);
+    const Decay dec(lam[bh % H]);
+    const float et = eta[bh % H];
+    const int nblk = (e - a + KB - 1) / KB;  // 1 .. 4
+#pragma unroll 1
+    for (int b = 0; b < nblk && b < PSTG; ++b) copy(b);
+#pragma unroll 1
+    for (int b = 0; b < nblk; ++b) {
+      // block b has landed (the blocks issued after it may still be in flight) and is visible to every wave
+      wait_blocks<NS>(min(nblk - 1, b + PSTG - 1) - b);
+      lds_barrier();
+      const char* sk = reinterpret_cast<const char*>(lds.k[b % PSTG]);
+      const char* sv = reinterpret_cast<const char*>(lds.v[b % PSTG]);
+      const int jb = a + KB * b;
+      prep_step<D, 0, TPW>(sk, sv, vl, kl, jb, e, et, dec, acc);
+      prep_step<D, 1, TPW>(sk, sv, vl, kl, jb, e, et, dec, acc);
+      prep_step<D, 2, TPW>(sk, sv, vl, kl, jb, e, et, dec, acc);
+      prep_step<D, 3, TPW>(sk, sv, vl, kl, jb, e, et, dec, acc);
+      if (b + PSTG < nblk) {
+        lds_barrier();  // every wave is done with this stage before it is refilled
+        copy(b + PSTG);
+      }
     }
+    lds_barrier();  // ... and before the stages hold delta below
   }
-}
 
-// A tile's delta (this wave's S^T tiles) into the workspace as bf16.  At
-// d = 128 a wave's two 32x32 tiles cover the same rows and adjacent column
-// blocks (dk0, dk0 + 32): the two halves of the wave trade values (lane
-// c <-> c + 32), so that each store writes 64 consecutive columns (128 bytes)
-// of one row instead of 32.
-template <int D>
-__device__ __forceinline__ void store_delta(uint16_t* __restrict__ out, const floatx16* acc) {
-  using ST = StateTiles<D>;
-  const int w = wave_id(), l = lane_id(), col = l & 31, hh = l >> 5;
-  if constexpr (ST::TPW == 2) {
-    const int dv0 = ST::dv0(w, 0), dk0 = ST::dk0(w, 0);  // tile 1: same rows, columns dk0 + 32 ..
+  // delta as bf16 [dv][dk] rows through LDS, then 16 bytes per lane
+  uint16_t* stage = reinterpret_cast<uint16_t*>(&lds);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float a0 = acc[0][e], a1 = acc[1][e];
-      const float s0 = __shfl_xor(a0, 32), s1 = __shfl_xor(a1, 32);
-      const int ra = dv0 + 8 * (e >> 2) + (e & 3);  // row of element e in the lower half
-      uint16_t* p = out + ra * D + dk0 + 32 * hh + col;
-      p[0] = f32_to_bf16(hh ? s1 : a0);      // row ra
-      p[4 * D] = f32_to_bf16(hh ? a1 : s0);  // row ra + 4
-    }
-  } else {
+  for (int i = 0; i < TPW; ++i) {
+    const int dk = 32 * ((t0 + i) % NT) + col;
 #pragma unroll
-    for (int i = 0; i < ST::TPW; ++i) {
-      if (!ST::owns(w, i)) continue;
-      const int dv0 = ST::dv0(w, i), dk0 = ST::dk0(w, i);
+    for (int r = 0; r < 16; ++r) stage[(32 * dvt + 8 * (r >> 2) + 4 * hh + (r & 3)) * D + dk] = f32_to_bf16(acc[i][r]);
+  }
+  lds_barrier();
+  uint4* out = reinterpret_cast<uint4*>(ws_state + ((long)bh * G.n_tiles + p) * D * D);
+  const uint4* st = reinterpret_cast<const uint4*>(stage);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) out[(dv0 + 8 * (e >> 2) + 4 * hh + (e & 3)) * D + dk0 + col] = f32_to_bf16(acc[i][e]);
-    }
-  }
-}
-
-// Next (tile, column block) of a pre-pass walk: every tile has >= 1 block.
-__device__ __forceinline__ void next_block(const FusedGeom& G, int& p, int& j) {
-  j += KB;
-  if (j >= G.col_end(p)) {
-    ++p;
-    j = G.col_begin(p);
-  }
-}
-
-// Workgroup (segment, b, h) walks tiles_per_seg consecutive tiles.  For each
-// tile p: the contribution of its evictions to the state, from zero,
-// delta_p = sum_j eta lam^(b_p - 1 - j) v_j k_j^T over [a_p, b_p), and the
-// V^T copy of its column blocks (keys outside [0, T) written as zero).  The
-// blocks of all the segment's tiles form one stream with three blocks in
-// flight in registers.
-template <int D>
-__global__ __launch_bounds__(NTHR) void fused_state_kernel(const uint16_t* __restrict__ k,
-                                                           const uint16_t* __restrict__ v,
-                                                           const float* __restrict__ lam,
-                                                           const float* __restrict__ eta, int H,
-                                                           FusedGeom G, uint16_t* __restrict__ ws_state,
-                                                           uint16_t* __restrict__ ws_vt) {
-  constexpr int SKT = KB + 4;  // K^T and V^T rows: keys contiguous, 34-word stride
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * SKT];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * SKT];
-  using ST = StateTiles<D>;
-  const int bh = blockIdx.y;
-  const int p_begin = blockIdx.x * G.tiles_per_seg;
-  const int p_end = min(p_begin + G.tiles_per_seg, G.n_tiles);
-  const Decay dec(lam[bh % H]);
-  const float et = eta[bh % H];
-  const long base = (long)bh * G.T;
-  const int voff = G.voff;
-  uint16_t* vt_out = G.vt_copy ? ws_vt + (long)bh * D * G.Tp : nullptr;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + base * D, (uint32_t)G.T * D * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + base * D, (uint32_t)G.T * D * 2);
-
-  floatx16 acc[ST::TPW];
-#pragma unroll
-  for (int i = 0; i < ST::TPW; ++i) acc[i] = zero16();
-
-  // compute cursor (pc, jc) and load cursor (pl, jl), three blocks apart.
-  // r0, r1, r2 keep fixed roles (a register that is the target of a load in
-  // flight is never copied) and the loads are issued on every path, so their
-  // count is the same everywhere; loads past the segment read zeros or data
-  // that is not used.
-  int pc = p_begin, jc = G.col_begin(pc);
-  int pl = pc, jl = jc;
-  PairRegs r0 = load_pair<D>(rk, rv, jl - voff);
-  next_block(G, pl, jl);
-  PairRegs r1 = load_pair<D>(rk, rv, jl - voff);
-  next_block(G, pl, jl);
-  PairRegs r2 = load_pair<D>(rk, rv, jl - voff);
-  next_block(G, pl, jl);
-#define TC_STATE_STEP(R)                                                              \
-  if (pc < p_end) {                                                                   \
-    lds_barrier();                                                                    \
-    store_pair<D, SKT>(R, sKt, sVt, vt_out, G.Tp, jc, voff, G.key_begin(pc),          \
-                       G.key_end(pc), et, dec);                                       \
-    lds_barrier();                                                                    \
-  }                                                                                   \
-  R = load_pair<D>(rk, rv, jl - voff);                                                \
-  next_block(G, pl, jl);                                                              \
-  if (pc < p_end) {                                                                   \
-    state_block_mma<D, SKT>(acc, sKt, sVt);                                           \
-    if (jc + KB >= G.col_end(pc)) {                                                   \
-      store_delta<D>(ws_state + ((long)bh * G.n_tiles + pc) * D * D, acc);            \
-      _Pragma("unroll") for (int i = 0; i < ST::TPW; ++i) acc[i] = zero16();          \
-    }                                                                                 \
-    next_block(G, pc, jc);                                                            \
-  }
-  while (pc < p_end) {
-    TC_STATE_STEP(r0)
-    TC_STATE_STEP(r1)
-    TC_STATE_STEP(r2)
-  }
-#undef TC_STATE_STEP
+  for (int c = threadIdx.x; c < D * D / 8; c += PTHR) out[c] = st[c];
 }
 
 // S_0 = 0, S_{p+1} = lam^len(p) S_p + delta_p, carried in fp32 (delta_p is
@@ -549,11 +472,7 @@ FusedGeom make_geom(int T, int W) {
   FusedGeom G{};
   G.T = T;
   G.W = W;
-  G.voff = W & 7;
-  G.Tp = (T + G.voff + KB - 1) / KB * KB;
   G.n_tiles = (T + MQ - 1) / MQ;
-  G.tiles_per_seg = 1;
-  G.vt_copy = 1;
   return G;
 }
 
@@ -567,15 +486,7 @@ hipError_t run_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
   const size_t ne = state_elems(G, B, H, D);
   uint16_t* delta = static_cast<uint16_t*>(ws);
   uint16_t* sst = delta + ne;
-  // about one pre-pass workgroup per CU, each streaming several tiles; the
-  // main kernel reads V rows itself (LDS transpose reads): no V^T copy
-  FusedGeom Gs = G;
-  Gs.vt_copy = 0;
-  const long units = (long)G.n_tiles * BH;
-  Gs.tiles_per_seg = (int)std::max<long>(1, (units + kPrepassWorkgroups - 1) / kPrepassWorkgroups);
-  const int n_seg = (G.n_tiles + Gs.tiles_per_seg - 1) / Gs.tiles_per_seg;
-  hipLaunchKernelGGL(fused_state_kernel<D>, dim3(n_seg, BH), dim3(NTHR), 0, s, k, v, lam, eta, H, Gs,
-                     delta, static_cast<uint16_t*>(nullptr));
+  hipLaunchKernelGGL(state_tile_kernel<D>, dim3(G.n_tiles, BH), dim3(PTHR), 0, s, k, v, lam, eta, H, G, delta);
   hipLaunchKernelGGL(fused_prefix_kernel, dim3((D * D / 4 + 63) / 64, BH), dim3(64), 0, s, lam, H, D,
                      G, delta, sst, A_final);
   const hipError_t e = hipGetLastError();
@@ -596,14 +507,7 @@ hipError_t run_scan_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v
   const size_t ne = state_elems(G, B, H, D);
   uint16_t* delta = static_cast<uint16_t*>(ws);
   uint16_t* sst = delta + ne;
-  // the read kernel transposes V itself: no V^T copy
-  FusedGeom Gs = G;
-  Gs.vt_copy = 0;
-  const long units = (long)G.n_tiles * BH;
-  Gs.tiles_per_seg = (int)std::max<long>(1, (units + kPrepassWorkgroups - 1) / kPrepassWorkgroups);
-  const int n_seg = (G.n_tiles + Gs.tiles_per_seg - 1) / Gs.tiles_per_seg;
-  hipLaunchKernelGGL(fused_state_kernel<D>, dim3(n_seg, BH), dim3(NTHR), 0, s, k, v, lam, eta, H, Gs,
-                     delta, static_cast<uint16_t*>(nullptr));
+  hipLaunchKernelGGL(state_tile_kernel<D>, dim3(G.n_tiles, BH), dim3(PTHR), 0, s, k, v, lam, eta, H, G, delta);
   hipLaunchKernelGGL(fused_prefix_kernel, dim3((D * D / 4 + 63) / 64, BH), dim3(64), 0, s, lam, H, D,
                      G, delta, sst, A_final);
   profile_mark_before(s);

@@ -31,6 +31,7 @@
 #include "tc_kernels.hpp"
 #include "tc_dma.hpp"
 #include "tc_mfma.hpp"
+#include "tc_tr.hpp"
 
 #include <math.h>
 
@@ -54,21 +55,9 @@ constexpr float kNegBig = -1.0e30f;
 template <int D>
 struct SwaLds {
   uint16_t k[NSTAGE][KB * D];
-  uint16_t v[NSTAGE][KB * D];  // V rows (key-major), 16-byte pieces permuted per row (v_swz)
+  uint16_t v[NSTAGE][KB * D];  // V rows in the row layout of tc_tr.hpp (16-byte pieces permuted per row)
   uint16_t st[D * D];  // entering L2 state S^T (rows dv), as D/64 K-layout blocks
 };
-
-// V block layout: row c (key c of the block) holds that key's D features; its
-// 16-byte piece p (features 8p .. 8p+7) sits at position p ^ v_swz(c).  A
-// transpose read of PV k-step j gives the 16 lanes of a quarter wave 4 keys
-// (rows) of 16 features: over the wave 8 rows x 4 pieces, and the XOR puts
-// every 4-bank group under exactly two of the 32 pieces (two LDS cycles, no
-// further conflict).
-template <int D>
-__device__ __forceinline__ int v_swz(int c) {
-  static_assert(D == 64 || D == 128, "V rows of 8 or 16 pieces");
-  return D == 128 ? 4 * (c & 3) : 4 * ((c >> 1) & 1);
-}
 
 template <int D>
 struct Dma {
@@ -96,9 +85,8 @@ __device__ __forceinline__ DmaOff<D> dma_offsets() {
   }
 #pragma unroll
   for (int i = 0; i < Dma<D>::NV; ++i) {
-    // slot s of the stage holds row s / (D / 8), position s % (D / 8)
-    const int sl = (i * NWAVE + w) * 64 + l, row = sl / (D / 8), pos = sl % (D / 8);
-    o.v[i] = (row * D + 8 * (pos ^ v_swz<D>(row))) * 2;
+    const int sl = (i * NWAVE + w) * 64 + l;
+    o.v[i] = tr::slot_src<D>(sl);
   }
   return o;
 }
@@ -185,39 +173,6 @@ __device__ __forceinline__ void mm_k2(const bf16x8* x, const bf16x8* qreg, float
     a0 = mfma32(x[2 * i], qreg[KS + i], a0);
     a1 = mfma32(x[2 * i + 1], qreg[KS + i], a1);
   }
-}
-// V^T operands of PV k-step KK, all D/32 row tiles: lane (col, hh) needs
-// keys 16 KK + 8 hh .. +7 of feature 32 dt + col.  Each comes from two
-// transpose reads of 4 key rows; vls[dt] is the lane's byte offset for tile dt
-// (v_lane_offsets), the key rows add immediates.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint2 lds_tr(const char* base, uint32_t off) {
-  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(base + off));
-  return __builtin_bit_cast(uint2, x);
-}
-template <int D, int KK>
-__device__ __forceinline__ void ld_v(const char* sv, const uint32_t* vls, bf16x8* x) {
-  constexpr uint32_t RB = 2 * D;  // bytes per V row
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const uint2 a = lds_tr(sv, vls[dt] + (16 * KK) * RB);
-    const uint2 b = lds_tr(sv, vls[dt] + (16 * KK + 4) * RB);
-    x[dt] = as_bf16x8(a.x, a.y, b.x, b.y);
-  }
-}
-// Lane offsets of the transpose reads (ld_v): the 16 lanes i of a quarter
-// wave (feature half (col / 16) % 2, key half hh) read row 8 hh + i / 4 at
-// features 32 dt + 16 ((col / 16) % 2) + 4 (i % 4), placed by v_swz.
-template <int D>
-__device__ __forceinline__ void v_lane_offsets(uint32_t* vls) {
-  const int l = lane_id(), col = l & 31, hh = l >> 5, i = col & 15;
-  const int row = 8 * hh + (i >> 2);
-  const int piece_lo = ((col & 16) >> 3) + ((col & 3) >> 1);  // piece within the 32 features of a tile
-  const int half = col & 1;                                    // 8-byte half of that piece
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-    vls[dt] = (uint32_t)(row * 2 * D + 16 * ((4 * dt + piece_lo) ^ v_swz<D>(row)) + 8 * half);
 }
 template <int D>
 __device__ __forceinline__ void mm_v(const bf16x8* x, bf16x8 pb, floatx16* o) {
@@ -375,12 +330,12 @@ __device__ __forceinline__ void swa_step(const char* sk_nxt, const char* sv_cur,
     p0 = probs<0>(sc, sl2, nms, psum);
     TC_GROUPS(4, 4, 6);
     TC_SB();
-    ld_v<D, 0>(sv_cur, vls, va);
+    tr::ld<D, 0>(sv_cur, vls, va);
     mm_k2<6>(kb, qreg, a0, a1);
   } else {
     dma_part<D, 1>(job, doff);
     TC_SB();
-    ld_v<D, 0>(sv_cur, vls, va);
+    tr::ld<D, 0>(sv_cur, vls, va);
     mm_k2<2>(kb, qreg, a0, a1);
     p0 = probs<0>(sc, sl2, nms, psum);
     TC_GROUPS(NVR, 4, 6);
@@ -395,17 +350,17 @@ __device__ __forceinline__ void swa_step(const char* sk_nxt, const char* sv_cur,
     dma_part<D, 3>(job, doff);
     TC_SB();
   }
-  ld_v<D, 1>(sv_cur, vls, vb);
+  tr::ld<D, 1>(sv_cur, vls, vb);
   mm_v<D>(va, p0, o);
   p2 = probs<2>(sc, sl2, nms, psum);
   TC_GROUPS(NVR, NDT, 24 / NDT);
   TC_SB();
-  ld_v<D, 2>(sv_cur, vls, va);
+  tr::ld<D, 2>(sv_cur, vls, va);
   mm_v<D>(vb, p1, o);
   p3 = probs<3>(sc, sl2, nms, psum);
   TC_GROUPS(NVR, NDT, 24 / NDT);
   TC_SB();
-  ld_v<D, 3>(sv_cur, vls, vb);
+  tr::ld<D, 3>(sv_cur, vls, vb);
   mm_v<D>(va, p2, o);
   TC_SB();
   mm_v<D>(vb, p3, o);
@@ -465,18 +420,18 @@ __device__ __forceinline__ void l2_block(const char* sk, const char* sv, const u
   const float xl = static_cast<float>(hi - 8 * hh) * log2lam;
   bf16x8 va[NDT], vb[NDT];
   TC_SB();
-  ld_v<D, 0>(sv, vls, va);
+  tr::ld<D, 0>(sv, vls, va);
   const bf16x8 p0 = l2probs<0>(s, lo, span, xl, log2lam, fe);
   TC_SB();
-  ld_v<D, 1>(sv, vls, vb);
+  tr::ld<D, 1>(sv, vls, vb);
   mm_v<D>(va, p0, o);
   const bf16x8 p1 = l2probs<1>(s, lo, span, xl, log2lam, fe);
   TC_SB();
-  ld_v<D, 2>(sv, vls, va);
+  tr::ld<D, 2>(sv, vls, va);
   mm_v<D>(vb, p1, o);
   const bf16x8 p2 = l2probs<2>(s, lo, span, xl, log2lam, fe);
   TC_SB();
-  ld_v<D, 3>(sv, vls, vb);
+  tr::ld<D, 3>(sv, vls, vb);
   mm_v<D>(va, p2, o);
   const bf16x8 p3 = l2probs<3>(s, lo, span, xl, log2lam, fe);
   TC_SB();
@@ -514,7 +469,7 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
 #pragma unroll
   for (int j = 0; j < 4; ++j) ls[j] = lane_slot(j);
   uint32_t vls[NDT];
-  v_lane_offsets<D>(vls);
+  tr::lane_offsets<D>(vls);
 
 #pragma unroll 1
   for (int local = blockIdx.x / NXCD; local < per_xcd; local += n_slots) {
