@@ -220,23 +220,48 @@ class KernelTimer:
         return sum(out) / len(out)
 
 
+def source_files(source):
+    """csrc/<source> and the local headers it includes (quoted #include, followed
+    recursively), each once, in first-seen order."""
+    import re
+
+    csrc = os.path.join(ROOT, "linear_attention_tensor_amd", "csrc")
+    seen, todo = [], [source]
+    while todo:
+        name = todo.pop(0)
+        path = os.path.join(csrc, name)
+        if name in seen or not os.path.exists(path):
+            continue
+        seen.append(name)
+        todo += re.findall(r'^#include "([^"]+)"', open(path).read(), flags=re.M)
+    return seen
+
+
+def source_digest(source):
+    """First 16 hex digits of the SHA-256 of csrc/<source> and its local headers
+    (source_files), concatenated: the code a counter summary was taken from."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "linear_attention_tensor_amd", "csrc")
+    h = hashlib.sha256()
+    for name in source_files(source):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def counters_from_profile(name, source):
     """Fields of a committed rocprofv3 counter summary profiles/<name>.txt
     ("key: value" lines), or None when there is none or its recorded source
-    hash no longer matches csrc/<source>."""
-    import hashlib
-
+    digest no longer matches csrc/<source> and its headers."""
     path = os.path.join(ROOT, "profiles", name + ".txt")
-    src = os.path.join(ROOT, "linear_attention_tensor_amd", "csrc", source)
-    if not os.path.exists(path) or not os.path.exists(src):
+    if not os.path.exists(path) or not source_files(source):
         return None
     fields = {}
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             fields[key.strip()] = val.strip()
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if fields.get("source_sha256_16") != digest:
+    if fields.get("source_sha256_16") != source_digest(source):
         return None
     return fields
 
@@ -244,20 +269,9 @@ def counters_from_profile(name, source):
 def traffic_from_profile(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (profiles/traffic_<kernel>_fused_layer_bf16.txt), or None when
-    there is none or its source hash no longer matches the kernel source."""
-    import hashlib
-
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_fused_layer_bf16.txt")
-    src = os.path.join(ROOT, "linear_attention_tensor_amd", "csrc", "tc_swa.hip")
-    if not os.path.exists(path) or not os.path.exists(src):
-        return None
-    fields = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            key, val = line.split(":", 1)
-            fields[key.strip()] = val.strip()
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if fields.get("source_sha256_16") != digest or "hbm_bytes_per_launch" not in fields:
+    there is none or the kernel source has changed since."""
+    fields = counters_from_profile(f"traffic_{kernel}_fused_layer_bf16", "tc_swa.hip")
+    if fields is None or "hbm_bytes_per_launch" not in fields:
         return None
     return float(fields["hbm_bytes_per_launch"])
 
