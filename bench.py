@@ -42,7 +42,7 @@ def parse():
                     help="decode steps to time (default: the workload's 4096; 1024 for the 4x side run); "
                          "short runs are for profiler counter passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fused", "scan", "scan_bf16", "scan_backward", "decode", "decode_x4", "decode_layer", "delta",
+    ap.add_argument("--only", choices=["fused", "scan", "scan_bf16", "scan_backward", "layer_backward", "decode", "decode_x4", "decode_layer", "delta",
                                            "delta_f32", "delta_backward", "hebbian", "capacity"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -94,6 +94,14 @@ def scan_backward_flops(B, H, T, d, W, C=64):
 def scan_backward_bytes(B, H, T, d):
     # read q, k, v, dm and write dq, dk, dv once, fp32
     return B * H * T * d * 4 * 7
+
+
+def window_backward_flops(B, H, T, d, W):
+    """Window softmax backward: per (query, key) pair of the window the scores
+    (2d), dp = <dy, v> (2d), dv += p dy (2d), dq += ds k (2d) and
+    dk += ds q (2d)."""
+    pairs = sum(min(W, t + 1) for t in range(min(T, W))) + max(T - W, 0) * W
+    return B * H * 10 * d * pairs
 
 
 def decode_bytes_per_head(d, in_bytes=2):
@@ -472,6 +480,47 @@ def bench_scan_backward(steps, warmup, dev):
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
 
 
+def bench_layer_backward(steps, warmup, dev, x=None):
+    """tc_fused_layer_backward at the fused layer's size (bf16 inputs, d =
+    128): the gated L2-read backward (four d = 64 pieces) and the window
+    softmax backward, fp32 arithmetic."""
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["fused_layer_bf16"]
+    if x is None:
+        x = I.draw_workload(w.name)
+    q, k, v = (to_dev_bf16(x[n], dev) for n in ("q", "k", "v"))
+    lam, eta, g = (to_dev_f32(x[n], dev) for n in ("lam", "eta", "g"))
+    dy = to_dev_f32(I.draw_cotangent(w.B, w.H, w.T, w.d, seed=w.seed), dev)
+    shape = (w.B, w.H, w.T, w.d)
+    gq, gk, gv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
+    glam, geta, gg = (torch.empty((w.H,), dtype=torch.float32, device=dev) for _ in range(3))
+    lib = ops.lib()
+    nb = lib.tc_fused_layer_backward_workspace_bytes(w.B, w.H, w.T, w.d, w.d, w.W, 64, 1)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 1, ops._ptr(lam), ops._ptr(eta), ops._ptr(g), w.B, w.H, w.T,
+            w.d, w.d, w.W, 64, 1.0 / math.sqrt(w.d), ops._ptr(dy), ops._ptr(gq), ops._ptr(gk), ops._ptr(gv),
+            ops._ptr(glam), ops._ptr(geta), ops._ptr(gg), ops._ptr(ws), ws.numel(), ops._stream())
+
+    def call(_):
+        if lib.tc_fused_layer_backward(*args) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    # about 10 ms per call: a few untimed calls settle the clock
+    ms, ms_call, _ = time_calls(call, max(1, steps // 4), min(warmup, 5))
+    flops = window_backward_flops(w.B, w.H, w.T, w.d, w.W) + scan_backward_flops(w.B, w.H, w.T, w.d, w.W)
+    return {"workload": w.name + " backward", "ms_per_step": ms,
+            "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+            "roofline": roofline("alu", flops / (ms_call * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
+            "roofline_scope": "whole call: window-softmax backward (fp32 vector ALU) plus the gated L2-read "
+                              "backward (fp32 MFMA); both units peak at 157.3 TFLOP/s",
+            "ms_per_call": ms_call, "workspace_bytes": nb,
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "bf16"}}
+
+
 def bench_decode(steps, warmup, dev, n_steps=4096, B=None):
     """The decode workload's L2 step (4096 steps, 64 x 32 heads).  With B
     given (the side run: 256 sequences, 512 MiB of A) the state no longer
@@ -846,6 +895,7 @@ def main():
     if only is None and not args.no_components:
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
         components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
+        components["fused_layer_backward_bf16"] = bench_layer_backward(args.steps, args.warmup, dev, x)
         components["scan_bf16_fused_size"] = bench_scan_bf16(args.steps, args.warmup, dev)
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 4096)
         components["decode_bf16_x4"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 1024,
@@ -862,6 +912,8 @@ def main():
         components["scan_bf16_fused_size"] = bench_scan_bf16(args.steps, args.warmup, dev)
     elif only == "scan_backward":
         components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
+    elif only == "layer_backward":
+        components["fused_layer_backward_bf16"] = bench_layer_backward(args.steps, args.warmup, dev)
     elif only == "decode":
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 4096)
     elif only == "decode_x4":
