@@ -482,8 +482,8 @@ def bench_scan_backward(steps, warmup, dev):
 
 def bench_layer_backward(steps, warmup, dev, x=None):
     """tc_fused_layer_backward at the fused layer's size (bf16 inputs, d =
-    128): the gated L2-read backward (four d = 64 pieces) and the window
-    softmax backward, fp32 arithmetic."""
+    128): the gated L2-read backward (four d = 64 pieces, fp32) and the window
+    softmax backward (bf16 MFMA)."""
     import torch
 
     from linear_attention_tensor_amd import inputs as I
@@ -514,9 +514,9 @@ def bench_layer_backward(steps, warmup, dev, x=None):
     flops = window_backward_flops(w.B, w.H, w.T, w.d, w.W) + scan_backward_flops(w.B, w.H, w.T, w.d, w.W)
     return {"workload": w.name + " backward", "ms_per_step": ms,
             "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
-            "roofline": roofline("alu", flops / (ms_call * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
-            "roofline_scope": "whole call: window-softmax backward (fp32 vector ALU) plus the gated L2-read "
-                              "backward (fp32 MFMA); both units peak at 157.3 TFLOP/s",
+            "roofline": roofline("mfma", flops / (ms_call * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
+            "roofline_scope": "whole call: the window-softmax backward (bf16 MFMA) plus the gated L2-read "
+                              "backward (fp32 MFMA, four d = 64 pieces), all flops over the fp32 peak",
             "ms_per_call": ms_call, "workspace_bytes": nb,
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "bf16"}}
 

@@ -220,12 +220,15 @@ tc_status tc_window_attention(const void* q, const void* k, const void* v, tc_dt
  * tc_window_attention with the same arguments,
  *   dv_j = sum_t p_tj dy_t,  ds_tj = p_tj (<dy_t, v_j> - <dy_t, y_t>),
  *   dq_t = scale sum_j ds_tj k_j,  dk_j = scale sum_t ds_tj q_t,
- * with p_tj the softmax weights over the window.  fp32 arithmetic for fp32
- * or bf16 inputs, any supported d.
+ * with p_tj the softmax weights over the window.  bf16 inputs with d in
+ * {64, 128} run on bf16 MFMA: the forward is recomputed (y and each query's
+ * log-sum-exp), dy, p and ds are rounded to bf16 as MFMA operands, sums are
+ * fp32 (held to the bf16-input bar).  Other inputs run in fp32 arithmetic.
  *   dy           [B, H, T, dv] float32.
  *   dq, dk, dv   out [B, H, T, d] float32.
  *   ws           at least tc_window_attention_backward_workspace_bytes(...)
- *                bytes (per query: the log-sum-exp of its scores and <dy, y>).
+ *                bytes: per query the log-sum-exp of its scores and <dy, y>,
+ *                and on the MFMA path also y (fp32) and dy (bf16).
  * ------------------------------------------------------------------------- */
 size_t tc_window_attention_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, tc_dtype dt);
 tc_status tc_window_attention_backward(const void* q, const void* k, const void* v, tc_dtype dt,

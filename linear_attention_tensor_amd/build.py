@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtc.so")
 
-SOURCES = ["tc_api.cpp", "tc_scan.hip", "tc_decode.hip", "tc_fused.hip", "tc_swa.hip", "tc_window.hip", "tc_window_bwd.hip", "tc_convert.hip", "delta_scan.hip", "delta_bf16.hip",
+SOURCES = ["tc_api.cpp", "tc_scan.hip", "tc_decode.hip", "tc_fused.hip", "tc_swa.hip", "tc_window.hip", "tc_window_bwd.hip", "tc_window_bwd_mfma.hip", "tc_convert.hip", "delta_scan.hip", "delta_bf16.hip",
            "delta_bwd.hip", "tc_memory.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -329,7 +329,7 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
 }
 
 static size_t fused_bwd_need(int B, int H, int T, int d, int W, tc_dtype dt) {
-  return round_up_256(scan_bwd_need(B, H, T, d, W, dt)) + tc::window_bwd_ws_bytes(B, H, T);
+  return round_up_256(scan_bwd_need(B, H, T, d, W, dt)) + tc::window_bwd_ws_bytes(B, H, T, d, dt == TC_BF16);
 }
 
 size_t tc_fused_layer_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk, tc_dtype dt) {
@@ -478,7 +478,7 @@ tc_status tc_window_attention(const void* q, const void* k, const void* v, tc_dt
       tc::profile_mark_before(s);
       const hipError_t e = tc::launch_swa(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                           static_cast<const uint16_t*>(v), nullptr, nullptr, nullptr, nullptr, B,
-                                          H, T, dk, W, softmax_scale, y, s);
+                                          H, T, dk, W, softmax_scale, y, nullptr, s);
       tc::profile_mark_after(s);
       return from_hip(e, fn);
     }
@@ -497,7 +497,7 @@ size_t tc_window_attention_backward_workspace_bytes(int B, int H, int T, int dk,
     return SIZE_MAX;
   }
   ok();
-  return tc::window_bwd_ws_bytes(B, H, T);
+  return tc::window_bwd_ws_bytes(B, H, T, dk, dt == TC_BF16);
 }
 
 tc_status tc_window_attention_backward(const void* q, const void* k, const void* v, tc_dtype dt, int B, int H, int T,
@@ -513,7 +513,7 @@ tc_status tc_window_attention_backward(const void* q, const void* k, const void*
     if (B == 0 || H == 0 || T == 0) return ok();
     if (!q || !k || !v || !dy || !dq || !dk_out || !dv_out)
       return fail(TC_ERR_INVALID_ARG, "%s: q, k, v, dy, dq, dk, dv must not be NULL", fn);
-    const size_t need = tc::window_bwd_ws_bytes(B, H, T);
+    const size_t need = tc::window_bwd_ws_bytes(B, H, T, dk, dt == TC_BF16);
     if (ws_bytes < need) return fail(TC_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
     if (!ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
     return from_hip(tc::launch_window_backward(q, k, v, dt == TC_BF16, dy, B, H, T, dk, W, softmax_scale, ws, false,

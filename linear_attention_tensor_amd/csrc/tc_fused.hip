@@ -492,7 +492,7 @@ hipError_t run_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   profile_mark_before(s);
-  const hipError_t e2 = launch_swa(q, k, v, sst, lam, eta, g, B, H, G.T, D, G.W, scale, y, s);
+  const hipError_t e2 = launch_swa(q, k, v, sst, lam, eta, g, B, H, G.T, D, G.W, scale, y, nullptr, s);
   profile_mark_after(s);
   return e2;
 }

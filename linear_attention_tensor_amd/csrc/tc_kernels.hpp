@@ -67,24 +67,33 @@ hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, cons
 hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const float* lam,
                            const float* eta, const float* g, int B, int H, int T, int d, int W,
                            float scale, float* y, float* A_final, void* ws, hipStream_t s);
-// Main kernel of the fused layer (tc_swa.hip): q, k, v rows [B*H][T][d] bf16,
-// sst the entering state of every 256-query tile
-// ([B*H][ceil(T/256)][d][d] bf16, S^T) or nullptr for no L2 term.
 // Exact window softmax in fp32 arithmetic (tc_window.hip): fp32 inputs or
 // bf16 with d in {16, 32}.  With g, y already holds the L2 read m and becomes
 // y_local + sigmoid(g[h]) m; without, y = y_local.
 hipError_t launch_window(const void* q, const void* k, const void* v, bool bf16, int B, int H, int T, int d, int W,
                          float scale, const float* g, float* y, hipStream_t s);
-// Backward of the exact window softmax (tc_window_bwd.hip), fp32 arithmetic:
-// dq, dk, dv of sum <dy, y_local>; with accumulate they are added to what the
-// buffers hold.  ws: window_bwd_ws_bytes (per-query log-sum-exp and <dy, y>).
-size_t window_bwd_ws_bytes(int B, int H, int T);
+// Backward of the exact window softmax: dq, dk, dv of sum <dy, y_local>; with
+// accumulate they are added to what the buffers hold.  bf16 inputs with d in
+// {64, 128} run on bf16 MFMA (tc_window_bwd_mfma.hip: ws holds y_local fp32,
+// dy as bf16 and the (log-sum-exp, <dy, y>) pairs), everything else in fp32
+// arithmetic (tc_window_bwd.hip: ws holds the log-sum-exp and <dy, y>).
+size_t window_bwd_ws_bytes(int B, int H, int T, int d, bool bf16);
+bool window_bwd_mfma(bool bf16, int d);
+size_t window_bwd_mfma_ws_bytes(int B, int H, int T, int d);
+hipError_t launch_window_backward_mfma(const void* q, const void* k, const void* v, const float* dy, int B, int H,
+                                       int T, int d, int W, float scale, void* ws, bool accumulate, float* dq,
+                                       float* dk, float* dv, hipStream_t s);
 hipError_t launch_window_backward(const void* q, const void* k, const void* v, bool bf16, const float* dy, int B,
                                   int H, int T, int d, int W, float scale, void* ws, bool accumulate, float* dq,
                                   float* dk, float* dv, hipStream_t s);
+// Main kernel of the fused layer (tc_swa.hip): q, k, v rows [B*H][T][d] bf16,
+// sst the entering state of every 256-query tile
+// ([B*H][ceil(T/256)][d][d] bf16, S^T) or nullptr for no L2 term; lse2, when
+// not nullptr, receives log2 of every query's softmax denominator in the
+// units exp2(scale log2(e) s) at lse2[2 row].
 hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* sst,
                       const float* lam, const float* eta, const float* g, int B, int H, int T, int d,
-                      int W, float scale, float* y, hipStream_t s);
+                      int W, float scale, float* y, float* lse2, hipStream_t s);
 
 size_t delta_ws_bytes(int B, int H, int T, int dk, int dv, bool bf16);
 hipError_t launch_delta_scan(const void* q, const void* k, const void* v, bool bf16,

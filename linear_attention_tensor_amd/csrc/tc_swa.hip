@@ -451,7 +451,7 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
                                                    const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v, L2Args l2,
                                                    int T, int W, int n_tiles, int n_items, float sl2,
-                                                   float* __restrict__ y) {
+                                                   float* __restrict__ y, float* __restrict__ lse2) {
   constexpr int NKS = D / 16;
   constexpr int NDT = D / 32;
   __shared__ __attribute__((aligned(16))) SwaLds<D> lds;
@@ -570,6 +570,9 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
 
     const float tot = sum_halves(sm.l);
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    // log2 of the softmax denominator in the exp2(sl2 s) units of the scores
+    // (for the backward), every other float of lse2
+    if (lse2 != nullptr && tq < T && hh == 0) lse2[2 * (base + tq)] = sm.m * sl2 + log2f(tot);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[dt] *= inv;
 
@@ -633,7 +636,7 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
 
 hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* sst,
                       const float* lam, const float* eta, const float* g, int B, int H, int T, int d,
-                      int W, float scale, float* y, hipStream_t s) {
+                      int W, float scale, float* y, float* lse2, hipStream_t s) {
   const int n_tiles = (T + MQ - 1) / MQ;
   const int n_items = B * H * n_tiles;
   // as many workgroups as fit at once (LDS: one per CU at d = 128, two at d = 64), a multiple of NXCD
@@ -643,10 +646,10 @@ hipError_t launch_swa(const uint16_t* q, const uint16_t* k, const uint16_t* v, c
   const L2Args l2{sst, lam, eta, g, H};
   if (d == 128)
     hipLaunchKernelGGL(swa_kernel<128>, dim3(grid), dim3(NTHR), 0, s, q, k, v, l2, T, W, n_tiles, n_items,
-                       sl2, y);
+                       sl2, y, lse2);
   else if (d == 64)
     hipLaunchKernelGGL(swa_kernel<64>, dim3(grid), dim3(NTHR), 0, s, q, k, v, l2, T, W, n_tiles, n_items,
-                       sl2, y);
+                       sl2, y, lse2);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -253,12 +253,17 @@ hipError_t dispatch_wbwd(const TIn* q, const TIn* k, const TIn* v, const float* 
 
 }  // namespace
 
-size_t window_bwd_ws_bytes(int B, int H, int T) { return (size_t)2 * B * H * T * sizeof(float); }
+size_t window_bwd_ws_bytes(int B, int H, int T, int d, bool bf16) {
+  if (window_bwd_mfma(bf16, d)) return window_bwd_mfma_ws_bytes(B, H, T, d);
+  return (size_t)2 * B * H * T * sizeof(float);
+}
 
 hipError_t launch_window_backward(const void* q, const void* k, const void* v, bool bf16, const float* dy, int B,
                                   int H, int T, int d, int W, float scale, void* ws, bool accumulate, float* dq,
                                   float* dk, float* dv, hipStream_t s) {
   if (B * H == 0 || T == 0) return hipSuccess;
+  if (window_bwd_mfma(bf16, d))  // bf16 MFMA kernels (tc_window_bwd_mfma.hip)
+    return launch_window_backward_mfma(q, k, v, dy, B, H, T, d, W, scale, ws, accumulate, dq, dk, dv, s);
   float* w = static_cast<float*>(ws);
   if (bf16)
     return dispatch_wbwd<uint16_t>(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),

@@ -23,6 +23,13 @@ TOL = {"f32": 1e-5, "bf16": 2e-2}
     ("f32", 1, 2, 130, 64, 1),
     ("bf16", 1, 2, 400, 128, 150),
     ("bf16", 2, 1, 257, 64, 64),
+    # bf16 with d in {64, 128} runs the MFMA kernels: ragged single tile, a
+    # window covering the sequence, several tiles of both kernels with B > 1,
+    # and the fused layer's window over many tiles
+    ("bf16", 1, 2, 70, 128, 2),
+    ("bf16", 1, 1, 200, 64, 300),
+    ("bf16", 2, 2, 700, 128, 256),
+    ("bf16", 1, 1, 3000, 128, 1024),
 ])
 def test_window_backward(dtype, B, H, T, d, W):
     print(f"[case] window backward {dtype} B={B} H={H} T={T} d={d} W={W}", flush=True)
