@@ -225,17 +225,12 @@ static tc_status check_scan_bwd(const char* fn, int B, int H, int T, int dk, int
 // d = 128: the read m = q A splits over halves of d_k and d_v into four
 // d = 64 reads m^(a,b) (q, k columns 64a.., v, dm columns 64b..), whose
 // gradients add: dq[:, a] and dk[:, a] sum over b, dv[:, b] over a, and the
-// per-head terms over all four.  Workspace: the widened copies (bf16), eight
-// contiguous half-width input pieces, three half-width outputs, three [H]
-// outputs, then the d = 64 backward's own workspace.
-static size_t half_bytes(int B, int H, int T) { return round_up_256((size_t)B * H * T * 64 * sizeof(float)); }
-static size_t scan_bwd128_bytes(int B, int H, int T, int W) {
-  return 11 * half_bytes(B, H, T) + round_up_256(3 * (size_t)H * sizeof(float)) +
-         tc::scan_bwd_ws_bytes(B, H, T, 64, W);
-}
-
+// per-head terms over all four.  The d = 64 kernels read the halves in place
+// (rows 128 floats apart) and add into the halves of the outputs, so the
+// workspace is the d = 64 backward's (plus the widened copies for bf16).
 static size_t scan_bwd_need(int B, int H, int T, int d, int W, tc_dtype dt) {
-  if (d == 128) return (dt == TC_BF16 ? 3 * widened_bytes(B, H, T, d) : 0) + scan_bwd128_bytes(B, H, T, W);
+  if (d == 128)
+    return (dt == TC_BF16 ? 3 * widened_bytes(B, H, T, d) : 0) + round_up_256(tc::scan_bwd_ws_bytes(B, H, T, 64, W));
   const size_t base = tc::scan_bwd_ws_bytes(B, H, T, d, W);
   return dt == TC_BF16 ? round_up_256(base) + 3 * widened_bytes(B, H, T, d) : base;
 }
@@ -243,30 +238,12 @@ static size_t scan_bwd_need(int B, int H, int T, int d, int W, tc_dtype dt) {
 static hipError_t scan_backward_128(const float* q, const float* k, const float* v, const float* lam, const float* eta,
                                     const float* g, int B, int H, int T, int W, const float* dm, float* dq, float* dk,
                                     float* dv, float* dlam, float* deta, float* dg, char* w, hipStream_t s) {
-  const long rows = (long)B * H * T;
-  const size_t hb = half_bytes(B, H, T);
-  float* piece[8];  // q0 q1 k0 k1 v0 v1 dm0 dm1
-  for (int i = 0; i < 8; ++i) piece[i] = reinterpret_cast<float*>(w + i * hb);
-  float* tq = reinterpret_cast<float*>(w + 8 * hb);
-  float* tk = reinterpret_cast<float*>(w + 9 * hb);
-  float* tv = reinterpret_cast<float*>(w + 10 * hb);
-  float* th = reinterpret_cast<float*>(w + 11 * hb);  // dlam, deta, dg of one piece
-  char* sub = w + 11 * hb + round_up_256(3 * (size_t)H * sizeof(float));
-  const float* src[4] = {q, k, v, dm};
   hipError_t e = hipSuccess;
-  for (int t = 0; t < 4 && e == hipSuccess; ++t)
-    for (int h = 0; h < 2 && e == hipSuccess; ++h) e = tc::launch_gather_cols(src[t], 128, 64 * h, 64, piece[2 * t + h], rows, s);
   for (int a = 0; a < 2 && e == hipSuccess; ++a) {
     for (int b = 0; b < 2 && e == hipSuccess; ++b) {
-      e = tc::launch_tc_scan_backward(piece[a], piece[2 + a], piece[4 + b], lam, eta, g, B, H, T, 64, W, piece[6 + b],
-                                      tq, tk, tv, th, th + H, g ? th + 2 * H : nullptr, sub, s);
-      if (e == hipSuccess) e = tc::launch_scatter_cols(tq, 64, dq, 128, 64 * a, rows, b != 0, s);
-      if (e == hipSuccess) e = tc::launch_scatter_cols(tk, 64, dk, 128, 64 * a, rows, b != 0, s);
-      if (e == hipSuccess) e = tc::launch_scatter_cols(tv, 64, dv, 128, 64 * b, rows, a != 0, s);
-      const bool first = a == 0 && b == 0;
-      if (e == hipSuccess) e = tc::launch_scatter_cols(th, H, dlam, H, 0, 1, !first, s);
-      if (e == hipSuccess) e = tc::launch_scatter_cols(th + H, H, deta, H, 0, 1, !first, s);
-      if (e == hipSuccess && g) e = tc::launch_scatter_cols(th + 2 * H, H, dg, H, 0, 1, !first, s);
+      const tc::ScanBwdPiece pc{128, b != 0, a != 0, a != 0 || b != 0};
+      e = tc::launch_tc_scan_backward(q + 64 * a, k + 64 * a, v + 64 * b, lam, eta, g, B, H, T, 64, W, dm + 64 * b,
+                                      dq + 64 * a, dk + 64 * a, dv + 64 * b, dlam, deta, dg, w, s, &pc);
     }
   }
   return e;
@@ -301,7 +278,7 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
     if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
     const float *q32 = static_cast<const float*>(q), *k32 = static_cast<const float*>(k),
                 *v32 = static_cast<const float*>(v);
-    // d = 128: the widened copies come first, then the pieces of scan_backward_128
+    // d = 128: the widened copies come first, then the d = 64 workspace of scan_backward_128
     const size_t wide_off = dk == 128 ? 0 : round_up_256(tc::scan_bwd_ws_bytes(B, H, T, dk, W));
     if (dt == TC_BF16 && T > 0) {
       char* wide = static_cast<char*>(ws) + wide_off;

@@ -1,6 +1,4 @@
-// tc_convert.hip — layout helpers of the backward passes: bf16 -> fp32
-// widening, and the column gathers and scatters that compose a d = 128
-// read backward from d = 64 pieces.
+// tc_convert.hip — bf16 -> fp32 widening for the backward passes.
 //
 // The backward passes run on fp32 kernels; bf16 inputs are widened first
 // into the caller's workspace.  Every bf16 value is exact in fp32, so the
@@ -33,43 +31,7 @@ __global__ __launch_bounds__(256) void widen_bf16_kernel(const uint16_t* __restr
     out[i] = bf16_to_f32(in[i]);
 }
 
-// dst[r][c] = src[r * ds + c0 + c] for c < w (one row of w floats per r)
-__global__ __launch_bounds__(256) void gather_cols_kernel(const float* __restrict__ src, int ds, int c0, int w,
-                                                          float* __restrict__ dst, long rows) {
-  const long n = rows * w, stride = (long)gridDim.x * blockDim.x;
-  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const long r = i / w;
-    dst[i] = src[r * ds + c0 + (i - r * w)];
-  }
-}
-
-// dst[r * dd + c0 + c] (+)= src[r][c] for c < w
-__global__ __launch_bounds__(256) void scatter_cols_kernel(const float* __restrict__ src, int w, float* __restrict__ dst,
-                                                           int dd, int c0, long rows, bool add) {
-  const long n = rows * w, stride = (long)gridDim.x * blockDim.x;
-  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const long r = i / w;
-    float* o = dst + r * dd + c0 + (i - r * w);
-    *o = add ? *o + src[i] : src[i];
-  }
-}
-
-unsigned grid_for(long n) { return (unsigned)std::min<long>((n + 255) / 256, 8192); }
-
 }  // namespace
-
-hipError_t launch_gather_cols(const float* src, int ds, int c0, int w, float* dst, long rows, hipStream_t s) {
-  if (rows * w <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_cols_kernel, dim3(grid_for(rows * w)), dim3(256), 0, s, src, ds, c0, w, dst, rows);
-  return hipGetLastError();
-}
-
-hipError_t launch_scatter_cols(const float* src, int w, float* dst, int dd, int c0, long rows, bool add,
-                               hipStream_t s) {
-  if (rows * w <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_cols_kernel, dim3(grid_for(rows * w)), dim3(256), 0, s, src, w, dst, dd, c0, rows, add);
-  return hipGetLastError();
-}
 
 hipError_t launch_widen_bf16(const void* in, float* out, long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

@@ -23,19 +23,23 @@ ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int W);
 size_t scan_ws_bytes(const ScanPlan& p, int B, int H, int dk, int dv);
 // Backward of the read (fp32 inputs, d = dk = dv in {16, 32, 64}).
 size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W);
+// One piece of a wider backward: the d columns of q, k, v, dm, dq, dk, dv
+// sit in rows rs floats apart (the pointers point at the piece's first
+// column); add_qk / add_v / add_h add dq and dk / dv / dlam, deta, dg to what
+// the buffers hold instead of writing them (and leave the rows that no
+// position writes alone).  nullptr: rows of d floats, everything written.
+struct ScanBwdPiece {
+  int rs;
+  bool add_qk, add_v, add_h;
+};
 hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
                                    const float* eta, const float* g, int B, int H, int T, int d, int W,
                                    const float* dm, float* dq, float* dk, float* dv, float* dlam,
-                                   float* deta, float* dg, void* ws, hipStream_t s);
+                                   float* deta, float* dg, void* ws, hipStream_t s,
+                                   const ScanBwdPiece* piece = nullptr);
 
 // bf16 -> fp32 of n elements (tc_convert.hip); any alignment, any n.
 hipError_t launch_widen_bf16(const void* in, float* out, long n, hipStream_t s);
-// Column pieces of row-major fp32 arrays (tc_convert.hip): gather
-// dst[r][c] = src[r * ds + c0 + c]; scatter dst[r * dd + c0 + c] (+)= src[r][c];
-// c < w, r < rows.
-hipError_t launch_gather_cols(const float* src, int ds, int c0, int w, float* dst, long rows, hipStream_t s);
-hipError_t launch_scatter_cols(const float* src, int w, float* dst, int dd, int c0, long rows, bool add,
-                               hipStream_t s);
 
 hipError_t launch_tc_scan(const void* q, const void* k, const void* v, bool bf16,
                           const float* lam, const float* eta, int B, int H, int T, int dk, int dv,

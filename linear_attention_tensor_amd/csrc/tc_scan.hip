@@ -624,19 +624,24 @@ __global__ void fill_kernel(float* __restrict__ p, int n, float x) {
   if (i < n) p[i] = x;
 }
 
-// dq rows t < W and dk, dv rows t >= T - W are 0 (nothing reads or writes them).
+// dq rows t < W and dk, dv rows t >= T - W are 0 (nothing reads or writes
+// them); rows are rs floats apart, of which the first D belong to the call;
+// a null output is left alone.
 __global__ void scan_bwd_zero_kernel(float* __restrict__ dq, float* __restrict__ dk,
-                                     float* __restrict__ dv, long T, int D, long zq, long n_act) {
+                                     float* __restrict__ dv, long T, int D, long zq, long n_act, long rs) {
   const long bh = blockIdx.y, n1 = zq * D, n2 = (T - n_act) * D;
-  const long base = bh * T * D;
+  const long base = bh * T * rs;
   for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < n1 + 2 * n2;
        i += (long)gridDim.x * blockDim.x) {
-    if (i < n1)
-      dq[base + i] = 0.f;
-    else if (i < n1 + n2)
-      dk[base + n_act * D + (i - n1)] = 0.f;
-    else
-      dv[base + n_act * D + (i - n1 - n2)] = 0.f;
+    if (i < n1) {
+      if (dq) dq[base + (i / D) * rs + i % D] = 0.f;
+    } else if (i < n1 + n2) {
+      const long j = i - n1;
+      if (dk) dk[base + (n_act + j / D) * rs + j % D] = 0.f;
+    } else {
+      const long j = i - n1 - n2;
+      if (dv) dv[base + (n_act + j / D) * rs + j % D] = 0.f;
+    }
   }
 }
 
@@ -717,7 +722,7 @@ __global__ __launch_bounds__(256) void scan_bwd_fwd_fast(
     RowView<const float> vq, RowView<const float> vk, RowView<const float> vv, RowView<const float> vg,
     const float* __restrict__ lam, const float* __restrict__ eta, int H, int n_act, int seg_chunks,
     int n_seg, const float* __restrict__ ws, const float* __restrict__ dws, const float* __restrict__ gate,
-    RowView<float> vdq, int zq, double* __restrict__ part_eta, double* __restrict__ part_lam) {
+    RowView<float> vdq, int zq, double* __restrict__ part_eta, double* __restrict__ part_lam, bool add_q) {
   using F = FastTiles<D>;
   constexpr int NT = D / 16;
   constexpr int ROWS = CH * F::S;  // one [64][D] array
@@ -758,7 +763,7 @@ __global__ __launch_bounds__(256) void scan_bwd_fwd_fast(
       fma_state_d<D>(acc, dacc, lf, dlf, ws + ((long)bh * n_seg + sp) * D * D,
                      dws + ((long)bh * n_seg + sp) * D * D, D);
   }
-  clear_rows_before<D>(vdq, bh, zq, seg, n_seg);  // row s of vdq is t = W + s
+  if (!add_q) clear_rows_before<D>(vdq, bh, zq, seg, n_seg);  // row s of vdq is t = W + s
   float4 xq[F::NV4], xk[F::NV4], xv[F::NV4], xg[F::NV4];
   if (c_begin < c_end) {
     const int s0 = c_begin * CH, L = min(CH, n_act - s0);
@@ -832,7 +837,10 @@ __global__ __launch_bounds__(256) void scan_bwd_fwd_fast(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int rr = 16 * w + 4 * g + e;
-        if (rr < L) vdq.row(bh, s0 + rr)[16 * t + r] = et * o[t][e];
+        if (rr < L) {
+          float* p = vdq.row(bh, s0 + rr) + 16 * t + r;
+          *p = add_q ? *p + et * o[t][e] : et * o[t][e];
+        }
       }
     // entering-state terms with E^T = G^T diag(w) Q' in the state's tile layout
     float st_eta = 0.f, st_lam = 0.f;
@@ -885,7 +893,7 @@ __global__ __launch_bounds__(256) void scan_bwd_rev_fast(
     RowView<const float> vv, RowView<const float> vk, RowView<const float> vq, RowView<const float> vg,
     const float* __restrict__ lam, const float* __restrict__ eta, int H, int n_act, int seg_chunks,
     int n_seg, const float* __restrict__ ws, const float* __restrict__ gate, RowView<float> vdk,
-    RowView<float> vdv, int ztail) {
+    RowView<float> vdv, int ztail, bool add_k, bool add_v) {
   using F = FastTiles<D>;
   constexpr int NT = D / 16;
   constexpr int ROWS = CH * F::S;
@@ -922,8 +930,8 @@ __global__ __launch_bounds__(256) void scan_bwd_rev_fast(
     const float lf = pow_int(lm, seg_chunks * CH);
     for (int sp = 0; sp < seg; ++sp) fma_state<D>(acc, lf, ws + ((long)bh * n_seg + sp) * D * D, D);
   }
-  clear_rows_before<D>(vdk, bh, ztail, seg, n_seg);
-  clear_rows_before<D>(vdv, bh, ztail, seg, n_seg);
+  if (!add_k) clear_rows_before<D>(vdk, bh, ztail, seg, n_seg);
+  if (!add_v) clear_rows_before<D>(vdv, bh, ztail, seg, n_seg);
   float4 xv[F::NV4], xk[F::NV4], xq[F::NV4], xg[F::NV4];
   if (c_begin < c_end) {
     const int s0 = c_begin * CH, L = min(CH, n_act - s0);
@@ -994,8 +1002,10 @@ __global__ __launch_bounds__(256) void scan_bwd_rev_fast(
       for (int e = 0; e < 4; ++e) {
         const int rr = 16 * w + 4 * g + e;
         if (rr < L) {
-          vdk.row(bh, s0 + rr)[16 * t + r] = et * ok[t][e];
-          vdv.row(bh, s0 + rr)[16 * t + r] = et * ov[t][e];
+          float* pk = vdk.row(bh, s0 + rr) + 16 * t + r;
+          float* pv = vdv.row(bh, s0 + rr) + 16 * t + r;
+          *pk = add_k ? *pk + et * ok[t][e] : et * ok[t][e];
+          *pv = add_v ? *pv + et * ov[t][e] : et * ov[t][e];
         }
       }
     fast_state_update<D>(acc, sQw, sGt, sPow[L]);
@@ -1009,7 +1019,7 @@ __global__ __launch_bounds__(256) void scan_bwd_rev_fast(
 __global__ void scan_bwd_reduce(const double* __restrict__ part_eta, const double* __restrict__ part_lam,
                                 const float* __restrict__ eta, const float* __restrict__ gate, int B, int H,
                                 int n_seg, float* __restrict__ dlam, float* __restrict__ deta,
-                                float* __restrict__ dgate) {
+                                float* __restrict__ dgate, bool add) {
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= H) return;
   double a = 0.0, b = 0.0;
@@ -1021,57 +1031,65 @@ __global__ void scan_bwd_reduce(const double* __restrict__ part_eta, const doubl
     }
   }
   const double s = gate != nullptr ? 1.0 / (1.0 + exp(-(double)gate[h])) : 1.0;
-  deta[h] = (float)(s * a);
-  dlam[h] = (float)(s * (double)eta[h] * b);
-  if (dgate != nullptr) dgate[h] = (float)(s * (1.0 - s) * (double)eta[h] * a);
+  const float de = (float)(s * a), dl = (float)(s * (double)eta[h] * b);
+  deta[h] = add ? deta[h] + de : de;
+  dlam[h] = add ? dlam[h] + dl : dl;
+  if (dgate != nullptr) {
+    const float dg = (float)(s * (1.0 - s) * (double)eta[h] * a);
+    dgate[h] = add ? dgate[h] + dg : dg;
+  }
 }
 
 template <int D>
 hipError_t run_scan_backward(const float* q, const float* k, const float* v, const float* lam,
                              const float* eta, const float* gate, int B, int H, int T, int W, const float* dm,
                              float* dq, float* dk, float* dv, float* dlam, float* deta, float* dgate,
-                             char* ws, hipStream_t s) {
+                             char* ws, hipStream_t s, const ScanBwdPiece& pc) {
   const int BH = B * H;
   const ScanPlan p = plan_scan(B, H, T, D, D, W);
   const int n_act = p.n_act;
   const long zq = std::min<long>(W, T);
+  const long rs = pc.rs;
   if (n_act <= 0) {  // (otherwise the two direction kernels clear these rows)
-    hipLaunchKernelGGL(scan_bwd_zero_kernel, dim3(kZeroBlocks, BH), dim3(256), 0, s, dq, dk, dv, (long)T, D,
-                       zq, 0L);
-    hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dlam, H, 0.f);
-    hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, deta, H, 0.f);
-    if (dgate != nullptr)
-      hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dgate, H, 0.f);
+    if (!pc.add_qk || !pc.add_v)
+      hipLaunchKernelGGL(scan_bwd_zero_kernel, dim3(kZeroBlocks, BH), dim3(256), 0, s, pc.add_qk ? nullptr : dq,
+                         pc.add_qk ? nullptr : dk, pc.add_v ? nullptr : dv, (long)T, D, zq, 0L, rs);
+    if (!pc.add_h) {
+      hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dlam, H, 0.f);
+      hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, deta, H, 0.f);
+      if (dgate != nullptr)
+        hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dgate, H, 0.f);
+    }
     return hipGetLastError();
   }
   double* part_eta = reinterpret_cast<double*>(ws);
   double* part_lam = part_eta + (long)BH * p.n_seg;
   float* sws = reinterpret_cast<float*>(ws + scan_bwd_part_bytes(B, H, p.n_seg));
   float* dws = reinterpret_cast<float*>(ws + scan_bwd_part_bytes(B, H, p.n_seg) + scan_ws_bytes(p, B, H, D, D));
-  const long bs = (long)T * D;
+  const long bs = (long)T * rs;
   // forward direction: dq, deta, dlam
-  const RowView<const float> fq{q + (long)W * D, bs, D}, fk{k, bs, D}, fv{v, bs, D},
-      fg{dm + (long)W * D, bs, D};
+  const RowView<const float> fq{q + (long)W * rs, bs, rs}, fk{k, bs, rs}, fv{v, bs, rs},
+      fg{dm + (long)W * rs, bs, rs};
   if (p.n_seg > 1)
     hipLaunchKernelGGL((scan_dstate_fast<D>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, fk, fv, lam, H,
                        n_act, p.seg_chunks, p.n_seg, sws, dws);
   profile_mark_before(s);
   hipLaunchKernelGGL((scan_bwd_fwd_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, fq, fk, fv, fg, lam,
                      eta, H, n_act, p.seg_chunks, p.n_seg, sws, dws, gate,
-                     RowView<float>{dq + (long)W * D, bs, D}, (int)zq, part_eta, part_lam);
+                     RowView<float>{dq + (long)W * rs, bs, rs}, (int)zq, part_eta, part_lam, pc.add_qk);
   profile_mark_after(s);
   // reverse direction: dk, dv (row r of each view is position n_act - 1 - r)
-  const long last = (long)(n_act - 1) * D, tl = (long)(T - 1) * D;
-  const RowView<const float> rv{v + last, bs, -D}, rk{k + last, bs, -D}, rq{q + tl, bs, -D},
-      rg{dm + tl, bs, -D};
+  const long last = (long)(n_act - 1) * rs, tl = (long)(T - 1) * rs;
+  const RowView<const float> rv{v + last, bs, -rs}, rk{k + last, bs, -rs}, rq{q + tl, bs, -rs},
+      rg{dm + tl, bs, -rs};
   if (p.n_seg > 1)
     hipLaunchKernelGGL((scan_state_fast<D, float>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, rg, rq, lam,
                        nullptr, H, n_act, p.seg_chunks, p.n_seg, sws);
   hipLaunchKernelGGL((scan_bwd_rev_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, rv, rk, rq, rg, lam, eta,
-                     H, n_act, p.seg_chunks, p.n_seg, sws, gate, RowView<float>{dk + last, bs, -D},
-                     RowView<float>{dv + last, bs, -D}, T - n_act);
+                     H, n_act, p.seg_chunks, p.n_seg, sws, gate, RowView<float>{dk + last, bs, -rs},
+                     RowView<float>{dv + last, bs, -rs}, T - n_act, pc.add_qk, pc.add_v);
   hipLaunchKernelGGL(scan_bwd_reduce, dim3((H + 63) / 64), dim3(64), 0, s, part_eta, part_lam, eta, gate, B,
-                     H, p.n_seg, dlam, deta, dgate);
+                     H, p.n_seg, dlam, deta, dgate, pc.add_h);
   return hipGetLastError();
 }
 
@@ -1190,12 +1208,13 @@ size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W) {
 hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
                                    const float* eta, const float* g, int B, int H, int T, int d, int W,
                                    const float* dm, float* dq, float* dk, float* dv, float* dlam,
-                                   float* deta, float* dg, void* ws, hipStream_t s) {
+                                   float* deta, float* dg, void* ws, hipStream_t s, const ScanBwdPiece* piece) {
   char* w = static_cast<char*>(ws);
+  const ScanBwdPiece pc = piece ? *piece : ScanBwdPiece{d, false, false, false};
   switch (d) {
-    case 16: return run_scan_backward<16>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s);
-    case 32: return run_scan_backward<32>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s);
-    case 64: return run_scan_backward<64>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s);
+    case 16: return run_scan_backward<16>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc);
+    case 32: return run_scan_backward<32>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc);
+    case 64: return run_scan_backward<64>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc);
     default: return hipErrorInvalidValue;
   }
 }

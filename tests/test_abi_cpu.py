@@ -149,7 +149,7 @@ def test_backward_entry_points_reject():
     bad = list(base); bad[11] = NULL
     assert f(*bad) == _lib.TC_ERR_INVALID_ARG
     fq = L.tc_fused_layer_backward_workspace_bytes
-    assert 0 < fq(1, 2, 100, 128, 128, 16, 64, _lib.TC_BF16) < _lib.SIZE_MAX  # d = 128: four d = 64 pieces
+    assert 0 < fq(1, 2, 100, 128, 128, 16, 64, _lib.TC_BF16) < _lib.SIZE_MAX  # d = 128: four d = 64 pieces in place
     assert fq(1, 2, 100, 48, 48, 16, 64, _lib.TC_BF16) == _lib.SIZE_MAX
     assert 0 < fq(1, 2, 100, 64, 64, 16, 64, _lib.TC_BF16) < _lib.SIZE_MAX
     g = L.tc_fused_layer_backward
@@ -260,7 +260,8 @@ def test_scan_backward_rejects():
     need16 = lib().tc_scan_backward_workspace_bytes(4, 8, 4096, 64, 64, 512, 64, _lib.TC_BF16)
     assert need16 >= need + 3 * 4 * 8 * 4096 * 64 * 4
     assert call(dt=_lib.TC_BF16) == _lib.TC_ERR_WORKSPACE
-    assert call(d=128) == _lib.TC_ERR_WORKSPACE  # d = 128 needs room for its four d = 64 pieces
+    need128 = lib().tc_scan_backward_workspace_bytes(4, 8, 4096, 128, 128, 512, 64, _lib.TC_F32)
+    assert call(d=128, ws_bytes=need128 - 1) == _lib.TC_ERR_WORKSPACE
     assert call(d=48) == _lib.TC_ERR_UNSUPPORTED
     assert call(W=0) == _lib.TC_ERR_INVALID_ARG
     assert call(chunk=128) == _lib.TC_ERR_UNSUPPORTED
@@ -271,10 +272,13 @@ def test_scan_backward_rejects():
     assert call(g=FAKE) == _lib.TC_ERR_INVALID_ARG  # a gate without dg
     assert call(dg=FAKE) == _lib.TC_ERR_INVALID_ARG
     assert call(B=0) == _lib.TC_OK
-    # d = 128: eight gathered half-width inputs and three half-width outputs on top of the d = 64 workspace
+    # d = 128 runs four d = 64 pieces in place: the d = 64 workspace (rounded to 256 bytes); bf16 adds the
+    # three widened copies
     w128 = lib().tc_scan_backward_workspace_bytes(1, 1, 10, 128, 128, 4, 64, _lib.TC_F32)
     w64 = lib().tc_scan_backward_workspace_bytes(1, 1, 10, 64, 64, 4, 64, _lib.TC_F32)
-    assert w64 + 11 * 10 * 64 * 4 <= w128 < _lib.SIZE_MAX
+    assert w64 <= w128 == (w64 + 255) // 256 * 256
+    w128b = lib().tc_scan_backward_workspace_bytes(1, 1, 10, 128, 128, 4, 64, _lib.TC_BF16)
+    assert w128b == w128 + 3 * ((10 * 128 * 4 + 255) // 256 * 256)
 
 
 def test_memory_entry_points_reject():
