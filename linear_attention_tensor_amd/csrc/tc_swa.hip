@@ -71,12 +71,14 @@ template <int D>
 struct DmaOff {
   int k[Dma<D>::NK];
   int v[Dma<D>::NV];
+  int w512;  // this wave's first 1 KiB piece of a stage (in elements)
 };
 
 template <int D>
 __device__ __forceinline__ DmaOff<D> dma_offsets() {
   DmaOff<D> o;
   const int w = wave_id(), l = lane_id();
+  o.w512 = w * 512;
 #pragma unroll
   for (int i = 0; i < Dma<D>::NK; ++i) {
     int m, c;
@@ -97,11 +99,10 @@ __device__ __forceinline__ DmaOff<D> dma_offsets() {
 template <int D>
 __device__ __forceinline__ void dma_block(i32x4 dk, i32x4 dv, const DmaOff<D>& off, int j,
                                           uint16_t* sk, uint16_t* sv) {
-  const int w = wave_id();
 #pragma unroll
-  for (int i = 0; i < Dma<D>::NK; ++i) dma16(dk, sk + (i * NWAVE + w) * 512, off.k[i] + j * D * 2);
+  for (int i = 0; i < Dma<D>::NK; ++i) dma16(dk, sk + i * NWAVE * 512 + off.w512, off.k[i] + j * D * 2);
 #pragma unroll
-  for (int i = 0; i < Dma<D>::NV; ++i) dma16(dv, sv + (i * NWAVE + w) * 512, off.v[i] + j * D * 2);
+  for (int i = 0; i < Dma<D>::NV; ++i) dma16(dv, sv + i * NWAVE * 512 + off.w512, off.v[i] + j * D * 2);
 }
 
 // DMA of the tile's entering state (bf16, [dv][dk] row-major in global) into
@@ -133,12 +134,15 @@ struct DmaJob {
 template <int D, int I>
 __device__ __forceinline__ void dma_part(const DmaJob<D>& job, const DmaOff<D>& off) {
   if (!job.on) return;
-  const int w = wave_id();
   if constexpr (I < Dma<D>::NK)
-    dma16(job.dk, job.sk + (I * NWAVE + w) * 512, off.k[I] + job.off);
+    dma16(job.dk, job.sk + I * NWAVE * 512 + off.w512, off.k[I] + job.off);
   else
-    dma16(job.dv, job.sv + ((I - Dma<D>::NK) * NWAVE + w) * 512, off.v[I - Dma<D>::NK] + job.off);
+    dma16(job.dv, job.sv + (I - Dma<D>::NK) * NWAVE * 512 + off.w512, off.v[I - Dma<D>::NK] + job.off);
 }
+
+// floor(a / b) and ceil(a / b) for b > 0 and any sign of a
+__device__ __forceinline__ int floordiv(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+__device__ __forceinline__ int ceildiv(int a, int b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); }
 
 // max / sum over the two 32-lane halves (the two halves of a query's keys)
 __device__ __forceinline__ float max_halves(float x) {
@@ -500,7 +504,11 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
     // block b + 4 of tile p, so neighbouring tiles (which run at the same time
     // on one XCD) read the same keys at the same step, out of its L2.
     const int nw = nb - 4, rot = (MQ / KB * tile) % nw;
-    auto block_at = [nw, rot](int idx) { return idx < nw ? 4 + (idx + nw - rot) % nw : idx - nw; };
+    auto block_at = [nw, rot](int idx) {
+      if (idx >= nw) return idx - nw;
+      const int x = idx + nw - rot;  // in [1, 2 nw): (idx - rot) mod nw without a division
+      return 4 + (x >= nw ? x - nw : x);
+    };
 
     bf16x8 qreg[NKS];
 #pragma unroll
@@ -524,6 +532,18 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
     qk_block<D>(reinterpret_cast<const char*>(lds.k[0]), ls, qreg, s0[0], s0[1]);
     if (has_l2) dma_state<D>(raw_desc(l2.sst + ((long)bh * n_tiles + tile) * D * D, D * D * 2), lds.st);
 
+    // The blocks b (keys j0 + 64 b ..) that some query of this wave sees
+    // (active) and the ones that every query of the wave sees whole (full,
+    // no masking) are two ranges of b:
+    //   active: 64 b + 63 > r_lo, 64 b <= r_hi + W, j0 + 64 b + 63 >= 0, j0 + 64 b < T;
+    //   full:   64 b > r_hi, 64 b + 63 <= r_lo + W, j0 + 64 b >= 0, j0 + 64 b + 63 < T.
+    int a_lo = max(max(0, ceildiv(r_lo - KB + 2, KB)), ceildiv(-j0 - KB + 1, KB));
+    int a_hi = min(min(nb - 1, floordiv(r_hi + W, KB)), floordiv(T - j0 - 1, KB));
+    if (tw >= T) a_lo = nb;
+    int f_lo = max(max(0, floordiv(r_hi, KB) + 1), ceildiv(-j0, KB));
+    const int f_hi = min(min(nb - 1, floordiv(r_lo + W - KB + 1, KB)), floordiv(T - KB - j0, KB));
+    if (tw + 31 >= T) f_lo = nb;
+
     // One step per block position; the scores alternate between s0 and s1.
     auto step = [&](int idx, floatx16* sc, floatx16* sn) __attribute__((always_inline)) {
       // block idx + 1 must have landed: its scores are formed in this step.
@@ -541,23 +561,22 @@ __global__ __launch_bounds__(NTHR) void swa_kernel(const uint16_t* __restrict__ 
         job = DmaJob<D>{rk, rv, jn * D * 2, lds.k[st], lds.v[st], idx + NSTAGE - 1 < nb};
       }
       const int b = block_at(idx);
-      const int c_lo = KB * b, jb = j0 + c_lo;
       // (bitwise &: the flags are formed without branches)
-      const bool active = (idx < nb) & (tw < T) & (c_lo + KB - 1 > r_lo) & (c_lo <= r_hi + W) &
-                          (jb + KB - 1 >= 0) & (jb < T);
-      const bool full = (c_lo > r_hi) & (c_lo + KB - 1 <= r_lo + W) & (jb >= 0) & (jb + KB - 1 < T) &
-                        (tw + 31 < T);
-      // keys c_lo + key valid for query r: r < c <= r + W and 0 <= j < T
-      const int r = r_lo + col;
-      int lo = max(r + 1 - c_lo, -jb);
-      const int hi = min(r + W - c_lo, T - 1 - jb);
-      KeyRange kr;
-      kr.span = static_cast<unsigned>(hi - lo);
-      if (hi < lo) {
-        lo = 1 << 20;  // no key matches
-        kr.span = 0;
+      const bool active = (idx < nb) & (b >= a_lo) & (b <= a_hi);
+      const bool full = (b >= f_lo) & (b <= f_hi);
+      KeyRange kr{0, 0u};
+      if (!full) {
+        // keys c_lo + key valid for query r: r < c <= r + W and 0 <= j < T
+        const int c_lo = KB * b, jb = j0 + c_lo, r = r_lo + col;
+        int lo = max(r + 1 - c_lo, -jb);
+        const int hi = min(r + W - c_lo, T - 1 - jb);
+        kr.span = static_cast<unsigned>(hi - lo);
+        if (hi < lo) {
+          lo = 1 << 20;  // no key matches
+          kr.span = 0;
+        }
+        kr.lo = lo - 8 * hh;
       }
-      kr.lo = lo - 8 * hh;
       swa_step<D>(reinterpret_cast<const char*>(lds.k[(idx + 1) & (NSTAGE - 1)]),
                   reinterpret_cast<const char*>(lds.v[idx & (NSTAGE - 1)]), ls, vls, qreg, sc, sn, o, sm,
                   sl2, active, !full, kr, job, doff);
