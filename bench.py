@@ -122,9 +122,9 @@ def delta_flops(B, H, T, d):
     return B * H * T * 6 * d * d  # prediction, write, read per token
 
 
-def delta_backward_bytes(B, H, T, d):
-    # read q, k, v, do, beta and write dq, dk, dv, dbeta once, fp32
-    return B * H * T * (7 * d * 4 + 8)
+def delta_backward_bytes(B, H, T, d, in_bytes=4):
+    # read q, k, v (input dtype), do, beta and write dq, dk, dv, dbeta once (fp32)
+    return B * H * T * (3 * d * in_bytes + 4 * d * 4 + 8)
 
 
 def delta_backward_flops(B, H, T, d):
@@ -737,24 +737,28 @@ def bench_delta_f32(steps, warmup, dev):
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "f32"}}
 
 
-def bench_delta_backward(steps, warmup, dev):
+def bench_delta_backward(steps, warmup, dev, workload="delta_backward_f32", bf16=False):
+    """delta_scan_backward: fp32 inputs at d = 64, or the delta-rule workload
+    itself (bf16 inputs, d = 128; the state rows in pieces of 16)."""
     import torch
 
     from linear_attention_tensor_amd import inputs as I
     from linear_attention_tensor_amd import ops
 
-    w = I.WORKLOADS["delta_backward_f32"]
+    w = I.WORKLOADS[workload]
     x = I.draw_workload(w.name)
-    q, k, v = (to_dev_f32(x[n], dev) for n in ("q", "k", "v"))
+    conv = to_dev_bf16 if bf16 else to_dev_f32
+    q, k, v = (conv(x[n], dev) for n in ("q", "k", "v"))
     beta = to_dev_f32(x["beta"], dev)
     do = to_dev_f32(I.draw_cotangent(w.B, w.H, w.T, w.d, seed=w.seed), dev)
     shape = (w.B, w.H, w.T, w.d)
     gq, gk, gv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
     gb = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
     lib = ops.lib()
-    nb = lib.delta_scan_backward_workspace_bytes(w.B, w.H, w.T, w.d, w.d, 64, 0)
+    dt = 1 if bf16 else 0
+    nb = lib.delta_scan_backward_workspace_bytes(w.B, w.H, w.T, w.d, w.d, 64, dt)
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
-    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, ops._ptr(beta), w.B, w.H, w.T, w.d, w.d, 64, None,
+    args = (ops._ptr(q), ops._ptr(k), ops._ptr(v), dt, ops._ptr(beta), w.B, w.H, w.T, w.d, w.d, 64, None,
             ops._ptr(do), None, ops._ptr(gq), ops._ptr(gk), ops._ptr(gv), ops._ptr(gb), None, ops._ptr(ws),
             ws.numel(), ops._stream())
 
@@ -763,14 +767,16 @@ def bench_delta_backward(steps, warmup, dev):
             raise RuntimeError(ops._lib.last_error())
 
     ms, ms_call, kernel_ms = time_calls(call, steps, warmup, KernelTimer(steps))
-    gbs = delta_backward_bytes(w.B, w.H, w.T, w.d) / (ms_call * 1e-3) / 1e9
+    gbs = delta_backward_bytes(w.B, w.H, w.T, w.d, 2 if bf16 else 4) / (ms_call * 1e-3) / 1e9
     tf = delta_backward_flops(w.B, w.H, w.T, w.d) / (ms_call * 1e-3) / 1e12
-    return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+    kernel = "delta_bwd_grads_pieces" if w.d == 128 else f"delta_bwd_grads<{w.d}>"
+    return {"workload": f"{w.name} backward" if bf16 else w.name, "ms_per_step": ms,
+            "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
             "mfma": roofline("mfma", tf, PEAK_FP32_TFLOPS, "TFLOP/s"),
-            "main_kernel": {"name": "delta_bwd_grads<64>", "ms": kernel_ms}, "ms_per_call": ms_call,
+            "main_kernel": {"name": kernel, "ms": kernel_ms}, "ms_per_call": ms_call,
             "workspace_bytes": nb,
-            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "f32"}}
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "dtype_in": "bf16" if bf16 else "f32"}}
 
 
 def bench_hebbian(steps, warmup, dev):
@@ -904,6 +910,7 @@ def main():
         components["delta_scan_bf16"] = bench_delta(args.steps, args.warmup, dev)
         components["delta_scan_f32"] = bench_delta_f32(args.steps, args.warmup, dev)
         components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
+        components["delta_backward_bf16"] = bench_delta_backward(args.steps, args.warmup, dev, "delta_scan_bf16", True)
         components["hebbian_f32"] = bench_hebbian(args.steps, args.warmup, dev)
         components["capacity_diagnostic"] = bench_capacity(dev)
     elif only == "scan":
@@ -927,6 +934,7 @@ def main():
         components["delta_scan_f32"] = bench_delta_f32(args.steps, args.warmup, dev)
     elif only == "delta_backward":
         components["delta_backward_f32"] = bench_delta_backward(args.steps, args.warmup, dev)
+        components["delta_backward_bf16"] = bench_delta_backward(args.steps, args.warmup, dev, "delta_scan_bf16", True)
     elif only == "hebbian":
         components["hebbian_f32"] = bench_hebbian(args.steps, args.warmup, dev)
     elif only == "capacity":

@@ -292,9 +292,12 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
  *            four state-independent products of every chunk, its entering
  *            state and its exit adjoint (B*H*ceil(T/64)*(2*64*64 + 2*64*d
  *            + 2*d*d) floats), and with bf16 inputs fp32 copies of q, k, v.
- * Supported: dk == dv in {16, 32, 64}, chunk = 64; anything else is
- * TC_ERR_UNSUPPORTED.  bf16 inputs are widened to fp32 copies inside the
- * workspace first (exact); the workspace query includes the copies.
+ * Supported: dk == dv in {16, 32, 64, 128}, chunk = 64; anything else is
+ * TC_ERR_UNSUPPORTED.  At 128 the rows of the state (the dv index, on which
+ * every gradient term is a sum of per-row products) are taken 16 at a time
+ * inside each chunk's gradient workgroup.  bf16 inputs are widened to fp32
+ * copies inside the workspace first (exact); the workspace query includes
+ * the copies.
  * ------------------------------------------------------------------------- */
 size_t delta_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt);
 tc_status delta_scan_backward(const void* q, const void* k, const void* v, tc_dtype dt,

@@ -1,5 +1,5 @@
 // delta_bwd.hip — backward of the chunked delta-rule scan (gfx950), fp32
-// inputs, d_k = d_v = D in {16, 32, 64}.
+// inputs, d_k = d_v = D in {16, 32, 64, 128}.
 //
 // "DeltaNet-family linear attention variants", DeltaNet section: the write
 // S_t = S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T with the learned write
@@ -28,7 +28,11 @@
 //      (2 and 3 are one launch, delta_bwd_walks);
 //   4. delta_bwd_grads  (chunks in parallel): dq, dk, dv, dbeta.
 // The rows of S (and of dS) are independent in 2 and 3: row j of S only sees
-// column j of V and U, row j of dS only column j of dO and dU.
+// column j of V and U, row j of dS only column j of dO and dU.  For the same
+// reason every term of 4 is a sum over the rows of S (the d_v index) of
+// products that involve one row each (dO S0, U dS1, dX S0, dO U^T, dY U^T,
+// <dY_r, X_r>), so at D = 128 the gradient kernel walks the d_v rows in
+// pieces of 16 and adds the pieces' terms, which keeps its LDS within a CU.
 // Products use fp32 MFMA (v_mfma_f32_16x16x4_f32) on LDS tiles.
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
@@ -338,12 +342,12 @@ __device__ __forceinline__ void delta_bwd_fwd(const float* __restrict__ k, const
       for (int i = 0; i < 4; ++i) sU[(16 * w + rq + i) * SV + col] = u[i] - g[i];
     }
     __syncthreads();
-    if (w < D / 16) {  // S += U^T K, tile (rows j0.., columns 16w..)
-      float* base = sS + rq * S + 16 * w + col;
+    for (int t = w; t < D / 16; t += 4) {  // S += U^T K, tile (rows j0.., columns 16t..)
+      float* base = sS + rq * S + 16 * t + col;
       floatx4 acc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = base[i * S];
-      acc = wmma_k4<CH>(sU, 1, SV, sK + 16 * w, S, 1, acc);
+      acc = wmma_k4<CH>(sU, 1, SV, sK + 16 * t, S, 1, acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) base[i * S] = acc[i];
     }
@@ -410,13 +414,13 @@ __device__ __forceinline__ void delta_bwd_rev(const float* __restrict__ q, const
       }
     }
     __syncthreads();
-    if (w < D / 16) {  // dS += dO^T Q - dX^T K, tile (rows j0.., columns 16w..)
-      float* base = sD + rq * S + 16 * w + col;
+    for (int t = w; t < D / 16; t += 4) {  // dS += dO^T Q - dX^T K, tile (rows j0.., columns 16t..)
+      float* base = sD + rq * S + 16 * t + col;
       floatx4 acc, neg = zero4();
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = base[i * S];
-      acc = wmma_k4<CH>(sO, 1, SV, sQ + 16 * w, S, 1, acc);
-      neg = wmma_k4<CH>(sX, 1, SV, sK + 16 * w, S, 1, neg);
+      acc = wmma_k4<CH>(sO, 1, SV, sQ + 16 * t, S, 1, acc);
+      neg = wmma_k4<CH>(sX, 1, SV, sK + 16 * t, S, 1, neg);
 #pragma unroll
       for (int i = 0; i < 4; ++i) base[i * S] = acc[i] - neg[i];
     }
@@ -443,6 +447,22 @@ __global__ __launch_bounds__(256) void delta_bwd_walks(const float* __restrict__
     delta_bwd_fwd<D>(k, v, T, n_chunks, S0, pre, Sc);
   else
     delta_bwd_rev<D>(q, k, dO, beta, T, n_chunks, dSf, pre, dSc, dS0);
+}
+
+// ... as two launches where their LDS together would not fit a CU (D = 128)
+template <int D>
+__global__ __launch_bounds__(256) void delta_bwd_fwd_walk(const float* __restrict__ k, const float* __restrict__ v,
+                                                          int T, int n_chunks, const float* __restrict__ S0,
+                                                          const float* __restrict__ pre, float* __restrict__ Sc) {
+  delta_bwd_fwd<D>(k, v, T, n_chunks, S0, pre, Sc);
+}
+template <int D>
+__global__ __launch_bounds__(256) void delta_bwd_rev_walk(const float* __restrict__ q, const float* __restrict__ k,
+                                                          const float* __restrict__ dO, const float* __restrict__ beta,
+                                                          int T, int n_chunks, const float* __restrict__ dSf,
+                                                          const float* __restrict__ pre, float* __restrict__ dSc,
+                                                          float* __restrict__ dS0) {
+  delta_bwd_rev<D>(q, k, dO, beta, T, n_chunks, dSf, pre, dSc, dS0);
 }
 
 // 4. Gradients of one chunk from its S0, dS1 and prep block.  Wave w owns
@@ -601,6 +621,156 @@ __global__ __launch_bounds__(256) void delta_bwd_grads(
   }
 }
 
+// 4 at D = 128: the gradients of one chunk with the d_v rows taken in pieces
+// of 16 (piece p: rows 16p.. of S0 and dS1, columns 16p.. of V, dO, dV).
+// Per piece, with wave w owning the chunk's tokens 16w..16w+15:
+//   X_p = V_p - K S0_p^T,  dY_p = E1 dS1_p^T + E2 dO_p,  dV_p = diag(beta) dY_p,
+//   U_p = Tm X_p,
+// and the sums over the pieces, kept in registers:
+//   P1 += dO_p U_p^T,  P2 += dY_p U_p^T,  <dY_r, X_r>,
+//   dQ += dO_p S0_p,   dK += U_p dS1_p - diag(beta) dY_p S0_p.
+// Then, as in delta_bwd_grads, P1 = tril_0(P1), P2 = tril_-1(P2), dLk =
+// -diag(beta) P2, dQ += P1 K, dK += P1^T Q + dLk K + dLk^T K and
+// dbeta_r = <dY_r, X_r> - sum_{c<r} P2[r][c] <k_r, k_c>.
+__global__ __launch_bounds__(256) void delta_bwd_grads_pieces(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ dO, const float* __restrict__ beta, int T, int n_chunks,
+    const float* __restrict__ pre, const float* __restrict__ Sc, const float* __restrict__ dSc,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dbeta) {
+  constexpr int D = 128, PV = 16;          // d, rows of a piece
+  constexpr int S = DB<D>::S, SV = PV + 4;
+  constexpr int NT = D / 16;
+  using P = Pre<D>;
+  __shared__ __attribute__((aligned(16))) float bK[CH * S];
+  __shared__ __attribute__((aligned(16))) float bE1[CH * S];  // E1, then Q
+  __shared__ __attribute__((aligned(16))) float bT[CH * SW];  // Tm, then P1
+  __shared__ __attribute__((aligned(16))) float bE[CH * SW];  // E2, then dLk
+  __shared__ __attribute__((aligned(16))) float bS0[PV * S];  // S0 rows of the piece
+  __shared__ __attribute__((aligned(16))) float bS1[PV * S];  // dS1 rows of the piece
+  __shared__ __attribute__((aligned(16))) float bX[CH * SV];  // V, then X
+  __shared__ __attribute__((aligned(16))) float bO[CH * SV];  // dO
+  __shared__ __attribute__((aligned(16))) float bU[CH * SV];
+  __shared__ __attribute__((aligned(16))) float bY[CH * SV];  // dY
+  __shared__ float sB[CH];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int t0 = c * CH, L = min(CH, T - t0);
+  const int w = wave_id(), l = lane_id(), col = l & 15, rq = (l >> 4) * 4;
+  const long cs = ((long)bh * n_chunks + c) * D * D;  // this chunk's state block
+  const long row0 = (long)bh * T + t0;
+  const float* pc = pre + ((long)bh * n_chunks + c) * P::SIZE;
+
+  stage<D>(bK, S, k + row0 * D, D, 0, L);
+  stage<D>(bE1, S, pc + P::E1, D, 0, CH);
+  stage<CH>(bT, SW, pc + P::TM, CH, 0, CH);
+  stage<CH>(bE, SW, pc + P::E2, CH, 0, CH);
+  if (threadIdx.x < CH) sB[threadIdx.x] = (int)threadIdx.x < L ? beta[row0 + threadIdx.x] : 0.f;
+
+  floatx4 aq[NT], ak[NT], p1[4], p2[4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) aq[t] = ak[t] = zero4();
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) p1[ct] = p2[ct] = zero4();
+  float db1[4] = {0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 1
+  for (int pp = 0; pp < D / PV; ++pp) {
+    const int j0 = PV * pp;
+    // the previous piece's reads of bS0, bS1, bX, bO, bU, bY are complete
+    __syncthreads();
+    for (int i = threadIdx.x; i < PV * D / 4; i += blockDim.x) {
+      const int r = i / (D / 4), cc = 4 * (i % (D / 4));
+      *reinterpret_cast<float4*>(bS0 + r * S + cc) =
+          *reinterpret_cast<const float4*>(Sc + cs + (long)(j0 + r) * D + cc);
+      *reinterpret_cast<float4*>(bS1 + r * S + cc) =
+          *reinterpret_cast<const float4*>(dSc + cs + (long)(j0 + r) * D + cc);
+    }
+    stage<PV>(bX, SV, v + row0 * D, D, j0, L);
+    stage<PV>(bO, SV, dO + row0 * D, D, j0, L);
+    __syncthreads();
+    // X_p = V_p - K S0_p^T and dY_p = E1 dS1_p^T + E2 dO_p, rows 16w..
+    {
+      const floatx4 ks = wmma_k4<D>(bK + 16 * w * S, S, 1, bS0, 1, S, zero4());
+      floatx4 y = wmma_k4<D>(bE1 + 16 * w * S, S, 1, bS1, 1, S, zero4());
+      y = wmma_k4<CH>(bE + 16 * w * SW, SW, 1, bO, SV, 1, y);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + rq + i;
+        const float x = bX[r * SV + col] - ks[i];
+        bX[r * SV + col] = x;
+        bY[r * SV + col] = y[i];
+        db1[i] += x * y[i];
+        if (r < L) dv[(row0 + r) * D + j0 + col] = sB[r] * y[i];
+      }
+    }
+    __syncthreads();
+    {  // U_p = Tm X_p, rows 16w..
+      const floatx4 u = wmma_k4<CH>(bT + 16 * w * SW, SW, 1, bX, SV, 1, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bU[(16 * w + rq + i) * SV + col] = u[i];
+    }
+    __syncthreads();
+    // sums over the pieces: P1, P2 (columns 16ct..), dQ, dK (columns 16t..)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      p1[ct] = wmma_k4<PV>(bO + 16 * w * SV, SV, 1, bU + 16 * ct * SV, 1, SV, p1[ct]);
+      p2[ct] = wmma_k4<PV>(bY + 16 * w * SV, SV, 1, bU + 16 * ct * SV, 1, SV, p2[ct]);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      aq[t] = wmma_k4<PV>(bO + 16 * w * SV, SV, 1, bS0 + 16 * t, S, 1, aq[t]);
+      ak[t] = wmma_k4<PV>(bU + 16 * w * SV, SV, 1, bS1 + 16 * t, S, 1, ak[t]);
+      const floatx4 ys = wmma_k4<PV>(bY + 16 * w * SV, SV, 1, bS0 + 16 * t, S, 1, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ak[t][i] -= sB[16 * w + rq + i] * ys[i];
+    }
+  }
+  __syncthreads();  // every wave is done with Tm, E2 and E1
+  // P1 = tril_0 into bT, dLk = -diag(beta) tril_-1(P2) into bE, Q into bE1;
+  // the second part of dbeta
+  stage<D>(bE1, S, q + row0 * D, D, 0, L);
+  float db2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const floatx4 kk = wmma_k4<D>(bK + 16 * w * S, S, 1, bK + 16 * ct * S, 1, S, zero4());
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + rq + i, cc = 16 * ct + col;
+      bT[r * SW + cc] = cc <= r ? p1[ct][i] : 0.f;
+      const float p = cc < r ? p2[ct][i] : 0.f;
+      bE[r * SW + cc] = -sB[r] * p;
+      db2[i] += p * kk[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float d1 = db1[i], d2 = db2[i];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      d1 += __shfl_xor(d1, off);
+      d2 += __shfl_xor(d2, off);
+    }
+    const int r = 16 * w + rq + i;
+    if (col == 0 && r < L) dbeta[row0 + r] = d1 - d2;
+  }
+  __syncthreads();
+  // dQ += P1 K;  dK += P1^T Q + dLk K + dLk^T K
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    aq[t] = wmma_k4<CH>(bT + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, aq[t]);
+    ak[t] = wmma_k4<CH>(bT + 16 * w, 1, SW, bE1 + 16 * t, S, 1, ak[t]);
+    ak[t] = wmma_k4<CH>(bE + 16 * w * SW, SW, 1, bK + 16 * t, S, 1, ak[t]);
+    ak[t] = wmma_k4<CH>(bE + 16 * w, 1, SW, bK + 16 * t, S, 1, ak[t]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + rq + i;
+      if (r < L) {
+        dq[(row0 + r) * D + 16 * t + col] = aq[t][i];
+        dk[(row0 + r) * D + 16 * t + col] = ak[t][i];
+      }
+    }
+  }
+}
+
 template <int D>
 hipError_t run_delta_backward(const float* q, const float* k, const float* v, const float* beta, int B, int H,
                               int T, const float* S0, const float* dO, const float* dSf, float* dq, float* dk,
@@ -610,12 +780,22 @@ hipError_t run_delta_backward(const float* q, const float* k, const float* v, co
   float* Sc = pre + (long)BH * nC * Pre<D>::SIZE;
   float* dSc = Sc + (long)BH * nC * D * D;
   hipLaunchKernelGGL((delta_bwd_prep<D, false>), dim3(nC, BH), dim3(256), 0, s, q, k, beta, T, nC, pre);
-  hipLaunchKernelGGL((delta_bwd_walks<D>), dim3(D / SL, BH, 2), dim3(256), 0, s, q, k, v, dO, beta, T, nC, S0, dSf,
-                     pre, Sc, dSc, dS0);
-  profile_mark_before(s);
-  hipLaunchKernelGGL((delta_bwd_grads<D>), dim3(nC, BH), dim3(256), 0, s, q, k, v, dO, beta, T, nC, pre, Sc, dSc,
-                     dq, dk, dv, dbeta);
-  profile_mark_after(s);
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL((delta_bwd_fwd_walk<D>), dim3(D / SL, BH), dim3(256), 0, s, k, v, T, nC, S0, pre, Sc);
+    hipLaunchKernelGGL((delta_bwd_rev_walk<D>), dim3(D / SL, BH), dim3(256), 0, s, q, k, dO, beta, T, nC, dSf, pre,
+                       dSc, dS0);
+    profile_mark_before(s);
+    hipLaunchKernelGGL(delta_bwd_grads_pieces, dim3(nC, BH), dim3(256), 0, s, q, k, v, dO, beta, T, nC, pre, Sc,
+                       dSc, dq, dk, dv, dbeta);
+    profile_mark_after(s);
+  } else {
+    hipLaunchKernelGGL((delta_bwd_walks<D>), dim3(D / SL, BH, 2), dim3(256), 0, s, q, k, v, dO, beta, T, nC, S0,
+                       dSf, pre, Sc, dSc, dS0);
+    profile_mark_before(s);
+    hipLaunchKernelGGL((delta_bwd_grads<D>), dim3(nC, BH), dim3(256), 0, s, q, k, v, dO, beta, T, nC, pre, Sc, dSc,
+                       dq, dk, dv, dbeta);
+    profile_mark_after(s);
+  }
   return hipGetLastError();
 }
 
@@ -776,6 +956,7 @@ hipError_t launch_delta_backward(const float* q, const float* k, const float* v,
     case 16: return run_delta_backward<16>(q, k, v, beta, B, H, T, S0, dO, dSf, dq, dk, dv, dbeta, dS0, w, s);
     case 32: return run_delta_backward<32>(q, k, v, beta, B, H, T, S0, dO, dSf, dq, dk, dv, dbeta, dS0, w, s);
     case 64: return run_delta_backward<64>(q, k, v, beta, B, H, T, S0, dO, dSf, dq, dk, dv, dbeta, dS0, w, s);
+    case 128: return run_delta_backward<128>(q, k, v, beta, B, H, T, S0, dO, dSf, dq, dk, dv, dbeta, dS0, w, s);
     default: return hipErrorInvalidValue;
   }
 }

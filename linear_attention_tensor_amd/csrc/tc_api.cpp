@@ -530,7 +530,8 @@ tc_status delta_scan_forward(const void* q, const void* k, const void* v, tc_dty
 static tc_status check_delta_bwd(const char* fn, int B, int H, int T, int dk, int dv, int chunk, tc_dtype dt) {
   tc_status st = check_seq(fn, B, H, T, dk, dv, chunk, dt);
   if (st != TC_OK) return st;
-  if (dk > 64) return fail(TC_ERR_UNSUPPORTED, "%s: the backward takes d in {16, 32, 64}", fn);
+  if (dk != 16 && dk != 32 && dk != 64 && dk != 128)
+    return fail(TC_ERR_UNSUPPORTED, "%s: the backward takes d in {16, 32, 64, 128}", fn);
   return TC_OK;
 }
 

@@ -299,3 +299,12 @@ def test_memory_entry_points_reject():
     assert L.recall_argmax(FAKE, FAKE, 1, 10, 0, 64, FAKE, NULL, NULL) == _lib.TC_ERR_INVALID_ARG
     assert L.recall_argmax(FAKE, FAKE, 70000, 10, 5, 64, FAKE, NULL, NULL) == _lib.TC_ERR_UNSUPPORTED
     assert L.recall_argmax(FAKE, FAKE, 1, 0, 5, 64, FAKE, NULL, NULL) == _lib.TC_OK
+
+
+def test_delta_backward_workspace_query_widths():
+    q = lib().delta_scan_backward_workspace_bytes
+    for dt in (_lib.TC_F32, _lib.TC_BF16):
+        for d in (16, 32, 64, 128):
+            assert 0 < q(2, 3, 300, d, d, 64, dt) < _lib.SIZE_MAX
+        assert q(2, 3, 300, 48, 48, 64, dt) == _lib.SIZE_MAX
+        assert q(2, 3, 300, 128, 64, 64, dt) == _lib.SIZE_MAX

@@ -37,6 +37,12 @@ def ref(x, do, S0=None, dSf=None):
     (1, 2, 37, 64, True),      # shorter than a chunk
     (2, 2, 513, 64, False),    # many chunks
     (1, 3, 300, 16, True),
+    # d = 128: the gradient kernel walks the state rows in pieces of 16
+    (1, 1, 64, 128, True),
+    (1, 2, 200, 128, False),
+    (2, 1, 37, 128, True),
+    (1, 1, 1, 128, True),
+    (1, 1, 300, 128, True),
 ])
 def test_delta_backward_small(B, H, T, d, states):
     print(f"[case] delta backward B={B} H={H} T={T} d={d} states={states}", flush=True)
@@ -75,9 +81,10 @@ def test_delta_backward_empty_sequence():
     assert torch.equal(g[4], dSf)
 
 
-def test_delta_backward_repeat_is_deterministic():
-    x = I.draw(1, 2, 700, 64, seed=9, dtype="f32")
-    do = I.draw_cotangent(1, 2, 700, 64, seed=9)
+@pytest.mark.parametrize("d", [64, 128])
+def test_delta_backward_repeat_is_deterministic(d):
+    x = I.draw(1, 2, 700, d, seed=9, dtype="f32")
+    do = I.draw_cotangent(1, 2, 700, d, seed=9)
     a = run(x, do)
     b = run(x, do)
     for u, w in zip(a, b):
@@ -103,6 +110,7 @@ def test_delta_backward_full_size_sampled_heads():
     (1, 2, 200, 64, False),
     (2, 1, 130, 32, True),
     (1, 1, 37, 16, True),
+    (1, 2, 150, 128, True),
 ])
 def test_delta_backward_bf16_inputs(B, H, T, d, states):
     # bf16 q, k, v are widened to fp32 in the workspace: the gradients are those
@@ -119,3 +127,22 @@ def test_delta_backward_bf16_inputs(B, H, T, d, states):
     torch.cuda.synchronize()
     for name, a, b in zip(NAMES, [t.cpu().numpy() for t in g], ref(x, do, S0, dSf)):
         check(name, a, b, TOL_BF16)
+
+
+def test_delta_backward_bf16_workload_full_size_sampled_head():
+    # the delta-rule workload itself (B=2 H=16 T=16384 d=128, bf16 inputs):
+    # the oracle on one whole head (every t)
+    w = I.WORKLOADS["delta_scan_bf16"]
+    print("[case] delta backward bf16 workload full size", flush=True)
+    x = I.draw_workload("delta_scan_bf16")
+    do = I.draw_cotangent(w.B, w.H, w.T, w.d, seed=w.seed)
+    g = ops.delta_scan_backward(*(to_dev(x[n], "bf16") for n in ("q", "k", "v")), f32_dev(x["beta"]), f32_dev(do),
+                                return_dS0=True)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in g]
+    b, h = 1, 5
+    xs = {n: x[n][b:b + 1, h:h + 1] for n in ("q64", "k64", "v64", "beta")}
+    want = D.delta_scan_backward(xs["q64"], xs["k64"], xs["v64"], xs["beta"].astype(np.float64),
+                                 do[b:b + 1, h:h + 1].astype(np.float64))
+    for name, a, r in zip(NAMES, got, want):
+        check(f"b={b} h={h} {name}", a[b:b + 1, h:h + 1], r, TOL_BF16)
