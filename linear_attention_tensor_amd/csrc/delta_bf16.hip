@@ -13,9 +13,12 @@
 //   O = Q S0^T + tril_0(Q K^T) U,      S = S0 + U^T K.
 // A depends on K and beta only, so it is computed for every chunk at once:
 //   delta_prep   per (chunk, b, h): A by blocked inversion (fp32), stored
-//                as a bf16 pair A = A_hi + A_lo, K^T of the chunk and
-//                tril_0(Q K^T) (bf16; it depends on q and k only);
-//   delta_main   per (b, h, 16-row slice of S): walks the chunks in order.
+//                as a bf16 pair A = A_hi + A_lo;
+//   delta_main   per (b, h, 16-row slice of S): walks the chunks in order;
+//                it forms tril_0(Q K^T) (it depends on q and k only) from
+//                the chunk's q and k rows itself, and takes the K^T operands
+//                by transpose reads of the K rows, so that a chunk brings
+//                only q, k, A and the V slice into LDS.
 // The rows of S are independent (row j only sees column j of V and U), so
 // the slices need no communication.  The terms that feed the recurrence (K
 // S0^T, A X, U^T K) use bf16 pairs for their fp32 operands, so each product
@@ -77,92 +80,39 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// delta_prep: four waves per (chunk, b, h).  Every output leaves in 16-byte
-// (A, K^T) or 8-byte (tril(Q K^T)) pieces per lane.  One buffer holds in
-// turn the K^T staging, Q, L and M = (I + L)^-1, so that four workgroups
-// fit in a CU's LDS.
+// delta_prep: four waves per (chunk, b, h).  A leaves in 16-byte pieces per
+// lane; one buffer holds in turn L and M = (I + L)^-1.
 template <int D>
-__global__ __launch_bounds__(256) void delta_prep_kernel(const uint16_t* __restrict__ q,
-                                                         const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256) void delta_prep_kernel(const uint16_t* __restrict__ k,
                                                          const float* __restrict__ beta, int T,
-                                                         int n_chunks, uint16_t* __restrict__ a_out,
-                                                         uint16_t* __restrict__ kt_out,
-                                                         uint16_t* __restrict__ qm_out) {
+                                                         int n_chunks, uint16_t* __restrict__ a_out) {
   constexpr int NCH = D / 8;
   constexpr int LS = CH + 4;                 // fp32 rows of L and M, 16-byte aligned
   constexpr int NP = CH * NCH / 256;         // 16-byte pieces per thread of a [64][D] array
-  static_assert(D * CH * 2 <= CH * LS * 4, "K^T and Q fit the L buffer");
   __shared__ __attribute__((aligned(16))) uint16_t sK[CH * D];
-  __shared__ __attribute__((aligned(16))) float sL[CH * LS];  // K^T staging, Q, L, M
+  __shared__ __attribute__((aligned(16))) float sL[CH * LS];  // L, then M
   __shared__ float sT[4][16 * 17];                            // one block product per wave
   __shared__ float sB[CH];
-  uint16_t* const sQ = reinterpret_cast<uint16_t*>(sL);
-  uint16_t* const skt = reinterpret_cast<uint16_t*>(sL);
   const int n = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int w = wave_id(), l = lane_id(), lr = l & 15, lg = l >> 4;
   const int t0 = n * CH;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + (long)bh * T * D, (uint32_t)T * D * 2);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + (long)bh * T * D, (uint32_t)T * D * 2);
 
-  // rows of K and Q (zero past T); piece i of this thread is row s / NCH,
-  // chunk s % NCH with s = 256 i + t
-  uint4 kr[NP], qr[NP];
+  // rows of K (zero past T); piece i of this thread is row s / NCH, chunk
+  // s % NCH with s = 256 i + t
+  uint4 kr[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int s = i * 256 + t, row = s / NCH, c = s % NCH;
     kr[i] = buf_load16(rk, ((t0 + row) * D + 8 * c) * 2);
-    qr[i] = buf_load16(rq, ((t0 + row) * D + 8 * c) * 2);
   }
   if (t < CH) sB[t] = t0 + t < T ? beta[(long)bh * T + t0 + t] : 0.f;
-  // K into sK and, transposed, into the staging area ([dk][key] bf16)
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int s = i * 256 + t, row = s / NCH, c = s % NCH;
     *reinterpret_cast<uint4*>(sK + pos<NCH>(row, c)) = kr[i];
-    const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      skt[(8 * c + 2 * e) * CH + row] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
-      skt[(8 * c + 2 * e + 1) * CH + row] = static_cast<uint16_t>(w4[e] >> 16);
-    }
   }
   __syncthreads();
-  // K^T of the chunk: D rows of 64 keys, eight 16-byte pieces per row
-  uint16_t* kt = kt_out + ((long)bh * n_chunks + n) * D * CH;
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    const int s = i * 256 + t;
-    *reinterpret_cast<uint4*>(kt + s * 8) = *reinterpret_cast<const uint4*>(skt + s * 8);
-  }
-  __syncthreads();  // the staged K^T has been read: Q takes its place
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int s = i * 256 + t, row = s / NCH, c = s % NCH;
-    *reinterpret_cast<uint4*>(sQ + pos<NCH>(row, c)) = qr[i];
-  }
-  __syncthreads();
-  // tril_0(Q K^T), bf16 row-major [query][key], formed as its transpose (keys
-  // as M) so that a lane holds four consecutive keys of one query: wave w
-  // takes queries 16w.., tile mi = keys 16mi.. (zero for mi > w)
-  {
-    uint16_t* qm = qm_out + ((long)bh * n_chunks + n) * CH * CH;
-    const int ni = w, rq = 16 * ni + lr;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const int c0 = 16 * mi + 4 * lg;
-      uint2 out = make_uint2(0u, 0u);
-      if (mi <= ni) {
-        floatx4 acc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-          acc = mma(ldc<NCH>(sK, 16 * mi + lr, 4 * ks + lg), ldc<NCH>(sQ, rq, 4 * ks + lg), acc);
-        out = make_uint2(cvt_pk(c0 <= rq ? acc[0] : 0.f, c0 + 1 <= rq ? acc[1] : 0.f),
-                         cvt_pk(c0 + 2 <= rq ? acc[2] : 0.f, c0 + 3 <= rq ? acc[3] : 0.f));
-      }
-      *reinterpret_cast<uint2*>(qm + rq * CH + c0) = out;
-    }
-  }
-  __syncthreads();  // Q has been read: L takes its place
   // L = diag(beta) tril_{-1}(K K^T): wave w takes rows 16w.. (tiles ni <= w)
   {
     const int mi = w;
@@ -271,24 +221,31 @@ struct DeltaLds {
   // double-buffered chunk inputs (swizzled rows)
   uint16_t q[2][CH * D];      // [token][dk]
   uint16_t k[2][CH * D];      // [token][dk]
-  uint16_t kt[2][D * CH];     // [dk][token]
   uint16_t a[2][2][CH * CH];  // [hi|lo][token r][token c]
   uint16_t v[2][CH * DVT];    // [token][dv] plain
   // per-chunk work
   uint16_t h[2][DVT * D];     // state slice [hi|lo][dv][dk]
   uint16_t xt[2][DVT * CH];   // (V - K S0^T)^T [hi|lo][dv][token]
   uint16_t ut[2][DVT * CH];   // U^T [hi|lo][dv][token]
-  uint16_t qk[CH * CH];       // tril_0(Q K^T) [r][c]
 };
+
+// ds_read_b64_tr_b16: lane j of each 16-lane group gets element j % 4 of the
+// 8-byte pieces addressed by lanes 4 i + j / 4 (i = 0..3)
+__device__ __forceinline__ uint2 lds_tr8(const uint16_t* base, int elem) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(base + elem));
+  return __builtin_bit_cast(uint2, x);
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void delta_main_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ a_in, const uint16_t* __restrict__ kt_in,
-    const uint16_t* __restrict__ qm_in, int T, int n_chunks,
-    int n_items, const float* __restrict__ S0, float* __restrict__ o, float* __restrict__ S_final) {
+    const uint16_t* __restrict__ a_in, int T, int n_chunks, int n_items, const float* __restrict__ S0,
+    float* __restrict__ o, float* __restrict__ S_final) {
   constexpr int NCH = D / 8;  // chunks per q/k/h row
   constexpr int NT = D / 64;  // 16-column state tiles per wave
+  constexpr int NK = D / 32;  // k-steps over d_k
   __shared__ __attribute__((aligned(16))) DeltaLds<D> lds;
 
   // the slices of one head take consecutive items on one XCD (shared L2)
@@ -303,15 +260,13 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
   const i32x4 dk = raw_desc(k + tb * D, (uint32_t)T * D * 2);
   const i32x4 dv = raw_desc(v + tb * D, (uint32_t)T * D * 2);
   const i32x4 da = raw_desc(a_in + (long)bh * n_chunks * 2 * CH * CH, (uint32_t)n_chunks * 2 * CH * CH * 2);
-  const i32x4 dkt = raw_desc(kt_in + (long)bh * n_chunks * D * CH, (uint32_t)n_chunks * D * CH * 2);
-  const i32x4 dqm = raw_desc(qm_in + (long)bh * n_chunks * CH * CH, (uint32_t)n_chunks * CH * CH * 2);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + tb * D, (uint32_t)T * D * 4);  // rows past T: dropped
 
-  // DMA of chunk n into buffer b, in three parts issued during different
+  // DMA of chunk n into buffer b, in two parts issued during different
   // phases of the previous chunk (so that the workgroup's copy instructions
   // do not queue all at once).  Slot s of an array holds the 16-byte chunk
   // that its swizzle maps there.
-  constexpr int NQ = CH * D / 8 / 256;  // 16-byte slots per thread per q/k/k^T array
+  constexpr int NQ = CH * D / 8 / 256;  // 16-byte slots per thread per q/k array
   auto issue_qkv = [&](int n, int b) __attribute__((always_inline)) {
     const int t0 = n * CH;
 #pragma unroll
@@ -321,9 +276,9 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
       dma16(dq, lds.q[b] + seg * 512, ((t0 + r) * D + 8 * c) * 2);
       dma16(dk, lds.k[b] + seg * 512, ((t0 + r) * D + 8 * c) * 2);
     }
-    {  // V slice: 64 rows of two 16-byte chunks; waves w and w + 2 copy the same half
-      const int s = (w & 1) * 64 + l, r = s / 2, c = s % 2;
-      dma16(dv, lds.v[b] + (w & 1) * 512, ((t0 + r) * D + dv0 + 8 * c) * 2);
+    if (w < 2) {  // V slice: 64 rows of two 16-byte chunks
+      const int s = w * 64 + l, r = s / 2, c = s % 2;
+      dma16(dv, lds.v[b] + w * 512, ((t0 + r) * D + dv0 + 8 * c) * 2);
     }
   };
   auto issue_a = [&](int n, int b) __attribute__((always_inline)) {
@@ -334,51 +289,31 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
       dma16(da, lds.a[b][0] + seg * 512, ((((long)n * 2 + h) * CH + r) * CH + 8 * c) * 2);
     }
   };
-  auto issue_kt = [&](int n, int b) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {  // K^T: D rows of 8 chunks
-      const int seg = i * 4 + w, s = seg * 64 + l;
-      const int r = s / 8, c = (s % 8) ^ swz<8>(r);
-      dma16(dkt, lds.kt[b] + seg * 512, (((long)n * D + r) * CH + 8 * c) * 2);
-    }
-  };
-  auto issue_qm = [&](int n) __attribute__((always_inline)) {  // tril_0(Q K^T): 64 rows of 8 chunks
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int seg = i * 4 + w, s = seg * 64 + l;
-      const int r = s / 8, c = (s % 8) ^ swz<8>(r);
-      dma16(dqm, lds.qk + seg * 512, (((long)n * CH + r) * CH + 8 * c) * 2);
-    }
-  };
   // copy instructions per wave and part (the waits below count them)
-  constexpr int N_QKV = 2 * NQ + 1, N_A = 4, N_KT = NQ, N_QM = 2;
-  auto issue = [&](int n, int b) __attribute__((always_inline)) {
-    issue_qkv(n, b);
-    issue_a(n, b);
-    issue_kt(n, b);
-  };
+  const int n_qkv = 2 * NQ + (w < 2 ? 1 : 0);
+  constexpr int N_A = 4;
 
-  // state slice: rows dv0 .. dv0+15; wave w owns columns D/4 w .. (NT tiles
-  // of 16); D layout: lane lr + 16 lg holds rows 4 lg + e of column lr.
+  // S^T slice: rows dk = (D/4) w + 16 t + 4 lg + e, column dv0 + lr (the
+  // accumulator layout of S^T += K^T U); published as bf16 hi/lo rows
+  // [dv][dk], four consecutive dk (8 bytes) per lane and tile.
   floatx4 hs[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 4 * lg + e, c = (D / 4) * w + 16 * t + lr;
-      hs[t][e] = S0 != nullptr ? S0[((long)bh * D + dv0 + r) * D + c] : 0.f;
+      const int c = (D / 4) * w + 16 * t + 4 * lg + e;
+      hs[t][e] = S0 != nullptr ? S0[((long)bh * D + dv0 + lr) * D + c] : 0.f;
     }
   }
   auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * lg + e, c = (D / 4) * w + 16 * t + lr;
-        const uint16_t hi = f32_to_bf16(hs[t][e]);
-        lds.h[0][epos<NCH>(r, c)] = hi;
-        lds.h[1][epos<NCH>(r, c)] = f32_to_bf16(hs[t][e] - bf16_to_f32(hi));
-      }
+      const int c = (D / 4) * w + 16 * t + 4 * lg;
+      uint32_t h0, h1, l0, l1;
+      split2(hs[t][0], hs[t][1], h0, l0);
+      split2(hs[t][2], hs[t][3], h1, l1);
+      *reinterpret_cast<uint2*>(lds.h[0] + epos<NCH>(lr, c)) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(lds.h[1] + epos<NCH>(lr, c)) = make_uint2(l0, l1);
     }
   };
   publish_state();
@@ -395,19 +330,25 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
     clear(&lds.v[0][0], (int)sizeof(lds.v));
     lds_barrier();
   }
-  if (n_chunks > 0) issue(0, 0);
+  if (n_chunks > 0) {
+    issue_qkv(0, 0);
+    issue_a(0, 0);
+  }
 
   floatx4 o_prev = zero4();
   int t_prev = -1;  // first token of the chunk whose O is still in registers
   const int r0 = 16 * w;  // this wave's tokens in the chunk
+  // K^T operand pieces by transpose reads of K rows: lane j of group lg
+  // addresses row R + j / 4, columns 4 (j % 4) .. of a 16-column tile, and
+  // receives column j of rows R .. R + 3
+  const int tr_row = lr >> 2, tr_col = 4 * (lr & 3);
 #pragma unroll 1
   for (int n = 0; n < n_chunks; ++n) {
     const int b = n & 1, t0 = n * CH;
     // Copies complete in issue order.  Issued for chunk n during chunk n - 1:
-    // q/k/v (phase 1), A (phase 2), k^T (phase 3); at the top of chunk n: the
-    // O stores of chunk n - 1, then tril(Q K^T) of chunk n.
-    wait_vmcnt<N_A + N_KT>();  // q, k, v of chunk n have landed
-    lds_barrier();  // ... for every wave; chunk n - 1's buffers, qk and h are free / published
+    // q/k/v (phase 1), then A (phase 2).
+    wait_vmcnt<N_A>();  // q, k, v of chunk n have landed
+    lds_barrier();      // ... for every wave; chunk n - 1's buffers are free, the state is published
     const bool more = n + 1 < n_chunks;  // chunk n + 1 is copied during this one
     if (t_prev >= 0) {  // O of the previous chunk, stored now so the stores overlap this chunk
 #pragma unroll
@@ -415,11 +356,9 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o_prev[e]), ro,
                                               ((t_prev + r0 + 4 * lg + e) * D + dv0 + lr) * 4, 0, 0);
     }
-    issue_qm(n);
 
-    // phase 1: K S0^T, Q S0^T (this wave's tokens); X = V - K S0^T.  Operand
-    // reads first, then the MFMAs.
-    constexpr int NK = D / 32;
+    // phase 1: K S0^T, Q S0^T (this wave's tokens); X = V - K S0^T; and,
+    // off the chain, tril_0(Q K^T) for this wave's queries
     bf16x8 ka[NK], hh[NK], hl[NK], qa[NK];
     TC_SB();
 #pragma unroll
@@ -439,6 +378,17 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
       kl = mma(ka[ks], hl[ks], kl);
       qh = mma(qa[ks], hh[ks], qh);
     }
+    // (Q K^T)^T tiles: keys 16 mt + 4 lg + e of query r0 + lr (only the
+    // tiles with keys <= the wave's last query)
+    floatx4 qkt[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      qkt[mt] = zero4();
+      if (mt <= w) {
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) qkt[mt] = mma(ldc<NCH>(lds.k[b], 16 * mt + lr, 4 * ks + lg), qa[ks], qkt[mt]);
+      }
+    }
     {
       // X^T row dv = lr, tokens r0 + 4 lg + e
       float x[4];
@@ -451,12 +401,16 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
       *reinterpret_cast<uint2*>(lds.xt[0] + epos<8>(lr, r0 + 4 * lg)) = make_uint2(h0, h1);
       *reinterpret_cast<uint2*>(lds.xt[1] + epos<8>(lr, r0 + 4 * lg)) = make_uint2(l0, l1);
     }
-    // A of chunk n: loads issued after it are k^T, tril(Q K^T) and (if any)
-    // q/k/v of chunk n + 1.  The O stores between them are not counted:
-    // stores may complete ahead of older loads, so the wait is exact only
-    // over loads (which complete in order) and merely longer otherwise.
-    if (more) wait_vmcnt<N_KT + N_QM + N_QKV>();
-    else wait_vmcnt<N_KT + N_QM>();
+    // A of chunk n: loads issued after it are (if any) q/k/v of chunk n + 1.
+    // The O stores between them are not counted: stores may complete ahead
+    // of older loads, so the wait is exact only over loads (which complete in
+    // order) and merely longer otherwise.
+    if (more) {
+      if (w < 2) wait_vmcnt<2 * NQ + 1>();
+      else wait_vmcnt<2 * NQ>();
+    } else {
+      wait_vmcnt<0>();
+    }
     lds_barrier();
 
     // phase 2: U = A X for this wave's tokens
@@ -487,38 +441,61 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
       *reinterpret_cast<uint2*>(lds.ut[0] + epos<8>(lr, r0 + 4 * lg)) = make_uint2(h0, h1);
       *reinterpret_cast<uint2*>(lds.ut[1] + epos<8>(lr, r0 + 4 * lg)) = make_uint2(l0, l1);
     }
-    // k^T and tril(Q K^T) of chunk n: issued after them are q/k/v and A of
-    // chunk n + 1 (if any)
-    if (more) wait_vmcnt<N_QKV + N_A>();
-    else wait_vmcnt<0>();
-    lds_barrier();
+    lds_barrier();  // U of every wave
 
-    // phase 3: O = Q S0^T + tril_0(Q K^T) U;  S += U^T K
-    bf16x8 qkr[2], uh[2], ul[2], kt[NT][2];
+    // phase 3: O = Q S0^T + tril_0(Q K^T) U;  S^T += K^T U.  U as the B
+    // operand (row dv0 + lr, keys in the k order of qkm) and the K^T pieces
+    // by transpose reads.
+    bf16x8 uh[2], ul[2], kt[NT][2];
     TC_SB();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      qkr[ks] = ldc<8>(lds.qk, r0 + lr, 4 * ks + lg);
-      uh[ks] = ldc<8>(lds.ut[0], lr, 4 * ks + lg);
-      ul[ks] = ldc<8>(lds.ut[1], lr, 4 * ks + lg);
+      const int c0 = 32 * ks + 4 * lg;
+      {
+        const uint2 h0 = *reinterpret_cast<const uint2*>(lds.ut[0] + epos<8>(lr, c0));
+        const uint2 h1 = *reinterpret_cast<const uint2*>(lds.ut[0] + epos<8>(lr, c0 + 16));
+        const uint2 l0 = *reinterpret_cast<const uint2*>(lds.ut[1] + epos<8>(lr, c0));
+        const uint2 l1 = *reinterpret_cast<const uint2*>(lds.ut[1] + epos<8>(lr, c0 + 16));
+        uh[ks] = as_bf16x8(h0.x, h0.y, h1.x, h1.y);
+        ul[ks] = as_bf16x8(l0.x, l0.y, l1.x, l1.y);
+      }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) kt[t][ks] = ldc<8>(lds.kt[b], (D / 4) * w + 16 * t + lr, 4 * ks + lg);
+      for (int t = 0; t < NT; ++t) {
+        const int col = (D / 4) * w + 16 * t + tr_col;
+        const uint2 p0 = lds_tr8(lds.k[b], epos<NCH>(c0 + tr_row, col));
+        const uint2 p1 = lds_tr8(lds.k[b], epos<NCH>(c0 + 16 + tr_row, col));
+        kt[t][ks] = as_bf16x8(p0.x, p0.y, p1.x, p1.y);
+      }
     }
     TC_SB();
-    if (more) issue_kt(n + 1, b ^ 1);
-    TC_SB();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) qh = mma(qkr[ks], uh[ks], qh);
-    o_prev = qh;
-    t_prev = t0;
+    // the state first (the next chunk waits for it), then O
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        hs[t] = mma(uh[ks], kt[t][ks], hs[t]);
-        hs[t] = mma(ul[ks], kt[t][ks], hs[t]);
+        hs[t] = mma(kt[t][ks], uh[ks], hs[t]);
+        hs[t] = mma(kt[t][ks], ul[ks], hs[t]);
       }
     }
+    // tril_0 as the A operand of O += tril(Q K^T) U: k-step ks takes keys
+    // 32 ks + 4 lg .. +3 and 32 ks + 16 + 4 lg .. +3 (tiles 2 ks, 2 ks + 1)
+    bf16x8 qkm[2];
+    {
+      const int rq = r0 + lr;
+      uint32_t pw[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int c0 = 16 * mt + 4 * lg;
+        pw[mt][0] = cvt_pk(c0 <= rq ? qkt[mt][0] : 0.f, c0 + 1 <= rq ? qkt[mt][1] : 0.f);
+        pw[mt][1] = cvt_pk(c0 + 2 <= rq ? qkt[mt][2] : 0.f, c0 + 3 <= rq ? qkt[mt][3] : 0.f);
+      }
+      qkm[0] = as_bf16x8(pw[0][0], pw[0][1], pw[1][0], pw[1][1]);
+      qkm[1] = as_bf16x8(pw[2][0], pw[2][1], pw[3][0], pw[3][1]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) qh = mma(qkm[ks], uh[ks], qh);
+    o_prev = qh;
+    t_prev = t0;
     publish_state();  // read next after the barrier at the top of the loop
   }
   if (t_prev >= 0) {
@@ -532,7 +509,7 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        S_final[((long)bh * D + dv0 + 4 * lg + e) * D + (D / 4) * w + 16 * t + lr] = hs[t][e];
+        S_final[((long)bh * D + dv0 + lr) * D + (D / 4) * w + 16 * t + 4 * lg + e] = hs[t][e];
   }
 }
 
@@ -542,16 +519,13 @@ hipError_t run_delta_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           hipStream_t s) {
   const int n_chunks = (T + CH - 1) / CH;
   uint16_t* a_ws = static_cast<uint16_t*>(ws);
-  uint16_t* kt_ws = a_ws + (size_t)BH * n_chunks * 2 * CH * CH;
-  uint16_t* qm_ws = kt_ws + (size_t)BH * n_chunks * D * CH;
   if (n_chunks > 0)
-    hipLaunchKernelGGL(delta_prep_kernel<D>, dim3(n_chunks, BH), dim3(256), 0, s, q, k, beta, T,
-                       n_chunks, a_ws, kt_ws, qm_ws);
+    hipLaunchKernelGGL(delta_prep_kernel<D>, dim3(n_chunks, BH), dim3(256), 0, s, k, beta, T, n_chunks, a_ws);
   const int n_items = BH * (D / DVT);
   const int grid = (n_items + NXCD - 1) / NXCD * NXCD;
   profile_mark_before(s);
-  hipLaunchKernelGGL(delta_main_kernel<D>, dim3(grid), dim3(256), 0, s, q, k, v, a_ws, kt_ws, qm_ws,
-                     T, n_chunks, n_items, S0, o, S_final);
+  hipLaunchKernelGGL(delta_main_kernel<D>, dim3(grid), dim3(256), 0, s, q, k, v, a_ws, T, n_chunks, n_items, S0,
+                     o, S_final);
   profile_mark_after(s);
   return hipGetLastError();
 }
@@ -562,7 +536,7 @@ bool delta_bf16_supported(bool bf16, int d) { return bf16 && (d == 64 || d == 12
 
 size_t delta_bf16_ws_bytes(int B, int H, int T, int d) {
   const size_t n_chunks = (T + CH - 1) / CH;
-  return (size_t)B * H * n_chunks * (3 * CH * CH + (size_t)d * CH) * sizeof(uint16_t);
+  return (size_t)B * H * n_chunks * 2 * CH * CH * sizeof(uint16_t);
 }
 
 hipError_t launch_delta_bf16(const void* q, const void* k, const void* v, const float* beta, int B,
