@@ -50,7 +50,7 @@ def test_fused_gate_closed_is_sliding_window():
     check("y", y, ref, 2e-2)
 
 
-def test_fused_layer_full_size_sampled_rows():
+def test_fused_layer_full_size_sampled_rows_and_a_whole_head():
     w = I.WORKLOADS["fused_layer_bf16"]
     print("[case] fused full size", flush=True)
     x = I.draw_workload("fused_layer_bf16")
@@ -59,6 +59,13 @@ def test_fused_layer_full_size_sampled_rows():
     ref = O.tc_fused_rows(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64), x["eta"],
                           x["g"].astype(np.float64), w.W, rows)
     check("y rows", y[:, :, rows], ref, 2e-2)
+    # one whole head, every row (each of its 128 tiles), and its final state
+    h = 5
+    y_h, A_h = O.tc_fused(x["q64"][:, h:h + 1], x["k64"][:, h:h + 1], x["v64"][:, h:h + 1],
+                          x["lam"][h:h + 1].astype(np.float64), x["eta"][h:h + 1],
+                          x["g"][h:h + 1].astype(np.float64), w.W)
+    check(f"y head {h}", y[:, h:h + 1], y_h, 2e-2)
+    check(f"A head {h}", A[:, h:h + 1], A_h, 2e-2)
 
 
 @pytest.mark.parametrize("dtype,B,H,T,d,W", [

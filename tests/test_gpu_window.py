@@ -60,7 +60,7 @@ def test_window_matches_closed_gate_layer():
     same_bits("window vs fused layer with the gate closed", y_win, y_lay)
 
 
-def test_window_full_size_sampled_rows():
+def test_window_full_size_sampled_rows_and_a_whole_head():
     w = I.WORKLOADS["fused_layer_bf16"]
     print("[case] window full size", flush=True)
     x = I.draw_workload("fused_layer_bf16")
@@ -68,3 +68,8 @@ def test_window_full_size_sampled_rows():
     rows = [0, 1, 63, 1023, 1024, 4097, 16384, 30000, w.T - 1]
     ref = O.window_softmax_rows(x["q64"], x["k64"], x["v64"], w.W, 1.0 / np.sqrt(w.d), rows)
     check("y rows", y[:, :, rows], ref, 2e-2)
+    # one whole head, every row
+    h = 11
+    ref_h = O.window_softmax(x["q64"][:, h:h + 1], x["k64"][:, h:h + 1], x["v64"][:, h:h + 1], w.W,
+                             1.0 / np.sqrt(w.d))
+    check(f"y head {h}", y[:, h:h + 1], ref_h, 2e-2)
