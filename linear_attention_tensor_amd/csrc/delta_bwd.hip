@@ -800,7 +800,7 @@ hipError_t run_delta_backward(const float* q, const float* k, const float* v, co
 }
 
 // ---------------------------------------------------------------------------
-// The forward itself (fp32, d <= 64) on the same prep: per chunk, with A =
+// The forward itself (fp32, d <= 128) on the same prep: per chunk, with A =
 // tril_0(Q K^T) kept by the prep in place of E2,
 //   U = Tm V - G2 S0^T,   O = Q S0^T + A U,   S1 = S0 + U^T K,
 // per (16-row slice of S, b, h), chunks in order, the next chunk prefetched
@@ -879,12 +879,12 @@ __global__ __launch_bounds__(256) void delta_fwd_walk(const float* __restrict__ 
     if (16 * w + r < L)
       *reinterpret_cast<float4*>(o + ((long)bh * T + t0 + 16 * w + r) * D + j0 + 4 * g) =
           make_float4(ot[0], ot[1], ot[2], ot[3]);
-    if (w < D / 16) {  // S += U^T K, tile (slice rows, columns 16w..)
-      float* base = sS + 4 * g * S + 16 * w + r;
+    for (int t = w; t < D / 16; t += 4) {  // S += U^T K, tile (slice rows, columns 16t..)
+      float* base = sS + 4 * g * S + 16 * t + r;
       floatx4 acc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = base[i * S];
-      mma_rows<CH, 1>(sUt, SW, sKt + 16 * w * SW, 0, SW, &acc);
+      mma_rows<CH, 1>(sUt, SW, sKt + 16 * t * SW, 0, SW, &acc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) base[i * S] = acc[i];
     }
@@ -918,7 +918,7 @@ __global__ void delta_bwd_empty(const float* __restrict__ dSf, float* __restrict
 
 }  // namespace
 
-bool delta_f32_fast(bool bf16, int d) { return !bf16 && (d == 16 || d == 32 || d == 64); }
+bool delta_f32_fast(bool bf16, int d) { return !bf16 && (d == 16 || d == 32 || d == 64 || d == 128); }
 
 size_t delta_f32_ws_bytes(int B, int H, int T, int d) {
   const long nC = (T + CH - 1) / CH;
@@ -932,6 +932,7 @@ hipError_t launch_delta_f32(const float* q, const float* k, const float* v, cons
     case 16: return run_delta_forward<16>(q, k, v, beta, B, H, T, S0, o, S_final, w, s);
     case 32: return run_delta_forward<32>(q, k, v, beta, B, H, T, S0, o, S_final, w, s);
     case 64: return run_delta_forward<64>(q, k, v, beta, B, H, T, S0, o, S_final, w, s);
+    case 128: return run_delta_forward<128>(q, k, v, beta, B, H, T, S0, o, S_final, w, s);
     default: return hipErrorInvalidValue;
   }
 }
