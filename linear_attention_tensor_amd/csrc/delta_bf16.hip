@@ -289,8 +289,8 @@ __global__ __launch_bounds__(256) void delta_main_kernel(
       dma16(da, lds.a[b][0] + seg * 512, ((((long)n * 2 + h) * CH + r) * CH + 8 * c) * 2);
     }
   };
-  // copy instructions per wave and part (the waits below count them)
-  const int n_qkv = 2 * NQ + (w < 2 ? 1 : 0);
+  // copy instructions per wave and part (the waits below count them): q/k/v
+  // 2 NQ, plus one V piece in waves 0 and 1; A 4
   constexpr int N_A = 4;
 
   // S^T slice: rows dk = (D/4) w + 16 t + 4 lg + e, column dv0 + lr (the
