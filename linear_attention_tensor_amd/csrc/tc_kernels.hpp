@@ -115,13 +115,13 @@ hipError_t launch_hebbian_read(const float* Q, int n, const float* A, const floa
 hipError_t launch_memory_read(const float* Q, const float* A, int groups, int n, int d, float* out, hipStream_t s);
 hipError_t launch_recall_argmax(const float* R, const float* V, int groups, int nq, int nc, int d, int* arg,
                                 float* best, hipStream_t s);
-// The delta-rule forward for fp32 inputs with d in {16, 32, 64} on the
+// The delta-rule forward for fp32 inputs with d in {16, 32, 64, 128} on the
 // backward's chunk preparation (delta_bwd.hip); launch_delta_scan dispatches to it.
 bool delta_f32_fast(bool bf16, int d);
 size_t delta_f32_ws_bytes(int B, int H, int T, int d);
 hipError_t launch_delta_f32(const float* q, const float* k, const float* v, const float* beta, int B, int H, int T,
                             int d, const float* S0, float* o, float* S_final, void* ws, hipStream_t s);
-// Backward of the delta-rule scan (delta_bwd.hip): fp32 inputs, d in {16, 32, 64}.
+// Backward of the delta-rule scan (delta_bwd.hip): fp32 inputs, d in {16, 32, 64, 128}.
 size_t delta_bwd_ws_bytes(int B, int H, int T, int d);
 hipError_t launch_delta_backward(const float* q, const float* k, const float* v, const float* beta, int B, int H,
                                  int T, int d, const float* S0, const float* dO, const float* dSf, float* dq,

@@ -373,7 +373,7 @@ def delta_scan_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, beta:
                         dS_final: Optional[torch.Tensor] = None, return_dS0: bool = False,
                         check_values: bool = True, ws: Optional[torch.Tensor] = None):
     """Gradients (dq, dk, dv, dbeta[, dS0]) of sum <do, o> (+ <dS_final, S_final>)
-    through delta_scan_forward; float32 or bfloat16 inputs, d in {16, 32, 64}."""
+    through delta_scan_forward; float32 or bfloat16 inputs, d in {16, 32, 64, 128}."""
     B, H, T, dk, dv, dt = _qkv(q, k, v)
     _check_tensor("beta", beta, (B, H, T), torch.float32, q.device)
     _check_tensor("do", do, (B, H, T, dv), torch.float32, q.device)
