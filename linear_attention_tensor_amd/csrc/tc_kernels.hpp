@@ -17,7 +17,6 @@ struct ScanPlan {
   int n_chunks;    // ceil(n_act / 64)
   int seg_chunks;  // chunks per segment
   int n_seg;       // segments per (b, h)
-  int dvt;         // width of the d_v tile one workgroup owns
 };
 ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int W);
 size_t scan_ws_bytes(const ScanPlan& p, int B, int H, int dk, int dv);

@@ -16,10 +16,10 @@
 //      segments' contributions (a Horner recurrence over them), then carry
 //      it through the segment's chunks and write m; the segments also clear
 //      the rows t < W, which are zero.
-// For d = 128 with fp32 inputs (scan_state_kernel / scan_output_kernel) the
-// entering states come from a separate scan_prefix launch, sequential over
-// the segments but parallel over the d_k x d_v elements, and the rows t < W
-// from zero_rows_kernel.
+// d = 128 runs as four d = 64 pieces: the read splits over the column halves
+// of the features, m[:, b] = sum_a m(q[:, a], k[:, a], v[:, b]), and the state
+// block A[a][b] is the piece's own state, so each piece is the d = 64 scan on
+// strided rows (the second a adds its read to m).
 // Arithmetic: fp32 MFMA (v_mfma_f32_16x16x4_f32) on LDS tiles; bf16 inputs
 // are widened to fp32 when staged, and the state is fp32 throughout.
 #include "tc_common.hpp"
@@ -32,218 +32,6 @@ namespace tc {
 namespace {
 
 constexpr int CH = 64;  // positions per chunk
-
-template <int DK, int DVT>
-struct ScanLds {
-  static constexpr int SQ = DK + 2;   // row stride of q', k: A-operand pattern
-  static constexpr int SV = DVT + 16; // row stride of v, S: B-operand pattern
-  static constexpr int SP = CH + 2;
-};
-
-// Copy rows [0, 64) x [0, D) of a row-major source (row stride `ld`, first
-// column `col0`) into LDS as fp32; rows >= nvalid become zero.
-template <typename TIn, int D>
-__device__ __forceinline__ void stage(float* dst, int dst_ld, const TIn* src, long ld, int col0,
-                                      int nvalid) {
-  constexpr int V4 = D / 4;
-  for (int idx = threadIdx.x; idx < CH * V4; idx += blockDim.x) {
-    const int r = idx / V4;
-    const int c = (idx % V4) * 4;
-    float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
-    if (r < nvalid) {
-      const TIn* p = src + r * ld + col0 + c;
-      x0 = InT<TIn>::ld(p, 0);
-      x1 = InT<TIn>::ld(p, 1);
-      x2 = InT<TIn>::ld(p, 2);
-      x3 = InT<TIn>::ld(p, 3);
-    }
-    float* d = dst + r * dst_ld + c;
-    d[0] = x0;
-    d[1] = x1;
-    d[2] = x2;
-    d[3] = x3;
-  }
-}
-
-// S (DK x DVT, LDS) <- lam^L S + K^T diag(w) V, with w already folded into V.
-template <int DK, int DVT>
-__device__ __forceinline__ void state_update(float* sS, const float* sK, const float* sV,
-                                             float lamL) {
-  using Ly = ScanLds<DK, DVT>;
-  constexpr int NVT = DVT / 16;
-  constexpr int NT = (DK / 16) * NVT;
-  const int l = lane_id();
-  const int col = l & 15, rq = (l >> 4) * 4;
-  for (int tile = wave_id(); tile < NT; tile += 4) {
-    const int dt = tile / NVT, vt = tile % NVT;
-    float* base = sS + (16 * dt + rq) * Ly::SV + 16 * vt + col;
-    floatx4 acc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = lamL * base[i * Ly::SV];
-    // A(m = d, k = key) = K[key][16dt + m];  B(k = key, n) = V[key][16vt + n]
-    acc = wave_mma_f32<CH>(sK + 16 * dt, 1, Ly::SQ, sV + 16 * vt, Ly::SV, 1, acc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) base[i * Ly::SV] = acc[i];
-  }
-}
-
-template <int DK, int DVT, typename TIn>
-__global__ __launch_bounds__(256) void scan_state_kernel(const TIn* __restrict__ k,
-                                                         const TIn* __restrict__ v,
-                                                         const float* __restrict__ lam,
-                                                         const float* __restrict__ eta, int H,
-                                                         int T, int dv, int n_act,
-                                                         int seg_chunks, int n_seg,
-                                                         float* __restrict__ ws) {
-  using Ly = ScanLds<DK, DVT>;
-  __shared__ float sK[CH * Ly::SQ];
-  __shared__ float sV[CH * Ly::SV];
-  __shared__ float sS[DK * Ly::SV];
-  __shared__ float sW[CH];
-
-  const int seg = blockIdx.x, dv0 = blockIdx.y * DVT, bh = blockIdx.z;
-  const int h = bh % H;
-  const float lm = lam[h], et = eta[h];
-  for (int i = threadIdx.x; i < DK * Ly::SV; i += blockDim.x) sS[i] = 0.f;
-
-  const int c_begin = seg * seg_chunks;
-  const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
-  const TIn* kb = k + (long)bh * T * DK;
-  const TIn* vb = v + (long)bh * T * dv;
-  for (int c = c_begin; c < c_end; ++c) {
-    const int s0 = c * CH;
-    const int L = min(CH, n_act - s0);
-    __syncthreads();
-    stage<TIn, DK>(sK, Ly::SQ, kb + (long)s0 * DK, DK, 0, L);
-    stage<TIn, DVT>(sV, Ly::SV, vb + (long)s0 * dv, dv, dv0, L);
-    if (threadIdx.x < CH) sW[threadIdx.x] = threadIdx.x < L ? et * pow_int(lm, L - 1 - threadIdx.x) : 0.f;
-    __syncthreads();
-    for (int i = threadIdx.x; i < CH * DVT; i += blockDim.x) {
-      const int r = i / DVT, cc = i % DVT;
-      sV[r * Ly::SV + cc] *= sW[r];
-    }
-    __syncthreads();
-    state_update<DK, DVT>(sS, sK, sV, pow_int(lm, L));
-  }
-  __syncthreads();
-  float* out = ws + ((long)bh * n_seg + seg) * DK * dv;
-  for (int i = threadIdx.x; i < DK * DVT; i += blockDim.x) {
-    const int r = i / DVT, cc = i % DVT;
-    out[r * dv + dv0 + cc] = sS[r * Ly::SV + cc];
-  }
-}
-
-// Turns per-segment contributions into entering states, in place:
-// entering(0) = 0, entering(p+1) = lam^len(p) entering(p) + delta(p).
-__global__ void scan_prefix_kernel(const float* __restrict__ lam, int H, int n_per_bh, int n_act,
-                                   int seg_len, int n_seg, float* __restrict__ ws) {
-  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const int bh = blockIdx.y;
-  if (idx >= n_per_bh) return;
-  const float lm = lam[bh % H];
-  const float lam_full = pow_int(lm, seg_len);
-  float* p = ws + (long)bh * n_seg * n_per_bh + idx;
-  float run = 0.f;
-  for (int s = 0; s < n_seg - 1; ++s) {
-    const float d = p[(long)s * n_per_bh];
-    p[(long)s * n_per_bh] = run;
-    run = lam_full * run + d;  // every segment but the last is full length
-  }
-  p[(long)(n_seg - 1) * n_per_bh] = run;
-}
-
-template <int DK, int DVT, typename TIn>
-__global__ __launch_bounds__(256) void scan_output_kernel(
-    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ lam, const float* __restrict__ eta, int H, int T, int dv, int W,
-    int n_act, int seg_chunks, int n_seg, const float* __restrict__ ws, float* __restrict__ m,
-    float* __restrict__ A_final) {
-  using Ly = ScanLds<DK, DVT>;
-  __shared__ float sQ[CH * Ly::SQ];
-  __shared__ float sK[CH * Ly::SQ];
-  __shared__ float sV[CH * Ly::SV];
-  __shared__ float sP[CH * Ly::SP];
-  __shared__ float sS[DK * Ly::SV];
-  __shared__ float sW[CH];
-
-  const int seg = blockIdx.x, dv0 = blockIdx.y * DVT, bh = blockIdx.z;
-  const int h = bh % H;
-  const float lm = lam[h], et = eta[h];
-  const int l = lane_id(), w = wave_id();
-  const int col = l & 15, rq = (l >> 4) * 4;
-
-  if (n_seg > 1 && seg > 0) {
-    const float* in = ws + ((long)bh * n_seg + seg) * DK * dv;
-    for (int i = threadIdx.x; i < DK * DVT; i += blockDim.x) {
-      const int r = i / DVT, cc = i % DVT;
-      sS[r * Ly::SV + cc] = in[r * dv + dv0 + cc];
-    }
-  } else {
-    for (int i = threadIdx.x; i < DK * Ly::SV; i += blockDim.x) sS[i] = 0.f;
-  }
-
-  const int c_begin = seg * seg_chunks;
-  const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
-  const TIn* qb = q + (long)bh * T * DK;
-  const TIn* kb = k + (long)bh * T * DK;
-  const TIn* vb = v + (long)bh * T * dv;
-  float* mb = m + (long)bh * T * dv;
-
-  for (int c = c_begin; c < c_end; ++c) {
-    const int s0 = c * CH;
-    const int L = min(CH, n_act - s0);
-    __syncthreads();
-    stage<TIn, DK>(sQ, Ly::SQ, qb + (long)(s0 + W) * DK, DK, 0, L);
-    stage<TIn, DK>(sK, Ly::SQ, kb + (long)s0 * DK, DK, 0, L);
-    stage<TIn, DVT>(sV, Ly::SV, vb + (long)s0 * dv, dv, dv0, L);
-    if (threadIdx.x < CH) sW[threadIdx.x] = threadIdx.x < L ? et * pow_int(lm, L - 1 - threadIdx.x) : 0.f;
-    __syncthreads();
-
-    // P = (Q' K^T) masked to c <= r and weighted by eta lam^(r-c); wave w owns rows 16w..16w+15.
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      floatx4 acc = wave_mma_f32<DK>(sQ + 16 * w * Ly::SQ, Ly::SQ, 1, sK + 16 * ct * Ly::SQ, 1,
-                                     Ly::SQ, zero4());
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + rq + i, cc = 16 * ct + col;
-        sP[r * Ly::SP + cc] = (cc <= r) ? acc[i] * et * pow_int(lm, r - cc) : 0.f;
-      }
-    }
-    __syncthreads();
-
-    // O = diag(lam^(r+1)) Q' S + P V  -> m rows W + s0 + r
-#pragma unroll
-    for (int ct = 0; ct < DVT / 16; ++ct) {
-      floatx4 acc = wave_mma_f32<DK>(sQ + 16 * w * Ly::SQ, Ly::SQ, 1, sS + 16 * ct, Ly::SV, 1,
-                                     zero4());
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= pow_int(lm, 16 * w + rq + i + 1);
-      acc = wave_mma_f32<CH>(sP + 16 * w * Ly::SP, Ly::SP, 1, sV + 16 * ct, Ly::SV, 1, acc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + rq + i;
-        if (r < L) mb[(long)(W + s0 + r) * dv + dv0 + 16 * ct + col] = acc[i];
-      }
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < CH * DVT; i += blockDim.x) {
-      const int r = i / DVT, cc = i % DVT;
-      sV[r * Ly::SV + cc] *= sW[r];
-    }
-    __syncthreads();
-    state_update<DK, DVT>(sS, sK, sV, pow_int(lm, L));
-  }
-
-  if (A_final != nullptr && seg == n_seg - 1) {
-    __syncthreads();
-    float* out = A_final + (long)bh * DK * dv;
-    for (int i = threadIdx.x; i < DK * DVT; i += blockDim.x) {
-      const int r = i / DVT, cc = i % DVT;
-      out[r * dv + dv0 + cc] = sS[r * Ly::SV + cc];
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // d <= 64: one workgroup (4 waves) per (segment, b, h) owns the whole d_v.
@@ -469,13 +257,15 @@ __global__ __launch_bounds__(256) void scan_state_fast(RowView<const TIn> kv_k, 
 // contributions (ws, from scan_state_fast; every segment but the last is
 // seg_chunks chunks long), S_in(s) = sum_{s' < s} lam^(L (s-1-s')) U_s'
 // evaluated as a Horner recurrence; then carry it through the segment's
-// chunks and write m (rows W + s).  The segments also clear rows t < zrows
-// (= min(W, T)) of m between them.
-template <int D, typename TIn>
+// chunks and write m (rows W + s; with ACC, add the read to what m holds).
+// The segments also clear rows t < zrows of m between them.  A_final, when
+// given, receives the final state [d_k][d_v] at a_bh floats per (b, h) and
+// a_rs floats per d_k row.
+template <int D, typename TIn, bool ACC>
 __global__ __launch_bounds__(256) void scan_output_fast(
     RowView<const TIn> vq, RowView<const TIn> vk, RowView<const TIn> vv, const float* __restrict__ lam,
     const float* __restrict__ eta, int H, int n_act, int seg_chunks, int n_seg,
-    const float* __restrict__ ws, RowView<float> vm, int zrows, float* __restrict__ A_final) {
+    const float* __restrict__ ws, RowView<float> vm, int zrows, float* __restrict__ A_final, long a_bh, int a_rs) {
   using F = FastTiles<D>;
   constexpr int NDV = D / 16;
   __shared__ __attribute__((aligned(16))) float sQ[CH * F::S];
@@ -555,13 +345,16 @@ __global__ __launch_bounds__(256) void scan_output_fast(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = 16 * w + 4 * g + e;
-          if (rr < L) vm.row(bh, s0 + rr)[16 * t + r] = o[t][e];
+          if (rr < L) {
+            float* out = vm.row(bh, s0 + rr) + 16 * t + r;
+            *out = ACC ? *out + o[t][e] : o[t][e];
+          }
         }
     }
     fast_state_update<D>(acc, sVt, sKt, sPow[L]);
     publish_state<D>(sSt[cur ^ 1], acc);
   }
-  if (A_final != nullptr && seg == n_seg - 1) store_state<D>(A_final + (long)bh * D * D, acc, D);
+  if (A_final != nullptr && seg == n_seg - 1) store_state<D>(A_final + bh * a_bh, acc, a_rs);
 }
 
 // m rows t < min(W, T) are exactly zero; with no active position the final
@@ -1093,51 +886,57 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   return hipGetLastError();
 }
 
-template <int DK, int DVT, typename TIn>
-hipError_t run_scan(const TIn* q, const TIn* k, const TIn* v, const float* lam, const float* eta,
-                    int B, int H, int T, int dv, int W, float* m, float* A_final, float* ws,
-                    const ScanPlan& p, hipStream_t s) {
+// One d = D read (D <= 64) of columns [0, D) of rows rs floats apart (q, k,
+// v and m point at the first column; A_final at the state block, rows a_rs
+// floats apart).  With ACC the read is added to m's rows t >= W; without, it
+// is written and the rows t < W are cleared.
+template <int D, bool ACC, typename TIn>
+void scan_piece(const TIn* q, const TIn* k, const TIn* v, long rs, const float* lam, const float* eta, int B,
+                int H, int T, int W, float* m, float* A_final, long a_bh, int a_rs, float* ws, const ScanPlan& p,
+                hipStream_t s) {
   const int BH = B * H;
-  const long zrows = std::min<long>(W, T);
-  constexpr bool fast = DK <= 64 && DVT == DK;  // the output kernel clears these rows itself
-  if (zrows > 0 && (!fast || p.n_act <= 0)) {
-    dim3 g((unsigned)std::min<long>((zrows * dv + 255) / 256, 1024), BH);
-    hipLaunchKernelGGL(zero_rows_kernel, g, dim3(256), 0, s, m, zrows, (long)T, dv);
-  }
-  if (p.n_act <= 0) {
+  const long bs = (long)T * rs;
+  const RowView<const TIn> vq{q + (long)W * rs, bs, rs}, vk{k, bs, rs}, vv{v, bs, rs};
+  const RowView<float> vm{m + (long)W * rs, bs, rs};
+  const int zrows = ACC ? 0 : std::min(W, T);
+  if (p.n_seg > 1)
+    hipLaunchKernelGGL((scan_state_fast<D, TIn>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, vk, vv, lam, eta, H,
+                       p.n_act, p.seg_chunks, p.n_seg, ws);
+  hipLaunchKernelGGL((scan_output_fast<D, TIn, ACC>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, vq, vk, vv, lam, eta,
+                     H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, zrows, A_final, a_bh, a_rs);
+}
+
+template <int D, typename TIn>
+hipError_t run_scan(const TIn* q, const TIn* k, const TIn* v, const float* lam, const float* eta, int B, int H,
+                    int T, int W, float* m, float* A_final, float* ws, const ScanPlan& p, hipStream_t s) {
+  const int BH = B * H;
+  if (p.n_act <= 0) {  // no write reaches the memory: m and the final state are zero
+    const long zrows = std::min<long>(W, T);
+    if (zrows > 0) {
+      dim3 g((unsigned)std::min<long>((zrows * D + 255) / 256, 1024), BH);
+      hipLaunchKernelGGL(zero_rows_kernel, g, dim3(256), 0, s, m, zrows, (long)T, D);
+    }
     if (A_final != nullptr) {
-      dim3 g((unsigned)std::min<long>(((long)DK * dv + 255) / 256, 1024), BH);
-      hipLaunchKernelGGL(zero_rows_kernel, g, dim3(256), 0, s, A_final, (long)DK, (long)DK, dv);
+      dim3 g((unsigned)std::min<long>(((long)D * D + 255) / 256, 1024), BH);
+      hipLaunchKernelGGL(zero_rows_kernel, g, dim3(256), 0, s, A_final, (long)D, (long)D, D);
     }
     return hipGetLastError();
   }
-  const int nvt = dv / DVT;
-  if constexpr (DK <= 64 && DVT == DK) {
-    const long bs = (long)T * DK;
-    const RowView<const TIn> vq{q + (long)W * DK, bs, DK}, vk{k, bs, DK}, vv{v, bs, DK};
-    const RowView<float> vm{m + (long)W * DK, bs, DK};
-    if (p.n_seg > 1)
-      hipLaunchKernelGGL((scan_state_fast<DK, TIn>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, vk, vv,
-                         lam, eta, H, p.n_act, p.seg_chunks, p.n_seg, ws);
-    profile_mark_before(s);
-    hipLaunchKernelGGL((scan_output_fast<DK, TIn>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, vq, vk, vv,
-                       lam, eta, H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, (int)zrows, A_final);
-    profile_mark_after(s);
-    return hipGetLastError();
-  }
-  if (p.n_seg > 1) {
-    dim3 g1(p.n_seg - 1, nvt, BH);
-    hipLaunchKernelGGL((scan_state_kernel<DK, DVT, TIn>), g1, dim3(256), 0, s, k, v, lam, eta, H,
-                       T, dv, p.n_act, p.seg_chunks, p.n_seg, ws);
-    const int nel = DK * dv;
-    dim3 g2((nel + 255) / 256, BH);
-    hipLaunchKernelGGL(scan_prefix_kernel, g2, dim3(256), 0, s, lam, H, nel, p.n_act,
-                       p.seg_chunks * CH, p.n_seg, ws);
-  }
-  dim3 g3(p.n_seg, nvt, BH);
   profile_mark_before(s);
-  hipLaunchKernelGGL((scan_output_kernel<DK, DVT, TIn>), g3, dim3(256), 0, s, q, k, v, lam, eta,
-                     H, T, dv, W, p.n_act, p.seg_chunks, p.n_seg, ws, m, A_final);
+  if constexpr (D <= 64) {
+    scan_piece<D, false>(q, k, v, D, lam, eta, B, H, T, W, m, A_final, (long)D * D, D, ws, p, s);
+  } else {
+    // four d = 64 pieces (a, b): q, k columns 64a.., v, m columns 64b.., state block A[64a.., 64b..]
+    for (int a = 0; a < 2; ++a)
+      for (int b = 0; b < 2; ++b) {
+        float* af = A_final != nullptr ? A_final + 64 * a * D + 64 * b : nullptr;
+        if (a == 0)
+          scan_piece<64, false>(q, k, v + 64 * b, D, lam, eta, B, H, T, W, m + 64 * b, af, (long)D * D, D, ws, p, s);
+        else
+          scan_piece<64, true>(q + 64, k + 64, v + 64 * b, D, lam, eta, B, H, T, W, m + 64 * b, af, (long)D * D, D,
+                               ws, p, s);
+      }
+  }
   profile_mark_after(s);
   return hipGetLastError();
 }
@@ -1150,10 +949,10 @@ hipError_t dispatch_scan(const void* q, const void* k, const void* v, const floa
   const TIn* K = static_cast<const TIn*>(k);
   const TIn* V = static_cast<const TIn*>(v);
   switch (d) {
-    case 16: return run_scan<16, 16, TIn>(Q, K, V, lam, eta, B, H, T, d, W, m, A_final, ws, p, s);
-    case 32: return run_scan<32, 32, TIn>(Q, K, V, lam, eta, B, H, T, d, W, m, A_final, ws, p, s);
-    case 64: return run_scan<64, 64, TIn>(Q, K, V, lam, eta, B, H, T, d, W, m, A_final, ws, p, s);
-    case 128: return run_scan<128, 64, TIn>(Q, K, V, lam, eta, B, H, T, d, W, m, A_final, ws, p, s);
+    case 16: return run_scan<16, TIn>(Q, K, V, lam, eta, B, H, T, W, m, A_final, ws, p, s);
+    case 32: return run_scan<32, TIn>(Q, K, V, lam, eta, B, H, T, W, m, A_final, ws, p, s);
+    case 64: return run_scan<64, TIn>(Q, K, V, lam, eta, B, H, T, W, m, A_final, ws, p, s);
+    case 128: return run_scan<128, TIn>(Q, K, V, lam, eta, B, H, T, W, m, A_final, ws, p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1164,8 +963,7 @@ ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int W) {
   ScanPlan p{};
   p.n_act = std::max(T - W, 0);
   p.n_chunks = (p.n_act + CH - 1) / CH;
-  p.dvt = dv > 64 ? 64 : dv;
-  const long units = (long)B * H * (dv / p.dvt);
+  const long units = (long)B * H;  // d = 128: four pieces of this plan, one after another
   // Aim for one round of output workgroups, about one per CU (MI355X: 256
   // CUs): the kernels hold one workgroup per CU and overlap the loads of a
   // chunk with the work on the previous one, so longer segments pay off up
@@ -1177,12 +975,14 @@ ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int W) {
   p.seg_chunks = seg_chunks;
   p.n_seg = p.n_chunks > 0 ? (p.n_chunks + seg_chunks - 1) / seg_chunks : 0;
   (void)dk;
+  (void)dv;
   return p;
 }
 
 size_t scan_ws_bytes(const ScanPlan& p, int B, int H, int dk, int dv) {
   if (p.n_seg <= 1) return 0;
-  return (size_t)B * H * p.n_seg * dk * dv * sizeof(float);
+  const int pk = std::min(dk, 64), pv = std::min(dv, 64);  // d = 128: one d = 64 piece at a time
+  return (size_t)B * H * p.n_seg * pk * pv * sizeof(float);
 }
 
 hipError_t launch_tc_scan(const void* q, const void* k, const void* v, bool bf16,

@@ -36,7 +36,7 @@ def test_fused_layer_repeat(B, H, T, d, W):
 
 @pytest.mark.parametrize("dtype,B,H,T,d,W", [
     ("f32", 4, 8, 4096, 64, 512),     # segmented fp32 MFMA scan
-    ("f32", 1, 4, 2000, 128, 100),    # d = 128 fp32 kernels
+    ("f32", 1, 4, 2000, 128, 100),    # d = 128 fp32: four d = 64 pieces
     ("bf16", 1, 16, 8192, 128, 1024),  # pre-pass + prefix + L2-read kernel
     ("bf16", 2, 4, 3000, 32, 64),     # bf16 inputs on the d <= 64 kernels
 ])
@@ -107,7 +107,7 @@ def test_decode_repeat(layer, dtype):
             same_bits(name, a, b)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 16)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("f32", 128), ("bf16", 16)])
 def test_window_and_fp32_layer_repeat(dtype, d):
     B, H, T, W = 1, 4, 2000, 300
     print(f"[case] window / layer repeat {dtype} d={d}", flush=True)

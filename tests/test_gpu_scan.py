@@ -30,7 +30,10 @@ def lam_of(x):
     (1, 1, 256, 16, 32),        # the tiny single-head workload shape
     (2, 3, 300, 32, 17),        # several chunks, ragged tail
     (1, 2, 1000, 64, 100),      # many segments
-    (2, 2, 777, 128, 64),       # d=128 with two d_v tiles
+    (2, 2, 777, 128, 64),       # d=128 (fp32: four d=64 pieces, the second column half of q, k added)
+    (1, 2, 3000, 128, 200),     # d=128, many segments per piece
+    (1, 2, 130, 128, 1),        # d=128, W = 1
+    (1, 1, 40, 128, 100),       # d=128, T < W: m and the final state are zero
     (1, 1, 64 + 10, 64, 10),    # exactly one full chunk of active rows
     (1, 2, 40, 16, 1),          # W = 1
     (1, 1, 30, 16, 30),         # T == W: nothing is evicted
