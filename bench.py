@@ -42,7 +42,7 @@ def parse():
                     help="decode steps to time (default: the workload's 4096; 1024 for the 4x side run); "
                          "short runs are for profiler counter passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fused", "scan", "scan_bf16", "scan_backward", "layer_backward", "decode", "decode_x4", "decode_layer", "delta",
+    ap.add_argument("--only", choices=["fused", "fused_f32", "scan", "scan_bf16", "scan_backward", "layer_backward", "decode", "decode_x4", "decode_layer", "delta",
                                            "delta_f32", "delta_backward", "hebbian", "capacity"], default=None,
                     help="time a single entry point (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -373,6 +373,58 @@ def bench_fused(steps, warmup, dev):
                          "not named; context only, not comparable with a kernel timing",
     }
     return res, x
+
+
+def window_flops(B, H, T, d, W):
+    """The window softmax alone: 4 d flops per (query, key) pair inside the window."""
+    pairs = sum(min(W, t + 1) for t in range(min(T, W))) + max(T - W, 0) * W
+    return B * H * 4 * d * pairs
+
+
+def bench_fused_f32(steps, warmup, dev, x=None):
+    """The fused layer with fp32 inputs at the headline shape (the bf16
+    workload's values, held in fp32): the four-piece fp32 prefill scan, then
+    the fp32-MFMA window softmax with the gate; and the window alone."""
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["fused_layer_bf16"]
+    if x is None:
+        x = I.draw_workload("fused_layer_bf16")
+    q, k, v = (to_dev_f32(x[n + "64"], dev) for n in ("q", "k", "v"))
+    lam, eta, g = (to_dev_f32(x[n], dev) for n in ("lam", "eta", "g"))
+    y = torch.empty((w.B, w.H, w.T, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ops.fused_workspace(w.B, w.H, w.T, w.d, w.d, w.W, 0), 1), dtype=torch.uint8, device=dev)
+    lib = ops.lib()
+    st = ops._stream()
+    scale = 1.0 / math.sqrt(w.d)
+    largs = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, ops._ptr(lam), ops._ptr(eta), ops._ptr(g),
+             w.B, w.H, w.T, w.d, w.d, w.W, 64, scale, ops._ptr(y), None, ops._ptr(ws), ws.numel(), st)
+    wargs = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, w.B, w.H, w.T, w.d, w.d, w.W, scale, ops._ptr(y), st)
+
+    def call_layer(_):
+        if lib.tc_fused_layer(*largs) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    def call_window(_):
+        if lib.tc_window_attention(*wargs) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, _ = time_calls(call_layer, steps, warmup)
+    _, ms_window, kernel_ms = time_calls(call_window, steps, warmup, KernelTimer(steps))
+    wf = window_flops(w.B, w.H, w.T, w.d, w.W)
+    flops = fused_flops(w.B, w.H, w.T, w.d, w.W)
+    return {"workload": "fused_layer_f32", "ms_per_step": ms, "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
+            "ms_per_call": ms_call,
+            "roofline": dict(roofline("mfma", wf / (kernel_ms * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
+                             scope="window_kernel<float, 128> alone (tc_window_attention, fp32): its algorithmic "
+                                   "flops / its own event-timed duration"),
+            "layer_tflops": flops / (ms_call * 1e-3) / 1e12,
+            "main_kernel": {"name": "window_kernel<float, 128>", "ms": kernel_ms, "algorithmic_flops": wf},
+            "window_only_ms_per_call": ms_window,
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
 
 
 def bench_scan(steps, warmup, dev):
@@ -899,6 +951,7 @@ def main():
     if only in (None, "fused"):
         head, x = bench_fused(args.steps, args.warmup, dev)
     if only is None and not args.no_components:
+        components["fused_layer_f32"] = bench_fused_f32(args.steps, args.warmup, dev, x)
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
         components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
         components["fused_layer_backward_bf16"] = bench_layer_backward(args.steps, args.warmup, dev, x)
@@ -913,6 +966,8 @@ def main():
         components["delta_backward_bf16"] = bench_delta_backward(args.steps, args.warmup, dev, "delta_scan_bf16", True)
         components["hebbian_f32"] = bench_hebbian(args.steps, args.warmup, dev)
         components["capacity_diagnostic"] = bench_capacity(dev)
+    elif only == "fused_f32":
+        components["fused_layer_f32"] = bench_fused_f32(args.steps, args.warmup, dev)
     elif only == "scan":
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
     elif only == "scan_bf16":
