@@ -73,6 +73,7 @@ def test_fused_layer_full_size_sampled_rows_and_a_whole_head():
     ("f32", 2, 3, 300, 32, 17),
     ("f32", 1, 2, 1000, 64, 100),
     ("f32", 1, 1, 300, 128, 64),
+    ("f32", 1, 2, 1100, 128, 333),  # the four-piece scan and several window tiles per head
     ("f32", 1, 2, 40, 16, 100),     # T < W: the L2 memory stays empty
     ("bf16", 1, 2, 300, 16, 40),
     ("bf16", 2, 1, 257, 32, 64),

@@ -33,6 +33,8 @@ def run(x, W, scale=None):
     ("f32", 1, 2, 500, 64, 100),
     ("f32", 1, 1, 200, 128, 300),
     ("f32", 1, 2, 130, 64, 1),
+    ("f32", 2, 2, 1000, 128, 300),    # several 128-query tiles per head, W not a multiple of the 32-key block
+    ("f32", 1, 3, 777, 16, 1500),     # W > T: causal softmax over the whole prefix
 ])
 def test_window_small(dtype, B, H, T, d, W):
     print(f"[case] window {dtype} B={B} H={H} T={T} d={d} W={W}", flush=True)
@@ -42,7 +44,7 @@ def test_window_small(dtype, B, H, T, d, W):
     check("y", y, ref, TOL[dtype])
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 32), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 32), ("bf16", 16), ("f32", 16), ("f32", 64), ("f32", 128)])
 def test_window_one_token_returns_v(dtype, d):
     # W = 1: each query sees only its own token, whose softmax weight is 1
     x = I.draw(1, 2, 150, d, seed=71, dtype=dtype)
