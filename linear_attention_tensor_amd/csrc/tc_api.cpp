@@ -229,24 +229,9 @@ static tc_status check_scan_bwd(const char* fn, int B, int H, int T, int dk, int
 // (rows 128 floats apart) and add into the halves of the outputs, so the
 // workspace is the d = 64 backward's (plus the widened copies for bf16).
 static size_t scan_bwd_need(int B, int H, int T, int d, int W, tc_dtype dt) {
-  if (d == 128)
-    return (dt == TC_BF16 ? 3 * widened_bytes(B, H, T, d) : 0) + round_up_256(tc::scan_bwd_ws_bytes(B, H, T, 64, W));
   const size_t base = tc::scan_bwd_ws_bytes(B, H, T, d, W);
+  if (d == 128) return (dt == TC_BF16 ? 3 * widened_bytes(B, H, T, d) : 0) + round_up_256(base);
   return dt == TC_BF16 ? round_up_256(base) + 3 * widened_bytes(B, H, T, d) : base;
-}
-
-static hipError_t scan_backward_128(const float* q, const float* k, const float* v, const float* lam, const float* eta,
-                                    const float* g, int B, int H, int T, int W, const float* dm, float* dq, float* dk,
-                                    float* dv, float* dlam, float* deta, float* dg, char* w, hipStream_t s) {
-  hipError_t e = hipSuccess;
-  for (int a = 0; a < 2 && e == hipSuccess; ++a) {
-    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
-      const tc::ScanBwdPiece pc{128, b != 0, a != 0, a != 0 || b != 0};
-      e = tc::launch_tc_scan_backward(q + 64 * a, k + 64 * a, v + 64 * b, lam, eta, g, B, H, T, 64, W, dm + 64 * b,
-                                      dq + 64 * a, dk + 64 * a, dv + 64 * b, dlam, deta, dg, w, s, &pc);
-    }
-  }
-  return e;
 }
 
 size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk,
@@ -278,7 +263,7 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
     if (need > 0 && !ws) return fail(TC_ERR_INVALID_ARG, "%s: ws must not be NULL", fn);
     const float *q32 = static_cast<const float*>(q), *k32 = static_cast<const float*>(k),
                 *v32 = static_cast<const float*>(v);
-    // d = 128: the widened copies come first, then the d = 64 workspace of scan_backward_128
+    // d = 128: the widened copies come first, then the workspace of the four-piece backward
     const size_t wide_off = dk == 128 ? 0 : round_up_256(tc::scan_bwd_ws_bytes(B, H, T, dk, W));
     if (dt == TC_BF16 && T > 0) {
       char* wide = static_cast<char*>(ws) + wide_off;
@@ -295,8 +280,8 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
     }
     if (dk == 128) {
       char* w = static_cast<char*>(ws) + (dt == TC_BF16 ? 3 * widened_bytes(B, H, T, dk) : 0);
-      return from_hip(scan_backward_128(q32, k32, v32, lam, eta, g, B, H, T, W, dm, dq, dk_out, dv_out, dlam, deta, dg,
-                                        w, s),
+      return from_hip(tc::launch_tc_scan_backward(q32, k32, v32, lam, eta, g, B, H, T, 128, W, dm, dq, dk_out,
+                                                  dv_out, dlam, deta, dg, w, s),
                       fn);
     }
     return from_hip(tc::launch_tc_scan_backward(q32, k32, v32, lam, eta, g, B, H, T, dk, W, dm, dq, dk_out,

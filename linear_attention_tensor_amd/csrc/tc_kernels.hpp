@@ -20,22 +20,13 @@ struct ScanPlan {
 };
 ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int W);
 size_t scan_ws_bytes(const ScanPlan& p, int B, int H, int dk, int dv);
-// Backward of the read (fp32 inputs, d = dk = dv in {16, 32, 64}).
+// Backward of the read (fp32 inputs, d = dk = dv in {16, 32, 64, 128}; d = 128
+// runs as four d = 64 pieces over the column halves).
 size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W);
-// One piece of a wider backward: the d columns of q, k, v, dm, dq, dk, dv
-// sit in rows rs floats apart (the pointers point at the piece's first
-// column); add_qk / add_v / add_h add dq and dk / dv / dlam, deta, dg to what
-// the buffers hold instead of writing them (and leave the rows that no
-// position writes alone).  nullptr: rows of d floats, everything written.
-struct ScanBwdPiece {
-  int rs;
-  bool add_qk, add_v, add_h;
-};
 hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
                                    const float* eta, const float* g, int B, int H, int T, int d, int W,
                                    const float* dm, float* dq, float* dk, float* dv, float* dlam,
-                                   float* deta, float* dg, void* ws, hipStream_t s,
-                                   const ScanBwdPiece* piece = nullptr);
+                                   float* deta, float* dg, void* ws, hipStream_t s);
 
 // bf16 -> fp32 of n elements (tc_convert.hip); any alignment, any n.
 hipError_t launch_widen_bf16(const void* in, float* out, long n, hipStream_t s);

@@ -212,18 +212,42 @@ __device__ __forceinline__ void store_state(float* dst, const floatx4* acc, int 
   }
 }
 
+// Up to four d = 64 pieces of a d = 128 problem in one launch (grid z =
+// n (B H)): piece i = blockIdx.z / (B H) reads its first array from column
+// xo[i] and its second from column yo[i] of the rows, and writes its segment
+// contributions ws_stride floats after piece i - 1's.  One piece: n = 1,
+// offsets 0.
+struct Pieces {
+  int n;
+  int xo[4], yo[4];
+  long ws_stride;
+};
+constexpr Pieces kOnePiece{1, {0, 0, 0, 0}, {0, 0, 0, 0}, 0};
+__device__ __forceinline__ int piece_index(const Pieces& pc, int& bh) {
+  const int bht = gridDim.z / pc.n;
+  bh = blockIdx.z % bht;
+  return blockIdx.z / bht;
+}
+template <typename TP>
+__device__ __forceinline__ RowView<TP> shift(RowView<TP> v, int cols) {
+  return RowView<TP>{v.base + cols, v.bh_stride, v.rs};
+}
+
 // Per-(segment, b, h) state contribution from zero (all segments but the last).
 template <int D, typename TIn>
-__global__ __launch_bounds__(256) void scan_state_fast(RowView<const TIn> kv_k, RowView<const TIn> kv_v,
+__global__ __launch_bounds__(256) void scan_state_fast(RowView<const TIn> kv_k0, RowView<const TIn> kv_v0,
                                                        const float* __restrict__ lam,
                                                        const float* __restrict__ eta, int H,
                                                        int n_act, int seg_chunks, int n_seg,
-                                                       float* __restrict__ ws) {
+                                                       float* __restrict__ ws, Pieces pcs) {
   using F = FastTiles<D>;
   __shared__ __attribute__((aligned(16))) float sKt[D * F::ST];
   __shared__ __attribute__((aligned(16))) float sVt[D * F::ST];
   __shared__ float sW[CH];
-  const int seg = blockIdx.x, bh = blockIdx.z;
+  int bh;
+  const int pi = piece_index(pcs, bh), seg = blockIdx.x;
+  const RowView<const TIn> kv_k = shift(kv_k0, pcs.xo[pi]), kv_v = shift(kv_v0, pcs.yo[pi]);
+  ws += pi * pcs.ws_stride;
   const float lm = lam[bh % H], et = eta != nullptr ? eta[bh % H] : 1.f;  // NULL: eta = 1
   const int c_begin = seg * seg_chunks;
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
@@ -456,16 +480,20 @@ __device__ __forceinline__ void publish_state_t(float* sS, const floatx4* acc) {
 // Per (segment, b, h) but the last: the segment's own state U and its lam
 // derivative U' from zero (eta = 1).
 template <int D>
-__global__ __launch_bounds__(256) void scan_dstate_fast(RowView<const float> vk, RowView<const float> vv,
+__global__ __launch_bounds__(256) void scan_dstate_fast(RowView<const float> vk0, RowView<const float> vv0,
                                                         const float* __restrict__ lam, int H, int n_act,
                                                         int seg_chunks, int n_seg, float* __restrict__ ws,
-                                                        float* __restrict__ dws) {
+                                                        float* __restrict__ dws, Pieces pcs) {
   using F = FastTiles<D>;
   __shared__ __attribute__((aligned(16))) float sKt[D * F::ST];
   __shared__ __attribute__((aligned(16))) float sVw[D * F::ST];
   __shared__ __attribute__((aligned(16))) float sVd[D * F::ST];
   __shared__ float sW[CH], sWd[CH];
-  const int seg = blockIdx.x, bh = blockIdx.z;
+  int bh;
+  const int pi = piece_index(pcs, bh), seg = blockIdx.x;
+  const RowView<const float> vk = shift(vk0, pcs.xo[pi]), vv = shift(vv0, pcs.yo[pi]);
+  ws += pi * pcs.ws_stride;
+  dws += pi * pcs.ws_stride;
   const float lm = lam[bh % H];
   const int c_begin = seg * seg_chunks;
   const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
@@ -833,11 +861,28 @@ __global__ void scan_bwd_reduce(const double* __restrict__ part_eta, const doubl
   }
 }
 
+// One piece of a wider backward: the d columns of q, k, v, dm, dq, dk, dv sit
+// in rows rs floats apart (the pointers point at the piece's first column);
+// add_qk / add_v / add_h add dq and dk / dv / dlam, deta, dg to what the
+// buffers hold instead of writing them (and leave the rows that no position
+// writes alone).
+struct ScanBwdPiece {
+  int rs;
+  bool add_qk, add_v, add_h;
+};
+
+// Segment contributions a d = 128 backward computes for its four pieces in
+// one launch each (nullptr: the piece computes its own): the forward
+// direction's state and lam derivative, and the reverse direction's state.
+struct BwdStates {
+  const float *fs, *fd, *rs;
+};
+
 template <int D>
 hipError_t run_scan_backward(const float* q, const float* k, const float* v, const float* lam,
                              const float* eta, const float* gate, int B, int H, int T, int W, const float* dm,
                              float* dq, float* dk, float* dv, float* dlam, float* deta, float* dgate,
-                             char* ws, hipStream_t s, const ScanBwdPiece& pc) {
+                             char* ws, hipStream_t s, const ScanBwdPiece& pc, const BwdStates& pre) {
   const int BH = B * H;
   const ScanPlan p = plan_scan(B, H, T, D, D, W);
   const int n_act = p.n_act;
@@ -863,27 +908,72 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   // forward direction: dq, deta, dlam
   const RowView<const float> fq{q + (long)W * rs, bs, rs}, fk{k, bs, rs}, fv{v, bs, rs},
       fg{dm + (long)W * rs, bs, rs};
-  if (p.n_seg > 1)
+  if (p.n_seg > 1 && pre.fs == nullptr)
     hipLaunchKernelGGL((scan_dstate_fast<D>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, fk, fv, lam, H,
-                       n_act, p.seg_chunks, p.n_seg, sws, dws);
+                       n_act, p.seg_chunks, p.n_seg, sws, dws, kOnePiece);
   profile_mark_before(s);
   hipLaunchKernelGGL((scan_bwd_fwd_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, fq, fk, fv, fg, lam,
-                     eta, H, n_act, p.seg_chunks, p.n_seg, sws, dws, gate,
+                     eta, H, n_act, p.seg_chunks, p.n_seg, pre.fs ? pre.fs : sws, pre.fd ? pre.fd : dws, gate,
                      RowView<float>{dq + (long)W * rs, bs, rs}, (int)zq, part_eta, part_lam, pc.add_qk);
   profile_mark_after(s);
   // reverse direction: dk, dv (row r of each view is position n_act - 1 - r)
   const long last = (long)(n_act - 1) * rs, tl = (long)(T - 1) * rs;
   const RowView<const float> rv{v + last, bs, -rs}, rk{k + last, bs, -rs}, rq{q + tl, bs, -rs},
       rg{dm + tl, bs, -rs};
-  if (p.n_seg > 1)
+  if (p.n_seg > 1 && pre.rs == nullptr)
     hipLaunchKernelGGL((scan_state_fast<D, float>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, rg, rq, lam,
-                       nullptr, H, n_act, p.seg_chunks, p.n_seg, sws);
+                       nullptr, H, n_act, p.seg_chunks, p.n_seg, sws, kOnePiece);
   hipLaunchKernelGGL((scan_bwd_rev_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, rv, rk, rq, rg, lam, eta,
-                     H, n_act, p.seg_chunks, p.n_seg, sws, gate, RowView<float>{dk + last, bs, -rs},
+                     H, n_act, p.seg_chunks, p.n_seg, pre.rs ? pre.rs : sws, gate, RowView<float>{dk + last, bs, -rs},
                      RowView<float>{dv + last, bs, -rs}, T - n_act, pc.add_qk, pc.add_v);
   hipLaunchKernelGGL(scan_bwd_reduce, dim3((H + 63) / 64), dim3(64), 0, s, part_eta, part_lam, eta, gate, B,
                      H, p.n_seg, dlam, deta, dgate, pc.add_h);
   return hipGetLastError();
+}
+
+// d = 128 as four d = 64 pieces (a, b): the read's gradients split over the
+// column halves like the read itself, piece (a, b) taking q, k columns 64 a..
+// and v, dm columns 64 b..; it adds to dq, dk (b = 1 after b = 0 wrote them),
+// dv (a = 1 after a = 0) and the per-head sums.  The segment contributions of
+// all four pieces come first, one launch per kind (workspace: the shares |
+// forward states | their lam derivatives | reverse states, four pieces each).
+hipError_t run_scan_backward_128(const float* q, const float* k, const float* v, const float* lam, const float* eta,
+                                 const float* gate, int B, int H, int T, int W, const float* dm, float* dq, float* dk,
+                                 float* dv, float* dlam, float* deta, float* dgate, char* ws, hipStream_t s) {
+  constexpr int D = 128, PD = 64;
+  const int BH = B * H;
+  const ScanPlan p = plan_scan(B, H, T, PD, PD, W);
+  BwdStates pre{nullptr, nullptr, nullptr};
+  if (p.n_act > 0 && p.n_seg > 1) {
+    const size_t part = scan_bwd_part_bytes(B, H, p.n_seg), region = scan_ws_bytes(p, B, H, D, D);
+    float* fs = reinterpret_cast<float*>(ws + part);
+    float* fd = reinterpret_cast<float*>(ws + part + region);
+    float* rs = reinterpret_cast<float*>(ws + part + 2 * region);
+    const long stride = (long)BH * p.n_seg * PD * PD;  // floats per piece
+    const long bs = (long)T * D;
+    // piece i = 2 a + b
+    const Pieces fwd{4, {0, 0, 64, 64}, {0, 64, 0, 64}, stride};  // k columns 64 a, v columns 64 b
+    const Pieces rev{4, {0, 64, 0, 64}, {0, 0, 64, 64}, stride};  // dm columns 64 b, q columns 64 a
+    const RowView<const float> fk{k, bs, D}, fv{v, bs, D};
+    hipLaunchKernelGGL((scan_dstate_fast<PD>), dim3(p.n_seg - 1, 1, 4 * BH), dim3(256), 0, s, fk, fv, lam, H,
+                       p.n_act, p.seg_chunks, p.n_seg, fs, fd, fwd);
+    const long tl = (long)(T - 1) * D;
+    const RowView<const float> rg{dm + tl, bs, -D}, rq{q + tl, bs, -D};
+    hipLaunchKernelGGL((scan_state_fast<PD, float>), dim3(p.n_seg - 1, 1, 4 * BH), dim3(256), 0, s, rg, rq, lam,
+                       nullptr, H, p.n_act, p.seg_chunks, p.n_seg, rs, rev);
+    pre = BwdStates{fs, fd, rs};
+  }
+  hipError_t e = hipSuccess;
+  for (int a = 0; a < 2 && e == hipSuccess; ++a)
+    for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+      const int i = 2 * a + b;
+      const long off = (long)i * BH * p.n_seg * PD * PD;
+      const BwdStates pi = pre.fs ? BwdStates{pre.fs + off, pre.fd + off, pre.rs + off} : pre;
+      const ScanBwdPiece pc{D, b != 0, a != 0, i != 0};  // dq_a, dk_a: two b; dv_b: two a
+      e = run_scan_backward<PD>(q + 64 * a, k + 64 * a, v + 64 * b, lam, eta, gate, B, H, T, W, dm + 64 * b,
+                                dq + 64 * a, dk + 64 * a, dv + 64 * b, dlam, deta, dgate, ws, s, pc, pi);
+    }
+  return e;
 }
 
 // One d = D read (D <= 64) of columns [0, D) of rows rs floats apart (q, k,
@@ -893,15 +983,15 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
 template <int D, bool ACC, typename TIn>
 void scan_piece(const TIn* q, const TIn* k, const TIn* v, long rs, const float* lam, const float* eta, int B,
                 int H, int T, int W, float* m, float* A_final, long a_bh, int a_rs, float* ws, const ScanPlan& p,
-                hipStream_t s) {
+                hipStream_t s, bool states_ready = false) {
   const int BH = B * H;
   const long bs = (long)T * rs;
   const RowView<const TIn> vq{q + (long)W * rs, bs, rs}, vk{k, bs, rs}, vv{v, bs, rs};
   const RowView<float> vm{m + (long)W * rs, bs, rs};
   const int zrows = ACC ? 0 : std::min(W, T);
-  if (p.n_seg > 1)
+  if (p.n_seg > 1 && !states_ready)
     hipLaunchKernelGGL((scan_state_fast<D, TIn>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, vk, vv, lam, eta, H,
-                       p.n_act, p.seg_chunks, p.n_seg, ws);
+                       p.n_act, p.seg_chunks, p.n_seg, ws, kOnePiece);
   hipLaunchKernelGGL((scan_output_fast<D, TIn, ACC>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, vq, vk, vv, lam, eta,
                      H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, zrows, A_final, a_bh, a_rs);
 }
@@ -926,15 +1016,26 @@ hipError_t run_scan(const TIn* q, const TIn* k, const TIn* v, const float* lam, 
   if constexpr (D <= 64) {
     scan_piece<D, false>(q, k, v, D, lam, eta, B, H, T, W, m, A_final, (long)D * D, D, ws, p, s);
   } else {
-    // four d = 64 pieces (a, b): q, k columns 64a.., v, m columns 64b.., state block A[64a.., 64b..]
+    // four d = 64 pieces (a, b): q, k columns 64a.., v, m columns 64b.., state block A[64a.., 64b..];
+    // the segment contributions of all four in one launch first (piece i = 2 a + b)
+    const long stride = (long)BH * p.n_seg * 64 * 64;
+    if (p.n_seg > 1) {
+      const long bs = (long)T * D;
+      const RowView<const TIn> vk{k, bs, D}, vv{v, bs, D};
+      const Pieces pcs{4, {0, 0, 64, 64}, {0, 64, 0, 64}, stride};
+      hipLaunchKernelGGL((scan_state_fast<64, TIn>), dim3(p.n_seg - 1, 1, 4 * BH), dim3(256), 0, s, vk, vv, lam,
+                         eta, H, p.n_act, p.seg_chunks, p.n_seg, ws, pcs);
+    }
     for (int a = 0; a < 2; ++a)
       for (int b = 0; b < 2; ++b) {
         float* af = A_final != nullptr ? A_final + 64 * a * D + 64 * b : nullptr;
+        float* wsi = ws + (2 * a + b) * stride;
         if (a == 0)
-          scan_piece<64, false>(q, k, v + 64 * b, D, lam, eta, B, H, T, W, m + 64 * b, af, (long)D * D, D, ws, p, s);
+          scan_piece<64, false>(q, k, v + 64 * b, D, lam, eta, B, H, T, W, m + 64 * b, af, (long)D * D, D, wsi, p, s,
+                                true);
         else
           scan_piece<64, true>(q + 64, k + 64, v + 64 * b, D, lam, eta, B, H, T, W, m + 64 * b, af, (long)D * D, D,
-                               ws, p, s);
+                               wsi, p, s, true);
       }
   }
   profile_mark_after(s);
@@ -981,8 +1082,7 @@ ScanPlan plan_scan(int B, int H, int T, int dk, int dv, int W) {
 
 size_t scan_ws_bytes(const ScanPlan& p, int B, int H, int dk, int dv) {
   if (p.n_seg <= 1) return 0;
-  const int pk = std::min(dk, 64), pv = std::min(dv, 64);  // d = 128: one d = 64 piece at a time
-  return (size_t)B * H * p.n_seg * pk * pv * sizeof(float);
+  return (size_t)B * H * p.n_seg * dk * dv * sizeof(float);  // d = 128: the four d = 64 pieces' contributions
 }
 
 hipError_t launch_tc_scan(const void* q, const void* k, const void* v, bool bf16,
@@ -1002,19 +1102,22 @@ namespace tc {
 
 size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W) {
   const ScanPlan p = plan_scan(B, H, T, d, d, W);
-  return scan_bwd_part_bytes(B, H, p.n_seg) + 2 * scan_ws_bytes(p, B, H, d, d);
+  // d = 128: forward states, their lam derivatives and reverse states of the four pieces
+  return scan_bwd_part_bytes(B, H, p.n_seg) + (d == 128 ? 3 : 2) * scan_ws_bytes(p, B, H, d, d);
 }
 
 hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
                                    const float* eta, const float* g, int B, int H, int T, int d, int W,
                                    const float* dm, float* dq, float* dk, float* dv, float* dlam,
-                                   float* deta, float* dg, void* ws, hipStream_t s, const ScanBwdPiece* piece) {
+                                   float* deta, float* dg, void* ws, hipStream_t s) {
   char* w = static_cast<char*>(ws);
-  const ScanBwdPiece pc = piece ? *piece : ScanBwdPiece{d, false, false, false};
+  const ScanBwdPiece pc{d, false, false, false};
+  const BwdStates none{nullptr, nullptr, nullptr};
   switch (d) {
-    case 16: return run_scan_backward<16>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc);
-    case 32: return run_scan_backward<32>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc);
-    case 64: return run_scan_backward<64>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc);
+    case 16: return run_scan_backward<16>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc, none);
+    case 32: return run_scan_backward<32>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc, none);
+    case 64: return run_scan_backward<64>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc, none);
+    case 128: return run_scan_backward_128(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s);
     default: return hipErrorInvalidValue;
   }
 }

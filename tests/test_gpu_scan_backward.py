@@ -47,6 +47,7 @@ def check_case(x, W, dm, label):
     (1, 2, 700, 128, 60),       # d = 128: four d = 64 pieces, gradients added
     (2, 1, 150, 128, 149),      # d = 128, one eviction
     (1, 1, 90, 128, 100),       # d = 128, T < W
+    (2, 2, 1500, 128, 200),     # d = 128, many segments: the four pieces' segment states in one launch per kind
 ])
 def test_scan_backward_small(B, H, T, d, W):
     print(f"[case] scan backward B={B} H={H} T={T} d={d} W={W}", flush=True)
