@@ -8,17 +8,27 @@
 //   dv_j = sum_t p_tj dy_t,
 //   ds_tj = p_tj (<dy_t, v_j> - D_t),
 //   dq_t = scale sum_j ds_tj k_j,   dk_j = scale sum_t ds_tj q_t.
-// Three launches: (1) per query the log-sum-exp of its scores and D_t
-// (recomputing y_t); (2) dq per query over its window; (3) dk, dv per key over
-// the W queries that see it, with p_tj = exp(s_tj - lse_t).  (2) and (3) can
-// add to what the output buffers hold (the fused layer's backward adds the
-// L2 branch this way).
 //
-// Four consecutive lanes share a row (a query or a key): lane c of the quad
-// holds the features 4 i + c, so a quad reads 4 consecutive floats of an LDS
-// row and full dot products come from two xor-shuffles.  Partner rows pass
-// through LDS in blocks of 64, row stride D + 4 floats, so the 16 quads of a
-// wave on 16 different rows hit 16 different 4-bank groups.
+// Every product is a dense fp32 contraction and runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: A(m, k) from lane m + 16 k, B(k, n) from lane
+// n + 16 k, D(m, n) in lane n + 16 (m / 4), element m % 4).  A wave owns 16
+// rows (queries, or keys); its partner rows pass through LDS in blocks of 32
+// (fp32, row stride D + 4 floats, double-buffered, the next block in
+// registers meanwhile).  The k order of the D-long dot products is permuted
+// so that lane group g takes the features g D/4 .. g D/4 + D/4 - 1 (one
+// 16-byte LDS read feeds four MFMAs).  A score tile leaves lane (g, n) with
+// row n and partner rows 4 g + e (e < 4), which are exactly the k rows lane
+// (g, n) supplies to a product over the partner rows at k-step e: the
+// probabilities and ds feed the next products from their registers.
+//   (1) per 128 queries (8 waves x 16): pass 1 over the key blocks forms the
+//       softmax of the scores (scaled by scale log2 e) and y, and writes
+//       lse2_t (log2 of the normaliser, in those units) and D_t = <dy_t, y_t>;
+//       pass 2 forms p = 2^(s - lse2), dp = <dy_t, v_j>, ds = p (dp - D_t) and
+//       dq^T += K^T ds^T.
+//   (2) per 128 keys (8 waves x 16): over the query blocks that see them,
+//       s and dp as above (transposed), dv^T += dY^T p, dk^T += Q^T ds.
+// (1) and (2) can add to what the output buffers hold (the fused layer's
+// backward adds the L2 branch this way).
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
 
@@ -28,211 +38,382 @@ namespace tc {
 
 namespace {
 
-constexpr int BR = 64;  // rows (queries or keys) per workgroup
-constexpr int BP = 64;  // partner rows per LDS block
+constexpr int NW = 8;               // waves per workgroup
+constexpr int NT = 64 * NW;         // threads per workgroup
+constexpr int RB = 16 * NW;         // rows (queries or keys) per workgroup
+constexpr int PB = 32;              // partner rows per LDS block
+constexpr int NXCD = 8;             // MI355X: 8 accelerator complex dies, workgroups dispatched round-robin
+constexpr float kNegBig = -1.0e30f;
 
-__device__ __forceinline__ float quad_sum(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  return x;
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ld4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
+// max / sum over the four lane groups (lanes n, n + 16, n + 32, n + 48)
+__device__ __forceinline__ float max_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
 }
 
-template <typename TIn, int D>
-__device__ __forceinline__ void load_row_part(const TIn* p, long row, int c, bool live, float* r) {
+// Rows r0 .. r0 + 31 of two [T][D] arrays (zero past T) through registers into
+// an LDS stage (row stride D + 4).
+template <typename TA, typename TB, int D>
+struct Block2 {
+  static constexpr int S = D + 4;
+  static constexpr int NP = 8 * D;             // float4 pieces per array and block
+  static constexpr int NLD = (NP + NT - 1) / NT;
+  float4 ra[NLD], rb[NLD];
+  __device__ __forceinline__ void load(const TA* a, const TB* b, long base, int r0, int T) {
 #pragma unroll
-  for (int i = 0; i < D / 4; ++i) r[i] = live ? InT<TIn>::ld(p, row * D + 4 * i + c) : 0.f;
-}
-
-// LDS block of up to BP rows of one or two tensors (fp32, padded stride)
-template <int D>
-struct RowBlock {
-  float a[BP][D + 4];
-  float b[BP][D + 4];
+    for (int i = 0; i < NLD; ++i) {
+      const int f = threadIdx.x + NT * i, row = f / (D / 4), c4 = f % (D / 4);
+      const bool in = (NP % NT == 0 || f < NP) && r0 + row < T;
+      const long off = (base + r0 + row) * D + 4 * c4;
+      ra[i] = in ? ld4(a + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+      rb[i] = in ? ld4(b + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  __device__ __forceinline__ void store(float* sa, float* sb) const {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int f = threadIdx.x + NT * i, row = f / (D / 4), c4 = f % (D / 4);
+      if (NP % NT == 0 || f < NP) {
+        *reinterpret_cast<float4*>(sa + row * S + 4 * c4) = ra[i];
+        *reinterpret_cast<float4*>(sb + row * S + 4 * c4) = rb[i];
+      }
+    }
+  }
 };
 
-template <typename TIn, int D, bool TWO>
-__device__ __forceinline__ void stage(RowBlock<D>& blk, const TIn* pa, const TIn* pb, long base, int r0, int r_hi) {
-  for (int e = threadIdx.x; e < BP * D; e += 256) {
-    const int rr = e / D, cc = e % D, row = r0 + rr;
-    const bool in = row <= r_hi;
-    blk.a[rr][cc] = in ? InT<TIn>::ld(pa, (base + row) * D + cc) : 0.f;
-    if (TWO) blk.b[rr][cc] = in ? InT<TIn>::ld(pb, (base + row) * D + cc) : 0.f;
+// 16 x 32 score-like tile of a wave: acc[t] (t = 0, 1) += sum over the
+// features of A rows (16 t + m of the LDS stage, m < 16) times the lane's own
+// row held in registers (xr[j] = feature D/4 g + j).
+template <int D>
+__device__ __forceinline__ void tile_dot(const float* stage, const float* xr, floatx4* acc) {
+  constexpr int S = D + 4, Q = D / 4;
+  const int l = threadIdx.x & 63, m = l & 15, g = l >> 4;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float* ar = stage + (16 * t + m) * S + Q * g;
+#pragma unroll
+    for (int j4 = 0; j4 < Q / 4; ++j4) {
+      const float4 a = *reinterpret_cast<const float4*>(ar + 4 * j4);
+      acc[t] = mfma4(a.x, xr[4 * j4], acc[t]);
+      acc[t] = mfma4(a.y, xr[4 * j4 + 1], acc[t]);
+      acc[t] = mfma4(a.z, xr[4 * j4 + 2], acc[t]);
+      acc[t] = mfma4(a.w, xr[4 * j4 + 3], acc[t]);
+    }
   }
 }
 
-// (1) per query: lse_t = max + log(sum exp), D_t = <dy_t, y_t>
-template <typename TIn, int D>
-__global__ __launch_bounds__(256) void wbwd_stats_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                                        const TIn* __restrict__ v, const float* __restrict__ dy,
-                                                        int T, int W, float scale, float* __restrict__ lse,
-                                                        float* __restrict__ dd) {
-  __shared__ RowBlock<D> blk;
-  const int bh = blockIdx.y, t0 = blockIdx.x * BR;
-  const int c = threadIdx.x & 3, tq = t0 + (threadIdx.x >> 2);
-  const long base = (long)bh * T;
-  const bool live = tq < T;
-  float qr[D / 4], acc[D / 4];
-  load_row_part<TIn, D>(q, base + tq, c, live, qr);
+// out^T[f][row n] (f = 16 dt + 4 g + e in acc[dt][e]) += sum over the 32
+// partner rows r of stage[r][f] w[r], where lane (g, n) holds w of partner
+// rows 16 t + 4 g + e in wt[t][e].
+template <int D>
+__device__ __forceinline__ void accum_rows(const float* stage, const floatx4* wt, floatx4* acc) {
+  constexpr int S = D + 4;
+  const int l = threadIdx.x & 63, m = l & 15, g = l >> 4;
 #pragma unroll
-  for (int i = 0; i < D / 4; ++i) acc[i] = 0.f;
-  float mx = -INFINITY, l = 0.f;
-  const int j_lo = max(0, t0 - W + 1), j_hi = min(T - 1, t0 + BR - 1);
-  for (int jb = j_lo; jb <= j_hi; jb += BP) {
-    __syncthreads();
-    stage<TIn, D, true>(blk, k, v, base, jb, j_hi);
-    __syncthreads();
-    const int lo = live ? max(tq - W + 1, jb) : 1, hi = live ? min(tq, jb + BP - 1) : 0;
-    for (int j = lo; j <= hi; ++j) {
-      float s = 0.f;
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < D / 4; ++i) s = fmaf(qr[i], blk.a[j - jb][4 * i + c], s);
-      s = quad_sum(s) * scale;
-      if (s > mx) {
-        const float a = expf(mx - s);
-        l *= a;
+    for (int e = 0; e < 4; ++e) {
+      const float* row = stage + (16 * t + 4 * g + e) * S + m;
 #pragma unroll
-        for (int i = 0; i < D / 4; ++i) acc[i] *= a;
-        mx = s;
-      }
-      const float p = expf(s - mx);
-      l += p;
-#pragma unroll
-      for (int i = 0; i < D / 4; ++i) acc[i] = fmaf(p, blk.b[j - jb][4 * i + c], acc[i]);
+      for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma4(row[16 * dt], wt[t][e], acc[dt]);
     }
+}
+
+__device__ __forceinline__ int xcd_item(int n_items) {
+  const int per_xcd = (n_items + NXCD - 1) / NXCD;
+  return ((int)blockIdx.x % NXCD) * per_xcd + (int)blockIdx.x / NXCD;
+}
+
+// (1) statistics and dq, per 128 queries
+template <typename TIn, int D>
+__global__ __launch_bounds__(NT) void wbwd_q_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                   const TIn* __restrict__ v, const float* __restrict__ dy,
+                                                   int T, int W, int n_tiles, int n_items, float sl2, float scale,
+                                                   float* __restrict__ lse2, float* __restrict__ dd,
+                                                   bool accumulate, float* __restrict__ dq) {
+  constexpr int S = D + 4, Q = D / 4, ND = D / 16;
+  __shared__ __attribute__((aligned(16))) float sk[2][PB * S];
+  __shared__ __attribute__((aligned(16))) float sv[2][PB * S];
+  const int item = xcd_item(n_items);
+  if (item >= n_items) return;  // whole workgroup, before any barrier
+  const int bh = item / n_tiles, t0 = (item % n_tiles) * RB;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+  const long base = (long)bh * T;
+  const int q0 = t0 + 16 * w, tq = q0 + n;
+  const int j_lo = max(0, t0 - W + 1), j_hi = min(T - 1, t0 + RB - 1);
+  const int nblk = (j_hi - j_lo + PB) / PB;
+  // the wave's key range: some key of the block in the window of one of its queries
+  auto active_at = [&](int jb) { return q0 < T && jb <= min(q0 + 15, T - 1) && jb + PB - 1 >= q0 - W + 1; };
+  auto full_at = [&](int jb) { return jb + PB - 1 <= q0 && jb >= q0 + 16 - W; };
+  // scores of keys jb + 16 t + 4 g + e (valid: tq - W < j <= tq, j < T) into s
+  auto mask = [&](int jb, floatx4* s) __attribute__((always_inline)) {
+    const int lo = tq - W + 1 - jb, hi = min(tq, T - 1) - jb;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = 16 * t + 4 * g + e;
+        s[t][e] = (kk >= lo && kk <= hi) ? s[t][e] : -INFINITY;
+      }
+  };
+
+  float xr[Q];  // q scale log2(e), features Q g ..
+#pragma unroll
+  for (int j4 = 0; j4 < Q / 4; ++j4) {
+    const float4 x = tq < T ? ld4(q + (base + tq) * D + Q * g + 4 * j4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    xr[4 * j4] = x.x * sl2;
+    xr[4 * j4 + 1] = x.y * sl2;
+    xr[4 * j4 + 2] = x.z * sl2;
+    xr[4 * j4 + 3] = x.w * sl2;
   }
+  floatx4 acc[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  Block2<TIn, TIn, D> blk;
+
+  // ---- pass 1: softmax statistics and y
+  float m = kNegBig, lsum = 0.f;
+  blk.load(k, v, base, j_lo, T);
+  blk.store(sk[0], sv[0]);
+  __syncthreads();
+#pragma unroll 1
+  for (int i = 0; i < nblk; ++i) {
+    const int jb = j_lo + PB * i, cur = i & 1;
+    if (i + 1 < nblk) blk.load(k, v, base, jb + PB, T);
+    if (active_at(jb)) {
+      floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      tile_dot<D>(sk[cur], xr, s);
+      if (!full_at(jb)) mask(jb, s);
+      float bm = s[0][0];
+#pragma unroll
+      for (int e = 1; e < 4; ++e) bm = fmaxf(bm, s[0][e]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bm = fmaxf(bm, s[1][e]);
+      bm = max_groups(bm);
+      if (__ballot(bm - m > 8.f) != 0) {  // lazy rescale: every probability stays <= 2^8
+        const float mnew = fmaxf(m, bm);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) acc[dt] *= alpha;
+        m = mnew;
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[t][e] = __builtin_amdgcn_exp2f(s[t][e] - m);
+          lsum += s[t][e];
+        }
+      accum_rows<D>(sv[cur], s, acc);  // y^T += V^T p^T
+    }
+    if (i + 1 < nblk) blk.store(sk[cur ^ 1], sv[cur ^ 1]);
+    __syncthreads();
+  }
+  const float ltot = sum_groups(lsum);
+  const float ls2 = m + log2f(ltot > 0.f ? ltot : 1.f);  // log2 of the normaliser
   float dpart = 0.f;
-  if (live) {
-    const float inv = 1.f / l;
+  if (tq < T) {
+    const float inv = 1.f / ltot;
 #pragma unroll
-    for (int i = 0; i < D / 4; ++i) dpart = fmaf(dy[(base + tq) * D + 4 * i + c], acc[i] * inv, dpart);
+    for (int dt = 0; dt < ND; ++dt) {
+      const float4 gy = *reinterpret_cast<const float4*>(dy + (base + tq) * D + 16 * dt + 4 * g);
+      dpart += gy.x * acc[dt][0] * inv + gy.y * acc[dt][1] * inv + gy.z * acc[dt][2] * inv + gy.w * acc[dt][3] * inv;
+    }
   }
-  const float dsum = quad_sum(dpart);
-  if (live && c == 0) {
-    lse[base + tq] = mx + logf(l);
-    dd[base + tq] = dsum;
+  const float dt_t = sum_groups(dpart);
+  if (tq < T && g == 0) {
+    lse2[base + tq] = ls2;
+    dd[base + tq] = dt_t;
   }
-}
 
-// (2) dq_t = scale sum_j p_tj (<dy_t, v_j> - D_t) k_j
-template <typename TIn, int D>
-__global__ __launch_bounds__(256) void wbwd_dq_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                                     const TIn* __restrict__ v, const float* __restrict__ dy,
-                                                     int T, int W, float scale, const float* __restrict__ lse,
-                                                     const float* __restrict__ dd, bool accumulate,
-                                                     float* __restrict__ dq) {
-  __shared__ RowBlock<D> blk;
-  const int bh = blockIdx.y, t0 = blockIdx.x * BR;
-  const int c = threadIdx.x & 3, tq = t0 + (threadIdx.x >> 2);
-  const long base = (long)bh * T;
-  const bool live = tq < T;
-  float qr[D / 4], gr[D / 4], acc[D / 4];
-  load_row_part<TIn, D>(q, base + tq, c, live, qr);
-  load_row_part<float, D>(dy, base + tq, c, live, gr);
+  // ---- pass 2: dq
+  float yr[Q];  // dy, features Q g ..
 #pragma unroll
-  for (int i = 0; i < D / 4; ++i) acc[i] = 0.f;
-  const float ls = live ? lse[base + tq] : 0.f, dt = live ? dd[base + tq] : 0.f;
-  const int j_lo = max(0, t0 - W + 1), j_hi = min(T - 1, t0 + BR - 1);
-  for (int jb = j_lo; jb <= j_hi; jb += BP) {
-    __syncthreads();
-    stage<TIn, D, true>(blk, k, v, base, jb, j_hi);
-    __syncthreads();
-    const int lo = live ? max(tq - W + 1, jb) : 1, hi = live ? min(tq, jb + BP - 1) : 0;
-    for (int j = lo; j <= hi; ++j) {
-      float s = 0.f, dp = 0.f;
+  for (int j4 = 0; j4 < Q / 4; ++j4) {
+    const float4 x = tq < T ? ld4(dy + (base + tq) * D + Q * g + 4 * j4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    yr[4 * j4] = x.x;
+    yr[4 * j4 + 1] = x.y;
+    yr[4 * j4 + 2] = x.z;
+    yr[4 * j4 + 3] = x.w;
+  }
 #pragma unroll
-      for (int i = 0; i < D / 4; ++i) {
-        s = fmaf(qr[i], blk.a[j - jb][4 * i + c], s);
-        dp = fmaf(gr[i], blk.b[j - jb][4 * i + c], dp);
+  for (int dt = 0; dt < ND; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  blk.load(k, v, base, j_lo, T);
+  blk.store(sk[0], sv[0]);  // every wave passed the last barrier of pass 1
+  __syncthreads();
+#pragma unroll 1
+  for (int i = 0; i < nblk; ++i) {
+    const int jb = j_lo + PB * i, cur = i & 1;
+    if (i + 1 < nblk) blk.load(k, v, base, jb + PB, T);
+    if (active_at(jb)) {
+      floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      floatx4 dp[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      tile_dot<D>(sk[cur], xr, s);
+      tile_dot<D>(sv[cur], yr, dp);
+      if (!full_at(jb)) mask(jb, s);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[t][e] = __builtin_amdgcn_exp2f(s[t][e] - ls2) * (dp[t][e] - dt_t);
+      accum_rows<D>(sk[cur], s, acc);  // dq^T += K^T ds^T
+    }
+    if (i + 1 < nblk) blk.store(sk[cur ^ 1], sv[cur ^ 1]);
+    __syncthreads();
+  }
+  if (tq < T) {
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      float4* o = reinterpret_cast<float4*>(dq + (base + tq) * D + 16 * dt + 4 * g);
+      float4 r = make_float4(scale * acc[dt][0], scale * acc[dt][1], scale * acc[dt][2], scale * acc[dt][3]);
+      if (accumulate) {
+        const float4 x = *o;
+        r = make_float4(x.x + r.x, x.y + r.y, x.z + r.z, x.w + r.w);
       }
-      s = quad_sum(s) * scale;
-      dp = quad_sum(dp);
-      const float ds = expf(s - ls) * (dp - dt) * scale;
-#pragma unroll
-      for (int i = 0; i < D / 4; ++i) acc[i] = fmaf(ds, blk.a[j - jb][4 * i + c], acc[i]);
-    }
-  }
-  if (live) {
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      float* o = dq + (base + tq) * D + 4 * i + c;
-      *o = accumulate ? *o + acc[i] : acc[i];
+      *o = r;
     }
   }
 }
 
-// (3) dv_j = sum_t p_tj dy_t,  dk_j = scale sum_t p_tj (<dy_t, v_j> - D_t) q_t
-// over the queries t in [j, min(T - 1, j + W - 1)]
+// (2) dk, dv per 128 keys, over the queries t in [j, min(T - 1, j + W - 1)]
 template <typename TIn, int D>
-__global__ __launch_bounds__(256) void wbwd_dkv_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
-                                                      const TIn* __restrict__ v, const float* __restrict__ dy,
-                                                      int T, int W, float scale, const float* __restrict__ lse,
-                                                      const float* __restrict__ dd, bool accumulate,
-                                                      float* __restrict__ dk, float* __restrict__ dv) {
-  __shared__ RowBlock<D> blk;
-  __shared__ float sl[BP], sd[BP];
-  const int bh = blockIdx.y, j0 = blockIdx.x * BR;
-  const int c = threadIdx.x & 3, jk = j0 + (threadIdx.x >> 2);
+__global__ __launch_bounds__(NT) void wbwd_kv_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                    const TIn* __restrict__ v, const float* __restrict__ dy,
+                                                    int T, int W, int n_tiles, int n_items, float sl2, float scale,
+                                                    const float* __restrict__ lse2, const float* __restrict__ dd,
+                                                    bool accumulate, float* __restrict__ dk, float* __restrict__ dv) {
+  constexpr int S = D + 4, Q = D / 4, ND = D / 16;
+  __shared__ __attribute__((aligned(16))) float sq[2][PB * S];
+  __shared__ __attribute__((aligned(16))) float sy[2][PB * S];
+  __shared__ __attribute__((aligned(16))) float sl[2][PB];
+  __shared__ __attribute__((aligned(16))) float sd[2][PB];
+  const int item = xcd_item(n_items);
+  if (item >= n_items) return;  // whole workgroup, before any barrier
+  const int bh = item / n_tiles, j0 = (item % n_tiles) * RB;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
   const long base = (long)bh * T;
-  const bool live = jk < T;
-  float kr[D / 4], vr[D / 4], ak[D / 4], av[D / 4];
-  load_row_part<TIn, D>(k, base + jk, c, live, kr);
-  load_row_part<TIn, D>(v, base + jk, c, live, vr);
+  const int kw = j0 + 16 * w, jk = kw + n;  // the wave's first key, this lane's key
+  const int t_lo = j0, t_hi = min(T - 1, j0 + RB - 1 + W - 1);
+  const int nblk = (t_hi - t_lo + PB) / PB;
+
+  float kr[Q], vr[Q];  // k scale log2(e) and v, features Q g ..
 #pragma unroll
-  for (int i = 0; i < D / 4; ++i) ak[i] = av[i] = 0.f;
-  const int t_lo = j0, t_hi = min(T - 1, j0 + BR - 1 + W - 1);
-  for (int tb = t_lo; tb <= t_hi; tb += BP) {
-    __syncthreads();
-    stage<float, D, false>(blk, dy, nullptr, base, tb, t_hi);  // dy rows in a
-    for (int e = threadIdx.x; e < BP * D; e += 256) {           // q rows in b
-      const int rr = e / D, cc = e % D, row = tb + rr;
-      blk.b[rr][cc] = row <= t_hi ? InT<TIn>::ld(q, (base + row) * D + cc) : 0.f;
-    }
-    if (threadIdx.x < BP) {
+  for (int j4 = 0; j4 < Q / 4; ++j4) {
+    const bool in = jk < T;
+    const float4 x = in ? ld4(k + (base + jk) * D + Q * g + 4 * j4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 y = in ? ld4(v + (base + jk) * D + Q * g + 4 * j4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    kr[4 * j4] = x.x * sl2;
+    kr[4 * j4 + 1] = x.y * sl2;
+    kr[4 * j4 + 2] = x.z * sl2;
+    kr[4 * j4 + 3] = x.w * sl2;
+    vr[4 * j4] = y.x;
+    vr[4 * j4 + 1] = y.y;
+    vr[4 * j4 + 2] = y.z;
+    vr[4 * j4 + 3] = y.w;
+  }
+  floatx4 ak[ND], av[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) ak[dt] = av[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  Block2<TIn, float, D> blk;
+  float rl = 0.f, rd = 0.f;  // lse2, D of query row tb + threadIdx.x (threads < 32)
+  auto load_stats = [&](int tb) __attribute__((always_inline)) {
+    if (threadIdx.x < PB) {
       const int row = tb + threadIdx.x;
-      sl[threadIdx.x] = row <= t_hi ? lse[base + row] : 0.f;
-      sd[threadIdx.x] = row <= t_hi ? dd[base + row] : 0.f;
+      rl = row < T ? lse2[base + row] : 0.f;
+      rd = row < T ? dd[base + row] : 0.f;
+    }
+  };
+  auto store_stats = [&](int st) __attribute__((always_inline)) {
+    if (threadIdx.x < PB) {
+      sl[st][threadIdx.x] = rl;
+      sd[st][threadIdx.x] = rd;
+    }
+  };
+  blk.load(q, dy, base, t_lo, T);
+  load_stats(t_lo);
+  blk.store(sq[0], sy[0]);
+  store_stats(0);
+  __syncthreads();
+#pragma unroll 1
+  for (int i = 0; i < nblk; ++i) {
+    const int tb = t_lo + PB * i, cur = i & 1;
+    if (i + 1 < nblk) {
+      blk.load(q, dy, base, tb + PB, T);
+      load_stats(tb + PB);
+    }
+    // some query of the block sees some key of the wave (wave-uniform)
+    const bool active = kw < T && tb <= kw + 15 + W - 1 && tb + PB - 1 >= kw;
+    if (active) {
+      floatx4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      floatx4 dp[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      tile_dot<D>(sq[cur], kr, s);   // s[t][e]: query tb + 16 t + 4 g + e, key jk
+      tile_dot<D>(sy[cur], vr, dp);  // <dy_t, v_j>, same layout
+      const bool full = tb >= kw + 15 && tb + PB - 1 <= kw + W - 1 && tb + PB - 1 < T;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&sl[cur][16 * t + 4 * g]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&sd[cur][16 * t + 4 * g]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tt = tb + 16 * t + 4 * g + e;
+          const bool ok = full || (tt >= jk && tt <= jk + W - 1 && tt < T);
+          const float p = ok ? __builtin_amdgcn_exp2f(s[t][e] - lv[e]) : 0.f;
+          s[t][e] = p;
+          dp[t][e] = p * (dp[t][e] - dv4[e]);
+        }
+      }
+      accum_rows<D>(sy[cur], s, av);   // dv^T += dY^T p
+      accum_rows<D>(sq[cur], dp, ak);  // dk^T += Q^T ds
+    }
+    if (i + 1 < nblk) {
+      blk.store(sq[cur ^ 1], sy[cur ^ 1]);
+      store_stats(cur ^ 1);
     }
     __syncthreads();
-    const int lo = live ? max(jk, tb) : 1, hi = live ? min(min(jk + W - 1, T - 1), tb + BP - 1) : 0;
-    for (int t = lo; t <= hi; ++t) {
-      const int r = t - tb;
-      float s = 0.f, dp = 0.f;
-#pragma unroll
-      for (int i = 0; i < D / 4; ++i) {
-        s = fmaf(kr[i], blk.b[r][4 * i + c], s);
-        dp = fmaf(vr[i], blk.a[r][4 * i + c], dp);
-      }
-      s = quad_sum(s) * scale;
-      dp = quad_sum(dp);
-      const float p = expf(s - sl[r]);
-      const float ds = p * (dp - sd[r]) * scale;
-#pragma unroll
-      for (int i = 0; i < D / 4; ++i) {
-        av[i] = fmaf(p, blk.a[r][4 * i + c], av[i]);
-        ak[i] = fmaf(ds, blk.b[r][4 * i + c], ak[i]);
-      }
-    }
   }
-  if (live) {
+  if (jk < T) {
 #pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      float* ok = dk + (base + jk) * D + 4 * i + c;
-      float* ov = dv + (base + jk) * D + 4 * i + c;
-      *ok = accumulate ? *ok + ak[i] : ak[i];
-      *ov = accumulate ? *ov + av[i] : av[i];
+    for (int dt = 0; dt < ND; ++dt) {
+      float4* ok = reinterpret_cast<float4*>(dk + (base + jk) * D + 16 * dt + 4 * g);
+      float4* ov = reinterpret_cast<float4*>(dv + (base + jk) * D + 16 * dt + 4 * g);
+      float4 rk = make_float4(scale * ak[dt][0], scale * ak[dt][1], scale * ak[dt][2], scale * ak[dt][3]);
+      float4 rv = make_float4(av[dt][0], av[dt][1], av[dt][2], av[dt][3]);
+      if (accumulate) {
+        const float4 xk = *ok, xv = *ov;
+        rk = make_float4(xk.x + rk.x, xk.y + rk.y, xk.z + rk.z, xk.w + rk.w);
+        rv = make_float4(xv.x + rv.x, xv.y + rv.y, xv.z + rv.z, xv.w + rv.w);
+      }
+      *ok = rk;
+      *ov = rv;
     }
   }
 }
 
 template <typename TIn, int D>
 hipError_t run_wbwd(const TIn* q, const TIn* k, const TIn* v, const float* dy, int BH, int T, int W, float scale,
-                    float* lse, float* dd, bool accumulate, float* dq, float* dk, float* dv, hipStream_t s) {
-  const dim3 grid((T + BR - 1) / BR, BH), block(256);
-  hipLaunchKernelGGL((wbwd_stats_kernel<TIn, D>), grid, block, 0, s, q, k, v, dy, T, W, scale, lse, dd);
-  hipLaunchKernelGGL((wbwd_dq_kernel<TIn, D>), grid, block, 0, s, q, k, v, dy, T, W, scale, lse, dd, accumulate, dq);
+                    float* lse2, float* dd, bool accumulate, float* dq, float* dk, float* dv, hipStream_t s) {
+  const int n_tiles = (T + RB - 1) / RB, n_items = BH * n_tiles;
+  const int grid = (n_items + NXCD - 1) / NXCD * NXCD;
+  const float sl2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((wbwd_q_kernel<TIn, D>), dim3(grid), dim3(NT), 0, s, q, k, v, dy, T, W, n_tiles, n_items, sl2,
+                     scale, lse2, dd, accumulate, dq);
   profile_mark_before(s);
-  hipLaunchKernelGGL((wbwd_dkv_kernel<TIn, D>), grid, block, 0, s, q, k, v, dy, T, W, scale, lse, dd, accumulate,
-                     dk, dv);
+  hipLaunchKernelGGL((wbwd_kv_kernel<TIn, D>), dim3(grid), dim3(NT), 0, s, q, k, v, dy, T, W, n_tiles, n_items, sl2,
+                     scale, lse2, dd, accumulate, dk, dv);
   profile_mark_after(s);
   return hipGetLastError();
 }
@@ -240,13 +421,13 @@ hipError_t run_wbwd(const TIn* q, const TIn* k, const TIn* v, const float* dy, i
 template <typename TIn>
 hipError_t dispatch_wbwd(const TIn* q, const TIn* k, const TIn* v, const float* dy, int BH, int T, int d, int W,
                          float scale, float* ws, bool accumulate, float* dq, float* dk, float* dv, hipStream_t s) {
-  float* lse = ws;
+  float* lse2 = ws;
   float* dd = ws + (long)BH * T;
   switch (d) {
-    case 16: return run_wbwd<TIn, 16>(q, k, v, dy, BH, T, W, scale, lse, dd, accumulate, dq, dk, dv, s);
-    case 32: return run_wbwd<TIn, 32>(q, k, v, dy, BH, T, W, scale, lse, dd, accumulate, dq, dk, dv, s);
-    case 64: return run_wbwd<TIn, 64>(q, k, v, dy, BH, T, W, scale, lse, dd, accumulate, dq, dk, dv, s);
-    case 128: return run_wbwd<TIn, 128>(q, k, v, dy, BH, T, W, scale, lse, dd, accumulate, dq, dk, dv, s);
+    case 16: return run_wbwd<TIn, 16>(q, k, v, dy, BH, T, W, scale, lse2, dd, accumulate, dq, dk, dv, s);
+    case 32: return run_wbwd<TIn, 32>(q, k, v, dy, BH, T, W, scale, lse2, dd, accumulate, dq, dk, dv, s);
+    case 64: return run_wbwd<TIn, 64>(q, k, v, dy, BH, T, W, scale, lse2, dd, accumulate, dq, dk, dv, s);
+    case 128: return run_wbwd<TIn, 128>(q, k, v, dy, BH, T, W, scale, lse2, dd, accumulate, dq, dk, dv, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -21,6 +21,8 @@ TOL = {"f32": 1e-5, "bf16": 2e-2}
     ("f32", 1, 2, 500, 64, 100),
     ("f32", 1, 1, 200, 128, 300),   # the window covers the sequence
     ("f32", 1, 2, 130, 64, 1),
+    ("f32", 2, 2, 700, 128, 150),   # several 128-row tiles per head, W not a multiple of the 32-row block
+    ("f32", 1, 1, 300, 16, 1000),   # W > T
     ("bf16", 1, 2, 400, 128, 150),
     ("bf16", 2, 1, 257, 64, 64),
     # bf16 with d in {64, 128} runs the MFMA kernels: ragged single tile, a
