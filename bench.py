@@ -573,6 +573,61 @@ def bench_layer_backward(steps, warmup, dev, x=None):
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "bf16"}}
 
 
+def bench_layer_backward_f32(steps, warmup, dev):
+    """tc_fused_layer_backward with fp32 inputs at the batched prefill
+    workload (B=4, H=8, T=4096, d=64, W=512): the gated L2-read backward and
+    the window softmax backward, both on fp32 MFMA; and the window softmax
+    backward alone (tc_window_attention_backward), whose dk/dv kernel the
+    library's timing events bracket."""
+    import numpy as np
+    import torch
+
+    from linear_attention_tensor_amd import inputs as I
+    from linear_attention_tensor_amd import ops
+
+    w = I.WORKLOADS["prefill_scan_f32"]
+    x = I.draw_workload(w.name)
+    q, k, v = (to_dev_f32(x[n], dev) for n in ("q", "k", "v"))
+    lam, eta = to_dev_f32(x["lam"], dev), to_dev_f32(x["eta"], dev)
+    g = to_dev_f32(np.random.default_rng(3).standard_normal(w.H), dev)
+    dy = to_dev_f32(I.draw_cotangent(w.B, w.H, w.T, w.d, seed=w.seed), dev)
+    shape = (w.B, w.H, w.T, w.d)
+    gq, gk, gv = (torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
+    glam, geta, gg = (torch.empty((w.H,), dtype=torch.float32, device=dev) for _ in range(3))
+    lib = ops.lib()
+    scale = 1.0 / math.sqrt(w.d)
+    nb = lib.tc_fused_layer_backward_workspace_bytes(w.B, w.H, w.T, w.d, w.d, w.W, 64, 0)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    largs = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, ops._ptr(lam), ops._ptr(eta), ops._ptr(g), w.B, w.H, w.T,
+             w.d, w.d, w.W, 64, scale, ops._ptr(dy), ops._ptr(gq), ops._ptr(gk), ops._ptr(gv),
+             ops._ptr(glam), ops._ptr(geta), ops._ptr(gg), ops._ptr(ws), ws.numel(), ops._stream())
+    nbw = lib.tc_window_attention_backward_workspace_bytes(w.B, w.H, w.T, w.d, w.d, w.W, 0)
+    wws = torch.empty(max(nbw, 1), dtype=torch.uint8, device=dev)
+    wargs = (ops._ptr(q), ops._ptr(k), ops._ptr(v), 0, w.B, w.H, w.T, w.d, w.d, w.W, scale, ops._ptr(dy),
+             ops._ptr(gq), ops._ptr(gk), ops._ptr(gv), ops._ptr(wws), wws.numel(), ops._stream())
+
+    def call_layer(_):
+        if lib.tc_fused_layer_backward(*largs) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    def call_window(_):
+        if lib.tc_window_attention_backward(*wargs) != 0:
+            raise RuntimeError(ops._lib.last_error())
+
+    ms, ms_call, _ = time_calls(call_layer, steps, warmup)
+    _, ms_window, kernel_ms = time_calls(call_window, steps, warmup, KernelTimer(steps))
+    wflops = window_backward_flops(w.B, w.H, w.T, w.d, w.W)
+    flops = wflops + scan_backward_flops(w.B, w.H, w.T, w.d, w.W)
+    return {"workload": w.name + " fused layer backward", "ms_per_step": ms,
+            "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3), "ms_per_call": ms_call,
+            "roofline": roofline("mfma", flops / (ms_call * 1e-3) / 1e12, PEAK_FP32_TFLOPS, "TFLOP/s"),
+            "roofline_scope": "whole call: the window-softmax backward plus the gated L2-read backward, all on "
+                              "fp32 MFMA, their algorithmic flops over the fp32 peak",
+            "window_backward": {"ms_per_call": ms_window, "kv_kernel_ms": kernel_ms,
+                                "tflops": wflops / (ms_window * 1e-3) / 1e12},
+            "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
+
+
 def bench_decode(steps, warmup, dev, n_steps=4096, B=None):
     """The decode workload's L2 step (4096 steps, 64 x 32 heads).  With B
     given (the side run: 256 sequences, 512 MiB of A) the state no longer
@@ -955,6 +1010,7 @@ def main():
         components["prefill_scan_f32"] = bench_scan(args.steps, args.warmup, dev)
         components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
         components["fused_layer_backward_bf16"] = bench_layer_backward(args.steps, args.warmup, dev, x)
+        components["fused_layer_backward_f32"] = bench_layer_backward_f32(args.steps, args.warmup, dev)
         components["scan_bf16_fused_size"] = bench_scan_bf16(args.steps, args.warmup, dev)
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 4096)
         components["decode_bf16_x4"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 1024,
@@ -976,6 +1032,7 @@ def main():
         components["prefill_scan_backward_f32"] = bench_scan_backward(args.steps, args.warmup, dev)
     elif only == "layer_backward":
         components["fused_layer_backward_bf16"] = bench_layer_backward(args.steps, args.warmup, dev)
+        components["fused_layer_backward_f32"] = bench_layer_backward_f32(args.steps, args.warmup, dev)
     elif only == "decode":
         components["decode_bf16"] = bench_decode(args.steps, args.warmup, dev, n_steps=args.decode_steps or 4096)
     elif only == "decode_x4":
