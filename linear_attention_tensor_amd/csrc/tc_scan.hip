@@ -326,6 +326,19 @@ __global__ __launch_bounds__(256) void scan_output_fast(
   for (int c = c_begin; c < c_end; ++c) {
     const int s0 = c * CH, L = min(CH, n_act - s0);
     const int cur = (c - c_begin) & 1;
+    // ACC: the read already in m for this wave's rows (each lane adds to the
+    // elements it loads here), loaded first so that it arrives while the
+    // chunk is computed
+    float prev[NDV][4];
+    if constexpr (ACC) {
+#pragma unroll
+      for (int t = 0; t < NDV; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 16 * w + 4 * g + e;
+          prev[t][e] = rr < L ? vm.row(bh, s0 + rr)[16 * t + r] : 0.f;
+        }
+    }
     lds_barrier();  // every wave is done with the previous chunk; its state is published
     if (threadIdx.x < CH) sW[threadIdx.x] = threadIdx.x < L ? et * sPow[L - 1 - threadIdx.x] : 0.f;
     lds_barrier();
@@ -369,10 +382,7 @@ __global__ __launch_bounds__(256) void scan_output_fast(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = 16 * w + 4 * g + e;
-          if (rr < L) {
-            float* out = vm.row(bh, s0 + rr) + 16 * t + r;
-            *out = ACC ? *out + o[t][e] : o[t][e];
-          }
+          if (rr < L) vm.row(bh, s0 + rr)[16 * t + r] = ACC ? prev[t][e] + o[t][e] : o[t][e];
         }
     }
     fast_state_update<D>(acc, sVt, sKt, sPow[L]);
