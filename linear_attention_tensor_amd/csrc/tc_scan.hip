@@ -69,30 +69,32 @@ struct RowView {
 };
 
 // One chunk's rows [0, 64) (row r at src + r rs) in registers, as float4
-// pieces i * 256 + thread; rows >= nvalid are zero.
-template <int D, typename TIn>
+// pieces i * NT + thread (NT threads per workgroup); rows >= nvalid are zero.
+template <int D, int NT>
+constexpr int kNV4 = CH * D / 4 / NT;
+template <int D, typename TIn, int NT = 256>
 __device__ __forceinline__ void load_rows(float4* x, const TIn* src, long rs, int nvalid) {
 #pragma unroll
-  for (int i = 0; i < FastTiles<D>::NV4; ++i) {
-    const int e4 = i * 256 + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
+  for (int i = 0; i < kNV4<D, NT>; ++i) {
+    const int e4 = i * NT + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
     x[i] = row < nvalid ? ld4(src + (long)row * rs + c4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 // ... into LDS row-major (stride S) ...
-template <int D>
+template <int D, int NT = 256>
 __device__ __forceinline__ void put_rows(float* dst, const float4* x) {
 #pragma unroll
-  for (int i = 0; i < FastTiles<D>::NV4; ++i) {
-    const int e4 = i * 256 + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
+  for (int i = 0; i < kNV4<D, NT>; ++i) {
+    const int e4 = i * NT + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
     *reinterpret_cast<float4*>(dst + row * FastTiles<D>::S + c4) = x[i];
   }
 }
 // ... or transposed (dst[col][row], stride ST), each row scaled by wr[row].
-template <int D>
+template <int D, int NT = 256>
 __device__ __forceinline__ void put_cols(float* dst, const float4* x, const float* wr) {
 #pragma unroll
-  for (int i = 0; i < FastTiles<D>::NV4; ++i) {
-    const int e4 = i * 256 + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
+  for (int i = 0; i < kNV4<D, NT>; ++i) {
+    const int e4 = i * NT + threadIdx.x, row = e4 / (D / 4), c4 = 4 * (e4 % (D / 4));
     const float f = wr != nullptr ? wr[row] : 1.f;
     dst[(c4 + 0) * FastTiles<D>::ST + row] = f * x[i].x;
     dst[(c4 + 1) * FastTiles<D>::ST + row] = f * x[i].y;
@@ -389,6 +391,161 @@ __global__ __launch_bounds__(256) void scan_output_fast(
     publish_state<D>(sSt[cur ^ 1], acc);
   }
   if (A_final != nullptr && seg == n_seg - 1) store_state<D>(A_final + bh * a_bh, acc, a_rs);
+}
+
+// The same walk at d = 64 with eight waves (two per SIMD, so that each
+// SIMD's two waves hide each other's latencies) and the causal structure of
+// the chunk used: with row tiles rt = 0..3 of the chunk (16 positions each),
+//   P tiles (rt, ct) exist for ct <= rt only (the pair of waves on row tile
+//     w % 4 splits its ct between them);
+//   O tile (rt, dvt) = lam^(r+1) Q'_rt S + P_rt V over the 16 (rt + 1) keys up
+//     to the tile: wave w takes d_v tile w / 2 of row tiles {0, 3} (w even) or
+//     {1, 2} (w odd), which cost the same;
+//   the state update takes S^T tiles 2 w, 2 w + 1 (one d_v row of tiles).
+// P is complete in LDS (a barrier) before any O tile reads it.
+template <typename TIn, bool ACC>
+__global__ __launch_bounds__(512) void scan_output_fast8(
+    RowView<const TIn> vq, RowView<const TIn> vk, RowView<const TIn> vv, const float* __restrict__ lam,
+    const float* __restrict__ eta, int H, int n_act, int seg_chunks, int n_seg,
+    const float* __restrict__ ws, RowView<float> vm, int zrows, float* __restrict__ A_final, long a_bh, int a_rs) {
+  constexpr int D = 64, NT = 512, NV = kNV4<D, NT>;
+  using F = FastTiles<D>;
+  __shared__ __attribute__((aligned(16))) float sQ[CH * F::S];
+  __shared__ __attribute__((aligned(16))) float sK[CH * F::S];
+  __shared__ __attribute__((aligned(16))) float sKt[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sVt[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sP[CH * F::ST];
+  __shared__ __attribute__((aligned(16))) float sSt[2][D * F::S];
+  __shared__ float sPow[CH + 1];  // lam^i
+  __shared__ float sW[CH];
+
+  const int seg = blockIdx.x, bh = blockIdx.z;
+  const float lm = lam[bh % H], et = eta[bh % H];
+  const int l = lane_id(), w = wave_id(), r = l & 15, g = l >> 4;
+  const int c_begin = seg * seg_chunks;
+  const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
+  if (threadIdx.x <= CH) sPow[threadIdx.x] = pow_int(lm, threadIdx.x);
+  // this wave's tiles
+  const int prt = w & 3;                                              // P row tile
+  const int pc0 = w < 4 ? 0 : (prt + 2) / 2, pc1 = w < 4 ? (prt + 2) / 2 : prt + 1;  // P column tiles [pc0, pc1)
+  const int dvt = w >> 1;                                             // O d_v tile
+  const int ort[2] = {(w & 1) ? 1 : 0, (w & 1) ? 2 : 3};              // O row tiles
+  const int sa = w >> 1, sb0 = 2 * (w & 1);                           // S^T tiles (sa, sb0), (sa, sb0 + 1)
+
+  float4 xq[NV], xk[NV], xv[NV];
+  if (c_begin < c_end) {
+    const int s0 = c_begin * CH, L = min(CH, n_act - s0);
+    load_rows<D, TIn, NT>(xq, vq.row(bh, s0), vq.rs, L);
+    load_rows<D, TIn, NT>(xk, vk.row(bh, s0), vk.rs, L);
+    load_rows<D, TIn, NT>(xv, vv.row(bh, s0), vv.rs, L);
+  }
+  // S^T tiles (sa, sb0 + i) of the entering state: Horner over the earlier segments' contributions
+  floatx4 acc[2] = {zero4(), zero4()};
+  if (seg > 0) {
+    const float lam_seg = pow_int(lm, seg_chunks * CH);
+    for (int sp = 0; sp < seg; ++sp) {
+      const float* src = ws + ((long)bh * n_seg + sp) * D * D;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[i][e] = fmaf(lam_seg, acc[i][e], src[(long)(16 * (sb0 + i) + r) * D + 16 * sa + 4 * g + e]);
+    }
+  }
+  auto publish = [&](float* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(16 * sa + 4 * g + e) * F::S + 16 * (sb0 + i) + r] = acc[i][e];
+  };
+  publish(sSt[0]);
+  clear_rows_before<D>(vm, bh, zrows, seg, n_seg);  // row s of vm is t = W + s
+  for (int c = c_begin; c < c_end; ++c) {
+    const int s0 = c * CH, L = min(CH, n_act - s0);
+    const int cur = (c - c_begin) & 1;
+    // ACC: the read already in m for this wave's O tiles (each lane adds to the
+    // elements it loads here), loaded first so that it arrives meanwhile
+    float prev[2][4];
+    if constexpr (ACC) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = 16 * ort[u] + 4 * g + e;
+          prev[u][e] = rr < L ? vm.row(bh, s0 + rr)[16 * dvt + r] : 0.f;
+        }
+    }
+    lds_barrier();  // every wave is done with the previous chunk; its state is published
+    if (threadIdx.x < CH) sW[threadIdx.x] = threadIdx.x < L ? et * sPow[L - 1 - threadIdx.x] : 0.f;
+    lds_barrier();
+    put_rows<D, NT>(sQ, xq);
+    put_rows<D, NT>(sK, xk);
+    put_cols<D, NT>(sKt, xk, sW);
+    put_cols<D, NT>(sVt, xv, nullptr);
+    lds_barrier();
+    if (c + 1 < c_end) {
+      const int s1 = s0 + CH, Ln = min(CH, n_act - s1);
+      load_rows<D, TIn, NT>(xq, vq.row(bh, s1), vq.rs, Ln);
+      load_rows<D, TIn, NT>(xk, vk.row(bh, s1), vk.rs, Ln);
+      load_rows<D, TIn, NT>(xv, vv.row(bh, s1), vv.rs, Ln);
+    }
+    // P tiles (prt, ct), ct in [pc0, pc1): (Q' K^T) masked to c <= r, weighted eta lam^(r-c)
+    for (int ct = pc0; ct < pc1; ++ct) {  // wave-uniform
+      floatx4 pa = zero4();
+      mma_rows<D, 1>(sQ + 16 * prt * F::S, F::S, sK + 16 * ct * F::S, 0, F::S, &pa);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * prt + 4 * g + e, cc = 16 * ct + r;
+        sP[rr * F::ST + cc] = cc <= rr ? pa[e] * et * sPow[rr - cc] : 0.f;
+      }
+    }
+    // O tiles before P is complete: the state term lam^(r+1) Q'_rt S
+    floatx4 o[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      o[u] = zero4();
+      mma_rows<D, 1>(sQ + 16 * ort[u] * F::S, F::S, sSt[cur] + 16 * dvt * F::S, 0, F::S, &o[u]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[u][e] *= sPow[16 * ort[u] + 4 * g + e + 1];
+    }
+    lds_barrier();  // every P tile is in LDS
+    // + P_rt V over the keys 0 .. 16 rt + 15
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float* ap = sP + (16 * ort[u] + r) * F::ST + 4 * g;
+      const float* bp = sVt + (16 * dvt + r) * F::ST + 4 * g;
+      const int nj = ort[u] + 1;  // 16-key steps
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        if (J < nj) {
+          const float4 x = *reinterpret_cast<const float4*>(ap + 16 * J);
+          const float4 y = *reinterpret_cast<const float4*>(bp + 16 * J);
+          o[u] = mfma4(x.x, y.x, o[u]);
+          o[u] = mfma4(x.y, y.y, o[u]);
+          o[u] = mfma4(x.z, y.z, o[u]);
+          o[u] = mfma4(x.w, y.w, o[u]);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = 16 * ort[u] + 4 * g + e;
+        if (rr < L) vm.row(bh, s0 + rr)[16 * dvt + r] = ACC ? prev[u][e] + o[u][e] : o[u][e];
+      }
+    }
+    // S^T tiles (sa, sb0 + i) <- lam^L S^T + V^T (w K)
+    const float lL = sPow[L];
+    acc[0] *= lL;
+    acc[1] *= lL;
+    mma_rows<CH, 2>(sVt + 16 * sa * F::ST, F::ST, sKt + 16 * sb0 * F::ST, 16 * F::ST, F::ST, acc);
+    publish(sSt[cur ^ 1]);
+  }
+  if (A_final != nullptr && seg == n_seg - 1) {
+    float* dst = A_final + bh * a_bh;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(long)(16 * (sb0 + i) + r) * a_rs + 16 * sa + 4 * g + e] = acc[i][e];
+  }
 }
 
 // m rows t < min(W, T) are exactly zero; with no active position the final
@@ -1002,8 +1159,12 @@ void scan_piece(const TIn* q, const TIn* k, const TIn* v, long rs, const float* 
   if (p.n_seg > 1 && !states_ready)
     hipLaunchKernelGGL((scan_state_fast<D, TIn>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, vk, vv, lam, eta, H,
                        p.n_act, p.seg_chunks, p.n_seg, ws, kOnePiece);
-  hipLaunchKernelGGL((scan_output_fast<D, TIn, ACC>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, vq, vk, vv, lam, eta,
-                     H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, zrows, A_final, a_bh, a_rs);
+  if constexpr (D == 64)
+    hipLaunchKernelGGL((scan_output_fast8<TIn, ACC>), dim3(p.n_seg, 1, BH), dim3(512), 0, s, vq, vk, vv, lam, eta,
+                       H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, zrows, A_final, a_bh, a_rs);
+  else
+    hipLaunchKernelGGL((scan_output_fast<D, TIn, ACC>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, vq, vk, vv, lam, eta,
+                       H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, zrows, A_final, a_bh, a_rs);
 }
 
 template <int D, typename TIn>
