@@ -457,7 +457,7 @@ def bench_scan(steps, warmup, dev):
     return {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.H * w.T / (ms * 1e-3),
             "roofline": roofline("mfma", tf, PEAK_FP32_TFLOPS, "TFLOP/s"),
             "hbm": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s"),
-            "main_kernel": {"name": "scan_state_fast<64> + scan_output_fast8 (the call's two launches)",
+            "main_kernel": {"name": "scan_state_fast8 + scan_output_fast8 (the call's two launches)",
                             "ms": kernel_ms}, "ms_per_call": ms_call,
             "config": {"B": w.B, "H": w.H, "T": w.T, "d": w.d, "W": w.W, "dtype_in": "f32"}}
 

@@ -279,6 +279,77 @@ __global__ __launch_bounds__(256) void scan_state_fast(RowView<const TIn> kv_k0,
   store_state<D>(ws + ((long)bh * n_seg + seg) * D * D, acc, D);
 }
 
+// The same at d = 64 with eight waves (two per SIMD), each owning the S^T
+// tiles 2 w, 2 w + 1 (one d_v row of tiles); the key weights are formed again
+// only when the chunk length changes.
+template <typename TIn>
+__global__ __launch_bounds__(512) void scan_state_fast8(RowView<const TIn> kv_k0, RowView<const TIn> kv_v0,
+                                                        const float* __restrict__ lam,
+                                                        const float* __restrict__ eta, int H, int n_act,
+                                                        int seg_chunks, int n_seg, float* __restrict__ ws,
+                                                        Pieces pcs) {
+  constexpr int D = 64, NT = 512, NV = kNV4<D, NT>;
+  using F = FastTiles<D>;
+  __shared__ __attribute__((aligned(16))) float sKt[D * F::ST];
+  __shared__ __attribute__((aligned(16))) float sVt[D * F::ST];
+  __shared__ float sW[CH];
+  int bh;
+  const int pi = piece_index(pcs, bh), seg = blockIdx.x;
+  const RowView<const TIn> kv_k = shift(kv_k0, pcs.xo[pi]), kv_v = shift(kv_v0, pcs.yo[pi]);
+  ws += pi * pcs.ws_stride;
+  const float lm = lam[bh % H], et = eta != nullptr ? eta[bh % H] : 1.f;  // NULL: eta = 1
+  const int l = lane_id(), w = wave_id(), r = l & 15, g = l >> 4;
+  const int sa = w >> 1, sb0 = 2 * (w & 1);
+  const int c_begin = seg * seg_chunks;
+  const int c_end = min(c_begin + seg_chunks, (n_act + CH - 1) / CH);
+  floatx4 acc[2] = {zero4(), zero4()};
+  float4 xk[NV], xv[NV];
+  if (c_begin < c_end) {
+    const int L = min(CH, n_act - c_begin * CH);
+    load_rows<D, TIn, NT>(xk, kv_k.row(bh, (long)c_begin * CH), kv_k.rs, L);
+    load_rows<D, TIn, NT>(xv, kv_v.row(bh, (long)c_begin * CH), kv_v.rs, L);
+  }
+  int wl = -1;  // chunk length the weights sW were formed for
+  for (int c = c_begin; c < c_end; ++c) {
+    const int L = min(CH, n_act - c * CH);
+    lds_barrier();  // every wave is done with the previous chunk
+    if (L != wl) {  // uniform
+      if (threadIdx.x < CH) sW[threadIdx.x] = threadIdx.x < L ? et * pow_int(lm, L - 1 - threadIdx.x) : 0.f;
+      lds_barrier();
+      wl = L;
+    }
+    put_cols<D, NT>(sKt, xk, sW);
+    put_cols<D, NT>(sVt, xv, nullptr);
+    lds_barrier();
+    if (c + 1 < c_end) {
+      const int Ln = min(CH, n_act - (c + 1) * CH);
+      load_rows<D, TIn, NT>(xk, kv_k.row(bh, (long)(c + 1) * CH), kv_k.rs, Ln);
+      load_rows<D, TIn, NT>(xv, kv_v.row(bh, (long)(c + 1) * CH), kv_v.rs, Ln);
+    }
+    const float lL = pow_int(lm, L);
+    acc[0] *= lL;
+    acc[1] *= lL;
+    mma_rows<CH, 2>(sVt + 16 * sa * F::ST, F::ST, sKt + 16 * sb0 * F::ST, 16 * F::ST, F::ST, acc);
+  }
+  float* dst = ws + ((long)bh * n_seg + seg) * D * D;  // [d_k][d_v]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[(long)(16 * (sb0 + i) + r) * D + 16 * sa + 4 * g + e] = acc[i][e];
+}
+
+// One launch of the state kernel: d = 64 on eight waves, d < 64 on four.
+template <int D, typename TIn>
+void launch_state_fast(dim3 grid, RowView<const TIn> x, RowView<const TIn> y, const float* lam, const float* eta,
+                       int H, int n_act, int seg_chunks, int n_seg, float* ws, const Pieces& pcs, hipStream_t s) {
+  if constexpr (D == 64)
+    hipLaunchKernelGGL((scan_state_fast8<TIn>), grid, dim3(512), 0, s, x, y, lam, eta, H, n_act, seg_chunks, n_seg,
+                       ws, pcs);
+  else
+    hipLaunchKernelGGL((scan_state_fast<D, TIn>), grid, dim3(256), 0, s, x, y, lam, eta, H, n_act, seg_chunks,
+                       n_seg, ws, pcs);
+}
+
 // Per-(segment, b, h): the entering state from the earlier segments'
 // contributions (ws, from scan_state_fast; every segment but the last is
 // seg_chunks chunks long), S_in(s) = sum_{s' < s} lam^(L (s-1-s')) U_s'
@@ -460,6 +531,7 @@ __global__ __launch_bounds__(512) void scan_output_fast8(
   };
   publish(sSt[0]);
   clear_rows_before<D>(vm, bh, zrows, seg, n_seg);  // row s of vm is t = W + s
+  int wl = -1;  // chunk length the weights sW were formed for
   for (int c = c_begin; c < c_end; ++c) {
     const int s0 = c * CH, L = min(CH, n_act - s0);
     const int cur = (c - c_begin) & 1;
@@ -476,8 +548,11 @@ __global__ __launch_bounds__(512) void scan_output_fast8(
         }
     }
     lds_barrier();  // every wave is done with the previous chunk; its state is published
-    if (threadIdx.x < CH) sW[threadIdx.x] = threadIdx.x < L ? et * sPow[L - 1 - threadIdx.x] : 0.f;
-    lds_barrier();
+    if (L != wl) {  // the weights depend on the chunk length only (uniform)
+      if (threadIdx.x < CH) sW[threadIdx.x] = threadIdx.x < L ? et * sPow[L - 1 - threadIdx.x] : 0.f;
+      lds_barrier();
+      wl = L;
+    }
     put_rows<D, NT>(sQ, xq);
     put_rows<D, NT>(sK, xk);
     put_cols<D, NT>(sKt, xk, sW);
@@ -1088,8 +1163,8 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   const RowView<const float> rv{v + last, bs, -rs}, rk{k + last, bs, -rs}, rq{q + tl, bs, -rs},
       rg{dm + tl, bs, -rs};
   if (p.n_seg > 1 && pre.rs == nullptr)
-    hipLaunchKernelGGL((scan_state_fast<D, float>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, rg, rq, lam,
-                       nullptr, H, n_act, p.seg_chunks, p.n_seg, sws, kOnePiece);
+    launch_state_fast<D, float>(dim3(p.n_seg - 1, 1, BH), rg, rq, lam, nullptr, H, n_act, p.seg_chunks, p.n_seg,
+                                sws, kOnePiece, s);
   hipLaunchKernelGGL((scan_bwd_rev_fast<D>), dim3(p.n_seg, 1, BH), dim3(256), 0, s, rv, rk, rq, rg, lam, eta,
                      H, n_act, p.seg_chunks, p.n_seg, pre.rs ? pre.rs : sws, gate, RowView<float>{dk + last, bs, -rs},
                      RowView<float>{dv + last, bs, -rs}, T - n_act, pc.add_qk, pc.add_v);
@@ -1126,8 +1201,8 @@ hipError_t run_scan_backward_128(const float* q, const float* k, const float* v,
                        p.n_act, p.seg_chunks, p.n_seg, fs, fd, fwd);
     const long tl = (long)(T - 1) * D;
     const RowView<const float> rg{dm + tl, bs, -D}, rq{q + tl, bs, -D};
-    hipLaunchKernelGGL((scan_state_fast<PD, float>), dim3(p.n_seg - 1, 1, 4 * BH), dim3(256), 0, s, rg, rq, lam,
-                       nullptr, H, p.n_act, p.seg_chunks, p.n_seg, rs, rev);
+    launch_state_fast<PD, float>(dim3(p.n_seg - 1, 1, 4 * BH), rg, rq, lam, nullptr, H, p.n_act, p.seg_chunks,
+                                 p.n_seg, rs, rev, s);
     pre = BwdStates{fs, fd, rs};
   }
   hipError_t e = hipSuccess;
@@ -1157,8 +1232,8 @@ void scan_piece(const TIn* q, const TIn* k, const TIn* v, long rs, const float* 
   const RowView<float> vm{m + (long)W * rs, bs, rs};
   const int zrows = ACC ? 0 : std::min(W, T);
   if (p.n_seg > 1 && !states_ready)
-    hipLaunchKernelGGL((scan_state_fast<D, TIn>), dim3(p.n_seg - 1, 1, BH), dim3(256), 0, s, vk, vv, lam, eta, H,
-                       p.n_act, p.seg_chunks, p.n_seg, ws, kOnePiece);
+    launch_state_fast<D, TIn>(dim3(p.n_seg - 1, 1, BH), vk, vv, lam, eta, H, p.n_act, p.seg_chunks, p.n_seg, ws,
+                              kOnePiece, s);
   if constexpr (D == 64)
     hipLaunchKernelGGL((scan_output_fast8<TIn, ACC>), dim3(p.n_seg, 1, BH), dim3(512), 0, s, vq, vk, vv, lam, eta,
                        H, p.n_act, p.seg_chunks, p.n_seg, ws, vm, zrows, A_final, a_bh, a_rs);
@@ -1194,8 +1269,8 @@ hipError_t run_scan(const TIn* q, const TIn* k, const TIn* v, const float* lam, 
       const long bs = (long)T * D;
       const RowView<const TIn> vk{k, bs, D}, vv{v, bs, D};
       const Pieces pcs{4, {0, 0, 64, 64}, {0, 64, 0, 64}, stride};
-      hipLaunchKernelGGL((scan_state_fast<64, TIn>), dim3(p.n_seg - 1, 1, 4 * BH), dim3(256), 0, s, vk, vv, lam,
-                         eta, H, p.n_act, p.seg_chunks, p.n_seg, ws, pcs);
+      launch_state_fast<64, TIn>(dim3(p.n_seg - 1, 1, 4 * BH), vk, vv, lam, eta, H, p.n_act, p.seg_chunks, p.n_seg,
+                                 ws, pcs, s);
     }
     for (int a = 0; a < 2; ++a)
       for (int b = 0; b < 2; ++b) {
