@@ -185,11 +185,13 @@ struct Pre {
 // 1. Per chunk (in parallel): W = (I + diag(beta) tril_-1(K K^T))^-1 (blocked:
 //    diagonal 16-blocks by substitution, the rest by 16x16 products), then
 //    Tm, E2, G2, E1.  Rows past the sequence end have beta = 0, so their rows
-//    and columns of W are those of I and their rows of Tm, G2 are zero.
+//    and columns of W are those of I and their rows of Tm, G2 are zero.  The
+//    forward (FWD) keeps tril_0(Q K^T) in the E2 slot and Tm V = W diag(beta) V
+//    in the E1 slot (v is read only then), and writes no Tm.
 template <int D, bool FWD>
 __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ q, const float* __restrict__ k,
-                                                      const float* __restrict__ beta, int T, int n_chunks,
-                                                      float* __restrict__ pre) {
+                                                      const float* __restrict__ v, const float* __restrict__ beta,
+                                                      int T, int n_chunks, float* __restrict__ pre) {
   constexpr int S = DB<D>::S, NT = D / 16;
   using P = Pre<D>;
   __shared__ __attribute__((aligned(16))) float sQ[CH * S];
@@ -200,9 +202,12 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
   __shared__ __attribute__((aligned(16))) float sTmp[3 * 16 * 17];
   __shared__ float sB[CH];
   float* const sWm = D == 64 ? sQ : sWx;  // W; at d = 64 it takes the place of Q, read before it is written
+  float* const sVv = D == 64 ? sM : sQ;   // FWD: the V rows, once M (or Q) is no longer read
   const int c = blockIdx.x, bh = blockIdx.y;
   const int t0 = c * CH, L = min(CH, T - t0);
   const int w = wave_id(), l = lane_id(), col = l & 15, rq = (l >> 4) * 4;
+  Rows<D> xv;  // FWD: the V rows, loaded now and staged after the inversion
+  if constexpr (FWD) xv.load(v + ((long)bh * T + t0) * D, D, 0, L);
   {
     Rows<D> xq, xk;
     xq.load(q + ((long)bh * T + t0) * D, D, 0, L);
@@ -267,10 +272,16 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
     }
     __syncthreads();
   }
+  if constexpr (FWD) {
+    xv.put(sVv, S);
+    __syncthreads();
+  }
   float* out = pre + ((long)bh * n_chunks + c) * P::SIZE;
-  for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) {
-    const int r = i / CH, cc = i % CH;
-    out[P::TM + i] = sWm[r * SW + cc] * sB[cc];
+  if constexpr (!FWD) {  // the forward reads Tm V only
+    for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) {
+      const int r = i / CH, cc = i % CH;
+      out[P::TM + i] = sWm[r * SW + cc] * sB[cc];
+    }
   }
   if constexpr (FWD) {  // the forward keeps tril_0(Q K^T) itself in the E2 slot
     for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) out[P::E2 + i] = sA[(i / CH) * SW + i % CH];
@@ -291,6 +302,10 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
       floatx4 e = wmma_k4<CH>(sWm + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = e[i];
+    } else {  // Tm V = W diag(beta) V
+      floatx4 u = wave_mma_f32_scaled<CH>(sWm + 16 * w * SW, SW, 1, sB, sVv + 16 * t, S, 1, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = u[i];
     }
   }
 }
@@ -779,7 +794,7 @@ hipError_t run_delta_backward(const float* q, const float* k, const float* v, co
   float* pre = reinterpret_cast<float*>(ws);
   float* Sc = pre + (long)BH * nC * Pre<D>::SIZE;
   float* dSc = Sc + (long)BH * nC * D * D;
-  hipLaunchKernelGGL((delta_bwd_prep<D, false>), dim3(nC, BH), dim3(256), 0, s, q, k, beta, T, nC, pre);
+  hipLaunchKernelGGL((delta_bwd_prep<D, false>), dim3(nC, BH), dim3(256), 0, s, q, k, nullptr, beta, T, nC, pre);
   if constexpr (D == 128) {
     hipLaunchKernelGGL((delta_bwd_fwd_walk<D>), dim3(D / SL, BH), dim3(256), 0, s, k, v, T, nC, S0, pre, Sc);
     hipLaunchKernelGGL((delta_bwd_rev_walk<D>), dim3(D / SL, BH), dim3(256), 0, s, q, k, dO, beta, T, nC, dSf, pre,
@@ -801,28 +816,26 @@ hipError_t run_delta_backward(const float* q, const float* k, const float* v, co
 
 // ---------------------------------------------------------------------------
 // The forward itself (fp32, d <= 128) on the same prep: per chunk, with A =
-// tril_0(Q K^T) kept by the prep in place of E2,
+// tril_0(Q K^T) kept by the prep in place of E2 and Tm V in place of E1,
 //   U = Tm V - G2 S0^T,   O = Q S0^T + A U,   S1 = S0 + U^T K,
 // per (16-row slice of S, b, h), chunks in order, the next chunk prefetched
 // into registers.  O's columns j0.. come from the slice (row j of S only
 // sees column j of V, U and O).  The products are formed transposed, so that
 // every MFMA operand is an LDS row contiguous in k (mma_rows: one 16-byte
 // read feeds four MFMAs): wave w takes the chunk's tokens 16w..16w+15 in
-//   U^T = V^T Tm^T - S G2^T,   O^T = S Q^T + U^T A^T,
+//   U^T = (Tm V)^T - S G2^T,   O^T = S Q^T + U^T A^T,
 // and the state tile (slice rows, d_k columns 16w..) in S += U^T K.
 template <int D>
 __global__ __launch_bounds__(256) void delta_fwd_walk(const float* __restrict__ q, const float* __restrict__ k,
-                                                      const float* __restrict__ v, int T, int n_chunks,
-                                                      const float* __restrict__ S0, const float* __restrict__ pre,
-                                                      float* __restrict__ o, float* __restrict__ S_final) {
+                                                      int T, int n_chunks, const float* __restrict__ S0,
+                                                      const float* __restrict__ pre, float* __restrict__ o,
+                                                      float* __restrict__ S_final) {
   constexpr int S = DB<D>::S;
   using P = Pre<D>;
   __shared__ __attribute__((aligned(16))) float sS[SL * S];        // the slice [16][D]
   __shared__ __attribute__((aligned(16))) float sGQ[2][CH * S];    // G2, Q rows [64][D]
   __shared__ __attribute__((aligned(16))) float sKt[D * SW];       // K^T [D][64]
-  __shared__ __attribute__((aligned(16))) float sVt[SL * SW];      // V^T of the slice [16][64]
   __shared__ __attribute__((aligned(16))) float sUt[SL * SW];      // U^T [16][64]
-  __shared__ __attribute__((aligned(16))) float sT[CH * SW];       // Tm
   __shared__ __attribute__((aligned(16))) float sA[CH * SW];       // tril_0(Q K^T)
   const int j0 = blockIdx.x * SL, bh = blockIdx.y;
   const int w = wave_id(), l = lane_id(), r = l & 15, g = l >> 4;
@@ -831,17 +844,16 @@ __global__ __launch_bounds__(256) void delta_fwd_walk(const float* __restrict__ 
     sS[rr * S + cc] = S0 != nullptr ? S0[((long)bh * D + j0 + rr) * D + cc] : 0.f;
   }
   Rows<D> pq, pk, pg;
-  Rows<SL> pv;
-  Rows<CH> pt, pa;
+  Rows<CH> pa;
+  float4 tv;  // (Tm V)[token 16 w + r][j0 + 4 g ..] of the chunk
   auto fetch = [&](int c) {
     const int t0 = c * CH, L = min(CH, T - t0);
     const float* pc = pre + ((long)bh * n_chunks + c) * P::SIZE;
     pq.load(q + ((long)bh * T + t0) * D, D, 0, L);
     pk.load(k + ((long)bh * T + t0) * D, D, 0, L);
-    pv.load(v + ((long)bh * T + t0) * D, D, j0, L);
-    pt.load(pc + P::TM, CH, 0, CH);
     pa.load(pc + P::E2, CH, 0, CH);
     pg.load(pc + P::G2, D, 0, CH);
+    tv = *reinterpret_cast<const float4*>(pc + P::E1 + (16 * w + r) * D + j0 + 4 * g);
   };
   // a [64][NC] row block into LDS transposed ([NC][64], row stride SW)
   auto put_t = [](float* dst, const float4* x, int n4, int nc) __attribute__((always_inline)) {
@@ -862,14 +874,12 @@ __global__ __launch_bounds__(256) void delta_fwd_walk(const float* __restrict__ 
     pg.put(sGQ[0], S);
     pq.put(sGQ[1], S);
     put_t(sKt, pk.x, Rows<D>::N, D);
-    put_t(sVt, pv.x, Rows<SL>::N, SL);
-    pt.put(sT, SW);
     pa.put(sA, SW);
+    const float ut[4] = {tv.x, tv.y, tv.z, tv.w};  // (Tm V)^T: slice rows 4g + i, token 16w + r
     __syncthreads();
     if (c + 1 < n_chunks) fetch(c + 1);
-    floatx4 gq[2] = {zero4(), zero4()}, ut = zero4();
+    floatx4 gq[2] = {zero4(), zero4()};
     mma_rows<D, 2>(sS, S, sGQ[0] + 16 * w * S, CH * S, S, gq);  // S G2^T, S Q^T (tokens 16w..)
-    mma_rows<CH, 1>(sVt, SW, sT + 16 * w * SW, 0, SW, &ut);     // V^T Tm^T
     // element i of lane (r, g): slice row 4g + i, token 16w + r
 #pragma unroll
     for (int i = 0; i < 4; ++i) sUt[(4 * g + i) * SW + 16 * w + r] = ut[i] - gq[0][i];
@@ -903,9 +913,9 @@ hipError_t run_delta_forward(const float* q, const float* k, const float* v, con
                              const float* S0, float* o, float* S_final, char* ws, hipStream_t s) {
   const int BH = B * H, nC = (T + CH - 1) / CH;
   float* pre = reinterpret_cast<float*>(ws);
-  hipLaunchKernelGGL((delta_bwd_prep<D, true>), dim3(nC, BH), dim3(256), 0, s, q, k, beta, T, nC, pre);
+  hipLaunchKernelGGL((delta_bwd_prep<D, true>), dim3(nC, BH), dim3(256), 0, s, q, k, v, beta, T, nC, pre);
   profile_mark_before(s);
-  hipLaunchKernelGGL((delta_fwd_walk<D>), dim3(D / SL, BH), dim3(256), 0, s, q, k, v, T, nC, S0, pre, o, S_final);
+  hipLaunchKernelGGL((delta_fwd_walk<D>), dim3(D / SL, BH), dim3(256), 0, s, q, k, T, nC, S0, pre, o, S_final);
   profile_mark_after(s);
   return hipGetLastError();
 }
