@@ -274,6 +274,11 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
   }
   if constexpr (FWD) {
     xv.put(sVv, S);
+    // the forward needs Tm = W diag(beta) only: scaled in place
+    for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) {
+      const int r = i / CH, cc = i % CH;
+      sWm[r * SW + cc] *= sB[cc];
+    }
     __syncthreads();
   }
   float* out = pre + ((long)bh * n_chunks + c) * P::SIZE;
@@ -295,17 +300,21 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {  // G2 = W diag(beta) K (and E1 = W^T K for the backward)
-    floatx4 g = wave_mma_f32_scaled<CH>(sWm + 16 * w * SW, SW, 1, sB, sK + 16 * t, S, 1, zero4());
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
     if constexpr (!FWD) {
+      floatx4 g = wave_mma_f32_scaled<CH>(sWm + 16 * w * SW, SW, 1, sB, sK + 16 * t, S, 1, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
       floatx4 e = wmma_k4<CH>(sWm + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = e[i];
-    } else {  // Tm V = W diag(beta) V
-      floatx4 u = wave_mma_f32_scaled<CH>(sWm + 16 * w * SW, SW, 1, sB, sVv + 16 * t, S, 1, zero4());
+    } else {  // sWm holds Tm: G2 = Tm K and Tm V, with Tm rows read 16 bytes at a time
+      floatx4 g = wmma_k4<CH>(sWm + 16 * w * SW, SW, 1, sK + 16 * t, S, 1, zero4());
+      floatx4 u = wmma_k4<CH>(sWm + 16 * w * SW, SW, 1, sVv + 16 * t, S, 1, zero4());
 #pragma unroll
-      for (int i = 0; i < 4; ++i) out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = u[i];
+      for (int i = 0; i < 4; ++i) {
+        out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
+        out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = u[i];
+      }
     }
   }
 }
