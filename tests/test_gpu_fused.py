@@ -105,3 +105,25 @@ def test_fused_fp32_prefill_workload_sampled_rows():
     ref = O.tc_fused_rows(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64), x["eta"],
                           g.astype(np.float64), w.W, rows)
     check("y rows", y[:, :, rows], ref, 1e-5)
+
+
+def test_fused_layer_f32_full_size_sampled_rows_and_a_whole_head():
+    # the fp32-input layer at the headline shape (the bf16 workload's values held in fp32), as bench.py runs it:
+    # the four-piece fp32 scan, then the fp32-MFMA window softmax with the gate
+    w = I.WORKLOADS["fused_layer_bf16"]
+    print("[case] fused fp32 full size", flush=True)
+    x = I.draw_workload("fused_layer_bf16")
+    y, A = ops.tc_fused_layer(*(to_dev(x[n + "64"], "f32") for n in ("q", "k", "v")), f32_dev(x["lam"]),
+                              f32_dev(x["eta"]), f32_dev(x["g"]), w.W, return_state=True)
+    torch.cuda.synchronize()
+    y, A = y.cpu().numpy(), A.cpu().numpy()
+    rows = [0, 1, 31, 32, w.W - 1, w.W, w.W + 1, 4097, 16383, 16384, 30000, w.T - 1]
+    ref = O.tc_fused_rows(x["q64"], x["k64"], x["v64"], x["lam"].astype(np.float64), x["eta"],
+                          x["g"].astype(np.float64), w.W, rows)
+    check("y rows", y[:, :, rows], ref, 1e-5)
+    h = 9
+    y_h, A_h = O.tc_fused(x["q64"][:, h:h + 1], x["k64"][:, h:h + 1], x["v64"][:, h:h + 1],
+                          x["lam"][h:h + 1].astype(np.float64), x["eta"][h:h + 1],
+                          x["g"][h:h + 1].astype(np.float64), w.W)
+    check(f"y head {h}", y[:, h:h + 1], y_h, 1e-5)
+    check(f"A head {h}", A[:, h:h + 1], A_h, 1e-5)

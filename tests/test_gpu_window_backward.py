@@ -75,3 +75,25 @@ def test_window_backward_repeat_is_deterministic():
     b = ops.tc_window_attention_backward(*args, 200, dy)
     for name, u, w in zip(("dq", "dk", "dv"), a, b):
         same_bits(name, u, w)
+
+
+def test_fused_layer_backward_f32_prefill_workload_two_heads():
+    # the fp32 layer backward at the batched prefill shape (B=4, H=8, T=4096, d=64, W=512), as bench.py runs it;
+    # heads 0 and 5 of every sequence against the oracle (the per-head sums over the whole batch)
+    w = I.WORKLOADS["prefill_scan_f32"]
+    print("[case] fused backward fp32 prefill workload", flush=True)
+    x = I.draw_workload(w.name)
+    g = np.random.default_rng(3).standard_normal(w.H).astype(np.float32)
+    dy = I.draw_cotangent(w.B, w.H, w.T, w.d, seed=w.seed)
+    got = ops.tc_fused_layer_backward(*(to_dev(x[n], "f32") for n in ("q", "k", "v")), f32_dev(x["lam"]),
+                                      f32_dev(x["eta"]), f32_dev(g), w.W, f32_dev(dy))
+    torch.cuda.synchronize()
+    hs = [0, 5]
+    sl = (slice(None), hs)
+    ref = O.tc_fused_backward(x["q64"][sl], x["k64"][sl], x["v64"][sl], x["lam"][hs].astype(np.float64),
+                              x["eta"][hs].astype(np.float64), g[hs].astype(np.float64), w.W,
+                              dy[sl].astype(np.float64))
+    for name, a, b in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        check(name, a.cpu().numpy()[sl], b, 1e-5)
+    for name, a, b in zip(("dlam", "deta", "dg"), got[3:], ref[3:]):
+        check(name, a.cpu().numpy()[hs], b, 1e-5)
