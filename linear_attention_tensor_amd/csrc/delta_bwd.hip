@@ -50,20 +50,6 @@ struct DB {
   static constexpr int SV = SL + 4;  // row stride of [64][16] slice arrays
 };
 
-// C += A diag(s) B over K (A[m][k] at pa + m am + k ak, s[k], B[k][n] at pb + k bk + n bn)
-template <int K>
-__device__ __forceinline__ floatx4 wave_mma_f32_scaled(const float* pa, int am, int ak, const float* s,
-                                                       const float* pb, int bk, int bn, floatx4 c) {
-  const int l = lane_id();
-  const int r = l & 15, kk = l >> 4;
-  const float* a = pa + r * am + kk * ak;
-  const float* b = pb + kk * bk + r * bn;
-  const float* sk = s + kk;
-#pragma unroll 8
-  for (int k0 = 0; k0 < K; k0 += 4) c = mfma4(a[k0 * ak] * sk[k0], b[k0 * bk], c);
-  return c;
-}
-
 // rows [0, 64) x [0, NC) of a row-major source (row stride ld, first column
 // col0) into LDS (stride dst_ld); rows >= nvalid become zero.
 // C += A B over K (a multiple of 16), A[m][k] at pa + m am + k ak, B[k][n] at
@@ -282,31 +268,43 @@ __global__ __launch_bounds__(256) void delta_bwd_prep(const float* __restrict__ 
     __syncthreads();
   }
   float* out = pre + ((long)bh * n_chunks + c) * P::SIZE;
+  float* const sWt = sM;  // backward: W^T ([64][SW]), once M is no longer read
   if constexpr (!FWD) {  // the forward reads Tm V only
     for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) {
       const int r = i / CH, cc = i % CH;
-      out[P::TM + i] = sWm[r * SW + cc] * sB[cc];
+      const float x = sWm[r * SW + cc];
+      out[P::TM + i] = x * sB[cc];
+      sWt[cc * SW + r] = x;
     }
+    __syncthreads();
   }
   if constexpr (FWD) {  // the forward keeps tril_0(Q K^T) itself in the E2 slot
     for (int i = threadIdx.x; i < CH * CH; i += blockDim.x) out[P::E2 + i] = sA[(i / CH) * SW + i % CH];
   } else {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {  // E2 = W^T A^T
-      floatx4 e = wmma_k4<CH>(sWm + 16 * w, 1, SW, sA + 16 * ct * SW, 1, SW, zero4());
+    for (int ct = 0; ct < 4; ++ct) {  // E2 = W^T A^T, W^T rows read 16 bytes at a time
+      floatx4 e = wmma_k4<CH>(sWt + 16 * w * SW, SW, 1, sA + 16 * ct * SW, 1, SW, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[P::E2 + (16 * w + rq + i) * CH + 16 * ct + col] = e[i];
     }
   }
+  if constexpr (!FWD) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {  // G2 = W diag(beta) K (and E1 = W^T K for the backward)
-    if constexpr (!FWD) {
-      floatx4 g = wave_mma_f32_scaled<CH>(sWm + 16 * w * SW, SW, 1, sB, sK + 16 * t, S, 1, zero4());
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
-      floatx4 e = wmma_k4<CH>(sWm + 16 * w, 1, SW, sK + 16 * t, S, 1, zero4());
+    for (int t = 0; t < NT; ++t) {  // E1 = W^T K
+      floatx4 e = wmma_k4<CH>(sWt + 16 * w * SW, SW, 1, sK + 16 * t, S, 1, zero4());
 #pragma unroll
       for (int i = 0; i < 4; ++i) out[P::E1 + (16 * w + rq + i) * D + 16 * t + col] = e[i];
+    }
+    __syncthreads();  // every wave is done with K itself
+    for (int i = threadIdx.x; i < CH * D; i += blockDim.x) sK[(i / D) * S + i % D] *= sB[i / D];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {  // G2 = W diag(beta) K (and the forward's Tm V)
+    if constexpr (!FWD) {  // sK holds diag(beta) K
+      floatx4 g = wmma_k4<CH>(sWm + 16 * w * SW, SW, 1, sK + 16 * t, S, 1, zero4());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[P::G2 + (16 * w + rq + i) * D + 16 * t + col] = g[i];
     } else {  // sWm holds Tm: G2 = Tm K and Tm V, with Tm rows read 16 bytes at a time
       floatx4 g = wmma_k4<CH>(sWm + 16 * w * SW, SW, 1, sK + 16 * t, S, 1, zero4());
       floatx4 u = wmma_k4<CH>(sWm + 16 * w * SW, SW, 1, sVv + 16 * t, S, 1, zero4());
