@@ -987,7 +987,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+              "(each GPU would run its own share of the heads); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 

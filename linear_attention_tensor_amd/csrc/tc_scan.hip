@@ -34,7 +34,8 @@ namespace {
 constexpr int CH = 64;  // positions per chunk
 
 // ---------------------------------------------------------------------------
-// d <= 64: one workgroup (4 waves) per (segment, b, h) owns the whole d_v.
+// d <= 64: one workgroup (4 waves; 8 for the d = 64 walks below) per
+// (segment, b, h) owns the whole d_v.
 // Every product reads both operands k-contiguous from LDS: the k order is
 // permuted so that MFMA 4J + s takes k = 16J + 4g + s from lane (row, g),
 // and one 16-byte read per operand feeds four MFMAs.  The state S^T
