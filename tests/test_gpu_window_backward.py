@@ -97,3 +97,24 @@ def test_fused_layer_backward_f32_prefill_workload_two_heads():
         check(name, a.cpu().numpy()[sl], b, 1e-5)
     for name, a, b in zip(("dlam", "deta", "dg"), got[3:], ref[3:]):
         check(name, a.cpu().numpy()[hs], b, 1e-5)
+
+
+def test_fused_layer_backward_bf16_full_size_one_head():
+    # the whole layer's backward at the headline size (B=1, H=16, T=32768, d=128, W=1024, bf16), as bench.py
+    # runs it; one whole head (every row of dq, dk, dv and its dlam, deta, dg) against the oracle
+    w = I.WORKLOADS["fused_layer_bf16"]
+    print("[case] fused backward bf16 full size", flush=True)
+    x = I.draw_workload(w.name)
+    dy = I.draw_cotangent(w.B, w.H, w.T, w.d, seed=w.seed)
+    got = ops.tc_fused_layer_backward(*(to_dev(x[n], "bf16") for n in ("q", "k", "v")), f32_dev(x["lam"]),
+                                      f32_dev(x["eta"]), f32_dev(x["g"]), w.W, f32_dev(dy))
+    torch.cuda.synchronize()
+    h = 3
+    sl = (slice(None), slice(h, h + 1))
+    ref = O.tc_fused_backward(x["q64"][sl], x["k64"][sl], x["v64"][sl], x["lam"][h:h + 1].astype(np.float64),
+                              x["eta"][h:h + 1].astype(np.float64), x["g"][h:h + 1].astype(np.float64), w.W,
+                              dy[sl].astype(np.float64))
+    for name, a, b in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        check(f"{name} head {h}", a.cpu().numpy()[sl], b, TOL["bf16"])
+    for name, a, b in zip(("dlam", "deta", "dg"), got[3:], ref[3:]):
+        check(f"{name} head {h}", a.cpu().numpy()[h:h + 1], b, TOL["bf16"])
