@@ -57,7 +57,7 @@ def _check_tensor(name: str, t: torch.Tensor, shape, dtype=None, device=None) ->
 
 
 def _check_unit_interval(name: str, t: torch.Tensor) -> None:
-    # Reading the verdict back synchronises with the device, which a stream
+    # Reading the check's result back synchronises with the device, which a stream
     # under graph capture forbids: there the check is skipped (as with
     # check_values=False, which latency-bound callers pass anyway).
     if not t.numel() or torch.cuda.is_current_stream_capturing():

@@ -16,7 +16,7 @@ Each old key reads its memory, r = k A, and the pair is recalled when the
 read has its largest inner product with its own value among all the
 sequence's values.
 
-Readings (listed in the design doc): ingest-all is modelled by the same write with
+Readings: ingest-all is modelled by the same write with
 window 1; a tie counts as the smallest index.
 """
 from __future__ import annotations

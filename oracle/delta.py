@@ -6,7 +6,7 @@ Page: "DeltaNet-family linear attention variants" (molayo1419.me).  The state
 S is d_v x d_k (the core-identity section stores the summed outer products
 |v><k| in a fixed d_v x d_k state), so a write is v k^T and a read is S q.
 
-Readings taken where the page is silent (listed in the design doc): the output of
+Readings taken where the page is silent: the output of
 step t is read after that step's write, o_t = S_t q_t; S starts at zero unless
 an initial state is passed.
 """

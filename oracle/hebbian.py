@@ -13,7 +13,7 @@ B = (1/F) sum_i v_{f(i)} phi(k_i)^T and the MLP is MLP(x) = B phi(x).  The
 fact i is stored when, fed k_i, the output has its largest inner product with
 v_{f(i)} among all value embeddings.
 
-Readings taken where the page is silent (listed in the design doc): A and G have
+Readings taken where the page is silent: A and G have
 independent N(0, 1) entries; a tie in the largest inner product counts as
 the smallest index.
 """

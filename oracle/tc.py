@@ -10,7 +10,7 @@ Shapes: q, k [B, H, T, dk]; v [B, H, T, dv]; per-head lam, eta, g [H].
 A is the per-head L2 matrix [B, H, dk, dv]; k (x) v is the outer product
 k v^T and the read is the row vector q A.
 
-Readings taken where the page is silent (each one is listed in the design doc):
+Readings taken where the page is silent:
 
 * the L1 window of query t holds the W most recent tokens, the current one
   included: positions max(0, t-W+1) .. t;
