@@ -120,11 +120,13 @@ tc_status tc_scan_forward_noalloc(const void* q, const void* k, const void* v, t
  * Supported: dk == dv in {16, 32, 64, 128}, chunk = 64; anything else is
  * TC_ERR_UNSUPPORTED.  d = 128 runs as four d = 64 problems, one per pair of
  * column halves (q and k columns of one half, v and dm columns of one half:
- * the read is a sum of those four), whose gradients are added; the workspace
- * then also holds the gathered halves (11 * B*H*T*64 floats).  bf16 inputs
- * are widened to fp32 copies inside the workspace first (exact), so the
- * gradients are those of the bf16 values at fp32 accuracy; the workspace
- * query includes the copies.  dlam at lam = 0 is the one-sided derivative.
+ * the read is a sum of those four), whose gradients are added.  bf16 inputs:
+ * dq, dlam, deta and dg come from the fp32 kernels on fp32 copies of q, k, v
+ * made inside the workspace (exact), so at fp32 accuracy; with d in {64,
+ * 128}, dk and dv come from two bf16 forward reads of the time-reversed
+ * sequences (q, k, v and sigmoid(g) dm reversed into the workspace as bf16),
+ * so at the accuracy of bf16 inputs.  The workspace query includes all of
+ * these copies.  dlam at lam = 0 is the one-sided derivative.
  * ------------------------------------------------------------------------- */
 size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk,
                                         tc_dtype dt);

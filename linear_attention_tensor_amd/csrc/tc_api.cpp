@@ -228,10 +228,29 @@ static tc_status check_scan_bwd(const char* fn, int B, int H, int T, int dk, int
 // per-head terms over all four.  The d = 64 kernels read the halves in place
 // (rows 128 floats apart) and add into the halves of the outputs, so the
 // workspace is the d = 64 backward's (plus the widened copies for bf16).
-static size_t scan_bwd_need(int B, int H, int T, int d, int W, tc_dtype dt) {
+//
+// bf16 inputs with d in {64, 128}: the reverse direction (dk, dv) runs on the
+// bf16 forward scan instead of the fp32 kernels.  For t >= i + W the weight of
+// the pair (t, i) is eta lam^(t - W - i); with t' = T - 1 - t, i' = T - 1 - i
+// that is eta lam^(i' - W - t') over t' <= i' - W, so on the time-reversed
+// sequences (primed)
+//   dv'_i' = sum_{t' <= i' - W} eta lam^(i' - W - t') <k'_i', q'_t'> dm'_t'  = read(q = k', k = q', v = dm'),
+//   dk'_i' = sum_{t' <= i' - W} eta lam^(i' - W - t') <v'_i', dm'_t'> q'_t' = read(q = v', k = dm', v = q'),
+// and rows i' < W (i >= T - W) are 0 in both.  The workspace then also holds
+// q', k', v', dm' (bf16) and the scan's own workspace.
+static bool scan_bwd_rev16(int d, tc_dtype dt, int T) { return dt == TC_BF16 && (d == 64 || d == 128) && T > 0; }
+static size_t rev16_bytes(int B, int H, int T, int d) { return round_up_256((size_t)B * H * T * d * sizeof(uint16_t)); }
+
+static size_t scan_bwd_need_fp32(int B, int H, int T, int d, int W, tc_dtype dt) {
   const size_t base = tc::scan_bwd_ws_bytes(B, H, T, d, W);
   if (d == 128) return (dt == TC_BF16 ? 3 * widened_bytes(B, H, T, d) : 0) + round_up_256(base);
   return dt == TC_BF16 ? round_up_256(base) + 3 * widened_bytes(B, H, T, d) : base;
+}
+
+static size_t scan_bwd_need(int B, int H, int T, int d, int W, tc_dtype dt) {
+  const size_t fp32 = scan_bwd_need_fp32(B, H, T, d, W, dt);
+  if (!scan_bwd_rev16(d, dt, T)) return fp32;
+  return round_up_256(fp32) + 4 * rev16_bytes(B, H, T, d) + round_up_256(tc::scan_bf16_ws_bytes(B, H, T, d, W));
 }
 
 size_t tc_scan_backward_workspace_bytes(int B, int H, int T, int dk, int dv, int W, int chunk,
@@ -278,15 +297,24 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
       k32 = tmp[1];
       v32 = tmp[2];
     }
-    if (dk == 128) {
-      char* w = static_cast<char*>(ws) + (dt == TC_BF16 ? 3 * widened_bytes(B, H, T, dk) : 0);
-      return from_hip(tc::launch_tc_scan_backward(q32, k32, v32, lam, eta, g, B, H, T, 128, W, dm, dq, dk_out,
-                                                  dv_out, dlam, deta, dg, w, s),
-                      fn);
-    }
-    return from_hip(tc::launch_tc_scan_backward(q32, k32, v32, lam, eta, g, B, H, T, dk, W, dm, dq, dk_out,
-                                                dv_out, dlam, deta, dg, ws, s),
-                    fn);
+    const bool rev16 = scan_bwd_rev16(dk, dt, T);
+    char* w = static_cast<char*>(ws) + (dk == 128 && dt == TC_BF16 ? 3 * widened_bytes(B, H, T, dk) : 0);
+    hipError_t e = tc::launch_tc_scan_backward(q32, k32, v32, lam, eta, g, B, H, T, dk, W, dm, dq, dk_out, dv_out,
+                                               dlam, deta, dg, w, s, rev16);
+    if (e != hipSuccess || !rev16) return from_hip(e, fn);
+    // reverse direction on the bf16 scan (see scan_bwd_need)
+    char* r = static_cast<char*>(ws) + round_up_256(scan_bwd_need_fp32(B, H, T, dk, W, dt));
+    const size_t rb = rev16_bytes(B, H, T, dk);
+    void *qr = r, *kr = r + rb, *vr = r + 2 * rb, *gr = r + 3 * rb, *sws = r + 4 * rb;
+    const void* src[3] = {q, k, v};
+    void* dst[3] = {qr, kr, vr};
+    for (int i = 0; i < 3 && e == hipSuccess; ++i) e = tc::launch_reverse_rows_bf16(src[i], dst[i], B * H, T, dk, s);
+    if (e == hipSuccess) e = tc::launch_reverse_rows_f32(dm, g, H, gr, B * H, T, dk, s);
+    if (e == hipSuccess)
+      e = tc::launch_tc_scan_bf16(kr, qr, gr, lam, eta, B, H, T, dk, W, dv_out, nullptr, sws, s, true);
+    if (e == hipSuccess)
+      e = tc::launch_tc_scan_bf16(vr, gr, qr, lam, eta, B, H, T, dk, W, dk_out, nullptr, sws, s, true);
+    return from_hip(e, fn);
   });
 }
 

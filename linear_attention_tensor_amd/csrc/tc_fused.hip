@@ -337,7 +337,9 @@ __device__ __forceinline__ void load_read_unit(ReadUnitRegs<D>& R, const uint16_
 // and Q are loaded at the top of their unit.  (Loading more of the next unit
 // ahead, or loading V^T and S^T ahead of the current unit's stores, made the
 // compiler spill: slower.)
-template <int D>
+// With REV the read of position t is stored in row T - 1 - t of m (a scan of
+// time-reversed inputs handing back rows in the original order).
+template <int D, bool REV>
 __global__ __launch_bounds__(NTHR) void scan_read_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v,
@@ -460,7 +462,7 @@ __global__ __launch_bounds__(NTHR) void scan_read_kernel(const uint16_t* __restr
     for (int nt = 0; nt < 2; ++nt) {
       const int t = t0 + r0 + 16 * nt + n;
       if (t >= T) continue;
-      float* out = m + ((long)bh * T + t) * D + 4 * g;
+      float* out = m + ((long)bh * T + (REV ? T - 1 - t : t)) * D + 4 * g;
 #pragma unroll
       for (int mt = 0; mt < D / 16; ++mt)
         *reinterpret_cast<float4*>(out + 16 * mt) = make_float4(o[mt][nt][0], o[mt][nt][1], o[mt][nt][2], o[mt][nt][3]);
@@ -502,7 +504,7 @@ hipError_t run_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
 template <int D>
 hipError_t run_scan_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, const float* lam,
                          const float* eta, int B, int H, const FusedGeom& G, float* m, float* A_final, void* ws,
-                         hipStream_t s) {
+                         bool rev_out, hipStream_t s) {
   const int BH = B * H;
   const size_t ne = state_elems(G, B, H, D);
   uint16_t* delta = static_cast<uint16_t*>(ws);
@@ -514,7 +516,12 @@ hipError_t run_scan_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v
   // persistent: as many workgroups as fit at once (LDS: one per CU at d = 128, two at d = 64)
   const int n_units = G.n_tiles * BH;
   const int grid = std::min<int>(n_units, kComputeUnits * (D == 128 ? 1 : 2));
-  hipLaunchKernelGGL(scan_read_kernel<D>, dim3(grid), dim3(NTHR), 0, s, q, k, v, sst, lam, eta, H, G, n_units, m);
+  if (rev_out)
+    hipLaunchKernelGGL((scan_read_kernel<D, true>), dim3(grid), dim3(NTHR), 0, s, q, k, v, sst, lam, eta, H, G,
+                       n_units, m);
+  else
+    hipLaunchKernelGGL((scan_read_kernel<D, false>), dim3(grid), dim3(NTHR), 0, s, q, k, v, sst, lam, eta, H, G,
+                       n_units, m);
   profile_mark_after(s);
   return hipGetLastError();
 }
@@ -531,13 +538,14 @@ size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W) {
 bool scan_bf16_fast(bool bf16, int dk, int dv, int T) { return bf16 && dk == dv && (dk == 64 || dk == 128) && T > 0; }
 
 hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, const float* lam, const float* eta,
-                               int B, int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s) {
+                               int B, int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s,
+                               bool rev_out) {
   const FusedGeom G = make_geom(T, W);
   const uint16_t* Q = static_cast<const uint16_t*>(q);
   const uint16_t* K = static_cast<const uint16_t*>(k);
   const uint16_t* V = static_cast<const uint16_t*>(v);
-  if (d == 128) return run_scan_bf16<128>(Q, K, V, lam, eta, B, H, G, m, A_final, ws, s);
-  if (d == 64) return run_scan_bf16<64>(Q, K, V, lam, eta, B, H, G, m, A_final, ws, s);
+  if (d == 128) return run_scan_bf16<128>(Q, K, V, lam, eta, B, H, G, m, A_final, ws, rev_out, s);
+  if (d == 64) return run_scan_bf16<64>(Q, K, V, lam, eta, B, H, G, m, A_final, ws, rev_out, s);
   return hipErrorInvalidValue;
 }
 

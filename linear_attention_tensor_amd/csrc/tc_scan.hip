@@ -1108,10 +1108,12 @@ __global__ void scan_bwd_reduce(const double* __restrict__ part_eta, const doubl
 // in rows rs floats apart (the pointers point at the piece's first column);
 // add_qk / add_v / add_h add dq and dk / dv / dlam, deta, dg to what the
 // buffers hold instead of writing them (and leave the rows that no position
-// writes alone).
+// writes alone); fwd_only leaves out the reverse direction (dk and dv are
+// not touched).
 struct ScanBwdPiece {
   int rs;
   bool add_qk, add_v, add_h;
+  bool fwd_only = false;
 };
 
 // Segment contributions a d = 128 backward computes for its four pieces in
@@ -1132,9 +1134,11 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
   const long zq = std::min<long>(W, T);
   const long rs = pc.rs;
   if (n_act <= 0) {  // (otherwise the two direction kernels clear these rows)
-    if (!pc.add_qk || !pc.add_v)
+    float* zk = pc.add_qk || pc.fwd_only ? nullptr : dk;
+    float* zv = pc.add_v || pc.fwd_only ? nullptr : dv;
+    if (!pc.add_qk || zv != nullptr)
       hipLaunchKernelGGL(scan_bwd_zero_kernel, dim3(kZeroBlocks, BH), dim3(256), 0, s, pc.add_qk ? nullptr : dq,
-                         pc.add_qk ? nullptr : dk, pc.add_v ? nullptr : dv, (long)T, D, zq, 0L, rs);
+                         zk, zv, (long)T, D, zq, 0L, rs);
     if (!pc.add_h) {
       hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, dlam, H, 0.f);
       hipLaunchKernelGGL(fill_kernel, dim3((H + 255) / 256), dim3(256), 0, s, deta, H, 0.f);
@@ -1160,6 +1164,11 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
                      RowView<float>{dq + (long)W * rs, bs, rs}, (int)zq, part_eta, part_lam, pc.add_qk);
   profile_mark_after(s);
   // reverse direction: dk, dv (row r of each view is position n_act - 1 - r)
+  if (pc.fwd_only) {
+    hipLaunchKernelGGL(scan_bwd_reduce, dim3((H + 63) / 64), dim3(64), 0, s, part_eta, part_lam, eta, gate, B,
+                       H, p.n_seg, dlam, deta, dgate, pc.add_h);
+    return hipGetLastError();
+  }
   const long last = (long)(n_act - 1) * rs, tl = (long)(T - 1) * rs;
   const RowView<const float> rv{v + last, bs, -rs}, rk{k + last, bs, -rs}, rq{q + tl, bs, -rs},
       rg{dm + tl, bs, -rs};
@@ -1182,7 +1191,8 @@ hipError_t run_scan_backward(const float* q, const float* k, const float* v, con
 // forward states | their lam derivatives | reverse states, four pieces each).
 hipError_t run_scan_backward_128(const float* q, const float* k, const float* v, const float* lam, const float* eta,
                                  const float* gate, int B, int H, int T, int W, const float* dm, float* dq, float* dk,
-                                 float* dv, float* dlam, float* deta, float* dgate, char* ws, hipStream_t s) {
+                                 float* dv, float* dlam, float* deta, float* dgate, char* ws, hipStream_t s,
+                                 bool fwd_only) {
   constexpr int D = 128, PD = 64;
   const int BH = B * H;
   const ScanPlan p = plan_scan(B, H, T, PD, PD, W);
@@ -1202,8 +1212,9 @@ hipError_t run_scan_backward_128(const float* q, const float* k, const float* v,
                        p.n_act, p.seg_chunks, p.n_seg, fs, fd, fwd);
     const long tl = (long)(T - 1) * D;
     const RowView<const float> rg{dm + tl, bs, -D}, rq{q + tl, bs, -D};
-    launch_state_fast<PD, float>(dim3(p.n_seg - 1, 1, 4 * BH), rg, rq, lam, nullptr, H, p.n_act, p.seg_chunks,
-                                 p.n_seg, rs, rev, s);
+    if (!fwd_only)
+      launch_state_fast<PD, float>(dim3(p.n_seg - 1, 1, 4 * BH), rg, rq, lam, nullptr, H, p.n_act, p.seg_chunks,
+                                   p.n_seg, rs, rev, s);
     pre = BwdStates{fs, fd, rs};
   }
   hipError_t e = hipSuccess;
@@ -1212,7 +1223,7 @@ hipError_t run_scan_backward_128(const float* q, const float* k, const float* v,
       const int i = 2 * a + b;
       const long off = (long)i * BH * p.n_seg * PD * PD;
       const BwdStates pi = pre.fs ? BwdStates{pre.fs + off, pre.fd + off, pre.rs + off} : pre;
-      const ScanBwdPiece pc{D, b != 0, a != 0, i != 0};  // dq_a, dk_a: two b; dv_b: two a
+      const ScanBwdPiece pc{D, b != 0, a != 0, i != 0, fwd_only};  // dq_a, dk_a: two b; dv_b: two a
       e = run_scan_backward<PD>(q + 64 * a, k + 64 * a, v + 64 * b, lam, eta, gate, B, H, T, W, dm + 64 * b,
                                 dq + 64 * a, dk + 64 * a, dv + 64 * b, dlam, deta, dgate, ws, s, pc, pi);
     }
@@ -1356,15 +1367,16 @@ size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W) {
 hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
                                    const float* eta, const float* g, int B, int H, int T, int d, int W,
                                    const float* dm, float* dq, float* dk, float* dv, float* dlam,
-                                   float* deta, float* dg, void* ws, hipStream_t s) {
+                                   float* deta, float* dg, void* ws, hipStream_t s, bool forward_only) {
   char* w = static_cast<char*>(ws);
-  const ScanBwdPiece pc{d, false, false, false};
+  const ScanBwdPiece pc{d, false, false, false, forward_only};
   const BwdStates none{nullptr, nullptr, nullptr};
   switch (d) {
     case 16: return run_scan_backward<16>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc, none);
     case 32: return run_scan_backward<32>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc, none);
     case 64: return run_scan_backward<64>(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s, pc, none);
-    case 128: return run_scan_backward_128(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s);
+    case 128: return run_scan_backward_128(q, k, v, lam, eta, g, B, H, T, W, dm, dq, dk, dv, dlam, deta, dg, w, s,
+                                           forward_only);
     default: return hipErrorInvalidValue;
   }
 }

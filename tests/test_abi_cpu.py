@@ -273,12 +273,19 @@ def test_scan_backward_rejects():
     assert call(dg=FAKE) == _lib.TC_ERR_INVALID_ARG
     assert call(B=0) == _lib.TC_OK
     # d = 128 runs four d = 64 pieces in place: the d = 64 workspace (rounded to 256 bytes); bf16 adds the
-    # three widened copies
+    # three widened copies, and (d in {64, 128}) the four time-reversed bf16 copies and the bf16 read's own
+    # workspace
     w128 = lib().tc_scan_backward_workspace_bytes(1, 1, 10, 128, 128, 4, 64, _lib.TC_F32)
     w64 = lib().tc_scan_backward_workspace_bytes(1, 1, 10, 64, 64, 4, 64, _lib.TC_F32)
     assert w64 <= w128 == (w64 + 255) // 256 * 256
     w128b = lib().tc_scan_backward_workspace_bytes(1, 1, 10, 128, 128, 4, 64, _lib.TC_BF16)
-    assert w128b == w128 + 3 * ((10 * 128 * 4 + 255) // 256 * 256)
+    r256 = lambda n: (n + 255) // 256 * 256
+    assert w128b > w128 + 3 * r256(10 * 128 * 4) + 4 * r256(10 * 128 * 2)
+    w32b = lib().tc_scan_backward_workspace_bytes(1, 1, 10, 32, 32, 4, 64, _lib.TC_BF16)
+    w32 = lib().tc_scan_backward_workspace_bytes(1, 1, 10, 32, 32, 4, 64, _lib.TC_F32)
+    assert w32b == r256(w32) + 3 * r256(10 * 32 * 4)
+    # the query is exactly what the call checks
+    assert call(dt=_lib.TC_BF16, B=1, H=1, T=10, d=128, W=4, ws_bytes=w128b - 1) == _lib.TC_ERR_WORKSPACE
 
 
 def test_memory_entry_points_reject():

@@ -120,10 +120,12 @@ def test_scan_backward_through_the_gate(B, H, T, d, W):
 @pytest.mark.parametrize("B,H,T,d,W", [(2, 3, 300, 32, 17), (1, 2, 1000, 64, 100), (1, 1, 256, 16, 32),
                                        (1, 2, 400, 128, 70)])
 def test_scan_backward_bf16_inputs(B, H, T, d, W):
-    # bf16 q, k, v are widened to fp32 in the workspace: the gradients are those
-    # of the bf16 values.  Held to the bar for bf16 inputs (2e-2); dq, dk, dv
-    # and deta come out near 1e-6, dlam (a per-head sum with much cancellation
-    # when lam is near 1) has reached 2e-5 on this data.
+    # bf16 q, k, v are widened to fp32 in the workspace for dq, dlam and deta
+    # (and, at d in {16, 32}, for dk and dv): those are the gradients of the bf16
+    # values, near 1e-6 (dlam, a per-head sum with much cancellation when lam is
+    # near 1, has reached 2e-5).  At d in {64, 128} dk and dv come from bf16
+    # reads of the time-reversed sequences (about 2e-3).  Held to the bar for
+    # bf16 inputs (2e-2).
     print(f"[case] scan backward bf16 B={B} H={H} T={T} d={d} W={W}", flush=True)
     x = I.draw(B, H, T, d, seed=4300 + T + d, dtype="bf16")
     dm = I.draw_cotangent(B, H, T, d, seed=4300 + T + d)
@@ -134,3 +136,44 @@ def test_scan_backward_bf16_inputs(B, H, T, d, W):
                              x["eta"].astype(np.float64), W, dm.astype(np.float64))
     for name, a, b in zip(("dq", "dk", "dv", "dlam", "deta"), got, ref):
         check(f"bf16 {name}", a.cpu().numpy(), b, TOL_BF16)
+
+
+@pytest.mark.parametrize("B,H,T,d,W,gated", [
+    (1, 2, 1, 64, 4, False),      # one position, no eviction
+    (1, 1, 50, 128, 64, False),   # T < W: every gradient 0
+    (2, 2, 64, 64, 64, False),    # T = W
+    (1, 3, 600, 64, 1, False),    # W = 1, several 256-row tiles
+    (1, 2, 777, 128, 300, False),  # ragged last tile, evictions across tiles
+    (2, 1, 513, 128, 32, True),   # through the gate
+    (1, 2, 1100, 64, 257, True),
+])
+def test_scan_backward_bf16_reverse_reads(B, H, T, d, W, gated):
+    # bf16 inputs with d in {64, 128}: dk and dv come from two bf16 forward
+    # reads of the time-reversed sequences (cotangent scaled by the gate and
+    # rounded to bf16 on the way), the rest from the fp32 kernels.
+    print(f"[case] scan backward bf16 reversed reads B={B} H={H} T={T} d={d} W={W} gated={gated}", flush=True)
+    x = I.draw(B, H, T, d, seed=4700 + T + d + W, dtype="bf16")
+    dm = I.draw_cotangent(B, H, T, d, seed=4700 + T + d + W)
+    args = [to_dev(x[n], "bf16") for n in ("q", "k", "v")] + [f32_dev(x["lam"]), f32_dev(x["eta"]), W,
+                                                                f32_dev(dm)]
+    lam64, eta64 = x["lam"].astype(np.float64), x["eta"].astype(np.float64)
+    if gated:
+        g = np.linspace(-1.5, 2.0, H).astype(np.float32)
+        got = ops.tc_scan_backward(*args, g=f32_dev(g))
+        ref = O.tc_gated_read_backward(x["q64"], x["k64"], x["v64"], lam64, eta64, g.astype(np.float64), W,
+                                       dm.astype(np.float64))
+        names = ("dq", "dk", "dv", "dlam", "deta", "dg")
+    else:
+        got = ops.tc_scan_backward(*args)
+        ref = O.tc_scan_backward(x["q64"], x["k64"], x["v64"], lam64, eta64, W, dm.astype(np.float64))
+        names = ("dq", "dk", "dv", "dlam", "deta")
+    torch.cuda.synchronize()
+    for name, a, b in zip(names, got, ref):
+        a = a.cpu().numpy()
+        if not np.any(b):
+            assert not np.any(a), f"{name}: expected all zeros"
+            continue
+        check(f"bf16 reversed {name}", a, b, TOL_BF16)
+    # rows with no pair: dk, dv rows i >= T - W are exactly 0
+    z0 = max(T - W, 0)
+    assert not np.any(got[1].cpu().numpy()[:, :, z0:]) and not np.any(got[2].cpu().numpy()[:, :, z0:])
