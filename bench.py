@@ -990,6 +990,15 @@ def cpu_baseline_fused(x, T_sample=16384):
                       f"have shorter windows)"}
 
 
+class _Components(dict):
+    """Component results by name; each announces itself on stderr when it is
+    done, so that a long run shows its progress."""
+
+    def __setitem__(self, key, value):
+        print(f"[bench] {key} done", file=sys.stderr, flush=True)
+        super().__setitem__(key, value)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -1010,7 +1019,7 @@ def main():
                                                "copies": 2}}))
         return
     only = args.only
-    components = {}
+    components = _Components()
     if only in (None, "fused"):
         head, x = bench_fused(args.steps, args.warmup, dev)
     if only is None and not args.no_components:

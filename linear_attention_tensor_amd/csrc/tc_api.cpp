@@ -7,6 +7,7 @@
 
 #include "../../include/tc.h"
 #include "tc_kernels.hpp"
+#include "tc_bwd_paths.hpp"
 
 #include <stdarg.h>
 #include <stdint.h>
@@ -299,8 +300,10 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
     }
     const bool rev16 = scan_bwd_rev16(dk, dt, T);
     char* w = static_cast<char*>(ws) + (dk == 128 && dt == TC_BF16 ? 3 * widened_bytes(B, H, T, dk) : 0);
-    hipError_t e = tc::launch_tc_scan_backward(q32, k32, v32, lam, eta, g, B, H, T, dk, W, dm, dq, dk_out, dv_out,
-                                               dlam, deta, dg, w, s, rev16);
+    hipError_t e = rev16 ? tc::launch_tc_scan_backward_fwd_only(q32, k32, v32, lam, eta, g, B, H, T, dk, W, dm, dq,
+                                                                 dlam, deta, dg, w, s)
+                         : tc::launch_tc_scan_backward(q32, k32, v32, lam, eta, g, B, H, T, dk, W, dm, dq, dk_out,
+                                                       dv_out, dlam, deta, dg, w, s);
     if (e != hipSuccess || !rev16) return from_hip(e, fn);
     // reverse direction on the bf16 scan (see scan_bwd_need)
     char* r = static_cast<char*>(ws) + round_up_256(scan_bwd_need_fp32(B, H, T, dk, W, dt));
@@ -311,9 +314,9 @@ tc_status tc_scan_backward(const void* q, const void* k, const void* v, tc_dtype
     for (int i = 0; i < 3 && e == hipSuccess; ++i) e = tc::launch_reverse_rows_bf16(src[i], dst[i], B * H, T, dk, s);
     if (e == hipSuccess) e = tc::launch_reverse_rows_f32(dm, g, H, gr, B * H, T, dk, s);
     if (e == hipSuccess)
-      e = tc::launch_tc_scan_bf16(kr, qr, gr, lam, eta, B, H, T, dk, W, dv_out, nullptr, sws, s, true);
+      e = tc::launch_tc_scan_bf16_rev_out(kr, qr, gr, lam, eta, B, H, T, dk, W, dv_out, nullptr, sws, s);
     if (e == hipSuccess)
-      e = tc::launch_tc_scan_bf16(vr, gr, qr, lam, eta, B, H, T, dk, W, dk_out, nullptr, sws, s, true);
+      e = tc::launch_tc_scan_bf16_rev_out(vr, gr, qr, lam, eta, B, H, T, dk, W, dk_out, nullptr, sws, s);
     return from_hip(e, fn);
   });
 }

@@ -12,6 +12,7 @@
 // even bf16.
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
+#include "tc_bwd_paths.hpp"
 
 #include <algorithm>
 

@@ -19,6 +19,7 @@
 // Workspace: delta (bf16) | entering states (bf16).
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
+#include "tc_bwd_paths.hpp"
 #include "tc_mfma.hpp"
 #include "tc_dma.hpp"
 #include "tc_tr.hpp"
@@ -537,9 +538,9 @@ size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W) {
 
 bool scan_bf16_fast(bool bf16, int dk, int dv, int T) { return bf16 && dk == dv && (dk == 64 || dk == 128) && T > 0; }
 
-hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, const float* lam, const float* eta,
-                               int B, int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s,
-                               bool rev_out) {
+static hipError_t scan_bf16(const void* q, const void* k, const void* v, const float* lam, const float* eta, int B,
+                            int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s,
+                            bool rev_out) {
   const FusedGeom G = make_geom(T, W);
   const uint16_t* Q = static_cast<const uint16_t*>(q);
   const uint16_t* K = static_cast<const uint16_t*>(k);
@@ -547,6 +548,17 @@ hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, cons
   if (d == 128) return run_scan_bf16<128>(Q, K, V, lam, eta, B, H, G, m, A_final, ws, rev_out, s);
   if (d == 64) return run_scan_bf16<64>(Q, K, V, lam, eta, B, H, G, m, A_final, ws, rev_out, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, const float* lam, const float* eta,
+                               int B, int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s) {
+  return scan_bf16(q, k, v, lam, eta, B, H, T, d, W, m, A_final, ws, s, false);
+}
+
+hipError_t launch_tc_scan_bf16_rev_out(const void* q, const void* k, const void* v, const float* lam,
+                                       const float* eta, int B, int H, int T, int d, int W, float* m, float* A_final,
+                                       void* ws, hipStream_t s) {
+  return scan_bf16(q, k, v, lam, eta, B, H, T, d, W, m, A_final, ws, s, true);
 }
 
 hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const float* lam,

@@ -23,21 +23,13 @@ size_t scan_ws_bytes(const ScanPlan& p, int B, int H, int dk, int dv);
 // Backward of the read (fp32 inputs, d = dk = dv in {16, 32, 64, 128}; d = 128
 // runs as four d = 64 pieces over the column halves).
 size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W);
-// With forward_only the reverse direction (dk, dv) is left out: dk and dv are
-// not touched.
 hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
                                    const float* eta, const float* g, int B, int H, int T, int d, int W,
                                    const float* dm, float* dq, float* dk, float* dv, float* dlam,
-                                   float* deta, float* dg, void* ws, hipStream_t s, bool forward_only = false);
+                                   float* deta, float* dg, void* ws, hipStream_t s);
 
 // bf16 -> fp32 of n elements (tc_convert.hip); any alignment, any n.
 hipError_t launch_widen_bf16(const void* in, float* out, long n, hipStream_t s);
-// Time reversal of BH sequences of T rows of d elements (tc_convert.hip): row
-// t goes to row T - 1 - t of out, as bf16; the fp32 form multiplies the rows
-// of head bh % H by sigmoid(gate[bh % H]) (gate may be NULL: factor 1).
-hipError_t launch_reverse_rows_bf16(const void* in, void* out, int BH, int T, int d, hipStream_t s);
-hipError_t launch_reverse_rows_f32(const float* in, const float* gate, int H, void* out, int BH, int T, int d,
-                                   hipStream_t s);
 
 hipError_t launch_tc_scan(const void* q, const void* k, const void* v, bool bf16,
                           const float* lam, const float* eta, int B, int H, int T, int dk, int dv,
@@ -64,10 +56,8 @@ size_t fused_ws_bytes(int B, int H, int T, int dk, int dv, int W);
 // (tc_fused.hip); its workspace is scan_bf16_ws_bytes.
 size_t scan_bf16_ws_bytes(int B, int H, int T, int d, int W);
 bool scan_bf16_fast(bool bf16, int dk, int dv, int T);
-// rev_out: the read of position t is stored in row T - 1 - t of m.
 hipError_t launch_tc_scan_bf16(const void* q, const void* k, const void* v, const float* lam, const float* eta,
-                               int B, int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s,
-                               bool rev_out = false);
+                               int B, int H, int T, int d, int W, float* m, float* A_final, void* ws, hipStream_t s);
 hipError_t launch_tc_fused(const void* q, const void* k, const void* v, const float* lam,
                            const float* eta, const float* g, int B, int H, int T, int d, int W,
                            float scale, float* y, float* A_final, void* ws, hipStream_t s);

@@ -24,6 +24,7 @@
 // are widened to fp32 when staged, and the state is fp32 throughout.
 #include "tc_common.hpp"
 #include "tc_kernels.hpp"
+#include "tc_bwd_paths.hpp"
 
 #include <algorithm>
 
@@ -1225,7 +1226,8 @@ hipError_t run_scan_backward_128(const float* q, const float* k, const float* v,
       const BwdStates pi = pre.fs ? BwdStates{pre.fs + off, pre.fd + off, pre.rs + off} : pre;
       const ScanBwdPiece pc{D, b != 0, a != 0, i != 0, fwd_only};  // dq_a, dk_a: two b; dv_b: two a
       e = run_scan_backward<PD>(q + 64 * a, k + 64 * a, v + 64 * b, lam, eta, gate, B, H, T, W, dm + 64 * b,
-                                dq + 64 * a, dk + 64 * a, dv + 64 * b, dlam, deta, dgate, ws, s, pc, pi);
+                                dq + 64 * a, fwd_only ? nullptr : dk + 64 * a, fwd_only ? nullptr : dv + 64 * b,
+                                dlam, deta, dgate, ws, s, pc, pi);
     }
   return e;
 }
@@ -1364,10 +1366,10 @@ size_t scan_bwd_ws_bytes(int B, int H, int T, int d, int W) {
   return scan_bwd_part_bytes(B, H, p.n_seg) + (d == 128 ? 3 : 2) * scan_ws_bytes(p, B, H, d, d);
 }
 
-hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
-                                   const float* eta, const float* g, int B, int H, int T, int d, int W,
-                                   const float* dm, float* dq, float* dk, float* dv, float* dlam,
-                                   float* deta, float* dg, void* ws, hipStream_t s, bool forward_only) {
+static hipError_t scan_backward(const float* q, const float* k, const float* v, const float* lam, const float* eta,
+                                const float* g, int B, int H, int T, int d, int W, const float* dm, float* dq,
+                                float* dk, float* dv, float* dlam, float* deta, float* dg, void* ws, hipStream_t s,
+                                bool forward_only) {
   char* w = static_cast<char*>(ws);
   const ScanBwdPiece pc{d, false, false, false, forward_only};
   const BwdStates none{nullptr, nullptr, nullptr};
@@ -1379,6 +1381,20 @@ hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* 
                                            forward_only);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_tc_scan_backward(const float* q, const float* k, const float* v, const float* lam,
+                                   const float* eta, const float* g, int B, int H, int T, int d, int W,
+                                   const float* dm, float* dq, float* dk, float* dv, float* dlam,
+                                   float* deta, float* dg, void* ws, hipStream_t s) {
+  return scan_backward(q, k, v, lam, eta, g, B, H, T, d, W, dm, dq, dk, dv, dlam, deta, dg, ws, s, false);
+}
+
+hipError_t launch_tc_scan_backward_fwd_only(const float* q, const float* k, const float* v, const float* lam,
+                                            const float* eta, const float* g, int B, int H, int T, int d, int W,
+                                            const float* dm, float* dq, float* dlam, float* deta, float* dg, void* ws,
+                                            hipStream_t s) {
+  return scan_backward(q, k, v, lam, eta, g, B, H, T, d, W, dm, dq, nullptr, nullptr, dlam, deta, dg, ws, s, true);
 }
 
 }  // namespace tc
